@@ -1,0 +1,19 @@
+"""KDA oracle (test infrastructure only).
+
+A plain fp64 CPU implementation of what the KDA forward computes, written from
+the pages and independent of the HIP library: the two share no code, header,
+helper or constant. Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` may import this package; the product path never
+does.
+
+Parity pins: every function here is pinned by ``tests/test_oracle_*.py``
+against closed forms, invariants and brute force (see the docstrings there).
+"""
+from .oracle import (  # noqa: F401
+    build_oracle,
+    oracle_cumsum,
+    oracle_gate,
+    oracle_recurrence,
+    oracle_forward,
+    library_path,
+)

@@ -1,0 +1,176 @@
+"""ctypes wrapper around ``kda_oracle.c`` (fp64, CPU, test infrastructure only).
+
+Sources, cited by page title and section:
+  [KDA-blog] "Kimi k3 技术报告详解（1）——架构再升华" (stevenstage.github.io,
+             posts/blog7), sections "Kimi Delta Attention" (KDA equation) and
+             "Chunkwise parallel form" (gamma equation, new-gate equation).
+
+Every array crossing this wrapper is converted to contiguous float64 numpy;
+bf16 inputs therefore enter as their exact (already rounded) values.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB_NAME = "libkda_oracle.so"
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def build_oracle(src: str = _SRC, out: Optional[str] = None) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math). Returns the .so path."""
+    out = out or library_path()
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-std=gnu99", "-Wall", "-shared", "-fPIC", src, "-o", tmp,
+           "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _load(path: Optional[str] = None):
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(library_path()) or (
+                os.path.getmtime(library_path()) < os.path.getmtime(_SRC)):
+            build_oracle()
+        _lib = _bind(ctypes.CDLL(library_path()))
+    return _lib
+
+
+def _bind(lib):
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lib.kda_oracle_gate.argtypes = [dp, dp, ctypes.c_double, ctypes.c_long, ctypes.c_int,
+                                    ctypes.c_int, dp]
+    lib.kda_oracle_gate.restype = None
+    lib.kda_oracle_cumsum.argtypes = [dp, ip, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, dp]
+    lib.kda_oracle_cumsum.restype = None
+    lib.kda_oracle_recurrence.argtypes = [dp, dp, dp, dp, dp, dp, ip, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_double, dp, dp, ctypes.c_int]
+    lib.kda_oracle_recurrence.restype = ctypes.c_int
+    return lib
+
+
+def _f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # torch tensor: exact upcast on the CPU
+        import torch
+        x = x.detach().to("cpu", torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _dp(a: Optional[np.ndarray]):
+    if a is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _cu_array(cu, n_tokens: int, batch: int) -> np.ndarray:
+    if cu is None:
+        T = n_tokens // batch
+        return np.arange(batch + 1, dtype=np.int32) * T
+    if hasattr(cu, "detach"):
+        cu = cu.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(cu, dtype=np.int32))
+
+
+def oracle_gate(z, A=None, g_min: float = -5.0, lib_path: Optional[str] = None) -> np.ndarray:
+    """g = g_min * sigmoid(exp(A_h) z) over z of shape [..., H, Dk] (fp64).
+
+    [KDA-blog §Chunkwise parallel form, new-gate equation]
+    """
+    lib = _load(lib_path)
+    z64 = _f64(z)
+    H, Dk = z64.shape[-2], z64.shape[-1]
+    rows = z64.size // (H * Dk)
+    A64 = None if A is None else _f64(A).reshape(H)
+    out = np.empty_like(z64)
+    lib.kda_oracle_gate(_dp(z64), _dp(A64), float(g_min), rows, H, Dk, _dp(out))
+    return out
+
+
+def oracle_cumsum(g, chunk: int, cu_seqlens=None, lib_path: Optional[str] = None) -> np.ndarray:
+    """Chunk-local inclusive cumsum of g [B, T, H, Dk] (restarting at every
+    sequence start and every `chunk` tokens from it).
+
+    [KDA-blog §Chunkwise parallel form, gamma equation]
+    """
+    lib = _load(lib_path)
+    g64 = _f64(g)
+    B, T, H, Dk = g64.shape
+    cu = _cu_array(cu_seqlens, B * T, B)
+    out = np.empty_like(g64)
+    lib.kda_oracle_cumsum(_dp(g64), cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                          len(cu) - 1, H, Dk, int(chunk), _dp(out))
+    return out
+
+
+def oracle_recurrence(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
+                      scale: float = 1.0, nthreads: Optional[int] = None,
+                      lib_path: Optional[str] = None):
+    """Token-by-token fp64 KDA recurrence.
+
+    q, k, g: [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H];
+    initial_state: [N, H, Dk, Dv] or None (zeros); cu_seqlens: [N+1] with
+    B == 1, or None (N = B dense sequences). g is the per-token log-decay.
+    Returns (o [B, T, H, Dv], final_state [N, H, Dk, Dv]) as float64.
+
+    [KDA-blog §Kimi Delta Attention, KDA equation]
+    """
+    lib = _load(lib_path)
+    q64, k64, v64, g64, b64 = (_f64(x) for x in (q, k, v, g, beta))
+    B, T, H, Dk = q64.shape
+    Dv = v64.shape[-1]
+    cu = _cu_array(cu_seqlens, B * T, B)
+    N = len(cu) - 1
+    h064 = None if initial_state is None else _f64(initial_state)
+    o = np.zeros((B, T, H, Dv), dtype=np.float64)
+    hT = np.zeros((N, H, Dk, Dv), dtype=np.float64)
+    nthreads = nthreads or os.cpu_count() or 1
+    rc = lib.kda_oracle_recurrence(_dp(q64), _dp(k64), _dp(v64), _dp(g64), _dp(b64),
+                                   _dp(h064), cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                   N, H, Dk, Dv, float(scale), _dp(o), _dp(hT), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle: invalid arguments")
+    return o, hT
+
+
+def oracle_forward(q, k, v, z, beta, initial_state=None, cu_seqlens=None, A=None,
+                   g_min: float = -5.0, scale: float = 1.0, nthreads: Optional[int] = None,
+                   lib_path: Optional[str] = None):
+    """Gate then recurrence: g = g_min * sigmoid(exp(A_h) z), alpha = exp(g).
+
+    [KDA-blog §Chunkwise parallel form, new-gate equation; §Kimi Delta
+    Attention, KDA equation]
+    """
+    g = oracle_gate(z, A, g_min, lib_path=lib_path)
+    return oracle_recurrence(q, k, v, g, beta, initial_state, cu_seqlens, scale, nthreads,
+                             lib_path=lib_path)
+
+
+def gather_units(x, cu, units: Sequence[tuple]):
+    """Pack the rows of the listed (sequence, head) units of a [1, Ttot, H, ...]
+    or [B, T, H, ...] tensor into [1, sum T_n, 1, ...] (fp64) with its own
+    cu_seqlens, so the oracle can compute a sample of units one by one."""
+    x64 = _f64(x)
+    B, T = x64.shape[0], x64.shape[1]
+    cu = _cu_array(cu, B * T, B)
+    flat = x64.reshape((B * T,) + x64.shape[2:])
+    parts = [flat[cu[n]:cu[n + 1], h][:, None] for (n, h) in units]
+    lens = [cu[n + 1] - cu[n] for (n, _) in units]
+    new_cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return np.concatenate(parts, axis=0)[None], new_cu
