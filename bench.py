@@ -1,0 +1,224 @@
+"""Benchmark of the KDA chunkwise forward on one MI355X.
+
+A step is one kda_chunk_fwd call over the whole batch: gate (from logits),
+chunk-local cumulative decay, intra-chunk products and inverse, the serial
+inter-chunk state scan and the output, all inside the library's kernels. The
+workload is the training-shaped batch B=8, H=32, T=8192, d_k=d_v=128, bf16,
+chunk 64, zero initial state (synthetic, seeded; inputs resident in HBM).
+
+Prints one JSON line. `roofline` reports the fused chunk kernel against HBM
+bandwidth: algorithmic bytes per launch (q, k, v, o in bf16; gate logits and
+beta in fp32; the fp32 state written once per (sequence, head)) divided by the
+kernel's average duration, taken from HIP events recorded around every launch
+on the stream the kernel runs on. `cpu_baseline` is the fp64 oracle timed on
+the host cores on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       python bench.py --copy-calibration   (plain copy kernel for counter scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+FP32_MATRIX_PEAK_TFLOPS = 157.3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fused_train8k_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_92_amd", "csrc", f)
+                  for f in ("kda_chunk.hip", "kda_common.h")]
+
+
+def log(msg: str):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def algorithmic_bytes(w, n_tokens: int, n_units: int, has_h0: bool) -> int:
+    """HBM bytes the forward must move at minimum for one launch."""
+    el = 2 if w.dtype_name == "bf16" else 4
+    per_tok_head = (2 * w.Dk + 2 * w.Dv) * el + w.Dk * 4 + 4  # q,k | v,o | logits | beta
+    state = w.Dk * w.Dv * 4 * n_units * (2 if has_h0 else 1)
+    return per_tok_head * n_tokens * w.H + state
+
+
+def algorithmic_flops(w, n_tokens: int) -> float:
+    """Matrix-core flops of the chunk arrangement per launch: per chunk of 64,
+    the causal 16x16 tiles (10 of 16) of A_kk, A_qk, the triangular solve and
+    A_qk V~ over d, plus the three state products (d_k x d_v each)."""
+    C, dk, dv = 64, w.Dk, w.Dv
+    tiles = 10 * 16 * 16 * 2
+    per_chunk = tiles * dk * 2 + tiles * dv * 2 + 3 * 2 * C * dk * dv
+    return per_chunk / C * n_tokens * w.H
+
+
+def cpu_baseline(d, w, budget_s: float = 20.0):
+    """The fp64 oracle on a bounded sample of (sequence, head) units of the
+    same workload, on the host cores; returns a dict for the JSON line."""
+    import numpy as np
+    from oracle import oracle_forward
+    cores = min(os.cpu_count() or 1, 16)
+    T = d["q"].shape[1]
+    H = d["q"].shape[2]
+
+    def unit_inputs(units):
+        qs, ks, vs, zs, bs = [], [], [], [], []
+        for (n, h) in units:
+            qs.append(d["q"][n, :, h].cpu())
+            ks.append(d["k"][n, :, h].cpu())
+            vs.append(d["v"][n, :, h].cpu())
+            zs.append(d["z"][n, :, h].cpu())
+            bs.append(d["beta"][n, :, h].cpu())
+        import torch
+        cu = torch.tensor(np.arange(len(units) + 1) * T, dtype=torch.int32)
+        cat = lambda xs: torch.cat(xs, 0)[None, :, None]  # noqa: E731
+        return cat(qs), cat(ks), cat(vs), cat(zs), torch.cat(bs, 0)[None, :, None], cu
+
+    # one unit on one thread to size the sample
+    q, k, v, z, b, cu = unit_inputs([(0, 0)])
+    t0 = time.perf_counter()
+    oracle_forward(q, k, v, z, b, None, cu, None, w.g_min, 1.0, nthreads=1)
+    per_unit = time.perf_counter() - t0
+    n_units = max(cores, int(budget_s / max(per_unit, 1e-3)))
+    n_units = min(n_units, d["q"].shape[0] * H)
+    n_units = max(cores, (n_units // cores) * cores)
+    units = [(i % d["q"].shape[0], (i // d["q"].shape[0]) % H) for i in range(n_units)]
+    q, k, v, z, b, cu = unit_inputs(units)
+    t0 = time.perf_counter()
+    oracle_forward(q, k, v, z, b, None, cu, None, w.g_min, 1.0, nthreads=cores)
+    wall = time.perf_counter() - t0
+    return {"value": n_units * T / wall, "unit": "tokens·heads/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{n_units} (sequence, head) units x {T} tokens of the {w.name} workload, "
+                      f"fp64 token-by-token recurrence, {cores} threads, {wall:.1f} s wall"}
+
+
+def copy_calibration(n_bytes: int = 1 << 30):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    x = torch.empty(n_bytes // 4, dtype=torch.float32, device="cuda").normal_()
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {n_bytes} bytes read and {n_bytes} bytes written per copy")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="train8k")
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path is built); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+
+    from gated_delta_rule_92_amd import chunk_fwd, workspace_size
+    from gated_delta_rule_92_amd.inputs import make_workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"bench: generating workload {args.workload} on {torch.cuda.get_device_name(dev)}")
+    d = make_workload(args.workload, device=dev)
+    w = d["workload"]
+    n_tokens = int(d["q"].shape[0] * d["q"].shape[1])
+    N = d["N"]
+    ws = workspace_size(d["q"].shape[0], d["q"].shape[1], w.H, w.Dk, w.Dv, N, w.chunk, w.dtype)
+    workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+    o = torch.empty(d["v"].shape, dtype=w.dtype, device=dev)
+    hT = torch.empty((N, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+
+    def step():
+        chunk_fwd(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"], d["cu_seqlens"],
+                  gate="logits", g_min=w.g_min, chunk=w.chunk, o=o, final_state=hT,
+                  workspace=workspace)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    log(f"bench: {args.steps} steps, wall {ms_per_step:.3f} ms/step, event {kernel_ms:.3f} ms/launch")
+
+    tok_heads = n_tokens * w.H
+    value = tok_heads / (ms_per_step / 1e3)
+    bytes_alg = algorithmic_bytes(w, n_tokens, N * w.H, d["h0"] is not None)
+    achieved = bytes_alg / (kernel_ms / 1e3) / 1e9
+    flops = algorithmic_flops(w, n_tokens)
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+        if rec.get("source_sha256") == kernel_source_hash() and rec.get("workload") == w.name:
+            traffic = rec.get("bytes_per_launch")
+
+    cpu = None
+    if not args.skip_cpu_baseline and d["cu_seqlens"] is None:
+        log("bench: timing the fp64 oracle on a bounded sample (cpu_baseline)")
+        cpu = cpu_baseline(d, w)
+
+    line = {
+        "metric": "KDA chunk fwd tokens·heads/s (H=32,d=128,bf16,T=8K); % MFMA peak",
+        "value": value,
+        "unit": "tokens·heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype_name,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": int(d["q"].shape[0]), "seq_len": w.T, "heads": w.H,
+                   "d_k": w.Dk, "d_v": w.Dv, "chunk": w.chunk, "gate": "logits",
+                   "g_min": w.g_min, "initial_state": d["h0"] is not None,
+                   "sequences": N},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+        "mfma_peak_frac": flops / (kernel_ms / 1e3) / (BF16_DENSE_PEAK_TFLOPS * 1e12)
+        if w.dtype_name == "bf16" else flops / (kernel_ms / 1e3) / (FP32_MATRIX_PEAK_TFLOPS * 1e12),
+        "kernel_ms": kernel_ms,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

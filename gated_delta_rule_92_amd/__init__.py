@@ -1,0 +1,12 @@
+"""MI355X-native KDA (Kimi Delta Attention) forward: gate, chunkwise forward and
+decode step, backed by hand-written gfx950 HIP kernels in libkda.so.
+
+Public API (thin wrappers over the C ABI in include/kda.h):
+    gate(z, A_log=None, g_min=-5.0, chunk=0, cu_seqlens=None)
+    chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
+              gate="logdecay", A_log=None, g_min=-5.0, chunk=64, scale=1.0)
+    recurrent_step(q, k, v, g, beta, state, gate="logdecay", ...)
+"""
+from .ops import chunk_fwd, gate, recurrent_step, workspace_size  # noqa: F401
+
+__all__ = ["chunk_fwd", "gate", "recurrent_step", "workspace_size"]

@@ -1,0 +1,167 @@
+// C ABI of libkda.so: argument validation (before anything touches the GPU),
+// workspace carving and kernel selection. Declarations and the contract of
+// every entry point are in include/kda.h.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr size_t kWorkspaceAlign = 256;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+kda_status_t launch_status(hipError_t e) {
+  return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH_FAILURE;
+}
+
+// Common sequence-geometry checks. Fills `s` on success.
+kda_status_t check_seqs(const int32_t* cu, int N, int B, int T, kda::Seqs* s) {
+  if (B <= 0 || T < 0) return KDA_ERROR_INVALID_VALUE;
+  if (cu) {
+    if (B != 1 || N < 0) return KDA_ERROR_INVALID_VALUE;
+    s->cu = cu;
+    s->N = N;
+  } else {
+    s->cu = nullptr;
+    s->N = B;
+  }
+  s->T = T;
+  s->Ttot = (long)B * T;
+  return KDA_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status_t status) {
+  switch (status) {
+    case KDA_SUCCESS: return "KDA_SUCCESS";
+    case KDA_ERROR_INVALID_VALUE: return "KDA_ERROR_INVALID_VALUE";
+    case KDA_ERROR_NOT_SUPPORTED: return "KDA_ERROR_NOT_SUPPORTED";
+    case KDA_ERROR_INSUFFICIENT_WORKSPACE: return "KDA_ERROR_INSUFFICIENT_WORKSPACE";
+    case KDA_ERROR_LAUNCH_FAILURE: return "KDA_ERROR_LAUNCH_FAILURE";
+  }
+  return "KDA_ERROR_UNKNOWN";
+}
+
+int kda_version(void) { return kVersion; }
+
+kda_status_t kda_gate(const float* z, const float* A_log, float g_min, const int32_t* cu_seqlens,
+                      int N, int B, int T, int H, int Dk, int chunk, float* g_out,
+                      kda_stream_t stream) {
+  kda::Seqs s;
+  kda_status_t st = check_seqs(cu_seqlens, N, B, T, &s);
+  if (st != KDA_SUCCESS) return st;
+  if (H <= 0 || Dk <= 0 || chunk < 0 || !(g_min < 0.0f)) return KDA_ERROR_INVALID_VALUE;
+  if (s.Ttot > 0 && (!z || !g_out)) return KDA_ERROR_INVALID_VALUE;
+  if (!aligned16(z) || !aligned16(g_out)) return KDA_ERROR_INVALID_VALUE;
+  if (chunk > 0 && z == g_out) return KDA_ERROR_INVALID_VALUE;
+  if (Dk % 4 != 0) return KDA_ERROR_NOT_SUPPORTED;
+  return launch_status(kda::launch_gate(z, A_log, g_min, s, H, Dk, chunk, g_out,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, int N, int chunk,
+                                          kda_dtype_t dtype, size_t* bytes) {
+  if (!bytes || B <= 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || N < 0 || chunk <= 0)
+    return KDA_ERROR_INVALID_VALUE;
+  if (dtype != KDA_FLOAT32 && dtype != KDA_BFLOAT16) return KDA_ERROR_INVALID_VALUE;
+  // Longest-first order of packed sequences (used only with cu_seqlens).
+  size_t need = 0;
+  if (B == 1 && N > 1 && N <= kda::kMaxOrderN) need += round_up(sizeof(int32_t) * (size_t)N, kWorkspaceAlign);
+  *bytes = need;
+  return KDA_SUCCESS;
+}
+
+kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                           const float* g, kda_gate_input_t gate_input, const float* A_log,
+                           float g_min, const float* beta, const float* initial_state,
+                           const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
+                           int Dv, int chunk, float scale, void* o, float* final_state,
+                           void* workspace, size_t workspace_bytes, kda_stream_t stream) {
+  kda::Seqs s;
+  kda_status_t st = check_seqs(cu_seqlens, N, B, T, &s);
+  if (st != KDA_SUCCESS) return st;
+  if (!cu_seqlens && N != B) return KDA_ERROR_INVALID_VALUE;
+  if (H <= 0 || Dk <= 0 || Dv <= 0 || chunk <= 0) return KDA_ERROR_INVALID_VALUE;
+  if (dtype != KDA_FLOAT32 && dtype != KDA_BFLOAT16) return KDA_ERROR_INVALID_VALUE;
+  if (gate_input != KDA_GATE_LOGDECAY && gate_input != KDA_GATE_CUMSUM &&
+      gate_input != KDA_GATE_LOGITS)
+    return KDA_ERROR_INVALID_VALUE;
+  if (gate_input == KDA_GATE_LOGITS && !(g_min < 0.0f)) return KDA_ERROR_INVALID_VALUE;
+  if (s.Ttot > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o) ||
+      !aligned16(initial_state) || !aligned16(final_state))
+    return KDA_ERROR_INVALID_VALUE;
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) % kWorkspaceAlign) != 0)
+    return KDA_ERROR_INVALID_VALUE;
+  const bool bf16 = dtype == KDA_BFLOAT16;
+  const bool fused = kda::chunk_fused_supported(bf16, Dk, Dv, chunk);
+  if (!fused) {
+    if (Dk > 256) return KDA_ERROR_NOT_SUPPORTED;
+    if (gate_input == KDA_GATE_CUMSUM) return KDA_ERROR_NOT_SUPPORTED;
+  }
+  size_t need = 0;
+  st = kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, s.N, chunk, dtype, &need);
+  if (st != KDA_SUCCESS) return st;
+  if (workspace && workspace_bytes < need) return KDA_ERROR_INSUFFICIENT_WORKSPACE;
+  if (s.N == 0) return KDA_SUCCESS;
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (fused) {
+    kda::ChunkArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.gate_mode = (int)gate_input;
+    a.A_log = A_log; a.g_min = g_min; a.beta = beta;
+    a.h0 = initial_state; a.hT = final_state; a.o = o;
+    a.seqs = s; a.order = nullptr;
+    a.H = H; a.Dk = Dk; a.Dv = Dv; a.scale = scale; a.bf16 = bf16;
+    if (cu_seqlens && workspace && need > 0 && s.N > 1) {
+      int32_t* order = static_cast<int32_t*>(workspace);
+      hipError_t e = kda::launch_order(cu_seqlens, s.N, order, hs);
+      if (e != hipSuccess) return KDA_ERROR_LAUNCH_FAILURE;
+      a.order = order;
+    }
+    return launch_status(kda::launch_chunk_fused(a, hs));
+  }
+  kda::RecurrentArgs r;
+  r.q = q; r.k = k; r.v = v; r.g = g; r.gate_mode = (int)gate_input;
+  r.A_log = A_log; r.g_min = g_min; r.beta = beta;
+  r.h0 = initial_state; r.hT = final_state; r.o = o;
+  r.seqs = s; r.H = H; r.Dk = Dk; r.Dv = Dv; r.scale = scale; r.bf16 = bf16;
+  return launch_status(kda::launch_recurrent(r, hs));
+}
+
+kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                                const float* g, kda_gate_input_t gate_input,
+                                const float* A_log, float g_min, const float* beta,
+                                float* state, int N, int H, int Dk, int Dv, float scale,
+                                void* o, kda_stream_t stream) {
+  if (N < 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_ERROR_INVALID_VALUE;
+  if (dtype != KDA_FLOAT32 && dtype != KDA_BFLOAT16) return KDA_ERROR_INVALID_VALUE;
+  if (gate_input != KDA_GATE_LOGDECAY && gate_input != KDA_GATE_LOGITS)
+    return KDA_ERROR_INVALID_VALUE;
+  if (gate_input == KDA_GATE_LOGITS && !(g_min < 0.0f)) return KDA_ERROR_INVALID_VALUE;
+  if (N > 0 && (!q || !k || !v || !g || !beta || !state || !o)) return KDA_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o) ||
+      !aligned16(state))
+    return KDA_ERROR_INVALID_VALUE;
+  if (Dk > 256) return KDA_ERROR_NOT_SUPPORTED;
+  if (N == 0) return KDA_SUCCESS;
+  kda::RecurrentArgs r;
+  r.q = q; r.k = k; r.v = v; r.g = g; r.gate_mode = (int)gate_input;
+  r.A_log = A_log; r.g_min = g_min; r.beta = beta;
+  r.h0 = state; r.hT = state; r.o = o;
+  r.seqs.cu = nullptr; r.seqs.N = N; r.seqs.T = 1; r.seqs.Ttot = N;
+  r.H = H; r.Dk = Dk; r.Dv = Dv; r.scale = scale; r.bf16 = dtype == KDA_BFLOAT16;
+  return launch_status(kda::launch_recurrent(r, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Host-side launchers of the KDA kernels (internal to libkda.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+enum GateMode { kGateLogDecay = 0, kGateCumsum = 1, kGateLogits = 2 };
+
+// Sequence geometry shared by the launchers. Either cu (device, N+1 entries)
+// describes packed sequences, or cu == nullptr and sequence n covers tokens
+// [n*T, (n+1)*T) of a dense batch.
+struct Seqs {
+  const int32_t* cu;
+  int N;
+  int T;        // dense sequence length (ignored when cu != nullptr)
+  long Ttot;    // total tokens in the packed token axis
+};
+
+hipError_t launch_gate(const float* z, const float* A_log, float g_min, Seqs s, int H, int Dk,
+                       int chunk, float* g, hipStream_t stream);
+
+// Token-serial kernel: the recurrence one token at a time for every
+// (sequence, head), the state held on chip. Used for decode (one token per
+// sequence) and for shapes the chunk path does not cover.
+struct RecurrentArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  int gate_mode;  // kGateLogDecay or kGateLogits
+  const float* A_log;
+  float g_min;
+  const float* beta;
+  const float* h0;   // [N, H, Dk, Dv] or nullptr
+  float* hT;         // [N, H, Dk, Dv] or nullptr (may alias h0)
+  void* o;
+  Seqs seqs;
+  int H, Dk, Dv;
+  float scale;
+  bool bf16;
+};
+hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream);
+
+// Fused chunk kernel (matrix cores), one workgroup per (sequence, head).
+struct ChunkArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  int gate_mode;
+  const float* A_log;
+  float g_min;
+  const float* beta;
+  const float* h0;
+  float* hT;
+  void* o;
+  Seqs seqs;
+  const int32_t* order;  // [N] longest-first sequence order, or nullptr
+  int H, Dk, Dv;
+  float scale;
+  bool bf16;
+};
+bool chunk_fused_supported(bool bf16, int Dk, int Dv, int chunk);
+hipError_t launch_chunk_fused(const ChunkArgs& a, hipStream_t stream);
+
+// Longest-first ordering of packed sequences (N <= kMaxOrderN), into order[N].
+constexpr int kMaxOrderN = 8192;
+hipError_t launch_order(const int32_t* cu, int N, int32_t* order, hipStream_t stream);
+
+}  // namespace kda

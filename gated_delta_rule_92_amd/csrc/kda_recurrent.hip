@@ -1,0 +1,140 @@
+// Token-serial KDA kernel: the recurrence of "Kimi k3 技术报告详解（1）——
+// 架构再升华", section "Kimi Delta Attention" (KDA equation), applied one
+// token at a time with the state held on chip:
+//   S <- Diag(alpha_t) S;  u = S^T k_t;  d = beta_t (v_t - u);
+//   S <- S + k_t d^T;      o_t = scale * S^T q_t,     alpha_t = exp(g_t).
+// Used for decode (one token per sequence, state updated in place) and as the
+// general path for shapes the matrix-core chunk kernel does not cover.
+//
+// The recurrence is exactly separable over the value columns of S: column j
+// of the state, output and update depends only on column j of v and of the
+// state. A workgroup therefore owns one (sequence, head, 64-column slice);
+// thread (j, p) keeps rows [p*Dk/4, (p+1)*Dk/4) of column j in registers and
+// the two Dk-long dot products per token are reduced across the four row
+// parts through LDS.
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+constexpr int kRecCols = 64;   // value columns per workgroup
+constexpr int kRecParts = 4;   // row parts per column
+constexpr int kRecMaxDk = 256;
+
+template <typename T, int MAXR>
+__global__ void __launch_bounds__(256) recurrent_kernel(RecurrentArgs a) {
+  const T* __restrict__ q = reinterpret_cast<const T*>(a.q);
+  const T* __restrict__ k = reinterpret_cast<const T*>(a.k);
+  const T* __restrict__ v = reinterpret_cast<const T*>(a.v);
+  T* __restrict__ o = reinterpret_cast<T*>(a.o);
+  const int H = a.H, Dk = a.Dk, Dv = a.Dv;
+  const int unit = blockIdx.x;
+  const int n = unit / H, h = unit % H;
+  const int col0 = blockIdx.y * kRecCols;
+  const int tid = threadIdx.x;
+  const int jl = tid % kRecCols, p = tid / kRecCols;
+  const int j = col0 + jl;
+  const bool jvalid = j < Dv;
+  const int rows_per_part = (Dk + kRecParts - 1) / kRecParts;
+  const int r0 = p * rows_per_part;
+
+  __shared__ float s_k[kRecMaxDk], s_q[kRecMaxDk], s_a[kRecMaxDk];
+  __shared__ float s_v[kRecCols];
+  __shared__ float s_red0[kRecParts][kRecCols], s_red1[kRecParts][kRecCols];
+  __shared__ float s_beta;
+
+  long bos, eos;
+  if (a.seqs.cu) {
+    bos = a.seqs.cu[n];
+    eos = a.seqs.cu[n + 1];
+  } else {
+    bos = (long)n * a.seqs.T;
+    eos = bos + a.seqs.T;
+  }
+  const size_t sbase = ((size_t)n * H + h) * Dk * Dv;
+  float s[MAXR];
+#pragma unroll
+  for (int i = 0; i < MAXR; ++i) {
+    int r = r0 + i;
+    s[i] = (a.h0 && jvalid && i < rows_per_part && r < Dk) ? a.h0[sbase + (size_t)r * Dv + j]
+                                                           : 0.f;
+  }
+  const float es = (a.gate_mode == kGateLogits && a.A_log) ? __expf(a.A_log[h]) : 1.0f;
+
+  for (long t = bos; t < eos; ++t) {
+    const size_t rk = ((size_t)t * H + h) * Dk;
+    for (int c = tid; c < Dk; c += blockDim.x) {
+      s_k[c] = to_f32(k[rk + c]);
+      s_q[c] = to_f32(q[rk + c]);
+      float gv = a.g[rk + c];
+      if (a.gate_mode == kGateLogits) gv = a.g_min / (1.0f + __expf(-es * gv));
+      s_a[c] = __expf(gv);
+    }
+    if (tid < kRecCols) {
+      int jj = col0 + tid;
+      s_v[tid] = jj < Dv ? to_f32(v[((size_t)t * H + h) * Dv + jj]) : 0.f;
+    }
+    if (tid == 0) s_beta = a.beta[(size_t)t * H + h];
+    __syncthreads();
+    // decay, then partial retrieval u_j = sum_i S_ij k_i over this row part
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXR; ++i) {
+      int r = r0 + i;
+      if (i < rows_per_part && r < Dk) {
+        s[i] *= s_a[r];
+        part += s[i] * s_k[r];
+      }
+    }
+    s_red0[p][jl] = part;
+    __syncthreads();
+    float u = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < kRecParts; ++pp) u += s_red0[pp][jl];
+    const float d = s_beta * (s_v[jl] - u);
+    float opart = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXR; ++i) {
+      int r = r0 + i;
+      if (i < rows_per_part && r < Dk) {
+        s[i] += s_k[r] * d;
+        opart += s[i] * s_q[r];
+      }
+    }
+    s_red1[p][jl] = opart;
+    __syncthreads();
+    if (p == 0 && jvalid) {
+      float ov = 0.f;
+#pragma unroll
+      for (int pp = 0; pp < kRecParts; ++pp) ov += s_red1[pp][jl];
+      o[((size_t)t * H + h) * Dv + j] = from_f32<T>(a.scale * ov);
+    }
+  }
+  if (a.hT && jvalid) {
+#pragma unroll
+    for (int i = 0; i < MAXR; ++i) {
+      int r = r0 + i;
+      if (i < rows_per_part && r < Dk) a.hT[sbase + (size_t)r * Dv + j] = s[i];
+    }
+  }
+}
+
+template <typename T>
+static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream) {
+  dim3 grid((unsigned)(a.seqs.N * a.H), (unsigned)((a.Dv + kRecCols - 1) / kRecCols));
+  int rpp = (a.Dk + kRecParts - 1) / kRecParts;
+  if (rpp <= 16)
+    hipLaunchKernelGGL((recurrent_kernel<T, 16>), grid, dim3(256), 0, stream, a);
+  else if (rpp <= 32)
+    hipLaunchKernelGGL((recurrent_kernel<T, 32>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((recurrent_kernel<T, 64>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream) {
+  if (a.seqs.N == 0 || a.H == 0) return hipSuccess;
+  return a.bf16 ? launch_recurrent_t<__bf16>(a, stream) : launch_recurrent_t<float>(a, stream);
+}
+
+}  // namespace kda

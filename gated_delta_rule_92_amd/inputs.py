@@ -44,6 +44,10 @@ class Workload:
     chunk: int = 64
     g_min: float = -5.0
 
+    @property
+    def dtype_name(self) -> str:
+        return "bf16" if self.dtype == torch.bfloat16 else "fp32"
+
 
 WORKLOADS = {
     "tiny": Workload("tiny", 1, 256, 2, 64, 64, torch.float32, 0.0),

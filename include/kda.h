@@ -1,0 +1,171 @@
+/*
+ * kda.h — C ABI of the MI355X (gfx950) KDA forward library (libkda.so).
+ *
+ * KDA (Kimi Delta Attention) is a gated delta-rule linear attention. Per
+ * (sequence, head) it keeps a d_k x d_v state S and, for every token,
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = scale * S_t^T q_t,          alpha_t = exp(g_t)  (per channel),
+ * with the lower-bounded log-decay gate g = g_min * sigmoid(exp(A_h) z).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [KDA-blog] "Kimi k3 技术报告详解（1）——架构再升华" (stevenstage.github.io,
+ *              posts/blog7): section "Kimi Delta Attention" (KDA equation),
+ *              section "Chunkwise parallel form" (gamma, W/U, pseudo-value
+ *              and A/O equations; old and new gate equations).
+ *   [Baidu-1]  "Kimi K3 Core Techniques Explained: How Three Innovations
+ *              Reshape LLM Training Efficiency", §1.2 (g_min = -5 fixed;
+ *              16-token tiles stay in range).
+ *   [Baidu-2]  "A Look at Kimi K3: Three Core Innovations and Engineering
+ *              Tuning Guide", §2.2 (kda_decay(Ah, z) = g_min*sigmoid(exp(Ah)*z)).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.  Every tensor argument is a DEVICE pointer owned by the caller; the
+ *   library never allocates or frees device memory. Tensors are contiguous,
+ *   row-major, in the layouts stated per argument. Dense batches use
+ *   [B, T, H, D]; packed variable-length batches use B = 1, T = total tokens
+ *   and cu_seqlens (device int32 [N+1], non-decreasing, cu_seqlens[0] = 0,
+ *   cu_seqlens[N] = T) to mark sequence n as tokens [cu[n], cu[n+1]).
+ *   Pointers to q, k, v, o, g, z must be 16-byte aligned.
+ * Streams.  Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *   stream) and the call returns without synchronising. Calls are stateless
+ *   and re-entrant; concurrent calls must not share outputs or workspaces.
+ * Errors.  Arguments are validated on the host before anything is enqueued:
+ *   KDA_ERROR_INVALID_VALUE for NULL required pointers, non-positive or
+ *   inconsistent sizes, misaligned pointers; KDA_ERROR_NOT_SUPPORTED for
+ *   shapes outside the supported set; KDA_ERROR_INSUFFICIENT_WORKSPACE.
+ *   A failed launch returns KDA_ERROR_LAUNCH_FAILURE. On any error nothing
+ *   has been enqueued. Not checked (documented preconditions): contiguity,
+ *   g within [g_min, 0] when g is passed directly, cu_seqlens well formed.
+ * Precision.  q, k, v, o share `dtype` (fp32 or bf16). g, z, A_log, beta and
+ *   the states are always fp32. Accumulation is fp32. For bf16 inputs the
+ *   matrix products round their operands to bf16.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t. */
+typedef struct ihipStream_t* kda_stream_t;
+
+typedef enum {
+  KDA_SUCCESS = 0,
+  KDA_ERROR_INVALID_VALUE = 1,
+  KDA_ERROR_NOT_SUPPORTED = 2,
+  KDA_ERROR_INSUFFICIENT_WORKSPACE = 3,
+  KDA_ERROR_LAUNCH_FAILURE = 4
+} kda_status_t;
+
+typedef enum { KDA_FLOAT32 = 0, KDA_BFLOAT16 = 1 } kda_dtype_t;
+
+/* What the `g` argument of kda_chunk_fwd / kda_recurrent_step holds. */
+typedef enum {
+  /* per-token log-decay g_t in [g_min, 0]; alpha_t = exp(g_t) */
+  KDA_GATE_LOGDECAY = 0,
+  /* chunk-local inclusive cumsum of the log-decay, as produced by kda_gate
+     with the same `chunk` (chunk_fwd only) */
+  KDA_GATE_CUMSUM = 1,
+  /* gate logits z; the library applies g = g_min * sigmoid(exp(A_h) z) */
+  KDA_GATE_LOGITS = 2
+} kda_gate_input_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* kda_status_string(kda_status_t status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int kda_version(void);
+
+/*
+ * kda_gate — the lower-bounded decay gate, optionally followed by the
+ * chunk-local cumulative sum.
+ *   g = g_min * sigmoid(exp(A_h) * z)      [KDA-blog §Chunkwise parallel
+ *                                            form, new-gate equation;
+ *                                            Baidu-2 §2.2 kda_decay]
+ *   then, if chunk > 0, G_r = g_1 + ... + g_r inside each chunk of `chunk`
+ *   tokens, chunks starting at each sequence's first token
+ *   (log of gamma^r = prod_{i<=r} alpha^i)  [KDA-blog §Chunkwise parallel
+ *                                            form, gamma equation]
+ * z       device fp32 [B, T, H, Dk] gate logits
+ * A_log   device fp32 [H] per-head A_h, or NULL for A_h = 0 (exp(A_h) = 1)
+ * g_min   lower bound of g (negative; -5 on the pages)
+ * cu_seqlens, N   packed sequences (then B must be 1) or NULL (N ignored)
+ * chunk   0 = no cumsum; else the chunk length (any positive value)
+ * g_out   device fp32 [B, T, H, Dk]; may alias z (in-place) only when chunk = 0
+ * Result is in [g_min, 0] per element (closed interval after rounding).
+ */
+kda_status_t kda_gate(const float* z, const float* A_log, float g_min,
+                      const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
+                      int chunk, float* g_out, kda_stream_t stream);
+
+/*
+ * kda_chunk_fwd_workspace_size — bytes of device workspace kda_chunk_fwd
+ * needs for these sizes (may be 0). The workspace must be 256-byte aligned.
+ */
+kda_status_t kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, int N,
+                                          int chunk, kda_dtype_t dtype, size_t* bytes);
+
+/*
+ * kda_chunk_fwd — chunkwise-parallel KDA forward over whole sequences.
+ * Computes exactly the token recurrence stated at the top of this file
+ * [KDA-blog §Kimi Delta Attention, KDA equation], arranged as the chunk form
+ * [KDA-blog §Chunkwise parallel form: gamma, W/U, pseudo-value, A/O
+ * equations]: inside each chunk of C = 64 tokens the decayed key-key matrix
+ * is inverted as a unit-triangular system, the pseudo-values
+ * V~ = U - W S are formed from the state entering the chunk, the output is
+ * O = (Gamma*Q) S + Tril[(Q*Gamma)(K/Gamma)^T] V~ and the state is handed
+ * to the next chunk as Diag(Gamma_C) S + (K*Gamma_C/Gamma)^T V~.
+ *
+ * q, k       device dtype [B, T, H, Dk]
+ * v          device dtype [B, T, H, Dv]
+ * g          device fp32 [B, T, H, Dk], meaning set by gate_input
+ * A_log, g_min   used only with KDA_GATE_LOGITS (A_log may be NULL)
+ * beta       device fp32 [B, T, H]
+ * initial_state  device fp32 [N, H, Dk, Dv] or NULL (zeros)
+ * cu_seqlens, N  packed sequences (B must be 1) or NULL (then N must equal B)
+ * chunk      must be 64
+ * scale      output scale (1.0 on the pages)
+ * o          device dtype [B, T, H, Dv] (written)
+ * final_state device fp32 [N, H, Dk, Dv] or NULL (written); may alias
+ *            initial_state
+ * workspace  device, >= kda_chunk_fwd_workspace_size(...) bytes, or NULL
+ *            when that size is 0
+ * Supported: bf16 with Dk, Dv in {64, 128}; fp32 with Dk = Dv = 64 on the
+ * matrix-core chunk path; any other Dk, Dv <= 256 (and fp32 at 128) runs a
+ * token-serial kernel with the same results. Zero-length sequences are
+ * allowed (final state = initial state).
+ */
+kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                           const float* g, kda_gate_input_t gate_input, const float* A_log,
+                           float g_min, const float* beta, const float* initial_state,
+                           const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
+                           int Dv, int chunk, float scale, void* o, float* final_state,
+                           void* workspace, size_t workspace_bytes, kda_stream_t stream);
+
+/*
+ * kda_recurrent_step — one token of the KDA recurrence (decode), updating
+ * the state in place [KDA-blog §Kimi Delta Attention, KDA equation]:
+ *   S <- Diag(alpha) S;  u = S^T k;  S <- S + beta k (v - u)^T;  o = scale S^T q
+ * q, k       device dtype [N, H, Dk];  v, o device dtype [N, H, Dv]
+ * g          device fp32 [N, H, Dk]: log-decay (KDA_GATE_LOGDECAY) or logits
+ *            (KDA_GATE_LOGITS, with A_log / g_min); KDA_GATE_CUMSUM is invalid
+ * beta       device fp32 [N, H]
+ * state      device fp32 [N, H, Dk, Dv], read and written
+ * Supported: Dk <= 256, any Dv >= 1.
+ */
+kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                                const float* g, kda_gate_input_t gate_input,
+                                const float* A_log, float g_min, const float* beta,
+                                float* state, int N, int H, int Dk, int Dv, float scale,
+                                void* o, kda_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,119 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+public header declares, and rejects bad arguments on the host before any GPU
+work (validation happens before the first HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_92_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libkda.so not built (run __graft_entry__.build())")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_expected_api():
+    assert _declared_functions() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    lib = _lib.load()
+    assert lib.kda_version() >= 100
+    for code, name in [(0, "KDA_SUCCESS"), (1, "KDA_ERROR_INVALID_VALUE"),
+                       (2, "KDA_ERROR_NOT_SUPPORTED"), (3, "KDA_ERROR_INSUFFICIENT_WORKSPACE"),
+                       (4, "KDA_ERROR_LAUNCH_FAILURE")]:
+        assert lib.kda_status_string(code).decode() == name
+    assert lib.kda_status_string(99).decode() == "KDA_ERROR_UNKNOWN"
+
+
+FAKE = 1 << 20  # an aligned, never-dereferenced address: validation fails first
+
+
+def _chunk(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, g=FAKE, gate=0, A=None, g_min=-5.0, beta=FAKE,
+                h0=None, cu=None, N=1, B=1, T=64, H=2, Dk=128, Dv=128, chunk=64, scale=1.0,
+                o=FAKE, hT=None, ws=None, ws_bytes=0, stream=None)
+    args.update(kw)
+    return _lib.load().kda_chunk_fwd(*args.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(k=None), dict(v=None), dict(g=None), dict(beta=None), dict(o=None),
+    dict(B=0), dict(T=-1), dict(H=0), dict(Dk=0), dict(Dv=0), dict(chunk=0),
+    dict(N=2),                          # N != B without cu_seqlens
+    dict(cu=FAKE, B=2, N=2),            # cu_seqlens needs B == 1
+    dict(q=FAKE + 4),                   # misaligned
+    dict(o=FAKE + 8),
+    dict(dtype=7), dict(gate=5),
+    dict(gate=2, g_min=0.0),            # logits need g_min < 0
+    dict(ws=FAKE + 64, ws_bytes=1024),  # workspace must be 256-byte aligned
+])
+def test_chunk_fwd_rejects_invalid(kw):
+    assert _chunk(**kw) == _lib.KDA_ERROR_INVALID_VALUE
+
+
+def test_chunk_fwd_not_supported_and_workspace():
+    assert _chunk(Dk=512) == _lib.KDA_ERROR_NOT_SUPPORTED
+    assert _chunk(chunk=32, gate=1) == _lib.KDA_ERROR_NOT_SUPPORTED
+    n = ctypes.c_size_t(123)
+    lib = _lib.load()
+    assert lib.kda_chunk_fwd_workspace_size(1, 1 << 20, 32, 128, 128, 64, 64, 1, ctypes.byref(n)) == 0
+    assert n.value >= 64 * 4 and n.value % 256 == 0
+    assert _chunk(cu=FAKE, N=64, T=4096, ws=FAKE, ws_bytes=4) == _lib.KDA_ERROR_INSUFFICIENT_WORKSPACE
+    assert lib.kda_chunk_fwd_workspace_size(0, 1, 1, 1, 1, 1, 64, 1, ctypes.byref(n)) == 1
+
+
+def test_zero_sized_problem_succeeds_without_gpu_work():
+    # N = 0 packed sequences: nothing to do, nothing enqueued.
+    assert _chunk(cu=FAKE, N=0, T=0) == _lib.KDA_SUCCESS
+
+
+def test_gate_and_step_validation():
+    lib = _lib.load()
+    ok = dict(z=FAKE, A=None, g_min=-5.0, cu=None, N=0, B=1, T=8, H=2, Dk=8, chunk=0, g=FAKE,
+              stream=None)
+
+    def gate(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.kda_gate(*a.values())
+    assert gate(z=None) == _lib.KDA_ERROR_INVALID_VALUE
+    assert gate(g_min=1.0) == _lib.KDA_ERROR_INVALID_VALUE
+    assert gate(chunk=-1) == _lib.KDA_ERROR_INVALID_VALUE
+    assert gate(chunk=64, g=FAKE) == _lib.KDA_ERROR_INVALID_VALUE   # in-place cumsum
+    assert gate(Dk=6) == _lib.KDA_ERROR_NOT_SUPPORTED
+    assert gate(T=0) == _lib.KDA_SUCCESS
+
+    def step(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, g=FAKE, gate=0, A=None, g_min=-5.0, beta=FAKE,
+                 state=FAKE, N=4, H=2, Dk=64, Dv=64, scale=1.0, o=FAKE, stream=None)
+        a.update(kw)
+        return lib.kda_recurrent_step(*a.values())
+    assert step(state=None) == _lib.KDA_ERROR_INVALID_VALUE
+    assert step(gate=1) == _lib.KDA_ERROR_INVALID_VALUE   # cumsum is meaningless for one token
+    assert step(Dk=300) == _lib.KDA_ERROR_NOT_SUPPORTED
+    assert step(N=0) == _lib.KDA_SUCCESS
+
+
+def test_python_binding_fails_loudly_without_gpu_tensors():
+    torch = pytest.importorskip("torch")
+    from gated_delta_rule_92_amd import chunk_fwd
+    x = torch.zeros(1, 64, 1, 64)
+    with pytest.raises(ValueError):
+        chunk_fwd(x, x, x, x, torch.zeros(1, 64, 1))
