@@ -22,10 +22,16 @@ ARCH = "gfx950"
 SOURCES = ["kda_api.cpp", "kda_gate.hip", "kda_recurrent.hip", "kda_chunk.hip"]
 
 # Packed fp32 VALU instructions are disabled for every device compile.
+# Matrix-core results are kept in ordinary VGPRs (-amdgpu-mfma-vgpr-form): with
+# the default accumulator-register form, reads of a fresh MFMA result through
+# v_accvgpr_read were observed to return stale values for some instruction
+# schedules on gfx950 (wrong accumulator elements 0-1 of a 16x16 tile), while
+# the VGPR form was correct for every shape at the same speed.
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Wno-unused-command-line-argument",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
