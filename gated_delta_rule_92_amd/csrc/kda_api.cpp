@@ -104,7 +104,11 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtyp
   if (workspace && (reinterpret_cast<uintptr_t>(workspace) % kWorkspaceAlign) != 0)
     return KDA_ERROR_INVALID_VALUE;
   const bool bf16 = dtype == KDA_BFLOAT16;
-  const bool fused = kda::chunk_fused_supported(bf16, Dk, Dv, chunk);
+  // The matrix-core path scales diagonal 16-token tiles by up to e^{16|g|};
+  // that stays finite in fp32/bf16 for g >= -5.5. A logits gate with a lower
+  // bound below that takes the token-serial path instead.
+  const bool gate_in_range = !(gate_input == KDA_GATE_LOGITS && g_min < kda::kMinFusedGmin);
+  const bool fused = gate_in_range && kda::chunk_fused_supported(bf16, Dk, Dv, chunk);
   if (!fused) {
     if (Dk > 256) return KDA_ERROR_NOT_SUPPORTED;
     if (gate_input == KDA_GATE_CUMSUM) return KDA_ERROR_NOT_SUPPORTED;

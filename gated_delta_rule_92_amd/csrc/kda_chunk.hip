@@ -48,11 +48,19 @@ namespace kda {
 
 namespace {
 
-constexpr int C = 64;        // chunk length
-constexpr int NTHR = 256;    // 4 wavefronts
+constexpr int C = 64;  // chunk length
+
+// Launch geometry and LDS layout of one instantiation. The workgroup has NW
+// wavefronts; wavefront w owns value columns [w*VCW, (w+1)*VCW) of the state.
+template <int DV>
+constexpr int waves_for() { return DV == 128 ? 8 : 4; }
 
 template <typename T, int DK, int DV>
-struct Lds {
+struct Cfg {
+  static constexpr int NW = waves_for<DV>();
+  static constexpr int NTHR = 64 * NW;
+  static constexpr int VCW = DV / NW;   // value columns per wavefront
+  static constexpr int NTV = VCW / 16;  // 16-column tiles per wavefront
   static constexpr int PADK = sizeof(T) == 2 ? 8 : 0;
   static constexpr int PADC = sizeof(T) == 2 ? 8 : 0;
   static constexpr int KS = DK + PADK;  // row stride of token-major arrays (elements)
@@ -73,37 +81,100 @@ struct Lds {
   static constexpr size_t oVT = oKtT + size_t(DK) * CS * sizeof(T); // v             [DV][CS]
   static constexpr size_t oAqk = oVT + size_t(DV) * CS * sizeof(T); // A_qk          [C][CS]
   static constexpr size_t oAkk = oAqk + size_t(C) * CS * sizeof(T); // -A_kk | T_II  [C][CS]
-  static constexpr size_t oAd = oAkk + size_t(C) * CS * sizeof(T);  // diag A_kk fp32 [4][16][16]
+  static constexpr size_t oAd = oAkk + size_t(C) * CS * sizeof(T);  // diag A_kk^T fp32 [4][16][16]
   static constexpr size_t oTot = oAd + 4 * 256 * 4;                 // fp32 [NRG][DK]
   static constexpr size_t oGb = oTot + size_t(NRG) * DK * 4;        // fp32 [5][DK]
   static constexpr size_t oF = oGb + size_t(5) * DK * 4;            // fp32 [6][DK]
   static constexpr size_t oEgc = oF + size_t(6) * DK * 4;           // fp32 [DK]
   static constexpr size_t oBeta = oEgc + size_t(DK) * 4;            // fp32 [C]
   static constexpr size_t total = oBeta + size_t(C) * 4;
-  static_assert(RPG >= 1 && 16 % RPG == 0, "row groups must tile 16-row tiles");
-  static_assert(RPGV >= 1 && C % RPGV == 0, "value row groups");
+  static_assert(RPG >= 2 && 16 % RPG == 0, "row groups must tile 16-row tiles");
+  static_assert(RPGV >= 2 && C % RPGV == 0, "value row groups");
+  static_assert(NTV >= 1, "a wavefront owns at least one 16-column tile");
+  static_assert(total <= 160 * 1024, "LDS budget");
 };
 
 // e^{x} for x given in log2 units.
 __device__ __forceinline__ float ex2(float x) { return fast_exp2(x); }
 
-template <int RPGN, typename T>
-__device__ __forceinline__ void store_run(T* dst, const float* vals) {
-  // RPGN consecutive elements, RPGN a multiple of 4.
+// RPGN consecutive elements (RPGN = 2, 4 or 8).
+template <int RPGN>
+__device__ __forceinline__ void store_run(__bf16* dst, const float* v) {
+  if constexpr (RPGN == 2) {
+    *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(v[0], v[1]);
+  } else {
 #pragma unroll
-  for (int i = 0; i < RPGN; i += 4) store4(dst + i, f32x4{vals[i], vals[i + 1], vals[i + 2], vals[i + 3]});
+    for (int i = 0; i < RPGN; i += 4) store4(dst + i, f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]});
+  }
+}
+template <int RPGN>
+__device__ __forceinline__ void store_run(float* dst, const float* v) {
+  if constexpr (RPGN == 2) {
+    *reinterpret_cast<float2*>(dst) = float2{v[0], v[1]};
+  } else {
+#pragma unroll
+    for (int i = 0; i < RPGN; i += 4) store4(dst + i, f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]});
+  }
+}
+
+// Raw (still packed) row data of four consecutive channels, loaded through a
+// buffer resource (zeros past the end of the chunk).
+template <typename T>
+struct Raw4;
+template <>
+struct Raw4<__bf16> {
+  i32x2 w;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  }
+  __device__ __forceinline__ f32x4 f32() const {
+    float a, b, c, d;
+    unpack_bf16x2((uint32_t)w.x, a, b);
+    unpack_bf16x2((uint32_t)w.y, c, d);
+    return f32x4{a, b, c, d};
+  }
+};
+template <>
+struct Raw4<float> {
+  i32x4 w;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    w = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  }
+  __device__ __forceinline__ f32x4 f32() const { return __builtin_bit_cast(f32x4, w); }
+};
+
+__device__ __forceinline__ f32x4 load_f32x4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int voff, int soff, float x,
+                                           __bf16*) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, (__bf16)x), r, voff, soff, 0);
+}
+__device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int voff, int soff, float x,
+                                           float*) {
+  __builtin_amdgcn_raw_buffer_store_b32(float_bits(x), r, voff, soff, 0);
+}
+
+// Map a causal tile index p = 0..9 to (I, J<=I) in the order (0,0),(1,0),(1,1),(2,0),...
+__device__ __forceinline__ void tile_of(int p, int& I, int& J) {
+  I = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
+  J = p - I * (I + 1) / 2;
 }
 
 template <typename T, int DK, int DV, int GATE>
-__global__ void __launch_bounds__(NTHR, 1) chunk_fused_kernel(ChunkArgs a) {
-  using L = Lds<T, DK, DV>;
+__global__ void __launch_bounds__(64 * waves_for<DV>(), 1) chunk_fused_kernel(ChunkArgs a) {
+  using L = Cfg<T, DK, DV>;
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int KS = L::KS, CS = L::CS;
-  constexpr int NCT = DK / 16;         // 16-row tiles of the state (key channels)
-  constexpr int NTV = DV / 64;         // 16-column tiles per wavefront
+  constexpr int NCT = DK / 16;  // 16-row tiles of the state (key channels)
+  constexpr int NTV = L::NTV;
   constexpr int RPG = L::RPG, NCQ = L::NCQ;
   constexpr int RPGV = L::RPGV, NCQV = L::NCQV;
+  constexpr int NW = L::NW;
 
   __shared__ __attribute__((aligned(16))) char smem[L::total];
   T* sKl = reinterpret_cast<T*>(smem + L::oKl);
@@ -122,11 +193,12 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fused_kernel(ChunkArgs a) {
   float* sEgc = reinterpret_cast<float*>(smem + L::oEgc);
   float* sBeta = reinterpret_cast<float*>(smem + L::oBeta);
 
-  const T* __restrict__ q = reinterpret_cast<const T*>(a.q);
-  const T* __restrict__ k = reinterpret_cast<const T*>(a.k);
-  const T* __restrict__ v = reinterpret_cast<const T*>(a.v);
-  T* __restrict__ o = reinterpret_cast<T*>(a.o);
+  const T* q = reinterpret_cast<const T*>(a.q);
+  const T* k = reinterpret_cast<const T*>(a.k);
+  const T* v = reinterpret_cast<const T*>(a.v);
+  T* o = reinterpret_cast<T*>(a.o);
   const float* __restrict__ gin = a.g;
+  const float* __restrict__ betain = a.beta;
   const int H = a.H;
 
   const int tid = threadIdx.x;
@@ -146,21 +218,28 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fused_kernel(ChunkArgs a) {
     bos = (long)n * a.seqs.T;
     len = a.seqs.T;
   }
-  const int vc0 = wave * (DV / 4);  // first value column owned by this wavefront
+  const int vc0 = wave * L::VCW;  // first value column owned by this wavefront
 
   // ---- state: S[c][vcol] for c-tile ct, column tile b (accumulator layout) ----
   f32x4 S[NCT][NTV];
   const size_t sbase = ((size_t)n * H + h) * DK * DV;
+  const int svoff = ((4 * g4) * DV + vc0 + m) * 4;  // + (16 ct + e) DV*4 + 16 b*4
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int b = 0; b < NTV; ++b)
+    for (int b = 0; b < NTV; ++b) S[ct][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (a.h0) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.h0 + sbase, DK * DV * 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        S[ct][b][e] = a.h0 ? a.h0[sbase + (size_t)(16 * ct + 4 * g4 + e) * DV + vc0 + 16 * b + m]
-                           : 0.f;
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int b = 0; b < NTV; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          S[ct][b][e] = load_f32(rs, svoff, ((16 * ct + e) * DV + 16 * b) * 4);
+  }
 
-  const float es = (GATE == kGateLogits && a.A_log) ? __expf(a.A_log[h]) : 1.0f;
+  const float es2 = ((GATE == kGateLogits && a.A_log) ? __expf(a.A_log[h]) : 1.0f) * kLog2e;
   const float gmin2 = a.g_min * kLog2e;
 
   const int cq = tid % NCQ, rg = tid / NCQ;
@@ -168,50 +247,70 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fused_kernel(ChunkArgs a) {
   const int tileI = (rg * RPG) / 16;
   const int cqv = tid % NCQV, rgv = tid / NCQV;
 
+  // ---- register prefetch of one chunk's inputs through buffer resources ----
+  // Row r of the chunk starting at token t0 sits at byte (r*H*D + c)*size
+  // from ((t0*H + h)*D); rows at or past the chunk's end read as zeros.
+  const int rowk = H * DK * (int)sizeof(T), rowv = H * DV * (int)sizeof(T);
+  const int rowg = H * DK * 4, rowb = H * 4;
+  const int voff_k = rg * RPG * rowk + c0 * (int)sizeof(T);
+  const int voff_g = rg * RPG * rowg + c0 * 4;
+  const int voff_b = rg * RPG * rowb;
+  const int voff_v = rgv * RPGV * rowv + 4 * cqv * (int)sizeof(T);
+  Raw4<T> pk[RPG], pq[RPG], pv[RPGV];
+  f32x4 pg[RPG];
+  float pb[RPG];
+  auto prefetch = [&](long t0, int Lr) {
+    const size_t rk = ((size_t)t0 * H + h) * DK, rv = ((size_t)t0 * H + h) * DV;
+    const uint32_t nk = (uint32_t)((Lr - 1) * H + 1) * DK, nv = (uint32_t)((Lr - 1) * H + 1) * DV;
+    const __amdgpu_buffer_rsrc_t rsk = make_rsrc(k + rk, nk * sizeof(T));
+    const __amdgpu_buffer_rsrc_t rsq = make_rsrc(q + rk, nk * sizeof(T));
+    const __amdgpu_buffer_rsrc_t rsg = make_rsrc(gin + rk, nk * 4);
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(betain + (size_t)t0 * H + h, ((Lr - 1) * H + 1) * 4);
+    const __amdgpu_buffer_rsrc_t rsv = make_rsrc(v + rv, nv * sizeof(T));
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      pk[i].load(rsk, voff_k, i * rowk);
+      pq[i].load(rsq, voff_k, i * rowk);
+      pg[i] = load_f32x4(rsg, voff_g, i * rowg);
+      pb[i] = load_f32(rsb, voff_b, i * rowb);
+    }
+#pragma unroll
+    for (int i = 0; i < RPGV; ++i) pv[i].load(rsv, voff_v, i * rowv);
+  };
+
   const long nchunks = (len + C - 1) / C;
+  if (nchunks > 0) prefetch(bos, (int)(len < C ? len : C));
+
   for (long ci = 0; ci < nchunks; ++ci) {
     const long tok0 = bos + ci * C;
     const int Lr = (int)(len - ci * C < C ? len - ci * C : C);
 
     // =============================== P1 ===============================
-    f32x4 kr[RPG], qr[RPG], gl[RPG];
+    // Rows past the chunk's end were read as zeros (k = q = v = beta = 0);
+    // their log-decay must be 0 too, which the logits gate needs a mask for.
+    f32x4 kr[RPG], qr[RPG], gl[RPG], vr[RPGV];
+    float br[RPG];
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
-      const int r = rg * RPG + i;
-      if (r < Lr) {
-        const size_t off = ((size_t)(tok0 + r) * H + h) * DK + c0;
-        kr[i] = load4_f32(k + off);
-        qr[i] = load4_f32(q + off);
-        f32x4 gg = *reinterpret_cast<const f32x4*>(gin + off);
-        if constexpr (GATE == kGateLogits) {
+      kr[i] = pk[i].f32();
+      qr[i] = pq[i].f32();
+      br[i] = pb[i];
+      f32x4 gg = pg[i];
+      if constexpr (GATE == kGateLogits) {
+        const bool valid = rg * RPG + i < Lr;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            gg[e] = gmin2 * __builtin_amdgcn_rcpf(1.0f + ex2(-es * kLog2e * gg[e]));
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) gg[e] *= kLog2e;
-        }
-        gl[i] = gg;
+        for (int e = 0; e < 4; ++e)
+          gg[e] = valid ? gmin2 * __builtin_amdgcn_rcpf(1.0f + ex2(-es2 * gg[e])) : 0.f;
       } else {
-        kr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        qr[i] = kr[i];
-        gl[i] = kr[i];
+        gg *= kLog2e;
       }
+      gl[i] = gg;
     }
-    // value rows for the transposed copy V^T
-    f32x4 vr[RPGV];
 #pragma unroll
-    for (int i = 0; i < RPGV; ++i) {
-      const int r = rgv * RPGV + i;
-      vr[i] = r < Lr ? load4_f32(v + ((size_t)(tok0 + r) * H + h) * DV + 4 * cqv)
-                     : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int i = 0; i < RPGV; ++i) vr[i] = pv[i].f32();
     if (cq == 0) {
 #pragma unroll
-      for (int i = 0; i < RPG; ++i) {
-        const int r = rg * RPG + i;
-        sBeta[r] = r < Lr ? a.beta[(size_t)(tok0 + r) * H + h] : 0.f;
-      }
+      for (int i = 0; i < RPG; ++i) sBeta[rg * RPG + i] = br[i];
     }
 
     // cumulative log2-decay G2 of every row; rho[I] = G2 just before tile I,
@@ -286,7 +385,6 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fused_kernel(ChunkArgs a) {
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) store_run<RPG>(sKtT + (c0 + e) * CS + rg * RPG, kt[e]);
-      // V^T
       float vt[4][RPGV];
 #pragma unroll
       for (int i = 0; i < RPGV; ++i)
@@ -313,75 +411,91 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fused_kernel(ChunkArgs a) {
         *reinterpret_cast<f32x4*>(sEgc + c0) = eg;
       }
     }
-    __syncthreads();
-
-    // =============================== I2 ===============================
-    // Causal tile pairs (I, J<=I) in the order (0,0),(1,0),(1,1),(2,0),...;
-    // wavefront w takes pairs w, w+4, w+8. Products are formed transposed,
-    // D[i][r] = sum_c Kr[i][c] X[r][c], so the accumulator rows run along i
-    // and each lane stores four consecutive i of one row r.
-    for (int pidx = wave; pidx < 10; pidx += 4) {
-      const int I = pidx < 1 ? 0 : pidx < 3 ? 1 : pidx < 6 ? 2 : 3;
-      const int J = pidx - I * (I + 1) / 2;
-      const float* fIJ = sF + (I * (I - 1) / 2 + J) * DK;
-      f32x4 accK = {0.f, 0.f, 0.f, 0.f}, accQ = accK;
-#pragma unroll
-      for (int ks = 0; ks < DK / 32; ++ks) {
-        const int ca = 32 * ks + 4 * g4, cb = ca + 16;
-        frag a0 = load_frag(sKd + (16 * J + m) * KS + ca);
-        frag a1 = load_frag(sKd + (16 * J + m) * KS + cb);
-        if (I != J) {
-          a0 = M::make(M::to_f32(a0) * *reinterpret_cast<const f32x4*>(fIJ + ca));
-          a1 = M::make(M::to_f32(a1) * *reinterpret_cast<const f32x4*>(fIJ + cb));
-        }
-        const frag bk0 = load_frag(sKl + (16 * I + m) * KS + ca);
-        const frag bk1 = load_frag(sKl + (16 * I + m) * KS + cb);
-        accK = M::k32(a0, a1, bk0, bk1, accK);
-        const frag bq0 = load_frag(sQl + (16 * I + m) * KS + ca);
-        const frag bq1 = load_frag(sQl + (16 * I + m) * KS + cb);
-        accQ = M::k32(a0, a1, bq0, bq1, accQ);
-      }
-      const int r = 16 * I + m;
-      const float br = sBeta[r];
-      f32x4 vk, vq;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 16 * J + 4 * g4 + e;
-        vk[e] = br * accK[e];
-        vq[e] = accQ[e];
-        if (I == J) {
-          if (i >= r) vk[e] = 0.f;
-          if (i > r) vq[e] = 0.f;
-        }
-      }
-      if (I == J)
-        *reinterpret_cast<f32x4*>(sAd + I * 256 + m * 16 + 4 * g4) = vk;
-      else
-        store4(sAkk + r * CS + 16 * J + 4 * g4, -vk);
-      store4(sAqk + r * CS + 16 * J + 4 * g4, vq);
+    // The next chunk's loads fly while this chunk's products are computed.
+    if (ci + 1 < nchunks) {
+      const long rem = len - (ci + 1) * C;
+      prefetch(tok0 + C, (int)(rem < C ? rem : C));
     }
     __syncthreads();
 
-    // =============================== I3 ===============================
-    // (I + A_II)^{-1} for the four diagonal blocks: lane = (block, column j),
-    // forward substitution down the rows, fp32.
+    // ============================== I2 / I3 ==============================
+    // Causal tiles (I, J<=I) are formed transposed, D[i][r] = sum_c Kr[i][c]
+    // X[r][c], so each lane ends with four consecutive i of one row r. The
+    // right operand Kr is k e^{rho_I - G_i}: the diagonal array sKd scaled by
+    // e^{rho_I - rho_J} for J < I.
+    auto right_operand = [&](int I, int J, int ca, frag& a0, frag& a1) {
+      a0 = load_frag(sKd + (16 * J + m) * KS + ca);
+      a1 = load_frag(sKd + (16 * J + m) * KS + ca + 16);
+      if (I != J) {
+        const float* fIJ = sF + (I * (I - 1) / 2 + J) * DK;
+        a0 = M::make(M::to_f32(a0) * *reinterpret_cast<const f32x4*>(fIJ + ca));
+        a1 = M::make(M::to_f32(a1) * *reinterpret_cast<const f32x4*>(fIJ + ca + 16));
+      }
+    };
+    // A_kk tiles: diagonal blocks (beta-scaled, strictly lower) go to sAd as
+    // columns (A^T) in fp32 for the inversion, off-diagonal blocks to sAkk as
+    // -A_IJ in the operand type.
+    for (int p = wave; p < 10; p += NW) {
+      int I, J;
+      tile_of(p, I, J);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) {
+        const int ca = 32 * ks + 4 * g4;
+        frag a0, a1;
+        right_operand(I, J, ca, a0, a1);
+        acc = M::k32(a0, a1, load_frag(sKl + (16 * I + m) * KS + ca),
+                     load_frag(sKl + (16 * I + m) * KS + ca + 16), acc);
+      }
+      const float br_ = sBeta[16 * I + m];
+      if (I == J) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int il = 4 * g4 + e;
+          sAd[I * 256 + il * 16 + m] = il < m ? br_ * acc[e] : 0.f;
+        }
+      } else {
+        store4(sAkk + (16 * I + m) * CS + 16 * J + 4 * g4, -br_ * acc);
+      }
+    }
+    __syncthreads();
     if (wave == 0) {
+      // (I + A_bb)^{-1}, column j per lane, right-looking: once t_r is final
+      // it is eliminated from every later row.
       const int blk = lane >> 4, j = lane & 15;
-      const float* Ab = sAd + blk * 256;
+      const float* At = sAd + blk * 256;  // At[i*16 + r] = A[r][i]
       float t[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s0 = (r == j) ? 1.f : 0.f, s1 = 0.f;
+      for (int r = 0; r < 16; ++r) t[r] = (r == j) ? 1.f : 0.f;
 #pragma unroll
-        for (int i = 0; i + 1 < r; i += 2) {
-          s0 -= Ab[r * 16 + i] * t[i];
-          s1 -= Ab[r * 16 + i + 1] * t[i + 1];
-        }
-        if (r & 1) s0 -= Ab[r * 16 + r - 1] * t[r - 1];
-        t[r] = s0 + s1;
+      for (int r = 0; r < 15; ++r) {
+        const float tr = t[r];
+#pragma unroll
+        for (int i = r + 1; i < 16; ++i) t[i] -= At[r * 16 + i] * tr;
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sAkk[(16 * blk + r) * CS + 16 * blk + j] = from_f32<T>(t[r]);
+    } else {
+      // A_qk tiles on the other wavefronts, lower triangle incl. diagonal.
+      for (int p = wave - 1; p < 10; p += NW - 1) {
+        int I, J;
+        tile_of(p, I, J);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks) {
+          const int ca = 32 * ks + 4 * g4;
+          frag a0, a1;
+          right_operand(I, J, ca, a0, a1);
+          acc = M::k32(a0, a1, load_frag(sQl + (16 * I + m) * KS + ca),
+                       load_frag(sQl + (16 * I + m) * KS + ca + 16), acc);
+        }
+        if (I == J) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * g4 + e > m) acc[e] = 0.f;
+        }
+        store4(sAqk + (16 * I + m) * CS + 16 * J + 4 * g4, acc);
+      }
     }
     __syncthreads();
 
@@ -429,7 +543,11 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fused_kernel(ChunkArgs a) {
       }
     }
 
-    // O = (Gamma*Q) S + A_qk V~
+    // O = (Gamma*Q) S + A_qk V~; rows past the chunk's end are dropped by the
+    // buffer range check.
+    const __amdgpu_buffer_rsrc_t rso =
+        make_rsrc(o + ((size_t)tok0 * H + h) * DV, (uint32_t)((Lr - 1) * H + 1) * DV * sizeof(T));
+    const int ovoff = (4 * g4) * rowv + (vc0 + m) * (int)sizeof(T);
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       f32x4 acc[NTV];
@@ -451,11 +569,9 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fused_kernel(ChunkArgs a) {
 #pragma unroll
       for (int b = 0; b < NTV; ++b)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * I + 4 * g4 + e;
-          if (r < Lr)
-            o[((size_t)(tok0 + r) * H + h) * DV + vc0 + 16 * b + m] = from_f32<T>(a.scale * acc[b][e]);
-        }
+        for (int e = 0; e < 4; ++e)
+          store_elem(rso, ovoff, ((16 * I + e) * rowv) + 16 * b * (int)sizeof(T),
+                     a.scale * acc[b][e], (T*)nullptr);
     }
 
     // S <- Diag(Gamma_C) S + (K e^{G_C-G})^T V~
@@ -477,31 +593,31 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_fused_kernel(ChunkArgs a) {
   }
 
   if (a.hT) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.hT + sbase, DK * DV * 4);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int b = 0; b < NTV; ++b)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          a.hT[sbase + (size_t)(16 * ct + 4 * g4 + e) * DV + vc0 + 16 * b + m] = S[ct][b][e];
+          __builtin_amdgcn_raw_buffer_store_b32(float_bits(S[ct][b][e]), rs, svoff,
+                                                ((16 * ct + e) * DV + 16 * b) * 4, 0);
   }
 }
 
 template <typename T, int DK, int DV>
 hipError_t launch_dk_dv(const ChunkArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)(a.seqs.N * a.H));
+  dim3 block(Cfg<T, DK, DV>::NTHR);
   switch (a.gate_mode) {
     case kGateLogDecay:
-      hipLaunchKernelGGL((chunk_fused_kernel<T, DK, DV, kGateLogDecay>), grid, dim3(NTHR), 0,
-                         stream, a);
+      hipLaunchKernelGGL((chunk_fused_kernel<T, DK, DV, kGateLogDecay>), grid, block, 0, stream, a);
       break;
     case kGateCumsum:
-      hipLaunchKernelGGL((chunk_fused_kernel<T, DK, DV, kGateCumsum>), grid, dim3(NTHR), 0,
-                         stream, a);
+      hipLaunchKernelGGL((chunk_fused_kernel<T, DK, DV, kGateCumsum>), grid, block, 0, stream, a);
       break;
     default:
-      hipLaunchKernelGGL((chunk_fused_kernel<T, DK, DV, kGateLogits>), grid, dim3(NTHR), 0,
-                         stream, a);
+      hipLaunchKernelGGL((chunk_fused_kernel<T, DK, DV, kGateLogits>), grid, block, 0, stream, a);
       break;
   }
   return hipGetLastError();

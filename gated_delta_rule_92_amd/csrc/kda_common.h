@@ -23,6 +23,22 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Bit pattern of a float passed by value. (Taking __builtin_bit_cast of a
+// vector element expression directly was observed to read element 0 for
+// every index; a by-value scalar is always correct.)
+__device__ __forceinline__ int float_bits(float x) { return __builtin_bit_cast(int, x); }
+
+// Buffer resource over [base, base + bytes): raw buffer loads past the end
+// return zeros and stores past the end are dropped, which gives ragged tails
+// for free. Offsets are 32-bit, so a resource covers one chunk or one state.
+constexpr int kBufferFlags = 0x00020000;  // data format 32 (raw access), gfx9 family
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferFlags);
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 

@@ -64,6 +64,8 @@ struct ChunkArgs {
   bool bf16;
 };
 bool chunk_fused_supported(bool bf16, int Dk, int Dv, int chunk);
+// Lowest per-token log-decay the chunk path handles (16 * 5.5 = 88 < 88.7 = ln FLT_MAX).
+constexpr float kMinFusedGmin = -5.5f;
 hipError_t launch_chunk_fused(const ChunkArgs& a, hipStream_t stream);
 
 // Longest-first ordering of packed sequences (N <= kMaxOrderN), into order[N].

@@ -137,7 +137,10 @@ kda_status_t kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, i
  *            when that size is 0
  * Supported: bf16 with Dk, Dv in {64, 128}; fp32 with Dk = Dv = 64 on the
  * matrix-core chunk path; any other Dk, Dv <= 256 (and fp32 at 128) runs a
- * token-serial kernel with the same results. Zero-length sequences are
+ * token-serial kernel with the same results, as does KDA_GATE_LOGITS with
+ * g_min < -5.5. The chunk path requires every per-token log-decay to be
+ * >= -5.5 (the pages fix g_min = -5): inside a 16-token tile it scales by
+ * up to e^{16|g|}, which must stay finite in fp32. Zero-length sequences are
  * allowed (final state = initial state).
  */
 kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype_t dtype,

@@ -219,6 +219,19 @@ def test_token_serial_path_shapes(dtype, Dk, Dv, chunk):
     _check(o, hT, _oracle(d), dtype, "token-serial")
 
 
+def test_low_gate_bound_takes_token_serial_path():
+    """g_min = -8 (outside the chunk path's -5.5 bound) must still be exact."""
+    _print_case("g_min = -8, logits gate")
+    d = make_inputs(1, 130, 2, 128, 128, torch.bfloat16, h0_std=0.02, seed=21)
+    d["z"] = d["z"] + 3.0        # push most gates toward g_min
+    dd = to_dev(d)
+    o, hT = chunk_fwd(dd["q"], dd["k"], dd["v"], dd["z"], dd["beta"], dd["h0"], None,
+                      gate="logits", g_min=-8.0)
+    torch.cuda.synchronize()
+    ref = oracle_forward(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"], None, None, -8.0)
+    _check(o, hT, ref, torch.bfloat16, "g_min=-8")
+
+
 def test_deterministic():
     _print_case("bitwise determinism")
     d = make_inputs(2, 300, 2, 128, 128, torch.bfloat16, h0_std=0.02, seed=20)
