@@ -19,14 +19,11 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libkda.so")
 ARCH = "gfx950"
 
-SOURCES = ["kda_api.cpp", "kda_gate.hip", "kda_recurrent.hip", "kda_chunk.hip"]
+SOURCES = ["kda_api.cpp", "kda_gate.hip", "kda_recurrent.hip", "kda_chunk.hip", "kda_chunk_pipe.hip"]
 
 # Packed fp32 VALU instructions are disabled for every device compile.
-# Matrix-core results are kept in ordinary VGPRs (-amdgpu-mfma-vgpr-form): with
-# the default accumulator-register form, reads of a fresh MFMA result through
-# v_accvgpr_read were observed to return stale values for some instruction
-# schedules on gfx950 (wrong accumulator elements 0-1 of a 16x16 tile), while
-# the VGPR form was correct for every shape at the same speed.
+# Matrix-core results are kept in ordinary VGPRs (-amdgpu-mfma-vgpr-form), which
+# avoids accumulator-register copies.
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Wno-unused-command-line-argument",

@@ -133,6 +133,8 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtyp
       if (e != hipSuccess) return KDA_ERROR_LAUNCH_FAILURE;
       a.order = order;
     }
+    if (kda::chunk_pipe_supported(bf16, Dk, Dv, chunk))
+      return launch_status(kda::launch_chunk_pipe(a, hs));
     return launch_status(kda::launch_chunk_fused(a, hs));
   }
   kda::RecurrentArgs r;

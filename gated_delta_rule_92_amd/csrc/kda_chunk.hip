@@ -543,7 +543,7 @@ __global__ void __launch_bounds__(64 * waves_for<DV>(), 1) chunk_fused_kernel(Ch
       }
     }
 
-    // O = (Gamma*Q) S + A_qk V~; rows past the chunk's end are dropped by the
+    // O = A_qk V~ + (Gamma*Q) S; rows past the chunk's end are dropped by the
     // buffer range check.
     const __amdgpu_buffer_rsrc_t rso =
         make_rsrc(o + ((size_t)tok0 * H + h) * DV, (uint32_t)((Lr - 1) * H + 1) * DV * sizeof(T));
@@ -554,17 +554,17 @@ __global__ void __launch_bounds__(64 * waves_for<DV>(), 1) chunk_fused_kernel(Ch
 #pragma unroll
       for (int b = 0; b < NTV; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
+      for (int J = 0; J <= I; ++J) {
+        const frag aa = load_frag(sAqk + (16 * I + m) * CS + 16 * J + 4 * g4);
+#pragma unroll
+        for (int b = 0; b < NTV; ++b) acc[b] = M::k16(aa, Xf[J][b], acc[b]);
+      }
+#pragma unroll
       for (int ks = 0; ks < DK / 32; ++ks) {
         const frag a0 = load_frag(sQg + (16 * I + m) * KS + 32 * ks + 4 * g4);
         const frag a1 = load_frag(sQg + (16 * I + m) * KS + 32 * ks + 16 + 4 * g4);
 #pragma unroll
         for (int b = 0; b < NTV; ++b) acc[b] = M::k32(a0, a1, Sf[2 * ks][b], Sf[2 * ks + 1][b], acc[b]);
-      }
-#pragma unroll
-      for (int J = 0; J <= I; ++J) {
-        const frag aa = load_frag(sAqk + (16 * I + m) * CS + 16 * J + 4 * g4);
-#pragma unroll
-        for (int b = 0; b < NTV; ++b) acc[b] = M::k16(aa, Xf[J][b], acc[b]);
       }
 #pragma unroll
       for (int b = 0; b < NTV; ++b)

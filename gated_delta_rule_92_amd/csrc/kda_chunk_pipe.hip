@@ -1,0 +1,454 @@
+// Pipelined chunkwise KDA forward for bf16, d_k = d_v = 128 (the training
+// shape), on CDNA4 matrix cores.
+//
+// Sources, cited by page title and section:
+//   [KDA-blog] "Kimi k3 技术报告详解（1）——架构再升华", section "Kimi Delta
+//              Attention" (KDA equation) and section "Chunkwise parallel
+//              form" (gamma, W/U, pseudo-value and A/O equations; the
+//              paragraph on 16-token tiles whose reciprocal decay factors the
+//              bounded gate keeps finite).
+//   [Baidu-1]  "Kimi K3 Core Techniques Explained ...", §1.2 (g_min = -5).
+//
+// The API's 64-token chunks are processed as four 16-token tiles, and the
+// state is advanced after every tile. For a tile starting at state S with G
+// the cumulative log2-decay inside the tile (G restarts at the tile start):
+//   A_kk[r,i] = beta_r sum_c k_r e^{G_r} k_i e^{-G_i}  (i < r)
+//   A_qk[r,i] = sum_c q_r e^{G_r} k_i e^{-G_i}          (i <= r)
+//   V~ = (I + A_kk)^{-1} Diag(beta) (V - (e^{G} * K) S)
+//   O  = (e^{G} * Q) S + A_qk V~
+//   S <- Diag(e^{G_15}) S + (K * e^{G_15 - G})^T V~
+// which is the pages' chunk form with C = 16 (M = (I + A_kk)^{-1} Diag(beta),
+// W = M(Gamma*K), U = M V, V~ = U - W S). Within a tile the reciprocal
+// factors e^{-G_i} are at most e^{16|g_min|} = e^{80}, finite in fp32 and
+// bf16: every tile, the diagonal included, is a dense matrix-core product.
+// Evaluated per 64-token chunk, this equals the chunk-form result with the
+// off-diagonal tile interactions carried through the on-chip state.
+//
+// Workgroup = 8 wavefronts on one (sequence, head), two per SIMD:
+//   producers (wavefronts 0-3): wavefront p builds the operands of tiles
+//     p, p+4, p+8, ... on its own (lane = 2 channels x 16 rows, so the
+//     cumulative sum needs no other wavefront): gate, cumsum, exponentials,
+//     the bf16 operand arrays, A_kk and A_qk (matrix cores), the 16x16
+//     inverse (fp32, right-looking), then publishes the slot;
+//   consumers (wavefronts 4-7): wavefront 4+c owns value columns
+//     [32c, 32c+32) of the state (the recurrence is separable over value
+//     columns), holds them in registers and applies each tile in order.
+// Producers and consumers meet through a ring of LDS slots with ready/done
+// counters, so a producer's VALU-heavy work on one SIMD overlaps a
+// consumer's matrix-core work on the same SIMD. Every wait is bounded.
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int PT = 16;        // tile rows
+constexpr int PDK = 128, PDV = 128;
+constexpr int NSLOT = 6;      // ring slots
+constexpr int NPROD = 4, NCONS = 4;
+constexpr int PNTHR = 64 * (NPROD + NCONS);
+constexpr int CCOLS = PDV / NCONS;  // value columns per consumer
+constexpr int CNTV = CCOLS / 16;    // 16-column tiles per consumer
+// Legitimate waits last a few thousand cycles; a wait that reaches this many
+// polls (about a millisecond) marks the workgroup aborted, and every later
+// wait returns at once, so the kernel always finishes.
+constexpr int kSpinLimit = 1 << 15;
+
+// Slot layout (bytes). bf16 unless noted.
+constexpr int sKg = 0;                      // k e^{G}      [16][128]
+constexpr int sQg = sKg + PT * PDK * 2;     // q e^{G}      [16][128]
+constexpr int sKtT = sQg + PT * PDK * 2;    // k e^{G15-G}  [128][16] (channel-major)
+constexpr int sVT = sKtT + PDK * PT * 2;    // v            [128][16] (channel-major)
+constexpr int sT = sVT + PDV * PT * 2;      // (I+A_kk)^-1  [16][16]
+constexpr int sAqk = sT + PT * PT * 2;      // A_qk         [16][16]
+constexpr int sBeta = sAqk + PT * PT * 2;   // fp32 [16]
+constexpr int sEgc = sBeta + PT * 4;        // fp32 [128]  e^{G_15}
+constexpr int kSlotBytes = ((sEgc + PDK * 4) + 255) / 256 * 256;
+// Producer-private scratch.
+constexpr int pKd = 0;                      // k e^{-G}     [16][128] bf16
+constexpr int pAc = pKd + PT * PDK * 2;     // A_kk by columns, fp32 [16][16]
+constexpr int kPrivBytes = pAc + PT * PT * 4;
+constexpr int kLdsBytes = NSLOT * kSlotBytes + NPROD * kPrivBytes + (2 * NSLOT + 1) * 4;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+
+__device__ __forceinline__ float ex2(float x) { return fast_exp2(x); }
+
+__device__ __forceinline__ int lds_load_relaxed(int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Wait until *p >= target, bounded by kSpinLimit polls and by the
+// workgroup's abort flag.
+__device__ __forceinline__ void wait_at_least(int* p, int target, int* abort_flag) {
+  int spins = 0;
+  while (lds_load_relaxed(p) < target) {
+    if (lds_load_relaxed(abort_flag) != 0) break;
+    if (++spins >= kSpinLimit) {
+      __hip_atomic_store(abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ void signal_set(int* p, int value) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __hip_atomic_store(p, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Adds one per wavefront: a single lane performs the add (an add issued by
+// every lane would count 64 times).
+__device__ __forceinline__ void signal_add(int* p, int lane) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  if (lane == 0) __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ uint32_t perm_lo16(uint32_t a, uint32_t b) {
+  // (a.lo16, b.lo16) -> one dword with a.lo in the low half
+  return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t perm_hi16(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xffff0000u);
+}
+
+template <int GATE>
+__global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
+  using M = Mma<__bf16>;
+  using frag = M::frag;
+  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  int* ready = reinterpret_cast<int*>(smem + NSLOT * kSlotBytes + NPROD * kPrivBytes);
+  int* done = ready + NSLOT;
+  int* abort_flag = done + NSLOT;
+
+  const __bf16* q = reinterpret_cast<const __bf16*>(a.q);
+  const __bf16* k = reinterpret_cast<const __bf16*>(a.k);
+  const __bf16* v = reinterpret_cast<const __bf16*>(a.v);
+  __bf16* o = reinterpret_cast<__bf16*>(a.o);
+  const int H = a.H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m = lane & 15, g4 = lane >> 4;
+
+  const int n = a.order ? a.order[blockIdx.x / H] : (int)(blockIdx.x / H);
+  const int h = blockIdx.x % H;
+  long bos, len;
+  if (a.seqs.cu) {
+    bos = a.seqs.cu[n];
+    len = (long)a.seqs.cu[n + 1] - bos;
+  } else {
+    bos = (long)n * a.seqs.T;
+    len = a.seqs.T;
+  }
+  const int nsteps = (int)((len + PT - 1) / PT);
+  const int rowk = H * PDK * 2, rowg = H * PDK * 4, rowb = H * 4;
+
+  if (tid < 2 * NSLOT + 1) ready[tid] = 0;  // ready[], done[], abort_flag are contiguous
+  __syncthreads();
+
+  if (wave < NPROD) {
+    // =========================== producer ===========================
+    const int p = wave;
+    char* priv = smem + NSLOT * kSlotBytes + p * kPrivBytes;
+    __bf16* Kd = reinterpret_cast<__bf16*>(priv + pKd);
+    float* Ac = reinterpret_cast<float*>(priv + pAc);
+    const float es2 = ((GATE == kGateLogits && a.A_log) ? __expf(a.A_log[h]) : 1.0f) * kLog2e;
+    const float gmin2 = a.g_min * kLog2e;
+    const int c2 = 2 * lane;  // this lane's two channels
+
+    // raw tile data: row r of channels (c2, c2+1)
+    uint32_t rk[PT], rq[PT], rv[PT];
+    float2 rz[PT];
+    float rb;  // beta of row `lane` (lanes 0..15)
+    auto load_tile = [&](int step) {
+      const long t0 = bos + (long)step * PT;
+      const int L = (int)min((long)PT, len - (long)step * PT);
+      const size_t base = ((size_t)t0 * H + h);
+      const __amdgpu_buffer_rsrc_t rsk = make_rsrc(k + base * PDK, (uint32_t)((L - 1) * H + 1) * PDK * 2);
+      const __amdgpu_buffer_rsrc_t rsq = make_rsrc(q + base * PDK, (uint32_t)((L - 1) * H + 1) * PDK * 2);
+      const __amdgpu_buffer_rsrc_t rsv = make_rsrc(v + base * PDV, (uint32_t)((L - 1) * H + 1) * PDV * 2);
+      const __amdgpu_buffer_rsrc_t rsg = make_rsrc(a.g + base * PDK, (uint32_t)((L - 1) * H + 1) * PDK * 4);
+      const __amdgpu_buffer_rsrc_t rsb = make_rsrc(a.beta + base, (uint32_t)((L - 1) * H + 1) * 4);
+#pragma unroll
+      for (int r = 0; r < PT; ++r) {
+        rk[r] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsk, c2 * 2, r * rowk, 0);
+        rq[r] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsq, c2 * 2, r * rowk, 0);
+        rv[r] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsv, c2 * 2, r * rowk, 0);
+        i32x2 zz = __builtin_amdgcn_raw_buffer_load_b64(rsg, c2 * 4, r * rowg, 0);
+        const int z0 = zz.x, z1 = zz.y;
+        rz[r] = float2{bits_float(z0), bits_float(z1)};
+      }
+      rb = bits_float(__builtin_amdgcn_raw_buffer_load_b32(rsb, lane * rowb, 0, 0));
+    };
+
+    if (p < nsteps) load_tile(p);
+    for (int step = p; step < nsteps; step += NPROD) {
+      const int slot = step % NSLOT;
+      const int use = step / NSLOT;
+      char* sl = smem + slot * kSlotBytes;
+      const long t0 = bos + (long)step * PT;
+      const int L = (int)min((long)PT, len - (long)step * PT);
+      // the slot's previous tile must have been consumed by every consumer
+      if (use > 0) wait_at_least(&done[slot], NCONS * use, abort_flag);
+
+      // cumulative log2-decay of this tile, channels (c2, c2+1)
+      float G0 = 0.f, G1 = 0.f;
+      float base0 = 0.f, base1 = 0.f;
+      if constexpr (GATE == kGateCumsum) {
+        // g holds the cumulative sum within 64-token chunks; rebase it at the
+        // tile start (the value just before the tile, when the tile is not
+        // the first of its chunk).
+        const long tin = (long)step * PT;
+        if (tin % 64 != 0) {
+          const float2 pv = *reinterpret_cast<const float2*>(
+              a.g + ((size_t)(t0 - 1) * H + h) * PDK + c2);
+          base0 = pv.x * kLog2e;
+          base1 = pv.y * kLog2e;
+        }
+      }
+      float kd0[PT], kd1[PT];
+#pragma unroll
+      for (int r = 0; r < PT; ++r) {
+        float g0 = rz[r].x, g1 = rz[r].y;
+        if constexpr (GATE == kGateLogits) {
+          const float gm = r < L ? gmin2 : 0.f;
+          g0 = gm * __builtin_amdgcn_rcpf(1.0f + ex2(-es2 * g0));
+          g1 = gm * __builtin_amdgcn_rcpf(1.0f + ex2(-es2 * g1));
+          G0 += g0;
+          G1 += g1;
+        } else if constexpr (GATE == kGateLogDecay) {
+          G0 += g0 * kLog2e;  // rows past the end read as 0
+          G1 += g1 * kLog2e;
+        } else {
+          if (r < L) {
+            G0 = g0 * kLog2e - base0;
+            G1 = g1 * kLog2e - base1;
+          }
+        }
+        const float E0 = ex2(G0), E1 = ex2(G1);
+        const float Ei0 = ex2(-G0), Ei1 = ex2(-G1);
+        float k0, k1, q0, q1;
+        unpack_bf16x2(rk[r], k0, k1);
+        unpack_bf16x2(rq[r], q0, q1);
+        const int off = r * PDK + c2;
+        *reinterpret_cast<uint32_t*>(sl + sKg + off * 2) = pack_bf16x2(k0 * E0, k1 * E1);
+        *reinterpret_cast<uint32_t*>(sl + sQg + off * 2) = pack_bf16x2(q0 * E0, q1 * E1);
+        kd0[r] = k0 * Ei0;
+        kd1[r] = k1 * Ei1;
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(Kd) + off * 2) = pack_bf16x2(kd0[r], kd1[r]);
+      }
+      // e^{G_15}, k e^{G_15 - G} and v, channel-major
+      const float eg0 = ex2(G0), eg1 = ex2(G1);
+      *reinterpret_cast<float2*>(sl + sEgc + c2 * 4) = float2{eg0, eg1};
+      uint32_t kt0[PT / 2], kt1[PT / 2], vt0[PT / 2], vt1[PT / 2];
+#pragma unroll
+      for (int r = 0; r < PT; r += 2) {
+        kt0[r / 2] = pack_bf16x2(kd0[r] * eg0, kd0[r + 1] * eg0);
+        kt1[r / 2] = pack_bf16x2(kd1[r] * eg1, kd1[r + 1] * eg1);
+        vt0[r / 2] = perm_lo16(rv[r], rv[r + 1]);
+        vt1[r / 2] = perm_hi16(rv[r], rv[r + 1]);
+      }
+      {
+        uint4* d0 = reinterpret_cast<uint4*>(sl + sKtT + (c2 * PT) * 2);
+        uint4* d1 = reinterpret_cast<uint4*>(sl + sKtT + ((c2 + 1) * PT) * 2);
+        d0[0] = uint4{kt0[0], kt0[1], kt0[2], kt0[3]};
+        d0[1] = uint4{kt0[4], kt0[5], kt0[6], kt0[7]};
+        d1[0] = uint4{kt1[0], kt1[1], kt1[2], kt1[3]};
+        d1[1] = uint4{kt1[4], kt1[5], kt1[6], kt1[7]};
+        uint4* w0 = reinterpret_cast<uint4*>(sl + sVT + (c2 * PT) * 2);
+        uint4* w1 = reinterpret_cast<uint4*>(sl + sVT + ((c2 + 1) * PT) * 2);
+        w0[0] = uint4{vt0[0], vt0[1], vt0[2], vt0[3]};
+        w0[1] = uint4{vt0[4], vt0[5], vt0[6], vt0[7]};
+        w1[0] = uint4{vt1[0], vt1[1], vt1[2], vt1[3]};
+        w1[1] = uint4{vt1[4], vt1[5], vt1[6], vt1[7]};
+      }
+      if (lane < PT) reinterpret_cast<float*>(sl + sBeta)[lane] = rb;
+      // the next tile of this producer loads while this one is finished
+      if (step + NPROD < nsteps) load_tile(step + NPROD);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wavefront's LDS writes landed
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup", "local");
+
+      // A_kk and A_qk, formed transposed: D[i][r] = sum_c Kd[i][c] X[r][c]
+      f32x4 dk = {0.f, 0.f, 0.f, 0.f}, dq = dk;
+#pragma unroll
+      for (int ks = 0; ks < PDK / 32; ++ks) {
+        const int ca = 32 * ks + 4 * g4;
+        const frag a0 = load_frag(Kd + m * PDK + ca), a1 = load_frag(Kd + m * PDK + ca + 16);
+        const __bf16* Kg = reinterpret_cast<const __bf16*>(sl + sKg);
+        const __bf16* Qg = reinterpret_cast<const __bf16*>(sl + sQg);
+        dk = M::k32(a0, a1, load_frag(Kg + m * PDK + ca), load_frag(Kg + m * PDK + ca + 16), dk);
+        dq = M::k32(a0, a1, load_frag(Qg + m * PDK + ca), load_frag(Qg + m * PDK + ca + 16), dq);
+      }
+      {
+        const float br = reinterpret_cast<const float*>(sl + sBeta)[m];
+        f32x4 aq;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g4 + e;
+          Ac[i * PT + m] = i < m ? br * dk[e] : 0.f;  // column i of A_kk, row m
+          aq[e] = i <= m ? dq[e] : 0.f;
+        }
+        store4(reinterpret_cast<__bf16*>(sl + sAqk) + m * PT + 4 * g4, aq);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup", "local");
+      // (I + A_kk)^{-1}, column j per lane, right-looking
+      {
+        const int j = lane & 15;
+        float t[PT];
+#pragma unroll
+        for (int r = 0; r < PT; ++r) t[r] = (r == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int r = 0; r < PT - 1; ++r) {
+          const float tr = t[r];
+#pragma unroll
+          for (int i = r + 1; i < PT; ++i) t[i] -= Ac[r * PT + i] * tr;
+        }
+        if (lane < PT) {
+          __bf16* T = reinterpret_cast<__bf16*>(sl + sT);
+#pragma unroll
+          for (int r = 0; r < PT; ++r) T[r * PT + j] = (__bf16)t[r];
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      signal_set(&ready[slot], step + 1);
+    }
+  } else {
+    // =========================== consumer ===========================
+    const int c = wave - NPROD;
+    const int vc0 = c * CCOLS;
+    constexpr int NCT = PDK / 16;
+    f32x4 S[NCT][CNTV];
+    const size_t sbase = ((size_t)n * H + h) * PDK * PDV;
+    const int svoff = ((4 * g4) * PDV + vc0 + m) * 4;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int b = 0; b < CNTV; ++b) S[ct][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (a.h0) {
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.h0 + sbase, PDK * PDV * 4);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int b = 0; b < CNTV; ++b)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            S[ct][b][e] = bits_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rs, svoff, ((16 * ct + e) * PDV + 16 * b) * 4, 0));
+    }
+    const int rowo = H * PDV * 2;
+    const int ovoff = (4 * g4) * rowo + (vc0 + m) * 2;
+
+    for (int step = 0; step < nsteps; ++step) {
+      const int slot = step % NSLOT;
+      const char* sl = smem + slot * kSlotBytes;
+      const long t0 = bos + (long)step * PT;
+      const int L = (int)min((long)PT, len - (long)step * PT);
+      wait_at_least(&ready[slot], step + 1, abort_flag);
+      const __bf16* Kg = reinterpret_cast<const __bf16*>(sl + sKg);
+      const __bf16* Qg = reinterpret_cast<const __bf16*>(sl + sQg);
+      const __bf16* KtT = reinterpret_cast<const __bf16*>(sl + sKtT);
+      const __bf16* VT = reinterpret_cast<const __bf16*>(sl + sVT);
+      const __bf16* T = reinterpret_cast<const __bf16*>(sl + sT);
+      const __bf16* Aqk = reinterpret_cast<const __bf16*>(sl + sAqk);
+      const float* bet = reinterpret_cast<const float*>(sl + sBeta);
+      const float* egc = reinterpret_cast<const float*>(sl + sEgc);
+
+      frag Sf[NCT][CNTV];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int b = 0; b < CNTV; ++b) Sf[ct][b] = M::make(S[ct][b]);
+
+      // Y = V - (e^G K) S ;  V~ = T (beta * Y)
+      f32x4 acc[CNTV];
+#pragma unroll
+      for (int b = 0; b < CNTV; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < PDK / 32; ++ks) {
+        const frag a0 = load_frag(Kg + m * PDK + 32 * ks + 4 * g4);
+        const frag a1 = load_frag(Kg + m * PDK + 32 * ks + 16 + 4 * g4);
+#pragma unroll
+        for (int b = 0; b < CNTV; ++b) acc[b] = M::k32(a0, a1, Sf[2 * ks][b], Sf[2 * ks + 1][b], acc[b]);
+      }
+      const f32x4 bb = *reinterpret_cast<const f32x4*>(bet + 4 * g4);
+      const frag tf = load_frag(T + m * PT + 4 * g4);
+      frag Xf[CNTV];
+#pragma unroll
+      for (int b = 0; b < CNTV; ++b) {
+        const f32x4 vv = load4_f32(VT + (vc0 + 16 * b + m) * PT + 4 * g4);
+        const f32x4 y = (vv - acc[b]) * bb;
+        Xf[b] = M::make(M::k16(tf, M::make(y), f32x4{0.f, 0.f, 0.f, 0.f}));
+      }
+      // O = A_qk V~ + (e^G Q) S
+      {
+        f32x4 oc[CNTV];
+        const frag aq = load_frag(Aqk + m * PT + 4 * g4);
+#pragma unroll
+        for (int b = 0; b < CNTV; ++b) oc[b] = M::k16(aq, Xf[b], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int ks = 0; ks < PDK / 32; ++ks) {
+          const frag a0 = load_frag(Qg + m * PDK + 32 * ks + 4 * g4);
+          const frag a1 = load_frag(Qg + m * PDK + 32 * ks + 16 + 4 * g4);
+#pragma unroll
+          for (int b = 0; b < CNTV; ++b) oc[b] = M::k32(a0, a1, Sf[2 * ks][b], Sf[2 * ks + 1][b], oc[b]);
+        }
+        const __amdgpu_buffer_rsrc_t rso =
+            make_rsrc(o + ((size_t)t0 * H + h) * PDV, (uint32_t)((L - 1) * H + 1) * PDV * 2);
+#pragma unroll
+        for (int b = 0; b < CNTV; ++b) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, (__bf16)(a.scale * oc[b][e])),
+                                                  rso, ovoff, e * rowo + 32 * b, 0);
+        }
+      }
+      // S <- Diag(e^{G_15}) S + (K e^{G_15 - G})^T V~
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const f32x4 eg = *reinterpret_cast<const f32x4*>(egc + 16 * ct + 4 * g4);
+        const frag ka = load_frag(KtT + (16 * ct + m) * PT + 4 * g4);
+#pragma unroll
+        for (int b = 0; b < CNTV; ++b) S[ct][b] = M::k16(ka, Xf[b], S[ct][b] * eg);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      signal_add(&done[slot], lane);
+    }
+    if (a.hT) {
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.hT + sbase, PDK * PDV * 4);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int b = 0; b < CNTV; ++b)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            __builtin_amdgcn_raw_buffer_store_b32(float_bits(S[ct][b][e]), rs, svoff,
+                                                  ((16 * ct + e) * PDV + 16 * b) * 4, 0);
+    }
+  }
+}
+
+}  // namespace
+
+bool chunk_pipe_supported(bool bf16, int Dk, int Dv, int chunk) {
+  return bf16 && Dk == PDK && Dv == PDV && chunk == 64;
+}
+
+hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t stream) {
+  if (a.seqs.N == 0 || a.H == 0) return hipSuccess;
+  dim3 grid((unsigned)(a.seqs.N * a.H)), block(PNTHR);
+  switch (a.gate_mode) {
+    case kGateLogDecay:
+      hipLaunchKernelGGL(chunk_pipe_kernel<kGateLogDecay>, grid, block, 0, stream, a);
+      break;
+    case kGateCumsum:
+      hipLaunchKernelGGL(chunk_pipe_kernel<kGateCumsum>, grid, block, 0, stream, a);
+      break;
+    default:
+      hipLaunchKernelGGL(chunk_pipe_kernel<kGateLogits>, grid, block, 0, stream, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kda

@@ -30,6 +30,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // vector element expression directly was observed to read element 0 for
 // every index; a by-value scalar is always correct.)
 __device__ __forceinline__ int float_bits(float x) { return __builtin_bit_cast(int, x); }
+__device__ __forceinline__ float bits_float(int x) { return __builtin_bit_cast(float, x); }
 
 // Buffer resource over [base, base + bytes): raw buffer loads past the end
 // return zeros and stores past the end are dropped, which gives ragged tails
@@ -65,6 +66,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
+// One matrix-core shape per precision. On gfx950, accumulator chains that mix
+// v_mfma_f32_16x16x32_bf16 and v_mfma_f32_16x16x16_bf16 were observed to
+// produce stale accumulator values (for example a 16x16x32 result fed as the
+// accumulator of a 16x16x16 less than five wait states later; the hardware
+// does not interlock that pair and the compiler does not pad it). The bf16
+// path therefore issues only 16x16x32: a k16 product is a 16x16x32 whose
+// second half of the contraction is zero. The fp32 path issues only
+// 16x16x4 f32.
 // ---------------------------------------------------------------- traits --
 // Operand storage type and the k16 / k32 products for each input precision.
 
@@ -94,8 +103,10 @@ struct Mma<__bf16> {
     return f32x4{(float)f[0], (float)f[1], (float)f[2], (float)f[3]};
   }
   static __device__ __forceinline__ f32x4 k16(const frag& a, const frag& b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+    const __bf16 z = (__bf16)0.0f;
+    const bf16x8 a8 = {a[0], a[1], a[2], a[3], z, z, z, z};
+    const bf16x8 b8 = {b[0], b[1], b[2], b[3], z, z, z, z};
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, c, 0, 0, 0);
   }
   static __device__ __forceinline__ f32x4 k32(const frag& a0, const frag& a1, const frag& b0,
                                               const frag& b1, f32x4 c) {

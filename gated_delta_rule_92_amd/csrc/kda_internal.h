@@ -64,6 +64,9 @@ struct ChunkArgs {
   bool bf16;
 };
 bool chunk_fused_supported(bool bf16, int Dk, int Dv, int chunk);
+// Pipelined producer/consumer chunk kernel (bf16, Dk = Dv = 128).
+bool chunk_pipe_supported(bool bf16, int Dk, int Dv, int chunk);
+hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t stream);
 // Lowest per-token log-decay the chunk path handles (16 * 5.5 = 88 < 88.7 = ln FLT_MAX).
 constexpr float kMinFusedGmin = -5.5f;
 hipError_t launch_chunk_fused(const ChunkArgs& a, hipStream_t stream);
