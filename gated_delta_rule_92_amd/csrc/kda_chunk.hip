@@ -202,7 +202,7 @@ __global__ void __launch_bounds__(64 * waves_for<DV>(), 1) chunk_fused_kernel(Ch
   const int H = a.H;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
   const int lane = tid & 63;
   const int m = lane & 15;   // row (A) / column (B, D) inside a 16x16 tile
   const int g4 = lane >> 4;  // k-group: contraction indices 4*g4 .. 4*g4+3

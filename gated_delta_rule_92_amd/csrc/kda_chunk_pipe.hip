@@ -26,8 +26,8 @@
 //
 // Workgroup = 8 wavefronts on one (sequence, head), two per SIMD:
 //   producers (wavefronts 0-3): wavefront p builds the operands of tiles
-//     p, p+4, p+8, ... on its own (lane = 2 channels x 16 rows, so the
-//     cumulative sum needs no other wavefront): gate, cumsum, exponentials,
+//     p, p+4, p+8, ... on its own (lane = 4 channels x 8 rows; the two row
+//     halves exchange their partial sums): gate, cumsum, exponentials,
 //     the bf16 operand arrays, A_kk and A_qk (matrix cores), the 16x16
 //     inverse (fp32, right-looking), then publishes the slot;
 //   consumers (wavefronts 4-7): wavefront 4+c owns value columns
@@ -45,7 +45,7 @@ namespace {
 
 constexpr int PT = 16;        // tile rows
 constexpr int PDK = 128, PDV = 128;
-constexpr int NSLOT = 6;      // ring slots
+constexpr int NSLOT = 5;      // ring slots
 constexpr int NPROD = 4, NCONS = 4;
 constexpr int PNTHR = 64 * (NPROD + NCONS);
 constexpr int CCOLS = PDV / NCONS;  // value columns per consumer
@@ -55,20 +55,26 @@ constexpr int CNTV = CCOLS / 16;    // 16-column tiles per consumer
 // wait returns at once, so the kernel always finishes.
 constexpr int kSpinLimit = 1 << 15;
 
+// LDS row strides (elements). Matrix-core fragments are read as 8 bytes per
+// lane from 16 rows; the padding spreads the 16 rows of a half-wavefront over
+// all 64 banks (an unpadded 256-byte row stride puts them in the same two).
+constexpr int RS = PDK + 8;  // token-major [16][128] bf16 arrays
+constexpr int TS = PT + 8;   // token-contiguous [*][16] bf16 arrays
+constexpr int AS = PT + 4;   // fp32 A_kk columns
 // Slot layout (bytes). bf16 unless noted.
-constexpr int sKg = 0;                      // k e^{G}      [16][128]
-constexpr int sQg = sKg + PT * PDK * 2;     // q e^{G}      [16][128]
-constexpr int sKtT = sQg + PT * PDK * 2;    // k e^{G15-G}  [128][16] (channel-major)
-constexpr int sVT = sKtT + PDK * PT * 2;    // v            [128][16] (channel-major)
-constexpr int sT = sVT + PDV * PT * 2;      // (I+A_kk)^-1  [16][16]
-constexpr int sAqk = sT + PT * PT * 2;      // A_qk         [16][16]
-constexpr int sBeta = sAqk + PT * PT * 2;   // fp32 [16]
+constexpr int sKg = 0;                      // k e^{G}      [16][RS]
+constexpr int sQg = sKg + PT * RS * 2;      // q e^{G}      [16][RS]
+constexpr int sKtT = sQg + PT * RS * 2;     // k e^{G15-G}  [128][TS] (channel-major)
+constexpr int sVT = sKtT + PDK * TS * 2;    // v            [128][TS] (channel-major)
+constexpr int sT = sVT + PDV * TS * 2;      // (I+A_kk)^-1  [16][TS]
+constexpr int sAqk = sT + PT * TS * 2;      // A_qk         [16][TS]
+constexpr int sBeta = sAqk + PT * TS * 2;   // fp32 [16]
 constexpr int sEgc = sBeta + PT * 4;        // fp32 [128]  e^{G_15}
 constexpr int kSlotBytes = ((sEgc + PDK * 4) + 255) / 256 * 256;
 // Producer-private scratch.
-constexpr int pKd = 0;                      // k e^{-G}     [16][128] bf16
-constexpr int pAc = pKd + PT * PDK * 2;     // A_kk by columns, fp32 [16][16]
-constexpr int kPrivBytes = pAc + PT * PT * 4;
+constexpr int pKd = 0;                      // k e^{-G}     [16][RS] bf16
+constexpr int pAc = pKd + PT * RS * 2;      // A_kk by columns, fp32 [16][AS]
+constexpr int kPrivBytes = pAc + PT * AS * 4;
 constexpr int kLdsBytes = NSLOT * kSlotBytes + NPROD * kPrivBytes + (2 * NSLOT + 1) * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
@@ -127,7 +133,9 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
   const __bf16* v = reinterpret_cast<const __bf16*>(a.v);
   __bf16* o = reinterpret_cast<__bf16*>(a.o);
   const int H = a.H;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wavefront index, known to the compiler as uniform (kept in scalar registers)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 15, g4 = lane >> 4;
 
   const int n = a.order ? a.order[blockIdx.x / H] : (int)(blockIdx.x / H);
@@ -154,29 +162,41 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
     float* Ac = reinterpret_cast<float*>(priv + pAc);
     const float es2 = ((GATE == kGateLogits && a.A_log) ? __expf(a.A_log[h]) : 1.0f) * kLog2e;
     const float gmin2 = a.g_min * kLog2e;
-    const int c2 = 2 * lane;  // this lane's two channels
+    // lane = (row half hr, channel quad cq): channels 4cq..4cq+3 of rows
+    // 8hr..8hr+7. The cumulative sum runs over the lane's 8 rows and the two
+    // halves then exchange their totals.
+    const int hr = lane >> 5, cq = lane & 31;
+    const int r0 = 8 * hr;
+    const int xaddr = (lane ^ 32) * 4;  // partner lane for the exchange
 
-    // raw tile data: row r of channels (c2, c2+1)
-    uint32_t rk[PT], rq[PT], rv[PT];
-    float2 rz[PT];
+    // raw tile data: row r0 + r of channels 4cq..4cq+3
+    i32x2 rk[8], rq[8], rv[8];
+    f32x4 rz[8];
     float rb;  // beta of row `lane` (lanes 0..15)
     auto load_tile = [&](int step) {
       const long t0 = bos + (long)step * PT;
       const int L = (int)min((long)PT, len - (long)step * PT);
       const size_t base = ((size_t)t0 * H + h);
-      const __amdgpu_buffer_rsrc_t rsk = make_rsrc(k + base * PDK, (uint32_t)((L - 1) * H + 1) * PDK * 2);
-      const __amdgpu_buffer_rsrc_t rsq = make_rsrc(q + base * PDK, (uint32_t)((L - 1) * H + 1) * PDK * 2);
-      const __amdgpu_buffer_rsrc_t rsv = make_rsrc(v + base * PDV, (uint32_t)((L - 1) * H + 1) * PDV * 2);
-      const __amdgpu_buffer_rsrc_t rsg = make_rsrc(a.g + base * PDK, (uint32_t)((L - 1) * H + 1) * PDK * 4);
-      const __amdgpu_buffer_rsrc_t rsb = make_rsrc(a.beta + base, (uint32_t)((L - 1) * H + 1) * 4);
+      const uint32_t nrow = (uint32_t)((L - 1) * H + 1);
+      const __amdgpu_buffer_rsrc_t rsk = make_rsrc(k + base * PDK, nrow * PDK * 2);
+      const __amdgpu_buffer_rsrc_t rsq = make_rsrc(q + base * PDK, nrow * PDK * 2);
+      const __amdgpu_buffer_rsrc_t rsv = make_rsrc(v + base * PDV, nrow * PDV * 2);
+      const __amdgpu_buffer_rsrc_t rsg = make_rsrc(a.g + base * PDK, nrow * PDK * 4);
+      const __amdgpu_buffer_rsrc_t rsb = make_rsrc(a.beta + base, nrow * 4);
+      const int vk = r0 * rowk + cq * 8, vz = r0 * rowg + cq * 16;
 #pragma unroll
-      for (int r = 0; r < PT; ++r) {
-        rk[r] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsk, c2 * 2, r * rowk, 0);
-        rq[r] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsq, c2 * 2, r * rowk, 0);
-        rv[r] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsv, c2 * 2, r * rowk, 0);
-        i32x2 zz = __builtin_amdgcn_raw_buffer_load_b64(rsg, c2 * 4, r * rowg, 0);
-        const int z0 = zz.x, z1 = zz.y;
-        rz[r] = float2{bits_float(z0), bits_float(z1)};
+      for (int r = 0; r < 8; ++r) {
+        rk[r] = __builtin_amdgcn_raw_buffer_load_b64(rsk, vk, r * rowk, 0);
+        rq[r] = __builtin_amdgcn_raw_buffer_load_b64(rsq, vk, r * rowk, 0);
+        rv[r] = __builtin_amdgcn_raw_buffer_load_b64(rsv, vk, r * rowk, 0);
+        if constexpr (GATE == kGateCumsum) {
+          // cumulative-sum input: rows past the end repeat the last row, so
+          // that their value equals the tile's final one
+          const int rg = min(r0 + r, L - 1);
+          rz[r] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsg, cq * 16 + rg * rowg, 0, 0));
+        } else {
+          rz[r] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsg, vz, r * rowg, 0));
+        }
       }
       rb = bits_float(__builtin_amdgcn_raw_buffer_load_b32(rsb, lane * rowb, 0, 0));
     };
@@ -191,76 +211,98 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
       // the slot's previous tile must have been consumed by every consumer
       if (use > 0) wait_at_least(&done[slot], NCONS * use, abort_flag);
 
-      // cumulative log2-decay of this tile, channels (c2, c2+1)
-      float G0 = 0.f, G1 = 0.f;
-      float base0 = 0.f, base1 = 0.f;
-      if constexpr (GATE == kGateCumsum) {
-        // g holds the cumulative sum within 64-token chunks; rebase it at the
-        // tile start (the value just before the tile, when the tile is not
-        // the first of its chunk).
-        const long tin = (long)step * PT;
-        if (tin % 64 != 0) {
-          const float2 pv = *reinterpret_cast<const float2*>(
-              a.g + ((size_t)(t0 - 1) * H + h) * PDK + c2);
-          base0 = pv.x * kLog2e;
-          base1 = pv.y * kLog2e;
-        }
-      }
-      float kd0[PT], kd1[PT];
+      // cumulative log2-decay of this lane's rows (local to the half for the
+      // incremental gate forms, absolute for the cumulative-sum form)
+      float Gl[8][4];
+      {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        float base[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (GATE == kGateCumsum) {
+          // g holds the cumulative sum within 64-token chunks; rebase it at
+          // the tile start (the value just before the tile, when the tile is
+          // not the first of its chunk).
+          if (((long)step * PT) % 64 != 0) {
+            const f32x4 pv = *reinterpret_cast<const f32x4*>(a.g + ((size_t)(t0 - 1) * H + h) * PDK + 4 * cq);
 #pragma unroll
-      for (int r = 0; r < PT; ++r) {
-        float g0 = rz[r].x, g1 = rz[r].y;
-        if constexpr (GATE == kGateLogits) {
-          const float gm = r < L ? gmin2 : 0.f;
-          g0 = gm * __builtin_amdgcn_rcpf(1.0f + ex2(-es2 * g0));
-          g1 = gm * __builtin_amdgcn_rcpf(1.0f + ex2(-es2 * g1));
-          G0 += g0;
-          G1 += g1;
-        } else if constexpr (GATE == kGateLogDecay) {
-          G0 += g0 * kLog2e;  // rows past the end read as 0
-          G1 += g1 * kLog2e;
-        } else {
-          if (r < L) {
-            G0 = g0 * kLog2e - base0;
-            G1 = g1 * kLog2e - base1;
+            for (int j = 0; j < 4; ++j) base[j] = pv[j] * kLog2e;
           }
         }
-        const float E0 = ex2(G0), E1 = ex2(G1);
-        const float Ei0 = ex2(-G0), Ei1 = ex2(-G1);
-        float k0, k1, q0, q1;
-        unpack_bf16x2(rk[r], k0, k1);
-        unpack_bf16x2(rq[r], q0, q1);
-        const int off = r * PDK + c2;
-        *reinterpret_cast<uint32_t*>(sl + sKg + off * 2) = pack_bf16x2(k0 * E0, k1 * E1);
-        *reinterpret_cast<uint32_t*>(sl + sQg + off * 2) = pack_bf16x2(q0 * E0, q1 * E1);
-        kd0[r] = k0 * Ei0;
-        kd1[r] = k1 * Ei1;
-        *reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(Kd) + off * 2) = pack_bf16x2(kd0[r], kd1[r]);
-      }
-      // e^{G_15}, k e^{G_15 - G} and v, channel-major
-      const float eg0 = ex2(G0), eg1 = ex2(G1);
-      *reinterpret_cast<float2*>(sl + sEgc + c2 * 4) = float2{eg0, eg1};
-      uint32_t kt0[PT / 2], kt1[PT / 2], vt0[PT / 2], vt1[PT / 2];
 #pragma unroll
-      for (int r = 0; r < PT; r += 2) {
-        kt0[r / 2] = pack_bf16x2(kd0[r] * eg0, kd0[r + 1] * eg0);
-        kt1[r / 2] = pack_bf16x2(kd1[r] * eg1, kd1[r + 1] * eg1);
-        vt0[r / 2] = perm_lo16(rv[r], rv[r + 1]);
-        vt1[r / 2] = perm_hi16(rv[r], rv[r + 1]);
+        for (int r = 0; r < 8; ++r) {
+          const f32x4 z = rz[r];
+          if constexpr (GATE == kGateLogits) {
+            const float gm = r0 + r < L ? gmin2 : 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = fmaf(gm, __builtin_amdgcn_rcpf(1.0f + ex2(-es2 * z[j])), acc[j]);
+          } else if constexpr (GATE == kGateLogDecay) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = fmaf(z[j], kLog2e, acc[j]);  // rows past the end read as 0
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = fmaf(z[j], kLog2e, -base[j]);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) Gl[r][j] = acc[j];
+        }
       }
-      {
-        uint4* d0 = reinterpret_cast<uint4*>(sl + sKtT + (c2 * PT) * 2);
-        uint4* d1 = reinterpret_cast<uint4*>(sl + sKtT + ((c2 + 1) * PT) * 2);
-        d0[0] = uint4{kt0[0], kt0[1], kt0[2], kt0[3]};
-        d0[1] = uint4{kt0[4], kt0[5], kt0[6], kt0[7]};
-        d1[0] = uint4{kt1[0], kt1[1], kt1[2], kt1[3]};
-        d1[1] = uint4{kt1[4], kt1[5], kt1[6], kt1[7]};
-        uint4* w0 = reinterpret_cast<uint4*>(sl + sVT + (c2 * PT) * 2);
-        uint4* w1 = reinterpret_cast<uint4*>(sl + sVT + ((c2 + 1) * PT) * 2);
-        w0[0] = uint4{vt0[0], vt0[1], vt0[2], vt0[3]};
-        w0[1] = uint4{vt0[4], vt0[5], vt0[6], vt0[7]};
-        w1[0] = uint4{vt1[0], vt1[1], vt1[2], vt1[3]};
-        w1[1] = uint4{vt1[4], vt1[5], vt1[6], vt1[7]};
+      // exchange the halves' last values; off = what the upper half adds,
+      // gc = G at the tile's last row (the tile's total decay)
+      float off[4], gc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float other = bits_float(__builtin_amdgcn_ds_bpermute(xaddr, float_bits(Gl[7][j])));
+        if constexpr (GATE == kGateCumsum) {
+          off[j] = 0.f;
+          gc[j] = hr ? Gl[7][j] : other;
+        } else {
+          off[j] = hr ? other : 0.f;
+          gc[j] = Gl[7][j] + other;
+        }
+      }
+      float eg[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) eg[j] = ex2(gc[j]);
+      float kt[8][4];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        float kk[4], qq[4], kg[4], qg[4], kd[4];
+        unpack_bf16x2((uint32_t)rk[r].x, kk[0], kk[1]);
+        unpack_bf16x2((uint32_t)rk[r].y, kk[2], kk[3]);
+        unpack_bf16x2((uint32_t)rq[r].x, qq[0], qq[1]);
+        unpack_bf16x2((uint32_t)rq[r].y, qq[2], qq[3]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float G = Gl[r][j] + off[j];
+          const float E = ex2(G);
+          kg[j] = kk[j] * E;
+          qg[j] = qq[j] * E;
+          kd[j] = kk[j] * ex2(-G);
+          kt[r][j] = kd[j] * eg[j];
+        }
+        const int o = (r0 + r) * RS + 4 * cq;
+        *reinterpret_cast<uint2*>(sl + sKg + o * 2) = uint2{pack_bf16x2(kg[0], kg[1]), pack_bf16x2(kg[2], kg[3])};
+        *reinterpret_cast<uint2*>(sl + sQg + o * 2) = uint2{pack_bf16x2(qg[0], qg[1]), pack_bf16x2(qg[2], qg[3])};
+        *reinterpret_cast<uint2*>(reinterpret_cast<char*>(Kd) + o * 2) =
+            uint2{pack_bf16x2(kd[0], kd[1]), pack_bf16x2(kd[2], kd[3])};
+      }
+      // e^{G_15}, k e^{G_15 - G} and v, channel-major (this lane: 8 tokens
+      // of 4 channels)
+      if (hr) {
+        *reinterpret_cast<f32x4*>(sl + sEgc + cq * 16) = f32x4{eg[0], eg[1], eg[2], eg[3]};
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = 4 * cq + j;
+        uint32_t w[4], u[4];
+#pragma unroll
+        for (int r = 0; r < 8; r += 2) {
+          w[r / 2] = pack_bf16x2(kt[r][j], kt[r + 1][j]);
+          const uint32_t a0 = (uint32_t)(j < 2 ? rv[r].x : rv[r].y);
+          const uint32_t a1 = (uint32_t)(j < 2 ? rv[r + 1].x : rv[r + 1].y);
+          u[r / 2] = (j & 1) ? perm_hi16(a0, a1) : perm_lo16(a0, a1);
+        }
+        *reinterpret_cast<uint4*>(sl + sKtT + (c * TS + r0) * 2) = uint4{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<uint4*>(sl + sVT + (c * TS + r0) * 2) = uint4{u[0], u[1], u[2], u[3]};
       }
       if (lane < PT) reinterpret_cast<float*>(sl + sBeta)[lane] = rb;
       // the next tile of this producer loads while this one is finished
@@ -273,11 +315,11 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
 #pragma unroll
       for (int ks = 0; ks < PDK / 32; ++ks) {
         const int ca = 32 * ks + 4 * g4;
-        const frag a0 = load_frag(Kd + m * PDK + ca), a1 = load_frag(Kd + m * PDK + ca + 16);
+        const frag a0 = load_frag(Kd + m * RS + ca), a1 = load_frag(Kd + m * RS + ca + 16);
         const __bf16* Kg = reinterpret_cast<const __bf16*>(sl + sKg);
         const __bf16* Qg = reinterpret_cast<const __bf16*>(sl + sQg);
-        dk = M::k32(a0, a1, load_frag(Kg + m * PDK + ca), load_frag(Kg + m * PDK + ca + 16), dk);
-        dq = M::k32(a0, a1, load_frag(Qg + m * PDK + ca), load_frag(Qg + m * PDK + ca + 16), dq);
+        dk = M::k32(a0, a1, load_frag(Kg + m * RS + ca), load_frag(Kg + m * RS + ca + 16), dk);
+        dq = M::k32(a0, a1, load_frag(Qg + m * RS + ca), load_frag(Qg + m * RS + ca + 16), dq);
       }
       {
         const float br = reinterpret_cast<const float*>(sl + sBeta)[m];
@@ -285,10 +327,10 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g4 + e;
-          Ac[i * PT + m] = i < m ? br * dk[e] : 0.f;  // column i of A_kk, row m
+          Ac[i * AS + m] = i < m ? br * dk[e] : 0.f;  // column i of A_kk, row m
           aq[e] = i <= m ? dq[e] : 0.f;
         }
-        store4(reinterpret_cast<__bf16*>(sl + sAqk) + m * PT + 4 * g4, aq);
+        store4(reinterpret_cast<__bf16*>(sl + sAqk) + m * TS + 4 * g4, aq);
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup", "local");
@@ -302,12 +344,12 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
         for (int r = 0; r < PT - 1; ++r) {
           const float tr = t[r];
 #pragma unroll
-          for (int i = r + 1; i < PT; ++i) t[i] -= Ac[r * PT + i] * tr;
+          for (int i = r + 1; i < PT; ++i) t[i] -= Ac[r * AS + i] * tr;
         }
         if (lane < PT) {
           __bf16* T = reinterpret_cast<__bf16*>(sl + sT);
 #pragma unroll
-          for (int r = 0; r < PT; ++r) T[r * PT + j] = (__bf16)t[r];
+          for (int r = 0; r < PT; ++r) T[r * TS + j] = (__bf16)t[r];
         }
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -366,30 +408,30 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
       for (int b = 0; b < CNTV; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < PDK / 32; ++ks) {
-        const frag a0 = load_frag(Kg + m * PDK + 32 * ks + 4 * g4);
-        const frag a1 = load_frag(Kg + m * PDK + 32 * ks + 16 + 4 * g4);
+        const frag a0 = load_frag(Kg + m * RS + 32 * ks + 4 * g4);
+        const frag a1 = load_frag(Kg + m * RS + 32 * ks + 16 + 4 * g4);
 #pragma unroll
         for (int b = 0; b < CNTV; ++b) acc[b] = M::k32(a0, a1, Sf[2 * ks][b], Sf[2 * ks + 1][b], acc[b]);
       }
       const f32x4 bb = *reinterpret_cast<const f32x4*>(bet + 4 * g4);
-      const frag tf = load_frag(T + m * PT + 4 * g4);
+      const frag tf = load_frag(T + m * TS + 4 * g4);
       frag Xf[CNTV];
 #pragma unroll
       for (int b = 0; b < CNTV; ++b) {
-        const f32x4 vv = load4_f32(VT + (vc0 + 16 * b + m) * PT + 4 * g4);
+        const f32x4 vv = load4_f32(VT + (vc0 + 16 * b + m) * TS + 4 * g4);
         const f32x4 y = (vv - acc[b]) * bb;
         Xf[b] = M::make(M::k16(tf, M::make(y), f32x4{0.f, 0.f, 0.f, 0.f}));
       }
       // O = A_qk V~ + (e^G Q) S
       {
         f32x4 oc[CNTV];
-        const frag aq = load_frag(Aqk + m * PT + 4 * g4);
+        const frag aq = load_frag(Aqk + m * TS + 4 * g4);
 #pragma unroll
         for (int b = 0; b < CNTV; ++b) oc[b] = M::k16(aq, Xf[b], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int ks = 0; ks < PDK / 32; ++ks) {
-          const frag a0 = load_frag(Qg + m * PDK + 32 * ks + 4 * g4);
-          const frag a1 = load_frag(Qg + m * PDK + 32 * ks + 16 + 4 * g4);
+          const frag a0 = load_frag(Qg + m * RS + 32 * ks + 4 * g4);
+          const frag a1 = load_frag(Qg + m * RS + 32 * ks + 16 + 4 * g4);
 #pragma unroll
           for (int b = 0; b < CNTV; ++b) oc[b] = M::k32(a0, a1, Sf[2 * ks][b], Sf[2 * ks + 1][b], oc[b]);
         }
@@ -407,7 +449,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         const f32x4 eg = *reinterpret_cast<const f32x4*>(egc + 16 * ct + 4 * g4);
-        const frag ka = load_frag(KtT + (16 * ct + m) * PT + 4 * g4);
+        const frag ka = load_frag(KtT + (16 * ct + m) * TS + 4 * g4);
 #pragma unroll
         for (int b = 0; b < CNTV; ++b) S[ct][b] = M::k16(ka, Xf[b], S[ct][b] * eg);
       }
