@@ -32,9 +32,9 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 FP32_MATRIX_PEAK_TFLOPS = 157.3
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fused_train8k_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_pipe_train8k_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_92_amd", "csrc", f)
-                  for f in ("kda_chunk.hip", "kda_common.h")]
+                  for f in ("kda_chunk_pipe.hip", "kda_common.h", "kda_internal.h")]
 
 
 def log(msg: str):
@@ -66,9 +66,11 @@ def algorithmic_flops(w, n_tokens: int) -> float:
     return per_chunk / C * n_tokens * w.H
 
 
-def cpu_baseline(d, w, budget_s: float = 20.0):
+def cpu_baseline(d, w, budget_s: float = 25.0):
     """The fp64 oracle on a bounded sample of (sequence, head) units of the
-    same workload, on the host cores; returns a dict for the JSON line."""
+    same workload, on the host cores; returns a dict for the JSON line.
+    The sample holds about `budget_s` seconds of single-thread oracle work
+    (at most the whole workload), spread over up to 16 threads."""
     import numpy as np
     from oracle import oracle_forward
     cores = min(os.cpu_count() or 1, 16)
@@ -94,8 +96,8 @@ def cpu_baseline(d, w, budget_s: float = 20.0):
     oracle_forward(q, k, v, z, b, None, cu, None, w.g_min, 1.0, nthreads=1)
     per_unit = time.perf_counter() - t0
     n_units = max(cores, int(budget_s / max(per_unit, 1e-3)))
-    n_units = min(n_units, d["q"].shape[0] * H)
     n_units = max(cores, (n_units // cores) * cores)
+    n_units = min(n_units, d["q"].shape[0] * H)
     units = [(i % d["q"].shape[0], (i // d["q"].shape[0]) % H) for i in range(n_units)]
     q, k, v, z, b, cu = unit_inputs(units)
     t0 = time.perf_counter()

@@ -357,6 +357,9 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
     }
   } else {
     // =========================== consumer ===========================
+    // The consumers carry the recurrence's serial chain; when a producer and
+    // a consumer on one SIMD are both ready to issue, the consumer goes first.
+    __builtin_amdgcn_s_setprio(3);
     const int c = wave - NPROD;
     const int vc0 = c * CCOLS;
     constexpr int NCT = PDK / 16;
@@ -379,7 +382,6 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
                 __builtin_amdgcn_raw_buffer_load_b32(rs, svoff, ((16 * ct + e) * PDV + 16 * b) * 4, 0));
     }
     const int rowo = H * PDV * 2;
-    const int ovoff = (4 * g4) * rowo + (vc0 + m) * 2;
 
     for (int step = 0; step < nsteps; ++step) {
       const int slot = step % NSLOT;
@@ -437,12 +439,20 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
         }
         const __amdgpu_buffer_rsrc_t rso =
             make_rsrc(o + ((size_t)t0 * H + h) * PDV, (uint32_t)((L - 1) * H + 1) * PDV * 2);
+        // adjacent lanes (columns m, m^1) swap one value per row pair, so
+        // that each lane stores two neighbouring columns of one row
+        const bool odd = m & 1;
+        const int ovoff2 = (4 * g4 + (odd ? 1 : 0)) * rowo + (vc0 + (m & ~1)) * 2;
 #pragma unroll
         for (int b = 0; b < CNTV; ++b) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, (__bf16)(a.scale * oc[b][e])),
-                                                  rso, ovoff, e * rowo + 32 * b, 0);
+          for (int i = 0; i < 2; ++i) {
+            const float send = odd ? oc[b][2 * i] : oc[b][2 * i + 1];
+            const float recv = bits_float(__builtin_amdgcn_mov_dpp(float_bits(send), 0xB1, 0xF, 0xF, false));
+            const uint32_t w = odd ? pack_bf16x2(a.scale * recv, a.scale * oc[b][2 * i + 1])
+                                   : pack_bf16x2(a.scale * oc[b][2 * i], a.scale * recv);
+            __builtin_amdgcn_raw_buffer_store_b32((int)w, rso, ovoff2, 2 * i * rowo + 32 * b, 0);
+          }
         }
       }
       // S <- Diag(e^{G_15}) S + (K e^{G_15 - G})^T V~
