@@ -57,13 +57,14 @@ def algorithmic_bytes(w, n_tokens: int, n_units: int, has_h0: bool) -> int:
 
 
 def algorithmic_flops(w, n_tokens: int) -> float:
-    """Matrix-core flops of the chunk arrangement per launch: per chunk of 64,
-    the causal 16x16 tiles (10 of 16) of A_kk, A_qk, the triangular solve and
-    A_qk V~ over d, plus the three state products (d_k x d_v each)."""
-    C, dk, dv = 64, w.Dk, w.Dv
-    tiles = 10 * 16 * 16 * 2
-    per_chunk = tiles * dk * 2 + tiles * dv * 2 + 3 * 2 * C * dk * dv
-    return per_chunk / C * n_tokens * w.H
+    """Useful matrix-core flops per launch for the arrangement the bf16
+    d=128 kernel runs (the state advanced every 16-token tile): per tile,
+    A_kk and A_qk over d_k (2 x 2*16*16*d_k), V - (G*K)S, (G*Q)S and the
+    state update over d_k x d_v (3 x 2*16*d_k*d_v), the solve and A_qk V~
+    over d_v (2 x 2*16*16*d_v)."""
+    P, dk, dv = 16, w.Dk, w.Dv
+    per_tile = 2 * (2 * P * P * dk) + 3 * (2 * P * dk * dv) + 2 * (2 * P * P * dv)
+    return per_tile / P * n_tokens * w.H
 
 
 def cpu_baseline(d, w, budget_s: float = 25.0):
