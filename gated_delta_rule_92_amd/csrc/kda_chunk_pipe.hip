@@ -29,7 +29,7 @@
 //     p, p+4, p+8, ... on its own (lane = 4 channels x 8 rows; the two row
 //     halves exchange their partial sums): gate, cumsum, exponentials,
 //     the bf16 operand arrays, A_kk and A_qk (matrix cores), the 16x16
-//     inverse (fp32, right-looking), then publishes the slot;
+//     inverse (fp32 matrix cores, product form), then publishes the slot;
 //   consumers (wavefronts 4-7): wavefront 4+c owns value columns
 //     [32c, 32c+32) of the state (the recurrence is separable over value
 //     columns), holds them in registers and applies each tile in order.
@@ -60,7 +60,6 @@ constexpr int kSpinLimit = 1 << 15;
 // all 64 banks (an unpadded 256-byte row stride puts them in the same two).
 constexpr int RS = PDK + 8;  // token-major [16][128] bf16 arrays
 constexpr int TS = PT + 8;   // token-contiguous [*][16] bf16 arrays
-constexpr int AS = PT + 4;   // fp32 A_kk columns
 // Slot layout (bytes). bf16 unless noted.
 constexpr int sKg = 0;                      // k e^{G}      [16][RS]
 constexpr int sQg = sKg + PT * RS * 2;      // q e^{G}      [16][RS]
@@ -73,8 +72,7 @@ constexpr int sEgc = sBeta + PT * 4;        // fp32 [128]  e^{G_15}
 constexpr int kSlotBytes = ((sEgc + PDK * 4) + 255) / 256 * 256;
 // Producer-private scratch.
 constexpr int pKd = 0;                      // k e^{-G}     [16][RS] bf16
-constexpr int pAc = pKd + PT * RS * 2;      // A_kk by columns, fp32 [16][AS]
-constexpr int kPrivBytes = pAc + PT * AS * 4;
+constexpr int kPrivBytes = pKd + PT * RS * 2;
 constexpr int kLdsBytes = NSLOT * kSlotBytes + NPROD * kPrivBytes + (2 * NSLOT + 1) * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
@@ -159,7 +157,6 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
     const int p = wave;
     char* priv = smem + NSLOT * kSlotBytes + p * kPrivBytes;
     __bf16* Kd = reinterpret_cast<__bf16*>(priv + pKd);
-    float* Ac = reinterpret_cast<float*>(priv + pAc);
     const float es2 = ((GATE == kGateLogits && a.A_log) ? __expf(a.A_log[h]) : 1.0f) * kLog2e;
     const float gmin2 = a.g_min * kLog2e;
     // lane = (row half hr, channel quad cq): channels 4cq..4cq+3 of rows
@@ -310,47 +307,61 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wavefront's LDS writes landed
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup", "local");
 
-      // A_kk and A_qk, formed transposed: D[i][r] = sum_c Kd[i][c] X[r][c]
-      f32x4 dk = {0.f, 0.f, 0.f, 0.f}, dq = dk;
+      // Raw key-key and query-key products. In the accumulator layout lane
+      // (m, g4) holds element e at row 4g4+e, column m:
+      //   dk[e] = sum_c Kg[m][c] Kd[4g4+e][c]   (= A_kk[m][4g4+e] / beta_m)
+      //   dn[e] = sum_c Kg[4g4+e][c] Kd[m][c]   (= A_kk[4g4+e][m] / beta_{4g4+e})
+      //   dq[e] = sum_c Qg[m][c] Kd[4g4+e][c]   (= A_qk[m][4g4+e])
+      f32x4 dk = {0.f, 0.f, 0.f, 0.f}, dn = dk, dq = dk;
 #pragma unroll
       for (int ks = 0; ks < PDK / 32; ++ks) {
         const int ca = 32 * ks + 4 * g4;
-        const frag a0 = load_frag(Kd + m * RS + ca), a1 = load_frag(Kd + m * RS + ca + 16);
         const __bf16* Kg = reinterpret_cast<const __bf16*>(sl + sKg);
         const __bf16* Qg = reinterpret_cast<const __bf16*>(sl + sQg);
-        dk = M::k32(a0, a1, load_frag(Kg + m * RS + ca), load_frag(Kg + m * RS + ca + 16), dk);
-        dq = M::k32(a0, a1, load_frag(Qg + m * RS + ca), load_frag(Qg + m * RS + ca + 16), dq);
+        const frag d0 = load_frag(Kd + m * RS + ca), d1 = load_frag(Kd + m * RS + ca + 16);
+        const frag k0 = load_frag(Kg + m * RS + ca), k1 = load_frag(Kg + m * RS + ca + 16);
+        dk = M::k32(d0, d1, k0, k1, dk);
+        dn = M::k32(k0, k1, d0, d1, dn);
+        dq = M::k32(d0, d1, load_frag(Qg + m * RS + ca), load_frag(Qg + m * RS + ca + 16), dq);
       }
+      // A = StrictTril(Diag(beta) raw) in the accumulator layout (An) and its
+      // transpose (At); A_qk keeps the diagonal.
+      f32x4 An, At;
       {
-        const float br = reinterpret_cast<const float*>(sl + sBeta)[m];
+        const float* bet = reinterpret_cast<const float*>(sl + sBeta);
+        const float bm = bet[m];
+        const f32x4 bi = *reinterpret_cast<const f32x4*>(bet + 4 * g4);
         f32x4 aq;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g4 + e;
-          Ac[i * AS + m] = i < m ? br * dk[e] : 0.f;  // column i of A_kk, row m
+          At[e] = i < m ? bm * dk[e] : 0.f;
+          An[e] = m < i ? bi[e] * dn[e] : 0.f;
           aq[e] = i <= m ? dq[e] : 0.f;
         }
         store4(reinterpret_cast<__bf16*>(sl + sAqk) + m * TS + 4 * g4, aq);
       }
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup", "local");
-      // (I + A_kk)^{-1}, column j per lane, right-looking
+      // T = (I + A)^{-1}. A is strictly lower triangular, so A^16 = 0 and
+      // (I + A)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8), a product of
+      // commuting factors. Evaluated on fp32 matrix cores: a product X Y
+      // takes X^T and Y in the accumulator layout, so both A^(2^k) and their
+      // transposes are formed. The result is T^T in the accumulator layout,
+      // i.e. lane (m, g4) holds T[m][4g4+e]: the consumers' operand fragment.
       {
-        const int j = lane & 15;
-        float t[PT];
+        using MF = Mma<float>;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 A2 = MF::k16(At, An, z);   // A^2
+        const f32x4 A2t = MF::k16(An, At, z);  // (A^2)^T
+        const f32x4 A4 = MF::k16(A2t, A2, z);
+        const f32x4 A4t = MF::k16(A2, A2t, z);
+        const f32x4 A8 = MF::k16(A4t, A4, z);
+        f32x4 R;  // I - A^T
 #pragma unroll
-        for (int r = 0; r < PT; ++r) t[r] = (r == j) ? 1.f : 0.f;
-#pragma unroll
-        for (int r = 0; r < PT - 1; ++r) {
-          const float tr = t[r];
-#pragma unroll
-          for (int i = r + 1; i < PT; ++i) t[i] -= Ac[r * AS + i] * tr;
-        }
-        if (lane < PT) {
-          __bf16* T = reinterpret_cast<__bf16*>(sl + sT);
-#pragma unroll
-          for (int r = 0; r < PT; ++r) T[r * TS + j] = (__bf16)t[r];
-        }
+        for (int e = 0; e < 4; ++e) R[e] = (4 * g4 + e == m ? 1.f : 0.f) - At[e];
+        R = MF::k16(A2, R, R);  // (I + (A^2)^T) R
+        R = MF::k16(A4, R, R);
+        R = MF::k16(A8, R, R);
+        store4(reinterpret_cast<__bf16*>(sl + sT) + m * TS + 4 * g4, R);
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);
       signal_set(&ready[slot], step + 1);
@@ -382,6 +393,11 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
                 __builtin_amdgcn_raw_buffer_load_b32(rs, svoff, ((16 * ct + e) * PDV + 16 * b) * 4, 0));
     }
     const int rowo = H * PDV * 2;
+    // output stores: byte selectors of v_perm (partner pair, own pair) and the
+    // lane's row / column-pair offset
+    const bool odd = m & 1;
+    const uint32_t psel = odd ? 0x03020706u : 0x05040100u;
+    const int ovoff2 = (4 * g4 + (odd ? 1 : 0)) * rowo + (vc0 + (m & ~1)) * 2;
 
     for (int step = 0; step < nsteps; ++step) {
       const int slot = step % NSLOT;
@@ -439,20 +455,20 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
         }
         const __amdgpu_buffer_rsrc_t rso =
             make_rsrc(o + ((size_t)t0 * H + h) * PDV, (uint32_t)((L - 1) * H + 1) * PDV * 2);
-        // adjacent lanes (columns m, m^1) swap one value per row pair, so
-        // that each lane stores two neighbouring columns of one row
-        const bool odd = m & 1;
-        const int ovoff2 = (4 * g4 + (odd ? 1 : 0)) * rowo + (vc0 + (m & ~1)) * 2;
+        // Each lane packs its rows (0,1) and (2,3) into bf16 pairs, adjacent
+        // lanes (columns m, m^1) swap the pairs, and each lane stores two
+        // neighbouring columns of one row: even lanes rows 0 and 2, odd lanes
+        // rows 1 and 3.
 #pragma unroll
         for (int b = 0; b < CNTV; ++b) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const float send = odd ? oc[b][2 * i] : oc[b][2 * i + 1];
-            const float recv = bits_float(__builtin_amdgcn_mov_dpp(float_bits(send), 0xB1, 0xF, 0xF, false));
-            const uint32_t w = odd ? pack_bf16x2(a.scale * recv, a.scale * oc[b][2 * i + 1])
-                                   : pack_bf16x2(a.scale * oc[b][2 * i], a.scale * recv);
-            __builtin_amdgcn_raw_buffer_store_b32((int)w, rso, ovoff2, 2 * i * rowo + 32 * b, 0);
-          }
+          f32x4 v = oc[b];
+          if (a.scale != 1.0f) v = v * a.scale;
+          const uint32_t p01 = pack_bf16x2(v[0], v[1]), p23 = pack_bf16x2(v[2], v[3]);
+          const uint32_t q01 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p01, 0xB1, 0xF, 0xF, false);
+          const uint32_t q23 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p23, 0xB1, 0xF, 0xF, false);
+          __builtin_amdgcn_raw_buffer_store_b32((int)__builtin_amdgcn_perm(q01, p01, psel), rso, ovoff2, 32 * b, 0);
+          __builtin_amdgcn_raw_buffer_store_b32((int)__builtin_amdgcn_perm(q23, p23, psel), rso, ovoff2,
+                                                2 * rowo + 32 * b, 0);
         }
       }
       // S <- Diag(e^{G_15}) S + (K e^{G_15 - G})^T V~
