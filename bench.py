@@ -124,8 +124,8 @@ def copy_calibration(n_bytes: int = 1 << 30):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--workload", default="train8k")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -176,7 +176,8 @@ def main(argv=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    launch_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    kernel_ms = sum(launch_ms) / args.steps
     log(f"bench: {args.steps} steps, wall {ms_per_step:.3f} ms/step, event {kernel_ms:.3f} ms/launch")
 
     tok_heads = n_tokens * w.H
@@ -217,6 +218,9 @@ def main(argv=None):
         "mfma_peak_frac": flops / (kernel_ms / 1e3) / (BF16_DENSE_PEAK_TFLOPS * 1e12)
         if w.dtype_name == "bf16" else flops / (kernel_ms / 1e3) / (FP32_MATRIX_PEAK_TFLOPS * 1e12),
         "kernel_ms": kernel_ms,
+        "kernel_ms_median": launch_ms[len(launch_ms) // 2],
+        "kernel_ms_min": launch_ms[0],
+        "kernel_ms_max": launch_ms[-1],
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

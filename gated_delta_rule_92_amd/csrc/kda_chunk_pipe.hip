@@ -414,45 +414,66 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
       const float* bet = reinterpret_cast<const float*>(sl + sBeta);
       const float* egc = reinterpret_cast<const float*>(sl + sEgc);
 
+      // This tile's operand fragments, all requested at once.
+      frag kgf[PDK / 32][2], qgf[PDK / 32][2], ktf[NCT];
+      f32x4 egv[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) egv[ct] = *reinterpret_cast<const f32x4*>(egc + 16 * ct + 4 * g4);
+#pragma unroll
+      for (int ks = 0; ks < PDK / 32; ++ks) {
+        kgf[ks][0] = load_frag(Kg + m * RS + 32 * ks + 4 * g4);
+        kgf[ks][1] = load_frag(Kg + m * RS + 32 * ks + 16 + 4 * g4);
+      }
+      const f32x4 bb = *reinterpret_cast<const f32x4*>(bet + 4 * g4);
+      const frag tf = load_frag(T + m * TS + 4 * g4);
+      f32x4 vv[CNTV];
+#pragma unroll
+      for (int b = 0; b < CNTV; ++b) vv[b] = load4_f32(VT + (vc0 + 16 * b + m) * TS + 4 * g4);
+      const frag aq = load_frag(Aqk + m * TS + 4 * g4);
+#pragma unroll
+      for (int ks = 0; ks < PDK / 32; ++ks) {
+        qgf[ks][0] = load_frag(Qg + m * RS + 32 * ks + 4 * g4);
+        qgf[ks][1] = load_frag(Qg + m * RS + 32 * ks + 16 + 4 * g4);
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) ktf[ct] = load_frag(KtT + (16 * ct + m) * TS + 4 * g4);
+
+      // bf16 copy of S for this tile's products, then the tile's decay of S
+      // in place (independent of the products, so it overlaps them)
       frag Sf[NCT][CNTV];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int b = 0; b < CNTV; ++b) Sf[ct][b] = M::make(S[ct][b]);
+        for (int b = 0; b < CNTV; ++b) {
+          Sf[ct][b] = M::make(S[ct][b]);
+          S[ct][b] = S[ct][b] * egv[ct];
+        }
 
       // Y = V - (e^G K) S ;  V~ = T (beta * Y)
       f32x4 acc[CNTV];
 #pragma unroll
       for (int b = 0; b < CNTV; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < PDK / 32; ++ks) {
-        const frag a0 = load_frag(Kg + m * RS + 32 * ks + 4 * g4);
-        const frag a1 = load_frag(Kg + m * RS + 32 * ks + 16 + 4 * g4);
+      for (int ks = 0; ks < PDK / 32; ++ks)
 #pragma unroll
-        for (int b = 0; b < CNTV; ++b) acc[b] = M::k32(a0, a1, Sf[2 * ks][b], Sf[2 * ks + 1][b], acc[b]);
-      }
-      const f32x4 bb = *reinterpret_cast<const f32x4*>(bet + 4 * g4);
-      const frag tf = load_frag(T + m * TS + 4 * g4);
+        for (int b = 0; b < CNTV; ++b)
+          acc[b] = M::k32(kgf[ks][0], kgf[ks][1], Sf[2 * ks][b], Sf[2 * ks + 1][b], acc[b]);
       frag Xf[CNTV];
 #pragma unroll
       for (int b = 0; b < CNTV; ++b) {
-        const f32x4 vv = load4_f32(VT + (vc0 + 16 * b + m) * TS + 4 * g4);
-        const f32x4 y = (vv - acc[b]) * bb;
+        const f32x4 y = (vv[b] - acc[b]) * bb;
         Xf[b] = M::make(M::k16(tf, M::make(y), f32x4{0.f, 0.f, 0.f, 0.f}));
       }
       // O = A_qk V~ + (e^G Q) S
       {
         f32x4 oc[CNTV];
-        const frag aq = load_frag(Aqk + m * TS + 4 * g4);
 #pragma unroll
         for (int b = 0; b < CNTV; ++b) oc[b] = M::k16(aq, Xf[b], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int ks = 0; ks < PDK / 32; ++ks) {
-          const frag a0 = load_frag(Qg + m * RS + 32 * ks + 4 * g4);
-          const frag a1 = load_frag(Qg + m * RS + 32 * ks + 16 + 4 * g4);
+        for (int ks = 0; ks < PDK / 32; ++ks)
 #pragma unroll
-          for (int b = 0; b < CNTV; ++b) oc[b] = M::k32(a0, a1, Sf[2 * ks][b], Sf[2 * ks + 1][b], oc[b]);
-        }
+          for (int b = 0; b < CNTV; ++b)
+            oc[b] = M::k32(qgf[ks][0], qgf[ks][1], Sf[2 * ks][b], Sf[2 * ks + 1][b], oc[b]);
         const __amdgpu_buffer_rsrc_t rso =
             make_rsrc(o + ((size_t)t0 * H + h) * PDV, (uint32_t)((L - 1) * H + 1) * PDV * 2);
         // Each lane packs its rows (0,1) and (2,3) into bf16 pairs, adjacent
@@ -471,14 +492,11 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
                                                 2 * rowo + 32 * b, 0);
         }
       }
-      // S <- Diag(e^{G_15}) S + (K e^{G_15 - G})^T V~
+      // S <- Diag(e^{G_15}) S + (K e^{G_15 - G})^T V~  (the decay is applied above)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const f32x4 eg = *reinterpret_cast<const f32x4*>(egc + 16 * ct + 4 * g4);
-        const frag ka = load_frag(KtT + (16 * ct + m) * TS + 4 * g4);
+      for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int b = 0; b < CNTV; ++b) S[ct][b] = M::k16(ka, Xf[b], S[ct][b] * eg);
-      }
+        for (int b = 0; b < CNTV; ++b) S[ct][b] = M::k16(ktf[ct], Xf[b], S[ct][b]);
       __builtin_amdgcn_s_waitcnt(0xc07f);
       signal_add(&done[slot], lane);
     }
