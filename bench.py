@@ -129,6 +129,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="train8k")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--split", type=int, default=1,
+                    help="cut every sequence into this many segments that run in parallel "
+                         "(state maps + composition + re-run); 1 = the plain forward")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -141,7 +144,7 @@ def main(argv=None):
         copy_calibration()
         return 0
 
-    from gated_delta_rule_92_amd import chunk_fwd, workspace_size
+    from gated_delta_rule_92_amd import chunk_fwd, chunk_fwd_split, workspace_size
     from gated_delta_rule_92_amd.inputs import make_workload
 
     dev = torch.device("cuda:0")
@@ -157,6 +160,10 @@ def main(argv=None):
     hT = torch.empty((N, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
 
     def step():
+        if args.split > 1:
+            chunk_fwd_split(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"], d["cu_seqlens"],
+                            segments=args.split, gate="logits", g_min=w.g_min, chunk=w.chunk)
+            return
         chunk_fwd(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"], d["cu_seqlens"],
                   gate="logits", g_min=w.g_min, chunk=w.chunk, o=o, final_state=hT,
                   workspace=workspace)
@@ -212,7 +219,7 @@ def main(argv=None):
         "config": {"workload": w.name, "batch": int(d["q"].shape[0]), "seq_len": w.T, "heads": w.H,
                    "d_k": w.Dk, "d_v": w.Dv, "chunk": w.chunk, "gate": "logits",
                    "g_min": w.g_min, "initial_state": d["h0"] is not None,
-                   "sequences": N},
+                   "sequences": N, "segments": args.split},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "mfma_peak_frac": flops / (kernel_ms / 1e3) / (BF16_DENSE_PEAK_TFLOPS * 1e12)

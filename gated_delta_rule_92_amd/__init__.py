@@ -6,7 +6,12 @@ Public API (thin wrappers over the C ABI in include/kda.h):
     chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
               gate="logdecay", A_log=None, g_min=-5.0, chunk=64, scale=1.0)
     recurrent_step(q, k, v, g, beta, state, gate="logdecay", ...)
+    transition(k, g, beta, cu_seqlens=None, gate="logdecay", ...)
+    compose_states(M, b, initial_state, nseq, P)
+    chunk_fwd_split(q, k, v, g, beta, initial_state=None, cu_seqlens=None, segments=8, ...)
 """
-from .ops import chunk_fwd, gate, recurrent_step, workspace_size  # noqa: F401
+from .ops import (chunk_fwd, chunk_fwd_split, compose_states, gate, recurrent_step,  # noqa: F401
+                  split_lengths, transition, workspace_size)
 
-__all__ = ["chunk_fwd", "gate", "recurrent_step", "workspace_size"]
+__all__ = ["chunk_fwd", "chunk_fwd_split", "compose_states", "gate", "recurrent_step",
+           "split_lengths", "transition", "workspace_size"]

@@ -19,7 +19,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libkda.so")
 ARCH = "gfx950"
 
-SOURCES = ["kda_api.cpp", "kda_gate.hip", "kda_recurrent.hip", "kda_chunk.hip", "kda_chunk_pipe.hip"]
+SOURCES = ["kda_api.cpp", "kda_gate.hip", "kda_recurrent.hip", "kda_chunk.hip", "kda_chunk_pipe.hip",
+           "kda_compose.hip"]
 
 # Packed fp32 VALU instructions are disabled for every device compile.
 # Matrix-core results are kept in ordinary VGPRs (-amdgpu-mfma-vgpr-form), which

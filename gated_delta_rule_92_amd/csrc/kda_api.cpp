@@ -97,7 +97,8 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtyp
       gate_input != KDA_GATE_LOGITS)
     return KDA_ERROR_INVALID_VALUE;
   if (gate_input == KDA_GATE_LOGITS && !(g_min < 0.0f)) return KDA_ERROR_INVALID_VALUE;
-  if (s.Ttot > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERROR_INVALID_VALUE;
+  if (s.Ttot > 0 && (!q || !k || !v || !g || !beta)) return KDA_ERROR_INVALID_VALUE;
+  if (!o && !final_state) return KDA_ERROR_INVALID_VALUE;  // nothing to compute
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o) ||
       !aligned16(initial_state) || !aligned16(final_state))
     return KDA_ERROR_INVALID_VALUE;
@@ -143,6 +144,61 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtyp
   r.h0 = initial_state; r.hT = final_state; r.o = o;
   r.seqs = s; r.H = H; r.Dk = Dk; r.Dv = Dv; r.scale = scale; r.bf16 = bf16;
   return launch_status(kda::launch_recurrent(r, hs));
+}
+
+kda_status_t kda_chunk_transition(const void* k, kda_dtype_t dtype, const float* g,
+                                  kda_gate_input_t gate_input, const float* A_log, float g_min,
+                                  const float* beta, const int32_t* cu_seqlens, int N, int B,
+                                  int T, int H, int Dk, int chunk, float* M, void* workspace,
+                                  size_t workspace_bytes, kda_stream_t stream) {
+  kda::Seqs s;
+  kda_status_t st = check_seqs(cu_seqlens, N, B, T, &s);
+  if (st != KDA_SUCCESS) return st;
+  if (!cu_seqlens && N != B) return KDA_ERROR_INVALID_VALUE;
+  if (H <= 0 || Dk <= 0 || chunk <= 0) return KDA_ERROR_INVALID_VALUE;
+  if (dtype != KDA_FLOAT32 && dtype != KDA_BFLOAT16) return KDA_ERROR_INVALID_VALUE;
+  if (gate_input != KDA_GATE_LOGDECAY && gate_input != KDA_GATE_CUMSUM &&
+      gate_input != KDA_GATE_LOGITS)
+    return KDA_ERROR_INVALID_VALUE;
+  if (gate_input == KDA_GATE_LOGITS && !(g_min < 0.0f)) return KDA_ERROR_INVALID_VALUE;
+  if (!M) return KDA_ERROR_INVALID_VALUE;
+  if (s.Ttot > 0 && (!k || !g || !beta)) return KDA_ERROR_INVALID_VALUE;
+  if (!aligned16(k) || !aligned16(g) || !aligned16(M)) return KDA_ERROR_INVALID_VALUE;
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) % kWorkspaceAlign) != 0)
+    return KDA_ERROR_INVALID_VALUE;
+  const bool bf16 = dtype == KDA_BFLOAT16;
+  if (!kda::chunk_pipe_supported(bf16, Dk, Dk, chunk)) return KDA_ERROR_NOT_SUPPORTED;
+  if (gate_input == KDA_GATE_LOGITS && g_min < kda::kMinFusedGmin) return KDA_ERROR_NOT_SUPPORTED;
+  size_t need = 0;
+  st = kda_chunk_fwd_workspace_size(B, T, H, Dk, Dk, s.N, chunk, dtype, &need);
+  if (st != KDA_SUCCESS) return st;
+  if (workspace && workspace_bytes < need) return KDA_ERROR_INSUFFICIENT_WORKSPACE;
+  if (s.N == 0) return KDA_SUCCESS;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  kda::ChunkArgs a;
+  a.q = nullptr; a.k = k; a.v = nullptr; a.g = g; a.gate_mode = (int)gate_input;
+  a.A_log = A_log; a.g_min = g_min; a.beta = beta;
+  a.h0 = nullptr; a.hT = M; a.o = nullptr;
+  a.seqs = s; a.order = nullptr;
+  a.H = H; a.Dk = Dk; a.Dv = Dk; a.scale = 1.0f; a.bf16 = bf16;
+  if (cu_seqlens && workspace && need > 0 && s.N > 1) {
+    int32_t* order = static_cast<int32_t*>(workspace);
+    hipError_t e = kda::launch_order(cu_seqlens, s.N, order, hs);
+    if (e != hipSuccess) return KDA_ERROR_LAUNCH_FAILURE;
+    a.order = order;
+  }
+  return launch_status(kda::launch_chunk_transition(a, hs));
+}
+
+kda_status_t kda_compose_states(const float* M, const float* b, const float* initial_state,
+                                int nseq, int P, int H, int Dk, int Dv, float* starts,
+                                kda_stream_t stream) {
+  if (nseq < 0 || P < 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_ERROR_INVALID_VALUE;
+  if (nseq > 0 && P > 0 && (!starts || (P > 1 && (!M || !b)))) return KDA_ERROR_INVALID_VALUE;
+  if (Dk > 256) return KDA_ERROR_NOT_SUPPORTED;
+  if ((size_t)nseq * P * H > (size_t)0x7fffffff) return KDA_ERROR_INVALID_VALUE;
+  return launch_status(kda::launch_compose(M, b, initial_state, nseq, P, H, Dk, Dv, starts,
+                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
 kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v, kda_dtype_t dtype,

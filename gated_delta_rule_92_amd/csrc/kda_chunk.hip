@@ -545,8 +545,9 @@ __global__ void __launch_bounds__(64 * waves_for<DV>(), 1) chunk_fused_kernel(Ch
 
     // O = A_qk V~ + (Gamma*Q) S; rows past the chunk's end are dropped by the
     // buffer range check.
+    // no output requested (o == NULL): a zero-size range drops every store
     const __amdgpu_buffer_rsrc_t rso =
-        make_rsrc(o + ((size_t)tok0 * H + h) * DV, (uint32_t)((Lr - 1) * H + 1) * DV * sizeof(T));
+        make_rsrc(o + ((size_t)tok0 * H + h) * DV, o ? (uint32_t)((Lr - 1) * H + 1) * DV * sizeof(T) : 0u);
     const int ovoff = (4 * g4) * rowv + (vc0 + m) * (int)sizeof(T);
 #pragma unroll
     for (int I = 0; I < 4; ++I) {

@@ -117,7 +117,11 @@ __device__ __forceinline__ uint32_t perm_hi16(uint32_t a, uint32_t b) {
   return (a >> 16) | (b & 0xffff0000u);
 }
 
-template <int GATE>
+// TRANS = false: the forward (o, final state). TRANS = true: the state
+// transition of each (sequence, head), M with S_final = M S_initial +
+// S_final(S_initial = 0), written to a.hT. It runs the same recurrence with
+// v = 0 starting from S = I; q, v, o and h0 are not read.
+template <int GATE, bool TRANS>
 __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
   using M = Mma<__bf16>;
   using frag = M::frag;
@@ -184,8 +188,10 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         rk[r] = __builtin_amdgcn_raw_buffer_load_b64(rsk, vk, r * rowk, 0);
-        rq[r] = __builtin_amdgcn_raw_buffer_load_b64(rsq, vk, r * rowk, 0);
-        rv[r] = __builtin_amdgcn_raw_buffer_load_b64(rsv, vk, r * rowk, 0);
+        if constexpr (!TRANS) {
+          rq[r] = __builtin_amdgcn_raw_buffer_load_b64(rsq, vk, r * rowk, 0);
+          rv[r] = __builtin_amdgcn_raw_buffer_load_b64(rsv, vk, r * rowk, 0);
+        }
         if constexpr (GATE == kGateCumsum) {
           // cumulative-sum input: rows past the end repeat the last row, so
           // that their value equals the tile's final one
@@ -265,20 +271,23 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
         float kk[4], qq[4], kg[4], qg[4], kd[4];
         unpack_bf16x2((uint32_t)rk[r].x, kk[0], kk[1]);
         unpack_bf16x2((uint32_t)rk[r].y, kk[2], kk[3]);
-        unpack_bf16x2((uint32_t)rq[r].x, qq[0], qq[1]);
-        unpack_bf16x2((uint32_t)rq[r].y, qq[2], qq[3]);
+        if constexpr (!TRANS) {
+          unpack_bf16x2((uint32_t)rq[r].x, qq[0], qq[1]);
+          unpack_bf16x2((uint32_t)rq[r].y, qq[2], qq[3]);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float G = Gl[r][j] + off[j];
           const float E = ex2(G);
           kg[j] = kk[j] * E;
-          qg[j] = qq[j] * E;
+          if constexpr (!TRANS) qg[j] = qq[j] * E;
           kd[j] = kk[j] * ex2(-G);
           kt[r][j] = kd[j] * eg[j];
         }
         const int o = (r0 + r) * RS + 4 * cq;
         *reinterpret_cast<uint2*>(sl + sKg + o * 2) = uint2{pack_bf16x2(kg[0], kg[1]), pack_bf16x2(kg[2], kg[3])};
-        *reinterpret_cast<uint2*>(sl + sQg + o * 2) = uint2{pack_bf16x2(qg[0], qg[1]), pack_bf16x2(qg[2], qg[3])};
+        if constexpr (!TRANS)
+          *reinterpret_cast<uint2*>(sl + sQg + o * 2) = uint2{pack_bf16x2(qg[0], qg[1]), pack_bf16x2(qg[2], qg[3])};
         *reinterpret_cast<uint2*>(reinterpret_cast<char*>(Kd) + o * 2) =
             uint2{pack_bf16x2(kd[0], kd[1]), pack_bf16x2(kd[2], kd[3])};
       }
@@ -294,12 +303,15 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
 #pragma unroll
         for (int r = 0; r < 8; r += 2) {
           w[r / 2] = pack_bf16x2(kt[r][j], kt[r + 1][j]);
-          const uint32_t a0 = (uint32_t)(j < 2 ? rv[r].x : rv[r].y);
-          const uint32_t a1 = (uint32_t)(j < 2 ? rv[r + 1].x : rv[r + 1].y);
-          u[r / 2] = (j & 1) ? perm_hi16(a0, a1) : perm_lo16(a0, a1);
+          if constexpr (!TRANS) {
+            const uint32_t a0 = (uint32_t)(j < 2 ? rv[r].x : rv[r].y);
+            const uint32_t a1 = (uint32_t)(j < 2 ? rv[r + 1].x : rv[r + 1].y);
+            u[r / 2] = (j & 1) ? perm_hi16(a0, a1) : perm_lo16(a0, a1);
+          }
         }
         *reinterpret_cast<uint4*>(sl + sKtT + (c * TS + r0) * 2) = uint4{w[0], w[1], w[2], w[3]};
-        *reinterpret_cast<uint4*>(sl + sVT + (c * TS + r0) * 2) = uint4{u[0], u[1], u[2], u[3]};
+        if constexpr (!TRANS)
+          *reinterpret_cast<uint4*>(sl + sVT + (c * TS + r0) * 2) = uint4{u[0], u[1], u[2], u[3]};
       }
       if (lane < PT) reinterpret_cast<float*>(sl + sBeta)[lane] = rb;
       // the next tile of this producer loads while this one is finished
@@ -322,7 +334,8 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
         const frag k0 = load_frag(Kg + m * RS + ca), k1 = load_frag(Kg + m * RS + ca + 16);
         dk = M::k32(d0, d1, k0, k1, dk);
         dn = M::k32(k0, k1, d0, d1, dn);
-        dq = M::k32(d0, d1, load_frag(Qg + m * RS + ca), load_frag(Qg + m * RS + ca + 16), dq);
+        if constexpr (!TRANS)
+          dq = M::k32(d0, d1, load_frag(Qg + m * RS + ca), load_frag(Qg + m * RS + ca + 16), dq);
       }
       // A = StrictTril(Diag(beta) raw) in the accumulator layout (An) and its
       // transpose (At); A_qk keeps the diagonal.
@@ -339,7 +352,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
           An[e] = m < i ? bi[e] * dn[e] : 0.f;
           aq[e] = i <= m ? dq[e] : 0.f;
         }
-        store4(reinterpret_cast<__bf16*>(sl + sAqk) + m * TS + 4 * g4, aq);
+        if constexpr (!TRANS) store4(reinterpret_cast<__bf16*>(sl + sAqk) + m * TS + 4 * g4, aq);
       }
       // T = (I + A)^{-1}. A is strictly lower triangular, so A^16 = 0 and
       // (I + A)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8), a product of
@@ -381,7 +394,15 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int b = 0; b < CNTV; ++b) S[ct][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (a.h0) {
+    if constexpr (TRANS) {
+      // the identity: row 16ct+4g4+e, column vc0+16b+m
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int b = 0; b < CNTV; ++b)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) S[ct][b][e] = (16 * ct + 4 * g4 + e == vc0 + 16 * b + m) ? 1.f : 0.f;
+    } else if (a.h0) {
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.h0 + sbase, PDK * PDV * 4);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
@@ -393,6 +414,8 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
                 __builtin_amdgcn_raw_buffer_load_b32(rs, svoff, ((16 * ct + e) * PDV + 16 * b) * 4, 0));
     }
     const int rowo = H * PDV * 2;
+    // with o == NULL only the final state is produced
+    const bool want_o = !TRANS && o != nullptr;
     // output stores: byte selectors of v_perm (partner pair, own pair) and the
     // lane's row / column-pair offset
     const bool odd = m & 1;
@@ -428,12 +451,16 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
       const frag tf = load_frag(T + m * TS + 4 * g4);
       f32x4 vv[CNTV];
 #pragma unroll
-      for (int b = 0; b < CNTV; ++b) vv[b] = load4_f32(VT + (vc0 + 16 * b + m) * TS + 4 * g4);
-      const frag aq = load_frag(Aqk + m * TS + 4 * g4);
+      for (int b = 0; b < CNTV; ++b)
+        vv[b] = TRANS ? f32x4{0.f, 0.f, 0.f, 0.f} : load4_f32(VT + (vc0 + 16 * b + m) * TS + 4 * g4);
+      frag aq = {};
+      if (want_o) {
+        aq = load_frag(Aqk + m * TS + 4 * g4);
 #pragma unroll
-      for (int ks = 0; ks < PDK / 32; ++ks) {
-        qgf[ks][0] = load_frag(Qg + m * RS + 32 * ks + 4 * g4);
-        qgf[ks][1] = load_frag(Qg + m * RS + 32 * ks + 16 + 4 * g4);
+        for (int ks = 0; ks < PDK / 32; ++ks) {
+          qgf[ks][0] = load_frag(Qg + m * RS + 32 * ks + 4 * g4);
+          qgf[ks][1] = load_frag(Qg + m * RS + 32 * ks + 16 + 4 * g4);
+        }
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) ktf[ct] = load_frag(KtT + (16 * ct + m) * TS + 4 * g4);
@@ -465,7 +492,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
         Xf[b] = M::make(M::k16(tf, M::make(y), f32x4{0.f, 0.f, 0.f, 0.f}));
       }
       // O = A_qk V~ + (e^G Q) S
-      {
+      if (want_o) {
         f32x4 oc[CNTV];
 #pragma unroll
         for (int b = 0; b < CNTV; ++b) oc[b] = M::k16(aq, Xf[b], f32x4{0.f, 0.f, 0.f, 0.f});
@@ -520,20 +547,31 @@ bool chunk_pipe_supported(bool bf16, int Dk, int Dv, int chunk) {
   return bf16 && Dk == PDK && Dv == PDV && chunk == 64;
 }
 
-hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t stream) {
-  if (a.seqs.N == 0 || a.H == 0) return hipSuccess;
+template <bool TRANS>
+static void launch_pipe_t(const ChunkArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)(a.seqs.N * a.H)), block(PNTHR);
   switch (a.gate_mode) {
     case kGateLogDecay:
-      hipLaunchKernelGGL(chunk_pipe_kernel<kGateLogDecay>, grid, block, 0, stream, a);
+      hipLaunchKernelGGL((chunk_pipe_kernel<kGateLogDecay, TRANS>), grid, block, 0, stream, a);
       break;
     case kGateCumsum:
-      hipLaunchKernelGGL(chunk_pipe_kernel<kGateCumsum>, grid, block, 0, stream, a);
+      hipLaunchKernelGGL((chunk_pipe_kernel<kGateCumsum, TRANS>), grid, block, 0, stream, a);
       break;
     default:
-      hipLaunchKernelGGL(chunk_pipe_kernel<kGateLogits>, grid, block, 0, stream, a);
+      hipLaunchKernelGGL((chunk_pipe_kernel<kGateLogits, TRANS>), grid, block, 0, stream, a);
       break;
   }
+}
+
+hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t stream) {
+  if (a.seqs.N == 0 || a.H == 0) return hipSuccess;
+  launch_pipe_t<false>(a, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_transition(const ChunkArgs& a, hipStream_t stream) {
+  if (a.seqs.N == 0 || a.H == 0) return hipSuccess;
+  launch_pipe_t<true>(a, stream);
   return hipGetLastError();
 }
 

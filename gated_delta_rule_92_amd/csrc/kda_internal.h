@@ -67,6 +67,12 @@ bool chunk_fused_supported(bool bf16, int Dk, int Dv, int chunk);
 // Pipelined producer/consumer chunk kernel (bf16, Dk = Dv = 128).
 bool chunk_pipe_supported(bool bf16, int Dk, int Dv, int chunk);
 hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t stream);
+// Same kernel in transition mode: writes M (a.hT, [N, H, Dk, Dk]) with
+// S_final = M S_initial + S_final(0); reads k, g and beta only.
+hipError_t launch_chunk_transition(const ChunkArgs& a, hipStream_t stream);
+// Chains segment maps: starts[0] = S0, starts[p+1] = M_p starts[p] + b_p.
+hipError_t launch_compose(const float* M, const float* b, const float* S0, int nseq, int P,
+                          int H, int Dk, int Dv, float* starts, hipStream_t stream);
 // Lowest per-token log-decay the chunk path handles (16 * 5.5 = 88 < 88.7 = ln FLT_MAX).
 constexpr float kMinFusedGmin = -5.5f;
 hipError_t launch_chunk_fused(const ChunkArgs& a, hipStream_t stream);

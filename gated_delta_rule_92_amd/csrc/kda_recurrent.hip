@@ -103,7 +103,7 @@ __global__ void __launch_bounds__(256) recurrent_kernel(RecurrentArgs a) {
     }
     s_red1[p][jl] = opart;
     __syncthreads();
-    if (p == 0 && jvalid) {
+    if (p == 0 && jvalid && o) {
       float ov = 0.f;
 #pragma unroll
       for (int pp = 0; pp < kRecParts; ++pp) ov += s_red1[pp][jl];

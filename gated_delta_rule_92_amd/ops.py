@@ -83,12 +83,13 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               A_log: Optional[torch.Tensor] = None, g_min: float = -5.0, chunk: int = 64,
               scale: float = 1.0, output_final_state: bool = True,
               o: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None
-              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              workspace: Optional[torch.Tensor] = None, output: bool = True
+              ) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
     """Chunkwise KDA forward. q, k: [B, T, H, Dk]; v: [B, T, H, Dv] (bf16 or
     fp32); g: fp32 [B, T, H, Dk] (log-decay, its chunk cumsum, or logits per
     `gate`); beta: fp32 [B, T, H]; initial_state: fp32 [N, H, Dk, Dv].
-    Returns (o, final_state)."""
+    Returns (o, final_state); with output=False only the final state is
+    computed and o is None."""
     lib = _lib.load()
     dev = q.device
     dt = q.dtype
@@ -112,9 +113,13 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
             raise ValueError("initial_state must be [N, H, Dk, Dv]")
     if A_log is not None:
         _need(A_log, "A_log", torch.float32, dev)
-    if o is None:
+    if not output:
+        o = None
+        output_final_state = True
+    elif o is None:
         o = torch.empty((B, T, H, Dv), dtype=dt, device=dev)
-    _need(o, "o", dt, dev)
+    if o is not None:
+        _need(o, "o", dt, dev)
     if output_final_state and final_state is None:
         final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
     if final_state is not None:
@@ -130,6 +135,122 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
                                _ptr(o), _ptr(final_state), _ptr(workspace), ws_len, _stream(dev))
     _lib.check(rc, "kda_chunk_fwd")
     return o, final_state
+
+
+def transition(k: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+               cu_seqlens: Optional[torch.Tensor] = None, gate: str = "logdecay",
+               A_log: Optional[torch.Tensor] = None, g_min: float = -5.0, chunk: int = 64,
+               M: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+               ) -> torch.Tensor:
+    """State map of each (sequence, head): fp32 M [N, H, Dk, Dk] with
+    S_final = M @ S_initial + S_final(S_initial = 0). k: [B, T, H, Dk] bf16."""
+    lib = _lib.load()
+    dev = k.device
+    _need(k, "k", None, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    B, T, H, Dk = k.shape
+    if g.shape != k.shape or beta.shape != k.shape[:3]:
+        raise ValueError("shape mismatch among k, g, beta")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if A_log is not None:
+        _need(A_log, "A_log", torch.float32, dev)
+    if M is None:
+        M = torch.empty((N, H, Dk, Dk), dtype=torch.float32, device=dev)
+    _need(M, "M", torch.float32, dev)
+    ws_bytes = workspace_size(B, T, H, Dk, Dk, N, chunk, k.dtype)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        rc = lib.kda_chunk_transition(_ptr(k), _dtype_code(k), _ptr(g), _GATES[gate], _ptr(A_log),
+                                      float(g_min), _ptr(beta), _ptr(cu_seqlens), N, B, T, H, Dk,
+                                      int(chunk), _ptr(M), _ptr(workspace), ws_len, _stream(dev))
+    _lib.check(rc, "kda_chunk_transition")
+    return M
+
+
+def compose_states(M: torch.Tensor, b: torch.Tensor, initial_state: Optional[torch.Tensor],
+                   nseq: int, P: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Entry states of P consecutive segments per sequence: starts[s*P] =
+    initial_state[s], starts[s*P+p+1] = M[s*P+p] @ starts[s*P+p] + b[s*P+p].
+    M: fp32 [nseq*P, H, Dk, Dk]; b: fp32 [nseq*P, H, Dk, Dv]."""
+    lib = _lib.load()
+    dev = b.device
+    _need(M, "M", torch.float32, dev)
+    _need(b, "b", torch.float32, dev)
+    _, H, Dk, Dv = b.shape
+    if b.shape[0] != nseq * P or tuple(M.shape) != (nseq * P, H, Dk, Dk):
+        raise ValueError("M must be [nseq*P, H, Dk, Dk] and b [nseq*P, H, Dk, Dv]")
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, dev)
+        if tuple(initial_state.shape) != (nseq, H, Dk, Dv):
+            raise ValueError("initial_state must be [nseq, H, Dk, Dv]")
+    if out is None:
+        out = torch.empty_like(b)
+    _need(out, "out", torch.float32, dev)
+    with torch.cuda.device(dev):
+        rc = lib.kda_compose_states(_ptr(M), _ptr(b), _ptr(initial_state), nseq, P, H, Dk, Dv,
+                                    _ptr(out), _stream(dev))
+    _lib.check(rc, "kda_compose_states")
+    return out
+
+
+def split_lengths(lengths, segments: int, align: int = 64):
+    """Cut each sequence into `segments` consecutive pieces whose lengths are
+    multiples of `align` (the last piece takes the rest; pieces may be empty).
+    Returns the flat list of piece lengths, sequence by sequence."""
+    out = []
+    for L in lengths:
+        per = -(-int(L) // segments)
+        per = -(-per // align) * align
+        rest = int(L)
+        for p in range(segments):
+            n = rest if p == segments - 1 else min(per, rest)
+            out.append(n)
+            rest -= n
+    return out
+
+
+def chunk_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                    cu_seqlens: Optional[torch.Tensor] = None, segments: int = 8,
+                    gate: str = "logdecay", A_log: Optional[torch.Tensor] = None,
+                    g_min: float = -5.0, chunk: int = 64, scale: float = 1.0
+                    ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The chunk forward with every sequence cut into `segments` consecutive
+    pieces that run in parallel (the one-GPU form of a context split):
+      1. per piece, its state map M (kda_chunk_transition) and its final
+         state b from a zero start (kda_chunk_fwd without output);
+      2. the pieces' entry states, chained per sequence (kda_compose_states);
+      3. every piece again from its entry state, producing o.
+    Same results as chunk_fwd up to rounding. Returns (o, final_state), the
+    final state as a view of the last pieces' states."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if cu_seqlens is not None:
+        lengths = [int(x) for x in torch.diff(cu_seqlens.cpu().to(torch.int64)).tolist()]
+        qq, kk, vv, gg, bb = q, k, v, g, beta
+    else:
+        lengths = [T] * B
+        qq, kk, vv = (x.reshape(1, B * T, H, x.shape[-1]) for x in (q, k, v))
+        gg, bb = g.reshape(1, B * T, H, Dk), beta.reshape(1, B * T, H)
+    nseq = len(lengths)
+    pieces = split_lengths(lengths, segments, chunk)
+    cu = torch.zeros(len(pieces) + 1, dtype=torch.int64)
+    cu[1:] = torch.cumsum(torch.tensor(pieces, dtype=torch.int64), 0)
+    cu = cu.to(torch.int32).to(q.device)
+    common = dict(cu_seqlens=cu, gate=gate, A_log=A_log, g_min=g_min, chunk=chunk)
+    M = transition(kk, gg, bb, **common)
+    _, b = chunk_fwd(qq, kk, vv, gg, bb, None, output=False, scale=scale, **common)
+    starts = compose_states(M, b, initial_state, nseq, segments)
+    o, finals = chunk_fwd(qq, kk, vv, gg, bb, starts, scale=scale, **common)
+    o = o.reshape(q.shape[:3] + (Dv,))
+    return o, finals.view(nseq, segments, H, Dk, Dv)[:, segments - 1]
 
 
 def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

@@ -130,7 +130,8 @@ kda_status_t kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, i
  * cu_seqlens, N  packed sequences (B must be 1) or NULL (then N must equal B)
  * chunk      must be 64
  * scale      output scale (1.0 on the pages)
- * o          device dtype [B, T, H, Dv] (written)
+ * o          device dtype [B, T, H, Dv] (written), or NULL: then only the
+ *            final state is computed (final_state must then be non-NULL)
  * final_state device fp32 [N, H, Dk, Dv] or NULL (written); may alias
  *            initial_state
  * workspace  device, >= kda_chunk_fwd_workspace_size(...) bytes, or NULL
@@ -149,6 +150,49 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtyp
                            const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
                            int Dv, int chunk, float scale, void* o, float* final_state,
                            void* workspace, size_t workspace_bytes, kda_stream_t stream);
+
+/*
+ * kda_chunk_transition — the state map of each (sequence, head).
+ * The KDA equation is linear in the state [KDA-blog §Kimi Delta Attention,
+ * KDA equation], so the state a sequence leaves behind is affine in the state
+ * it starts from: S_final = M S_initial + S_final(S_initial = 0), with
+ * M = prod_t (I - beta_t k_t k_t^T) Diag(alpha_t) (latest token leftmost).
+ * This writes M, computed as the chunk forward with v = 0 from S = I. It is
+ * the per-segment half of a context split: a sequence cut into segments
+ * has its true segment entry states chained by kda_compose_states from each
+ * segment's M and its zero-start final state (kda_chunk_fwd with
+ * initial_state = NULL, o = NULL).
+ * k          device dtype [B, T, H, Dk]; q and v are not needed
+ * g, gate_input, A_log, g_min, beta, cu_seqlens, N, B, T, H, chunk
+ *            as for kda_chunk_fwd
+ * M          device fp32 [N, H, Dk, Dk] (written), row-major per (n, h)
+ * workspace  as for kda_chunk_fwd with Dv = Dk
+ * Supported: bf16, Dk = 128, chunk = 64, per-token log-decay >= -5.5
+ * (KDA_ERROR_NOT_SUPPORTED otherwise).
+ */
+kda_status_t kda_chunk_transition(const void* k, kda_dtype_t dtype, const float* g,
+                                  kda_gate_input_t gate_input, const float* A_log, float g_min,
+                                  const float* beta, const int32_t* cu_seqlens, int N, int B,
+                                  int T, int H, int Dk, int chunk, float* M, void* workspace,
+                                  size_t workspace_bytes, kda_stream_t stream);
+
+/*
+ * kda_compose_states — entry states of consecutive segments.
+ * For each of nseq sequences cut into P consecutive segments (segment p of
+ * sequence s at index s*P + p), with M_p its state map and b_p its zero-start
+ * final state: starts_0 = initial_state, starts_{p+1} = M_p starts_p + b_p.
+ * Running kda_chunk_fwd on each segment from its entry state then gives the
+ * same outputs and final state as the unsplit sequence.
+ * M              device fp32 [nseq*P, H, Dk, Dk] (entries p = P-1 unused)
+ * b              device fp32 [nseq*P, H, Dk, Dv] (entries p = P-1 unused)
+ * initial_state  device fp32 [nseq, H, Dk, Dv] or NULL (zeros)
+ * starts         device fp32 [nseq*P, H, Dk, Dv] (written)
+ * fp32 arithmetic, one workgroup per (sequence, head, 16 value columns),
+ * sequential over p. Supported: Dk <= 256.
+ */
+kda_status_t kda_compose_states(const float* M, const float* b, const float* initial_state,
+                                int nseq, int P, int H, int Dk, int Dv, float* starts,
+                                kda_stream_t stream);
 
 /*
  * kda_recurrent_step — one token of the KDA recurrence (decode), updating

@@ -54,7 +54,8 @@ def _chunk(**kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(q=None), dict(k=None), dict(v=None), dict(g=None), dict(beta=None), dict(o=None),
+    dict(q=None), dict(k=None), dict(v=None), dict(g=None), dict(beta=None),
+    dict(o=None),                       # neither o nor a final state: nothing to compute
     dict(B=0), dict(T=-1), dict(H=0), dict(Dk=0), dict(Dv=0), dict(chunk=0),
     dict(N=2),                          # N != B without cu_seqlens
     dict(cu=FAKE, B=2, N=2),            # cu_seqlens needs B == 1
@@ -109,6 +110,45 @@ def test_gate_and_step_validation():
     assert step(gate=1) == _lib.KDA_ERROR_INVALID_VALUE   # cumsum is meaningless for one token
     assert step(Dk=300) == _lib.KDA_ERROR_NOT_SUPPORTED
     assert step(N=0) == _lib.KDA_SUCCESS
+
+
+def test_transition_and_compose_validation():
+    lib = _lib.load()
+
+    def trans(**kw):
+        a = dict(k=FAKE, dtype=1, g=FAKE, gate=0, A=None, g_min=-5.0, beta=FAKE, cu=None, N=1, B=1,
+                 T=64, H=2, Dk=128, chunk=64, M=FAKE, ws=None, ws_bytes=0, stream=None)
+        a.update(kw)
+        return lib.kda_chunk_transition(*a.values())
+    for kw in (dict(M=None), dict(k=None), dict(g=None), dict(beta=None), dict(N=2), dict(H=0),
+               dict(k=FAKE + 4), dict(M=FAKE + 8), dict(gate=9), dict(gate=2, g_min=0.0)):
+        assert trans(**kw) == _lib.KDA_ERROR_INVALID_VALUE, kw
+    # the transition runs on the bf16 d = 128 pipelined kernel only
+    for kw in (dict(dtype=0), dict(Dk=64), dict(chunk=32), dict(gate=2, g_min=-8.0)):
+        assert trans(**kw) == _lib.KDA_ERROR_NOT_SUPPORTED, kw
+    assert trans(cu=FAKE, N=0, T=0) == _lib.KDA_SUCCESS
+
+    def comp(**kw):
+        a = dict(M=FAKE, b=FAKE, S0=None, nseq=1, P=4, H=2, Dk=128, Dv=128, out=FAKE, stream=None)
+        a.update(kw)
+        return lib.kda_compose_states(*a.values())
+    for kw in (dict(out=None), dict(M=None), dict(b=None), dict(H=0), dict(Dv=0), dict(P=-1)):
+        assert comp(**kw) == _lib.KDA_ERROR_INVALID_VALUE, kw
+    assert comp(Dk=300) == _lib.KDA_ERROR_NOT_SUPPORTED
+    assert comp(nseq=0) == _lib.KDA_SUCCESS
+
+
+def test_split_lengths_cover_each_sequence_in_aligned_pieces():
+    from gated_delta_rule_92_amd.ops import split_lengths
+    for lengths, P in (([262144], 8), ([1, 63, 64, 65, 1000, 0], 3), ([130, 7], 5)):
+        pieces = split_lengths(lengths, P)
+        assert len(pieces) == len(lengths) * P
+        for i, L in enumerate(lengths):
+            mine = pieces[i * P:(i + 1) * P]
+            assert sum(mine) == L and min(mine) >= 0
+            # every non-empty piece starts on a 64-token chunk boundary
+            starts = [sum(mine[:j]) for j in range(P) if mine[j] > 0]
+            assert all(st % 64 == 0 for st in starts)
 
 
 def test_python_binding_fails_loudly_without_gpu_tensors():

@@ -224,6 +224,63 @@ def test_split_and_resume():
     np.testing.assert_allclose(Sb, S, rtol=1e-13, atol=1e-13)
 
 
+def _state_map(k, g, beta):
+    """Per head, the product of the per-token state maps
+    (I - beta_t k_t k_t^T) Diag(e^{g_t}), latest token leftmost, written out
+    directly (numpy, fp64) for one sequence. Returns [H, Dk, Dk]."""
+    _, T, H, Dk = k.shape
+    out = np.empty((H, Dk, Dk))
+    for h in range(H):
+        Mh = np.eye(Dk)
+        for t in range(T):
+            kt = k[0, t, h]
+            step = (np.eye(Dk) - beta[0, t, h] * np.outer(kt, kt)) @ np.diag(np.exp(g[0, t, h]))
+            Mh = step @ Mh
+        out[h] = Mh
+    return out
+
+
+def test_state_map_is_affine_and_equals_the_product_of_token_maps():
+    """S_T(S_0) = M S_0 + S_T(0), with M the product of the per-token maps;
+    the run with v = 0 from S_0 = I yields M (what kda_chunk_transition
+    computes)."""
+    rng = np.random.default_rng(61)
+    q, k, v, g, beta = _rand_problem(rng, 1, 23, 2, 6, 5)
+    M = _state_map(k, g, beta)
+    eye = np.broadcast_to(np.eye(6), (1, 2, 6, 6)).copy()
+    _, M_run = oracle_recurrence(q, k, np.zeros((1, 23, 2, 6)), g, beta, eye)
+    np.testing.assert_allclose(M_run[0], M, rtol=1e-12, atol=1e-13)
+    S0 = rng.standard_normal((1, 2, 6, 5))
+    _, S_from = oracle_recurrence(q, k, v, g, beta, S0)
+    _, S_zero = oracle_recurrence(q, k, v, g, beta)
+    np.testing.assert_allclose(S_from[0], np.einsum("hij,hjc->hic", M, S0[0]) + S_zero[0],
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_segment_composition_equals_the_unsplit_run():
+    """A sequence cut into segments: entry states chained from each segment's
+    map and zero-start final state, then every segment re-run from its entry
+    state, reproduce the unsplit outputs and final state."""
+    rng = np.random.default_rng(62)
+    T, H, Dk, Dv = 100, 2, 6, 5
+    q, k, v, g, beta = _rand_problem(rng, 1, T, H, Dk, Dv)
+    S_init = rng.standard_normal((1, H, Dk, Dv))
+    o_ref, S_ref = oracle_recurrence(q, k, v, g, beta, S_init)
+    bounds = [0, 31, 32, 64, 100]   # includes a one-token segment
+    start = S_init[0]
+    outs = []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        sl = (slice(None), slice(a, b))
+        eye = np.broadcast_to(np.eye(Dk), (1, H, Dk, Dk)).copy()
+        _, M = oracle_recurrence(q[sl], k[sl], np.zeros((1, b - a, H, Dk)), g[sl], beta[sl], eye)
+        _, b0 = oracle_recurrence(q[sl], k[sl], v[sl], g[sl], beta[sl])
+        o_seg, _ = oracle_recurrence(q[sl], k[sl], v[sl], g[sl], beta[sl], start[None])
+        outs.append(o_seg)
+        start = np.einsum("hij,hjc->hic", M[0], start) + b0[0]
+    np.testing.assert_allclose(np.concatenate(outs, axis=1), o_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(start, S_ref[0], rtol=1e-11, atol=1e-12)
+
+
 def test_varlen_equals_independent_runs():
     """Packed sequences with cu_seqlens == independent per-sequence runs
     (bit-for-bit), including an empty sequence (final = initial)."""
