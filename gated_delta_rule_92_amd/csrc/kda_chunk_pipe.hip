@@ -117,12 +117,18 @@ __device__ __forceinline__ uint32_t perm_hi16(uint32_t a, uint32_t b) {
   return (a >> 16) | (b & 0xffff0000u);
 }
 
-// TRANS = false: the forward (o, final state). TRANS = true: the state
-// transition of each (sequence, head), M with S_final = M S_initial +
-// S_final(S_initial = 0), written to a.hT. It runs the same recurrence with
-// v = 0 starting from S = I; q, v, o and h0 are not read.
-template <int GATE, bool TRANS>
+// What one launch computes.
+//   kModeForward:   o and the final state.
+//   kModeStateOnly: the final state only (q is not read, o not written).
+//   kModeTransition: the state map of each (sequence, head), M with
+//     S_final = M S_initial + S_final(S_initial = 0), written to a.hT: the
+//     same recurrence with v = 0 starting from S = I (q, v, o, h0 unused).
+enum { kModeForward = 0, kModeStateOnly = 1, kModeTransition = 2 };
+
+template <int GATE, int MODE>
 __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
+  constexpr bool TRANS = MODE == kModeTransition;
+  constexpr bool NEEDQ = MODE == kModeForward;
   using M = Mma<__bf16>;
   using frag = M::frag;
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
@@ -188,10 +194,8 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         rk[r] = __builtin_amdgcn_raw_buffer_load_b64(rsk, vk, r * rowk, 0);
-        if constexpr (!TRANS) {
-          rq[r] = __builtin_amdgcn_raw_buffer_load_b64(rsq, vk, r * rowk, 0);
-          rv[r] = __builtin_amdgcn_raw_buffer_load_b64(rsv, vk, r * rowk, 0);
-        }
+        if constexpr (NEEDQ) rq[r] = __builtin_amdgcn_raw_buffer_load_b64(rsq, vk, r * rowk, 0);
+        if constexpr (!TRANS) rv[r] = __builtin_amdgcn_raw_buffer_load_b64(rsv, vk, r * rowk, 0);
         if constexpr (GATE == kGateCumsum) {
           // cumulative-sum input: rows past the end repeat the last row, so
           // that their value equals the tile's final one
@@ -271,7 +275,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
         float kk[4], qq[4], kg[4], qg[4], kd[4];
         unpack_bf16x2((uint32_t)rk[r].x, kk[0], kk[1]);
         unpack_bf16x2((uint32_t)rk[r].y, kk[2], kk[3]);
-        if constexpr (!TRANS) {
+        if constexpr (NEEDQ) {
           unpack_bf16x2((uint32_t)rq[r].x, qq[0], qq[1]);
           unpack_bf16x2((uint32_t)rq[r].y, qq[2], qq[3]);
         }
@@ -280,13 +284,13 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
           const float G = Gl[r][j] + off[j];
           const float E = ex2(G);
           kg[j] = kk[j] * E;
-          if constexpr (!TRANS) qg[j] = qq[j] * E;
+          if constexpr (NEEDQ) qg[j] = qq[j] * E;
           kd[j] = kk[j] * ex2(-G);
           kt[r][j] = kd[j] * eg[j];
         }
         const int o = (r0 + r) * RS + 4 * cq;
         *reinterpret_cast<uint2*>(sl + sKg + o * 2) = uint2{pack_bf16x2(kg[0], kg[1]), pack_bf16x2(kg[2], kg[3])};
-        if constexpr (!TRANS)
+        if constexpr (NEEDQ)
           *reinterpret_cast<uint2*>(sl + sQg + o * 2) = uint2{pack_bf16x2(qg[0], qg[1]), pack_bf16x2(qg[2], qg[3])};
         *reinterpret_cast<uint2*>(reinterpret_cast<char*>(Kd) + o * 2) =
             uint2{pack_bf16x2(kd[0], kd[1]), pack_bf16x2(kd[2], kd[3])};
@@ -334,7 +338,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
         const frag k0 = load_frag(Kg + m * RS + ca), k1 = load_frag(Kg + m * RS + ca + 16);
         dk = M::k32(d0, d1, k0, k1, dk);
         dn = M::k32(k0, k1, d0, d1, dn);
-        if constexpr (!TRANS)
+        if constexpr (NEEDQ)
           dq = M::k32(d0, d1, load_frag(Qg + m * RS + ca), load_frag(Qg + m * RS + ca + 16), dq);
       }
       // A = StrictTril(Diag(beta) raw) in the accumulator layout (An) and its
@@ -352,7 +356,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
           An[e] = m < i ? bi[e] * dn[e] : 0.f;
           aq[e] = i <= m ? dq[e] : 0.f;
         }
-        if constexpr (!TRANS) store4(reinterpret_cast<__bf16*>(sl + sAqk) + m * TS + 4 * g4, aq);
+        if constexpr (NEEDQ) store4(reinterpret_cast<__bf16*>(sl + sAqk) + m * TS + 4 * g4, aq);
       }
       // T = (I + A)^{-1}. A is strictly lower triangular, so A^16 = 0 and
       // (I + A)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8), a product of
@@ -415,7 +419,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
     }
     const int rowo = H * PDV * 2;
     // with o == NULL only the final state is produced
-    const bool want_o = !TRANS && o != nullptr;
+    constexpr bool want_o = NEEDQ;
     // output stores: byte selectors of v_perm (partner pair, own pair) and the
     // lane's row / column-pair offset
     const bool odd = m & 1;
@@ -547,31 +551,34 @@ bool chunk_pipe_supported(bool bf16, int Dk, int Dv, int chunk) {
   return bf16 && Dk == PDK && Dv == PDV && chunk == 64;
 }
 
-template <bool TRANS>
+template <int MODE>
 static void launch_pipe_t(const ChunkArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)(a.seqs.N * a.H)), block(PNTHR);
   switch (a.gate_mode) {
     case kGateLogDecay:
-      hipLaunchKernelGGL((chunk_pipe_kernel<kGateLogDecay, TRANS>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((chunk_pipe_kernel<kGateLogDecay, MODE>), grid, block, 0, stream, a);
       break;
     case kGateCumsum:
-      hipLaunchKernelGGL((chunk_pipe_kernel<kGateCumsum, TRANS>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((chunk_pipe_kernel<kGateCumsum, MODE>), grid, block, 0, stream, a);
       break;
     default:
-      hipLaunchKernelGGL((chunk_pipe_kernel<kGateLogits, TRANS>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((chunk_pipe_kernel<kGateLogits, MODE>), grid, block, 0, stream, a);
       break;
   }
 }
 
 hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t stream) {
   if (a.seqs.N == 0 || a.H == 0) return hipSuccess;
-  launch_pipe_t<false>(a, stream);
+  if (a.o)
+    launch_pipe_t<kModeForward>(a, stream);
+  else
+    launch_pipe_t<kModeStateOnly>(a, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_transition(const ChunkArgs& a, hipStream_t stream) {
   if (a.seqs.N == 0 || a.H == 0) return hipSuccess;
-  launch_pipe_t<true>(a, stream);
+  launch_pipe_t<kModeTransition>(a, stream);
   return hipGetLastError();
 }
 
