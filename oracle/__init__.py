@@ -17,3 +17,4 @@ from .oracle import (  # noqa: F401
     oracle_forward,
     library_path,
 )
+from .epilogue import oracle_gated_rmsnorm  # noqa: F401
