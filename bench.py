@@ -129,6 +129,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="train8k")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--epilogue", choices=["none", "fused", "separate"], default="none",
+                    help="add the output epilogue sigmoid(gate) * RMSNorm(o): fused into the "
+                         "chunk kernel, or as a second kernel after it")
     ap.add_argument("--split", type=int, default=1,
                     help="cut every sequence into this many segments that run in parallel "
                          "(state maps + composition + re-run); 1 = the plain forward")
@@ -144,7 +147,8 @@ def main(argv=None):
         copy_calibration()
         return 0
 
-    from gated_delta_rule_92_amd import chunk_fwd, chunk_fwd_split, workspace_size
+    from gated_delta_rule_92_amd import (chunk_fwd, chunk_fwd_gated, chunk_fwd_split, gated_rmsnorm,
+                                         workspace_size)
     from gated_delta_rule_92_amd.inputs import make_workload
 
     dev = torch.device("cuda:0")
@@ -159,7 +163,18 @@ def main(argv=None):
     o = torch.empty(d["v"].shape, dtype=w.dtype, device=dev)
     hT = torch.empty((N, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
 
+    if args.epilogue != "none":
+        gen = torch.Generator(device=dev).manual_seed(1)
+        out_gate = torch.randn(d["v"].shape, generator=gen, device=dev).to(w.dtype)
+        norm_w = torch.ones(w.Dv, device=dev)
+        y = torch.empty_like(o)
+
     def step():
+        if args.epilogue == "fused":
+            chunk_fwd_gated(d["q"], d["k"], d["v"], d["z"], d["beta"], out_gate, norm_w, 1e-6,
+                            d["h0"], d["cu_seqlens"], gate="logits", g_min=w.g_min, chunk=w.chunk,
+                            y=y, final_state=hT, workspace=workspace)
+            return
         if args.split > 1:
             chunk_fwd_split(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"], d["cu_seqlens"],
                             segments=args.split, gate="logits", g_min=w.g_min, chunk=w.chunk)
@@ -167,6 +182,8 @@ def main(argv=None):
         chunk_fwd(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"], d["cu_seqlens"],
                   gate="logits", g_min=w.g_min, chunk=w.chunk, o=o, final_state=hT,
                   workspace=workspace)
+        if args.epilogue == "separate":
+            gated_rmsnorm(o, out_gate, norm_w, 1e-6, y=y)
 
     for _ in range(args.warmup):
         step()
@@ -219,7 +236,7 @@ def main(argv=None):
         "config": {"workload": w.name, "batch": int(d["q"].shape[0]), "seq_len": w.T, "heads": w.H,
                    "d_k": w.Dk, "d_v": w.Dv, "chunk": w.chunk, "gate": "logits",
                    "g_min": w.g_min, "initial_state": d["h0"] is not None,
-                   "sequences": N, "segments": args.split},
+                   "sequences": N, "segments": args.split, "epilogue": args.epilogue},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "mfma_peak_frac": flops / (kernel_ms / 1e3) / (BF16_DENSE_PEAK_TFLOPS * 1e12)

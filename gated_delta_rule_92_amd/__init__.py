@@ -9,9 +9,11 @@ Public API (thin wrappers over the C ABI in include/kda.h):
     transition(k, g, beta, cu_seqlens=None, gate="logdecay", ...)
     compose_states(M, b, initial_state, nseq, P)
     chunk_fwd_split(q, k, v, g, beta, initial_state=None, cu_seqlens=None, segments=8, ...)
+    chunk_fwd_gated(q, k, v, g, beta, out_gate, norm_weight=None, eps=1e-6, ...)
+    gated_rmsnorm(o, out_gate, norm_weight=None, eps=1e-6)
 """
-from .ops import (chunk_fwd, chunk_fwd_split, compose_states, gate, recurrent_step,  # noqa: F401
-                  split_lengths, transition, workspace_size)
+from .ops import (chunk_fwd, chunk_fwd_gated, chunk_fwd_split, compose_states, gate,  # noqa: F401
+                  gated_rmsnorm, recurrent_step, split_lengths, transition, workspace_size)
 
-__all__ = ["chunk_fwd", "chunk_fwd_split", "compose_states", "gate", "recurrent_step",
-           "split_lengths", "transition", "workspace_size"]
+__all__ = ["chunk_fwd", "chunk_fwd_gated", "chunk_fwd_split", "compose_states", "gate",
+           "gated_rmsnorm", "recurrent_step", "split_lengths", "transition", "workspace_size"]

@@ -25,7 +25,8 @@ KDA_GATE_LOGITS = 2
 
 # Every symbol include/kda.h declares.
 EXPORTED = ("kda_status_string", "kda_version", "kda_gate", "kda_chunk_fwd_workspace_size",
-            "kda_chunk_fwd", "kda_chunk_transition", "kda_compose_states", "kda_recurrent_step")
+            "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_gated_rmsnorm", "kda_chunk_transition",
+            "kda_compose_states", "kda_recurrent_step")
 
 _lib = None
 
@@ -57,6 +58,12 @@ def load(path: str = LIB_PATH):
                                   i32, i32, i32, i32, i32, i32, i32,  # N B T H Dk Dv chunk
                                   f32, vp, fp, vp, sz, vp]
     lib.kda_chunk_fwd.restype = i32
+    lib.kda_chunk_fwd_gated.argtypes = [vp, vp, vp, i32, fp, i32, fp, f32, fp, fp, ip,
+                                        i32, i32, i32, i32, i32, i32, i32,  # N B T H Dk Dv chunk
+                                        f32, vp, fp, f32, vp, fp, vp, sz, vp]
+    lib.kda_chunk_fwd_gated.restype = i32
+    lib.kda_gated_rmsnorm.argtypes = [vp, vp, i32, fp, f32, ctypes.c_long, i32, vp, vp]
+    lib.kda_gated_rmsnorm.restype = i32
     lib.kda_chunk_transition.argtypes = [vp, i32, fp, i32, fp, f32, fp, ip,
                                          i32, i32, i32, i32, i32, i32,  # N B T H Dk chunk
                                          fp, vp, sz, vp]

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(PKG, "libkda.so")
 ARCH = "gfx950"
 
 SOURCES = ["kda_api.cpp", "kda_gate.hip", "kda_recurrent.hip", "kda_chunk.hip", "kda_chunk_pipe.hip",
-           "kda_compose.hip"]
+           "kda_compose.hip", "kda_epilogue.hip"]
 
 # Packed fp32 VALU instructions are disabled for every device compile.
 # Matrix-core results are kept in ordinary VGPRs (-amdgpu-mfma-vgpr-form), which

@@ -37,6 +37,14 @@ kda_status_t check_seqs(const int32_t* cu, int N, int B, int T, kda::Seqs* s) {
   return KDA_SUCCESS;
 }
 
+kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                            const float* g, kda_gate_input_t gate_input, const float* A_log,
+                            float g_min, const float* beta, const float* initial_state,
+                            const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
+                            int Dv, int chunk, float scale, void* o, float* final_state,
+                            void* workspace, size_t workspace_bytes, kda_stream_t stream,
+                            const void* og, const float* onw, float oeps);
+
 }  // namespace
 
 extern "C" {
@@ -87,6 +95,48 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtyp
                            const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
                            int Dv, int chunk, float scale, void* o, float* final_state,
                            void* workspace, size_t workspace_bytes, kda_stream_t stream) {
+  return chunk_fwd_impl(q, k, v, dtype, g, gate_input, A_log, g_min, beta, initial_state,
+                        cu_seqlens, N, B, T, H, Dk, Dv, chunk, scale, o, final_state, workspace,
+                        workspace_bytes, stream, nullptr, nullptr, 0.f);
+}
+
+kda_status_t kda_chunk_fwd_gated(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                                 const float* g, kda_gate_input_t gate_input, const float* A_log,
+                                 float g_min, const float* beta, const float* initial_state,
+                                 const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
+                                 int Dv, int chunk, float scale, const void* out_gate,
+                                 const float* norm_weight, float eps, void* y, float* final_state,
+                                 void* workspace, size_t workspace_bytes, kda_stream_t stream) {
+  if (!out_gate || !y) return KDA_ERROR_INVALID_VALUE;
+  if (!aligned16(out_gate) || !(eps >= 0.0f)) return KDA_ERROR_INVALID_VALUE;
+  if (Dv > 512) return KDA_ERROR_NOT_SUPPORTED;
+  return chunk_fwd_impl(q, k, v, dtype, g, gate_input, A_log, g_min, beta, initial_state,
+                        cu_seqlens, N, B, T, H, Dk, Dv, chunk, scale, y, final_state, workspace,
+                        workspace_bytes, stream, out_gate, norm_weight, eps);
+}
+
+kda_status_t kda_gated_rmsnorm(const void* o, const void* gate, kda_dtype_t dtype,
+                               const float* weight, float eps, long rows, int Dv, void* y,
+                               kda_stream_t stream) {
+  if (rows < 0 || Dv <= 0 || !(eps >= 0.0f)) return KDA_ERROR_INVALID_VALUE;
+  if (dtype != KDA_FLOAT32 && dtype != KDA_BFLOAT16) return KDA_ERROR_INVALID_VALUE;
+  if (rows > 0 && (!o || !gate || !y)) return KDA_ERROR_INVALID_VALUE;
+  if (Dv > 512) return KDA_ERROR_NOT_SUPPORTED;
+  return launch_status(kda::launch_gated_rmsnorm(o, gate, dtype == KDA_BFLOAT16, weight, eps, rows,
+                                                 Dv, y, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                            const float* g, kda_gate_input_t gate_input, const float* A_log,
+                            float g_min, const float* beta, const float* initial_state,
+                            const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
+                            int Dv, int chunk, float scale, void* o, float* final_state,
+                            void* workspace, size_t workspace_bytes, kda_stream_t stream,
+                            const void* og, const float* onw, float oeps) {
   kda::Seqs s;
   kda_status_t st = check_seqs(cu_seqlens, N, B, T, &s);
   if (st != KDA_SUCCESS) return st;
@@ -134,17 +184,29 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtyp
       if (e != hipSuccess) return KDA_ERROR_LAUNCH_FAILURE;
       a.order = order;
     }
-    if (kda::chunk_pipe_supported(bf16, Dk, Dv, chunk))
+    if (kda::chunk_pipe_supported(bf16, Dk, Dv, chunk)) {
+      a.og = og; a.onw = onw; a.oeps = oeps;  // epilogue fused into the consumers
       return launch_status(kda::launch_chunk_pipe(a, hs));
-    return launch_status(kda::launch_chunk_fused(a, hs));
+    }
+    hipError_t e = kda::launch_chunk_fused(a, hs);
+    if (e == hipSuccess && og)
+      e = kda::launch_gated_rmsnorm(o, og, bf16, onw, oeps, s.Ttot * H, Dv, o, hs);
+    return launch_status(e);
   }
   kda::RecurrentArgs r;
   r.q = q; r.k = k; r.v = v; r.g = g; r.gate_mode = (int)gate_input;
   r.A_log = A_log; r.g_min = g_min; r.beta = beta;
   r.h0 = initial_state; r.hT = final_state; r.o = o;
   r.seqs = s; r.H = H; r.Dk = Dk; r.Dv = Dv; r.scale = scale; r.bf16 = bf16;
-  return launch_status(kda::launch_recurrent(r, hs));
+  hipError_t e = kda::launch_recurrent(r, hs);
+  if (e == hipSuccess && og)
+    e = kda::launch_gated_rmsnorm(o, og, bf16, onw, oeps, s.Ttot * H, Dv, o, hs);
+  return launch_status(e);
 }
+
+}  // namespace
+
+extern "C" {
 
 kda_status_t kda_chunk_transition(const void* k, kda_dtype_t dtype, const float* g,
                                   kda_gate_input_t gate_input, const float* A_log, float g_min,

@@ -69,11 +69,12 @@ constexpr int sT = sVT + PDV * TS * 2;      // (I+A_kk)^-1  [16][TS]
 constexpr int sAqk = sT + PT * TS * 2;      // A_qk         [16][TS]
 constexpr int sBeta = sAqk + PT * TS * 2;   // fp32 [16]
 constexpr int sEgc = sBeta + PT * 4;        // fp32 [128]  e^{G_15}
-constexpr int kSlotBytes = ((sEgc + PDK * 4) + 255) / 256 * 256;
+constexpr int sNrm = sEgc + PDK * 4;        // fp32 [4 consumers][16] output sums of squares
+constexpr int kSlotBytes = ((sNrm + NCONS * PT * 4) + 255) / 256 * 256;
 // Producer-private scratch.
 constexpr int pKd = 0;                      // k e^{-G}     [16][RS] bf16
 constexpr int kPrivBytes = pKd + PT * RS * 2;
-constexpr int kLdsBytes = NSLOT * kSlotBytes + NPROD * kPrivBytes + (2 * NSLOT + 1) * 4;
+constexpr int kLdsBytes = NSLOT * kSlotBytes + NPROD * kPrivBytes + (3 * NSLOT + 1) * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ float ex2(float x) { return fast_exp2(x); }
@@ -123,18 +124,23 @@ __device__ __forceinline__ uint32_t perm_hi16(uint32_t a, uint32_t b) {
 //   kModeTransition: the state map of each (sequence, head), M with
 //     S_final = M S_initial + S_final(S_initial = 0), written to a.hT: the
 //     same recurrence with v = 0 starting from S = I (q, v, o, h0 unused).
-enum { kModeForward = 0, kModeStateOnly = 1, kModeTransition = 2 };
+//   kModeForwardGated: o replaced by the block's output epilogue
+//     sigmoid(a.og) * RMSNorm(o) * a.onw, with the mean square over each
+//     token-head's d_v outputs taken in fp32 before rounding.
+enum { kModeForward = 0, kModeStateOnly = 1, kModeTransition = 2, kModeForwardGated = 3 };
 
 template <int GATE, int MODE>
 __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
   constexpr bool TRANS = MODE == kModeTransition;
-  constexpr bool NEEDQ = MODE == kModeForward;
+  constexpr bool GATED = MODE == kModeForwardGated;
+  constexpr bool NEEDQ = MODE == kModeForward || GATED;
   using M = Mma<__bf16>;
   using frag = M::frag;
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
   int* ready = reinterpret_cast<int*>(smem + NSLOT * kSlotBytes + NPROD * kPrivBytes);
   int* done = ready + NSLOT;
   int* abort_flag = done + NSLOT;
+  int* nrm_ready = abort_flag + 1;  // per slot: consumers that posted their sums of squares
 
   const __bf16* q = reinterpret_cast<const __bf16*>(a.q);
   const __bf16* k = reinterpret_cast<const __bf16*>(a.k);
@@ -159,7 +165,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
   const int nsteps = (int)((len + PT - 1) / PT);
   const int rowk = H * PDK * 2, rowg = H * PDK * 4, rowb = H * 4;
 
-  if (tid < 2 * NSLOT + 1) ready[tid] = 0;  // ready[], done[], abort_flag are contiguous
+  if (tid < 3 * NSLOT + 1) ready[tid] = 0;  // ready[], done[], abort_flag, nrm_ready[] are contiguous
   __syncthreads();
 
   if (wave < NPROD) {
@@ -425,6 +431,28 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
     const bool odd = m & 1;
     const uint32_t psel = odd ? 0x03020706u : 0x05040100u;
     const int ovoff2 = (4 * g4 + (odd ? 1 : 0)) * rowo + (vc0 + (m & ~1)) * 2;
+    // gated epilogue: this lane's norm weights (columns vc0 + 16b + m) and the
+    // gate logits of its rows 4g4+e, loaded one tile ahead
+    float nw[CNTV];
+    short zg[CNTV][4];
+    auto load_gate = [&](int step) {
+      const long tg = bos + (long)step * PT;
+      const int Lg = (int)min((long)PT, len - (long)step * PT);
+      const __amdgpu_buffer_rsrc_t rsz =
+          make_rsrc(reinterpret_cast<const __bf16*>(a.og) + ((size_t)tg * H + h) * PDV,
+                    (uint32_t)((Lg - 1) * H + 1) * PDV * 2);
+#pragma unroll
+      for (int b = 0; b < CNTV; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          zg[b][e] = __builtin_amdgcn_raw_buffer_load_b16(rsz, (4 * g4) * rowo + (vc0 + m) * 2,
+                                                          e * rowo + 32 * b, 0);
+    };
+    if constexpr (GATED) {
+#pragma unroll
+      for (int b = 0; b < CNTV; ++b) nw[b] = a.onw ? a.onw[vc0 + 16 * b + m] : 1.0f;
+      if (nsteps > 0) load_gate(0);
+    }
 
     for (int step = 0; step < nsteps; ++step) {
       const int slot = step % NSLOT;
@@ -511,10 +539,50 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
         // lanes (columns m, m^1) swap the pairs, and each lane stores two
         // neighbouring columns of one row: even lanes rows 0 and 2, odd lanes
         // rows 1 and 3.
+        if (a.scale != 1.0f) {
+#pragma unroll
+          for (int b = 0; b < CNTV; ++b) oc[b] = oc[b] * a.scale;
+        }
+        if constexpr (GATED) {
+          // mean square over the d_v outputs of each row: this consumer's 32
+          // columns summed over the 16 lanes of the row group (DPP), then the
+          // four consumers' sums exchanged through LDS
+          f32x4 ss = oc[0] * oc[0];
+#pragma unroll
+          for (int b = 1; b < CNTV; ++b) ss = ss + oc[b] * oc[b];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float t = ss[e];
+            t += bits_float(__builtin_amdgcn_mov_dpp(float_bits(t), 0xB1, 0xF, 0xF, false));   // lane ^ 1
+            t += bits_float(__builtin_amdgcn_mov_dpp(float_bits(t), 0x4E, 0xF, 0xF, false));   // lane ^ 2
+            t += bits_float(__builtin_amdgcn_mov_dpp(float_bits(t), 0x141, 0xF, 0xF, false));  // half-row mirror
+            t += bits_float(__builtin_amdgcn_mov_dpp(float_bits(t), 0x140, 0xF, 0xF, false));  // row mirror
+            ss[e] = t;
+          }
+          float* nrm = reinterpret_cast<float*>(const_cast<char*>(sl) + sNrm);
+          if (m == 0) *reinterpret_cast<f32x4*>(nrm + c * PT + 4 * g4) = ss;
+          __builtin_amdgcn_s_waitcnt(0xc07f);
+          signal_add(&nrm_ready[slot], lane);
+          wait_at_least(&nrm_ready[slot], NCONS * (step / NSLOT + 1), abort_flag);
+          f32x4 tot = *reinterpret_cast<const f32x4*>(nrm + 4 * g4);
+#pragma unroll
+          for (int cc = 1; cc < NCONS; ++cc) tot = tot + *reinterpret_cast<const f32x4*>(nrm + cc * PT + 4 * g4);
+          f32x4 rinv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rinv[e] = __builtin_amdgcn_rsqf(tot[e] * (1.0f / PDV) + a.oeps);
+#pragma unroll
+          for (int b = 0; b < CNTV; ++b)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float z = bits_float((int)(uint32_t)(uint16_t)zg[b][e] << 16);
+              const float sg = __builtin_amdgcn_rcpf(1.0f + ex2(-kLog2e * z));
+              oc[b][e] = oc[b][e] * rinv[e] * nw[b] * sg;
+            }
+          if (step + 1 < nsteps) load_gate(step + 1);
+        }
 #pragma unroll
         for (int b = 0; b < CNTV; ++b) {
-          f32x4 v = oc[b];
-          if (a.scale != 1.0f) v = v * a.scale;
+          const f32x4 v = oc[b];
           const uint32_t p01 = pack_bf16x2(v[0], v[1]), p23 = pack_bf16x2(v[2], v[3]);
           const uint32_t q01 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p01, 0xB1, 0xF, 0xF, false);
           const uint32_t q23 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p23, 0xB1, 0xF, 0xF, false);
@@ -569,7 +637,9 @@ static void launch_pipe_t(const ChunkArgs& a, hipStream_t stream) {
 
 hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t stream) {
   if (a.seqs.N == 0 || a.H == 0) return hipSuccess;
-  if (a.o)
+  if (a.o && a.og)
+    launch_pipe_t<kModeForwardGated>(a, stream);
+  else if (a.o)
     launch_pipe_t<kModeForward>(a, stream);
   else
     launch_pipe_t<kModeStateOnly>(a, stream);

@@ -62,6 +62,11 @@ struct ChunkArgs {
   int H, Dk, Dv;
   float scale;
   bool bf16;
+  // output epilogue (pipelined kernel only; og == nullptr: plain output):
+  // o = sigmoid(og) * RMSNorm(o) * onw, eps oeps
+  const void* og = nullptr;
+  const float* onw = nullptr;
+  float oeps = 0.f;
 };
 bool chunk_fused_supported(bool bf16, int Dk, int Dv, int chunk);
 // Pipelined producer/consumer chunk kernel (bf16, Dk = Dv = 128).
@@ -70,6 +75,10 @@ hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t stream);
 // Same kernel in transition mode: writes M (a.hT, [N, H, Dk, Dk]) with
 // S_final = M S_initial + S_final(0); reads k, g and beta only.
 hipError_t launch_chunk_transition(const ChunkArgs& a, hipStream_t stream);
+// Output epilogue y = sigmoid(z) * o / sqrt(mean(o^2) + eps) * w over rows of
+// Dv (<= 512) elements; y may alias o.
+hipError_t launch_gated_rmsnorm(const void* o, const void* z, bool bf16, const float* w, float eps,
+                                long rows, int Dv, void* y, hipStream_t stream);
 // Chains segment maps: starts[0] = S0, starts[p+1] = M_p starts[p] + b_p.
 hipError_t launch_compose(const float* M, const float* b, const float* S0, int nseq, int P,
                           int H, int Dk, int Dv, float* starts, hipStream_t stream);

@@ -137,6 +137,89 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     return o, final_state
 
 
+def chunk_fwd_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    beta: torch.Tensor, out_gate: torch.Tensor,
+                    norm_weight: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                    initial_state: Optional[torch.Tensor] = None,
+                    cu_seqlens: Optional[torch.Tensor] = None, gate: str = "logdecay",
+                    A_log: Optional[torch.Tensor] = None, g_min: float = -5.0, chunk: int = 64,
+                    scale: float = 1.0, output_final_state: bool = True,
+                    y: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """chunk_fwd followed by the block's output epilogue:
+    y = sigmoid(out_gate) * RMSNorm(o) * norm_weight (per token-head over Dv).
+    out_gate: [B, T, H, Dv] in q's dtype; norm_weight: fp32 [Dv] or None.
+    Returns (y, final_state)."""
+    lib = _lib.load()
+    dev = q.device
+    dt = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v), ("out_gate", out_gate)):
+        _need(t, name, dt, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or g.shape != q.shape or \
+            beta.shape != q.shape[:3] or out_gate.shape != v.shape:
+        raise ValueError("shape mismatch among q, k, v, g, beta, out_gate")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, dev)
+        if tuple(initial_state.shape) != (N, H, Dk, Dv):
+            raise ValueError("initial_state must be [N, H, Dk, Dv]")
+    if norm_weight is not None:
+        _need(norm_weight, "norm_weight", torch.float32, dev)
+        if tuple(norm_weight.shape) != (Dv,):
+            raise ValueError("norm_weight must be [Dv]")
+    if A_log is not None:
+        _need(A_log, "A_log", torch.float32, dev)
+    if y is None:
+        y = torch.empty((B, T, H, Dv), dtype=dt, device=dev)
+    _need(y, "y", dt, dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
+    ws_bytes = workspace_size(B, T, H, Dk, Dv, N, chunk, dt)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        rc = lib.kda_chunk_fwd_gated(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g),
+                                     _GATES[gate], _ptr(A_log), float(g_min), _ptr(beta),
+                                     _ptr(initial_state), _ptr(cu_seqlens), N, B, T, H, Dk, Dv,
+                                     int(chunk), float(scale), _ptr(out_gate), _ptr(norm_weight),
+                                     float(eps), _ptr(y), _ptr(final_state), _ptr(workspace),
+                                     ws_len, _stream(dev))
+    _lib.check(rc, "kda_chunk_fwd_gated")
+    return y, final_state
+
+
+def gated_rmsnorm(o: torch.Tensor, out_gate: torch.Tensor, norm_weight: Optional[torch.Tensor] = None,
+                  eps: float = 1e-6, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The output epilogue alone: y = sigmoid(out_gate) * RMSNorm(o) * norm_weight
+    over the last dimension. o, out_gate: [..., Dv] (bf16 or fp32)."""
+    lib = _lib.load()
+    dev = o.device
+    _need(o, "o", None, dev)
+    _need(out_gate, "out_gate", o.dtype, dev)
+    if out_gate.shape != o.shape:
+        raise ValueError("o and out_gate must have the same shape")
+    Dv = o.shape[-1]
+    if norm_weight is not None:
+        _need(norm_weight, "norm_weight", torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(o)
+    _need(y, "y", o.dtype, dev)
+    rows = o.numel() // Dv
+    with torch.cuda.device(dev):
+        rc = lib.kda_gated_rmsnorm(_ptr(o), _ptr(out_gate), _dtype_code(o), _ptr(norm_weight),
+                                   float(eps), rows, Dv, _ptr(y), _stream(dev))
+    _lib.check(rc, "kda_gated_rmsnorm")
+    return y
+
+
 def transition(k: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
                cu_seqlens: Optional[torch.Tensor] = None, gate: str = "logdecay",
                A_log: Optional[torch.Tensor] = None, g_min: float = -5.0, chunk: int = 64,

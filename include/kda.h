@@ -152,6 +152,42 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtyp
                            void* workspace, size_t workspace_bytes, kda_stream_t stream);
 
 /*
+ * kda_chunk_fwd_gated — kda_chunk_fwd followed by the attention block's
+ * output epilogue [KDA-blog §Gated MLA, output equation; the weight product
+ * W_o after it is not part of this library]:
+ *   y = sigmoid(out_gate) * o / sqrt(mean(o^2) + eps) * norm_weight,
+ * the mean taken over each token-head's Dv outputs. On the bf16 d = 128 path
+ * the epilogue runs inside the chunk kernel on the fp32 outputs before
+ * rounding (o itself never reaches memory); other shapes run kda_chunk_fwd
+ * and then the epilogue in place on y.
+ * out_gate     device dtype [B, T, H, Dv]: the gate logits (W_g x)
+ * norm_weight  device fp32 [Dv] or NULL (ones)
+ * eps          >= 0
+ * y            device dtype [B, T, H, Dv] (written)
+ * Other arguments and support as for kda_chunk_fwd; Dv <= 512.
+ */
+kda_status_t kda_chunk_fwd_gated(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                                 const float* g, kda_gate_input_t gate_input, const float* A_log,
+                                 float g_min, const float* beta, const float* initial_state,
+                                 const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
+                                 int Dv, int chunk, float scale, const void* out_gate,
+                                 const float* norm_weight, float eps, void* y, float* final_state,
+                                 void* workspace, size_t workspace_bytes, kda_stream_t stream);
+
+/*
+ * kda_gated_rmsnorm — the output epilogue on its own
+ * [KDA-blog §Gated MLA, output equation]:
+ *   y = sigmoid(gate) * o / sqrt(mean(o^2) + eps) * weight
+ * over rows of Dv elements (rows = B * T * H for a [B, T, H, Dv] tensor).
+ * o, gate, y   device dtype [rows, Dv]; y may alias o
+ * weight       device fp32 [Dv] or NULL (ones); eps >= 0
+ * Supported: Dv <= 512.
+ */
+kda_status_t kda_gated_rmsnorm(const void* o, const void* gate, kda_dtype_t dtype,
+                               const float* weight, float eps, long rows, int Dv, void* y,
+                               kda_stream_t stream);
+
+/*
  * kda_chunk_transition — the state map of each (sequence, head).
  * The KDA equation is linear in the state [KDA-blog §Kimi Delta Attention,
  * KDA equation], so the state a sequence leaves behind is affine in the state

@@ -138,6 +138,30 @@ def test_transition_and_compose_validation():
     assert comp(nseq=0) == _lib.KDA_SUCCESS
 
 
+def test_epilogue_entry_points_validation():
+    lib = _lib.load()
+
+    def gated(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, g=FAKE, gate=0, A=None, g_min=-5.0, beta=FAKE,
+                 h0=None, cu=None, N=1, B=1, T=64, H=2, Dk=128, Dv=128, chunk=64, scale=1.0,
+                 og=FAKE, w=None, eps=1e-6, y=FAKE, hT=None, ws=None, ws_bytes=0, stream=None)
+        a.update(kw)
+        return lib.kda_chunk_fwd_gated(*a.values())
+    for kw in (dict(og=None), dict(y=None), dict(og=FAKE + 2), dict(eps=-1.0), dict(q=None)):
+        assert gated(**kw) == _lib.KDA_ERROR_INVALID_VALUE, kw
+    assert gated(Dv=1024, Dk=64) == _lib.KDA_ERROR_NOT_SUPPORTED
+
+    def rms(**kw):
+        a = dict(o=FAKE, z=FAKE, dtype=1, w=None, eps=1e-6, rows=10, Dv=128, y=FAKE, stream=None)
+        a.update(kw)
+        return lib.kda_gated_rmsnorm(*a.values())
+    for kw in (dict(o=None), dict(z=None), dict(y=None), dict(rows=-1), dict(Dv=0),
+               dict(dtype=5), dict(eps=-0.5)):
+        assert rms(**kw) == _lib.KDA_ERROR_INVALID_VALUE, kw
+    assert rms(Dv=513) == _lib.KDA_ERROR_NOT_SUPPORTED
+    assert rms(rows=0) == _lib.KDA_SUCCESS
+
+
 def test_split_lengths_cover_each_sequence_in_aligned_pieces():
     from gated_delta_rule_92_amd.ops import split_lengths
     for lengths, P in (([262144], 8), ([1, 63, 64, 65, 1000, 0], 3), ([130, 7], 5)):

@@ -1,0 +1,129 @@
+"""GPU parity for the block's output epilogue ([KDA-blog] "Kimi k3 技术报告详解
+（1）——架构再升华", section "Gated MLA", output equation, before W_o):
+y = sigmoid(gate) * RMSNorm(o) * weight, fused into the bf16 d = 128 chunk
+kernel and as a standalone kernel, against the fp64 oracle (oracle forward,
+then the oracle epilogue on its fp64 output).
+
+Bar. RMSNorm rescales every token-head row to unit root mean square, so an
+absolute error in o of size e becomes e / rms(o_row) in that row of y: rows
+with small outputs (the first tokens of a sequence) amplify the o error the
+tolerance allows. The gated forward is therefore checked two ways:
+  (a) the epilogue arithmetic: y against the oracle epilogue applied to the
+      GPU's own o (chunk_fwd on the same inputs), max|d| / max|ref| <= tol;
+  (b) end to end against the oracle: in every row,
+      max|y - y_ref| <= tol * max|o_ref| / rms(o_ref, row) * max|sigmoid(z) w|,
+      the o tolerance carried through the normalisation;
+with tol = 2e-2 (bf16) or 1e-4 (fp32). The final state keeps the plain bar."""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_92_amd import chunk_fwd, chunk_fwd_gated, gated_rmsnorm
+from gated_delta_rule_92_amd.inputs import make_inputs
+from oracle import oracle_forward, oracle_gated_rmsnorm
+from tests.gpu_helpers import TOL_BF16, TOL_FP32, rel_err, to_dev, tol_for
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _print_case(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+def _gate_and_weight(shape, Dv, dtype, seed, with_weight):
+    gen = torch.Generator().manual_seed(seed)
+    zg = torch.randn(shape, generator=gen).to(dtype)
+    w = (1.0 + 0.5 * torch.randn(Dv, generator=gen)) if with_weight else None
+    return zg, w
+
+
+CASES = [
+    ("bf16 d=128 dense, weight", torch.bfloat16, 128, 128, dict(B=2, T=300, lengths=None), True),
+    ("bf16 d=128 varlen, no weight", torch.bfloat16, 128, 128,
+     dict(B=1, T=0, lengths=[0, 1, 63, 64, 65, 130, 16]), False),
+    ("bf16 d=64 (tile kernel + epilogue)", torch.bfloat16, 64, 64, dict(B=2, T=200, lengths=None), True),
+    ("fp32 d=64 (tile kernel + epilogue)", torch.float32, 64, 64, dict(B=1, T=256, lengths=None), True),
+    ("fp32 d=96x40 (token-serial + epilogue)", torch.float32, 96, 40, dict(B=1, T=90, lengths=None), True),
+]
+
+
+@pytest.mark.parametrize("name,dtype,Dk,Dv,kw,with_w", CASES, ids=[c[0] for c in CASES])
+def test_gated_forward_matches_oracle(name, dtype, Dk, Dv, kw, with_w):
+    _print_case(f"gated forward: {name}")
+    H = 2
+    d = make_inputs(kw["B"], kw["T"], H, Dk, Dv, dtype, h0_std=0.02, lengths=kw["lengths"], seed=41)
+    zg, w = _gate_and_weight(d["v"].shape, Dv, dtype, 42, with_w)
+    dd = to_dev(d)
+    eps = 1e-6
+    y, hT = chunk_fwd_gated(dd["q"], dd["k"], dd["v"], dd["z"], dd["beta"], zg.cuda(),
+                            None if w is None else w.cuda(), eps, dd["h0"], dd["cu_seqlens"],
+                            gate="logits")
+    o_gpu, _ = chunk_fwd(dd["q"], dd["k"], dd["v"], dd["z"], dd["beta"], dd["h0"], dd["cu_seqlens"],
+                         gate="logits")
+    torch.cuda.synchronize()
+    tol = tol_for(dtype)
+    # (a) the epilogue arithmetic, on the GPU's own outputs
+    ea = rel_err(y, oracle_gated_rmsnorm(o_gpu, zg, w, eps))
+    # (b) end to end, row by row, with the o tolerance carried through the norm
+    o_ref, s_ref = oracle_forward(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"],
+                                  d["cu_seqlens"], None, -5.0)
+    y_ref = oracle_gated_rmsnorm(o_ref, zg, w, eps)
+    gw = 1.0 / (1.0 + np.exp(-zg.double().numpy()))
+    if w is not None:
+        gw = gw * w.double().numpy()
+    rms = np.sqrt(np.mean(o_ref * o_ref, axis=-1) + eps)
+    bound = tol * np.abs(o_ref).max() / rms * np.abs(gw).max(axis=-1)
+    dy = np.abs(y.double().cpu().numpy() - y_ref).max(axis=-1)
+    worst = float((dy / bound).max())
+    es = rel_err(hT, s_ref)
+    print(f"  (a) err_y_vs_oracle_epilogue={ea:.3e}  (b) worst row / bound={worst:.3f}  "
+          f"err_y_plain={rel_err(y, y_ref):.3e}  err_state={es:.3e} tol={tol:g}", flush=True)
+    assert ea <= tol
+    assert worst <= 1.0
+    assert es <= tol
+
+
+@pytest.mark.parametrize("dtype,Dv", [(torch.bfloat16, 128), (torch.float32, 40), (torch.bfloat16, 300),
+                                     (torch.float32, 41), (torch.bfloat16, 129)])
+def test_standalone_epilogue_matches_oracle(dtype, Dv):
+    _print_case(f"standalone epilogue {dtype} Dv={Dv}")
+    gen = torch.Generator().manual_seed(43)
+    o = (3.0 * torch.randn(3, 50, 4, Dv, generator=gen)).to(dtype)
+    o[0, 0, 0] = 0.0                                  # a zero row: eps keeps it finite (0)
+    zg = torch.randn(o.shape, generator=gen).to(dtype)
+    w = 1.0 + 0.5 * torch.randn(Dv, generator=gen)
+    for eps in (1e-6, 0.5):
+        y = gated_rmsnorm(o.cuda(), zg.cuda(), w.cuda(), eps)
+        torch.cuda.synchronize()
+        ref = oracle_gated_rmsnorm(o, zg, w, eps)
+        err = rel_err(y, ref)
+        tol = TOL_FP32 if dtype == torch.float32 else TOL_BF16
+        print(f"  eps={eps} err={err:.3e} tol={tol:g}", flush=True)
+        assert err <= tol
+        assert torch.all(y[0, 0, 0].float().cpu() == 0.0)
+    # in place
+    oc = o.cuda()
+    y2 = gated_rmsnorm(oc, zg.cuda(), w.cuda(), 1e-6, y=oc)
+    torch.cuda.synchronize()
+    assert rel_err(y2, oracle_gated_rmsnorm(o, zg, w, 1e-6)) <= (TOL_FP32 if dtype == torch.float32 else TOL_BF16)
+
+
+def test_fused_equals_two_kernel_form():
+    """The fused epilogue (fp32 outputs before rounding) and chunk_fwd followed
+    by the standalone epilogue (on bf16-rounded outputs) agree within bf16
+    rounding."""
+    _print_case("fused vs two-kernel epilogue, bf16 d=128")
+    H = 4
+    d = make_inputs(1, 500, H, 128, 128, torch.bfloat16, seed=44)
+    zg, w = _gate_and_weight(d["v"].shape, 128, torch.bfloat16, 45, True)
+    dd = to_dev(d)
+    y_f, _ = chunk_fwd_gated(dd["q"], dd["k"], dd["v"], dd["z"], dd["beta"], zg.cuda(), w.cuda(),
+                             1e-6, gate="logits")
+    o, _ = chunk_fwd(dd["q"], dd["k"], dd["v"], dd["z"], dd["beta"], gate="logits")
+    y_2 = gated_rmsnorm(o, zg.cuda(), w.cuda(), 1e-6)
+    torch.cuda.synchronize()
+    between = rel_err(y_f, y_2.double().cpu().numpy())
+    e_f = rel_err(y_f, oracle_gated_rmsnorm(o, zg, w, 1e-6))
+    print(f"  fused vs two-kernel={between:.3e}  fused vs oracle epilogue of o={e_f:.3e}", flush=True)
+    assert between <= TOL_BF16 and e_f <= TOL_BF16
