@@ -162,6 +162,34 @@ def oracle_forward(q, k, v, z, beta, initial_state=None, cu_seqlens=None, A=None
                              lib_path=lib_path)
 
 
+def oracle_gate_softplus(z, A=None) -> np.ndarray:
+    """The pages' earlier, unbounded gate: g = -exp(A_h) * softplus(z), with
+    softplus(z) = log(1 + e^z) written as max(z, 0) + log1p(e^{-|z|}) so that
+    it neither overflows nor loses its small values. z: [..., H, Dk]; A: [H]
+    or None (e^{A_h} = 1). fp64 numpy.
+
+    [KDA-blog §Chunkwise parallel form, old-gate equation]
+    """
+    z64 = _f64(z)
+    sp = np.maximum(z64, 0.0) + np.log1p(np.exp(-np.abs(z64)))
+    scale = 1.0 if A is None else np.exp(_f64(A))[:, None]
+    return -scale * sp
+
+
+def oracle_forward_softplus(q, k, v, z, beta, initial_state=None, cu_seqlens=None, A=None,
+                            scale: float = 1.0, nthreads: Optional[int] = None,
+                            lib_path: Optional[str] = None):
+    """The unbounded-gate forward: g = -exp(A_h) softplus(z), alpha = exp(g),
+    then the token recurrence.
+
+    [KDA-blog §Chunkwise parallel form, old-gate equation; §Kimi Delta
+    Attention, KDA equation]
+    """
+    g = oracle_gate_softplus(z, A)
+    return oracle_recurrence(q, k, v, g, beta, initial_state, cu_seqlens, scale, nthreads,
+                             lib_path=lib_path)
+
+
 def gather_units(x, cu, units: Sequence[tuple]):
     """Pack the rows of the listed (sequence, head) units of a [1, Ttot, H, ...]
     or [B, T, H, ...] tensor into [1, sum T_n, 1, ...] (fp64) with its own

@@ -67,6 +67,28 @@ def test_gate_matches_library_sigmoid_and_range():
     assert lim[0] == -5.0 and -1e-16 < lim[1] < 0 and lim[2] == 0.0
 
 
+def test_softplus_gate_closed_forms_and_library():
+    """The pages' earlier gate g = -e^{A_h} softplus(z): softplus(0) = ln 2,
+    softplus(ln 3) = ln 4, equality with numpy's logaddexp(0, z), the
+    asymptotes (z for z >> 0, e^z for z << 0), sign and monotonicity."""
+    from oracle import oracle_gate_softplus
+    z = np.array([[[0.0, np.log(3.0), 40.0, -40.0, 1e-8]]])
+    g = oracle_gate_softplus(z)
+    np.testing.assert_allclose(g[0, 0, :2], [-np.log(2.0), -np.log(4.0)], rtol=1e-15)
+    np.testing.assert_allclose(g[0, 0, 2], -40.0, rtol=1e-15)
+    np.testing.assert_allclose(g[0, 0, 3], -np.exp(-40.0), rtol=1e-12)
+    gA = oracle_gate_softplus(z, np.array([np.log(2.0)]))
+    np.testing.assert_allclose(gA, 2.0 * g, rtol=1e-15)
+    rng = np.random.default_rng(9)
+    zz = 10 * rng.standard_normal((3, 4, 2, 16))
+    A = rng.standard_normal(2)
+    np.testing.assert_allclose(oracle_gate_softplus(zz, A),
+                               -np.exp(A)[:, None] * np.logaddexp(0.0, zz), rtol=1e-13)
+    assert np.all(oracle_gate_softplus(zz, A) < 0)
+    zs = np.sort(zz.reshape(-1))
+    assert np.all(np.diff(oracle_gate_softplus(zs[None, None, :])[0, 0]) <= 0)
+
+
 def test_cumsum_matches_numpy_per_chunk():
     """Inclusive chunk-local cumsum (gamma equation) == numpy.cumsum on every
     chunk segment, chunks restarting at each sequence start (ragged tails)."""
