@@ -129,6 +129,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="train8k")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--gate", choices=["logits", "softplus"], default="logits",
+                    help="logits: g = g_min sigmoid(z), diagonal tiles on matrix cores; softplus: "
+                         "the earlier unbounded gate -softplus(z), diagonal tiles by position pairs")
     ap.add_argument("--epilogue", choices=["none", "fused", "separate"], default="none",
                     help="add the output epilogue sigmoid(gate) * RMSNorm(o): fused into the "
                          "chunk kernel, or as a second kernel after it")
@@ -180,7 +183,7 @@ def main(argv=None):
                             segments=args.split, gate="logits", g_min=w.g_min, chunk=w.chunk)
             return
         chunk_fwd(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"], d["cu_seqlens"],
-                  gate="logits", g_min=w.g_min, chunk=w.chunk, o=o, final_state=hT,
+                  gate=args.gate, g_min=w.g_min, chunk=w.chunk, o=o, final_state=hT,
                   workspace=workspace)
         if args.epilogue == "separate":
             gated_rmsnorm(o, out_gate, norm_w, 1e-6, y=y)
@@ -234,7 +237,7 @@ def main(argv=None):
         "dtype": w.dtype_name,
         "data": "synthetic",
         "config": {"workload": w.name, "batch": int(d["q"].shape[0]), "seq_len": w.T, "heads": w.H,
-                   "d_k": w.Dk, "d_v": w.Dv, "chunk": w.chunk, "gate": "logits",
+                   "d_k": w.Dk, "d_v": w.Dv, "chunk": w.chunk, "gate": args.gate,
                    "g_min": w.g_min, "initial_state": d["h0"] is not None,
                    "sequences": N, "segments": args.split, "epilogue": args.epilogue},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

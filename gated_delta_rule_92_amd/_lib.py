@@ -22,6 +22,7 @@ KDA_BFLOAT16 = 1
 KDA_GATE_LOGDECAY = 0
 KDA_GATE_CUMSUM = 1
 KDA_GATE_LOGITS = 2
+KDA_GATE_SOFTPLUS = 3
 
 # Every symbol include/kda.h declares.
 EXPORTED = ("kda_status_string", "kda_version", "kda_gate", "kda_chunk_fwd_workspace_size",

@@ -144,7 +144,7 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
   if (H <= 0 || Dk <= 0 || Dv <= 0 || chunk <= 0) return KDA_ERROR_INVALID_VALUE;
   if (dtype != KDA_FLOAT32 && dtype != KDA_BFLOAT16) return KDA_ERROR_INVALID_VALUE;
   if (gate_input != KDA_GATE_LOGDECAY && gate_input != KDA_GATE_CUMSUM &&
-      gate_input != KDA_GATE_LOGITS)
+      gate_input != KDA_GATE_LOGITS && gate_input != KDA_GATE_SOFTPLUS)
     return KDA_ERROR_INVALID_VALUE;
   if (gate_input == KDA_GATE_LOGITS && !(g_min < 0.0f)) return KDA_ERROR_INVALID_VALUE;
   if (s.Ttot > 0 && (!q || !k || !v || !g || !beta)) return KDA_ERROR_INVALID_VALUE;
@@ -159,7 +159,11 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
   // that stays finite in fp32/bf16 for g >= -5.5. A logits gate with a lower
   // bound below that takes the token-serial path instead.
   const bool gate_in_range = !(gate_input == KDA_GATE_LOGITS && g_min < kda::kMinFusedGmin);
-  const bool fused = gate_in_range && kda::chunk_fused_supported(bf16, Dk, Dv, chunk);
+  // the unbounded gate runs only on the pairwise-diagonal pipelined kernel
+  // (forward with an output, no epilogue), else token by token
+  const bool softplus = gate_input == KDA_GATE_SOFTPLUS;
+  const bool fused = gate_in_range && kda::chunk_fused_supported(bf16, Dk, Dv, chunk) &&
+                     (!softplus || (kda::chunk_pipe_supported(bf16, Dk, Dv, chunk) && o && !og));
   if (!fused) {
     if (Dk > 256) return KDA_ERROR_NOT_SUPPORTED;
     if (gate_input == KDA_GATE_CUMSUM) return KDA_ERROR_NOT_SUPPORTED;
@@ -220,7 +224,7 @@ kda_status_t kda_chunk_transition(const void* k, kda_dtype_t dtype, const float*
   if (H <= 0 || Dk <= 0 || chunk <= 0) return KDA_ERROR_INVALID_VALUE;
   if (dtype != KDA_FLOAT32 && dtype != KDA_BFLOAT16) return KDA_ERROR_INVALID_VALUE;
   if (gate_input != KDA_GATE_LOGDECAY && gate_input != KDA_GATE_CUMSUM &&
-      gate_input != KDA_GATE_LOGITS)
+      gate_input != KDA_GATE_LOGITS && gate_input != KDA_GATE_SOFTPLUS)
     return KDA_ERROR_INVALID_VALUE;
   if (gate_input == KDA_GATE_LOGITS && !(g_min < 0.0f)) return KDA_ERROR_INVALID_VALUE;
   if (!M) return KDA_ERROR_INVALID_VALUE;
@@ -230,6 +234,7 @@ kda_status_t kda_chunk_transition(const void* k, kda_dtype_t dtype, const float*
     return KDA_ERROR_INVALID_VALUE;
   const bool bf16 = dtype == KDA_BFLOAT16;
   if (!kda::chunk_pipe_supported(bf16, Dk, Dk, chunk)) return KDA_ERROR_NOT_SUPPORTED;
+  if (gate_input == KDA_GATE_SOFTPLUS) return KDA_ERROR_NOT_SUPPORTED;
   if (gate_input == KDA_GATE_LOGITS && g_min < kda::kMinFusedGmin) return KDA_ERROR_NOT_SUPPORTED;
   size_t need = 0;
   st = kda_chunk_fwd_workspace_size(B, T, H, Dk, Dk, s.N, chunk, dtype, &need);
@@ -270,7 +275,8 @@ kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v, kda
                                 void* o, kda_stream_t stream) {
   if (N < 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_ERROR_INVALID_VALUE;
   if (dtype != KDA_FLOAT32 && dtype != KDA_BFLOAT16) return KDA_ERROR_INVALID_VALUE;
-  if (gate_input != KDA_GATE_LOGDECAY && gate_input != KDA_GATE_LOGITS)
+  if (gate_input != KDA_GATE_LOGDECAY && gate_input != KDA_GATE_LOGITS &&
+      gate_input != KDA_GATE_SOFTPLUS)
     return KDA_ERROR_INVALID_VALUE;
   if (gate_input == KDA_GATE_LOGITS && !(g_min < 0.0f)) return KDA_ERROR_INVALID_VALUE;
   if (N > 0 && (!q || !k || !v || !g || !beta || !state || !o)) return KDA_ERROR_INVALID_VALUE;

@@ -132,6 +132,11 @@ enum { kModeForward = 0, kModeStateOnly = 1, kModeTransition = 2, kModeForwardGa
 template <int GATE, int MODE>
 __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
   constexpr bool TRANS = MODE == kModeTransition;
+  // Unbounded gate (the pages' earlier -e^A softplus(z)): in-tile reciprocal
+  // decay factors can overflow, so the diagonal tiles A_kk, A_qk are formed
+  // position pair by position pair with e^{G_r - G_i} <= 1 (VALU) instead of
+  // as one matrix-core product.
+  constexpr bool PAIR = GATE == kGateSoftplus;
   constexpr bool GATED = MODE == kModeForwardGated;
   constexpr bool NEEDQ = MODE == kModeForward || GATED;
   using M = Mma<__bf16>;
@@ -175,6 +180,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
     __bf16* Kd = reinterpret_cast<__bf16*>(priv + pKd);
     const float es2 = ((GATE == kGateLogits && a.A_log) ? __expf(a.A_log[h]) : 1.0f) * kLog2e;
     const float gmin2 = a.g_min * kLog2e;
+    const float es_sp = (GATE == kGateSoftplus && a.A_log) ? __expf(a.A_log[h]) : 1.0f;
     // lane = (row half hr, channel quad cq): channels 4cq..4cq+3 of rows
     // 8hr..8hr+7. The cumulative sum runs over the lane's 8 rows and the two
     // halves then exchange their totals.
@@ -247,6 +253,15 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
             const float gm = r0 + r < L ? gmin2 : 0.f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[j] = fmaf(gm, __builtin_amdgcn_rcpf(1.0f + ex2(-es2 * z[j])), acc[j]);
+          } else if constexpr (GATE == kGateSoftplus) {
+            // log2-decay -e^A softplus(z) / ln 2, softplus(z) = max(z, 0) + log1p(e^{-|z|})
+            const float gs = r0 + r < L ? -es_sp : 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float sp2 = fmaxf(z[j], 0.f) * kLog2e +
+                                __builtin_amdgcn_logf(1.0f + ex2(-fabsf(z[j]) * kLog2e));
+              acc[j] = fmaf(gs, sp2, acc[j]);
+            }
           } else if constexpr (GATE == kGateLogDecay) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[j] = fmaf(z[j], kLog2e, acc[j]);  // rows past the end read as 0
@@ -291,21 +306,35 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
           const float E = ex2(G);
           kg[j] = kk[j] * E;
           if constexpr (NEEDQ) qg[j] = qq[j] * E;
-          kd[j] = kk[j] * ex2(-G);
-          kt[r][j] = kd[j] * eg[j];
+          if constexpr (PAIR) {
+            kt[r][j] = kk[j] * ex2(gc[j] - G);  // e^{G_15 - G} <= 1; e^{-G} alone may overflow
+          } else {
+            kd[j] = kk[j] * ex2(-G);
+            kt[r][j] = kd[j] * eg[j];
+          }
         }
         const int o = (r0 + r) * RS + 4 * cq;
         *reinterpret_cast<uint2*>(sl + sKg + o * 2) = uint2{pack_bf16x2(kg[0], kg[1]), pack_bf16x2(kg[2], kg[3])};
         if constexpr (NEEDQ)
           *reinterpret_cast<uint2*>(sl + sQg + o * 2) = uint2{pack_bf16x2(qg[0], qg[1]), pack_bf16x2(qg[2], qg[3])};
-        *reinterpret_cast<uint2*>(reinterpret_cast<char*>(Kd) + o * 2) =
-            uint2{pack_bf16x2(kd[0], kd[1]), pack_bf16x2(kd[2], kd[3])};
+        if constexpr (PAIR) {
+          // scratch for the position-pair step: G (fp32), raw k and q rows
+          const int row = r0 + r;
+          *reinterpret_cast<f32x4*>(sl + sKtT + row * PDK * 4 + cq * 16) =
+              f32x4{Gl[r][0] + off[0], Gl[r][1] + off[1], Gl[r][2] + off[2], Gl[r][3] + off[3]};
+          *reinterpret_cast<i32x2*>(sl + sKtT + PT * PDK * 4 + row * PDK * 2 + cq * 8) = rk[r];
+          *reinterpret_cast<i32x2*>(reinterpret_cast<char*>(Kd) + row * PDK * 2 + cq * 8) = rq[r];
+        } else {
+          *reinterpret_cast<uint2*>(reinterpret_cast<char*>(Kd) + o * 2) =
+              uint2{pack_bf16x2(kd[0], kd[1]), pack_bf16x2(kd[2], kd[3])};
+        }
       }
       // e^{G_15}, k e^{G_15 - G} and v, channel-major (this lane: 8 tokens
       // of 4 channels)
       if (hr) {
         *reinterpret_cast<f32x4*>(sl + sEgc + cq * 16) = f32x4{eg[0], eg[1], eg[2], eg[3]};
       }
+      auto write_ktvt = [&]() {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int c = 4 * cq + j;
@@ -323,9 +352,13 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
         if constexpr (!TRANS)
           *reinterpret_cast<uint4*>(sl + sVT + (c * TS + r0) * 2) = uint4{u[0], u[1], u[2], u[3]};
       }
+      };
       if (lane < PT) reinterpret_cast<float*>(sl + sBeta)[lane] = rb;
-      // the next tile of this producer loads while this one is finished
-      if (step + NPROD < nsteps) load_tile(step + NPROD);
+      if constexpr (!PAIR) {
+        write_ktvt();
+        // the next tile of this producer loads while this one is finished
+        if (step + NPROD < nsteps) load_tile(step + NPROD);
+      }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wavefront's LDS writes landed
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup", "local");
 
@@ -335,8 +368,110 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
       //   dn[e] = sum_c Kg[4g4+e][c] Kd[m][c]   (= A_kk[4g4+e][m] / beta_{4g4+e})
       //   dq[e] = sum_c Qg[m][c] Kd[4g4+e][c]   (= A_qk[m][4g4+e])
       f32x4 dk = {0.f, 0.f, 0.f, 0.f}, dn = dk, dq = dk;
+      if constexpr (PAIR) {
+        // Position pairs: lane (rp = lane / 8, cg = lane % 8) sums channels
+        // 16cg..16cg+15 of rows ra = rp (against i = 0..7) and rb = 15 - rp
+        // (against i = 0..15); entries with i > r are computed and dropped,
+        // which keeps every lane on the same trip count.
+        const int rp = lane >> 3, cg = lane & 7;
+        const int ra = rp, rbw = PT - 1 - rp;
+        const char* sG = sl + sKtT;
+        const char* sK = sl + sKtT + PT * PDK * 4;
+        const char* sQ = reinterpret_cast<const char*>(Kd);
+        // 8 channels (16cg + 8hc .. + 7) of one scratch row, as fp32
+        auto row8 = [&](const char* base, int row, int stride, int hc, float* out, bool is_f32) {
+          const int c0 = 16 * cg + 8 * hc;
+          if (is_f32) {
 #pragma unroll
-      for (int ks = 0; ks < PDK / 32; ++ks) {
+            for (int u = 0; u < 2; ++u) {
+              const f32x4 x = *reinterpret_cast<const f32x4*>(base + row * stride + (c0 + 4 * u) * 4);
+              out[4 * u] = x[0]; out[4 * u + 1] = x[1]; out[4 * u + 2] = x[2]; out[4 * u + 3] = x[3];
+            }
+          } else {
+            const uint4 x = *reinterpret_cast<const uint4*>(base + row * stride + c0 * 2);
+            unpack_bf16x2(x.x, out[0], out[1]);
+            unpack_bf16x2(x.y, out[2], out[3]);
+            unpack_bf16x2(x.z, out[4], out[5]);
+            unpack_bf16x2(x.w, out[6], out[7]);
+          }
+        };
+        float akka[8], aqka[8], akkb[16], aqkb[16];
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+          akkb[i] = aqkb[i] = 0.f;
+          if (i < 8) akka[i] = aqka[i] = 0.f;
+        }
+#pragma unroll
+        for (int hc = 0; hc < 2; ++hc) {
+          float Ga[8], Gb[8], ka[8], kb[8], qa[8], qb[8];
+          row8(sG, ra, PDK * 4, hc, Ga, true);
+          row8(sG, rbw, PDK * 4, hc, Gb, true);
+          row8(sK, ra, PDK * 2, hc, ka, false);
+          row8(sK, rbw, PDK * 2, hc, kb, false);
+          row8(sQ, ra, PDK * 2, hc, qa, false);
+          row8(sQ, rbw, PDK * 2, hc, qb, false);
+#pragma unroll
+          for (int i = 0; i < PT; ++i) {
+            float Gi[8], ki[8];
+            row8(sG, i, PDK * 4, hc, Gi, true);
+            row8(sK, i, PDK * 2, hc, ki, false);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+              const float eb = ex2(Gb[c] - Gi[c]);
+              akkb[i] = fmaf(kb[c] * ki[c], eb, akkb[i]);
+              aqkb[i] = fmaf(qb[c] * ki[c], eb, aqkb[i]);
+              if (i < 8) {
+                const float ea = ex2(Ga[c] - Gi[c]);
+                akka[i] = fmaf(ka[c] * ki[c], ea, akka[i]);
+                aqka[i] = fmaf(qa[c] * ki[c], ea, aqka[i]);
+              }
+            }
+          }
+        }
+        // sum over the 8 channel groups (lanes 8rp..8rp+7)
+        auto sum8 = [](float t) {
+          t += bits_float(__builtin_amdgcn_mov_dpp(float_bits(t), 0xB1, 0xF, 0xF, false));
+          t += bits_float(__builtin_amdgcn_mov_dpp(float_bits(t), 0x4E, 0xF, 0xF, false));
+          t += bits_float(__builtin_amdgcn_mov_dpp(float_bits(t), 0x141, 0xF, 0xF, false));
+          return t;
+        };
+        float* Akk = reinterpret_cast<float*>(Kd);             // [16][16] fp32, after the scratch is read
+        float* Aqq = reinterpret_cast<float*>(Kd) + PT * PT;   // [16][16] fp32
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+          akkb[i] = sum8(akkb[i]);
+          aqkb[i] = sum8(aqkb[i]);
+          if (i < 8) {
+            akka[i] = sum8(akka[i]);
+            aqka[i] = sum8(aqka[i]);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // every lane's scratch reads have returned
+        if (cg == 0) {
+#pragma unroll
+          for (int i = 0; i < PT; ++i) {
+            Akk[rbw * PT + i] = akkb[i];
+            Aqq[rbw * PT + i] = aqkb[i];
+            if (i < 8) {
+              Akk[ra * PT + i] = akka[i];
+              Aqq[ra * PT + i] = aqka[i];
+            }
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup", "local");
+        // into the accumulator layout used below: dk[e] = raw A_kk[m][4g4+e],
+        // dn[e] = raw A_kk[4g4+e][m], dq[e] = A_qk[m][4g4+e]
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g4 + e;
+          dk[e] = Akk[m * PT + i];
+          dn[e] = Akk[i * PT + m];
+          dq[e] = Aqq[m * PT + i];
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < (PAIR ? 0 : PDK / 32); ++ks) {
         const int ca = 32 * ks + 4 * g4;
         const __bf16* Kg = reinterpret_cast<const __bf16*>(sl + sKg);
         const __bf16* Qg = reinterpret_cast<const __bf16*>(sl + sQg);
@@ -385,6 +520,11 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
         R = MF::k16(A4, R, R);
         R = MF::k16(A8, R, R);
         store4(reinterpret_cast<__bf16*>(sl + sT) + m * TS + 4 * g4, R);
+      }
+      if constexpr (PAIR) {
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // scratch reads done before KtT / VT overwrite it
+        write_ktvt();
+        if (step + NPROD < nsteps) load_tile(step + NPROD);
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);
       signal_set(&ready[slot], step + 1);
@@ -628,6 +768,11 @@ static void launch_pipe_t(const ChunkArgs& a, hipStream_t stream) {
       break;
     case kGateCumsum:
       hipLaunchKernelGGL((chunk_pipe_kernel<kGateCumsum, MODE>), grid, block, 0, stream, a);
+      break;
+    case kGateSoftplus:
+      // unbounded gate: forward only, diagonal tiles by position pairs
+      if constexpr (MODE == kModeForward)
+        hipLaunchKernelGGL((chunk_pipe_kernel<kGateSoftplus, MODE>), grid, block, 0, stream, a);
       break;
     default:
       hipLaunchKernelGGL((chunk_pipe_kernel<kGateLogits, MODE>), grid, block, 0, stream, a);

@@ -7,7 +7,7 @@
 
 namespace kda {
 
-enum GateMode { kGateLogDecay = 0, kGateCumsum = 1, kGateLogits = 2 };
+enum GateMode { kGateLogDecay = 0, kGateCumsum = 1, kGateLogits = 2, kGateSoftplus = 3 };
 
 // Sequence geometry shared by the launchers. Either cu (device, N+1 entries)
 // describes packed sequences, or cu == nullptr and sequence n covers tokens
@@ -30,7 +30,7 @@ struct RecurrentArgs {
   const void* k;
   const void* v;
   const float* g;
-  int gate_mode;  // kGateLogDecay or kGateLogits
+  int gate_mode;  // kGateLogDecay, kGateLogits or kGateSoftplus
   const float* A_log;
   float g_min;
   const float* beta;

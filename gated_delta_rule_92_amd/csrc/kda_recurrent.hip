@@ -59,7 +59,8 @@ __global__ void __launch_bounds__(256) recurrent_kernel(RecurrentArgs a) {
     s[i] = (a.h0 && jvalid && i < rows_per_part && r < Dk) ? a.h0[sbase + (size_t)r * Dv + j]
                                                            : 0.f;
   }
-  const float es = (a.gate_mode == kGateLogits && a.A_log) ? __expf(a.A_log[h]) : 1.0f;
+  const float es = ((a.gate_mode == kGateLogits || a.gate_mode == kGateSoftplus) && a.A_log)
+                       ? __expf(a.A_log[h]) : 1.0f;
 
   for (long t = bos; t < eos; ++t) {
     const size_t rk = ((size_t)t * H + h) * Dk;
@@ -68,6 +69,8 @@ __global__ void __launch_bounds__(256) recurrent_kernel(RecurrentArgs a) {
       s_q[c] = to_f32(q[rk + c]);
       float gv = a.g[rk + c];
       if (a.gate_mode == kGateLogits) gv = a.g_min / (1.0f + __expf(-es * gv));
+      // the earlier, unbounded gate: -e^A softplus(z), softplus = max(z, 0) + log1p(e^{-|z|})
+      if (a.gate_mode == kGateSoftplus) gv = -es * (fmaxf(gv, 0.f) + log1pf(__expf(-fabsf(gv))));
       s_a[c] = __expf(gv);
     }
     if (tid < kRecCols) {

@@ -13,7 +13,7 @@ import torch
 from . import _lib
 
 _GATES = {"logdecay": _lib.KDA_GATE_LOGDECAY, "cumsum": _lib.KDA_GATE_CUMSUM,
-          "logits": _lib.KDA_GATE_LOGITS}
+          "logits": _lib.KDA_GATE_LOGITS, "softplus": _lib.KDA_GATE_SOFTPLUS}
 
 
 def _dtype_code(t: torch.Tensor) -> int:

@@ -72,7 +72,14 @@ typedef enum {
      with the same `chunk` (chunk_fwd only) */
   KDA_GATE_CUMSUM = 1,
   /* gate logits z; the library applies g = g_min * sigmoid(exp(A_h) z) */
-  KDA_GATE_LOGITS = 2
+  KDA_GATE_LOGITS = 2,
+  /* gate logits z of the pages' earlier, unbounded gate
+     g = -exp(A_h) * softplus(z) [KDA-blog §Chunkwise parallel form, old-gate
+     equation]; g_min is ignored. On the bf16 d = 128 chunk path the diagonal
+     tiles are then formed position pair by position pair (VALU), since their
+     reciprocal decay factors can overflow; this is the path the bounded gate
+     removes, kept for comparison. */
+  KDA_GATE_SOFTPLUS = 3
 } kda_gate_input_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -139,7 +146,8 @@ kda_status_t kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, i
  * Supported: bf16 with Dk, Dv in {64, 128}; fp32 with Dk = Dv = 64 on the
  * matrix-core chunk path; any other Dk, Dv <= 256 (and fp32 at 128) runs a
  * token-serial kernel with the same results, as does KDA_GATE_LOGITS with
- * g_min < -5.5. The chunk path requires every per-token log-decay to be
+ * g_min < -5.5. KDA_GATE_SOFTPLUS runs the pairwise-diagonal chunk kernel for
+ * bf16 Dk = Dv = 128 with o requested, else the token-serial kernel. The chunk path requires every per-token log-decay to be
  * >= -5.5 (the pages fix g_min = -5): inside a 16-token tile it scales by
  * up to e^{16|g|}, which must stay finite in fp32. Zero-length sequences are
  * allowed (final state = initial state).
