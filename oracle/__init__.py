@@ -15,6 +15,8 @@ from .oracle import (  # noqa: F401
     oracle_gate,
     oracle_recurrence,
     oracle_forward,
+    oracle_backward,
+    oracle_gate_backward,
     oracle_forward_softplus,
     oracle_gate_softplus,
     library_path,

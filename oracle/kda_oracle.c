@@ -30,6 +30,13 @@
  *                          with alpha_t = exp(g_t) [KDA-blog, new-gate
  *                          equation]. No chunking: the chunkwise form is
  *                          stated on the same page to equal this exactly.
+ *   kda_oracle_gate_bwd    derivative of the gate w.r.t. z and A_h
+ *   kda_oracle_backward    derivative of the recurrence w.r.t. q, k, v, g,
+ *                          beta and the initial state, given the gradients
+ *                          of every o_t and of the final state: each forward
+ *                          step differentiated in reverse order, from states
+ *                          kept by a forward pass. The pages do not give a
+ *                          backward; this is the plain derivative.
  *
  * Parity pins (closed forms, invariants, brute force) live in the tests.
  * Build: gcc -O2 -std=c99 -shared -fPIC (no fast-math, no intrinsics).
@@ -235,4 +242,223 @@ int kda_oracle_recurrence(const double* q, const double* k, const double* v, con
   pthread_mutex_destroy(&jb.lock);
   free(order);
   return 0;
+}
+
+/* -------------------------------------------------------------- backward */
+
+/*
+ * Gradient of the gate g = g_min * sigmoid(s z), s = exp(A_h), for a tensor
+ * laid out as [rows, H, Dk]: with p = sigmoid(s z) and p' = p (1 - p),
+ *   dz = dg * g_min * p' * s,     dA_h = sum over rows, c of dg * g_min * p' * s * z.
+ * dA may be NULL (not wanted); A may be NULL (A_h = 0).
+ * [KDA-blog §Chunkwise parallel form, new-gate equation], differentiated.
+ */
+void kda_oracle_gate_bwd(const double* z, const double* A, double g_min, const double* dg,
+                         long rows, int H, int Dk, double* dz, double* dA) {
+  if (dA)
+    for (int h = 0; h < H; ++h) dA[h] = 0.0;
+  for (long r = 0; r < rows; ++r)
+    for (int h = 0; h < H; ++h) {
+      double s = A ? exp(A[h]) : 1.0;
+      for (int c = 0; c < Dk; ++c) {
+        long i = (r * H + h) * (long)Dk + c;
+        double p = sigmoid(s * z[i]);
+        double dx = dg[i] * g_min * p * (1.0 - p); /* gradient w.r.t. x = s z */
+        dz[i] = dx * s;
+        if (dA) dA[h] += dx * s * z[i];
+      }
+    }
+}
+
+/*
+ * Reverse-mode derivative of unit_recurrence for one unit: given do (the
+ * gradient of the loss w.r.t. every o_t) and dS (w.r.t. the final state, in:
+ * [Dk][Dv], out: the gradient w.r.t. the initial state), writes the
+ * gradients w.r.t. q, k, v, g and beta. The pages state the forward
+ * recurrence only [KDA-blog §Kimi Delta Attention, KDA equation]; this is
+ * its exact derivative, every step of the forward undone in reverse order
+ * (Sb = the decayed state, u = Sb^T k, d = beta (v - u)):
+ *   5. o = scale S^T q         dq = scale S do;           dS += scale q do^T
+ *   4. S = Sb + k d^T          dd = dS^T k;  dk = dS d;   dSb = dS
+ *   3. d = beta (v - u)        dv = beta dd; dbeta = dd . (v - u); du = -beta dd
+ *   2. u = Sb^T k              dSb += k du^T;  dk += Sb du
+ *   1. Sb = Diag(alpha) S_prev dg_i = sum_j dSb_ij Sb_ij;  dS_prev = Diag(alpha) dSb
+ * The states S_0 .. S_T of the forward pass are kept (T+1 of them).
+ * Returns 0, or -1 if memory runs out.
+ */
+static int unit_backward(long T, int Dk, int Dv, const double* q, const double* k,
+                         const double* v, const double* g, long rk, long rv, const double* beta,
+                         long bs, double scale, const double* h0, const double* dO, double* dS,
+                         double* dq, double* dk, double* dv, double* dg, double* dbeta) {
+  size_t ssz = (size_t)Dk * Dv;
+  double* st = (double*)malloc(sizeof(double) * ssz * (size_t)(T + 1));
+  double* Sb = (double*)malloc(sizeof(double) * ssz);
+  double* u = (double*)malloc(sizeof(double) * (size_t)Dv * 3);
+  if (!st || !Sb || !u) {
+    free(st); free(Sb); free(u);
+    return -1;
+  }
+  double* d = u + Dv;
+  double* dd = u + 2 * Dv;
+  /* forward pass, keeping every state */
+  if (h0)
+    memcpy(st, h0, sizeof(double) * ssz);
+  else
+    memset(st, 0, sizeof(double) * ssz);
+  for (long t = 0; t < T; ++t) {
+    const double *kt = k + t * rk, *gt = g + t * rk, *vt = v + t * rv;
+    double bt = beta[t * bs];
+    double* S = st + (size_t)(t + 1) * ssz;
+    for (int i = 0; i < Dk; ++i) {
+      double a = exp(gt[i]);
+      for (int j = 0; j < Dv; ++j) S[i * Dv + j] = a * st[(size_t)t * ssz + i * Dv + j];
+    }
+    for (int j = 0; j < Dv; ++j) u[j] = 0.0;
+    for (int i = 0; i < Dk; ++i)
+      for (int j = 0; j < Dv; ++j) u[j] += S[i * Dv + j] * kt[i];
+    for (int j = 0; j < Dv; ++j) d[j] = bt * (vt[j] - u[j]);
+    for (int i = 0; i < Dk; ++i)
+      for (int j = 0; j < Dv; ++j) S[i * Dv + j] += kt[i] * d[j];
+  }
+  /* reverse pass */
+  for (long t = T - 1; t >= 0; --t) {
+    const double *qt = q + t * rk, *kt = k + t * rk, *gt = g + t * rk, *vt = v + t * rv;
+    const double* dot = dO + t * rv;
+    double bt = beta[t * bs];
+    const double* S = st + (size_t)(t + 1) * ssz;
+    const double* Sp = st + (size_t)t * ssz;
+    double *dqt = dq + t * rk, *dkt = dk + t * rk, *dgt = dg + t * rk, *dvt = dv + t * rv;
+    /* 5. o = scale S^T q */
+    for (int i = 0; i < Dk; ++i) {
+      double acc = 0.0;
+      for (int j = 0; j < Dv; ++j) acc += S[i * Dv + j] * dot[j];
+      dqt[i] = scale * acc;
+      for (int j = 0; j < Dv; ++j) dS[i * Dv + j] += scale * qt[i] * dot[j];
+    }
+    /* recompute the decayed state, u and d of this token */
+    for (int i = 0; i < Dk; ++i) {
+      double a = exp(gt[i]);
+      for (int j = 0; j < Dv; ++j) Sb[i * Dv + j] = a * Sp[i * Dv + j];
+    }
+    for (int j = 0; j < Dv; ++j) u[j] = 0.0;
+    for (int i = 0; i < Dk; ++i)
+      for (int j = 0; j < Dv; ++j) u[j] += Sb[i * Dv + j] * kt[i];
+    for (int j = 0; j < Dv; ++j) d[j] = bt * (vt[j] - u[j]);
+    /* 4. S = Sb + k d^T */
+    for (int j = 0; j < Dv; ++j) dd[j] = 0.0;
+    for (int i = 0; i < Dk; ++i) {
+      double acc = 0.0;
+      for (int j = 0; j < Dv; ++j) {
+        dd[j] += dS[i * Dv + j] * kt[i];
+        acc += dS[i * Dv + j] * d[j];
+      }
+      dkt[i] = acc;
+    }
+    /* 3. d = beta (v - u); du = -beta dd is kept in dd */
+    double db = 0.0;
+    for (int j = 0; j < Dv; ++j) {
+      dvt[j] = bt * dd[j];
+      db += dd[j] * (vt[j] - u[j]);
+      dd[j] = -bt * dd[j];
+    }
+    dbeta[t * bs] = db;
+    /* 2. u = Sb^T k */
+    for (int i = 0; i < Dk; ++i) {
+      double acc = 0.0;
+      for (int j = 0; j < Dv; ++j) {
+        dS[i * Dv + j] += kt[i] * dd[j];
+        acc += Sb[i * Dv + j] * dd[j];
+      }
+      dkt[i] += acc;
+    }
+    /* 1. Sb = Diag(alpha) S_prev */
+    for (int i = 0; i < Dk; ++i) {
+      double a = exp(gt[i]), acc = 0.0;
+      for (int j = 0; j < Dv; ++j) {
+        acc += dS[i * Dv + j] * Sb[i * Dv + j];
+        dS[i * Dv + j] *= a;
+      }
+      dgt[i] = acc;
+    }
+  }
+  free(st); free(Sb); free(u);
+  return 0;
+}
+
+typedef struct {
+  int H, Dk, Dv;
+  const double *q, *k, *v, *g, *beta, *h0, *dO, *dhT;
+  const int32_t* cu;
+  double scale;
+  double *dq, *dk, *dv, *dg, *dbeta, *dh0;
+  int n_units;
+  int next, failed;
+  pthread_mutex_t lock;
+} bjob_t;
+
+static void* bworker(void* arg) {
+  bjob_t* jb = (bjob_t*)arg;
+  for (;;) {
+    pthread_mutex_lock(&jb->lock);
+    int unit = jb->next++;
+    pthread_mutex_unlock(&jb->lock);
+    if (unit >= jb->n_units) break;
+    int H = jb->H, Dk = jb->Dk, Dv = jb->Dv;
+    int n = unit / H, h = unit % H;
+    long t0 = jb->cu[n], T = (long)jb->cu[n + 1] - t0;
+    size_t ssz = (size_t)Dk * Dv;
+    double* dS = jb->dh0 + (size_t)unit * ssz;
+    if (jb->dhT)
+      memcpy(dS, jb->dhT + (size_t)unit * ssz, sizeof(double) * ssz);
+    else
+      memset(dS, 0, sizeof(double) * ssz);
+    long rk = (long)H * Dk, rv = (long)H * Dv;
+    long ok = t0 * rk + (long)h * Dk, ov = t0 * rv + (long)h * Dv, ob = t0 * H + h;
+    int rc = unit_backward(T, Dk, Dv, jb->q + ok, jb->k + ok, jb->v + ov, jb->g + ok, rk, rv,
+                           jb->beta + ob, H, jb->scale, jb->h0 ? jb->h0 + (size_t)unit * ssz : NULL,
+                           jb->dO + ov, dS, jb->dq + ok, jb->dk + ok, jb->dv + ov, jb->dg + ok,
+                           jb->dbeta + ob);
+    if (rc) {
+      pthread_mutex_lock(&jb->lock);
+      jb->failed = 1;
+      pthread_mutex_unlock(&jb->lock);
+    }
+  }
+  return NULL;
+}
+
+/*
+ * Backward of kda_oracle_recurrence, same packed layout: dO like o, dhT like
+ * hT (NULL = zero gradient on the final state); writes dq, dk, dg like q,
+ * dv like v, dbeta like beta and dh0 like h0. Units run on `nthreads`
+ * threads; each keeps T+1 states of Dk*Dv doubles. Returns 0, or -1 on bad
+ * arguments or when memory runs out.
+ */
+int kda_oracle_backward(const double* q, const double* k, const double* v, const double* g,
+                        const double* beta, const double* h0, const int32_t* cu, int N, int H,
+                        int Dk, int Dv, double scale, const double* dO, const double* dhT,
+                        double* dq, double* dk, double* dv, double* dg, double* dbeta,
+                        double* dh0, int nthreads) {
+  if (!q || !k || !v || !g || !beta || !cu || !dO || !dq || !dk || !dv || !dg || !dbeta ||
+      !dh0 || N < 0 || H <= 0 || Dk <= 0 || Dv <= 0)
+    return -1;
+  for (int n = 0; n < N; ++n)
+    if (cu[n + 1] < cu[n]) return -1;
+  bjob_t jb;
+  jb.H = H; jb.Dk = Dk; jb.Dv = Dv;
+  jb.q = q; jb.k = k; jb.v = v; jb.g = g; jb.beta = beta; jb.h0 = h0; jb.dO = dO; jb.dhT = dhT;
+  jb.cu = cu; jb.scale = scale;
+  jb.dq = dq; jb.dk = dk; jb.dv = dv; jb.dg = dg; jb.dbeta = dbeta; jb.dh0 = dh0;
+  jb.n_units = N * H;
+  jb.next = 0;
+  jb.failed = 0;
+  pthread_mutex_init(&jb.lock, NULL);
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > jb.n_units) nthreads = jb.n_units > 0 ? jb.n_units : 1;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, bworker, &jb);
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  free(th);
+  pthread_mutex_destroy(&jb.lock);
+  return jb.failed ? -1 : 0;
 }

@@ -63,6 +63,13 @@ def _bind(lib):
                                           ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_double, dp, dp, ctypes.c_int]
     lib.kda_oracle_recurrence.restype = ctypes.c_int
+    lib.kda_oracle_gate_bwd.argtypes = [dp, dp, ctypes.c_double, dp, ctypes.c_long, ctypes.c_int,
+                                        ctypes.c_int, dp, dp]
+    lib.kda_oracle_gate_bwd.restype = None
+    lib.kda_oracle_backward.argtypes = [dp, dp, dp, dp, dp, dp, ip, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_double, dp, dp,
+                                        dp, dp, dp, dp, dp, dp, ctypes.c_int]
+    lib.kda_oracle_backward.restype = ctypes.c_int
     return lib
 
 
@@ -147,6 +154,58 @@ def oracle_recurrence(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
     if rc != 0:
         raise ValueError("oracle: invalid arguments")
     return o, hT
+
+
+def oracle_backward(q, k, v, g, beta, do, initial_state=None, d_final_state=None,
+                    cu_seqlens=None, scale: float = 1.0, nthreads: Optional[int] = None,
+                    lib_path: Optional[str] = None):
+    """Gradients of the token recurrence (fp64): given do [B, T, H, Dv] (the
+    gradient w.r.t. o) and d_final_state [N, H, Dk, Dv] (w.r.t. the final
+    state, None = zero), returns a dict with dq, dk, dg [B, T, H, Dk],
+    dv [B, T, H, Dv], dbeta [B, T, H] and dh0 [N, H, Dk, Dv]. g is the
+    per-token log-decay, as in oracle_recurrence; dg is the gradient w.r.t. it.
+
+    [KDA-blog §Kimi Delta Attention, KDA equation], differentiated step by
+    step in reverse order (the pages give no backward).
+    """
+    lib = _load(lib_path)
+    q64, k64, v64, g64, b64, do64 = (_f64(x) for x in (q, k, v, g, beta, do))
+    B, T, H, Dk = q64.shape
+    Dv = v64.shape[-1]
+    cu = _cu_array(cu_seqlens, B * T, B)
+    N = len(cu) - 1
+    h064 = None if initial_state is None else _f64(initial_state)
+    dhT64 = None if d_final_state is None else _f64(d_final_state)
+    out = {"dq": np.zeros_like(q64), "dk": np.zeros_like(k64), "dv": np.zeros_like(v64),
+           "dg": np.zeros_like(g64), "dbeta": np.zeros_like(b64),
+           "dh0": np.zeros((N, H, Dk, Dv), dtype=np.float64)}
+    nthreads = nthreads or os.cpu_count() or 1
+    rc = lib.kda_oracle_backward(_dp(q64), _dp(k64), _dp(v64), _dp(g64), _dp(b64), _dp(h064),
+                                 cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), N, H, Dk, Dv,
+                                 float(scale), _dp(do64), _dp(dhT64), _dp(out["dq"]),
+                                 _dp(out["dk"]), _dp(out["dv"]), _dp(out["dg"]),
+                                 _dp(out["dbeta"]), _dp(out["dh0"]), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle backward: invalid arguments or out of memory")
+    return out
+
+
+def oracle_gate_backward(z, dg, A=None, g_min: float = -5.0, lib_path: Optional[str] = None):
+    """Gradient of g = g_min * sigmoid(exp(A_h) z) (z, dg: [..., H, Dk]):
+    returns (dz, dA) with dA [H] the gradient w.r.t. A_h (None if A is None).
+
+    [KDA-blog §Chunkwise parallel form, new-gate equation], differentiated.
+    """
+    lib = _load(lib_path)
+    z64, dg64 = _f64(z), _f64(dg)
+    H, Dk = z64.shape[-2], z64.shape[-1]
+    rows = z64.size // (H * Dk)
+    A64 = None if A is None else _f64(A).reshape(H)
+    dz = np.empty_like(z64)
+    dA = None if A is None else np.empty(H, dtype=np.float64)
+    lib.kda_oracle_gate_bwd(_dp(z64), _dp(A64), float(g_min), _dp(dg64), rows, H, Dk, _dp(dz),
+                            _dp(dA))
+    return dz, dA
 
 
 def oracle_forward(q, k, v, z, beta, initial_state=None, cu_seqlens=None, A=None,

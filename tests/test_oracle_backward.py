@@ -1,0 +1,205 @@
+"""Pins of the fp64 backward oracle (gradients of the KDA recurrence and of
+the gate) against what the mathematics fixes.
+
+Sources, cited by page title and section:
+  [KDA-blog] "Kimi k3 技术报告详解（1）——架构再升华": section "Kimi Delta
+             Attention" (KDA equation), section "Chunkwise parallel form"
+             (new-gate equation). The pages give no backward pass; what is
+             pinned here is that the oracle's gradients are the derivatives
+             of the (separately pinned) forward oracle.
+
+Pins:
+  * central finite differences of the forward oracle, for every element of
+    every input (q, k, v, g, beta, initial state), on a varlen batch with an
+    empty sequence and a non-unit output scale;
+  * Euler's identity for functions linear in their argument: o and the final
+    state are jointly linear in (v, initial state), and o is linear in q;
+  * one-token closed forms of dv, dbeta, dq and the initial-state gradient;
+  * zero cotangents give zero gradients; an empty sequence passes the
+    final-state gradient straight through;
+  * gate: finite differences of the forward gate, and the closed form at
+    z = 0 (sigmoid' = 1/4);
+  * planted mistakes in a copy of the oracle's C source each fail the
+    finite-difference pin.
+"""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+from oracle import oracle_backward, oracle_gate, oracle_gate_backward, oracle_recurrence
+from oracle.oracle import _SRC
+
+CU = np.array([0, 4, 4, 7], dtype=np.int32)   # lengths 4, 0, 3
+
+
+def _problem(rng, T, H, Dk, Dv, N):
+    q = rng.standard_normal((1, T, H, Dk))
+    k = rng.standard_normal((1, T, H, Dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((1, T, H, Dv))
+    g = -5.0 * expit(rng.standard_normal((1, T, H, Dk)))
+    beta = expit(rng.standard_normal((1, T, H)))
+    h0 = rng.standard_normal((N, H, Dk, Dv))
+    do = rng.standard_normal((1, T, H, Dv))
+    dhT = rng.standard_normal((N, H, Dk, Dv))
+    return dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0), do, dhT
+
+
+def _loss(x, do, dhT, cu, scale, lib_path=None):
+    o, hT = oracle_recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], cu, scale,
+                              nthreads=1, lib_path=lib_path)
+    return float(np.sum(o * do) + np.sum(hT * dhT))
+
+
+def _fd_grads(x, do, dhT, cu, scale, eps=1e-5):
+    fd = {}
+    for name, arr in x.items():
+        grad = np.zeros_like(arr)
+        flat, gflat = arr.reshape(-1), grad.reshape(-1)
+        for i in range(flat.size):
+            keep = flat[i]
+            flat[i] = keep + eps
+            lp = _loss(x, do, dhT, cu, scale)
+            flat[i] = keep - eps
+            lm = _loss(x, do, dhT, cu, scale)
+            flat[i] = keep
+            gflat[i] = (lp - lm) / (2 * eps)
+        fd[name] = grad
+    return fd
+
+
+_NAMES = {"q": "dq", "k": "dk", "v": "dv", "g": "dg", "beta": "dbeta", "h0": "dh0"}
+
+
+def _fd_mismatch(got, fd):
+    """Worst relative disagreement over all inputs."""
+    worst = 0.0
+    for name, ref in fd.items():
+        err = np.max(np.abs(got[_NAMES[name]] - ref)) / max(1.0, np.max(np.abs(ref)))
+        worst = max(worst, err)
+    return worst
+
+
+def _fd_case():
+    rng = np.random.default_rng(7)
+    x, do, dhT = _problem(rng, int(CU[-1]), 2, 3, 2, len(CU) - 1)
+    return x, do, dhT, 0.7
+
+
+def test_backward_matches_finite_differences():
+    x, do, dhT, scale = _fd_case()
+    got = oracle_backward(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["h0"], dhT, CU, scale,
+                          nthreads=1)
+    fd = _fd_grads(x, do, dhT, CU, scale)
+    assert _fd_mismatch(got, fd) < 1e-7
+
+
+def test_backward_linear_identities():
+    """o and hT are linear in (v, h0) jointly, so for L = <do, o> + <dhT, hT>
+    Euler's identity gives <dv, v> + <dh0, h0> = L; o is linear in q and hT
+    does not depend on q, so <dq, q> = <do, o>."""
+    rng = np.random.default_rng(8)
+    cu = np.array([0, 50, 50, 81], dtype=np.int32)
+    x, do, dhT = _problem(rng, 81, 2, 16, 8, 3)
+    o, hT = oracle_recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], cu, 1.3)
+    got = oracle_backward(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["h0"], dhT, cu, 1.3)
+    L = np.sum(o * do) + np.sum(hT * dhT)
+    lhs = np.sum(got["dv"] * x["v"]) + np.sum(got["dh0"] * x["h0"])
+    assert abs(lhs - L) <= 1e-10 * max(1.0, abs(L))
+    assert abs(np.sum(got["dq"] * x["q"]) - np.sum(o * do)) <= 1e-10 * max(1.0, abs(L))
+
+
+def test_backward_one_token_closed_forms():
+    """One token from state S0: Sb = Diag(e^g) S0, u = Sb^T k,
+    d = beta (v - u), S1 = Sb + k d^T, o = s S1^T q. With G = dhT + s q do^T
+    (the total gradient on S1): dv = beta G^T k, dbeta = (G^T k).(v - u),
+    dq = s S1 do and dS0 = Diag(e^g) (I - beta k k^T) G (the map
+    S -> (I - beta k k^T) S is symmetric, so it is its own adjoint)."""
+    rng = np.random.default_rng(9)
+    Dk, Dv, s = 5, 4, 0.6
+    cu = np.array([0, 1], dtype=np.int32)
+    x, do, dhT = _problem(rng, 1, 1, Dk, Dv, 1)
+    q, k, v, g = (x[n][0, 0, 0] for n in ("q", "k", "v", "g"))
+    b = x["beta"][0, 0, 0]
+    S0, dS1 = x["h0"][0, 0], dhT[0, 0]
+    Sb = np.exp(g)[:, None] * S0
+    u = Sb.T @ k
+    S1 = Sb + np.outer(k, b * (v - u))
+    G = dS1 + s * np.outer(q, do[0, 0, 0])
+    got = oracle_backward(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["h0"], dhT, cu, s)
+    np.testing.assert_allclose(got["dv"][0, 0, 0], b * (G.T @ k), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(got["dbeta"][0, 0, 0], (G.T @ k) @ (v - u), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(got["dq"][0, 0, 0], s * S1 @ do[0, 0, 0], rtol=1e-12, atol=1e-12)
+    ref_dS0 = np.exp(g)[:, None] * ((np.eye(Dk) - b * np.outer(k, k)) @ G)
+    np.testing.assert_allclose(got["dh0"][0, 0], ref_dS0, rtol=1e-12, atol=1e-12)
+
+
+def test_backward_zero_cotangent_and_empty_sequence():
+    rng = np.random.default_rng(10)
+    x, do, dhT = _problem(rng, int(CU[-1]), 2, 4, 3, 3)
+    zero = oracle_backward(x["q"], x["k"], x["v"], x["g"], x["beta"], np.zeros_like(do), x["h0"],
+                           None, CU)
+    for name in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert not np.any(zero[name]), name
+    got = oracle_backward(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["h0"], dhT, CU)
+    assert np.array_equal(got["dh0"][1], dhT[1])     # sequence 1 is empty
+
+
+def test_gate_backward_matches_finite_differences_and_closed_form():
+    rng = np.random.default_rng(11)
+    z = rng.standard_normal((2, 3, 4, 5)) * 3
+    A = rng.standard_normal(4)
+    dg = rng.standard_normal(z.shape)
+    dz, dA = oracle_gate_backward(z, dg, A, -5.0)
+    eps = 1e-6
+    fd_z = (oracle_gate(z + eps, A, -5.0) - oracle_gate(z - eps, A, -5.0)) / (2 * eps) * dg
+    np.testing.assert_allclose(dz, fd_z, rtol=1e-7, atol=1e-9)
+    for h in range(4):
+        Ap, Am = A.copy(), A.copy()
+        Ap[h] += eps
+        Am[h] -= eps
+        fd = np.sum((oracle_gate(z, Ap, -5.0) - oracle_gate(z, Am, -5.0)) * dg) / (2 * eps)
+        assert abs(dA[h] - fd) <= 1e-7 * max(1.0, abs(fd))
+    # z = 0: sigmoid'(0) = 1/4, so dz = dg g_min e^A / 4 and dA = 0
+    z0 = np.zeros((1, 1, 2, 3))
+    dg0 = np.ones_like(z0)
+    dz0, dA0 = oracle_gate_backward(z0, dg0, np.array([0.0, np.log(2.0)]), -5.0)
+    np.testing.assert_allclose(dz0[0, 0, 0], -1.25, rtol=1e-15)
+    np.testing.assert_allclose(dz0[0, 0, 1], -2.5, rtol=1e-15)
+    assert not np.any(dA0)
+    dz_none, dA_none = oracle_gate_backward(z0, dg0, None, -5.0)
+    np.testing.assert_allclose(dz_none, -1.25, rtol=1e-15)
+    assert dA_none is None
+
+
+MUTANTS = [
+    # drop the write-back path of u = Sb^T k into the state gradient
+    ("dS[i * Dv + j] += kt[i] * dd[j];", "(void)0;"),
+    # forget that d carries beta: dv = dd
+    ("dvt[j] = bt * dd[j];", "dvt[j] = dd[j];"),
+    # decay gradient against the undecayed state
+    ("acc += dS[i * Dv + j] * Sb[i * Dv + j];", "acc += dS[i * Dv + j] * Sp[i * Dv + j];"),
+    # read o before the write instead of after it
+    ("acc += S[i * Dv + j] * dot[j];", "acc += Sp[i * Dv + j] * dot[j];"),
+]
+
+
+@pytest.mark.parametrize("old,new", MUTANTS, ids=["no-dS-from-u", "dv-no-beta", "dg-undecayed",
+                                                   "dq-old-state"])
+def test_planted_mistakes_fail_the_pin(tmp_path, old, new):
+    src = open(_SRC).read()
+    assert src.count(old) == 1, old
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new))
+    lib = str(tmp_path / "libmutant.so")
+    subprocess.run(["gcc", "-O2", "-std=gnu99", "-shared", "-fPIC", str(path), "-o", lib, "-lm",
+                    "-lpthread"], check=True)
+    x, do, dhT, scale = _fd_case()
+    got = oracle_backward(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["h0"], dhT, CU, scale,
+                          nthreads=1, lib_path=lib)
+    fd = _fd_grads(x, do, dhT, CU, scale)   # from the unmodified forward
+    assert _fd_mismatch(got, fd) > 1e-3
