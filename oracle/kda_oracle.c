@@ -310,12 +310,12 @@ static int unit_backward(long T, int Dk, int Dv, const double* q, const double* 
     double bt = beta[t * bs];
     double* S = st + (size_t)(t + 1) * ssz;
     for (int i = 0; i < Dk; ++i) {
-      double a = exp(gt[i]);
-      for (int j = 0; j < Dv; ++j) S[i * Dv + j] = a * st[(size_t)t * ssz + i * Dv + j];
+      double al = exp(gt[i]);
+      for (int j = 0; j < Dv; ++j) S[i * Dv + j] = al * st[(size_t)t * ssz + i * Dv + j];
     }
     for (int j = 0; j < Dv; ++j) u[j] = 0.0;
     for (int i = 0; i < Dk; ++i)
-      for (int j = 0; j < Dv; ++j) u[j] += S[i * Dv + j] * kt[i];
+      for (int j = 0; j < Dv; ++j) u[j] += kt[i] * S[i * Dv + j];
     for (int j = 0; j < Dv; ++j) d[j] = bt * (vt[j] - u[j]);
     for (int i = 0; i < Dk; ++i)
       for (int j = 0; j < Dv; ++j) S[i * Dv + j] += kt[i] * d[j];
@@ -337,12 +337,12 @@ static int unit_backward(long T, int Dk, int Dv, const double* q, const double* 
     }
     /* recompute the decayed state, u and d of this token */
     for (int i = 0; i < Dk; ++i) {
-      double a = exp(gt[i]);
-      for (int j = 0; j < Dv; ++j) Sb[i * Dv + j] = a * Sp[i * Dv + j];
+      double al = exp(gt[i]);
+      for (int j = 0; j < Dv; ++j) Sb[i * Dv + j] = al * Sp[i * Dv + j];
     }
     for (int j = 0; j < Dv; ++j) u[j] = 0.0;
     for (int i = 0; i < Dk; ++i)
-      for (int j = 0; j < Dv; ++j) u[j] += Sb[i * Dv + j] * kt[i];
+      for (int j = 0; j < Dv; ++j) u[j] += kt[i] * Sb[i * Dv + j];
     for (int j = 0; j < Dv; ++j) d[j] = bt * (vt[j] - u[j]);
     /* 4. S = Sb + k d^T */
     for (int j = 0; j < Dv; ++j) dd[j] = 0.0;
@@ -373,10 +373,10 @@ static int unit_backward(long T, int Dk, int Dv, const double* q, const double* 
     }
     /* 1. Sb = Diag(alpha) S_prev */
     for (int i = 0; i < Dk; ++i) {
-      double a = exp(gt[i]), acc = 0.0;
+      double al = exp(gt[i]), acc = 0.0;
       for (int j = 0; j < Dv; ++j) {
         acc += dS[i * Dv + j] * Sb[i * Dv + j];
-        dS[i * Dv + j] *= a;
+        dS[i * Dv + j] *= al;
       }
       dgt[i] = acc;
     }
