@@ -1,4 +1,4 @@
-"""MI355X-native KDA (Kimi Delta Attention) forward: gate, chunkwise forward and
+"""MI355X-native KDA (Kimi Delta Attention): gate, chunkwise forward and backward,
 decode step, backed by hand-written gfx950 HIP kernels in libkda.so.
 
 Public API (thin wrappers over the C ABI in include/kda.h):
@@ -11,9 +11,13 @@ Public API (thin wrappers over the C ABI in include/kda.h):
     chunk_fwd_split(q, k, v, g, beta, initial_state=None, cu_seqlens=None, segments=8, ...)
     chunk_fwd_gated(q, k, v, g, beta, out_gate, norm_weight=None, eps=1e-6, ...)
     gated_rmsnorm(o, out_gate, norm_weight=None, eps=1e-6)
+    chunk_bwd(q, k, v, g, beta, do, initial_state=None, d_final_state=None, ...)
+    gate_bwd(z, dg, A_log=None, g_min=-5.0)
 """
-from .ops import (chunk_fwd, chunk_fwd_gated, chunk_fwd_split, compose_states, gate,  # noqa: F401
-                  gated_rmsnorm, recurrent_step, split_lengths, transition, workspace_size)
+from .ops import (bwd_workspace_size, chunk_bwd, chunk_fwd, chunk_fwd_gated,  # noqa: F401
+                  chunk_fwd_split, compose_states, gate, gate_bwd, gated_rmsnorm, recurrent_step,
+                  split_lengths, transition, workspace_size)
 
-__all__ = ["chunk_fwd", "chunk_fwd_gated", "chunk_fwd_split", "compose_states", "gate",
-           "gated_rmsnorm", "recurrent_step", "split_lengths", "transition", "workspace_size"]
+__all__ = ["bwd_workspace_size", "chunk_bwd", "chunk_fwd", "chunk_fwd_gated", "chunk_fwd_split",
+           "compose_states", "gate", "gate_bwd", "gated_rmsnorm", "recurrent_step",
+           "split_lengths", "transition", "workspace_size"]

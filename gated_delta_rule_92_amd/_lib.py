@@ -27,7 +27,8 @@ KDA_GATE_SOFTPLUS = 3
 # Every symbol include/kda.h declares.
 EXPORTED = ("kda_status_string", "kda_version", "kda_gate", "kda_chunk_fwd_workspace_size",
             "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_gated_rmsnorm", "kda_chunk_transition",
-            "kda_compose_states", "kda_recurrent_step")
+            "kda_compose_states", "kda_recurrent_step", "kda_chunk_bwd_workspace_size",
+            "kda_chunk_bwd", "kda_gate_bwd")
 
 _lib = None
 
@@ -74,6 +75,15 @@ def load(path: str = LIB_PATH):
     lib.kda_recurrent_step.argtypes = [vp, vp, vp, i32, fp, i32, fp, f32, fp, fp, i32, i32, i32,
                                        i32, f32, vp, vp]
     lib.kda_recurrent_step.restype = i32
+    lib.kda_chunk_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
+                                                 ctypes.POINTER(sz)]
+    lib.kda_chunk_bwd_workspace_size.restype = i32
+    lib.kda_chunk_bwd.argtypes = [vp, vp, vp, i32, fp, i32, fp, f32, fp, fp, ip,
+                                  i32, i32, i32, i32, i32, i32, i32,  # N B T H Dk Dv chunk
+                                  f32, vp, fp, vp, vp, vp, fp, fp, fp, vp, sz, vp]
+    lib.kda_chunk_bwd.restype = i32
+    lib.kda_gate_bwd.argtypes = [fp, fp, f32, fp, ctypes.c_long, i32, i32, fp, fp, vp]
+    lib.kda_gate_bwd.restype = i32
     if path == LIB_PATH:
         _lib = lib
     return lib

@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libkda.so")
 ARCH = "gfx950"
 
-SOURCES = ["kda_api.cpp", "kda_gate.hip", "kda_recurrent.hip", "kda_chunk.hip", "kda_chunk_pipe.hip",
+SOURCES = ["kda_api.cpp", "kda_gate.hip", "kda_recurrent.hip", "kda_chunk.hip", "kda_chunk_pipe.hip", "kda_backward.hip",
            "kda_compose.hip", "kda_epilogue.hip"]
 
 # Packed fp32 VALU instructions are disabled for every device compile.

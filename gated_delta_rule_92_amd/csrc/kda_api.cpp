@@ -294,4 +294,95 @@ kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v, kda
   return launch_status(kda::launch_recurrent(r, reinterpret_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+size_t bwd_elt(kda_dtype_t dtype) { return dtype == KDA_BFLOAT16 ? 2 : 4; }
+
+// Upper bound on the checkpoint slots of either layout (dense: B sequences of
+// ceil(T / 16) tiles; packed: floor(T / 16) + N).
+long bwd_slots_bound(int B, int T, int N) {
+  const long dense = (long)B * ((T + 15) / 16);
+  const long packed = (long)B * T / 16 + N;
+  return dense > packed ? dense : packed;
+}
+
+}  // namespace
+
+kda_status_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv, int N, int chunk,
+                                          kda_dtype_t dtype, size_t* bytes) {
+  if (!bytes || B <= 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || N < 0 || chunk <= 0)
+    return KDA_ERROR_INVALID_VALUE;
+  if (dtype != KDA_FLOAT32 && dtype != KDA_BFLOAT16) return KDA_ERROR_INVALID_VALUE;
+  const size_t e = bwd_elt(dtype);
+  const size_t ck = round_up((size_t)bwd_slots_bound(B, T, N) * H * Dk * Dv * e, kWorkspaceAlign);
+  const size_t tok = round_up((size_t)B * T * H * Dv * e, kWorkspaceAlign);
+  *bytes = 2 * ck + 3 * tok;
+  return KDA_SUCCESS;
+}
+
+kda_status_t kda_chunk_bwd(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                           const float* g, kda_gate_input_t gate_input, const float* A_log,
+                           float g_min, const float* beta, const float* initial_state,
+                           const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk, int Dv,
+                           int chunk, float scale, const void* d_o, const float* d_final_state,
+                           void* dq, void* dk, void* dv, float* dg, float* dbeta,
+                           float* d_initial_state, void* workspace, size_t workspace_bytes,
+                           kda_stream_t stream) {
+  kda::Seqs s;
+  kda_status_t st = check_seqs(cu_seqlens, N, B, T, &s);
+  if (st != KDA_SUCCESS) return st;
+  if (!cu_seqlens && N != B) return KDA_ERROR_INVALID_VALUE;
+  if (H <= 0 || Dk <= 0 || Dv <= 0 || chunk <= 0) return KDA_ERROR_INVALID_VALUE;
+  if (dtype != KDA_FLOAT32 && dtype != KDA_BFLOAT16) return KDA_ERROR_INVALID_VALUE;
+  if (gate_input != KDA_GATE_LOGDECAY && gate_input != KDA_GATE_CUMSUM &&
+      gate_input != KDA_GATE_LOGITS && gate_input != KDA_GATE_SOFTPLUS)
+    return KDA_ERROR_INVALID_VALUE;
+  if (gate_input == KDA_GATE_LOGITS && !(g_min < 0.0f)) return KDA_ERROR_INVALID_VALUE;
+  if (s.Ttot > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
+    return KDA_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(d_o) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dg) ||
+      !aligned16(initial_state) || !aligned16(d_final_state) || !aligned16(d_initial_state))
+    return KDA_ERROR_INVALID_VALUE;
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) % kWorkspaceAlign) != 0)
+    return KDA_ERROR_INVALID_VALUE;
+  if (chunk != 64) return KDA_ERROR_NOT_SUPPORTED;
+  if (gate_input == KDA_GATE_CUMSUM || gate_input == KDA_GATE_SOFTPLUS)
+    return KDA_ERROR_NOT_SUPPORTED;
+  if (gate_input == KDA_GATE_LOGITS && g_min < kda::kMinFusedGmin) return KDA_ERROR_NOT_SUPPORTED;
+  if (!kda::chunk_bwd_supported(Dk, Dv)) return KDA_ERROR_NOT_SUPPORTED;
+  size_t need = 0;
+  st = kda_chunk_bwd_workspace_size(B, T, H, Dk, Dv, s.N, chunk, dtype, &need);
+  if (st != KDA_SUCCESS) return st;
+  if (!workspace || workspace_bytes < need) return KDA_ERROR_INSUFFICIENT_WORKSPACE;
+  const long slots = kda::chunk_bwd_slots(s);
+  if (slots > 0x7fffffffL || (long)s.N * H > 0x7fffffffL) return KDA_ERROR_NOT_SUPPORTED;
+  if (s.N == 0) return KDA_SUCCESS;
+  const size_t e = bwd_elt(dtype);
+  const size_t ck = round_up((size_t)bwd_slots_bound(B, T, s.N) * H * Dk * Dv * e, kWorkspaceAlign);
+  const size_t tok = round_up((size_t)B * T * H * Dv * e, kWorkspaceAlign);
+  char* ws = static_cast<char*>(workspace);
+  kda::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.gate = (int)gate_input;
+  a.A_log = A_log; a.g_min = g_min; a.beta = beta; a.h0 = initial_state;
+  a.cu = cu_seqlens; a.N = s.N; a.T = T; a.H = H; a.scale = scale;
+  a.dO = d_o; a.dhT = d_final_state;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = d_initial_state;
+  a.ckS = ws; a.ckdS = ws + ck; a.U = ws + 2 * ck; a.Vt = ws + 2 * ck + tok;
+  a.dY = ws + 2 * ck + 2 * tok;
+  return launch_status(kda::launch_chunk_bwd(a, dtype == KDA_BFLOAT16, Dk, Dv, slots,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_gate_bwd(const float* z, const float* A_log, float g_min, const float* dg,
+                          long rows, int H, int Dk, float* dz, float* dA_log,
+                          kda_stream_t stream) {
+  if (rows < 0 || H <= 0 || Dk <= 0 || !(g_min < 0.0f)) return KDA_ERROR_INVALID_VALUE;
+  if (rows > 0 && (!z || !dg || !dz)) return KDA_ERROR_INVALID_VALUE;
+  if (!aligned16(z) || !aligned16(dg) || !aligned16(dz)) return KDA_ERROR_INVALID_VALUE;
+  if (Dk % 4 != 0 || Dk > 1024 || H > 65535) return KDA_ERROR_NOT_SUPPORTED;
+  return launch_status(kda::launch_gate_bwd(z, A_log, g_min, dg, rows, H, Dk, dz, dA_log,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -1,0 +1,761 @@
+// Backward pass of the chunkwise KDA forward on CDNA4 matrix cores.
+//
+// Sources, cited by page title and section:
+//   [KDA-blog] "Kimi k3 技术报告详解（1）——架构再升华", section "Kimi Delta
+//              Attention" (KDA equation) and section "Chunkwise parallel
+//              form" (gamma equation, W/U and pseudo-value equations, A/O
+//              equation; 16-token tiles). The pages give no backward pass;
+//              what follows is the derivative of the 16-token tile form of
+//              the forward, checked against the derivative of the token
+//              recurrence.
+//
+// Tile form (one (sequence, head) unit, tiles of 16 tokens, L valid). With G
+// the inclusive cumulative log-decay inside the tile, Gamma = e^G,
+// Kg = K*Gamma, Qg = s Q*Gamma, Kt = K*e^{G_L - G},
+// Akk[r,i] = beta_r sum_c k_r k_i e^{G_r-G_i} (i < r),
+// Aqk[r,i] = s sum_c q_r k_i e^{G_r-G_i} (i <= r), T = (I + Akk)^{-1}:
+//   forward    U = V - Kg S,  V~ = T (beta U),  S' = Diag(Gamma_L) S + Kt^T V~,
+//              O = Qg S + Aqk V~
+//   reverse    dV~ = Kt dS' + Aqk^T dO,  dY = T^T dV~,
+//              dS = Diag(Gamma_L) dS' + Qg^T dO - Kg^T (beta dY)
+//   per tile   dQg = dO S^T,  dKg = -(beta dY) S^T,  dKt = V~ dS'^T,
+//              dGamma_L = rowsum(dS' * S),  dAqk = Tril(dO V~^T),
+//              dAkk = -StrictTril(dY V~^T),  dV = beta dY,
+//              dbeta = rowsum(dY * U) + rowsum(dAkk * Akk / beta),
+//              then through the decay factors into dq, dk and dG, and
+//              dg = reverse cumulative sum of dG inside the tile.
+// The triangular products split their decay at a reference point rho (G of
+// the tile's eighth token): left factors e^{G-rho}, right factors e^{rho-G},
+// at most e^{8 * 5.5} each way for g >= -5.5. The products do not depend on
+// rho, so rho carries no derivative.
+//
+// Three kernels:
+//   fwd_scan   one workgroup per unit, tiles in order: writes the state
+//              entering every tile (checkpoint), U and V~.
+//   rev_scan   one workgroup per unit, tiles in reverse: writes the state
+//              gradient leaving every tile (checkpoint) and dY, and dS_0.
+//   tile_grad  one workgroup per (tile, head), all tiles at once: every
+//              input gradient of the tile from the two checkpoints.
+// In the scans wavefront w owns value columns [w*Dv/4, (w+1)*Dv/4) of the
+// state, which the recurrence never mixes; in tile_grad it owns channel
+// tiles w, w+4, ...
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int BT = 16;   // tokens per tile
+constexpr int NWB = 4;   // wavefronts per workgroup
+constexpr int NTH = 64 * NWB;
+
+template <typename T>
+constexpr int pad_of() { return sizeof(T) == 2 ? 8 : 4; }
+
+template <typename T, int DK, int DV>
+struct BCfg {
+  static constexpr int DKP = DK + pad_of<T>();  // row stride of [16][DK] operand arrays
+  static constexpr int TSP = BT + pad_of<T>();  // row stride of token-contiguous arrays
+  static constexpr int NTV = DV / 64;           // value-column tiles per wavefront (scans)
+  static constexpr int NCT = DK / 64;           // channel tiles per wavefront (tile_grad)
+  static constexpr int NKB = DK / 32;           // 32-wide contraction blocks over d_k
+  static constexpr int NVB = DV / 32;           // ... over d_v
+};
+
+struct Unit {
+  long t0;    // first token of the sequence in the packed token axis
+  int len;    // tokens in the sequence
+  long base;  // first checkpoint slot of the sequence
+};
+
+__device__ __forceinline__ Unit unit_of(const BwdArgs& a, int n) {
+  Unit u;
+  if (a.cu) {
+    const int s = a.cu[n], e = a.cu[n + 1];
+    u.t0 = s;
+    u.len = e - s;
+    u.base = (long)(s / BT) + n;
+  } else {
+    u.t0 = (long)n * a.T;
+    u.len = a.T;
+    u.base = (long)n * ((a.T + BT - 1) / BT);
+  }
+  return u;
+}
+
+// ---------------------------------------------------------------- tile load --
+// fp32 copies of one tile's rows in LDS: q, k, the cumulative log-decay G in
+// log2 units, beta. Rows past the tile's end are zero, so G stays constant
+// there and every product with them vanishes.
+template <int DK>
+struct TileF32 {
+  float q[BT][DK + 4];
+  float k[BT][DK + 4];
+  float G[BT][DK + 4];
+  float beta[BT];
+};
+
+template <typename T, int DK>
+__device__ __forceinline__ void load_rows(float (*dst)[DK + 4], const T* src, long t0, int L, int h,
+                                          int H) {
+  constexpr int Q = DK / 4;
+  for (int idx = threadIdx.x; idx < BT * Q; idx += NTH) {
+    const int r = idx / Q, c = (idx % Q) * 4;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (r < L) x = load4_f32(src + ((t0 + r) * H + h) * (long)DK + c);
+    *reinterpret_cast<f32x4*>(&dst[r][c]) = x;
+  }
+}
+
+// Loads q (if wanted), k, the gate and beta of tokens [t0, t0+L), then forms G
+// (two barriers inside; the caller's LDS arrays are free on entry).
+template <typename T, int DK>
+__device__ void load_tile(TileF32<DK>& tf, const BwdArgs& a, long t0, int L, int h, bool want_q) {
+  const int H = a.H;
+  if (want_q) load_rows<T, DK>(tf.q, static_cast<const T*>(a.q), t0, L, h, H);
+  load_rows<T, DK>(tf.k, static_cast<const T*>(a.k), t0, L, h, H);
+  load_rows<float, DK>(tf.G, a.g, t0, L, h, H);
+  if (threadIdx.x < BT) tf.beta[threadIdx.x] = (int)threadIdx.x < L ? a.beta[(t0 + threadIdx.x) * H + h] : 0.f;
+  __syncthreads();
+  if (threadIdx.x < DK) {
+    const int c = threadIdx.x;
+    const float es = (a.gate == kGateLogits && a.A_log) ? __expf(a.A_log[h]) : 1.f;
+    float run = 0.f;
+#pragma unroll
+    for (int r = 0; r < BT; ++r) {
+      float gv = tf.G[r][c];
+      if (a.gate == kGateLogits && r < L)
+        gv = a.g_min * __builtin_amdgcn_rcpf(1.f + fast_exp2(-kLog2e * es * gv));
+      run += gv;
+      tf.G[r][c] = run * kLog2e;
+    }
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------ tile inverse --
+// 16 x 16 transpose of an accumulator-layout tile through LDS (one wavefront).
+__device__ __forceinline__ f32x4 transpose16(const f32x4& x, float (*xs)[17], int lr, int lg) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) xs[4 * lg + e][lr] = x[e];
+  f32x4 y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = xs[lr][4 * lg + e];
+  return y;
+}
+
+// (I - N)^{-1} = (I + N)(I + N^2)(I + N^4)(I + N^8) for strictly lower
+// triangular N (N^16 = 0), fp32 matrix cores, one wavefront. N and the
+// result are in accumulator layout. Mma<float>::k16(P, Q, C) = P^T Q + C, and
+// every factor is a polynomial in N, so all factors commute.
+__device__ f32x4 unit_lower_inverse(const f32x4& N, float (*xs)[17], int lr, int lg) {
+  using MF = Mma<float>;
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  f32x4 I4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) I4[e] = (4 * lg + e == lr) ? 1.f : 0.f;
+  const f32x4 Nt = transpose16(N, xs, lr, lg);
+  const f32x4 N2 = MF::k16(Nt, N, z);
+  const f32x4 N2t = transpose16(N2, xs, lr, lg);
+  const f32x4 N4 = MF::k16(N2t, N2, z);
+  const f32x4 N4t = transpose16(N4, xs, lr, lg);
+  const f32x4 N8 = MF::k16(N4t, N4, z);
+  const f32x4 N8t = transpose16(N8, xs, lr, lg);
+  const f32x4 X1 = I4 + N + N2 + MF::k16(Nt, N2, z);
+  const f32x4 X2 = X1 + MF::k16(N4t, X1, z);
+  return X2 + MF::k16(N8t, X2, z);
+}
+
+// X Y^T for two row-major [16][DKP] operand arrays (contraction over d_k),
+// in accumulator layout: element e of lane l is row 4*(l/16)+e, column l%16.
+// The caller applies the triangular mask.
+template <typename T, int DK, int DKP>
+__device__ __forceinline__ f32x4 tri_product(const T (*X)[DKP], const T (*Y)[DKP], int lr, int lg) {
+  using M = Mma<T>;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < DK / 32; ++kb)
+    acc = M::k32(load_frag(&X[lr][32 * kb + 4 * lg]), load_frag(&X[lr][32 * kb + 16 + 4 * lg]),
+                 load_frag(&Y[lr][32 * kb + 4 * lg]), load_frag(&Y[lr][32 * kb + 16 + 4 * lg]), acc);
+  return acc;
+}
+
+template <typename T>
+__device__ __forceinline__ void st(void* base, long idx, float x) {
+  static_cast<T*>(base)[idx] = (T)x;
+}
+
+// ================================================================ fwd_scan ==
+template <typename T, int DK, int DV>
+struct FwdSmem {
+  using C = BCfg<T, DK, DV>;
+  TileF32<DK> tf;
+  float v[BT][DV + 4];
+  float gl[DK];                // Gamma_L per channel
+  float xs[16][17];            // transpose scratch
+  T Kgn[BT][C::DKP];           // -K Gamma
+  T Kl[BT][C::DKP];            // K e^{G - rho}
+  T Kd[BT][C::DKP];            // K e^{rho - G}
+  T KtT[DK][C::TSP];           // (K e^{G_L - G})^T
+  T Tm[BT][C::TSP];            // T, row-major
+};
+
+template <typename T, int DK, int DV>
+__global__ void __launch_bounds__(NTH) bwd_fwd_scan(BwdArgs a) {
+  using C = BCfg<T, DK, DV>;
+  using M = Mma<T>;
+  __shared__ FwdSmem<T, DK, DV> sm;
+  const int n = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const Unit un = unit_of(a, n);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int H = a.H;
+
+  f32x4 S[DK / 16][C::NTV];
+#pragma unroll
+  for (int tr = 0; tr < DK / 16; ++tr)
+#pragma unroll
+    for (int tv = 0; tv < C::NTV; ++tv) {
+      const int col = (w * C::NTV + tv) * 16 + lr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * tr + 4 * lg + e;
+        S[tr][tv][e] = a.h0 ? a.h0[(((long)n * H + h) * DK + row) * DV + col] : 0.f;
+      }
+    }
+
+  const int nt = (un.len + BT - 1) / BT;
+  for (int j = 0; j < nt; ++j) {
+    const long t0 = un.t0 + (long)j * BT;
+    const int L = min(BT, un.len - j * BT);
+    // checkpoint: the state entering this tile
+    const long ck = ((un.base + j) * H + h) * (long)DK * DV;
+#pragma unroll
+    for (int tr = 0; tr < DK / 16; ++tr)
+#pragma unroll
+      for (int tv = 0; tv < C::NTV; ++tv) {
+        const int col = (w * C::NTV + tv) * 16 + lr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          st<T>(a.ckS, ck + (long)(16 * tr + 4 * lg + e) * DV + col, S[tr][tv][e]);
+      }
+
+    load_tile<T, DK>(sm.tf, a, t0, L, h, false);
+    load_rows<T, DV>(sm.v, static_cast<const T*>(a.v), t0, L, h, H);
+    for (int idx = threadIdx.x; idx < BT * DK; idx += NTH) {
+      const int r = idx / DK, c = idx % DK;
+      const float G = sm.tf.G[r][c], kk = sm.tf.k[r][c];
+      const float rho = sm.tf.G[7][c], GL = sm.tf.G[BT - 1][c];
+      sm.Kgn[r][c] = (T)(-kk * fast_exp2(G));
+      sm.Kl[r][c] = (T)(kk * fast_exp2(G - rho));
+      sm.Kd[r][c] = (T)(kk * fast_exp2(rho - G));
+      sm.KtT[c][r] = (T)(kk * fast_exp2(GL - G));
+      if (r == 0) sm.gl[c] = fast_exp2(GL);
+    }
+    __syncthreads();
+
+    if (w == 0) {
+      const f32x4 At = tri_product<T, DK, C::DKP>(sm.Kl, sm.Kd, lr, lg);
+      f32x4 N;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * lg + e;
+        N[e] = lr < r ? -sm.tf.beta[r] * At[e] : 0.f;
+      }
+      const f32x4 Tm = unit_lower_inverse(N, sm.xs, lr, lg);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.Tm[4 * lg + e][lr] = (T)Tm[e];
+    }
+    // U = V - Kg S for this wavefront's columns
+    f32x4 U[C::NTV];
+#pragma unroll
+    for (int tv = 0; tv < C::NTV; ++tv) {
+      const int col = (w * C::NTV + tv) * 16 + lr;
+      f32x4 acc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = sm.v[4 * lg + e][col];
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+        acc = M::k32(load_frag(&sm.Kgn[lr][32 * kb + 4 * lg]),
+                     load_frag(&sm.Kgn[lr][32 * kb + 16 + 4 * lg]), M::make(S[2 * kb][tv]),
+                     M::make(S[2 * kb + 1][tv]), acc);
+      U[tv] = acc;
+    }
+    __syncthreads();  // T ready
+
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tv = 0; tv < C::NTV; ++tv) {
+      const int col = (w * C::NTV + tv) * 16 + lr;
+      f32x4 bu;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bu[e] = sm.tf.beta[4 * lg + e] * U[tv][e];
+      const f32x4 Vt = M::k16(load_frag(&sm.Tm[lr][4 * lg]), M::make(bu), z);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * lg + e;
+        if (r < L) {
+          const long idx = ((t0 + r) * H + h) * (long)DV + col;
+          st<T>(a.U, idx, U[tv][e]);
+          st<T>(a.Vt, idx, Vt[e]);
+        }
+      }
+      const auto vf = M::make(Vt);
+#pragma unroll
+      for (int tr = 0; tr < DK / 16; ++tr) {
+        f32x4 s = S[tr][tv];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[e] *= sm.gl[16 * tr + 4 * lg + e];
+        S[tr][tv] = M::k16(load_frag(&sm.KtT[16 * tr + lr][4 * lg]), vf, s);
+      }
+    }
+    __syncthreads();  // LDS reused by the next tile
+  }
+}
+
+// ================================================================ rev_scan ==
+template <typename T, int DK, int DV>
+struct RevSmem {
+  using C = BCfg<T, DK, DV>;
+  TileF32<DK> tf;
+  float gl[DK];
+  float xs[16][17];
+  T Kt[BT][C::DKP];            // K e^{G_L - G}
+  T Kl[BT][C::DKP];
+  T Ql[BT][C::DKP];            // s Q e^{G - rho}
+  T Kd[BT][C::DKP];
+  T QgT[DK][C::TSP];           // (s Q Gamma)^T
+  T KgT[DK][C::TSP];           // (K Gamma)^T
+  T dOT[DV][C::TSP];           // dO^T
+  T TT[BT][C::TSP];            // T^T, row-major
+  T AqkT[BT][C::TSP];          // Aqk^T, row-major
+};
+
+template <typename T, int DK, int DV>
+__global__ void __launch_bounds__(NTH) bwd_rev_scan(BwdArgs a) {
+  using C = BCfg<T, DK, DV>;
+  using M = Mma<T>;
+  __shared__ RevSmem<T, DK, DV> sm;
+  const int n = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const Unit un = unit_of(a, n);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int H = a.H;
+  const float sc = a.scale;
+
+  f32x4 dS[DK / 16][C::NTV];
+#pragma unroll
+  for (int tr = 0; tr < DK / 16; ++tr)
+#pragma unroll
+    for (int tv = 0; tv < C::NTV; ++tv) {
+      const int col = (w * C::NTV + tv) * 16 + lr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * tr + 4 * lg + e;
+        dS[tr][tv][e] = a.dhT ? a.dhT[(((long)n * H + h) * DK + row) * DV + col] : 0.f;
+      }
+    }
+
+  const int nt = (un.len + BT - 1) / BT;
+  for (int j = nt - 1; j >= 0; --j) {
+    const long t0 = un.t0 + (long)j * BT;
+    const int L = min(BT, un.len - j * BT);
+    // checkpoint: the state gradient leaving this tile
+    const long ck = ((un.base + j) * H + h) * (long)DK * DV;
+#pragma unroll
+    for (int tr = 0; tr < DK / 16; ++tr)
+#pragma unroll
+      for (int tv = 0; tv < C::NTV; ++tv) {
+        const int col = (w * C::NTV + tv) * 16 + lr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          st<T>(a.ckdS, ck + (long)(16 * tr + 4 * lg + e) * DV + col, dS[tr][tv][e]);
+      }
+
+    load_tile<T, DK>(sm.tf, a, t0, L, h, true);
+    {
+      constexpr int Q = DV / 4;
+      const T* dO = static_cast<const T*>(a.dO);
+      for (int idx = threadIdx.x; idx < BT * Q; idx += NTH) {
+        const int r = idx / Q, c = (idx % Q) * 4;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (r < L) x = load4_f32(dO + ((t0 + r) * H + h) * (long)DV + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.dOT[c + e][r] = (T)x[e];
+      }
+    }
+    for (int idx = threadIdx.x; idx < BT * DK; idx += NTH) {
+      const int r = idx / DK, c = idx % DK;
+      const float G = sm.tf.G[r][c], kk = sm.tf.k[r][c], qq = sc * sm.tf.q[r][c];
+      const float rho = sm.tf.G[7][c], GL = sm.tf.G[BT - 1][c];
+      const float gam = fast_exp2(G), el = fast_exp2(G - rho);
+      sm.Kt[r][c] = (T)(kk * fast_exp2(GL - G));
+      sm.Kl[r][c] = (T)(kk * el);
+      sm.Ql[r][c] = (T)(qq * el);
+      sm.Kd[r][c] = (T)(kk * fast_exp2(rho - G));
+      sm.QgT[c][r] = (T)(qq * gam);
+      sm.KgT[c][r] = (T)(kk * gam);
+      if (r == 0) sm.gl[c] = fast_exp2(GL);
+    }
+    __syncthreads();
+
+    if (w == 0) {
+      const f32x4 At = tri_product<T, DK, C::DKP>(sm.Kl, sm.Kd, lr, lg);
+      f32x4 N;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * lg + e;
+        N[e] = lr < r ? -sm.tf.beta[r] * At[e] : 0.f;
+      }
+      const f32x4 Tm = unit_lower_inverse(N, sm.xs, lr, lg);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.TT[lr][4 * lg + e] = (T)Tm[e];
+    } else if (w == 1) {
+      const f32x4 Aq = tri_product<T, DK, C::DKP>(sm.Ql, sm.Kd, lr, lg);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.AqkT[lr][4 * lg + e] = (T)(lr <= 4 * lg + e ? Aq[e] : 0.f);
+    }
+    // dV~ = Kt dS' (first part)
+    f32x4 dV[C::NTV];
+#pragma unroll
+    for (int tv = 0; tv < C::NTV; ++tv) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+        acc = M::k32(load_frag(&sm.Kt[lr][32 * kb + 4 * lg]),
+                     load_frag(&sm.Kt[lr][32 * kb + 16 + 4 * lg]), M::make(dS[2 * kb][tv]),
+                     M::make(dS[2 * kb + 1][tv]), acc);
+      dV[tv] = acc;
+    }
+    __syncthreads();  // T^T and Aqk^T ready
+
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tv = 0; tv < C::NTV; ++tv) {
+      const int col = (w * C::NTV + tv) * 16 + lr;
+      const auto dof = load_frag(&sm.dOT[col][4 * lg]);
+      dV[tv] = M::k16(load_frag(&sm.AqkT[lr][4 * lg]), dof, dV[tv]);
+      const f32x4 dY = M::k16(load_frag(&sm.TT[lr][4 * lg]), M::make(dV[tv]), z);
+      f32x4 bdy;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * lg + e;
+        bdy[e] = sm.tf.beta[r] * dY[e];
+        if (r < L) st<T>(a.dY, ((t0 + r) * H + h) * (long)DV + col, dY[e]);
+      }
+      const auto nbdy = M::make_neg(bdy);
+#pragma unroll
+      for (int tr = 0; tr < DK / 16; ++tr) {
+        f32x4 s = dS[tr][tv];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[e] *= sm.gl[16 * tr + 4 * lg + e];
+        dS[tr][tv] = M::k32(load_frag(&sm.QgT[16 * tr + lr][4 * lg]),
+                            load_frag(&sm.KgT[16 * tr + lr][4 * lg]), dof, nbdy, s);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (a.dh0) {
+#pragma unroll
+    for (int tr = 0; tr < DK / 16; ++tr)
+#pragma unroll
+      for (int tv = 0; tv < C::NTV; ++tv) {
+        const int col = (w * C::NTV + tv) * 16 + lr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * tr + 4 * lg + e;
+          a.dh0[(((long)n * H + h) * DK + row) * DV + col] = dS[tr][tv][e];
+        }
+      }
+  }
+}
+
+// =============================================================== tile_grad ==
+template <typename T, int DK, int DV>
+struct GradSmem {
+  using C = BCfg<T, DK, DV>;
+  TileF32<DK> tf;
+  float dbA[BT];
+  float dbU[BT];
+  T Kl[BT][C::DKP];
+  T Kd[BT][C::DKP];
+  T dAqk[BT][C::TSP];          // dAqk, row-major
+  T dAqkT[BT][C::TSP];         // its transpose
+  T dAt[BT][C::TSP];           // beta_r dAkk[r, i] (gradient of A~ = Akk / beta)
+  T dAtT[BT][C::TSP];
+};
+
+template <typename T, int DK, int DV>
+__global__ void __launch_bounds__(NTH) bwd_tile_grad(BwdArgs a) {
+  using C = BCfg<T, DK, DV>;
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  __shared__ GradSmem<T, DK, DV> sm;
+  const int h = blockIdx.y;
+  const long slot = blockIdx.x;
+  const int H = a.H;
+  int n;
+  if (a.cu) {  // last sequence whose first slot is <= slot
+    int lo = 0, hi = a.N - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if ((long)(a.cu[mid] / BT) + mid <= slot) lo = mid; else hi = mid - 1;
+    }
+    n = lo;
+  } else {
+    n = (int)(slot / ((a.T + BT - 1) / BT));
+  }
+  const Unit un = unit_of(a, n);
+  const long j = slot - un.base;
+  if (j * BT >= un.len) return;  // slot past the sequence's last tile (uniform)
+  const long t0 = un.t0 + j * BT;
+  const int L = min((long)BT, un.len - j * BT);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const float sc = a.scale;
+
+  // Row fragments of dO, dY, V~ (row lr, value positions of the 32-blocks)
+  // and of both checkpoints (row = channel of this wavefront's tiles).
+  const frag fz = M::make(f32x4{0.f, 0.f, 0.f, 0.f});
+  frag aO[C::NVB][2], aY[C::NVB][2], aV[C::NVB][2];
+  {
+    const bool ok = lr < L;
+    const long row = ((t0 + lr) * H + h) * (long)DV;
+#pragma unroll
+    for (int kb = 0; kb < C::NVB; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const long off = row + 32 * kb + 16 * hf + 4 * lg;
+        aO[kb][hf] = ok ? load_frag(static_cast<const T*>(a.dO) + off) : fz;
+        aY[kb][hf] = ok ? load_frag(static_cast<const T*>(a.dY) + off) : fz;
+        aV[kb][hf] = ok ? load_frag(static_cast<const T*>(a.Vt) + off) : fz;
+      }
+  }
+  const long ck = ((un.base + j) * H + h) * (long)DK * DV;
+  frag bS[C::NCT][C::NVB][2], bD[C::NCT][C::NVB][2];
+#pragma unroll
+  for (int i = 0; i < C::NCT; ++i) {
+    const int c = 16 * (w + NWB * i) + lr;
+#pragma unroll
+    for (int kb = 0; kb < C::NVB; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const long off = ck + (long)c * DV + 32 * kb + 16 * hf + 4 * lg;
+        bS[i][kb][hf] = load_frag(static_cast<const T*>(a.ckS) + off);
+        bD[i][kb][hf] = load_frag(static_cast<const T*>(a.ckdS) + off);
+      }
+  }
+
+  load_tile<T, DK>(sm.tf, a, t0, L, h, true);
+  for (int idx = threadIdx.x; idx < BT * DK; idx += NTH) {
+    const int r = idx / DK, c = idx % DK;
+    const float G = sm.tf.G[r][c], kk = sm.tf.k[r][c], rho = sm.tf.G[7][c];
+    sm.Kl[r][c] = (T)(kk * fast_exp2(G - rho));
+    sm.Kd[r][c] = (T)(kk * fast_exp2(rho - G));
+  }
+  __syncthreads();
+
+  // dQg = dO S^T, dKg = -(beta dY) S^T, dKt = V~ dS'^T on this wavefront's
+  // channel tiles; dGamma_L = rowsum(dS' * S).
+  f32x4 dQg[C::NCT], dKg[C::NCT], dKt[C::NCT];
+  float dGL[C::NCT];
+#pragma unroll
+  for (int i = 0; i < C::NCT; ++i) {
+    f32x4 p = {0.f, 0.f, 0.f, 0.f}, y = p, t = p;
+    float gsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < C::NVB; ++kb) {
+      p = M::k32(aO[kb][0], aO[kb][1], bS[i][kb][0], bS[i][kb][1], p);
+      y = M::k32(aY[kb][0], aY[kb][1], bS[i][kb][0], bS[i][kb][1], y);
+      t = M::k32(aV[kb][0], aV[kb][1], bD[i][kb][0], bD[i][kb][1], t);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4 s4 = M::to_f32(bS[i][kb][hf]), d4 = M::to_f32(bD[i][kb][hf]);
+        gsum += s4[0] * d4[0] + s4[1] * d4[1] + s4[2] * d4[2] + s4[3] * d4[3];
+      }
+    }
+    gsum += __shfl_xor(gsum, 16, 64);
+    gsum += __shfl_xor(gsum, 32, 64);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] *= -sm.tf.beta[4 * lg + e];
+    dQg[i] = p;
+    dKg[i] = y;
+    dKt[i] = t;
+    dGL[i] = gsum;
+  }
+
+  if (w == 0) {
+    // dAqk = Tril(dO V~^T)
+    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < C::NVB; ++kb) p = M::k32(aO[kb][0], aO[kb][1], aV[kb][0], aV[kb][1], p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * lg + e;
+      const T x = (T)(lr <= r ? p[e] : 0.f);
+      sm.dAqk[r][lr] = x;
+      sm.dAqkT[lr][r] = x;
+    }
+  } else if (w == 1) {
+    // dAkk = -StrictTril(dY V~^T); A~ = Kl Kd^T; dbeta from both and from U
+    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < C::NVB; ++kb) p = M::k32(aY[kb][0], aY[kb][1], aV[kb][0], aV[kb][1], p);
+    const f32x4 At = tri_product<T, DK, C::DKP>(sm.Kl, sm.Kd, lr, lg);
+    f32x4 part;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * lg + e;
+      const float dA = lr < r ? -p[e] : 0.f;
+      part[e] = lr < r ? dA * At[e] : 0.f;
+      const T x = (T)(sm.tf.beta[r] * dA);
+      sm.dAt[r][lr] = x;
+      sm.dAtT[lr][r] = x;
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part[e] += __shfl_xor(part[e], m, 64);
+    if (lr == 0)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.dbA[4 * lg + e] = part[e];
+    // rowsum(dY * U), row lr
+    float u = 0.f;
+    const bool ok = lr < L;
+    const long row = ((t0 + lr) * H + h) * (long)DV;
+#pragma unroll
+    for (int kb = 0; kb < C::NVB; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const frag uf = ok ? load_frag(static_cast<const T*>(a.U) + row + 32 * kb + 16 * hf + 4 * lg)
+                           : fz;
+        const f32x4 u4 = M::to_f32(uf), y4 = M::to_f32(aY[kb][hf]);
+        u += u4[0] * y4[0] + u4[1] * y4[1] + u4[2] * y4[2] + u4[3] * y4[3];
+      }
+    u += __shfl_xor(u, 16, 64);
+    u += __shfl_xor(u, 32, 64);
+    if (lg == 0) sm.dbU[lr] = u;
+  }
+  __syncthreads();
+
+  if ((int)threadIdx.x < L) a.dbeta[(t0 + threadIdx.x) * H + h] = sm.dbA[threadIdx.x] + sm.dbU[threadIdx.x];
+  // dV = beta dY, one 32-block of value positions per wavefront
+  for (int kb = w; kb < C::NVB; kb += NWB) {
+    if (lr < L) {
+      const float b = sm.tf.beta[lr];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4 y4 = M::to_f32(aY[kb][hf]);
+        store4(static_cast<T*>(a.dv) + ((t0 + lr) * H + h) * (long)DV + 32 * kb + 16 * hf + 4 * lg,
+               f32x4{b * y4[0], b * y4[1], b * y4[2], b * y4[3]});
+      }
+    }
+  }
+
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < C::NCT; ++i) {
+    const int c = 16 * (w + NWB * i) + lr;
+    const float rho = sm.tf.G[7][c], GL = sm.tf.G[BT - 1][c];
+    f32x4 Gv, gam, el, ed, et, qq, kk;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * lg + e;
+      Gv[e] = sm.tf.G[t][c];
+      gam[e] = fast_exp2(Gv[e]);
+      el[e] = fast_exp2(Gv[e] - rho);
+      ed[e] = fast_exp2(rho - Gv[e]);
+      et[e] = fast_exp2(GL - Gv[e]);
+      qq[e] = sc * sm.tf.q[t][c];
+      kk[e] = sm.tf.k[t][c];
+    }
+    const f32x4 Kd = kk * ed, Kl = kk * el, Ql = qq * el;
+    const f32x4 dQl = M::k16(load_frag(&sm.dAqk[lr][4 * lg]), M::make(Kd), z);
+    const f32x4 dKl = M::k16(load_frag(&sm.dAt[lr][4 * lg]), M::make(Kd), z);
+    const f32x4 dKd = M::k32(load_frag(&sm.dAqkT[lr][4 * lg]), load_frag(&sm.dAtT[lr][4 * lg]),
+                             M::make(Ql), M::make(Kl), z);
+    f32x4 dq, dk, dG;
+    float tsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float Kt = kk[e] * et[e];
+      dq[e] = sc * (dQg[i][e] * gam[e] + dQl[e] * el[e]);
+      dk[e] = dKg[i][e] * gam[e] + dKt[i][e] * et[e] + dKl[e] * el[e] + dKd[e] * ed[e];
+      dG[e] = dQg[i][e] * qq[e] * gam[e] + dKg[i][e] * kk[e] * gam[e] - dKt[i][e] * Kt +
+              dQl[e] * Ql[e] + dKl[e] * Kl[e] - dKd[e] * Kd[e];
+      tsum += dKt[i][e] * Kt;
+    }
+    tsum += __shfl_xor(tsum, 16, 64);
+    tsum += __shfl_xor(tsum, 32, 64);
+    // G_L is the last row's G (rows past the end repeat it), so its
+    // gradient joins row 15 and reaches every valid row through the
+    // reverse cumulative sum.
+    if (lg == 3) dG[3] += tsum + dGL[i] * fast_exp2(GL);
+    // reverse cumulative sum over the 16 tokens (4 per lane, 4 lane groups)
+    f32x4 suf;
+    suf[3] = dG[3];
+    suf[2] = dG[2] + suf[3];
+    suf[1] = dG[1] + suf[2];
+    suf[0] = dG[0] + suf[1];
+    const float tot = suf[0];
+    const float t1 = __shfl(tot, (lane + 16) & 63, 64);
+    const float t2 = __shfl(tot, (lane + 32) & 63, 64);
+    const float t3 = __shfl(tot, (lane + 48) & 63, 64);
+    const float after = (lg < 3 ? t1 : 0.f) + (lg < 2 ? t2 : 0.f) + (lg < 1 ? t3 : 0.f);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * lg + e;
+      if (t < L) {
+        const long idx = ((t0 + t) * H + h) * (long)DK + c;
+        st<T>(a.dq, idx, dq[e]);
+        st<T>(a.dk, idx, dk[e]);
+        a.dg[idx] = suf[e] + after;
+      }
+    }
+  }
+}
+
+template <typename T, int DK, int DV>
+hipError_t launch_bwd_t(const BwdArgs& a, long slots, hipStream_t stream) {
+  const unsigned units = (unsigned)(a.N * a.H);
+  hipLaunchKernelGGL((bwd_fwd_scan<T, DK, DV>), dim3(units), dim3(NTH), 0, stream, a);
+  hipLaunchKernelGGL((bwd_rev_scan<T, DK, DV>), dim3(units), dim3(NTH), 0, stream, a);
+  if (slots > 0)
+    hipLaunchKernelGGL((bwd_tile_grad<T, DK, DV>), dim3((unsigned)slots, (unsigned)a.H), dim3(NTH),
+                       0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_bwd_d(const BwdArgs& a, int Dk, int Dv, long slots, hipStream_t stream) {
+  if (Dk == 128 && Dv == 128) return launch_bwd_t<T, 128, 128>(a, slots, stream);
+  if (Dk == 128 && Dv == 64) return launch_bwd_t<T, 128, 64>(a, slots, stream);
+  if (Dk == 64 && Dv == 128) return launch_bwd_t<T, 64, 128>(a, slots, stream);
+  if (Dk == 64 && Dv == 64) return launch_bwd_t<T, 64, 64>(a, slots, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool chunk_bwd_supported(int Dk, int Dv) {
+  return (Dk == 64 || Dk == 128) && (Dv == 64 || Dv == 128);
+}
+
+long chunk_bwd_slots(const Seqs& s) {
+  if (s.cu) return s.Ttot / BT + s.N;
+  return (long)s.N * ((s.T + BT - 1) / BT);
+}
+
+hipError_t launch_chunk_bwd(const BwdArgs& a, bool bf16, int Dk, int Dv, long slots,
+                            hipStream_t stream) {
+  if (a.N == 0) return hipSuccess;
+  if (bf16) return launch_bwd_d<__bf16>(a, Dk, Dv, slots, stream);
+  return launch_bwd_d<float>(a, Dk, Dv, slots, stream);
+}
+
+}  // namespace kda

@@ -122,4 +122,68 @@ hipError_t launch_gate(const float* z, const float* A_log, float g_min, Seqs s, 
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------- backward --
+// g = g_min * p, p = sigmoid(x), x = e^{A_h} z, p' = p (1 - p):
+//   dz = dg * g_min * p' * e^{A_h},  dA_h = sum over rows, channels of dg * g_min * p' * x.
+// Block (row block, head): threads own 4 channels and a row stride; the
+// block's dA_h partial is reduced in LDS and added with one atomic.
+constexpr int kGateBwdRows = 256;
+
+__global__ void __launch_bounds__(256) fill_zero_kernel(float* x, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) x[i] = 0.f;
+}
+
+__global__ void __launch_bounds__(256) gate_bwd_kernel(const float* z, const float* __restrict__ A_log,
+                                                       float g_min, const float* dg, long rows,
+                                                       int H, int Dk4, float* dz, float* dA) {
+  __shared__ float part[256];
+  const int h = blockIdx.y;
+  const int c4 = threadIdx.x % Dk4, r0 = threadIdx.x / Dk4, rstep = 256 / Dk4;
+  const float es = A_log ? __expf(A_log[h]) : 1.0f;
+  const long rb = (long)blockIdx.x * kGateBwdRows;
+  const long re = rb + kGateBwdRows < rows ? rb + kGateBwdRows : rows;
+  float acc = 0.f;
+  if (r0 < rstep) {
+    for (long r = rb + r0; r < re; r += rstep) {
+      const long i = (r * H + h) * Dk4 + c4;
+      const f32x4 x = reinterpret_cast<const f32x4*>(z)[i];
+      const f32x4 d = reinterpret_cast<const f32x4*>(dg)[i];
+      f32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float xs = es * x[e];
+        const float p = 1.0f / (1.0f + __expf(-xs));
+        const float dx = d[e] * g_min * p * (1.0f - p);
+        o[e] = dx * es;
+        acc += dx * xs;
+      }
+      reinterpret_cast<f32x4*>(dz)[i] = o;
+    }
+  }
+  if (!dA) return;
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) part[threadIdx.x] += part[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) atomicAdd(dA + h, part[0]);
+}
+
+hipError_t launch_gate_bwd(const float* z, const float* A_log, float g_min, const float* dg,
+                           long rows, int H, int Dk, float* dz, float* dA, hipStream_t stream) {
+  if (dA) {
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((H + 255) / 256)), dim3(256), 0, stream, dA,
+                       H);
+  }
+  if (rows > 0) {
+    const long blocks = (rows + kGateBwdRows - 1) / kGateBwdRows;
+    if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(gate_bwd_kernel, dim3((unsigned)blocks, (unsigned)H), dim3(256), 0, stream,
+                       z, A_log, g_min, dg, rows, H, Dk / 4, dz, dA);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace kda

@@ -86,6 +86,48 @@ hipError_t launch_compose(const float* M, const float* b, const float* S0, int n
 constexpr float kMinFusedGmin = -5.5f;
 hipError_t launch_chunk_fused(const ChunkArgs& a, hipStream_t stream);
 
+// Backward of the chunk forward (three kernels: forward scan writing the
+// per-tile state checkpoints, U and V~; reverse scan writing the per-tile
+// state-gradient checkpoints and dY; per-tile gradients). Tiles are 16 tokens
+// of one sequence; checkpoint slot of tile j of sequence n is
+// tile_base(n) + j, tile_base(n) = floor(cu[n] / 16) + n (packed) or
+// n * ceil(T / 16) (dense).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  int gate;  // kGateLogDecay or kGateLogits
+  const float* A_log;
+  float g_min;
+  const float* beta;
+  const float* h0;     // [N, H, Dk, Dv] or nullptr
+  const int32_t* cu;   // packed sequences or nullptr (dense)
+  int N, T, H;         // T: dense sequence length
+  float scale;
+  const void* dO;      // [Ttot, H, Dv]
+  const float* dhT;    // [N, H, Dk, Dv] or nullptr
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;
+  float* dbeta;
+  float* dh0;          // or nullptr
+  void* ckS;           // [slots, H, Dk, Dv] states entering each tile
+  void* ckdS;          // [slots, H, Dk, Dv] state gradients leaving each tile
+  void* U;             // [Ttot, H, Dv] V - Kg S
+  void* Vt;            // [Ttot, H, Dv] pseudo-values
+  void* dY;            // [Ttot, H, Dv] T^T dV~
+};
+bool chunk_bwd_supported(int Dk, int Dv);
+long chunk_bwd_slots(const Seqs& s);
+hipError_t launch_chunk_bwd(const BwdArgs& a, bool bf16, int Dk, int Dv, long slots,
+                            hipStream_t stream);
+// Gradient of the gate w.r.t. z (dz, may alias dg) and, if dA != nullptr,
+// w.r.t. A_log (summed over rows and channels; dA is overwritten).
+hipError_t launch_gate_bwd(const float* z, const float* A_log, float g_min, const float* dg,
+                           long rows, int H, int Dk, float* dz, float* dA, hipStream_t stream);
+
 // Longest-first ordering of packed sequences (N <= kMaxOrderN), into order[N].
 constexpr int kMaxOrderN = 8192;
 hipError_t launch_order(const int32_t* cu, int N, int32_t* order, hipStream_t stream);

@@ -365,3 +365,95 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
                                     _stream(dev))
     _lib.check(rc, "kda_recurrent_step")
     return o
+
+
+def bwd_workspace_size(B: int, T: int, H: int, Dk: int, Dv: int, N: int, chunk: int = 64,
+                       dtype=torch.bfloat16) -> int:
+    lib = _lib.load()
+    import ctypes
+    out = ctypes.c_size_t(0)
+    code = _lib.KDA_BFLOAT16 if dtype == torch.bfloat16 else _lib.KDA_FLOAT32
+    _lib.check(lib.kda_chunk_bwd_workspace_size(B, T, H, Dk, Dv, N, chunk, code,
+                                                ctypes.byref(out)),
+               "kda_chunk_bwd_workspace_size")
+    return int(out.value)
+
+
+def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+              beta: torch.Tensor, do: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+              d_final_state: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, gate: str = "logdecay",
+              A_log: Optional[torch.Tensor] = None, g_min: float = -5.0, chunk: int = 64,
+              scale: float = 1.0, want_dh0: bool = True,
+              workspace: Optional[torch.Tensor] = None) -> dict:
+    """Gradients of chunk_fwd: given do [B, T, H, Dv] and d_final_state
+    [N, H, Dk, Dv] (None = zero), returns a dict with dq, dk, dv (input
+    dtype), dg (fp32, w.r.t. the per-token log-decay), dbeta (fp32) and dh0
+    (fp32 [N, H, Dk, Dv], or None when want_dh0 is False). gate is
+    "logdecay" (g = log-decay) or "logits" (g = z)."""
+    lib = _lib.load()
+    dev = q.device
+    dt = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v), ("do", do)):
+        _need(t, name, dt, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or g.shape != q.shape or \
+            beta.shape != q.shape[:3] or do.shape != v.shape:
+        raise ValueError("shape mismatch among q, k, v, g, beta, do")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if t is not None:
+            _need(t, name, torch.float32, dev)
+            if tuple(t.shape) != (N, H, Dk, Dv):
+                raise ValueError(f"{name} must be [N, H, Dk, Dv]")
+    if A_log is not None:
+        _need(A_log, "A_log", torch.float32, dev)
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+           "dg": torch.empty_like(g), "dbeta": torch.empty_like(beta),
+           "dh0": torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev) if want_dh0
+           else None}
+    ws_bytes = bwd_workspace_size(B, T, H, Dk, Dv, N, chunk, dt)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws_len = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        rc = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _GATES[gate],
+                               _ptr(A_log), float(g_min), _ptr(beta), _ptr(initial_state),
+                               _ptr(cu_seqlens), N, B, T, H, Dk, Dv, int(chunk), float(scale),
+                               _ptr(do), _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]),
+                               _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
+                               _ptr(out["dh0"]), _ptr(workspace), ws_len, _stream(dev))
+    _lib.check(rc, "kda_chunk_bwd")
+    return out
+
+
+def gate_bwd(z: torch.Tensor, dg: torch.Tensor, A_log: Optional[torch.Tensor] = None,
+             g_min: float = -5.0, want_dA: bool = True,
+             dz: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Gradient of g = g_min * sigmoid(exp(A_log[h]) z) w.r.t. z and A_log.
+    z, dg: fp32 [..., H, Dk]. Returns (dz, dA_log [H] or None)."""
+    lib = _lib.load()
+    _need(z, "z", torch.float32)
+    _need(dg, "dg", torch.float32, z.device)
+    if dg.shape != z.shape:
+        raise ValueError("dg must have z's shape")
+    H, Dk = z.shape[-2], z.shape[-1]
+    rows = z.numel() // (H * Dk)
+    if A_log is not None:
+        _need(A_log, "A_log", torch.float32, z.device)
+    if dz is None:
+        dz = torch.empty_like(z)
+    _need(dz, "dz", torch.float32, z.device)
+    dA = torch.empty(H, dtype=torch.float32, device=z.device) if want_dA else None
+    with torch.cuda.device(z.device):
+        rc = lib.kda_gate_bwd(_ptr(z), _ptr(A_log), float(g_min), _ptr(dg), rows, H, Dk, _ptr(dz),
+                              _ptr(dA), _stream(z.device))
+    _lib.check(rc, "kda_gate_bwd")
+    return dz, dA

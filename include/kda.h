@@ -255,6 +255,70 @@ kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v, kda
                                 float* state, int N, int H, int Dk, int Dv, float scale,
                                 void* o, kda_stream_t stream);
 
+/*
+ * kda_chunk_bwd_workspace_size — bytes of device workspace kda_chunk_bwd
+ * needs (256-byte aligned): two per-tile state checkpoints
+ * [slots, H, Dk, Dv] and three per-token [B*T, H, Dv] arrays in the input
+ * dtype, slots = max(B * ceil(T/16), B*T/16 + N).
+ */
+kda_status_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv, int N,
+                                          int chunk, kda_dtype_t dtype, size_t* bytes);
+
+/*
+ * kda_chunk_bwd — gradients of kda_chunk_fwd. Given d_o (the gradient of a
+ * loss w.r.t. o) and d_final_state (w.r.t. the final state), computes the
+ * gradients w.r.t. q, k, v, the per-token log-decay g, beta and the initial
+ * state. The pages state the forward only [KDA-blog §Kimi Delta Attention,
+ * KDA equation; §Chunkwise parallel form]; this is the exact derivative of
+ * that recurrence, evaluated on 16-token tiles: a forward scan stores the
+ * state entering every tile, a reverse scan stores the state gradient
+ * leaving every tile, and every tile then forms its gradients on its own.
+ *
+ * Inputs as for kda_chunk_fwd (same layouts, dtype, gate, scale, sequences);
+ * gate_input is KDA_GATE_LOGDECAY (g = log-decay) or KDA_GATE_LOGITS (g = z,
+ * the library applies the gate); chunk must be 64.
+ * d_o            device dtype [B, T, H, Dv]
+ * d_final_state  device fp32 [N, H, Dk, Dv] or NULL (zero)
+ * dq, dk         device dtype [B, T, H, Dk] (written)
+ * dv             device dtype [B, T, H, Dv] (written)
+ * dg             device fp32 [B, T, H, Dk] (written): gradient w.r.t. the
+ *                per-token log-decay g, also when gate_input is LOGITS
+ *                (kda_gate_bwd then maps it to the logits and A_log)
+ * dbeta          device fp32 [B, T, H] (written)
+ * d_initial_state device fp32 [N, H, Dk, Dv] or NULL (not wanted)
+ * workspace      device, >= kda_chunk_bwd_workspace_size(...) bytes (required)
+ * Supported: Dk, Dv in {64, 128}, fp32 or bf16; per-token log-decay
+ * >= -5.5 (KDA_GATE_LOGITS with g_min < -5.5 and KDA_GATE_SOFTPLUS return
+ * KDA_ERROR_NOT_SUPPORTED, as does KDA_GATE_CUMSUM). Outputs must not alias
+ * inputs. Gradients of bf16 tensors are rounded to bf16; states,
+ * checkpoints of fp32 inputs and all accumulation are fp32; bf16 inputs keep
+ * their checkpoints in bf16.
+ */
+kda_status_t kda_chunk_bwd(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                           const float* g, kda_gate_input_t gate_input, const float* A_log,
+                           float g_min, const float* beta, const float* initial_state,
+                           const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk, int Dv,
+                           int chunk, float scale, const void* d_o, const float* d_final_state,
+                           void* dq, void* dk, void* dv, float* dg, float* dbeta,
+                           float* d_initial_state, void* workspace, size_t workspace_bytes,
+                           kda_stream_t stream);
+
+/*
+ * kda_gate_bwd — gradient of the gate g = g_min * sigmoid(exp(A_h) z)
+ * [KDA-blog §Chunkwise parallel form, new-gate equation], elementwise over
+ * rows x H x Dk (layout [rows, H, Dk]):
+ *   dz = dg * g_min * p (1 - p) * exp(A_h),   p = sigmoid(exp(A_h) z)
+ *   dA_log[h] = sum over rows and channels of dg * g_min * p (1 - p) * exp(A_h) z
+ * z, dg, dz  device fp32; dz may alias dg
+ * A_log      device fp32 [H] or NULL (A_h = 0)
+ * dA_log     device fp32 [H] (overwritten) or NULL (not wanted); summed
+ *            with floating-point atomics, so its last bits depend on order
+ * Supported: Dk % 4 == 0, Dk <= 1024.
+ */
+kda_status_t kda_gate_bwd(const float* z, const float* A_log, float g_min, const float* dg,
+                          long rows, int H, int Dk, float* dz, float* dA_log,
+                          kda_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -138,3 +138,98 @@ def chunk_form_tiled(q, k, v, g, beta, S0, C=64, tile=16, round_bf16=False):
         o[s:e] = O[:L]
         S = np.exp(GC)[:, None] * S + Kt.T @ X
     return o, S
+
+
+def tile_backward(q, k, v, g, beta, S0, do, dST, tile=16, scale=1.0):
+    """Backward of one unit in the 16-token tile arrangement of the GPU
+    backward (three passes), fp64.
+
+    q, k, g: [T, Dk]; v, do: [T, Dv]; beta: [T]; S0, dST: [Dk, Dv].
+    Inside a tile with inclusive cumulative log-decay G (natural log),
+    Gamma = e^G, Kg = K*Gamma, Qg = scale*Q*Gamma, Kt = K*e^{G_L-G},
+    Akk = beta_r sum_c k_r k_i e^{G_r-G_i} (i < r), Aqk = scale sum_c q_r k_i
+    e^{G_r-G_i} (i <= r), T = (I + Akk)^{-1}:
+      forward   U = V - Kg S,  V~ = T (beta U),  S' = Diag(Gamma_L) S + Kt^T V~
+      reverse   dV~ = Kt dS' + Aqk^T dO,  dY = T^T dV~,
+                dS = Diag(Gamma_L) dS' + Qg^T dO - Kg^T (beta dY)
+      per tile  the products' derivatives, chained into q, k, G, then
+                dg = reverse cumulative sum of dG inside the tile.
+    The decay factors of the tile products are split at a reference point
+    rho (G of the tile's eighth token); the products do not depend on rho,
+    so its own derivative is zero.
+    Returns dq, dk, dv, dg, dbeta, dS0.
+    """
+    T, Dk = k.shape
+    Dv = v.shape[1]
+    nt = (T + tile - 1) // tile
+    tiles = [(j * tile, min(T, (j + 1) * tile)) for j in range(nt)]
+
+    def prep(a, b):
+        G = np.cumsum(g[a:b], axis=0)
+        L = b - a
+        Gam = np.exp(G)
+        Kg = k[a:b] * Gam
+        Qg = scale * q[a:b] * Gam
+        Kt = k[a:b] * np.exp(G[L - 1] - G)
+        rho = G[min(7, L - 1)]
+        Kl, Ql, Kd = k[a:b] * np.exp(G - rho), scale * q[a:b] * np.exp(G - rho), k[a:b] * np.exp(rho - G)
+        At = np.tril(Kl @ Kd.T, -1)
+        Akk = beta[a:b, None] * At
+        Aqk = np.tril(Ql @ Kd.T)
+        Tm = np.linalg.inv(np.eye(L) + Akk)
+        return dict(G=G, Gam=Gam, Kg=Kg, Qg=Qg, Kt=Kt, Kl=Kl, Ql=Ql, Kd=Kd, At=At, Aqk=Aqk,
+                    T=Tm, GL=Gam[L - 1], rho=rho)
+
+    # pass 1: states entering each tile, U and V~
+    S = S0.copy()
+    Ss, Us, Vts = [], [], []
+    for (a, b) in tiles:
+        p = prep(a, b)
+        Ss.append(S.copy())
+        U = v[a:b] - p["Kg"] @ S
+        Vt = p["T"] @ (beta[a:b, None] * U)
+        Us.append(U)
+        Vts.append(Vt)
+        S = p["GL"][:, None] * S + p["Kt"].T @ Vt
+    # pass 2: state gradients leaving each tile, dY
+    dS = dST.copy()
+    dSs, dYs = [None] * nt, [None] * nt
+    for j in reversed(range(nt)):
+        a, b = tiles[j]
+        p = prep(a, b)
+        dSs[j] = dS.copy()
+        dVt = p["Kt"] @ dS + p["Aqk"].T @ do[a:b]
+        dY = p["T"].T @ dVt
+        dYs[j] = dY
+        dS = p["GL"][:, None] * dS + p["Qg"].T @ do[a:b] - p["Kg"].T @ (beta[a:b, None] * dY)
+    dS0 = dS
+    # pass 3: per-tile gradients
+    dq, dk, dg = np.zeros_like(q), np.zeros_like(k), np.zeros_like(g)
+    dv, dbeta = np.zeros_like(v), np.zeros_like(beta)
+    for j, (a, b) in enumerate(tiles):
+        p = prep(a, b)
+        L = b - a
+        Sj, dSp, U, Vt, dY = Ss[j], dSs[j], Us[j], Vts[j], dYs[j]
+        bt = beta[a:b]
+        dO = do[a:b]
+        dQg = dO @ Sj.T
+        dKg = -(bt[:, None] * dY) @ Sj.T
+        dKt = Vt @ dSp.T
+        dGL = np.sum(dSp * Sj, axis=1)
+        dAqk = np.tril(dO @ Vt.T)
+        dA = -np.tril(dY @ Vt.T, -1)
+        dbeta[a:b] = np.sum(dY * U, axis=1) + np.sum(dA * p["At"], axis=1)
+        dv[a:b] = bt[:, None] * dY
+        dAt = bt[:, None] * dA
+        dQl = dAqk @ p["Kd"]
+        dKl = dAt @ p["Kd"]
+        dKd = dAqk.T @ p["Ql"] + dAt.T @ p["Kl"]
+        G, rho = p["G"], p["rho"]
+        dq[a:b] = scale * (dQg * p["Gam"] + dQl * np.exp(G - rho))
+        dk[a:b] = (dKg * p["Gam"] + dKt * np.exp(G[L - 1] - G) + dKl * np.exp(G - rho)
+                   + dKd * np.exp(rho - G))
+        dG = (dQg * p["Qg"] + dKg * p["Kg"] - dKt * p["Kt"] + dQl * p["Ql"] + dKl * p["Kl"]
+              - dKd * p["Kd"])
+        dG[L - 1] += np.sum(dKt * p["Kt"], axis=0) + dGL * p["GL"]
+        dg[a:b] = np.cumsum(dG[::-1], axis=0)[::-1]
+    return dq, dk, dv, dg, dbeta, dS0

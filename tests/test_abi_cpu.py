@@ -181,3 +181,62 @@ def test_python_binding_fails_loudly_without_gpu_tensors():
     x = torch.zeros(1, 64, 1, 64)
     with pytest.raises(ValueError):
         chunk_fwd(x, x, x, x, torch.zeros(1, 64, 1))
+
+
+def _bwd(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, g=FAKE, gate=0, A=None, g_min=-5.0, beta=FAKE,
+                h0=None, cu=None, N=1, B=1, T=64, H=2, Dk=128, Dv=128, chunk=64, scale=1.0,
+                do=FAKE, dhT=None, dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, dbeta=FAKE, dh0=None,
+                ws=FAKE, ws_bytes=1 << 40, stream=None)
+    args.update(kw)
+    return _lib.load().kda_chunk_bwd(*args.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(do=None), dict(dq=None), dict(dg=None), dict(dbeta=None),
+    dict(B=0), dict(H=0), dict(Dk=0), dict(chunk=0), dict(N=2), dict(cu=FAKE, B=2, N=2),
+    dict(dk=FAKE + 4), dict(dhT=FAKE + 8), dict(dtype=3), dict(gate=9),
+    dict(gate=2, g_min=1.0), dict(ws=FAKE + 64),
+])
+def test_chunk_bwd_rejects_invalid(kw):
+    assert _bwd(**kw) == _lib.KDA_ERROR_INVALID_VALUE
+
+
+def test_chunk_bwd_not_supported_and_workspace():
+    assert _bwd(Dk=96) == _lib.KDA_ERROR_NOT_SUPPORTED
+    assert _bwd(Dv=256) == _lib.KDA_ERROR_NOT_SUPPORTED
+    assert _bwd(chunk=32) == _lib.KDA_ERROR_NOT_SUPPORTED
+    assert _bwd(gate=1) == _lib.KDA_ERROR_NOT_SUPPORTED          # cumsum input
+    assert _bwd(gate=3) == _lib.KDA_ERROR_NOT_SUPPORTED          # unbounded gate
+    assert _bwd(gate=2, g_min=-6.0) == _lib.KDA_ERROR_NOT_SUPPORTED
+    assert _bwd(ws=None) == _lib.KDA_ERROR_INSUFFICIENT_WORKSPACE
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    assert lib.kda_chunk_bwd_workspace_size(8, 8192, 32, 128, 128, 8, 64, 1, ctypes.byref(n)) == 0
+    # two bf16 checkpoints per 16-token tile slot (slots = max(B ceil(T/16),
+    # B T / 16 + N) per head) and three bf16 per-token arrays
+    tiles, tokens = (8 * 8192 // 16 + 8) * 32, 8 * 8192 * 32
+    assert n.value == 2 * tiles * 128 * 128 * 2 + 3 * tokens * 128 * 2
+    assert _bwd(ws_bytes=n.value - 1, B=8, N=8, T=8192, H=32) == \
+        _lib.KDA_ERROR_INSUFFICIENT_WORKSPACE
+    # packed sequences: up to one ragged tile per sequence
+    assert lib.kda_chunk_bwd_workspace_size(1, 100, 1, 64, 64, 10, 64, 0, ctypes.byref(n)) == 0
+    assert n.value >= 2 * (100 // 16 + 10) * 64 * 64 * 4
+    assert _bwd(cu=FAKE, N=0, T=0) == _lib.KDA_SUCCESS
+
+
+def test_gate_bwd_validation():
+    lib = _lib.load()
+    ok = dict(z=FAKE, A=None, g_min=-5.0, dg=FAKE, rows=8, H=2, Dk=8, dz=FAKE, dA=None,
+              stream=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.kda_gate_bwd(*a.values())
+    assert call(z=None) == _lib.KDA_ERROR_INVALID_VALUE
+    assert call(dz=None) == _lib.KDA_ERROR_INVALID_VALUE
+    assert call(rows=-1) == _lib.KDA_ERROR_INVALID_VALUE
+    assert call(g_min=0.0) == _lib.KDA_ERROR_INVALID_VALUE
+    assert call(dg=FAKE + 4) == _lib.KDA_ERROR_INVALID_VALUE
+    assert call(Dk=6) == _lib.KDA_ERROR_NOT_SUPPORTED

@@ -1,0 +1,145 @@
+"""GPU parity of the backward pass (kda_chunk_bwd, kda_gate_bwd) against the
+fp64 oracle's derivative of the token recurrence.
+
+Bar: max|gpu - ref| / max|ref| per gradient (dq, dk, dv, dg, dbeta, dh0)
+<= 2e-2 for bf16 inputs and <= 1e-4 for fp32 inputs, the forward's bar; the
+backward's arithmetic is the same kind (bf16 operands, fp32 accumulation,
+fp32 states). Inputs: the seeded generators of the forward tests (unit-norm
+q, k; beta = sigmoid; gate logits z ~ N(0, 1)), plus seeded normal
+cotangents do and d_final_state. Where the kernel takes the log-decay g
+directly, g is the oracle's gate of z rounded to fp32, so both sides read
+the same g.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_92_amd import chunk_bwd, gate_bwd
+from gated_delta_rule_92_amd.inputs import make_inputs
+from oracle import oracle_backward, oracle_gate, oracle_gate_backward
+from tests.gpu_helpers import TOL_BF16, TOL_FP32, rel_err
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def _print_case(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+def _cotangents(d, N, seed):
+    gen = torch.Generator().manual_seed(seed)
+    B, T, H, _ = d["q"].shape
+    Dk, Dv = d["k"].shape[-1], d["v"].shape[-1]
+    do = torch.randn(B, T, H, Dv, generator=gen).to(d["q"].dtype)
+    dhT = torch.randn(N, H, Dk, Dv, generator=gen)
+    return do, dhT
+
+
+def _run(name, B, T, H, Dk, Dv, dtype, lengths=None, gate="logits", h0_std=0.02, dh=True,
+         scale=1.0, seed=41):
+    _print_case(name)
+    d = make_inputs(B, T, H, Dk, Dv, dtype, h0_std=h0_std, lengths=lengths, seed=seed)
+    N = B if d["cu_seqlens"] is None else d["cu_seqlens"].numel() - 1
+    do, dhT = _cotangents(d, N, seed + 1)
+    if not dh:
+        dhT = None
+    g64 = oracle_gate(d["z"], None, -5.0)
+    g32 = torch.from_numpy(g64).float()
+    g_in = d["z"] if gate == "logits" else g32
+    ref = oracle_backward(d["q"], d["k"], d["v"], g64 if gate == "logits" else g32, d["beta"], do,
+                          d["h0"], dhT, d["cu_seqlens"], scale)
+    dev = lambda x: None if x is None else x.cuda()  # noqa: E731
+    got = chunk_bwd(dev(d["q"]), dev(d["k"]), dev(d["v"]), dev(g_in), dev(d["beta"]), dev(do),
+                    dev(d["h0"]), dev(dhT), dev(d["cu_seqlens"]), gate=gate, scale=scale)
+    torch.cuda.synchronize()
+    tol = TOL_FP32 if dtype == torch.float32 else TOL_BF16
+    errs = {n: rel_err(got[n], ref[n]) for n in NAMES}
+    print("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()) + f" tol={tol:g}", flush=True)
+    for n in NAMES:
+        assert np.all(np.isfinite(got[n].double().cpu().numpy())), n
+        assert errs[n] <= tol, (n, errs[n])
+    return got, ref
+
+
+def test_bwd_bf16_dense_ragged_logits():
+    _run("bf16 d=128 dense B=2 T=100 logits", 2, 100, 2, 128, 128, torch.bfloat16)
+
+
+def test_bwd_bf16_varlen_logdecay():
+    _run("bf16 d=128 varlen logdecay", 1, 0, 2, 128, 128, torch.bfloat16,
+         lengths=[0, 1, 15, 16, 17, 33, 64, 130], gate="logdecay", h0_std=0.0, scale=0.75)
+
+
+def test_bwd_fp32_d64_tiny():
+    _run("fp32 d=64 dense B=1 T=256", 1, 256, 2, 64, 64, torch.float32, gate="logdecay")
+
+
+@pytest.mark.parametrize("Dk,Dv", [(64, 128), (128, 64), (64, 64)])
+def test_bwd_bf16_mixed_dims(Dk, Dv):
+    _run(f"bf16 Dk={Dk} Dv={Dv} dense B=1 T=77", 1, 77, 3, Dk, Dv, torch.bfloat16, dh=False)
+
+
+def test_bwd_fp32_d128_varlen():
+    _run("fp32 d=128 varlen", 1, 0, 2, 128, 128, torch.float32, lengths=[40, 0, 90],
+         gate="logits")
+
+
+def test_gate_bwd_matches_oracle():
+    _print_case("gate backward, fp32 [3, 70, 4, 128]")
+    gen = torch.Generator().manual_seed(43)
+    z = torch.randn(3, 70, 4, 128, generator=gen) * 2
+    A = torch.randn(4, generator=gen) * 0.5
+    dg = torch.randn(3, 70, 4, 128, generator=gen)
+    for Au in (A, None):
+        dz, dA = gate_bwd(z.cuda(), dg.cuda(), None if Au is None else Au.cuda(), -5.0)
+        torch.cuda.synchronize()
+        rz, rA = oracle_gate_backward(z, dg, Au, -5.0)
+        ez = rel_err(dz, rz)
+        eA = rel_err(dA, rA if rA is not None else oracle_gate_backward(z, dg, torch.zeros(4),
+                                                                        -5.0)[1])
+        print(f"  A={'yes' if Au is not None else 'none'} err_dz={ez:.2e} err_dA={eA:.2e}",
+              flush=True)
+        assert ez <= 1e-5 and eA <= 1e-5
+
+
+def test_bwd_logits_chain_through_gate():
+    """dz from kda_chunk_bwd (gate applied inside) followed by kda_gate_bwd
+    equals the oracle's dg mapped through the oracle gate's derivative."""
+    _print_case("bf16 d=128 logits + gate backward chain")
+    got, ref = _run("bf16 d=128 dense B=1 T=64 logits", 1, 64, 2, 128, 128, torch.bfloat16)
+    d = make_inputs(1, 64, 2, 128, 128, torch.bfloat16, h0_std=0.02, seed=41)
+    dz, _ = gate_bwd(d["z"].cuda(), got["dg"], None, -5.0)
+    torch.cuda.synchronize()
+    rz, _ = oracle_gate_backward(d["z"], ref["dg"], None, -5.0)
+    e = rel_err(dz, rz)
+    print(f"  err_dz={e:.2e} tol={TOL_BF16:g}", flush=True)
+    assert e <= TOL_BF16
+
+
+def test_bwd_train8k_full_size_sampled():
+    """B=8, T=8192, H=32, d=128 bf16 (the headline forward's shape): the
+    whole backward on the GPU, two (sequence, head) units checked against
+    the oracle (units are independent, so a unit's gradients are exact)."""
+    _print_case("bf16 train8k shape backward, sampled units")
+    d = make_inputs(8, 8192, 32, 128, 128, torch.bfloat16, h0_std=0.0, seed=0, device="cuda")
+    gen = torch.Generator("cuda").manual_seed(44)
+    do = torch.randn(8, 8192, 32, 128, generator=gen, device="cuda").to(torch.bfloat16)
+    dhT = torch.randn(8, 32, 128, 128, generator=gen, device="cuda")
+    got = chunk_bwd(d["q"], d["k"], d["v"], d["z"], d["beta"], do, None, dhT, None, gate="logits")
+    torch.cuda.synchronize()
+    d = {key: d[key] for key in ("q", "k", "v", "z", "beta")}
+    for (n, h) in [(0, 0), (5, 17)]:
+        sl = lambda x: x[n:n + 1, :, h:h + 1].cpu()  # noqa: E731
+        g64 = oracle_gate(sl(d["z"]), None, -5.0)
+        ref = oracle_backward(sl(d["q"]), sl(d["k"]), sl(d["v"]), g64, sl(d["beta"]), sl(do), None,
+                              dhT[n:n + 1, h:h + 1].cpu(), None, 1.0, nthreads=1)
+        errs = {}
+        for name in NAMES:
+            x = got[name][n:n + 1, h:h + 1] if name == "dh0" else got[name][n:n + 1, :, h:h + 1]
+            errs[name] = rel_err(x, ref[name])
+        print(f"  unit ({n},{h}) " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+        for name, e in errs.items():
+            assert e <= TOL_BF16, (name, e)

@@ -22,8 +22,6 @@ Pins:
   * planted mistakes in a copy of the oracle's C source each fail the
     finite-difference pin.
 """
-import os
-import re
 import subprocess
 
 import numpy as np
@@ -203,3 +201,29 @@ def test_planted_mistakes_fail_the_pin(tmp_path, old, new):
                           nthreads=1, lib_path=lib)
     fd = _fd_grads(x, do, dhT, CU, scale)   # from the unmodified forward
     assert _fd_mismatch(got, fd) > 1e-3
+
+
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 50])
+def test_tile_arrangement_matches_oracle(T):
+    """The 16-token tile arrangement the GPU backward uses (forward scan for
+    U and V~, reverse scan for dY and the state gradients, then per-tile
+    gradients through the decay factors), written in fp64 numpy, gives the
+    oracle's gradients to rounding."""
+    from tests.chunk_mirror import tile_backward
+    rng = np.random.default_rng(12 + T)
+    Dk, Dv = 8, 6
+    q = rng.standard_normal((T, Dk))
+    k = rng.standard_normal((T, Dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.standard_normal((T, Dv))
+    g = -5.0 * expit(rng.standard_normal((T, Dk)))
+    beta = expit(rng.standard_normal(T))
+    S0, dST = rng.standard_normal((Dk, Dv)), rng.standard_normal((Dk, Dv))
+    do = rng.standard_normal((T, Dv))
+    got = tile_backward(q, k, v, g, beta, S0, do, dST, scale=0.8)
+    e = lambda x: x[None, :, None]  # noqa: E731
+    ref = oracle_backward(e(q), e(k), e(v), e(g), e(beta), e(do), S0[None, None], dST[None, None],
+                          None, 0.8)
+    for name, x in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), got):
+        r = ref[name].reshape(x.shape)
+        assert np.max(np.abs(x - r)) <= 1e-12 * max(1.0, np.max(np.abs(r))), name
