@@ -135,10 +135,22 @@ __device__ void load_tile(TileF32<DK>& tf, const BwdArgs& a, long t0, int L, int
 }
 
 // ------------------------------------------------------------ tile inverse --
+// Orders one wavefront's LDS accesses across its lanes: waits for the
+// wavefront's outstanding LDS operations and keeps the compiler from moving
+// LDS accesses across this point. Needed where lanes read what other lanes
+// wrote (per thread, a read of [i][j] and a write of [j][i] never alias, so
+// the compiler may otherwise reorder them).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup", "local");
+}
+
 // 16 x 16 transpose of an accumulator-layout tile through LDS (one wavefront).
 __device__ __forceinline__ f32x4 transpose16(const f32x4& x, float (*xs)[17], int lr, int lg) {
+  wave_lds_sync();  // earlier reads of xs by every lane have returned
 #pragma unroll
   for (int e = 0; e < 4; ++e) xs[4 * lg + e][lr] = x[e];
+  wave_lds_sync();  // every lane's writes have landed
   f32x4 y;
 #pragma unroll
   for (int e = 0; e < 4; ++e) y[e] = xs[lr][4 * lg + e];
