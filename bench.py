@@ -14,6 +14,7 @@ on the stream the kernel runs on. `cpu_baseline` is the fp64 oracle timed on
 the host cores on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       python bench.py --pass backward      (kda_chunk_bwd on the same workload)
        python bench.py --copy-calibration   (plain copy kernel for counter scaling)
 """
 from __future__ import annotations
@@ -65,6 +66,61 @@ def algorithmic_flops(w, n_tokens: int) -> float:
     P, dk, dv = 16, w.Dk, w.Dv
     per_tile = 2 * (2 * P * P * dk) + 3 * (2 * P * dk * dv) + 2 * (2 * P * P * dv)
     return per_tile / P * n_tokens * w.H
+
+
+def backward_algorithmic_bytes(w, n_tokens: int, n_units: int) -> int:
+    """HBM bytes any backward must move at minimum for one call: read q, k, v,
+    do (input dtype), gate logits (fp32) and beta; write dq, dk, dv (input
+    dtype), dg (fp32) and dbeta; read the final-state gradient and write the
+    initial-state gradient (fp32) once per (sequence, head)."""
+    el = 2 if w.dtype_name == "bf16" else 4
+    per_tok_head = (2 * w.Dk + 2 * w.Dv) * el + w.Dk * 4 + 4 + (2 * w.Dk + w.Dv) * el + w.Dk * 4 + 4
+    return per_tok_head * n_tokens * w.H + 2 * w.Dk * w.Dv * 4 * n_units
+
+
+def backward_design_bytes(w, n_tokens: int, n_units: int) -> int:
+    """HBM bytes the three-kernel backward moves by design: the minimum above,
+    plus the per-16-token-tile state and state-gradient checkpoints (written
+    once, read once) and U, V~, dY (written once, read once), plus the second
+    reads of q, k, the gate and beta by the scans and of v, do by the scans."""
+    el = 2 if w.dtype_name == "bf16" else 4
+    tiles = n_tokens // 16 * w.H
+    ck = 2 * tiles * w.Dk * w.Dv * el * 2
+    tok = 3 * n_tokens * w.H * w.Dv * el * 2
+    rereads = n_tokens * w.H * (2 * (w.Dk * el + w.Dk * 4 + 4) + w.Dk * el + 2 * w.Dv * el)
+    return backward_algorithmic_bytes(w, n_tokens, n_units) + ck + tok + rereads
+
+
+def cpu_baseline_backward(d, do, dhT, w, budget_s: float = 15.0):
+    """The fp64 oracle's backward on a bounded sample of (sequence, head)
+    units (each keeps T+1 states of d_k*d_v doubles, so at most 8 threads)."""
+    from oracle import oracle_backward, oracle_gate
+    cores = min(os.cpu_count() or 1, 8)
+    B, T, H = d["q"].shape[0], d["q"].shape[1], d["q"].shape[2]
+
+    def run(units, threads):
+        import torch
+        sl = lambda x, n, h: x[n, :, h].cpu()  # noqa: E731
+        cat = lambda name: torch.cat([sl(d[name], n, h) for (n, h) in units], 0)[None, :, None]  # noqa: E731
+        q, k, v, z, b = (cat(n) for n in ("q", "k", "v", "z", "beta"))
+        o = torch.cat([sl(do, n, h) for (n, h) in units], 0)[None, :, None]
+        dst = torch.stack([dhT[n, h].cpu() for (n, h) in units], 0)[:, None]
+        cu = torch.arange(len(units) + 1, dtype=torch.int32) * T
+        g = oracle_gate(z, None, w.g_min)
+        t0 = time.perf_counter()
+        oracle_backward(q, k, v, g, b, o, None, dst, cu, 1.0, nthreads=threads)
+        return time.perf_counter() - t0
+
+    per_unit = run([(0, 0)], 1)
+    n_units = max(cores, int(budget_s / max(per_unit, 1e-3)) // cores * cores)
+    n_units = min(n_units, B * H)
+    units = [(i % B, (i // B) % H) for i in range(n_units)]
+    wall = run(units, cores)
+    return {"value": n_units * T / wall, "unit": "tokens·heads/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{n_units} (sequence, head) units x {T} tokens of the {w.name} workload, "
+                      f"fp64 token-by-token backward from stored states, {cores} threads, "
+                      f"{wall:.1f} s wall"}
 
 
 def cpu_baseline(d, w, budget_s: float = 25.0):
@@ -121,6 +177,85 @@ def copy_calibration(n_bytes: int = 1 << 30):
     log(f"copy calibration: {n_bytes} bytes read and {n_bytes} bytes written per copy")
 
 
+def _timed(step, steps, warmup, dev):
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+
+
+def bench_backward(args, d, w, dev):
+    """One step = one kda_chunk_bwd call over the whole batch (forward scan,
+    reverse scan, per-tile gradients), inputs and cotangents resident."""
+    import torch
+    from gated_delta_rule_92_amd import bwd_workspace_size, chunk_bwd
+    B, T = d["q"].shape[0], d["q"].shape[1]
+    N = d["N"]
+    gen = torch.Generator(device=dev).manual_seed(2)
+    do = torch.randn(d["v"].shape, generator=gen, device=dev).to(w.dtype)
+    dhT = torch.randn((N, w.H, w.Dk, w.Dv), generator=gen, device=dev)
+    ws = bwd_workspace_size(B, T, w.H, w.Dk, w.Dv, N, w.chunk, w.dtype)
+    workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        chunk_bwd(d["q"], d["k"], d["v"], d["z"], d["beta"], do, d["h0"], dhT, d["cu_seqlens"],
+                  gate="logits", g_min=w.g_min, chunk=w.chunk, workspace=workspace)
+
+    ms_per_step, launch_ms = _timed(step, args.steps, args.warmup, dev)
+    kernel_ms = sum(launch_ms) / args.steps
+    log(f"bench: backward {args.steps} steps, wall {ms_per_step:.3f} ms/step, "
+        f"event {kernel_ms:.3f} ms/call")
+    n_tokens = int(B * T)
+    bytes_alg = backward_algorithmic_bytes(w, n_tokens, N * w.H)
+    achieved = bytes_alg / (kernel_ms / 1e3) / 1e9
+    cpu = None
+    if not args.skip_cpu_baseline and d["cu_seqlens"] is None:
+        log("bench: timing the fp64 oracle backward on a bounded sample (cpu_baseline)")
+        cpu = cpu_baseline_backward(d, do, dhT, w)
+    line = {
+        "metric": "KDA chunk bwd tokens·heads/s (H=32,d=128,bf16,T=8K)",
+        "value": n_tokens * w.H / (ms_per_step / 1e3),
+        "unit": "tokens·heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype_name,
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "backward", "batch": int(B), "seq_len": w.T,
+                   "heads": w.H, "d_k": w.Dk, "d_v": w.Dv, "chunk": w.chunk, "gate": "logits",
+                   "g_min": w.g_min, "initial_state": d["h0"] is not None, "sequences": N},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "scope": "all three backward kernels of one call (HIP events around the "
+                              "call); bytes = the minimum any backward must move",
+                     "design_bytes": backward_design_bytes(w, n_tokens, N * w.H),
+                     "algorithmic_bytes": bytes_alg},
+        "kernel_ms": kernel_ms,
+        "kernel_ms_median": launch_ms[len(launch_ms) // 2],
+        "kernel_ms_min": launch_ms[0],
+        "kernel_ms_max": launch_ms[-1],
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +273,9 @@ def main(argv=None):
     ap.add_argument("--split", type=int, default=1,
                     help="cut every sequence into this many segments that run in parallel "
                          "(state maps + composition + re-run); 1 = the plain forward")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward",
+                    help="forward: kda_chunk_fwd (the default line); backward: kda_chunk_bwd with "
+                         "seeded normal output and final-state gradients")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -165,6 +303,9 @@ def main(argv=None):
     workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
     o = torch.empty(d["v"].shape, dtype=w.dtype, device=dev)
     hT = torch.empty((N, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+
+    if args.which == "backward":
+        return bench_backward(args, d, w, dev)
 
     if args.epilogue != "none":
         gen = torch.Generator(device=dev).manual_seed(1)
