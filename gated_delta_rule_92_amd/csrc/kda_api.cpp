@@ -298,11 +298,12 @@ namespace {
 
 size_t bwd_elt(kda_dtype_t dtype) { return dtype == KDA_BFLOAT16 ? 2 : 4; }
 
-// Upper bound on the checkpoint slots of either layout (dense: B sequences of
-// ceil(T / 16) tiles; packed: floor(T / 16) + N).
-long bwd_slots_bound(int B, int T, int N) {
-  const long dense = (long)B * ((T + 15) / 16);
-  const long packed = (long)B * T / 16 + N;
+// Upper bound on the checkpoint slots of either layout, CT tokens per slot
+// (dense: B sequences of ceil(T / CT) chunks; packed: floor(T / CT) + N).
+long bwd_slots_bound(int B, int T, int N, kda_dtype_t dtype) {
+  const int CT = kda::chunk_bwd_checkpoint_tokens(dtype == KDA_BFLOAT16);
+  const long dense = (long)B * ((T + CT - 1) / CT);
+  const long packed = (long)B * T / CT + N;
   return dense > packed ? dense : packed;
 }
 
@@ -314,7 +315,7 @@ kda_status_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv, i
     return KDA_ERROR_INVALID_VALUE;
   if (dtype != KDA_FLOAT32 && dtype != KDA_BFLOAT16) return KDA_ERROR_INVALID_VALUE;
   const size_t e = bwd_elt(dtype);
-  const size_t ck = round_up((size_t)bwd_slots_bound(B, T, N) * H * Dk * Dv * e, kWorkspaceAlign);
+  const size_t ck = round_up((size_t)bwd_slots_bound(B, T, N, dtype) * H * Dk * Dv * e, kWorkspaceAlign);
   const size_t tok = round_up((size_t)B * T * H * Dv * e, kWorkspaceAlign);
   *bytes = 2 * ck + 3 * tok;
   return KDA_SUCCESS;
@@ -355,11 +356,11 @@ kda_status_t kda_chunk_bwd(const void* q, const void* k, const void* v, kda_dtyp
   st = kda_chunk_bwd_workspace_size(B, T, H, Dk, Dv, s.N, chunk, dtype, &need);
   if (st != KDA_SUCCESS) return st;
   if (!workspace || workspace_bytes < need) return KDA_ERROR_INSUFFICIENT_WORKSPACE;
-  const long slots = kda::chunk_bwd_slots(s);
+  const long slots = kda::chunk_bwd_slots(s, dtype == KDA_BFLOAT16);
   if (slots > 0x7fffffffL || (long)s.N * H > 0x7fffffffL) return KDA_ERROR_NOT_SUPPORTED;
   if (s.N == 0) return KDA_SUCCESS;
   const size_t e = bwd_elt(dtype);
-  const size_t ck = round_up((size_t)bwd_slots_bound(B, T, s.N) * H * Dk * Dv * e, kWorkspaceAlign);
+  const size_t ck = round_up((size_t)bwd_slots_bound(B, T, s.N, dtype) * H * Dk * Dv * e, kWorkspaceAlign);
   const size_t tok = round_up((size_t)B * T * H * Dv * e, kWorkspaceAlign);
   char* ws = static_cast<char*>(workspace);
   kda::BwdArgs a;

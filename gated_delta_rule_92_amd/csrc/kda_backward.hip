@@ -63,24 +63,36 @@ struct BCfg {
   static constexpr int NVB = DV / 32;           // ... over d_v
 };
 
+// Checkpoints are kept every CKT tiles (CT = 16 * CKT tokens): the state
+// entering tile j is stored when j % CKT == 0 and the state gradient leaving
+// tile j when j is the last tile of its checkpoint chunk. Chunk c of
+// sequence n has slot base(n) + c.
+template <typename T>
+constexpr int ckt_of() { return sizeof(T) == 2 ? 4 : 1; }
+
 struct Unit {
   long t0;    // first token of the sequence in the packed token axis
   int len;    // tokens in the sequence
   long base;  // first checkpoint slot of the sequence
 };
 
+template <int CT>
+__device__ __forceinline__ long chunk_base(const BwdArgs& a, int n) {
+  return a.cu ? (long)(a.cu[n] / CT) + n : (long)n * ((a.T + CT - 1) / CT);
+}
+
+template <int CT>
 __device__ __forceinline__ Unit unit_of(const BwdArgs& a, int n) {
   Unit u;
   if (a.cu) {
     const int s = a.cu[n], e = a.cu[n + 1];
     u.t0 = s;
     u.len = e - s;
-    u.base = (long)(s / BT) + n;
   } else {
     u.t0 = (long)n * a.T;
     u.len = a.T;
-    u.base = (long)n * ((a.T + BT - 1) / BT);
   }
+  u.base = chunk_base<CT>(a, n);
   return u;
 }
 
@@ -96,11 +108,11 @@ struct TileF32 {
   float beta[BT];
 };
 
-template <typename T, int DK>
+template <typename T, int DK, int NT = NTH>
 __device__ __forceinline__ void load_rows(float (*dst)[DK + 4], const T* src, long t0, int L, int h,
                                           int H) {
   constexpr int Q = DK / 4;
-  for (int idx = threadIdx.x; idx < BT * Q; idx += NTH) {
+  for (int idx = threadIdx.x; idx < BT * Q; idx += NT) {
     const int r = idx / Q, c = (idx % Q) * 4;
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
     if (r < L) x = load4_f32(src + ((t0 + r) * H + h) * (long)DK + c);
@@ -110,12 +122,20 @@ __device__ __forceinline__ void load_rows(float (*dst)[DK + 4], const T* src, lo
 
 // Loads q (if wanted), k, the gate and beta of tokens [t0, t0+L), then forms G
 // (two barriers inside; the caller's LDS arrays are free on entry).
-template <typename T, int DK>
-__device__ void load_tile(TileF32<DK>& tf, const BwdArgs& a, long t0, int L, int h, bool want_q) {
+// Also stages, before its first barrier, whatever `extra` loads (a callable
+// run by every thread), so that those loads overlap the tile's.
+struct NoExtra {
+  __device__ void operator()() const {}
+};
+
+template <typename T, int DK, int NT = NTH, typename Extra = NoExtra>
+__device__ void load_tile(TileF32<DK>& tf, const BwdArgs& a, long t0, int L, int h, bool want_q,
+                          const Extra& extra = Extra()) {
   const int H = a.H;
-  if (want_q) load_rows<T, DK>(tf.q, static_cast<const T*>(a.q), t0, L, h, H);
-  load_rows<T, DK>(tf.k, static_cast<const T*>(a.k), t0, L, h, H);
-  load_rows<float, DK>(tf.G, a.g, t0, L, h, H);
+  if (want_q) load_rows<T, DK, NT>(tf.q, static_cast<const T*>(a.q), t0, L, h, H);
+  load_rows<T, DK, NT>(tf.k, static_cast<const T*>(a.k), t0, L, h, H);
+  load_rows<float, DK, NT>(tf.G, a.g, t0, L, h, H);
+  extra();
   if (threadIdx.x < BT) tf.beta[threadIdx.x] = (int)threadIdx.x < L ? a.beta[(t0 + threadIdx.x) * H + h] : 0.f;
   __syncthreads();
   if (threadIdx.x < DK) {
@@ -218,8 +238,9 @@ __global__ void __launch_bounds__(NTH) bwd_fwd_scan(BwdArgs a) {
   using C = BCfg<T, DK, DV>;
   using M = Mma<T>;
   __shared__ FwdSmem<T, DK, DV> sm;
+  constexpr int CKT = ckt_of<T>();
   const int n = blockIdx.x / a.H, h = blockIdx.x % a.H;
-  const Unit un = unit_of(a, n);
+  const Unit un = unit_of<BT * CKT>(a, n);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
@@ -242,17 +263,19 @@ __global__ void __launch_bounds__(NTH) bwd_fwd_scan(BwdArgs a) {
   for (int j = 0; j < nt; ++j) {
     const long t0 = un.t0 + (long)j * BT;
     const int L = min(BT, un.len - j * BT);
-    // checkpoint: the state entering this tile
-    const long ck = ((un.base + j) * H + h) * (long)DK * DV;
+    // checkpoint: the state entering this tile, at the start of every chunk
+    if (j % CKT == 0) {
+      const long ck = ((un.base + j / CKT) * H + h) * (long)DK * DV;
 #pragma unroll
-    for (int tr = 0; tr < DK / 16; ++tr)
+      for (int tr = 0; tr < DK / 16; ++tr)
 #pragma unroll
-      for (int tv = 0; tv < C::NTV; ++tv) {
-        const int col = (w * C::NTV + tv) * 16 + lr;
+        for (int tv = 0; tv < C::NTV; ++tv) {
+          const int col = (w * C::NTV + tv) * 16 + lr;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          st<T>(a.ckS, ck + (long)(16 * tr + 4 * lg + e) * DV + col, S[tr][tv][e]);
-      }
+          for (int e = 0; e < 4; ++e)
+            st<T>(a.ckS, ck + (long)(16 * tr + 4 * lg + e) * DV + col, S[tr][tv][e]);
+        }
+    }
 
     load_tile<T, DK>(sm.tf, a, t0, L, h, false);
     load_rows<T, DV>(sm.v, static_cast<const T*>(a.v), t0, L, h, H);
@@ -350,8 +373,9 @@ __global__ void __launch_bounds__(NTH) bwd_rev_scan(BwdArgs a) {
   using C = BCfg<T, DK, DV>;
   using M = Mma<T>;
   __shared__ RevSmem<T, DK, DV> sm;
+  constexpr int CKT = ckt_of<T>();
   const int n = blockIdx.x / a.H, h = blockIdx.x % a.H;
-  const Unit un = unit_of(a, n);
+  const Unit un = unit_of<BT * CKT>(a, n);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
@@ -375,17 +399,19 @@ __global__ void __launch_bounds__(NTH) bwd_rev_scan(BwdArgs a) {
   for (int j = nt - 1; j >= 0; --j) {
     const long t0 = un.t0 + (long)j * BT;
     const int L = min(BT, un.len - j * BT);
-    // checkpoint: the state gradient leaving this tile
-    const long ck = ((un.base + j) * H + h) * (long)DK * DV;
+    // checkpoint: the state gradient leaving the last tile of every chunk
+    if (j % CKT == CKT - 1 || j == nt - 1) {
+      const long ck = ((un.base + j / CKT) * H + h) * (long)DK * DV;
 #pragma unroll
-    for (int tr = 0; tr < DK / 16; ++tr)
+      for (int tr = 0; tr < DK / 16; ++tr)
 #pragma unroll
-      for (int tv = 0; tv < C::NTV; ++tv) {
-        const int col = (w * C::NTV + tv) * 16 + lr;
+        for (int tv = 0; tv < C::NTV; ++tv) {
+          const int col = (w * C::NTV + tv) * 16 + lr;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          st<T>(a.ckdS, ck + (long)(16 * tr + 4 * lg + e) * DV + col, dS[tr][tv][e]);
-      }
+          for (int e = 0; e < 4; ++e)
+            st<T>(a.ckdS, ck + (long)(16 * tr + 4 * lg + e) * DV + col, dS[tr][tv][e]);
+        }
+    }
 
     load_tile<T, DK>(sm.tf, a, t0, L, h, true);
     {
@@ -487,6 +513,17 @@ __global__ void __launch_bounds__(NTH) bwd_rev_scan(BwdArgs a) {
 }
 
 // =============================================================== tile_grad ==
+// One workgroup per (checkpoint chunk, head): d_k/16 wavefronts, wavefront w
+// owns channels c = 16w + (lane % 16). A lane keeps rows c of the state and
+// of the state gradient as S[c][16b + 4*(lane/16) + e] (b = value block):
+// exactly the matrix-core operand that contracts over d_v, and the layout in
+// which the row-separable updates
+//   S_{j+1}[c,:] = Gamma_L[c] S_j[c,:] + sum_t Kt[t,c] V~[t,:]
+//   dS'_{j-1}[c,:] = Gamma_L[c] dS'_j[c,:] + sum_t Qg[t,c] dO[t,:] - sum_t beta_t Kg[t,c] dY[t,:]
+// need nothing from other wavefronts. From the chunk's two checkpoints the
+// workgroup rebuilds the states entering its inner tiles (from the stored
+// V~), then walks the tiles backwards forming every gradient and carrying the
+// state gradient down (from the stored dY).
 template <typename T, int DK, int DV>
 struct GradSmem {
   using C = BCfg<T, DK, DV>;
@@ -499,13 +536,35 @@ struct GradSmem {
   T dAqkT[BT][C::TSP];         // its transpose
   T dAt[BT][C::TSP];           // beta_r dAkk[r, i] (gradient of A~ = Akk / beta)
   T dAtT[BT][C::TSP];
+  T VT[DV][C::TSP];            // V~^T, dO^T, dY^T of the current tile
+  T dOT[DV][C::TSP];
+  T dYT[DV][C::TSP];
 };
 
+// Rows [t0, t0+L) of a [Ttot, H, DV] array, transposed into dst[DV][TSP].
+template <typename T, int DV, int TSP, int NT>
+__device__ __forceinline__ void stage_t(T (*dst)[TSP], const void* src, long t0, int L, int h,
+                                        int H) {
+  constexpr int Q = DV / 4;
+  for (int idx = threadIdx.x; idx < BT * Q; idx += NT) {
+    const int r = idx / Q, c = (idx % Q) * 4;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (r < L) x = load4_f32(static_cast<const T*>(src) + ((t0 + r) * H + h) * (long)DV + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[c + e][r] = (T)x[e];
+  }
+}
+
 template <typename T, int DK, int DV>
-__global__ void __launch_bounds__(NTH) bwd_tile_grad(BwdArgs a) {
+__global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
   using C = BCfg<T, DK, DV>;
   using M = Mma<T>;
   using frag = typename M::frag;
+  constexpr int NW = DK / 16;
+  constexpr int NT = 64 * NW;
+  constexpr int CKT = ckt_of<T>();
+  constexpr int CT = BT * CKT;
+  constexpr int NVT = DV / 16;
   __shared__ GradSmem<T, DK, DV> sm;
   const int h = blockIdx.y;
   const long slot = blockIdx.x;
@@ -515,178 +574,198 @@ __global__ void __launch_bounds__(NTH) bwd_tile_grad(BwdArgs a) {
     int lo = 0, hi = a.N - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) / 2;
-      if ((long)(a.cu[mid] / BT) + mid <= slot) lo = mid; else hi = mid - 1;
+      if (chunk_base<CT>(a, mid) <= slot) lo = mid; else hi = mid - 1;
     }
     n = lo;
   } else {
-    n = (int)(slot / ((a.T + BT - 1) / BT));
+    n = (int)(slot / ((a.T + CT - 1) / CT));
   }
-  const Unit un = unit_of(a, n);
-  const long j = slot - un.base;
-  if (j * BT >= un.len) return;  // slot past the sequence's last tile (uniform)
-  const long t0 = un.t0 + j * BT;
-  const int L = min((long)BT, un.len - j * BT);
+  const Unit un = unit_of<CT>(a, n);
+  const long cidx = slot - un.base;
+  if (cidx * CT >= un.len) return;  // slot past the sequence's last chunk (uniform)
+  const int j0 = (int)cidx * CKT;
+  const int nt = (un.len + BT - 1) / BT;
+  const int nsub = min(CKT, nt - j0);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
+  const int c = 16 * w + lr;
   const float sc = a.scale;
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  const frag fz = M::make(z);
 
-  // Row fragments of dO, dY, V~ (row lr, value positions of the 32-blocks)
-  // and of both checkpoints (row = channel of this wavefront's tiles).
-  const frag fz = M::make(f32x4{0.f, 0.f, 0.f, 0.f});
-  frag aO[C::NVB][2], aY[C::NVB][2], aV[C::NVB][2];
+  // rows c of the chunk's two checkpoints
+  const long ck = (slot * H + h) * (long)DK * DV + (long)c * DV;
+  f32x4 dSr[NVT];
+  frag Sf[CKT][NVT];
   {
-    const bool ok = lr < L;
-    const long row = ((t0 + lr) * H + h) * (long)DV;
+    f32x4 Sr[NVT];
 #pragma unroll
-    for (int kb = 0; kb < C::NVB; ++kb)
+    for (int b = 0; b < NVT; ++b) {
+      Sr[b] = load4_f32(static_cast<const T*>(a.ckS) + ck + 16 * b + 4 * lg);
+      dSr[b] = load4_f32(static_cast<const T*>(a.ckdS) + ck + 16 * b + 4 * lg);
+      Sf[0][b] = M::make(Sr[b]);
+    }
+    // states entering the inner tiles: S_{j+1} = Diag(Gamma_L) S_j + Kt^T V~
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const long off = row + 32 * kb + 16 * hf + 4 * lg;
-        aO[kb][hf] = ok ? load_frag(static_cast<const T*>(a.dO) + off) : fz;
-        aY[kb][hf] = ok ? load_frag(static_cast<const T*>(a.dY) + off) : fz;
-        aV[kb][hf] = ok ? load_frag(static_cast<const T*>(a.Vt) + off) : fz;
+    for (int j = 0; j + 1 < CKT; ++j) {
+      if (j + 1 >= nsub) break;
+      const long t0 = un.t0 + (long)(j0 + j) * BT;
+      const int L = min(BT, un.len - (j0 + j) * BT);
+      load_tile<T, DK, NT>(sm.tf, a, t0, L, h, false, [&] {
+        stage_t<T, DV, C::TSP, NT>(sm.VT, a.Vt, t0, L, h, H);
+      });
+      const float GL = sm.tf.G[BT - 1][c], gl = fast_exp2(GL);
+      f32x4 Kt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Kt[e] = sm.tf.k[4 * lg + e][c] * fast_exp2(GL - sm.tf.G[4 * lg + e][c]);
+      const frag ktf = M::make(Kt);
+#pragma unroll
+      for (int b = 0; b < NVT; ++b) {
+        Sr[b] = M::k16(load_frag(&sm.VT[16 * b + lr][4 * lg]), ktf, Sr[b] * gl);
+        Sf[j + 1][b] = M::make(Sr[b]);
       }
-  }
-  const long ck = ((un.base + j) * H + h) * (long)DK * DV;
-  frag bS[C::NCT][C::NVB][2], bD[C::NCT][C::NVB][2];
-#pragma unroll
-  for (int i = 0; i < C::NCT; ++i) {
-    const int c = 16 * (w + NWB * i) + lr;
-#pragma unroll
-    for (int kb = 0; kb < C::NVB; ++kb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const long off = ck + (long)c * DV + 32 * kb + 16 * hf + 4 * lg;
-        bS[i][kb][hf] = load_frag(static_cast<const T*>(a.ckS) + off);
-        bD[i][kb][hf] = load_frag(static_cast<const T*>(a.ckdS) + off);
-      }
+      __syncthreads();  // LDS reused by the next tile
+    }
   }
 
-  load_tile<T, DK>(sm.tf, a, t0, L, h, true);
-  for (int idx = threadIdx.x; idx < BT * DK; idx += NTH) {
-    const int r = idx / DK, c = idx % DK;
-    const float G = sm.tf.G[r][c], kk = sm.tf.k[r][c], rho = sm.tf.G[7][c];
-    sm.Kl[r][c] = (T)(kk * fast_exp2(G - rho));
-    sm.Kd[r][c] = (T)(kk * fast_exp2(rho - G));
-  }
-  __syncthreads();
-
-  // dQg = dO S^T, dKg = -(beta dY) S^T, dKt = V~ dS'^T on this wavefront's
-  // channel tiles; dGamma_L = rowsum(dS' * S).
-  f32x4 dQg[C::NCT], dKg[C::NCT], dKt[C::NCT];
-  float dGL[C::NCT];
 #pragma unroll
-  for (int i = 0; i < C::NCT; ++i) {
-    f32x4 p = {0.f, 0.f, 0.f, 0.f}, y = p, t = p;
+  for (int j = CKT - 1; j >= 0; --j) {
+    if (j >= nsub) continue;
+    const long t0 = un.t0 + (long)(j0 + j) * BT;
+    const int L = min(BT, un.len - (j0 + j) * BT);
+    // row fragments of dO, dY, V~ (row lr, value positions of the 32-blocks)
+    frag aO[C::NVB][2], aY[C::NVB][2], aV[C::NVB][2];
+    {
+      const bool ok = lr < L;
+      const long row = ((t0 + lr) * H + h) * (long)DV;
+#pragma unroll
+      for (int kb = 0; kb < C::NVB; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const long off = row + 32 * kb + 16 * hf + 4 * lg;
+          aO[kb][hf] = ok ? load_frag(static_cast<const T*>(a.dO) + off) : fz;
+          aY[kb][hf] = ok ? load_frag(static_cast<const T*>(a.dY) + off) : fz;
+          aV[kb][hf] = ok ? load_frag(static_cast<const T*>(a.Vt) + off) : fz;
+        }
+    }
+    load_tile<T, DK, NT>(sm.tf, a, t0, L, h, true, [&] {
+      if (j > 0) {
+        stage_t<T, DV, C::TSP, NT>(sm.dOT, a.dO, t0, L, h, H);
+        stage_t<T, DV, C::TSP, NT>(sm.dYT, a.dY, t0, L, h, H);
+      }
+    });
+    for (int idx = threadIdx.x; idx < BT * DK; idx += NT) {
+      const int r = idx / DK, cc = idx % DK;
+      const float G = sm.tf.G[r][cc], kk = sm.tf.k[r][cc], rho = sm.tf.G[7][cc];
+      sm.Kl[r][cc] = (T)(kk * fast_exp2(G - rho));
+      sm.Kd[r][cc] = (T)(kk * fast_exp2(rho - G));
+    }
+    __syncthreads();
+
+    // dQg = dO S^T, dKg = -(beta dY) S^T, dKt = V~ dS'^T on this wavefront's
+    // channels; dGamma_L = rowsum(dS' * S).
+    f32x4 dQg = z, dKg = z, dKt = z;
     float gsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < C::NVB; ++kb) {
-      p = M::k32(aO[kb][0], aO[kb][1], bS[i][kb][0], bS[i][kb][1], p);
-      y = M::k32(aY[kb][0], aY[kb][1], bS[i][kb][0], bS[i][kb][1], y);
-      t = M::k32(aV[kb][0], aV[kb][1], bD[i][kb][0], bD[i][kb][1], t);
+      const frag d0 = M::make(dSr[2 * kb]), d1 = M::make(dSr[2 * kb + 1]);
+      dQg = M::k32(aO[kb][0], aO[kb][1], Sf[j][2 * kb], Sf[j][2 * kb + 1], dQg);
+      dKg = M::k32(aY[kb][0], aY[kb][1], Sf[j][2 * kb], Sf[j][2 * kb + 1], dKg);
+      dKt = M::k32(aV[kb][0], aV[kb][1], d0, d1, dKt);
+    }
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const f32x4 s4 = M::to_f32(bS[i][kb][hf]), d4 = M::to_f32(bD[i][kb][hf]);
-        gsum += s4[0] * d4[0] + s4[1] * d4[1] + s4[2] * d4[2] + s4[3] * d4[3];
-      }
+    for (int b = 0; b < NVT; ++b) {
+      const f32x4 s4 = M::to_f32(Sf[j][b]);
+      gsum += s4[0] * dSr[b][0] + s4[1] * dSr[b][1] + s4[2] * dSr[b][2] + s4[3] * dSr[b][3];
     }
     gsum += __shfl_xor(gsum, 16, 64);
     gsum += __shfl_xor(gsum, 32, 64);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) y[e] *= -sm.tf.beta[4 * lg + e];
-    dQg[i] = p;
-    dKg[i] = y;
-    dKt[i] = t;
-    dGL[i] = gsum;
-  }
+    for (int e = 0; e < 4; ++e) dKg[e] *= -sm.tf.beta[4 * lg + e];
 
-  if (w == 0) {
-    // dAqk = Tril(dO V~^T)
-    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+    if (w == 0) {
+      // dAqk = Tril(dO V~^T)
+      f32x4 p = z;
 #pragma unroll
-    for (int kb = 0; kb < C::NVB; ++kb) p = M::k32(aO[kb][0], aO[kb][1], aV[kb][0], aV[kb][1], p);
+      for (int kb = 0; kb < C::NVB; ++kb) p = M::k32(aO[kb][0], aO[kb][1], aV[kb][0], aV[kb][1], p);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 4 * lg + e;
-      const T x = (T)(lr <= r ? p[e] : 0.f);
-      sm.dAqk[r][lr] = x;
-      sm.dAqkT[lr][r] = x;
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * lg + e;
+        const T x = (T)(lr <= r ? p[e] : 0.f);
+        sm.dAqk[r][lr] = x;
+        sm.dAqkT[lr][r] = x;
+      }
+    } else if (w == 1) {
+      // dAkk = -StrictTril(dY V~^T); A~ = Kl Kd^T; dbeta from both and from U
+      f32x4 p = z;
+#pragma unroll
+      for (int kb = 0; kb < C::NVB; ++kb) p = M::k32(aY[kb][0], aY[kb][1], aV[kb][0], aV[kb][1], p);
+      const f32x4 At = tri_product<T, DK, C::DKP>(sm.Kl, sm.Kd, lr, lg);
+      f32x4 part;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * lg + e;
+        const float dA = lr < r ? -p[e] : 0.f;
+        part[e] = lr < r ? dA * At[e] : 0.f;
+        const T x = (T)(sm.tf.beta[r] * dA);
+        sm.dAt[r][lr] = x;
+        sm.dAtT[lr][r] = x;
+      }
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part[e] += __shfl_xor(part[e], m, 64);
+      if (lr == 0)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.dbA[4 * lg + e] = part[e];
+      // rowsum(dY * U), row lr
+      float u = 0.f;
+      const bool ok = lr < L;
+      const long row = ((t0 + lr) * H + h) * (long)DV;
+#pragma unroll
+      for (int kb = 0; kb < C::NVB; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const frag uf =
+              ok ? load_frag(static_cast<const T*>(a.U) + row + 32 * kb + 16 * hf + 4 * lg) : fz;
+          const f32x4 u4 = M::to_f32(uf), y4 = M::to_f32(aY[kb][hf]);
+          u += u4[0] * y4[0] + u4[1] * y4[1] + u4[2] * y4[2] + u4[3] * y4[3];
+        }
+      u += __shfl_xor(u, 16, 64);
+      u += __shfl_xor(u, 32, 64);
+      if (lg == 0) sm.dbU[lr] = u;
     }
-  } else if (w == 1) {
-    // dAkk = -StrictTril(dY V~^T); A~ = Kl Kd^T; dbeta from both and from U
-    f32x4 p = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < C::NVB; ++kb) p = M::k32(aY[kb][0], aY[kb][1], aV[kb][0], aV[kb][1], p);
-    const f32x4 At = tri_product<T, DK, C::DKP>(sm.Kl, sm.Kd, lr, lg);
-    f32x4 part;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 4 * lg + e;
-      const float dA = lr < r ? -p[e] : 0.f;
-      part[e] = lr < r ? dA * At[e] : 0.f;
-      const T x = (T)(sm.tf.beta[r] * dA);
-      sm.dAt[r][lr] = x;
-      sm.dAtT[lr][r] = x;
-    }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) part[e] += __shfl_xor(part[e], m, 64);
-    if (lr == 0)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sm.dbA[4 * lg + e] = part[e];
-    // rowsum(dY * U), row lr
-    float u = 0.f;
-    const bool ok = lr < L;
-    const long row = ((t0 + lr) * H + h) * (long)DV;
-#pragma unroll
-    for (int kb = 0; kb < C::NVB; ++kb)
+    __syncthreads();
+
+    if ((int)threadIdx.x < L)
+      a.dbeta[(t0 + threadIdx.x) * H + h] = sm.dbA[threadIdx.x] + sm.dbU[threadIdx.x];
+    // dV = beta dY, one 32-block of value positions per wavefront
+    if (w < C::NVB && lr < L) {
+      const float bb = sm.tf.beta[lr];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const frag uf = ok ? load_frag(static_cast<const T*>(a.U) + row + 32 * kb + 16 * hf + 4 * lg)
-                           : fz;
-        const f32x4 u4 = M::to_f32(uf), y4 = M::to_f32(aY[kb][hf]);
-        u += u4[0] * y4[0] + u4[1] * y4[1] + u4[2] * y4[2] + u4[3] * y4[3];
-      }
-    u += __shfl_xor(u, 16, 64);
-    u += __shfl_xor(u, 32, 64);
-    if (lg == 0) sm.dbU[lr] = u;
-  }
-  __syncthreads();
-
-  if ((int)threadIdx.x < L) a.dbeta[(t0 + threadIdx.x) * H + h] = sm.dbA[threadIdx.x] + sm.dbU[threadIdx.x];
-  // dV = beta dY, one 32-block of value positions per wavefront
-  for (int kb = w; kb < C::NVB; kb += NWB) {
-    if (lr < L) {
-      const float b = sm.tf.beta[lr];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const f32x4 y4 = M::to_f32(aY[kb][hf]);
-        store4(static_cast<T*>(a.dv) + ((t0 + lr) * H + h) * (long)DV + 32 * kb + 16 * hf + 4 * lg,
-               f32x4{b * y4[0], b * y4[1], b * y4[2], b * y4[3]});
+        const f32x4 y4 = M::to_f32(aY[w][hf]);
+        store4(static_cast<T*>(a.dv) + ((t0 + lr) * H + h) * (long)DV + 32 * w + 16 * hf + 4 * lg,
+               f32x4{bb * y4[0], bb * y4[1], bb * y4[2], bb * y4[3]});
       }
     }
-  }
 
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < C::NCT; ++i) {
-    const int c = 16 * (w + NWB * i) + lr;
     const float rho = sm.tf.G[7][c], GL = sm.tf.G[BT - 1][c];
-    f32x4 Gv, gam, el, ed, et, qq, kk;
+    f32x4 gam, el, ed, et, qq, kk, bt;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = 4 * lg + e;
-      Gv[e] = sm.tf.G[t][c];
-      gam[e] = fast_exp2(Gv[e]);
-      el[e] = fast_exp2(Gv[e] - rho);
-      ed[e] = fast_exp2(rho - Gv[e]);
-      et[e] = fast_exp2(GL - Gv[e]);
+      const float Gv = sm.tf.G[t][c];
+      gam[e] = fast_exp2(Gv);
+      el[e] = fast_exp2(Gv - rho);
+      ed[e] = fast_exp2(rho - Gv);
+      et[e] = fast_exp2(GL - Gv);
       qq[e] = sc * sm.tf.q[t][c];
       kk[e] = sm.tf.k[t][c];
+      bt[e] = sm.tf.beta[t];
     }
-    const f32x4 Kd = kk * ed, Kl = kk * el, Ql = qq * el;
+    const f32x4 Kd = kk * ed, Kl = kk * el, Ql = qq * el, Qg = qq * gam, Kg = kk * gam;
     const f32x4 dQl = M::k16(load_frag(&sm.dAqk[lr][4 * lg]), M::make(Kd), z);
     const f32x4 dKl = M::k16(load_frag(&sm.dAt[lr][4 * lg]), M::make(Kd), z);
     const f32x4 dKd = M::k32(load_frag(&sm.dAqkT[lr][4 * lg]), load_frag(&sm.dAtT[lr][4 * lg]),
@@ -696,18 +775,18 @@ __global__ void __launch_bounds__(NTH) bwd_tile_grad(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float Kt = kk[e] * et[e];
-      dq[e] = sc * (dQg[i][e] * gam[e] + dQl[e] * el[e]);
-      dk[e] = dKg[i][e] * gam[e] + dKt[i][e] * et[e] + dKl[e] * el[e] + dKd[e] * ed[e];
-      dG[e] = dQg[i][e] * qq[e] * gam[e] + dKg[i][e] * kk[e] * gam[e] - dKt[i][e] * Kt +
-              dQl[e] * Ql[e] + dKl[e] * Kl[e] - dKd[e] * Kd[e];
-      tsum += dKt[i][e] * Kt;
+      dq[e] = sc * (dQg[e] * gam[e] + dQl[e] * el[e]);
+      dk[e] = dKg[e] * gam[e] + dKt[e] * et[e] + dKl[e] * el[e] + dKd[e] * ed[e];
+      dG[e] = dQg[e] * Qg[e] + dKg[e] * Kg[e] - dKt[e] * Kt + dQl[e] * Ql[e] + dKl[e] * Kl[e] -
+              dKd[e] * Kd[e];
+      tsum += dKt[e] * Kt;
     }
     tsum += __shfl_xor(tsum, 16, 64);
     tsum += __shfl_xor(tsum, 32, 64);
     // G_L is the last row's G (rows past the end repeat it), so its
     // gradient joins row 15 and reaches every valid row through the
     // reverse cumulative sum.
-    if (lg == 3) dG[3] += tsum + dGL[i] * fast_exp2(GL);
+    if (lg == 3) dG[3] += tsum + gsum * fast_exp2(GL);
     // reverse cumulative sum over the 16 tokens (4 per lane, 4 lane groups)
     f32x4 suf;
     suf[3] = dG[3];
@@ -729,6 +808,17 @@ __global__ void __launch_bounds__(NTH) bwd_tile_grad(BwdArgs a) {
         a.dg[idx] = suf[e] + after;
       }
     }
+
+    // the state gradient entering this tile = the one leaving the tile before
+    if (j > 0) {
+      const float gl = fast_exp2(GL);
+      const frag qf = M::make(Qg), kf = M::make_neg(Kg * bt);
+#pragma unroll
+      for (int b = 0; b < NVT; ++b)
+        dSr[b] = M::k32(load_frag(&sm.dOT[16 * b + lr][4 * lg]), load_frag(&sm.dYT[16 * b + lr][4 * lg]),
+                        qf, kf, dSr[b] * gl);
+    }
+    __syncthreads();  // LDS reused by the next tile
   }
 }
 
@@ -738,8 +828,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, long slots, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_fwd_scan<T, DK, DV>), dim3(units), dim3(NTH), 0, stream, a);
   hipLaunchKernelGGL((bwd_rev_scan<T, DK, DV>), dim3(units), dim3(NTH), 0, stream, a);
   if (slots > 0)
-    hipLaunchKernelGGL((bwd_tile_grad<T, DK, DV>), dim3((unsigned)slots, (unsigned)a.H), dim3(NTH),
-                       0, stream, a);
+    hipLaunchKernelGGL((bwd_tile_grad<T, DK, DV>), dim3((unsigned)slots, (unsigned)a.H),
+                       dim3(64 * (DK / 16)), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -758,9 +848,12 @@ bool chunk_bwd_supported(int Dk, int Dv) {
   return (Dk == 64 || Dk == 128) && (Dv == 64 || Dv == 128);
 }
 
-long chunk_bwd_slots(const Seqs& s) {
-  if (s.cu) return s.Ttot / BT + s.N;
-  return (long)s.N * ((s.T + BT - 1) / BT);
+int chunk_bwd_checkpoint_tokens(bool bf16) { return BT * (bf16 ? ckt_of<__bf16>() : ckt_of<float>()); }
+
+long chunk_bwd_slots(const Seqs& s, bool bf16) {
+  const int CT = chunk_bwd_checkpoint_tokens(bf16);
+  if (s.cu) return s.Ttot / CT + s.N;
+  return (long)s.N * ((s.T + CT - 1) / CT);
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs& a, bool bf16, int Dk, int Dv, long slots,

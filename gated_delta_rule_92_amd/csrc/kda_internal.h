@@ -87,11 +87,12 @@ constexpr float kMinFusedGmin = -5.5f;
 hipError_t launch_chunk_fused(const ChunkArgs& a, hipStream_t stream);
 
 // Backward of the chunk forward (three kernels: forward scan writing the
-// per-tile state checkpoints, U and V~; reverse scan writing the per-tile
-// state-gradient checkpoints and dY; per-tile gradients). Tiles are 16 tokens
-// of one sequence; checkpoint slot of tile j of sequence n is
-// tile_base(n) + j, tile_base(n) = floor(cu[n] / 16) + n (packed) or
-// n * ceil(T / 16) (dense).
+// state checkpoints, U and V~; reverse scan writing the state-gradient
+// checkpoints and dY; per-chunk gradients). Tiles are 16 tokens of one
+// sequence; checkpoints are kept every CT tokens (chunk_bwd_checkpoint_tokens:
+// 64 for bf16, 16 for fp32); checkpoint chunk c of sequence n has slot
+// base(n) + c, base(n) = floor(cu[n] / CT) + n (packed) or n * ceil(T / CT)
+// (dense).
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -113,14 +114,15 @@ struct BwdArgs {
   float* dg;
   float* dbeta;
   float* dh0;          // or nullptr
-  void* ckS;           // [slots, H, Dk, Dv] states entering each tile
-  void* ckdS;          // [slots, H, Dk, Dv] state gradients leaving each tile
+  void* ckS;           // [slots, H, Dk, Dv] states entering each checkpoint chunk
+  void* ckdS;          // [slots, H, Dk, Dv] state gradients leaving each chunk
   void* U;             // [Ttot, H, Dv] V - Kg S
   void* Vt;            // [Ttot, H, Dv] pseudo-values
   void* dY;            // [Ttot, H, Dv] T^T dV~
 };
 bool chunk_bwd_supported(int Dk, int Dv);
-long chunk_bwd_slots(const Seqs& s);
+int chunk_bwd_checkpoint_tokens(bool bf16);
+long chunk_bwd_slots(const Seqs& s, bool bf16);
 hipError_t launch_chunk_bwd(const BwdArgs& a, bool bf16, int Dk, int Dv, long slots,
                             hipStream_t stream);
 // Gradient of the gate w.r.t. z (dz, may alias dg) and, if dA != nullptr,

@@ -257,9 +257,10 @@ kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v, kda
 
 /*
  * kda_chunk_bwd_workspace_size — bytes of device workspace kda_chunk_bwd
- * needs (256-byte aligned): two per-tile state checkpoints
- * [slots, H, Dk, Dv] and three per-token [B*T, H, Dv] arrays in the input
- * dtype, slots = max(B * ceil(T/16), B*T/16 + N).
+ * needs (256-byte aligned): two state checkpoints [slots, H, Dk, Dv], one
+ * every C tokens of each sequence (C = 64 for bf16, 16 for fp32), and three
+ * per-token [B*T, H, Dv] arrays, all in the input dtype;
+ * slots = max(B * ceil(T/C), B*T/C + N).
  */
 kda_status_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv, int N,
                                           int chunk, kda_dtype_t dtype, size_t* bytes);
@@ -271,8 +272,9 @@ kda_status_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv, i
  * state. The pages state the forward only [KDA-blog §Kimi Delta Attention,
  * KDA equation; §Chunkwise parallel form]; this is the exact derivative of
  * that recurrence, evaluated on 16-token tiles: a forward scan stores the
- * state entering every tile, a reverse scan stores the state gradient
- * leaving every tile, and every tile then forms its gradients on its own.
+ * state entering every 64-token chunk (16 for fp32), a reverse scan the
+ * state gradient leaving it, and every chunk then forms its gradients on its
+ * own, rebuilding the states inside it.
  *
  * Inputs as for kda_chunk_fwd (same layouts, dtype, gate, scale, sequences);
  * gate_input is KDA_GATE_LOGDECAY (g = log-decay) or KDA_GATE_LOGITS (g = z,

@@ -213,13 +213,13 @@ def test_chunk_bwd_not_supported_and_workspace():
     lib = _lib.load()
     n = ctypes.c_size_t(0)
     assert lib.kda_chunk_bwd_workspace_size(8, 8192, 32, 128, 128, 8, 64, 1, ctypes.byref(n)) == 0
-    # two bf16 checkpoints per 16-token tile slot (slots = max(B ceil(T/16),
-    # B T / 16 + N) per head) and three bf16 per-token arrays
-    tiles, tokens = (8 * 8192 // 16 + 8) * 32, 8 * 8192 * 32
+    # two bf16 checkpoints per 64-token chunk slot (slots = max(B ceil(T/64),
+    # B T / 64 + N) per head) and three bf16 per-token arrays
+    tiles, tokens = (8 * 8192 // 64 + 8) * 32, 8 * 8192 * 32
     assert n.value == 2 * tiles * 128 * 128 * 2 + 3 * tokens * 128 * 2
     assert _bwd(ws_bytes=n.value - 1, B=8, N=8, T=8192, H=32) == \
         _lib.KDA_ERROR_INSUFFICIENT_WORKSPACE
-    # packed sequences: up to one ragged tile per sequence
+    # packed sequences: up to one ragged chunk per sequence (fp32: 16-token chunks)
     assert lib.kda_chunk_bwd_workspace_size(1, 100, 1, 64, 64, 10, 64, 0, ctypes.byref(n)) == 0
     assert n.value >= 2 * (100 // 16 + 10) * 64 * 64 * 4
     assert _bwd(cu=FAKE, N=0, T=0) == _lib.KDA_SUCCESS
