@@ -520,39 +520,56 @@ __global__ void __launch_bounds__(NTH) bwd_rev_scan(BwdArgs a) {
 // which the row-separable updates
 //   S_{j+1}[c,:] = Gamma_L[c] S_j[c,:] + sum_t Kt[t,c] V~[t,:]
 //   dS'_{j-1}[c,:] = Gamma_L[c] dS'_j[c,:] + sum_t Qg[t,c] dO[t,:] - sum_t beta_t Kg[t,c] dY[t,:]
-// need nothing from other wavefronts. From the chunk's two checkpoints the
-// workgroup rebuilds the states entering its inner tiles (from the stored
-// V~), then walks the tiles backwards forming every gradient and carrying the
-// state gradient down (from the stored dY).
+// need nothing from other wavefronts. The whole chunk (q, k, the tile-local
+// decay sums, beta, dO, dY, V~, U) is staged in LDS once; from the chunk's
+// two checkpoints the workgroup rebuilds the states entering its inner tiles
+// (from the stored V~), then walks the tiles backwards forming every
+// gradient and carrying the state gradient down (from the stored dY), with
+// one barrier per tile (the per-tile exchange buffers alternate).
 template <typename T, int DK, int DV>
 struct GradSmem {
   using C = BCfg<T, DK, DV>;
-  TileF32<DK> tf;
-  float dbA[BT];
-  float dbU[BT];
-  T Kl[BT][C::DKP];
-  T Kd[BT][C::DKP];
-  T dAqk[BT][C::TSP];          // dAqk, row-major
-  T dAqkT[BT][C::TSP];         // its transpose
-  T dAt[BT][C::TSP];           // beta_r dAkk[r, i] (gradient of A~ = Akk / beta)
-  T dAtT[BT][C::TSP];
-  T VT[DV][C::TSP];            // V~^T, dO^T, dY^T of the current tile
-  T dOT[DV][C::TSP];
-  T dYT[DV][C::TSP];
+  static constexpr int CT = BT * ckt_of<T>();
+  static constexpr int DVP = DV + pad_of<T>();
+  T q[CT][C::DKP];
+  T k[CT][C::DKP];
+  float G[CT][DK + 4];         // inclusive decay sum inside each 16-token tile, log2 units
+  float beta[CT];
+  T dO[CT][DVP];
+  T dY[CT][DVP];
+  T Vt[CT][DVP];
+  T U[CT][DVP];
+  T dAqk[2][BT][C::TSP];       // dAqk, row-major
+  T dAqkT[2][BT][C::TSP];      // its transpose
+  T dAt[2][BT][C::TSP];        // beta_r dAkk[r, i] (gradient of A~ = Akk / beta)
+  T dAtT[2][BT][C::TSP];
+  float dbA[2][BT];
+  float dbU[2][BT];
 };
 
-// Rows [t0, t0+L) of a [Ttot, H, DV] array, transposed into dst[DV][TSP].
-template <typename T, int DV, int TSP, int NT>
-__device__ __forceinline__ void stage_t(T (*dst)[TSP], const void* src, long t0, int L, int h,
-                                        int H) {
-  constexpr int Q = DV / 4;
-  for (int idx = threadIdx.x; idx < BT * Q; idx += NT) {
+// Rows [t0, t0 + rows) of a [Ttot, H, D] array into dst[CT][ld] (zeros past
+// the end), four elements per thread and step.
+template <typename T, int D, int LD, int CT, int NT>
+__device__ __forceinline__ void stage_rows(T (*dst)[LD], const void* src, long t0, int rows, int h,
+                                           int H) {
+  constexpr int Q = D / 4;
+  for (int idx = threadIdx.x; idx < CT * Q; idx += NT) {
     const int r = idx / Q, c = (idx % Q) * 4;
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if (r < L) x = load4_f32(static_cast<const T*>(src) + ((t0 + r) * H + h) * (long)DV + c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dst[c + e][r] = (T)x[e];
+    if (r < rows) x = load4_f32(static_cast<const T*>(src) + ((t0 + r) * H + h) * (long)D + c);
+    store4(&dst[r][c], x);
   }
+}
+
+// Accumulator-layout tile of a row-major LDS array: element e of lane l is
+// X[r0 + 4*(l/16) + e][c0 + l%16].
+template <typename T, int LD>
+__device__ __forceinline__ typename Mma<T>::frag acc_tile(const T (*X)[LD], int r0, int c0, int lr,
+                                                         int lg) {
+  typename Mma<T>::frag f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f[e] = X[r0 + 4 * lg + e][c0 + lr];
+  return f;
 }
 
 template <typename T, int DK, int DV>
@@ -560,12 +577,15 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
   using C = BCfg<T, DK, DV>;
   using M = Mma<T>;
   using frag = typename M::frag;
+  using SM = GradSmem<T, DK, DV>;
   constexpr int NW = DK / 16;
   constexpr int NT = 64 * NW;
   constexpr int CKT = ckt_of<T>();
   constexpr int CT = BT * CKT;
   constexpr int NVT = DV / 16;
-  __shared__ GradSmem<T, DK, DV> sm;
+  static_assert(CKT * DK <= NT, "one thread per (tile, channel) for the decay sums");
+  static_assert(C::NVB <= NW, "one wavefront per 32 value positions stores dV");
+  __shared__ SM sm;
   const int h = blockIdx.y;
   const long slot = blockIdx.x;
   const int H = a.H;
@@ -583,85 +603,94 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
   const Unit un = unit_of<CT>(a, n);
   const long cidx = slot - un.base;
   if (cidx * CT >= un.len) return;  // slot past the sequence's last chunk (uniform)
-  const int j0 = (int)cidx * CKT;
-  const int nt = (un.len + BT - 1) / BT;
-  const int nsub = min(CKT, nt - j0);
+  const long ct0 = un.t0 + cidx * CT;
+  const int CL = (int)min((long)CT, un.len - cidx * CT);
+  const int nsub = (CL + BT - 1) / BT;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   const int c = 16 * w + lr;
   const float sc = a.scale;
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  const frag fz = M::make(z);
 
-  // rows c of the chunk's two checkpoints
+  // rows c of the chunk's two checkpoints (loads in flight during staging)
   const long ck = (slot * H + h) * (long)DK * DV + (long)c * DV;
-  f32x4 dSr[NVT];
+  f32x4 Sr[NVT], dSr[NVT];
+#pragma unroll
+  for (int b = 0; b < NVT; ++b) {
+    Sr[b] = load4_f32(static_cast<const T*>(a.ckS) + ck + 16 * b + 4 * lg);
+    dSr[b] = load4_f32(static_cast<const T*>(a.ckdS) + ck + 16 * b + 4 * lg);
+  }
+
+  // stage the chunk
+  stage_rows<T, DK, C::DKP, CT, NT>(sm.q, a.q, ct0, CL, h, H);
+  stage_rows<T, DK, C::DKP, CT, NT>(sm.k, a.k, ct0, CL, h, H);
+  stage_rows<T, DV, SM::DVP, CT, NT>(sm.dO, a.dO, ct0, CL, h, H);
+  stage_rows<T, DV, SM::DVP, CT, NT>(sm.dY, a.dY, ct0, CL, h, H);
+  stage_rows<T, DV, SM::DVP, CT, NT>(sm.Vt, a.Vt, ct0, CL, h, H);
+  stage_rows<T, DV, SM::DVP, CT, NT>(sm.U, a.U, ct0, CL, h, H);
+  if ((int)threadIdx.x < CT) {
+    const int r = threadIdx.x;
+    sm.beta[r] = r < CL ? a.beta[(ct0 + r) * H + h] : 0.f;
+  }
+  if ((int)threadIdx.x < CKT * DK) {
+    const int sb = threadIdx.x / DK, cc = threadIdx.x % DK;
+    const float es = (a.gate == kGateLogits && a.A_log) ? __expf(a.A_log[h]) : 1.f;
+    float run = 0.f;
+#pragma unroll
+    for (int r = 0; r < BT; ++r) {
+      const int t = BT * sb + r;
+      float gv = 0.f;
+      if (t < CL) {
+        gv = a.g[((ct0 + t) * H + h) * (long)DK + cc];
+        if (a.gate == kGateLogits) gv = a.g_min * __builtin_amdgcn_rcpf(1.f + fast_exp2(-kLog2e * es * gv));
+      }
+      run += gv;
+      sm.G[t][cc] = run * kLog2e;
+    }
+  }
+  __syncthreads();
+
+  // states entering the inner tiles: S_{j+1} = Diag(Gamma_L) S_j + Kt^T V~
   frag Sf[CKT][NVT];
-  {
-    f32x4 Sr[NVT];
+#pragma unroll
+  for (int b = 0; b < NVT; ++b) Sf[0][b] = M::make(Sr[b]);
+#pragma unroll
+  for (int j = 0; j + 1 < CKT; ++j) {
+    if (j + 1 >= nsub) break;
+    const float GL = sm.G[BT * j + BT - 1][c], gl = fast_exp2(GL);
+    f32x4 Kt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = BT * j + 4 * lg + e;
+      Kt[e] = (float)sm.k[t][c] * fast_exp2(GL - sm.G[t][c]);
+    }
+    const frag ktf = M::make(Kt);
 #pragma unroll
     for (int b = 0; b < NVT; ++b) {
-      Sr[b] = load4_f32(static_cast<const T*>(a.ckS) + ck + 16 * b + 4 * lg);
-      dSr[b] = load4_f32(static_cast<const T*>(a.ckdS) + ck + 16 * b + 4 * lg);
-      Sf[0][b] = M::make(Sr[b]);
-    }
-    // states entering the inner tiles: S_{j+1} = Diag(Gamma_L) S_j + Kt^T V~
-#pragma unroll
-    for (int j = 0; j + 1 < CKT; ++j) {
-      if (j + 1 >= nsub) break;
-      const long t0 = un.t0 + (long)(j0 + j) * BT;
-      const int L = min(BT, un.len - (j0 + j) * BT);
-      load_tile<T, DK, NT>(sm.tf, a, t0, L, h, false, [&] {
-        stage_t<T, DV, C::TSP, NT>(sm.VT, a.Vt, t0, L, h, H);
-      });
-      const float GL = sm.tf.G[BT - 1][c], gl = fast_exp2(GL);
-      f32x4 Kt;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Kt[e] = sm.tf.k[4 * lg + e][c] * fast_exp2(GL - sm.tf.G[4 * lg + e][c]);
-      const frag ktf = M::make(Kt);
-#pragma unroll
-      for (int b = 0; b < NVT; ++b) {
-        Sr[b] = M::k16(load_frag(&sm.VT[16 * b + lr][4 * lg]), ktf, Sr[b] * gl);
-        Sf[j + 1][b] = M::make(Sr[b]);
-      }
-      __syncthreads();  // LDS reused by the next tile
+      Sr[b] = M::k16(acc_tile<T, SM::DVP>(sm.Vt, BT * j, 16 * b, lr, lg), ktf, Sr[b] * gl);
+      Sf[j + 1][b] = M::make(Sr[b]);
     }
   }
 
 #pragma unroll
   for (int j = CKT - 1; j >= 0; --j) {
     if (j >= nsub) continue;
-    const long t0 = un.t0 + (long)(j0 + j) * BT;
-    const int L = min(BT, un.len - (j0 + j) * BT);
+    const int pb = j & 1;
+    const int r0 = BT * j;
+    const long t0 = ct0 + r0;
+    const int L = min(BT, CL - r0);
     // row fragments of dO, dY, V~ (row lr, value positions of the 32-blocks)
     frag aO[C::NVB][2], aY[C::NVB][2], aV[C::NVB][2];
-    {
-      const bool ok = lr < L;
-      const long row = ((t0 + lr) * H + h) * (long)DV;
 #pragma unroll
-      for (int kb = 0; kb < C::NVB; ++kb)
+    for (int kb = 0; kb < C::NVB; ++kb)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const long off = row + 32 * kb + 16 * hf + 4 * lg;
-          aO[kb][hf] = ok ? load_frag(static_cast<const T*>(a.dO) + off) : fz;
-          aY[kb][hf] = ok ? load_frag(static_cast<const T*>(a.dY) + off) : fz;
-          aV[kb][hf] = ok ? load_frag(static_cast<const T*>(a.Vt) + off) : fz;
-        }
-    }
-    load_tile<T, DK, NT>(sm.tf, a, t0, L, h, true, [&] {
-      if (j > 0) {
-        stage_t<T, DV, C::TSP, NT>(sm.dOT, a.dO, t0, L, h, H);
-        stage_t<T, DV, C::TSP, NT>(sm.dYT, a.dY, t0, L, h, H);
+      for (int hf = 0; hf < 2; ++hf) {
+        const int off = 32 * kb + 16 * hf + 4 * lg;
+        aO[kb][hf] = load_frag(&sm.dO[r0 + lr][off]);
+        aY[kb][hf] = load_frag(&sm.dY[r0 + lr][off]);
+        aV[kb][hf] = load_frag(&sm.Vt[r0 + lr][off]);
       }
-    });
-    for (int idx = threadIdx.x; idx < BT * DK; idx += NT) {
-      const int r = idx / DK, cc = idx % DK;
-      const float G = sm.tf.G[r][cc], kk = sm.tf.k[r][cc], rho = sm.tf.G[7][cc];
-      sm.Kl[r][cc] = (T)(kk * fast_exp2(G - rho));
-      sm.Kd[r][cc] = (T)(kk * fast_exp2(rho - G));
-    }
-    __syncthreads();
 
     // dQg = dO S^T, dKg = -(beta dY) S^T, dKt = V~ dS'^T on this wavefront's
     // channels; dGamma_L = rowsum(dS' * S).
@@ -682,7 +711,7 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
     gsum += __shfl_xor(gsum, 16, 64);
     gsum += __shfl_xor(gsum, 32, 64);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) dKg[e] *= -sm.tf.beta[4 * lg + e];
+    for (int e = 0; e < 4; ++e) dKg[e] *= -sm.beta[r0 + 4 * lg + e];
 
     if (w == 0) {
       // dAqk = Tril(dO V~^T)
@@ -693,24 +722,37 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * lg + e;
         const T x = (T)(lr <= r ? p[e] : 0.f);
-        sm.dAqk[r][lr] = x;
-        sm.dAqkT[lr][r] = x;
+        sm.dAqk[pb][r][lr] = x;
+        sm.dAqkT[pb][lr][r] = x;
       }
     } else if (w == 1) {
-      // dAkk = -StrictTril(dY V~^T); A~ = Kl Kd^T; dbeta from both and from U
+      // dAkk = -StrictTril(dY V~^T); A~ = Kl Kd^T over all channels; dbeta
       f32x4 p = z;
 #pragma unroll
       for (int kb = 0; kb < C::NVB; ++kb) p = M::k32(aY[kb][0], aY[kb][1], aV[kb][0], aV[kb][1], p);
-      const f32x4 At = tri_product<T, DK, C::DKP>(sm.Kl, sm.Kd, lr, lg);
+      f32x4 At = z;
+#pragma unroll
+      for (int cb = 0; cb < DK / 16; ++cb) {
+        f32x4 kl, kd;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int cc = 16 * cb + 4 * lg + e;
+          const float kv = (float)sm.k[r0 + lr][cc];
+          const float d = sm.G[r0 + lr][cc] - sm.G[r0 + 7][cc];
+          kl[e] = kv * fast_exp2(d);
+          kd[e] = kv * fast_exp2(-d);
+        }
+        At = M::k16(M::make(kl), M::make(kd), At);
+      }
       f32x4 part;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * lg + e;
         const float dA = lr < r ? -p[e] : 0.f;
         part[e] = lr < r ? dA * At[e] : 0.f;
-        const T x = (T)(sm.tf.beta[r] * dA);
-        sm.dAt[r][lr] = x;
-        sm.dAtT[lr][r] = x;
+        const T x = (T)(sm.beta[r0 + r] * dA);
+        sm.dAt[pb][r][lr] = x;
+        sm.dAtT[pb][lr][r] = x;
       }
 #pragma unroll
       for (int m = 1; m < 16; m <<= 1)
@@ -718,31 +760,28 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
         for (int e = 0; e < 4; ++e) part[e] += __shfl_xor(part[e], m, 64);
       if (lr == 0)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.dbA[4 * lg + e] = part[e];
+        for (int e = 0; e < 4; ++e) sm.dbA[pb][4 * lg + e] = part[e];
       // rowsum(dY * U), row lr
       float u = 0.f;
-      const bool ok = lr < L;
-      const long row = ((t0 + lr) * H + h) * (long)DV;
 #pragma unroll
       for (int kb = 0; kb < C::NVB; ++kb)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const frag uf =
-              ok ? load_frag(static_cast<const T*>(a.U) + row + 32 * kb + 16 * hf + 4 * lg) : fz;
-          const f32x4 u4 = M::to_f32(uf), y4 = M::to_f32(aY[kb][hf]);
+          const f32x4 u4 = M::to_f32(load_frag(&sm.U[r0 + lr][32 * kb + 16 * hf + 4 * lg]));
+          const f32x4 y4 = M::to_f32(aY[kb][hf]);
           u += u4[0] * y4[0] + u4[1] * y4[1] + u4[2] * y4[2] + u4[3] * y4[3];
         }
       u += __shfl_xor(u, 16, 64);
       u += __shfl_xor(u, 32, 64);
-      if (lg == 0) sm.dbU[lr] = u;
+      if (lg == 0) sm.dbU[pb][lr] = u;
     }
     __syncthreads();
 
     if ((int)threadIdx.x < L)
-      a.dbeta[(t0 + threadIdx.x) * H + h] = sm.dbA[threadIdx.x] + sm.dbU[threadIdx.x];
+      a.dbeta[(t0 + threadIdx.x) * H + h] = sm.dbA[pb][threadIdx.x] + sm.dbU[pb][threadIdx.x];
     // dV = beta dY, one 32-block of value positions per wavefront
     if (w < C::NVB && lr < L) {
-      const float bb = sm.tf.beta[lr];
+      const float bb = sm.beta[r0 + lr];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const f32x4 y4 = M::to_f32(aY[w][hf]);
@@ -751,24 +790,24 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
       }
     }
 
-    const float rho = sm.tf.G[7][c], GL = sm.tf.G[BT - 1][c];
+    const float rho = sm.G[r0 + 7][c], GL = sm.G[r0 + BT - 1][c];
     f32x4 gam, el, ed, et, qq, kk, bt;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int t = 4 * lg + e;
-      const float Gv = sm.tf.G[t][c];
+      const int t = r0 + 4 * lg + e;
+      const float Gv = sm.G[t][c];
       gam[e] = fast_exp2(Gv);
       el[e] = fast_exp2(Gv - rho);
       ed[e] = fast_exp2(rho - Gv);
       et[e] = fast_exp2(GL - Gv);
-      qq[e] = sc * sm.tf.q[t][c];
-      kk[e] = sm.tf.k[t][c];
-      bt[e] = sm.tf.beta[t];
+      qq[e] = sc * (float)sm.q[t][c];
+      kk[e] = (float)sm.k[t][c];
+      bt[e] = sm.beta[t];
     }
     const f32x4 Kd = kk * ed, Kl = kk * el, Ql = qq * el, Qg = qq * gam, Kg = kk * gam;
-    const f32x4 dQl = M::k16(load_frag(&sm.dAqk[lr][4 * lg]), M::make(Kd), z);
-    const f32x4 dKl = M::k16(load_frag(&sm.dAt[lr][4 * lg]), M::make(Kd), z);
-    const f32x4 dKd = M::k32(load_frag(&sm.dAqkT[lr][4 * lg]), load_frag(&sm.dAtT[lr][4 * lg]),
+    const f32x4 dQl = M::k16(load_frag(&sm.dAqk[pb][lr][4 * lg]), M::make(Kd), z);
+    const f32x4 dKl = M::k16(load_frag(&sm.dAt[pb][lr][4 * lg]), M::make(Kd), z);
+    const f32x4 dKd = M::k32(load_frag(&sm.dAqkT[pb][lr][4 * lg]), load_frag(&sm.dAtT[pb][lr][4 * lg]),
                              M::make(Ql), M::make(Kl), z);
     f32x4 dq, dk, dG;
     float tsum = 0.f;
@@ -815,10 +854,9 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
       const frag qf = M::make(Qg), kf = M::make_neg(Kg * bt);
 #pragma unroll
       for (int b = 0; b < NVT; ++b)
-        dSr[b] = M::k32(load_frag(&sm.dOT[16 * b + lr][4 * lg]), load_frag(&sm.dYT[16 * b + lr][4 * lg]),
-                        qf, kf, dSr[b] * gl);
+        dSr[b] = M::k32(acc_tile<T, SM::DVP>(sm.dO, r0, 16 * b, lr, lg),
+                        acc_tile<T, SM::DVP>(sm.dY, r0, 16 * b, lr, lg), qf, kf, dSr[b] * gl);
     }
-    __syncthreads();  // LDS reused by the next tile
   }
 }
 
