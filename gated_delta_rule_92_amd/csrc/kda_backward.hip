@@ -108,51 +108,94 @@ struct TileF32 {
   float beta[BT];
 };
 
-template <typename T, int DK, int NT = NTH>
-__device__ __forceinline__ void load_rows(float (*dst)[DK + 4], const T* src, long t0, int L, int h,
-                                          int H) {
-  constexpr int Q = DK / 4;
-  for (int idx = threadIdx.x; idx < BT * Q; idx += NT) {
-    const int r = idx / Q, c = (idx % Q) * 4;
-    f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if (r < L) x = load4_f32(src + ((t0 + r) * H + h) * (long)DK + c);
-    *reinterpret_cast<f32x4*>(&dst[r][c]) = x;
+// Four consecutive elements of T as loaded (converted only when stored), so
+// that a thread issues all of a tile's loads before it waits for any.
+template <typename T>
+struct Raw;
+template <>
+struct Raw<__bf16> {
+  uint2 w;
+  __device__ __forceinline__ void load(const __bf16* p) { w = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void zero() { w = make_uint2(0u, 0u); }
+  __device__ __forceinline__ f32x4 f32() const {
+    float x0, x1, x2, x3;
+    unpack_bf16x2(w.x, x0, x1);
+    unpack_bf16x2(w.y, x2, x3);
+    return f32x4{x0, x1, x2, x3};
   }
-}
-
-// Loads q (if wanted), k, the gate and beta of tokens [t0, t0+L), then forms G
-// (two barriers inside; the caller's LDS arrays are free on entry).
-// Also stages, before its first barrier, whatever `extra` loads (a callable
-// run by every thread), so that those loads overlap the tile's.
-struct NoExtra {
-  __device__ void operator()() const {}
+};
+template <>
+struct Raw<float> {
+  f32x4 w;
+  __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const f32x4*>(p); }
+  __device__ __forceinline__ void zero() { w = f32x4{0.f, 0.f, 0.f, 0.f}; }
+  __device__ __forceinline__ f32x4 f32() const { return w; }
 };
 
-template <typename T, int DK, int NT = NTH, typename Extra = NoExtra>
-__device__ void load_tile(TileF32<DK>& tf, const BwdArgs& a, long t0, int L, int h, bool want_q,
-                          const Extra& extra = Extra()) {
-  const int H = a.H;
-  if (want_q) load_rows<T, DK, NT>(tf.q, static_cast<const T*>(a.q), t0, L, h, H);
-  load_rows<T, DK, NT>(tf.k, static_cast<const T*>(a.k), t0, L, h, H);
-  load_rows<float, DK, NT>(tf.G, a.g, t0, L, h, H);
-  extra();
-  if (threadIdx.x < BT) tf.beta[threadIdx.x] = (int)threadIdx.x < L ? a.beta[(t0 + threadIdx.x) * H + h] : 0.f;
-  __syncthreads();
-  if (threadIdx.x < DK) {
-    const int c = threadIdx.x;
-    const float es = (a.gate == kGateLogits && a.A_log) ? __expf(a.A_log[h]) : 1.f;
+// ROWS rows [t0, t0 + rows) of a [Ttot, H, D] array (zeros past `rows`),
+// four elements per thread and step: load() issues every load into
+// registers, store() / store_t() write them to LDS row-major / transposed.
+template <typename T, int D, int ROWS, int NT>
+struct RowsIn {
+  static constexpr int Q = D / 4;
+  static constexpr int IT = (ROWS * Q + NT - 1) / NT;
+  Raw<T> x[IT];
+  __device__ __forceinline__ void load(const void* src, long t0, int rows, int h, int H) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int idx = threadIdx.x + i * NT, r = idx / Q, c = (idx % Q) * 4;
+      if (idx < ROWS * Q && r < rows)
+        x[i].load(static_cast<const T*>(src) + ((t0 + r) * H + h) * (long)D + c);
+      else
+        x[i].zero();
+    }
+  }
+  template <typename U, int LD>
+  __device__ __forceinline__ void store(U (*dst)[LD]) const {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int idx = threadIdx.x + i * NT, r = idx / Q, c = (idx % Q) * 4;
+      if (idx < ROWS * Q) store4(&dst[r][c], x[i].f32());
+    }
+  }
+  template <typename U, int LD>
+  __device__ __forceinline__ void store_t(U (*dst)[LD]) const {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int idx = threadIdx.x + i * NT, r = idx / Q, c = (idx % Q) * 4;
+      if (idx < ROWS * Q) {
+        const f32x4 v = x[i].f32();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[c + e][r] = (U)v[e];
+      }
+    }
+  }
+};
+
+// The gate input of one channel over a 16-token tile, held by one thread:
+// load() issues the 16 loads, store() applies the gate if the input is
+// logits and writes the inclusive sum (log2 units) to G[row0 .. row0+15][c].
+template <int DK>
+struct GateIn {
+  float g[BT];
+  __device__ __forceinline__ void load(const BwdArgs& a, long t0, int L, int h, int c) {
+#pragma unroll
+    for (int r = 0; r < BT; ++r) g[r] = r < L ? a.g[((t0 + r) * a.H + h) * (long)DK + c] : 0.f;
+  }
+  __device__ __forceinline__ void store(float (*G)[DK + 4], const BwdArgs& a, int L, int h, int c,
+                                        int row0) const {
+    const bool logits = a.gate == kGateLogits;
+    const float es = (logits && a.A_log) ? __expf(a.A_log[h]) : 1.f;
     float run = 0.f;
 #pragma unroll
     for (int r = 0; r < BT; ++r) {
-      float gv = tf.G[r][c];
-      if (a.gate == kGateLogits && r < L)
-        gv = a.g_min * __builtin_amdgcn_rcpf(1.f + fast_exp2(-kLog2e * es * gv));
+      float gv = g[r];
+      if (logits && r < L) gv = a.g_min * __builtin_amdgcn_rcpf(1.f + fast_exp2(-kLog2e * es * gv));
       run += gv;
-      tf.G[r][c] = run * kLog2e;
+      G[row0 + r][c] = run * kLog2e;
     }
   }
-  __syncthreads();
-}
+};
 
 // ------------------------------------------------------------ tile inverse --
 // Orders one wavefront's LDS accesses across its lanes: waits for the
@@ -260,6 +303,21 @@ __global__ void __launch_bounds__(NTH) bwd_fwd_scan(BwdArgs a) {
     }
 
   const int nt = (un.len + BT - 1) / BT;
+  // inputs of the next tile, loaded while the current one computes
+  RowsIn<T, DK, BT, NTH> in_k;
+  RowsIn<T, DV, BT, NTH> in_v;
+  GateIn<DK> in_g;
+  float in_b = 0.f;
+  const int tid = threadIdx.x;
+  auto issue = [&](int jj) {
+    const long tt = un.t0 + (long)jj * BT;
+    const int LL = min(BT, un.len - jj * BT);
+    in_k.load(a.k, tt, LL, h, H);
+    in_v.load(a.v, tt, LL, h, H);
+    if (tid < DK) in_g.load(a, tt, LL, h, tid);
+    if (tid < BT) in_b = tid < LL ? a.beta[(tt + tid) * H + h] : 0.f;
+  };
+  if (nt > 0) issue(0);
   for (int j = 0; j < nt; ++j) {
     const long t0 = un.t0 + (long)j * BT;
     const int L = min(BT, un.len - j * BT);
@@ -277,8 +335,12 @@ __global__ void __launch_bounds__(NTH) bwd_fwd_scan(BwdArgs a) {
         }
     }
 
-    load_tile<T, DK>(sm.tf, a, t0, L, h, false);
-    load_rows<T, DV>(sm.v, static_cast<const T*>(a.v), t0, L, h, H);
+    in_k.store(sm.tf.k);
+    in_v.store(sm.v);
+    if (tid < DK) in_g.store(sm.tf.G, a, L, h, tid, 0);
+    if (tid < BT) sm.tf.beta[tid] = in_b;
+    __syncthreads();
+    if (j + 1 < nt) issue(j + 1);
     for (int idx = threadIdx.x; idx < BT * DK; idx += NTH) {
       const int r = idx / DK, c = idx % DK;
       const float G = sm.tf.G[r][c], kk = sm.tf.k[r][c];
@@ -396,6 +458,22 @@ __global__ void __launch_bounds__(NTH) bwd_rev_scan(BwdArgs a) {
     }
 
   const int nt = (un.len + BT - 1) / BT;
+  // inputs of the next tile (backwards), loaded while the current one computes
+  RowsIn<T, DK, BT, NTH> in_q, in_k;
+  RowsIn<T, DV, BT, NTH> in_o;
+  GateIn<DK> in_g;
+  float in_b = 0.f;
+  const int tid = threadIdx.x;
+  auto issue = [&](int jj) {
+    const long tt = un.t0 + (long)jj * BT;
+    const int LL = min(BT, un.len - jj * BT);
+    in_q.load(a.q, tt, LL, h, H);
+    in_k.load(a.k, tt, LL, h, H);
+    in_o.load(a.dO, tt, LL, h, H);
+    if (tid < DK) in_g.load(a, tt, LL, h, tid);
+    if (tid < BT) in_b = tid < LL ? a.beta[(tt + tid) * H + h] : 0.f;
+  };
+  if (nt > 0) issue(nt - 1);
   for (int j = nt - 1; j >= 0; --j) {
     const long t0 = un.t0 + (long)j * BT;
     const int L = min(BT, un.len - j * BT);
@@ -413,18 +491,13 @@ __global__ void __launch_bounds__(NTH) bwd_rev_scan(BwdArgs a) {
         }
     }
 
-    load_tile<T, DK>(sm.tf, a, t0, L, h, true);
-    {
-      constexpr int Q = DV / 4;
-      const T* dO = static_cast<const T*>(a.dO);
-      for (int idx = threadIdx.x; idx < BT * Q; idx += NTH) {
-        const int r = idx / Q, c = (idx % Q) * 4;
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        if (r < L) x = load4_f32(dO + ((t0 + r) * H + h) * (long)DV + c);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sm.dOT[c + e][r] = (T)x[e];
-      }
-    }
+    in_q.store(sm.tf.q);
+    in_k.store(sm.tf.k);
+    in_o.store_t(sm.dOT);
+    if (tid < DK) in_g.store(sm.tf.G, a, L, h, tid, 0);
+    if (tid < BT) sm.tf.beta[tid] = in_b;
+    __syncthreads();
+    if (j > 0) issue(j - 1);
     for (int idx = threadIdx.x; idx < BT * DK; idx += NTH) {
       const int r = idx / DK, c = idx % DK;
       const float G = sm.tf.G[r][c], kk = sm.tf.k[r][c], qq = sc * sm.tf.q[r][c];
@@ -547,20 +620,6 @@ struct GradSmem {
   float dbU[2][BT];
 };
 
-// Rows [t0, t0 + rows) of a [Ttot, H, D] array into dst[CT][ld] (zeros past
-// the end), four elements per thread and step.
-template <typename T, int D, int LD, int CT, int NT>
-__device__ __forceinline__ void stage_rows(T (*dst)[LD], const void* src, long t0, int rows, int h,
-                                           int H) {
-  constexpr int Q = D / 4;
-  for (int idx = threadIdx.x; idx < CT * Q; idx += NT) {
-    const int r = idx / Q, c = (idx % Q) * 4;
-    f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if (r < rows) x = load4_f32(static_cast<const T*>(src) + ((t0 + r) * H + h) * (long)D + c);
-    store4(&dst[r][c], x);
-  }
-}
-
 // Accumulator-layout tile of a row-major LDS array: element e of lane l is
 // X[r0 + 4*(l/16) + e][c0 + l%16].
 template <typename T, int LD>
@@ -622,32 +681,30 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
     dSr[b] = load4_f32(static_cast<const T*>(a.ckdS) + ck + 16 * b + 4 * lg);
   }
 
-  // stage the chunk
-  stage_rows<T, DK, C::DKP, CT, NT>(sm.q, a.q, ct0, CL, h, H);
-  stage_rows<T, DK, C::DKP, CT, NT>(sm.k, a.k, ct0, CL, h, H);
-  stage_rows<T, DV, SM::DVP, CT, NT>(sm.dO, a.dO, ct0, CL, h, H);
-  stage_rows<T, DV, SM::DVP, CT, NT>(sm.dY, a.dY, ct0, CL, h, H);
-  stage_rows<T, DV, SM::DVP, CT, NT>(sm.Vt, a.Vt, ct0, CL, h, H);
-  stage_rows<T, DV, SM::DVP, CT, NT>(sm.U, a.U, ct0, CL, h, H);
-  if ((int)threadIdx.x < CT) {
-    const int r = threadIdx.x;
-    sm.beta[r] = r < CL ? a.beta[(ct0 + r) * H + h] : 0.f;
-  }
-  if ((int)threadIdx.x < CKT * DK) {
-    const int sb = threadIdx.x / DK, cc = threadIdx.x % DK;
-    const float es = (a.gate == kGateLogits && a.A_log) ? __expf(a.A_log[h]) : 1.f;
-    float run = 0.f;
-#pragma unroll
-    for (int r = 0; r < BT; ++r) {
-      const int t = BT * sb + r;
-      float gv = 0.f;
-      if (t < CL) {
-        gv = a.g[((ct0 + t) * H + h) * (long)DK + cc];
-        if (a.gate == kGateLogits) gv = a.g_min * __builtin_amdgcn_rcpf(1.f + fast_exp2(-kLog2e * es * gv));
-      }
-      run += gv;
-      sm.G[t][cc] = run * kLog2e;
-    }
+  // stage the chunk: every load issued first, then the LDS writes
+  {
+    RowsIn<T, DK, CT, NT> in_q, in_k;
+    RowsIn<T, DV, CT, NT> in_o, in_y, in_v, in_u;
+    GateIn<DK> in_g;
+    const int tid = threadIdx.x;
+    const int sb = tid / DK, cc = tid % DK;
+    const int Lsb = min(BT, CL - BT * sb);
+    in_q.load(a.q, ct0, CL, h, H);
+    in_k.load(a.k, ct0, CL, h, H);
+    in_o.load(a.dO, ct0, CL, h, H);
+    in_y.load(a.dY, ct0, CL, h, H);
+    in_v.load(a.Vt, ct0, CL, h, H);
+    in_u.load(a.U, ct0, CL, h, H);
+    if (tid < CKT * DK) in_g.load(a, ct0 + BT * sb, Lsb, h, cc);
+    const float bv = tid < CL ? a.beta[(ct0 + tid) * H + h] : 0.f;
+    in_q.store(sm.q);
+    in_k.store(sm.k);
+    in_o.store(sm.dO);
+    in_y.store(sm.dY);
+    in_v.store(sm.Vt);
+    in_u.store(sm.U);
+    if (tid < CKT * DK) in_g.store(sm.G, a, Lsb, h, cc, BT * sb);
+    if (tid < CT) sm.beta[tid] = bv;
   }
   __syncthreads();
 
