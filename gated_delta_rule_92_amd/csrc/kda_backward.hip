@@ -39,6 +39,8 @@
 // In the scans wavefront w owns value columns [w*Dv/4, (w+1)*Dv/4) of the
 // state, which the recurrence never mixes; in tile_grad it owns channel
 // tiles w, w+4, ...
+#include <type_traits>
+
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -616,8 +618,8 @@ struct GradSmem {
   T dAqkT[2][BT][C::TSP];      // its transpose
   T dAt[2][BT][C::TSP];        // beta_r dAkk[r, i] (gradient of A~ = Akk / beta)
   T dAtT[2][BT][C::TSP];
-  float dbA[2][BT];
-  float dbU[2][BT];
+  float dbA[2][DK / 16][BT];   // per-wavefront partial sums of dbeta
+  float dbU[2][DV / 32][BT];
 };
 
 // Accumulator-layout tile of a row-major LDS array: element e of lane l is
@@ -770,6 +772,55 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) dKg[e] *= -sm.beta[r0 + 4 * lg + e];
 
+    // dAkk = -StrictTril(dY V~^T) (every wavefront); its dbeta term
+    // sum_i dAkk[r,i] A~[r,i] with A~ = Kl Kd^T split over the wavefronts'
+    // channel blocks; rowsum(dY * U) split over 32-blocks of values.
+    {
+      f32x4 p = z;
+#pragma unroll
+      for (int kb = 0; kb < C::NVB; ++kb) p = M::k32(aY[kb][0], aY[kb][1], aV[kb][0], aV[kb][1], p);
+      f32x4 kl, kd;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int cc = 16 * w + 4 * lg + e;
+        const float kv = (float)sm.k[r0 + lr][cc];
+        const float d = sm.G[r0 + lr][cc] - sm.G[r0 + 7][cc];
+        kl[e] = kv * fast_exp2(d);
+        kd[e] = kv * fast_exp2(-d);
+      }
+      const f32x4 At = M::k16(M::make(kl), M::make(kd), z);
+      f32x4 part;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * lg + e;
+        const float dA = lr < r ? -p[e] : 0.f;
+        part[e] = dA * At[e];
+        if (w == 1) {
+          const T x = (T)(sm.beta[r0 + r] * dA);
+          sm.dAt[pb][r][lr] = x;
+          sm.dAtT[pb][lr][r] = x;
+        }
+      }
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part[e] += __shfl_xor(part[e], m, 64);
+      if (lr == 0)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.dbA[pb][w][4 * lg + e] = part[e];
+      if (w < C::NVB) {
+        float u = 0.f;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const f32x4 u4 = M::to_f32(load_frag(&sm.U[r0 + lr][32 * w + 16 * hf + 4 * lg]));
+          const f32x4 y4 = M::to_f32(aY[w][hf]);
+          u += u4[0] * y4[0] + u4[1] * y4[1] + u4[2] * y4[2] + u4[3] * y4[3];
+        }
+        u += __shfl_xor(u, 16, 64);
+        u += __shfl_xor(u, 32, 64);
+        if (lg == 0) sm.dbU[pb][w][lr] = u;
+      }
+    }
     if (w == 0) {
       // dAqk = Tril(dO V~^T)
       f32x4 p = z;
@@ -782,60 +833,17 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
         sm.dAqk[pb][r][lr] = x;
         sm.dAqkT[pb][lr][r] = x;
       }
-    } else if (w == 1) {
-      // dAkk = -StrictTril(dY V~^T); A~ = Kl Kd^T over all channels; dbeta
-      f32x4 p = z;
-#pragma unroll
-      for (int kb = 0; kb < C::NVB; ++kb) p = M::k32(aY[kb][0], aY[kb][1], aV[kb][0], aV[kb][1], p);
-      f32x4 At = z;
-#pragma unroll
-      for (int cb = 0; cb < DK / 16; ++cb) {
-        f32x4 kl, kd;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int cc = 16 * cb + 4 * lg + e;
-          const float kv = (float)sm.k[r0 + lr][cc];
-          const float d = sm.G[r0 + lr][cc] - sm.G[r0 + 7][cc];
-          kl[e] = kv * fast_exp2(d);
-          kd[e] = kv * fast_exp2(-d);
-        }
-        At = M::k16(M::make(kl), M::make(kd), At);
-      }
-      f32x4 part;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * lg + e;
-        const float dA = lr < r ? -p[e] : 0.f;
-        part[e] = lr < r ? dA * At[e] : 0.f;
-        const T x = (T)(sm.beta[r0 + r] * dA);
-        sm.dAt[pb][r][lr] = x;
-        sm.dAtT[pb][lr][r] = x;
-      }
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) part[e] += __shfl_xor(part[e], m, 64);
-      if (lr == 0)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sm.dbA[pb][4 * lg + e] = part[e];
-      // rowsum(dY * U), row lr
-      float u = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < C::NVB; ++kb)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const f32x4 u4 = M::to_f32(load_frag(&sm.U[r0 + lr][32 * kb + 16 * hf + 4 * lg]));
-          const f32x4 y4 = M::to_f32(aY[kb][hf]);
-          u += u4[0] * y4[0] + u4[1] * y4[1] + u4[2] * y4[2] + u4[3] * y4[3];
-        }
-      u += __shfl_xor(u, 16, 64);
-      u += __shfl_xor(u, 32, 64);
-      if (lg == 0) sm.dbU[pb][lr] = u;
     }
     __syncthreads();
 
-    if ((int)threadIdx.x < L)
-      a.dbeta[(t0 + threadIdx.x) * H + h] = sm.dbA[pb][threadIdx.x] + sm.dbU[pb][threadIdx.x];
+    if ((int)threadIdx.x < L) {
+      float db = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) db += sm.dbA[pb][ww][threadIdx.x];
+#pragma unroll
+      for (int ww = 0; ww < C::NVB; ++ww) db += sm.dbU[pb][ww][threadIdx.x];
+      a.dbeta[(t0 + threadIdx.x) * H + h] = db;
+    }
     // dV = beta dY, one 32-block of value positions per wavefront
     if (w < C::NVB && lr < L) {
       const float bb = sm.beta[r0 + lr];
@@ -920,7 +928,22 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
 template <typename T, int DK, int DV>
 hipError_t launch_bwd_t(const BwdArgs& a, long slots, hipStream_t stream) {
   const unsigned units = (unsigned)(a.N * a.H);
-  hipLaunchKernelGGL((bwd_fwd_scan<T, DK, DV>), dim3(units), dim3(NTH), 0, stream, a);
+  if (std::is_same<T, __bf16>::value && chunk_pipe_supported(true, DK, DV, 64)) {
+    // the pipelined forward kernel in checkpoint mode writes the same
+    // checkpoints, U and V~ as bwd_fwd_scan
+    ChunkArgs c;
+    c.q = nullptr; c.k = a.k; c.v = a.v; c.g = a.g; c.gate_mode = a.gate;
+    c.A_log = a.A_log; c.g_min = a.g_min; c.beta = a.beta;
+    c.h0 = a.h0; c.hT = nullptr; c.o = nullptr;
+    c.seqs.cu = a.cu; c.seqs.N = a.N; c.seqs.T = a.T; c.seqs.Ttot = 0;
+    c.order = nullptr;
+    c.H = a.H; c.Dk = DK; c.Dv = DV; c.scale = a.scale; c.bf16 = true;
+    c.ck_state = a.ckS; c.ck_u = a.U; c.ck_vt = a.Vt;
+    hipError_t e = launch_chunk_checkpoint(c, stream);
+    if (e != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL((bwd_fwd_scan<T, DK, DV>), dim3(units), dim3(NTH), 0, stream, a);
+  }
   hipLaunchKernelGGL((bwd_rev_scan<T, DK, DV>), dim3(units), dim3(NTH), 0, stream, a);
   if (slots > 0)
     hipLaunchKernelGGL((bwd_tile_grad<T, DK, DV>), dim3((unsigned)slots, (unsigned)a.H),

@@ -127,7 +127,17 @@ __device__ __forceinline__ uint32_t perm_hi16(uint32_t a, uint32_t b) {
 //   kModeForwardGated: o replaced by the block's output epilogue
 //     sigmoid(a.og) * RMSNorm(o) * a.onw, with the mean square over each
 //     token-head's d_v outputs taken in fp32 before rounding.
-enum { kModeForward = 0, kModeStateOnly = 1, kModeTransition = 2, kModeForwardGated = 3 };
+//   kModeCheckpoint: no output and no final state; the state entering every
+//     fourth tile (every 64 tokens) is written in bf16, and per token
+//     U = V - (e^G K) S and the pseudo-values V~ (what the backward pass
+//     reads).
+enum {
+  kModeForward = 0,
+  kModeStateOnly = 1,
+  kModeTransition = 2,
+  kModeForwardGated = 3,
+  kModeCheckpoint = 4
+};
 
 template <int GATE, int MODE>
 __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
@@ -139,6 +149,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
   constexpr bool PAIR = GATE == kGateSoftplus;
   constexpr bool GATED = MODE == kModeForwardGated;
   constexpr bool NEEDQ = MODE == kModeForward || GATED;
+  constexpr bool CKPT = MODE == kModeCheckpoint;
   using M = Mma<__bf16>;
   using frag = M::frag;
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
@@ -571,6 +582,21 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
     const bool odd = m & 1;
     const uint32_t psel = odd ? 0x03020706u : 0x05040100u;
     const int ovoff2 = (4 * g4 + (odd ? 1 : 0)) * rowo + (vc0 + (m & ~1)) * 2;
+    // two bf16 columns of one row per lane (rows 4g4 + 0..3 of a tile whose
+    // rows are rowb bytes apart): even lanes rows 0 and 2, odd lanes 1 and 3
+    auto store_pairs = [&](const f32x4& v, __amdgpu_buffer_rsrc_t rs, int voff, int rowb, int soff) {
+      const uint32_t p01 = pack_bf16x2(v[0], v[1]), p23 = pack_bf16x2(v[2], v[3]);
+      const uint32_t q01 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p01, 0xB1, 0xF, 0xF, false);
+      const uint32_t q23 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p23, 0xB1, 0xF, 0xF, false);
+      __builtin_amdgcn_raw_buffer_store_b32((int)__builtin_amdgcn_perm(q01, p01, psel), rs, voff, soff, 0);
+      __builtin_amdgcn_raw_buffer_store_b32((int)__builtin_amdgcn_perm(q23, p23, psel), rs, voff,
+                                            soff + 2 * rowb, 0);
+    };
+    // checkpoint mode: first 64-token slot of this sequence
+    long ckbase = 0;
+    if constexpr (CKPT)
+      ckbase = a.seqs.cu ? (long)(a.seqs.cu[n] / 64) + n : (long)n * ((a.seqs.T + 63) / 64);
+    const int ckvoff = (4 * g4 + (odd ? 1 : 0)) * (PDV * 2) + (vc0 + (m & ~1)) * 2;
     // gated epilogue: this lane's norm weights (columns vc0 + 16b + m) and the
     // gate logits of its rows 4g4+e, loaded one tile ahead
     float nw[CNTV];
@@ -640,6 +666,17 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
       // bf16 copy of S for this tile's products, then the tile's decay of S
       // in place (independent of the products, so it overlaps them)
       frag Sf[NCT][CNTV];
+      if constexpr (CKPT) {
+        if (step % 4 == 0) {
+          const __amdgpu_buffer_rsrc_t rsc = make_rsrc(
+              static_cast<__bf16*>(a.ck_state) + ((size_t)(ckbase + step / 4) * H + h) * PDK * PDV,
+              PDK * PDV * 2);
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int b = 0; b < CNTV; ++b) store_pairs(S[ct][b], rsc, ckvoff, PDV * 2, (16 * ct * PDV + 16 * b) * 2);
+        }
+      }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -661,7 +698,17 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
 #pragma unroll
       for (int b = 0; b < CNTV; ++b) {
         const f32x4 y = (vv[b] - acc[b]) * bb;
-        Xf[b] = M::make(M::k16(tf, M::make(y), f32x4{0.f, 0.f, 0.f, 0.f}));
+        const f32x4 x = M::k16(tf, M::make(y), f32x4{0.f, 0.f, 0.f, 0.f});
+        Xf[b] = M::make(x);
+        if constexpr (CKPT) {
+          const uint32_t rows = (uint32_t)((L - 1) * H + 1) * PDV * 2;
+          const __amdgpu_buffer_rsrc_t rsu =
+              make_rsrc(static_cast<__bf16*>(a.ck_u) + ((size_t)t0 * H + h) * PDV, rows);
+          const __amdgpu_buffer_rsrc_t rsv =
+              make_rsrc(static_cast<__bf16*>(a.ck_vt) + ((size_t)t0 * H + h) * PDV, rows);
+          store_pairs(vv[b] - acc[b], rsu, ovoff2, rowo, 32 * b);
+          store_pairs(x, rsv, ovoff2, rowo, 32 * b);
+        }
       }
       // O = A_qk V~ + (e^G Q) S
       if (want_o) {
@@ -788,6 +835,12 @@ hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t stream) {
     launch_pipe_t<kModeForward>(a, stream);
   else
     launch_pipe_t<kModeStateOnly>(a, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_checkpoint(const ChunkArgs& a, hipStream_t stream) {
+  if (a.seqs.N == 0 || a.H == 0) return hipSuccess;
+  launch_pipe_t<kModeCheckpoint>(a, stream);
   return hipGetLastError();
 }
 

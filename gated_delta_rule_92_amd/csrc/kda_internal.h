@@ -67,6 +67,13 @@ struct ChunkArgs {
   const void* og = nullptr;
   const float* onw = nullptr;
   float oeps = 0.f;
+  // checkpoint mode (pipelined kernel, for the backward pass): the state
+  // entering every 64-token chunk, bf16 [slots, H, Dk, Dv] with chunk c of
+  // sequence n at slot floor(cu[n] / 64) + n + c (packed) or n ceil(T/64) + c;
+  // U = V - (e^G K) S and V~ per token, bf16 [Ttot, H, Dv]
+  void* ck_state = nullptr;
+  void* ck_u = nullptr;
+  void* ck_vt = nullptr;
 };
 bool chunk_fused_supported(bool bf16, int Dk, int Dv, int chunk);
 // Pipelined producer/consumer chunk kernel (bf16, Dk = Dv = 128).
@@ -75,6 +82,8 @@ hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t stream);
 // Same kernel in transition mode: writes M (a.hT, [N, H, Dk, Dk]) with
 // S_final = M S_initial + S_final(0); reads k, g and beta only.
 hipError_t launch_chunk_transition(const ChunkArgs& a, hipStream_t stream);
+// Same kernel in checkpoint mode (ck_state, ck_u, ck_vt must be set).
+hipError_t launch_chunk_checkpoint(const ChunkArgs& a, hipStream_t stream);
 // Output epilogue y = sigmoid(z) * o / sqrt(mean(o^2) + eps) * w over rows of
 // Dv (<= 512) elements; y may alias o.
 hipError_t launch_gated_rmsnorm(const void* o, const void* z, bool bf16, const float* w, float eps,
