@@ -710,35 +710,37 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
   }
   __syncthreads();
 
-  // states entering the inner tiles: S_{j+1} = Diag(Gamma_L) S_j + Kt^T V~
-  frag Sf[CKT][NVT];
-#pragma unroll
-  for (int b = 0; b < NVT; ++b) Sf[0][b] = M::make(Sr[b]);
-#pragma unroll
-  for (int j = 0; j + 1 < CKT; ++j) {
-    if (j + 1 >= nsub) break;
-    const float GL = sm.G[BT * j + BT - 1][c], gl = fast_exp2(GL);
-    f32x4 Kt;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = BT * j + 4 * lg + e;
-      Kt[e] = (float)sm.k[t][c] * fast_exp2(GL - sm.G[t][c]);
-    }
-    const frag ktf = M::make(Kt);
-#pragma unroll
-    for (int b = 0; b < NVT; ++b) {
-      Sr[b] = M::k16(acc_tile<T, SM::DVP>(sm.Vt, BT * j, 16 * b, lr, lg), ktf, Sr[b] * gl);
-      Sf[j + 1][b] = M::make(Sr[b]);
-    }
-  }
-
-#pragma unroll
-  for (int j = CKT - 1; j >= 0; --j) {
-    if (j >= nsub) continue;
+  // Tiles are walked backwards in a rolled loop (the unrolled body would not
+  // fit the instruction cache); the state entering tile j is rebuilt from
+  // the chunk's checkpoint each time: S_{i+1} = Diag(Gamma_L) S_i + Kt^T V~.
+#pragma unroll 1
+  for (int j = nsub - 1; j >= 0; --j) {
     const int pb = j & 1;
     const int r0 = BT * j;
     const long t0 = ct0 + r0;
     const int L = min(BT, CL - r0);
+    frag Sf[NVT];
+    {
+      f32x4 Sj[NVT];
+#pragma unroll
+      for (int b = 0; b < NVT; ++b) Sj[b] = Sr[b];
+#pragma unroll 1
+      for (int i = 0; i < j; ++i) {
+        const float GL = sm.G[BT * i + BT - 1][c], gl = fast_exp2(GL);
+        f32x4 Kt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = BT * i + 4 * lg + e;
+          Kt[e] = (float)sm.k[t][c] * fast_exp2(GL - sm.G[t][c]);
+        }
+        const frag ktf = M::make(Kt);
+#pragma unroll
+        for (int b = 0; b < NVT; ++b)
+          Sj[b] = M::k16(acc_tile<T, SM::DVP>(sm.Vt, BT * i, 16 * b, lr, lg), ktf, Sj[b] * gl);
+      }
+#pragma unroll
+      for (int b = 0; b < NVT; ++b) Sf[b] = M::make(Sj[b]);
+    }
     // row fragments of dO, dY, V~ (row lr, value positions of the 32-blocks)
     frag aO[C::NVB][2], aY[C::NVB][2], aV[C::NVB][2];
 #pragma unroll
@@ -758,13 +760,13 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < C::NVB; ++kb) {
       const frag d0 = M::make(dSr[2 * kb]), d1 = M::make(dSr[2 * kb + 1]);
-      dQg = M::k32(aO[kb][0], aO[kb][1], Sf[j][2 * kb], Sf[j][2 * kb + 1], dQg);
-      dKg = M::k32(aY[kb][0], aY[kb][1], Sf[j][2 * kb], Sf[j][2 * kb + 1], dKg);
+      dQg = M::k32(aO[kb][0], aO[kb][1], Sf[2 * kb], Sf[2 * kb + 1], dQg);
+      dKg = M::k32(aY[kb][0], aY[kb][1], Sf[2 * kb], Sf[2 * kb + 1], dKg);
       dKt = M::k32(aV[kb][0], aV[kb][1], d0, d1, dKt);
     }
 #pragma unroll
     for (int b = 0; b < NVT; ++b) {
-      const f32x4 s4 = M::to_f32(Sf[j][b]);
+      const f32x4 s4 = M::to_f32(Sf[b]);
       gsum += s4[0] * dSr[b][0] + s4[1] * dSr[b][1] + s4[2] * dSr[b][2] + s4[3] * dSr[b][3];
     }
     gsum += __shfl_xor(gsum, 16, 64);
