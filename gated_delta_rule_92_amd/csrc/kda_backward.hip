@@ -946,7 +946,21 @@ hipError_t launch_bwd_t(const BwdArgs& a, long slots, hipStream_t stream) {
   } else {
     hipLaunchKernelGGL((bwd_fwd_scan<T, DK, DV>), dim3(units), dim3(NTH), 0, stream, a);
   }
-  hipLaunchKernelGGL((bwd_rev_scan<T, DK, DV>), dim3(units), dim3(NTH), 0, stream, a);
+  if (std::is_same<T, __bf16>::value && chunk_pipe_supported(true, DK, DV, 64)) {
+    // the pipelined kernel in reverse mode: same checkpoints, dY and dS_0
+    ChunkArgs c;
+    c.q = a.q; c.k = a.k; c.v = a.dO; c.g = a.g; c.gate_mode = a.gate;
+    c.A_log = a.A_log; c.g_min = a.g_min; c.beta = a.beta;
+    c.h0 = a.dhT; c.hT = a.dh0; c.o = nullptr;
+    c.seqs.cu = a.cu; c.seqs.N = a.N; c.seqs.T = a.T; c.seqs.Ttot = 0;
+    c.order = nullptr;
+    c.H = a.H; c.Dk = DK; c.Dv = DV; c.scale = a.scale; c.bf16 = true;
+    c.ck_state = a.ckdS; c.ck_vt = a.dY;
+    hipError_t e = launch_chunk_reverse(c, stream);
+    if (e != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL((bwd_rev_scan<T, DK, DV>), dim3(units), dim3(NTH), 0, stream, a);
+  }
   if (slots > 0)
     hipLaunchKernelGGL((bwd_tile_grad<T, DK, DV>), dim3((unsigned)slots, (unsigned)a.H),
                        dim3(64 * (DK / 16)), 0, stream, a);

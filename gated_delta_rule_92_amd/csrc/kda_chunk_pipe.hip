@@ -61,9 +61,12 @@ constexpr int kSpinLimit = 1 << 15;
 constexpr int RS = PDK + 8;  // token-major [16][128] bf16 arrays
 constexpr int TS = PT + 8;   // token-contiguous [*][16] bf16 arrays
 // Slot layout (bytes). bf16 unless noted.
+// (reverse mode: sKg holds k e^{G15-G} row-major, sQg (k e^{G})^T, sKtT
+// (q e^{G})^T, sVT dO^T, sT T^T and sAqk A_qk^T)
 constexpr int sKg = 0;                      // k e^{G}      [16][RS]
-constexpr int sQg = sKg + PT * RS * 2;      // q e^{G}      [16][RS]
-constexpr int sKtT = sQg + PT * RS * 2;     // k e^{G15-G}  [128][TS] (channel-major)
+constexpr int sQg = sKg + PT * RS * 2;      // q e^{G}      [16][RS], or [128][TS]
+constexpr int kQgBytes = PT * RS * 2 > PDK * TS * 2 ? PT * RS * 2 : PDK * TS * 2;
+constexpr int sKtT = sQg + kQgBytes;        // k e^{G15-G}  [128][TS] (channel-major)
 constexpr int sVT = sKtT + PDK * TS * 2;    // v            [128][TS] (channel-major)
 constexpr int sT = sVT + PDV * TS * 2;      // (I+A_kk)^-1  [16][TS]
 constexpr int sAqk = sT + PT * TS * 2;      // A_qk         [16][TS]
@@ -131,12 +134,20 @@ __device__ __forceinline__ uint32_t perm_hi16(uint32_t a, uint32_t b) {
 //     fourth tile (every 64 tokens) is written in bf16, and per token
 //     U = V - (e^G K) S and the pseudo-values V~ (what the backward pass
 //     reads).
+//   kModeReverse: the backward's state-gradient recurrence, tiles taken last
+//     to first (a.v holds dO, a.h0 the final-state gradient, a.hT receives
+//     the initial-state gradient):
+//       dV~ = Kt dS' + A_qk^T dO,  dY = T^T dV~,
+//       dS = Diag(e^{G_15}) dS' + (e^G Q)^T dO - (e^G K)^T (beta dY);
+//     writes dY per token (a.ck_vt) and, in bf16, the state gradient leaving
+//     the last tile of every 64-token chunk (a.ck_state).
 enum {
   kModeForward = 0,
   kModeStateOnly = 1,
   kModeTransition = 2,
   kModeForwardGated = 3,
-  kModeCheckpoint = 4
+  kModeCheckpoint = 4,
+  kModeReverse = 5
 };
 
 template <int GATE, int MODE>
@@ -150,6 +161,8 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
   constexpr bool GATED = MODE == kModeForwardGated;
   constexpr bool NEEDQ = MODE == kModeForward || GATED;
   constexpr bool CKPT = MODE == kModeCheckpoint;
+  constexpr bool REV = MODE == kModeReverse;
+  constexpr bool LOADQ = NEEDQ || REV;
   using M = Mma<__bf16>;
   using frag = M::frag;
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
@@ -180,6 +193,8 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
   }
   const int nsteps = (int)((len + PT - 1) / PT);
   const int rowk = H * PDK * 2, rowg = H * PDK * 4, rowb = H * 4;
+  // tile handled at a step: in order, or last to first in reverse mode
+  auto tile_of = [&](int step) { return REV ? nsteps - 1 - step : step; };
 
   if (tid < 3 * NSLOT + 1) ready[tid] = 0;  // ready[], done[], abort_flag, nrm_ready[] are contiguous
   __syncthreads();
@@ -204,8 +219,9 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
     f32x4 rz[8];
     float rb;  // beta of row `lane` (lanes 0..15)
     auto load_tile = [&](int step) {
-      const long t0 = bos + (long)step * PT;
-      const int L = (int)min((long)PT, len - (long)step * PT);
+      const int tile = tile_of(step);
+      const long t0 = bos + (long)tile * PT;
+      const int L = (int)min((long)PT, len - (long)tile * PT);
       const size_t base = ((size_t)t0 * H + h);
       const uint32_t nrow = (uint32_t)((L - 1) * H + 1);
       const __amdgpu_buffer_rsrc_t rsk = make_rsrc(k + base * PDK, nrow * PDK * 2);
@@ -217,7 +233,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         rk[r] = __builtin_amdgcn_raw_buffer_load_b64(rsk, vk, r * rowk, 0);
-        if constexpr (NEEDQ) rq[r] = __builtin_amdgcn_raw_buffer_load_b64(rsq, vk, r * rowk, 0);
+        if constexpr (LOADQ) rq[r] = __builtin_amdgcn_raw_buffer_load_b64(rsq, vk, r * rowk, 0);
         if constexpr (!TRANS) rv[r] = __builtin_amdgcn_raw_buffer_load_b64(rsv, vk, r * rowk, 0);
         if constexpr (GATE == kGateCumsum) {
           // cumulative-sum input: rows past the end repeat the last row, so
@@ -236,8 +252,9 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
       const int slot = step % NSLOT;
       const int use = step / NSLOT;
       char* sl = smem + slot * kSlotBytes;
-      const long t0 = bos + (long)step * PT;
-      const int L = (int)min((long)PT, len - (long)step * PT);
+      const int tile = tile_of(step);
+      const long t0 = bos + (long)tile * PT;
+      const int L = (int)min((long)PT, len - (long)tile * PT);
       // the slot's previous tile must have been consumed by every consumer
       if (use > 0) wait_at_least(&done[slot], NCONS * use, abort_flag);
 
@@ -251,7 +268,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
           // g holds the cumulative sum within 64-token chunks; rebase it at
           // the tile start (the value just before the tile, when the tile is
           // not the first of its chunk).
-          if (((long)step * PT) % 64 != 0) {
+          if (((long)tile * PT) % 64 != 0) {
             const f32x4 pv = *reinterpret_cast<const f32x4*>(a.g + ((size_t)(t0 - 1) * H + h) * PDK + 4 * cq);
 #pragma unroll
             for (int j = 0; j < 4; ++j) base[j] = pv[j] * kLog2e;
@@ -307,7 +324,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
         float kk[4], qq[4], kg[4], qg[4], kd[4];
         unpack_bf16x2((uint32_t)rk[r].x, kk[0], kk[1]);
         unpack_bf16x2((uint32_t)rk[r].y, kk[2], kk[3]);
-        if constexpr (NEEDQ) {
+        if constexpr (LOADQ) {
           unpack_bf16x2((uint32_t)rq[r].x, qq[0], qq[1]);
           unpack_bf16x2((uint32_t)rq[r].y, qq[2], qq[3]);
         }
@@ -316,7 +333,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
           const float G = Gl[r][j] + off[j];
           const float E = ex2(G);
           kg[j] = kk[j] * E;
-          if constexpr (NEEDQ) qg[j] = qq[j] * E;
+          if constexpr (LOADQ) qg[j] = (REV ? a.scale : 1.0f) * qq[j] * E;
           if constexpr (PAIR) {
             kt[r][j] = kk[j] * ex2(gc[j] - G);  // e^{G_15 - G} <= 1; e^{-G} alone may overflow
           } else {
@@ -326,7 +343,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
         }
         const int o = (r0 + r) * RS + 4 * cq;
         *reinterpret_cast<uint2*>(sl + sKg + o * 2) = uint2{pack_bf16x2(kg[0], kg[1]), pack_bf16x2(kg[2], kg[3])};
-        if constexpr (NEEDQ)
+        if constexpr (LOADQ)
           *reinterpret_cast<uint2*>(sl + sQg + o * 2) = uint2{pack_bf16x2(qg[0], qg[1]), pack_bf16x2(qg[2], qg[3])};
         if constexpr (PAIR) {
           // scratch for the position-pair step: G (fp32), raw k and q rows
@@ -365,7 +382,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
       }
       };
       if (lane < PT) reinterpret_cast<float*>(sl + sBeta)[lane] = rb;
-      if constexpr (!PAIR) {
+      if constexpr (!PAIR && !REV) {
         write_ktvt();
         // the next tile of this producer loads while this one is finished
         if (step + NPROD < nsteps) load_tile(step + NPROD);
@@ -490,7 +507,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
         const frag k0 = load_frag(Kg + m * RS + ca), k1 = load_frag(Kg + m * RS + ca + 16);
         dk = M::k32(d0, d1, k0, k1, dk);
         dn = M::k32(k0, k1, d0, d1, dn);
-        if constexpr (NEEDQ)
+        if constexpr (LOADQ)
           dq = M::k32(d0, d1, load_frag(Qg + m * RS + ca), load_frag(Qg + m * RS + ca + 16), dq);
       }
       // A = StrictTril(Diag(beta) raw) in the accumulator layout (An) and its
@@ -509,6 +526,11 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
           aq[e] = i <= m ? dq[e] : 0.f;
         }
         if constexpr (NEEDQ) store4(reinterpret_cast<__bf16*>(sl + sAqk) + m * TS + 4 * g4, aq);
+        if constexpr (REV) {
+          // A_qk^T row-major: element [4g4+e][m]
+#pragma unroll
+          for (int e = 0; e < 4; ++e) reinterpret_cast<__bf16*>(sl + sAqk)[(4 * g4 + e) * TS + m] = (__bf16)aq[e];
+        }
       }
       // T = (I + A)^{-1}. A is strictly lower triangular, so A^16 = 0 and
       // (I + A)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8), a product of
@@ -530,7 +552,53 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
         R = MF::k16(A2, R, R);  // (I + (A^2)^T) R
         R = MF::k16(A4, R, R);
         R = MF::k16(A8, R, R);
-        store4(reinterpret_cast<__bf16*>(sl + sT) + m * TS + 4 * g4, R);
+        if constexpr (REV) {
+          // T^T row-major: element [4g4+e][m] = T[m][4g4+e]
+#pragma unroll
+          for (int e = 0; e < 4; ++e) reinterpret_cast<__bf16*>(sl + sT)[(4 * g4 + e) * TS + m] = (__bf16)R[e];
+        } else {
+          store4(reinterpret_cast<__bf16*>(sl + sT) + m * TS + 4 * g4, R);
+        }
+      }
+      if constexpr (REV) {
+        // The products above read e^G K and e^G Q row-major from this slot;
+        // now this lane's own 8 rows x 4 channels of them are read back and
+        // rewritten channel-major, and k e^{G15-G} takes their place
+        // row-major; dO (loaded as v) goes channel-major as well.
+        uint2 kgw[8], qgw[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int o = (r0 + r) * RS + 4 * cq;
+          kgw[r] = *reinterpret_cast<const uint2*>(sl + sKg + o * 2);
+          qgw[r] = *reinterpret_cast<const uint2*>(sl + sQg + o * 2);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // every lane's product reads and read-backs are done
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup", "local");
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int o = (r0 + r) * RS + 4 * cq;
+          *reinterpret_cast<uint2*>(sl + sKg + o * 2) =
+              uint2{pack_bf16x2(kt[r][0], kt[r][1]), pack_bf16x2(kt[r][2], kt[r][3])};
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = 4 * cq + j;
+          uint32_t wk[4], wq[4], u[4];
+#pragma unroll
+          for (int r = 0; r < 8; r += 2) {
+            const uint32_t k0 = j < 2 ? kgw[r].x : kgw[r].y, k1 = j < 2 ? kgw[r + 1].x : kgw[r + 1].y;
+            const uint32_t q0 = j < 2 ? qgw[r].x : qgw[r].y, q1 = j < 2 ? qgw[r + 1].x : qgw[r + 1].y;
+            const uint32_t a0 = (uint32_t)(j < 2 ? rv[r].x : rv[r].y);
+            const uint32_t a1 = (uint32_t)(j < 2 ? rv[r + 1].x : rv[r + 1].y);
+            wk[r / 2] = (j & 1) ? perm_hi16(k0, k1) : perm_lo16(k0, k1);
+            wq[r / 2] = (j & 1) ? perm_hi16(q0, q1) : perm_lo16(q0, q1);
+            u[r / 2] = (j & 1) ? perm_hi16(a0, a1) : perm_lo16(a0, a1);
+          }
+          *reinterpret_cast<uint4*>(sl + sQg + (c * TS + r0) * 2) = uint4{wk[0], wk[1], wk[2], wk[3]};
+          *reinterpret_cast<uint4*>(sl + sKtT + (c * TS + r0) * 2) = uint4{wq[0], wq[1], wq[2], wq[3]};
+          *reinterpret_cast<uint4*>(sl + sVT + (c * TS + r0) * 2) = uint4{u[0], u[1], u[2], u[3]};
+        }
+        if (step + NPROD < nsteps) load_tile(step + NPROD);
       }
       if constexpr (PAIR) {
         __builtin_amdgcn_s_waitcnt(0xc07f);  // scratch reads done before KtT / VT overwrite it
@@ -592,9 +660,9 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
       __builtin_amdgcn_raw_buffer_store_b32((int)__builtin_amdgcn_perm(q23, p23, psel), rs, voff,
                                             soff + 2 * rowb, 0);
     };
-    // checkpoint mode: first 64-token slot of this sequence
+    // checkpoint and reverse modes: first 64-token slot of this sequence
     long ckbase = 0;
-    if constexpr (CKPT)
+    if constexpr (CKPT || REV)
       ckbase = a.seqs.cu ? (long)(a.seqs.cu[n] / 64) + n : (long)n * ((a.seqs.T + 63) / 64);
     const int ckvoff = (4 * g4 + (odd ? 1 : 0)) * (PDV * 2) + (vc0 + (m & ~1)) * 2;
     // gated epilogue: this lane's norm weights (columns vc0 + 16b + m) and the
@@ -623,8 +691,9 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
     for (int step = 0; step < nsteps; ++step) {
       const int slot = step % NSLOT;
       const char* sl = smem + slot * kSlotBytes;
-      const long t0 = bos + (long)step * PT;
-      const int L = (int)min((long)PT, len - (long)step * PT);
+      const int tile = tile_of(step);
+      const long t0 = bos + (long)tile * PT;
+      const int L = (int)min((long)PT, len - (long)tile * PT);
       wait_at_least(&ready[slot], step + 1, abort_flag);
       const __bf16* Kg = reinterpret_cast<const __bf16*>(sl + sKg);
       const __bf16* Qg = reinterpret_cast<const __bf16*>(sl + sQg);
@@ -648,10 +717,20 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
       const f32x4 bb = *reinterpret_cast<const f32x4*>(bet + 4 * g4);
       const frag tf = load_frag(T + m * TS + 4 * g4);
       f32x4 vv[CNTV];
+      frag dof[CNTV], kgtf[NCT];
+      if constexpr (REV) {
 #pragma unroll
-      for (int b = 0; b < CNTV; ++b)
-        vv[b] = TRANS ? f32x4{0.f, 0.f, 0.f, 0.f} : load4_f32(VT + (vc0 + 16 * b + m) * TS + 4 * g4);
+        for (int b = 0; b < CNTV; ++b) dof[b] = load_frag(VT + (vc0 + 16 * b + m) * TS + 4 * g4);
+        const __bf16* KgT = reinterpret_cast<const __bf16*>(sl + sQg);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) kgtf[ct] = load_frag(KgT + (16 * ct + m) * TS + 4 * g4);
+      } else {
+#pragma unroll
+        for (int b = 0; b < CNTV; ++b)
+          vv[b] = TRANS ? f32x4{0.f, 0.f, 0.f, 0.f} : load4_f32(VT + (vc0 + 16 * b + m) * TS + 4 * g4);
+      }
       frag aq = {};
+      if (REV) aq = load_frag(Aqk + m * TS + 4 * g4);
       if (want_o) {
         aq = load_frag(Aqk + m * TS + 4 * g4);
 #pragma unroll
@@ -666,6 +745,17 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
       // bf16 copy of S for this tile's products, then the tile's decay of S
       // in place (independent of the products, so it overlaps them)
       frag Sf[NCT][CNTV];
+      if constexpr (REV) {
+        if (tile % 4 == 3 || tile == nsteps - 1) {
+          const __amdgpu_buffer_rsrc_t rsc = make_rsrc(
+              static_cast<__bf16*>(a.ck_state) + ((size_t)(ckbase + tile / 4) * H + h) * PDK * PDV,
+              PDK * PDV * 2);
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int b = 0; b < CNTV; ++b) store_pairs(S[ct][b], rsc, ckvoff, PDV * 2, (16 * ct * PDV + 16 * b) * 2);
+        }
+      }
       if constexpr (CKPT) {
         if (step % 4 == 0) {
           const __amdgpu_buffer_rsrc_t rsc = make_rsrc(
@@ -694,6 +784,25 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
 #pragma unroll
         for (int b = 0; b < CNTV; ++b)
           acc[b] = M::k32(kgf[ks][0], kgf[ks][1], Sf[2 * ks][b], Sf[2 * ks + 1][b], acc[b]);
+      if constexpr (REV) {
+        // acc = Kt dS'; dV~ = acc + A_qk^T dO; dY = T^T dV~;
+        // dS <- (decayed dS') + (e^G Q)^T dO - (e^G K)^T (beta dY)
+        const uint32_t rows = (uint32_t)((L - 1) * H + 1) * PDV * 2;
+        const __amdgpu_buffer_rsrc_t rsy =
+            make_rsrc(static_cast<__bf16*>(a.ck_vt) + ((size_t)t0 * H + h) * PDV, rows);
+#pragma unroll
+        for (int b = 0; b < CNTV; ++b) {
+          const f32x4 dv = M::k16(aq, dof[b], acc[b]);
+          const f32x4 dy = M::k16(tf, M::make(dv), f32x4{0.f, 0.f, 0.f, 0.f});
+          store_pairs(dy, rsy, ovoff2, rowo, 32 * b);
+          const frag nb = M::make_neg(dy * bb);
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) S[ct][b] = M::k32(ktf[ct], kgtf[ct], dof[b], nb, S[ct][b]);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        signal_add(&done[slot], lane);
+        continue;
+      }
       frag Xf[CNTV];
 #pragma unroll
       for (int b = 0; b < CNTV; ++b) {
@@ -841,6 +950,12 @@ hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t stream) {
 hipError_t launch_chunk_checkpoint(const ChunkArgs& a, hipStream_t stream) {
   if (a.seqs.N == 0 || a.H == 0) return hipSuccess;
   launch_pipe_t<kModeCheckpoint>(a, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_reverse(const ChunkArgs& a, hipStream_t stream) {
+  if (a.seqs.N == 0 || a.H == 0) return hipSuccess;
+  launch_pipe_t<kModeReverse>(a, stream);
   return hipGetLastError();
 }
 

@@ -84,6 +84,11 @@ hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t stream);
 hipError_t launch_chunk_transition(const ChunkArgs& a, hipStream_t stream);
 // Same kernel in checkpoint mode (ck_state, ck_u, ck_vt must be set).
 hipError_t launch_chunk_checkpoint(const ChunkArgs& a, hipStream_t stream);
+// Same kernel in reverse mode, the backward's state-gradient recurrence:
+// v = dO, h0 = final-state gradient (or nullptr), hT = initial-state gradient
+// (or nullptr); writes dY (ck_vt) and the bf16 state gradient leaving every
+// 64-token chunk (ck_state).
+hipError_t launch_chunk_reverse(const ChunkArgs& a, hipStream_t stream);
 // Output epilogue y = sigmoid(z) * o / sqrt(mean(o^2) + eps) * w over rows of
 // Dv (<= 512) elements; y may alias o.
 hipError_t launch_gated_rmsnorm(const void* o, const void* z, bool bf16, const float* w, float eps,
