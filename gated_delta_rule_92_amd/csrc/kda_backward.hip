@@ -618,8 +618,8 @@ struct GradSmem {
   T dAqkT[2][BT][C::TSP];      // its transpose
   T dAt[2][BT][C::TSP];        // beta_r dAkk[r, i] (gradient of A~ = Akk / beta)
   T dAtT[2][BT][C::TSP];
-  float dbA[2][DK / 16][BT];   // per-wavefront partial sums of dbeta
-  float dbU[2][DV / 32][BT];
+  float dbA[2][BT];
+  float dbU[2][BT];
 };
 
 // Accumulator-layout tile of a row-major LDS array: element e of lane l is
@@ -710,37 +710,35 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
   }
   __syncthreads();
 
-  // Tiles are walked backwards in a rolled loop (the unrolled body would not
-  // fit the instruction cache); the state entering tile j is rebuilt from
-  // the chunk's checkpoint each time: S_{i+1} = Diag(Gamma_L) S_i + Kt^T V~.
-#pragma unroll 1
-  for (int j = nsub - 1; j >= 0; --j) {
+  // states entering the inner tiles: S_{j+1} = Diag(Gamma_L) S_j + Kt^T V~
+  frag Sf[CKT][NVT];
+#pragma unroll
+  for (int b = 0; b < NVT; ++b) Sf[0][b] = M::make(Sr[b]);
+#pragma unroll
+  for (int j = 0; j + 1 < CKT; ++j) {
+    if (j + 1 >= nsub) break;
+    const float GL = sm.G[BT * j + BT - 1][c], gl = fast_exp2(GL);
+    f32x4 Kt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = BT * j + 4 * lg + e;
+      Kt[e] = (float)sm.k[t][c] * fast_exp2(GL - sm.G[t][c]);
+    }
+    const frag ktf = M::make(Kt);
+#pragma unroll
+    for (int b = 0; b < NVT; ++b) {
+      Sr[b] = M::k16(acc_tile<T, SM::DVP>(sm.Vt, BT * j, 16 * b, lr, lg), ktf, Sr[b] * gl);
+      Sf[j + 1][b] = M::make(Sr[b]);
+    }
+  }
+
+#pragma unroll
+  for (int j = CKT - 1; j >= 0; --j) {
+    if (j >= nsub) continue;
     const int pb = j & 1;
     const int r0 = BT * j;
     const long t0 = ct0 + r0;
     const int L = min(BT, CL - r0);
-    frag Sf[NVT];
-    {
-      f32x4 Sj[NVT];
-#pragma unroll
-      for (int b = 0; b < NVT; ++b) Sj[b] = Sr[b];
-#pragma unroll 1
-      for (int i = 0; i < j; ++i) {
-        const float GL = sm.G[BT * i + BT - 1][c], gl = fast_exp2(GL);
-        f32x4 Kt;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = BT * i + 4 * lg + e;
-          Kt[e] = (float)sm.k[t][c] * fast_exp2(GL - sm.G[t][c]);
-        }
-        const frag ktf = M::make(Kt);
-#pragma unroll
-        for (int b = 0; b < NVT; ++b)
-          Sj[b] = M::k16(acc_tile<T, SM::DVP>(sm.Vt, BT * i, 16 * b, lr, lg), ktf, Sj[b] * gl);
-      }
-#pragma unroll
-      for (int b = 0; b < NVT; ++b) Sf[b] = M::make(Sj[b]);
-    }
     // row fragments of dO, dY, V~ (row lr, value positions of the 32-blocks)
     frag aO[C::NVB][2], aY[C::NVB][2], aV[C::NVB][2];
 #pragma unroll
@@ -760,13 +758,13 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < C::NVB; ++kb) {
       const frag d0 = M::make(dSr[2 * kb]), d1 = M::make(dSr[2 * kb + 1]);
-      dQg = M::k32(aO[kb][0], aO[kb][1], Sf[2 * kb], Sf[2 * kb + 1], dQg);
-      dKg = M::k32(aY[kb][0], aY[kb][1], Sf[2 * kb], Sf[2 * kb + 1], dKg);
+      dQg = M::k32(aO[kb][0], aO[kb][1], Sf[j][2 * kb], Sf[j][2 * kb + 1], dQg);
+      dKg = M::k32(aY[kb][0], aY[kb][1], Sf[j][2 * kb], Sf[j][2 * kb + 1], dKg);
       dKt = M::k32(aV[kb][0], aV[kb][1], d0, d1, dKt);
     }
 #pragma unroll
     for (int b = 0; b < NVT; ++b) {
-      const f32x4 s4 = M::to_f32(Sf[b]);
+      const f32x4 s4 = M::to_f32(Sf[j][b]);
       gsum += s4[0] * dSr[b][0] + s4[1] * dSr[b][1] + s4[2] * dSr[b][2] + s4[3] * dSr[b][3];
     }
     gsum += __shfl_xor(gsum, 16, 64);
@@ -774,55 +772,6 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) dKg[e] *= -sm.beta[r0 + 4 * lg + e];
 
-    // dAkk = -StrictTril(dY V~^T) (every wavefront); its dbeta term
-    // sum_i dAkk[r,i] A~[r,i] with A~ = Kl Kd^T split over the wavefronts'
-    // channel blocks; rowsum(dY * U) split over 32-blocks of values.
-    {
-      f32x4 p = z;
-#pragma unroll
-      for (int kb = 0; kb < C::NVB; ++kb) p = M::k32(aY[kb][0], aY[kb][1], aV[kb][0], aV[kb][1], p);
-      f32x4 kl, kd;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int cc = 16 * w + 4 * lg + e;
-        const float kv = (float)sm.k[r0 + lr][cc];
-        const float d = sm.G[r0 + lr][cc] - sm.G[r0 + 7][cc];
-        kl[e] = kv * fast_exp2(d);
-        kd[e] = kv * fast_exp2(-d);
-      }
-      const f32x4 At = M::k16(M::make(kl), M::make(kd), z);
-      f32x4 part;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * lg + e;
-        const float dA = lr < r ? -p[e] : 0.f;
-        part[e] = dA * At[e];
-        if (w == 1) {
-          const T x = (T)(sm.beta[r0 + r] * dA);
-          sm.dAt[pb][r][lr] = x;
-          sm.dAtT[pb][lr][r] = x;
-        }
-      }
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) part[e] += __shfl_xor(part[e], m, 64);
-      if (lr == 0)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sm.dbA[pb][w][4 * lg + e] = part[e];
-      if (w < C::NVB) {
-        float u = 0.f;
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const f32x4 u4 = M::to_f32(load_frag(&sm.U[r0 + lr][32 * w + 16 * hf + 4 * lg]));
-          const f32x4 y4 = M::to_f32(aY[w][hf]);
-          u += u4[0] * y4[0] + u4[1] * y4[1] + u4[2] * y4[2] + u4[3] * y4[3];
-        }
-        u += __shfl_xor(u, 16, 64);
-        u += __shfl_xor(u, 32, 64);
-        if (lg == 0) sm.dbU[pb][w][lr] = u;
-      }
-    }
     if (w == 0) {
       // dAqk = Tril(dO V~^T)
       f32x4 p = z;
@@ -835,17 +784,60 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
         sm.dAqk[pb][r][lr] = x;
         sm.dAqkT[pb][lr][r] = x;
       }
+    } else if (w == 1) {
+      // dAkk = -StrictTril(dY V~^T); A~ = Kl Kd^T over all channels; dbeta
+      f32x4 p = z;
+#pragma unroll
+      for (int kb = 0; kb < C::NVB; ++kb) p = M::k32(aY[kb][0], aY[kb][1], aV[kb][0], aV[kb][1], p);
+      f32x4 At = z;
+#pragma unroll
+      for (int cb = 0; cb < DK / 16; ++cb) {
+        f32x4 kl, kd;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int cc = 16 * cb + 4 * lg + e;
+          const float kv = (float)sm.k[r0 + lr][cc];
+          const float d = sm.G[r0 + lr][cc] - sm.G[r0 + 7][cc];
+          kl[e] = kv * fast_exp2(d);
+          kd[e] = kv * fast_exp2(-d);
+        }
+        At = M::k16(M::make(kl), M::make(kd), At);
+      }
+      f32x4 part;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * lg + e;
+        const float dA = lr < r ? -p[e] : 0.f;
+        part[e] = lr < r ? dA * At[e] : 0.f;
+        const T x = (T)(sm.beta[r0 + r] * dA);
+        sm.dAt[pb][r][lr] = x;
+        sm.dAtT[pb][lr][r] = x;
+      }
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part[e] += __shfl_xor(part[e], m, 64);
+      if (lr == 0)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.dbA[pb][4 * lg + e] = part[e];
+      // rowsum(dY * U), row lr
+      float u = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < C::NVB; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const f32x4 u4 = M::to_f32(load_frag(&sm.U[r0 + lr][32 * kb + 16 * hf + 4 * lg]));
+          const f32x4 y4 = M::to_f32(aY[kb][hf]);
+          u += u4[0] * y4[0] + u4[1] * y4[1] + u4[2] * y4[2] + u4[3] * y4[3];
+        }
+      u += __shfl_xor(u, 16, 64);
+      u += __shfl_xor(u, 32, 64);
+      if (lg == 0) sm.dbU[pb][lr] = u;
     }
     __syncthreads();
 
-    if ((int)threadIdx.x < L) {
-      float db = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) db += sm.dbA[pb][ww][threadIdx.x];
-#pragma unroll
-      for (int ww = 0; ww < C::NVB; ++ww) db += sm.dbU[pb][ww][threadIdx.x];
-      a.dbeta[(t0 + threadIdx.x) * H + h] = db;
-    }
+    if ((int)threadIdx.x < L)
+      a.dbeta[(t0 + threadIdx.x) * H + h] = sm.dbA[pb][threadIdx.x] + sm.dbU[pb][threadIdx.x];
     // dV = beta dY, one 32-block of value positions per wavefront
     if (w < C::NVB && lr < L) {
       const float bb = sm.beta[r0 + lr];
