@@ -710,13 +710,12 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
   }
   __syncthreads();
 
-  // states entering the inner tiles: S_{j+1} = Diag(Gamma_L) S_j + Kt^T V~
-  frag Sf[CKT][NVT];
-#pragma unroll
-  for (int b = 0; b < NVT; ++b) Sf[0][b] = M::make(Sr[b]);
-#pragma unroll
-  for (int j = 0; j + 1 < CKT; ++j) {
-    if (j + 1 >= nsub) break;
+  // states entering the inner tiles: S_{j+1} = Diag(Gamma_L) S_j + Kt^T V~.
+  // Each tile's state has an array of its own (a register array indexed by
+  // a loop variable would be lowered to select chains).
+  frag Sf0[NVT], Sf1[NVT], Sf2[NVT], Sf3[NVT];
+  static_assert(CKT == 1 || CKT == 4, "tiles per checkpoint chunk");
+  auto advance = [&](int j, frag (&out)[NVT]) {
     const float GL = sm.G[BT * j + BT - 1][c], gl = fast_exp2(GL);
     f32x4 Kt;
 #pragma unroll
@@ -728,13 +727,19 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
 #pragma unroll
     for (int b = 0; b < NVT; ++b) {
       Sr[b] = M::k16(acc_tile<T, SM::DVP>(sm.Vt, BT * j, 16 * b, lr, lg), ktf, Sr[b] * gl);
-      Sf[j + 1][b] = M::make(Sr[b]);
+      out[b] = M::make(Sr[b]);
     }
+  };
+#pragma unroll
+  for (int b = 0; b < NVT; ++b) Sf0[b] = M::make(Sr[b]);
+  if constexpr (CKT == 4) {
+    if (nsub > 1) advance(0, Sf1);
+    if (nsub > 2) advance(1, Sf2);
+    if (nsub > 3) advance(2, Sf3);
   }
 
-#pragma unroll
-  for (int j = CKT - 1; j >= 0; --j) {
-    if (j >= nsub) continue;
+  // one tile of the backward walk, given the state entering it
+  auto tile_step = [&](const int j, const frag (&Sfj)[NVT]) {
     const int pb = j & 1;
     const int r0 = BT * j;
     const long t0 = ct0 + r0;
@@ -758,13 +763,13 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < C::NVB; ++kb) {
       const frag d0 = M::make(dSr[2 * kb]), d1 = M::make(dSr[2 * kb + 1]);
-      dQg = M::k32(aO[kb][0], aO[kb][1], Sf[j][2 * kb], Sf[j][2 * kb + 1], dQg);
-      dKg = M::k32(aY[kb][0], aY[kb][1], Sf[j][2 * kb], Sf[j][2 * kb + 1], dKg);
+      dQg = M::k32(aO[kb][0], aO[kb][1], Sfj[2 * kb], Sfj[2 * kb + 1], dQg);
+      dKg = M::k32(aY[kb][0], aY[kb][1], Sfj[2 * kb], Sfj[2 * kb + 1], dKg);
       dKt = M::k32(aV[kb][0], aV[kb][1], d0, d1, dKt);
     }
 #pragma unroll
     for (int b = 0; b < NVT; ++b) {
-      const f32x4 s4 = M::to_f32(Sf[j][b]);
+      const f32x4 s4 = M::to_f32(Sfj[b]);
       gsum += s4[0] * dSr[b][0] + s4[1] * dSr[b][1] + s4[2] * dSr[b][2] + s4[3] * dSr[b][3];
     }
     gsum += __shfl_xor(gsum, 16, 64);
@@ -838,14 +843,19 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
 
     if ((int)threadIdx.x < L)
       a.dbeta[(t0 + threadIdx.x) * H + h] = sm.dbA[pb][threadIdx.x] + sm.dbU[pb][threadIdx.x];
-    // dV = beta dY, one 32-block of value positions per wavefront
-    if (w < C::NVB && lr < L) {
-      const float bb = sm.beta[r0 + lr];
+    // dV = beta dY, one 32-block of value positions per wavefront (a
+    // static loop: indexing the fragment array by the wavefront number would
+    // turn into select chains)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const f32x4 y4 = M::to_f32(aY[w][hf]);
-        store4(static_cast<T*>(a.dv) + ((t0 + lr) * H + h) * (long)DV + 32 * w + 16 * hf + 4 * lg,
-               f32x4{bb * y4[0], bb * y4[1], bb * y4[2], bb * y4[3]});
+    for (int kb = 0; kb < C::NVB; ++kb) {
+      if (kb == w && lr < L) {
+        const float bb = sm.beta[r0 + lr];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const f32x4 y4 = M::to_f32(aY[kb][hf]);
+          store4(static_cast<T*>(a.dv) + ((t0 + lr) * H + h) * (long)DV + 32 * kb + 16 * hf + 4 * lg,
+                 f32x4{bb * y4[0], bb * y4[1], bb * y4[2], bb * y4[3]});
+        }
       }
     }
 
@@ -916,7 +926,13 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
         dSr[b] = M::k32(acc_tile<T, SM::DVP>(sm.dO, r0, 16 * b, lr, lg),
                         acc_tile<T, SM::DVP>(sm.dY, r0, 16 * b, lr, lg), qf, kf, dSr[b] * gl);
     }
+  };
+  if constexpr (CKT == 4) {
+    if (nsub > 3) tile_step(3, Sf3);
+    if (nsub > 2) tile_step(2, Sf2);
+    if (nsub > 1) tile_step(1, Sf1);
   }
+  tile_step(0, Sf0);
 }
 
 template <typename T, int DK, int DV>
