@@ -80,14 +80,19 @@ def backward_algorithmic_bytes(w, n_tokens: int, n_units: int) -> int:
 
 def backward_design_bytes(w, n_tokens: int, n_units: int) -> int:
     """HBM bytes the three-kernel backward moves by design: the minimum above,
-    plus the per-16-token-tile state and state-gradient checkpoints (written
-    once, read once) and U, V~, dY (written once, read once), plus the second
-    reads of q, k, the gate and beta by the scans and of v, do by the scans."""
+    plus the state and state-gradient checkpoints (one each per 64 tokens for
+    bf16, 16 for fp32; written once, read once), U, V~ and dY (written once,
+    read once), and the inputs that the two scans and the per-chunk kernel
+    each read again (q, k, the gate, beta, v or dO)."""
     el = 2 if w.dtype_name == "bf16" else 4
-    tiles = n_tokens // 16 * w.H
-    ck = 2 * tiles * w.Dk * w.Dv * el * 2
-    tok = 3 * n_tokens * w.H * w.Dv * el * 2
-    rereads = n_tokens * w.H * (2 * (w.Dk * el + w.Dk * 4 + 4) + w.Dk * el + 2 * w.Dv * el)
+    ct = 64 if w.dtype_name == "bf16" else 16
+    ck = 2 * 2 * (n_tokens // ct) * w.H * w.Dk * w.Dv * el
+    tok = 3 * 2 * n_tokens * w.H * w.Dv * el
+    kin, gin, vin = w.Dk * el, w.Dk * 4 + 4, w.Dv * el     # k or q row, gate + beta, v or dO row
+    scans = (kin + gin + vin) + (2 * kin + gin + vin)       # forward scan; reverse scan
+    grads = 2 * kin + gin + vin                             # per-chunk kernel (q, k, gate, beta, dO)
+    minimal_in = 2 * kin + gin + 2 * vin
+    rereads = n_tokens * w.H * (scans + grads - minimal_in)
     return backward_algorithmic_bytes(w, n_tokens, n_units) + ck + tok + rereads
 
 
