@@ -317,7 +317,8 @@ kda_status_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv, i
   const size_t e = bwd_elt(dtype);
   const size_t ck = round_up((size_t)bwd_slots_bound(B, T, N, dtype) * H * Dk * Dv * e, kWorkspaceAlign);
   const size_t tok = round_up((size_t)B * T * H * Dv * e, kWorkspaceAlign);
-  *bytes = 2 * ck + 3 * tok;
+  const size_t at = round_up((size_t)B * T * H * 16 * sizeof(float), kWorkspaceAlign);
+  *bytes = 2 * ck + 3 * tok + at;
   return KDA_SUCCESS;
 }
 
@@ -371,6 +372,7 @@ kda_status_t kda_chunk_bwd(const void* q, const void* k, const void* v, kda_dtyp
   a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = d_initial_state;
   a.ckS = ws; a.ckdS = ws + ck; a.U = ws + 2 * ck; a.Vt = ws + 2 * ck + tok;
   a.dY = ws + 2 * ck + 2 * tok;
+  a.At = reinterpret_cast<float*>(ws + 2 * ck + 3 * tok);
   return launch_status(kda::launch_chunk_bwd(a, dtype == KDA_BFLOAT16, Dk, Dv, slots,
                                              reinterpret_cast<hipStream_t>(stream)));
 }

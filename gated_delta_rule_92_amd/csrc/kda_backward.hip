@@ -362,6 +362,7 @@ __global__ void __launch_bounds__(NTH) bwd_fwd_scan(BwdArgs a) {
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * lg + e;
         N[e] = lr < r ? -sm.tf.beta[r] * At[e] : 0.f;
+        if (r < L) a.At[((t0 + r) * H + h) * BT + lr] = lr < r ? At[e] : 0.f;
       }
       const f32x4 Tm = unit_lower_inverse(N, sm.xs, lr, lg);
 #pragma unroll
@@ -614,6 +615,7 @@ struct GradSmem {
   T dY[CT][DVP];
   T Vt[CT][DVP];
   T U[CT][DVP];
+  float At[CT][20];            // A~ = A_kk / beta, row r of its tile (strictly lower)
   T dAqk[2][BT][C::TSP];       // dAqk, row-major
   T dAqkT[2][BT][C::TSP];      // its transpose
   T dAt[2][BT][C::TSP];        // beta_r dAkk[r, i] (gradient of A~ = Akk / beta)
@@ -687,6 +689,7 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
   {
     RowsIn<T, DK, CT, NT> in_q, in_k;
     RowsIn<T, DV, CT, NT> in_o, in_y, in_v, in_u;
+    RowsIn<float, BT, CT, NT> in_a;
     GateIn<DK> in_g;
     const int tid = threadIdx.x;
     const int sb = tid / DK, cc = tid % DK;
@@ -697,6 +700,7 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
     in_y.load(a.dY, ct0, CL, h, H);
     in_v.load(a.Vt, ct0, CL, h, H);
     in_u.load(a.U, ct0, CL, h, H);
+    in_a.load(a.At, ct0, CL, h, H);
     if (tid < CKT * DK) in_g.load(a, ct0 + BT * sb, Lsb, h, cc);
     const float bv = tid < CL ? a.beta[(ct0 + tid) * H + h] : 0.f;
     in_q.store(sm.q);
@@ -705,6 +709,7 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
     in_y.store(sm.dY);
     in_v.store(sm.Vt);
     in_u.store(sm.U);
+    in_a.store(sm.At);
     if (tid < CKT * DK) in_g.store(sm.G, a, Lsb, h, cc, BT * sb);
     if (tid < CT) sm.beta[tid] = bv;
   }
@@ -794,20 +799,9 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
       f32x4 p = z;
 #pragma unroll
       for (int kb = 0; kb < C::NVB; ++kb) p = M::k32(aY[kb][0], aY[kb][1], aV[kb][0], aV[kb][1], p);
-      f32x4 At = z;
+      f32x4 At;
 #pragma unroll
-      for (int cb = 0; cb < DK / 16; ++cb) {
-        f32x4 kl, kd;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int cc = 16 * cb + 4 * lg + e;
-          const float kv = (float)sm.k[r0 + lr][cc];
-          const float d = sm.G[r0 + lr][cc] - sm.G[r0 + 7][cc];
-          kl[e] = kv * fast_exp2(d);
-          kd[e] = kv * fast_exp2(-d);
-        }
-        At = M::k16(M::make(kl), M::make(kd), At);
-      }
+      for (int e = 0; e < 4; ++e) At[e] = sm.At[r0 + 4 * lg + e][lr];
       f32x4 part;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -948,7 +942,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, long slots, hipStream_t stream) {
     c.seqs.cu = a.cu; c.seqs.N = a.N; c.seqs.T = a.T; c.seqs.Ttot = 0;
     c.order = nullptr;
     c.H = a.H; c.Dk = DK; c.Dv = DV; c.scale = a.scale; c.bf16 = true;
-    c.ck_state = a.ckS; c.ck_u = a.U; c.ck_vt = a.Vt;
+    c.ck_state = a.ckS; c.ck_u = a.U; c.ck_vt = a.Vt; c.ck_at = a.At;
     hipError_t e = launch_chunk_checkpoint(c, stream);
     if (e != hipSuccess) return e;
   } else {

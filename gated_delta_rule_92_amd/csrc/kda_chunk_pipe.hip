@@ -526,6 +526,15 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
           aq[e] = i <= m ? dq[e] : 0.f;
         }
         if constexpr (NEEDQ) store4(reinterpret_cast<__bf16*>(sl + sAqk) + m * TS + 4 * g4, aq);
+        if constexpr (CKPT) {
+          // the backward's dbeta needs A~ = A_kk / beta: row m, entries 4g4..4g4+3
+          const __amdgpu_buffer_rsrc_t rsa =
+              make_rsrc(a.ck_at + ((size_t)t0 * H + h) * PT, (uint32_t)((L - 1) * H + 1) * PT * 4);
+          f32x4 ar;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ar[e] = 4 * g4 + e < m ? dk[e] : 0.f;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, ar), rsa, m * H * PT * 4 + g4 * 16, 0, 0);
+        }
         if constexpr (REV) {
           // A_qk^T row-major: element [4g4+e][m]
 #pragma unroll

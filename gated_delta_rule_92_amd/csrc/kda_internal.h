@@ -74,6 +74,7 @@ struct ChunkArgs {
   void* ck_state = nullptr;
   void* ck_u = nullptr;
   void* ck_vt = nullptr;
+  float* ck_at = nullptr;  // checkpoint mode: A_kk / beta per tile row, fp32 [Ttot, H, 16]
 };
 bool chunk_fused_supported(bool bf16, int Dk, int Dv, int chunk);
 // Pipelined producer/consumer chunk kernel (bf16, Dk = Dv = 128).
@@ -133,6 +134,8 @@ struct BwdArgs {
   void* U;             // [Ttot, H, Dv] V - Kg S
   void* Vt;            // [Ttot, H, Dv] pseudo-values
   void* dY;            // [Ttot, H, Dv] T^T dV~
+  float* At;           // [Ttot, H, 16] row r of each tile's A~ = A_kk / beta
+                       // (strictly lower part; zeros elsewhere)
 };
 bool chunk_bwd_supported(int Dk, int Dv);
 int chunk_bwd_checkpoint_tokens(bool bf16);

@@ -214,9 +214,10 @@ def test_chunk_bwd_not_supported_and_workspace():
     n = ctypes.c_size_t(0)
     assert lib.kda_chunk_bwd_workspace_size(8, 8192, 32, 128, 128, 8, 64, 1, ctypes.byref(n)) == 0
     # two bf16 checkpoints per 64-token chunk slot (slots = max(B ceil(T/64),
-    # B T / 64 + N) per head) and three bf16 per-token arrays
+    # B T / 64 + N) per head), three bf16 per-token arrays
     tiles, tokens = (8 * 8192 // 64 + 8) * 32, 8 * 8192 * 32
-    assert n.value == 2 * tiles * 128 * 128 * 2 + 3 * tokens * 128 * 2
+    # plus A~ = A_kk / beta, 16 fp32 per token-head
+    assert n.value == 2 * tiles * 128 * 128 * 2 + 3 * tokens * 128 * 2 + tokens * 16 * 4
     assert _bwd(ws_bytes=n.value - 1, B=8, N=8, T=8192, H=32) == \
         _lib.KDA_ERROR_INSUFFICIENT_WORKSPACE
     # packed sequences: up to one ragged chunk per sequence (fp32: 16-token chunks)
