@@ -143,3 +143,11 @@ def test_bwd_train8k_full_size_sampled():
         print(f"  unit ({n},{h}) " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
         for name, e in errs.items():
             assert e <= TOL_BF16, (name, e)
+
+
+def test_bwd_bf16_varlen_long_mixed():
+    """Packed sequences of very different lengths (1 to 4096 tokens, ragged
+    tails, several 64-token checkpoint chunks per sequence), initial state
+    and final-state gradient, every unit checked against the oracle."""
+    _run("bf16 d=128 varlen long mixed", 1, 0, 3, 128, 128, torch.bfloat16,
+         lengths=[4096, 1, 700, 64, 2049, 129], gate="logits", h0_std=0.02, seed=45)
