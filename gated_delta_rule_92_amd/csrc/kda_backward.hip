@@ -125,6 +125,7 @@ struct Raw<__bf16> {
     unpack_bf16x2(w.y, x2, x3);
     return f32x4{x0, x1, x2, x3};
   }
+  __device__ __forceinline__ void put(__bf16* p) const { *reinterpret_cast<uint2*>(p) = w; }
 };
 template <>
 struct Raw<float> {
@@ -132,7 +133,17 @@ struct Raw<float> {
   __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const f32x4*>(p); }
   __device__ __forceinline__ void zero() { w = f32x4{0.f, 0.f, 0.f, 0.f}; }
   __device__ __forceinline__ f32x4 f32() const { return w; }
+  __device__ __forceinline__ void put(float* p) const { *reinterpret_cast<f32x4*>(p) = w; }
 };
+
+// p advanced by a byte offset below 2^32. With p the same on every lane the
+// access takes a scalar base address and a 32-bit vector offset, instead of
+// 64-bit address arithmetic per lane.
+template <typename P>
+__device__ __forceinline__ P* byte_at(P* p, uint32_t off) {
+  using B = typename std::conditional<std::is_const<P>::value, const char, char>::type;
+  return reinterpret_cast<P*>(reinterpret_cast<B*>(p) + off);
+}
 
 // ROWS rows [t0, t0 + rows) of a [Ttot, H, D] array (zeros past `rows`),
 // four elements per thread and step: load() issues every load into
@@ -142,12 +153,14 @@ struct RowsIn {
   static constexpr int Q = D / 4;
   static constexpr int IT = (ROWS * Q + NT - 1) / NT;
   Raw<T> x[IT];
+  // t0, h and H are the same on every lane
   __device__ __forceinline__ void load(const void* src, long t0, int rows, int h, int H) {
+    const T* base = static_cast<const T*>(src) + (t0 * H + h) * (long)D;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int idx = threadIdx.x + i * NT, r = idx / Q, c = (idx % Q) * 4;
       if (idx < ROWS * Q && r < rows)
-        x[i].load(static_cast<const T*>(src) + ((t0 + r) * H + h) * (long)D + c);
+        x[i].load(byte_at(base, (uint32_t)((r * H * D + c) * (int)sizeof(T))));
       else
         x[i].zero();
     }
@@ -157,7 +170,12 @@ struct RowsIn {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int idx = threadIdx.x + i * NT, r = idx / Q, c = (idx % Q) * 4;
-      if (idx < ROWS * Q) store4(&dst[r][c], x[i].f32());
+      if (idx < ROWS * Q) {
+        if constexpr (std::is_same<U, T>::value)
+          x[i].put(&dst[r][c]);
+        else
+          store4(&dst[r][c], x[i].f32());
+      }
     }
   }
   template <typename U, int LD>
@@ -180,9 +198,12 @@ struct RowsIn {
 template <int DK>
 struct GateIn {
   float g[BT];
-  __device__ __forceinline__ void load(const BwdArgs& a, long t0, int L, int h, int c) {
+  // rows row0 .. row0 + L - 1 after token t0 (t0 and h the same on every lane)
+  __device__ __forceinline__ void load(const BwdArgs& a, long t0, int row0, int L, int h, int c) {
+    const float* base = a.g + (t0 * a.H + h) * (long)DK;
 #pragma unroll
-    for (int r = 0; r < BT; ++r) g[r] = r < L ? a.g[((t0 + r) * a.H + h) * (long)DK + c] : 0.f;
+    for (int r = 0; r < BT; ++r)
+      g[r] = r < L ? *byte_at(base, (uint32_t)(((row0 + r) * a.H * DK + c) * 4)) : 0.f;
   }
   __device__ __forceinline__ void store(float (*G)[DK + 4], const BwdArgs& a, int L, int h, int c,
                                         int row0) const {
@@ -258,6 +279,24 @@ __device__ __forceinline__ f32x4 tri_product(const T (*X)[DKP], const T (*Y)[DKP
   return acc;
 }
 
+// acc + sum_e x[e] y[e] over two fragments; for bf16 two packed dot
+// products (exact products, fp32 sums) instead of eight conversions and four
+// multiply-adds.
+// (the packed words go through a by-value helper: a bit cast applied to one
+// element of a vector is miscompiled to read element 0)
+__device__ __forceinline__ float dot2_bf16(uint32_t x, uint32_t y, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y), acc,
+                                         false);
+}
+__device__ __forceinline__ float frag_dot(const bf16x4& x, const bf16x4& y, float acc) {
+  const uint2 xa = __builtin_bit_cast(uint2, x), ya = __builtin_bit_cast(uint2, y);
+  return dot2_bf16(xa.y, ya.y, dot2_bf16(xa.x, ya.x, acc));
+}
+__device__ __forceinline__ float frag_dot(const f32x4& x, const f32x4& y, float acc) {
+  return acc + x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+}
+
 template <typename T>
 __device__ __forceinline__ void st(void* base, long idx, float x) {
   static_cast<T*>(base)[idx] = (T)x;
@@ -316,7 +355,7 @@ __global__ void __launch_bounds__(NTH) bwd_fwd_scan(BwdArgs a) {
     const int LL = min(BT, un.len - jj * BT);
     in_k.load(a.k, tt, LL, h, H);
     in_v.load(a.v, tt, LL, h, H);
-    if (tid < DK) in_g.load(a, tt, LL, h, tid);
+    if (tid < DK) in_g.load(a, tt, 0, LL, h, tid);
     if (tid < BT) in_b = tid < LL ? a.beta[(tt + tid) * H + h] : 0.f;
   };
   if (nt > 0) issue(0);
@@ -473,7 +512,7 @@ __global__ void __launch_bounds__(NTH) bwd_rev_scan(BwdArgs a) {
     in_q.load(a.q, tt, LL, h, H);
     in_k.load(a.k, tt, LL, h, H);
     in_o.load(a.dO, tt, LL, h, H);
-    if (tid < DK) in_g.load(a, tt, LL, h, tid);
+    if (tid < DK) in_g.load(a, tt, 0, LL, h, tid);
     if (tid < BT) in_b = tid < LL ? a.beta[(tt + tid) * H + h] : 0.f;
   };
   if (nt > 0) issue(nt - 1);
@@ -677,12 +716,15 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 
   // rows c of the chunk's two checkpoints (loads in flight during staging)
-  const long ck = (slot * H + h) * (long)DK * DV + (long)c * DV;
+  const long ck = (slot * H + h) * (long)DK * DV;
+  const T* ckS = static_cast<const T*>(a.ckS) + ck;
+  const T* ckdS = static_cast<const T*>(a.ckdS) + ck;
   f32x4 Sr[NVT], dSr[NVT];
 #pragma unroll
   for (int b = 0; b < NVT; ++b) {
-    Sr[b] = load4_f32(static_cast<const T*>(a.ckS) + ck + 16 * b + 4 * lg);
-    dSr[b] = load4_f32(static_cast<const T*>(a.ckdS) + ck + 16 * b + 4 * lg);
+    const uint32_t off = (uint32_t)((c * DV + 16 * b + 4 * lg) * (int)sizeof(T));
+    Sr[b] = load4_f32(byte_at(ckS, off));
+    dSr[b] = load4_f32(byte_at(ckdS, off));
   }
 
   // stage the chunk: every load issued first, then the LDS writes
@@ -701,8 +743,8 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
     in_v.load(a.Vt, ct0, CL, h, H);
     in_u.load(a.U, ct0, CL, h, H);
     in_a.load(a.At, ct0, CL, h, H);
-    if (tid < CKT * DK) in_g.load(a, ct0 + BT * sb, Lsb, h, cc);
-    const float bv = tid < CL ? a.beta[(ct0 + tid) * H + h] : 0.f;
+    if (tid < CKT * DK) in_g.load(a, ct0, BT * sb, Lsb, h, cc);
+    const float bv = tid < CL ? *byte_at(a.beta + ct0 * H + h, (uint32_t)(tid * H * 4)) : 0.f;
     in_q.store(sm.q);
     in_k.store(sm.k);
     in_o.store(sm.dO);
@@ -762,7 +804,7 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
       }
 
     // dQg = dO S^T, dKg = -(beta dY) S^T, dKt = V~ dS'^T on this wavefront's
-    // channels; dGamma_L = rowsum(dS' * S).
+    // channels; dGamma_L = rowsum(dS' * S) (both in the operand precision).
     f32x4 dQg = z, dKg = z, dKt = z;
     float gsum = 0.f;
 #pragma unroll
@@ -771,11 +813,8 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
       dQg = M::k32(aO[kb][0], aO[kb][1], Sfj[2 * kb], Sfj[2 * kb + 1], dQg);
       dKg = M::k32(aY[kb][0], aY[kb][1], Sfj[2 * kb], Sfj[2 * kb + 1], dKg);
       dKt = M::k32(aV[kb][0], aV[kb][1], d0, d1, dKt);
-    }
-#pragma unroll
-    for (int b = 0; b < NVT; ++b) {
-      const f32x4 s4 = M::to_f32(Sfj[b]);
-      gsum += s4[0] * dSr[b][0] + s4[1] * dSr[b][1] + s4[2] * dSr[b][2] + s4[3] * dSr[b][3];
+      gsum = frag_dot(Sfj[2 * kb], d0, gsum);
+      gsum = frag_dot(Sfj[2 * kb + 1], d1, gsum);
     }
     gsum += __shfl_xor(gsum, 16, 64);
     gsum += __shfl_xor(gsum, 32, 64);
@@ -824,11 +863,8 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < C::NVB; ++kb)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const f32x4 u4 = M::to_f32(load_frag(&sm.U[r0 + lr][32 * kb + 16 * hf + 4 * lg]));
-          const f32x4 y4 = M::to_f32(aY[kb][hf]);
-          u += u4[0] * y4[0] + u4[1] * y4[1] + u4[2] * y4[2] + u4[3] * y4[3];
-        }
+        for (int hf = 0; hf < 2; ++hf)
+          u = frag_dot(load_frag(&sm.U[r0 + lr][32 * kb + 16 * hf + 4 * lg]), aY[kb][hf], u);
       u += __shfl_xor(u, 16, 64);
       u += __shfl_xor(u, 32, 64);
       if (lg == 0) sm.dbU[pb][lr] = u;
@@ -836,7 +872,8 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
     __syncthreads();
 
     if ((int)threadIdx.x < L)
-      a.dbeta[(t0 + threadIdx.x) * H + h] = sm.dbA[pb][threadIdx.x] + sm.dbU[pb][threadIdx.x];
+      *byte_at(a.dbeta + t0 * H + h, (uint32_t)(threadIdx.x * H * 4)) =
+          sm.dbA[pb][threadIdx.x] + sm.dbU[pb][threadIdx.x];
     // dV = beta dY, one 32-block of value positions per wavefront (a
     // static loop: indexing the fragment array by the wavefront number would
     // turn into select chains)
@@ -844,10 +881,11 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
     for (int kb = 0; kb < C::NVB; ++kb) {
       if (kb == w && lr < L) {
         const float bb = sm.beta[r0 + lr];
+        T* dvb = static_cast<T*>(a.dv) + (t0 * H + h) * (long)DV;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           const f32x4 y4 = M::to_f32(aY[kb][hf]);
-          store4(static_cast<T*>(a.dv) + ((t0 + lr) * H + h) * (long)DV + 32 * kb + 16 * hf + 4 * lg,
+          store4(byte_at(dvb, (uint32_t)((lr * H * DV + 32 * kb + 16 * hf + 4 * lg) * (int)sizeof(T))),
                  f32x4{bb * y4[0], bb * y4[1], bb * y4[2], bb * y4[3]});
         }
       }
@@ -900,14 +938,18 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
     const float t2 = __shfl(tot, (lane + 32) & 63, 64);
     const float t3 = __shfl(tot, (lane + 48) & 63, 64);
     const float after = (lg < 3 ? t1 : 0.f) + (lg < 2 ? t2 : 0.f) + (lg < 1 ? t3 : 0.f);
+    const long ob = (t0 * H + h) * (long)DK;
+    T* dqb = static_cast<T*>(a.dq) + ob;
+    T* dkb = static_cast<T*>(a.dk) + ob;
+    float* dgb = a.dg + ob;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = 4 * lg + e;
       if (t < L) {
-        const long idx = ((t0 + t) * H + h) * (long)DK + c;
-        st<T>(a.dq, idx, dq[e]);
-        st<T>(a.dk, idx, dk[e]);
-        a.dg[idx] = suf[e] + after;
+        const uint32_t oi = (uint32_t)(t * H * DK + c);
+        *byte_at(dqb, oi * (uint32_t)sizeof(T)) = (T)dq[e];
+        *byte_at(dkb, oi * (uint32_t)sizeof(T)) = (T)dk[e];
+        *byte_at(dgb, oi * 4u) = suf[e] + after;
       }
     }
 
