@@ -23,7 +23,9 @@
 //              dAkk = -StrictTril(dY V~^T),  dV = beta dY,
 //              dbeta = rowsum(dY * U) + rowsum(dAkk * Akk / beta),
 //              then through the decay factors into dq, dk and dG, and
-//              dg = reverse cumulative sum of dG inside the tile.
+//              dg = reverse cumulative sum of dG inside the tile. The
+//              diagonal of dAqk goes straight to dq and dk (Aqk[t,t] has no
+//              decay factor, hence no G derivative).
 // The triangular products split their decay at a reference point rho (G of
 // the tile's eighth token): left factors e^{G-rho}, right factors e^{rho-G},
 // at most e^{8 * 5.5} each way for g >= -5.5. The products do not depend on
@@ -655,8 +657,9 @@ struct GradSmem {
   T Vt[CT][DVP];
   T U[CT][DVP];
   float At[CT][20];            // A~ = A_kk / beta, row r of its tile (strictly lower)
-  T dAqk[2][BT][C::TSP];       // dAqk, row-major
+  T dAqk[2][BT][C::TSP];       // dAqk below the diagonal, row-major
   T dAqkT[2][BT][C::TSP];      // its transpose
+  float dAd[2][BT];            // the diagonal of dAqk
   T dAt[2][BT][C::TSP];        // beta_r dAkk[r, i] (gradient of A~ = Akk / beta)
   T dAtT[2][BT][C::TSP];
   float dbA[2][BT];
@@ -822,16 +825,22 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
     for (int e = 0; e < 4; ++e) dKg[e] *= -sm.beta[r0 + 4 * lg + e];
 
     if (w == 0) {
-      // dAqk = Tril(dO V~^T)
+      // dAqk = Tril(dO V~^T). The diagonal entries A_qk[t,t] = s q_t . k_t
+      // carry no decay factor, so they have no G derivative; they are kept
+      // apart and applied to dq, dk directly. Through the split-decay
+      // products their row and column terms would cancel only up to the
+      // operands' rounding, an O(|q k|) residue that swamps dG when the
+      // off-diagonal decay factors are small.
       f32x4 p = z;
 #pragma unroll
       for (int kb = 0; kb < C::NVB; ++kb) p = M::k32(aO[kb][0], aO[kb][1], aV[kb][0], aV[kb][1], p);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * lg + e;
-        const T x = (T)(lr <= r ? p[e] : 0.f);
+        const T x = (T)(lr < r ? p[e] : 0.f);
         sm.dAqk[pb][r][lr] = x;
         sm.dAqkT[pb][lr][r] = x;
+        if (lr == r) sm.dAd[pb][r] = p[e];
       }
     } else if (w == 1) {
       // dAkk = -StrictTril(dY V~^T); A~ = Kl Kd^T over all channels; dbeta
@@ -915,8 +924,9 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float Kt = kk[e] * et[e];
-      dq[e] = sc * (dQg[e] * gam[e] + dQl[e] * el[e]);
-      dk[e] = dKg[e] * gam[e] + dKt[e] * et[e] + dKl[e] * el[e] + dKd[e] * ed[e];
+      const float dd = sm.dAd[pb][4 * lg + e];  // dAqk[t, t]
+      dq[e] = sc * (dQg[e] * gam[e] + dQl[e] * el[e] + dd * kk[e]);
+      dk[e] = dKg[e] * gam[e] + dKt[e] * et[e] + dKl[e] * el[e] + dKd[e] * ed[e] + dd * qq[e];
       dG[e] = dQg[e] * Qg[e] + dKg[e] * Kg[e] - dKt[e] * Kt + dQl[e] * Ql[e] + dKl[e] * Kl[e] -
               dKd[e] * Kd[e];
       tsum += dKt[e] * Kt;

@@ -221,13 +221,17 @@ def tile_backward(q, k, v, g, beta, S0, do, dST, tile=16, scale=1.0):
         dbeta[a:b] = np.sum(dY * U, axis=1) + np.sum(dA * p["At"], axis=1)
         dv[a:b] = bt[:, None] * dY
         dAt = bt[:, None] * dA
+        # the diagonal Aqk[t, t] = scale q_t . k_t has no decay factor: its
+        # gradient goes to q and k directly and never enters dG
+        dAd = np.diag(dAqk).copy()
+        dAqk = np.tril(dAqk, -1)
         dQl = dAqk @ p["Kd"]
         dKl = dAt @ p["Kd"]
         dKd = dAqk.T @ p["Ql"] + dAt.T @ p["Kl"]
         G, rho = p["G"], p["rho"]
-        dq[a:b] = scale * (dQg * p["Gam"] + dQl * np.exp(G - rho))
+        dq[a:b] = scale * (dQg * p["Gam"] + dQl * np.exp(G - rho) + dAd[:, None] * k[a:b])
         dk[a:b] = (dKg * p["Gam"] + dKt * np.exp(G[L - 1] - G) + dKl * np.exp(G - rho)
-                   + dKd * np.exp(rho - G))
+                   + dKd * np.exp(rho - G) + dAd[:, None] * scale * q[a:b])
         dG = (dQg * p["Qg"] + dKg * p["Kg"] - dKt * p["Kt"] + dQl * p["Ql"] + dKl * p["Kl"]
               - dKd * p["Kd"])
         dG[L - 1] += np.sum(dKt * p["Kt"], axis=0) + dGL * p["GL"]

@@ -39,21 +39,24 @@ def _cotangents(d, N, seed):
 
 
 def _run(name, B, T, H, Dk, Dv, dtype, lengths=None, gate="logits", h0_std=0.02, dh=True,
-         scale=1.0, seed=41):
+         scale=1.0, seed=41, mutate=None, A=None):
     _print_case(name)
     d = make_inputs(B, T, H, Dk, Dv, dtype, h0_std=h0_std, lengths=lengths, seed=seed)
+    if mutate is not None:
+        mutate(d)
     N = B if d["cu_seqlens"] is None else d["cu_seqlens"].numel() - 1
     do, dhT = _cotangents(d, N, seed + 1)
     if not dh:
         dhT = None
-    g64 = oracle_gate(d["z"], None, -5.0)
+    g64 = oracle_gate(d["z"], A, -5.0)
     g32 = torch.from_numpy(g64).float()
     g_in = d["z"] if gate == "logits" else g32
     ref = oracle_backward(d["q"], d["k"], d["v"], g64 if gate == "logits" else g32, d["beta"], do,
                           d["h0"], dhT, d["cu_seqlens"], scale)
     dev = lambda x: None if x is None else x.cuda()  # noqa: E731
     got = chunk_bwd(dev(d["q"]), dev(d["k"]), dev(d["v"]), dev(g_in), dev(d["beta"]), dev(do),
-                    dev(d["h0"]), dev(dhT), dev(d["cu_seqlens"]), gate=gate, scale=scale)
+                    dev(d["h0"]), dev(dhT), dev(d["cu_seqlens"]), gate=gate, scale=scale,
+                    A_log=dev(A) if gate == "logits" else None)
     torch.cuda.synchronize()
     tol = TOL_FP32 if dtype == torch.float32 else TOL_BF16
     errs = {n: rel_err(got[n], ref[n]) for n in NAMES}
@@ -151,3 +154,55 @@ def test_bwd_bf16_varlen_long_mixed():
     and final-state gradient, every unit checked against the oracle."""
     _run("bf16 d=128 varlen long mixed", 1, 0, 3, 128, 128, torch.bfloat16,
          lengths=[4096, 1, 700, 64, 2049, 129], gate="logits", h0_std=0.02, seed=45)
+
+
+def _stress(kind):
+    def mutate(d):
+        if kind == "g_min_everywhere":
+            d["z"] = torch.full_like(d["z"], 40.0)        # sigmoid -> 1, g = g_min
+        elif kind == "g_zero":
+            d["z"] = torch.full_like(d["z"], -200.0)      # sigmoid -> 0, g = 0
+        elif kind == "beta_zero":
+            d["beta"] = torch.zeros_like(d["beta"])
+        elif kind == "beta_one":
+            d["beta"] = torch.ones_like(d["beta"])
+        elif kind == "identical_keys":
+            d["k"] = d["k"][:, :1].expand_as(d["k"]).contiguous()
+        elif kind == "large_values":
+            d["v"] = (d["v"].float() * 100).to(d["v"].dtype)
+    return mutate
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)])
+@pytest.mark.parametrize("stress", ["g_min_everywhere", "g_zero", "beta_zero", "beta_one",
+                                    "identical_keys", "large_values"])
+def test_bwd_numeric_stress(dtype, D, stress):
+    """The forward's extreme cases, differentiated: the gate's lower bound on
+    every token (largest in-tile decay ratios), no decay, no writes (beta = 0:
+    the gradient w.r.t. beta is still nonzero), full writes, identical keys
+    (rank-one key-key matrix) and large values."""
+    _run(f"stress {stress} {dtype} D={D}", 1, 150, 2, D, D, dtype, mutate=_stress(stress), seed=46)
+
+
+def test_bwd_many_short_sequences():
+    """200 packed sequences of 1 to 40 tokens (most shorter than one 64-token
+    checkpoint chunk, so slots outnumber chunks), with a learned gate scale
+    A_log, an output scale and an initial state."""
+    gen = torch.Generator().manual_seed(47)
+    lengths = torch.randint(1, 41, (200,), generator=gen).tolist()
+    A = torch.randn(2, generator=gen) * 0.5
+    _run("bf16 d=128 200 short sequences, A_log, scale 0.5", 1, 0, 2, 128, 128, torch.bfloat16,
+         lengths=lengths, scale=0.5, A=A, seed=48)
+
+
+def test_bwd_deterministic():
+    """Two calls on the same inputs give bitwise-equal gradients."""
+    _print_case("backward bitwise determinism")
+    d = make_inputs(1, 0, 2, 128, 128, torch.bfloat16, h0_std=0.02, lengths=[300, 5, 129], seed=49)
+    do, dhT = _cotangents(d, 3, 50)
+    dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    outs = [chunk_bwd(dev["q"], dev["k"], dev["v"], dev["z"], dev["beta"], do.cuda(), dev["h0"],
+                      dhT.cuda(), dev["cu_seqlens"], gate="logits") for _ in range(2)]
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.equal(outs[0][n], outs[1][n]), n
