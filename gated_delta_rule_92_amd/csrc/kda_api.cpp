@@ -318,7 +318,10 @@ kda_status_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv, i
   const size_t ck = round_up((size_t)bwd_slots_bound(B, T, N, dtype) * H * Dk * Dv * e, kWorkspaceAlign);
   const size_t tok = round_up((size_t)B * T * H * Dv * e, kWorkspaceAlign);
   const size_t at = round_up((size_t)B * T * H * 16 * sizeof(float), kWorkspaceAlign);
-  *bytes = 2 * ck + 3 * tok + at;
+  // longest-first order of packed sequences for the two scans
+  const size_t ord = (B == 1 && N > 1 && N <= kda::kMaxOrderN)
+                         ? round_up(sizeof(int32_t) * (size_t)N, kWorkspaceAlign) : 0;
+  *bytes = 2 * ck + 3 * tok + at + ord;
   return KDA_SUCCESS;
 }
 
@@ -373,8 +376,15 @@ kda_status_t kda_chunk_bwd(const void* q, const void* k, const void* v, kda_dtyp
   a.ckS = ws; a.ckdS = ws + ck; a.U = ws + 2 * ck; a.Vt = ws + 2 * ck + tok;
   a.dY = ws + 2 * ck + 2 * tok;
   a.At = reinterpret_cast<float*>(ws + 2 * ck + 3 * tok);
-  return launch_status(kda::launch_chunk_bwd(a, dtype == KDA_BFLOAT16, Dk, Dv, slots,
-                                             reinterpret_cast<hipStream_t>(stream)));
+  a.order = nullptr;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (cu_seqlens && B == 1 && s.N > 1 && s.N <= kda::kMaxOrderN) {
+    const size_t at = round_up((size_t)B * T * H * 16 * sizeof(float), kWorkspaceAlign);
+    int32_t* order = reinterpret_cast<int32_t*>(ws + 2 * ck + 3 * tok + at);
+    if (kda::launch_order(cu_seqlens, s.N, order, hs) != hipSuccess) return KDA_ERROR_LAUNCH_FAILURE;
+    a.order = order;
+  }
+  return launch_status(kda::launch_chunk_bwd(a, dtype == KDA_BFLOAT16, Dk, Dv, slots, hs));
 }
 
 kda_status_t kda_gate_bwd(const float* z, const float* A_log, float g_min, const float* dg,

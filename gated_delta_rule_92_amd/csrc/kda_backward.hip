@@ -325,7 +325,7 @@ __global__ void __launch_bounds__(NTH) bwd_fwd_scan(BwdArgs a) {
   using M = Mma<T>;
   __shared__ FwdSmem<T, DK, DV> sm;
   constexpr int CKT = ckt_of<T>();
-  const int n = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int n = a.order ? a.order[blockIdx.x / a.H] : (int)(blockIdx.x / a.H), h = blockIdx.x % a.H;
   const Unit un = unit_of<BT * CKT>(a, n);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -480,7 +480,7 @@ __global__ void __launch_bounds__(NTH) bwd_rev_scan(BwdArgs a) {
   using M = Mma<T>;
   __shared__ RevSmem<T, DK, DV> sm;
   constexpr int CKT = ckt_of<T>();
-  const int n = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int n = a.order ? a.order[blockIdx.x / a.H] : (int)(blockIdx.x / a.H), h = blockIdx.x % a.H;
   const Unit un = unit_of<BT * CKT>(a, n);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -992,7 +992,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, long slots, hipStream_t stream) {
     c.A_log = a.A_log; c.g_min = a.g_min; c.beta = a.beta;
     c.h0 = a.h0; c.hT = nullptr; c.o = nullptr;
     c.seqs.cu = a.cu; c.seqs.N = a.N; c.seqs.T = a.T; c.seqs.Ttot = 0;
-    c.order = nullptr;
+    c.order = a.order;
     c.H = a.H; c.Dk = DK; c.Dv = DV; c.scale = a.scale; c.bf16 = true;
     c.ck_state = a.ckS; c.ck_u = a.U; c.ck_vt = a.Vt; c.ck_at = a.At;
     hipError_t e = launch_chunk_checkpoint(c, stream);
@@ -1007,7 +1007,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, long slots, hipStream_t stream) {
     c.A_log = a.A_log; c.g_min = a.g_min; c.beta = a.beta;
     c.h0 = a.dhT; c.hT = a.dh0; c.o = nullptr;
     c.seqs.cu = a.cu; c.seqs.N = a.N; c.seqs.T = a.T; c.seqs.Ttot = 0;
-    c.order = nullptr;
+    c.order = a.order;
     c.H = a.H; c.Dk = DK; c.Dv = DV; c.scale = a.scale; c.bf16 = true;
     c.ck_state = a.ckdS; c.ck_vt = a.dY;
     hipError_t e = launch_chunk_reverse(c, stream);

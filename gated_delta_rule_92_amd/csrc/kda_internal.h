@@ -119,6 +119,7 @@ struct BwdArgs {
   const float* beta;
   const float* h0;     // [N, H, Dk, Dv] or nullptr
   const int32_t* cu;   // packed sequences or nullptr (dense)
+  const int32_t* order;  // [N] longest-first sequence order for the scans, or nullptr
   int N, T, H;         // T: dense sequence length
   float scale;
   const void* dO;      // [Ttot, H, Dv]

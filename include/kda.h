@@ -259,8 +259,10 @@ kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v, kda
  * kda_chunk_bwd_workspace_size — bytes of device workspace kda_chunk_bwd
  * needs (256-byte aligned): two state checkpoints [slots, H, Dk, Dv], one
  * every C tokens of each sequence (C = 64 for bf16, 16 for fp32), three
- * per-token [B*T, H, Dv] arrays, all in the input dtype, and one fp32
- * [B*T, H, 16] array; slots = max(B * ceil(T/C), B*T/C + N).
+ * per-token [B*T, H, Dv] arrays, all in the input dtype, one fp32
+ * [B*T, H, 16] array, and, for packed sequences (B == 1, 1 < N <= 8192), N
+ * int32 (the longest-first order in which the scans take the sequences);
+ * slots = max(B * ceil(T/C), B*T/C + N).
  */
 kda_status_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv, int N,
                                           int chunk, kda_dtype_t dtype, size_t* bytes);

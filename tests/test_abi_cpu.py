@@ -223,6 +223,11 @@ def test_chunk_bwd_not_supported_and_workspace():
     # packed sequences: up to one ragged chunk per sequence (fp32: 16-token chunks)
     assert lib.kda_chunk_bwd_workspace_size(1, 100, 1, 64, 64, 10, 64, 0, ctypes.byref(n)) == 0
     assert n.value >= 2 * (100 // 16 + 10) * 64 * 64 * 4
+    # packed bf16 sequences: the same arrays plus the scans' longest-first
+    # order (N int32, padded to 256 bytes)
+    assert lib.kda_chunk_bwd_workspace_size(1, 1000, 2, 128, 128, 5, 64, 1, ctypes.byref(n)) == 0
+    slots = max(1000 // 64 + 5, (1000 + 63) // 64) * 2
+    assert n.value == 2 * slots * 128 * 128 * 2 + 3 * 1000 * 2 * 128 * 2 + 1000 * 2 * 16 * 4 + 256
     assert _bwd(cu=FAKE, N=0, T=0) == _lib.KDA_SUCCESS
 
 
