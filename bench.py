@@ -182,6 +182,28 @@ def copy_calibration(n_bytes: int = 1 << 30):
     log(f"copy calibration: {n_bytes} bytes read and {n_bytes} bytes written per copy")
 
 
+def copy_bandwidth(dev, n_bytes: int = 1 << 30, reps: int = 10) -> float:
+    """Rate of a plain device-to-device copy (bytes read + bytes written per
+    second, GB/s): the practical ceiling next to the spec peak."""
+    import torch
+    x = torch.empty(n_bytes // 4, dtype=torch.float32, device=dev).normal_()
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gbs = 2 * n_bytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def _timed(step, steps, warmup, dev):
     import torch
     for _ in range(warmup):
@@ -364,6 +386,9 @@ def main(argv=None):
         if rec.get("source_sha256") == kernel_source_hash() and rec.get("workload") == w.name:
             traffic = rec.get("bytes_per_launch")
 
+    copy_gbs = copy_bandwidth(dev)
+    log(f"bench: device copy {copy_gbs:.0f} GB/s; kernel at {achieved / copy_gbs:.1%} of it")
+
     cpu = None
     if not args.skip_cpu_baseline and d["cu_seqlens"] is None:
         log("bench: timing the fp64 oracle on a bounded sample (cpu_baseline)")
@@ -390,6 +415,8 @@ def main(argv=None):
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "mfma_peak_frac": flops / (kernel_ms / 1e3) / (BF16_DENSE_PEAK_TFLOPS * 1e12)
         if w.dtype_name == "bf16" else flops / (kernel_ms / 1e3) / (FP32_MATRIX_PEAK_TFLOPS * 1e12),
+        "copy_gbs": copy_gbs,
+        "frac_of_copy": achieved / copy_gbs,
         "kernel_ms": kernel_ms,
         "kernel_ms_median": launch_ms[len(launch_ms) // 2],
         "kernel_ms_min": launch_ms[0],
