@@ -16,6 +16,7 @@ the host cores on a bounded sample of the same workload.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        python bench.py --pass backward      (kda_chunk_bwd on the same workload)
        python bench.py --copy-calibration   (plain copy kernel for counter scaling)
+       python bench.py --pass decode        (one decode token per (sequence, head))
 """
 from __future__ import annotations
 
@@ -283,6 +284,81 @@ def bench_backward(args, d, w, dev):
     return 0
 
 
+def bench_decode(args, d, w, dev):
+    """One step = one kda_recurrent_step: a single token for every (sequence,
+    head) of the workload, the fp32 state updated in place. The step reads and
+    writes the whole state, so it is bound by HBM on the state bytes."""
+    import torch
+    from gated_delta_rule_92_amd import recurrent_step
+    N = d["N"]
+    if d["cu_seqlens"] is not None:
+        first = d["cu_seqlens"][:-1].long()
+        tok = lambda x: x[0, first].contiguous()  # noqa: E731  first token of each sequence
+    else:
+        tok = lambda x: x[:, 0].contiguous()  # noqa: E731
+    q, k, v, z, beta = (tok(d[n]) for n in ("q", "k", "v", "z", "beta"))
+    state = (d["h0"].clone() if d["h0"] is not None
+             else torch.zeros((N, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev))
+    o = torch.empty((N, w.H, w.Dv), dtype=w.dtype, device=dev)
+
+    def step():
+        recurrent_step(q, k, v, z, beta, state, gate="logits", g_min=w.g_min, o=o)
+
+    ms_per_step, launch_ms = _timed(step, args.steps, args.warmup, dev)
+    kernel_ms = sum(launch_ms) / args.steps
+    el = 2 if w.dtype_name == "bf16" else 4
+    units = N * w.H
+    bytes_alg = units * (2 * w.Dk * w.Dv * 4 + (2 * w.Dk + 2 * w.Dv) * el + w.Dk * 4 + 4)
+    achieved = bytes_alg / (kernel_ms / 1e3) / 1e9
+    log(f"bench: decode {args.steps} steps, event {kernel_ms * 1e3:.1f} us/step, "
+        f"{achieved:.0f} GB/s")
+    cpu = None
+    if not args.skip_cpu_baseline:
+        # the oracle's token recurrence on one token per unit from the same
+        # state, repeated for about 5 s
+        from oracle import oracle_forward
+        cores = min(os.cpu_count() or 1, 16)
+        hq, hk, hv, hz, hb = (x.cpu()[:, None] for x in (q, k, v, z, beta))
+        h0 = state.cpu()
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 5.0:
+            oracle_forward(hq, hk, hv, hz, hb, h0, None, None, w.g_min, 1.0, nthreads=cores)
+            reps += 1
+        wall = time.perf_counter() - t0
+        cpu = {"value": units * reps / wall, "unit": "tokens·heads/s", "cores": cores,
+               "kind": "oracle",
+               "sample": f"{reps} decode steps of all {units} (sequence, head) units of the "
+                         f"{w.name} workload, fp64 token recurrence, {cores} threads, "
+                         f"{wall:.1f} s wall"}
+    line = {
+        "metric": "KDA decode step tokens·heads/s (H=32,d=128,bf16)",
+        "value": units / (ms_per_step / 1e3),
+        "unit": "tokens·heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype_name,
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "decode", "sequences": N, "heads": w.H,
+                   "d_k": w.Dk, "d_v": w.Dv, "gate": "logits", "g_min": w.g_min},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "scope": "one kda_recurrent_step launch; bytes = state read and written "
+                              "once plus the token's inputs and output"},
+        "kernel_ms": kernel_ms,
+        "kernel_ms_median": launch_ms[len(launch_ms) // 2],
+        "kernel_ms_min": launch_ms[0],
+        "kernel_ms_max": launch_ms[-1],
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -300,9 +376,11 @@ def main(argv=None):
     ap.add_argument("--split", type=int, default=1,
                     help="cut every sequence into this many segments that run in parallel "
                          "(state maps + composition + re-run); 1 = the plain forward")
-    ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward",
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "decode"],
+                    default="forward",
                     help="forward: kda_chunk_fwd (the default line); backward: kda_chunk_bwd with "
-                         "seeded normal output and final-state gradients")
+                         "seeded normal output and final-state gradients; decode: one "
+                         "kda_recurrent_step for every (sequence, head)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -333,6 +411,8 @@ def main(argv=None):
 
     if args.which == "backward":
         return bench_backward(args, d, w, dev)
+    if args.which == "decode":
+        return bench_decode(args, d, w, dev)
 
     if args.epilogue != "none":
         gen = torch.Generator(device=dev).manual_seed(1)
