@@ -155,7 +155,8 @@ def test_numeric_stress(dtype, D, stress):
 # ------------------------------------------------------------ decode step ---
 
 @pytest.mark.parametrize("dtype,Dk,Dv", [(torch.bfloat16, 128, 128), (torch.float32, 64, 64),
-                                         (torch.float32, 96, 40)])
+                                         (torch.float32, 96, 40), (torch.float32, 256, 130),
+                                         (torch.bfloat16, 8, 200)])
 def test_decode_steps_match_oracle(dtype, Dk, Dv):
     _print_case(f"decode steps {dtype} Dk={Dk} Dv={Dv}")
     N, H, T = 3, 4, 6
@@ -211,7 +212,10 @@ def test_chunk_forward_equals_token_steps():
 @pytest.mark.parametrize("dtype,Dk,Dv,chunk", [(torch.float32, 32, 48, 64),
                                                (torch.bfloat16, 96, 96, 64),
                                                (torch.float32, 128, 128, 64),
-                                               (torch.bfloat16, 128, 128, 32)])
+                                               (torch.bfloat16, 128, 128, 32),
+                                               (torch.float32, 256, 64, 64),
+                                               (torch.bfloat16, 200, 130, 64),
+                                               (torch.float32, 8, 16, 64)])
 def test_token_serial_path_shapes(dtype, Dk, Dv, chunk):
     _print_case(f"token-serial path {dtype} Dk={Dk} Dv={Dv} chunk={chunk}")
     d = make_inputs(1, 0, 2, Dk, Dv, dtype, h0_std=0.02, lengths=[70, 0, 33], seed=19)
