@@ -37,15 +37,22 @@ FP32_MATRIX_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_pipe_train8k_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_92_amd", "csrc", f)
                   for f in ("kda_chunk_pipe.hip", "kda_common.h", "kda_internal.h")]
+# the backward's three kernels: the pipelined kernel's checkpoint and reverse
+# modes and the per-chunk gradient kernel
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_backward_train8k_traffic.json")
+BWD_KERNEL_SOURCES = KERNEL_SOURCES + [os.path.join(ROOT, "gated_delta_rule_92_amd", "csrc",
+                                                    "kda_backward.hip")]
 
 
 def log(msg: str):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
+    """sha256 over the kernel sources a stored counter record was taken on:
+    the record is used only while the sources are unchanged."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (sources or KERNEL_SOURCES):
         h.update(open(p, "rb").read())
     return h.hexdigest()
 
@@ -248,6 +255,12 @@ def bench_backward(args, d, w, dev):
     n_tokens = int(B * T)
     bytes_alg = backward_algorithmic_bytes(w, n_tokens, N * w.H)
     achieved = bytes_alg / (kernel_ms / 1e3) / 1e9
+    traffic = None
+    if os.path.exists(BWD_TRAFFIC_FILE):
+        rec = json.load(open(BWD_TRAFFIC_FILE))
+        if rec.get("source_sha256") == kernel_source_hash(BWD_KERNEL_SOURCES) and \
+                rec.get("workload") == w.name:
+            traffic = rec.get("bytes_per_call")
     cpu = None
     if not args.skip_cpu_baseline and d["cu_seqlens"] is None:
         log("bench: timing the fp64 oracle backward on a bounded sample (cpu_baseline)")
@@ -269,9 +282,10 @@ def bench_backward(args, d, w, dev):
                    "heads": w.H, "d_k": w.Dk, "d_v": w.Dv, "chunk": w.chunk, "gate": "logits",
                    "g_min": w.g_min, "initial_state": d["h0"] is not None, "sequences": N},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "scope": "all three backward kernels of one call (HIP events around the "
-                              "call); bytes = the minimum any backward must move",
+                              "call); bytes = the minimum any backward must move; traffic = "
+                              "FETCH_SIZE + WRITE_SIZE of the three kernels, copy-scaled",
                      "design_bytes": backward_design_bytes(w, n_tokens, N * w.H),
                      "algorithmic_bytes": bytes_alg},
         "kernel_ms": kernel_ms,
