@@ -356,6 +356,9 @@ kda_status_t kda_chunk_bwd(const void* q, const void* k, const void* v, kda_dtyp
     return KDA_ERROR_NOT_SUPPORTED;
   if (gate_input == KDA_GATE_LOGITS && g_min < kda::kMinFusedGmin) return KDA_ERROR_NOT_SUPPORTED;
   if (!kda::chunk_bwd_supported(Dk, Dv)) return KDA_ERROR_NOT_SUPPORTED;
+  // the gradient kernel's grid has one row per head (at most 65535), which
+  // also keeps its 32-bit per-lane byte offsets within a chunk below 2^32
+  if (H > 65535) return KDA_ERROR_NOT_SUPPORTED;
   size_t need = 0;
   st = kda_chunk_bwd_workspace_size(B, T, H, Dk, Dv, s.N, chunk, dtype, &need);
   if (st != KDA_SUCCESS) return st;

@@ -140,7 +140,9 @@ struct Raw<float> {
 
 // p advanced by a byte offset below 2^32. With p the same on every lane the
 // access takes a scalar base address and a 32-bit vector offset, instead of
-// 64-bit address arithmetic per lane.
+// 64-bit address arithmetic per lane. The offsets used here span at most one
+// 64-token chunk of one array: rows * H * D * 4 bytes < 64 * 65535 * 128 * 4
+// < 2^31 for the supported H <= 65535 and D <= 128.
 template <typename P>
 __device__ __forceinline__ P* byte_at(P* p, uint32_t off) {
   using B = typename std::conditional<std::is_const<P>::value, const char, char>::type;

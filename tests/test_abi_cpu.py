@@ -209,6 +209,7 @@ def test_chunk_bwd_not_supported_and_workspace():
     assert _bwd(gate=1) == _lib.KDA_ERROR_NOT_SUPPORTED          # cumsum input
     assert _bwd(gate=3) == _lib.KDA_ERROR_NOT_SUPPORTED          # unbounded gate
     assert _bwd(gate=2, g_min=-6.0) == _lib.KDA_ERROR_NOT_SUPPORTED
+    assert _bwd(H=65536) == _lib.KDA_ERROR_NOT_SUPPORTED         # one grid row per head
     assert _bwd(ws=None) == _lib.KDA_ERROR_INSUFFICIENT_WORKSPACE
     lib = _lib.load()
     n = ctypes.c_size_t(0)
