@@ -163,6 +163,13 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
   constexpr bool CKPT = MODE == kModeCheckpoint;
   constexpr bool REV = MODE == kModeReverse;
   constexpr bool LOADQ = NEEDQ || REV;
+  // Outside reverse mode the slot holds -(k e^G), so that the consumers form
+  // Y = V - (e^G K) S by accumulating onto V, and T is stored with beta folded
+  // in (T Diag(beta)), so that V~ = (T Diag(beta)) Y needs no scaling.
+  constexpr bool NEGKG = !REV;
+  // sign that turns the products with the slot's k e^G back into raw A_kk
+  // (the position-pair path forms them from the raw rows instead)
+  constexpr float kAsign = (NEGKG && !PAIR) ? -1.0f : 1.0f;
   using M = Mma<__bf16>;
   using frag = M::frag;
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
@@ -332,7 +339,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
         for (int j = 0; j < 4; ++j) {
           const float G = Gl[r][j] + off[j];
           const float E = ex2(G);
-          kg[j] = kk[j] * E;
+          kg[j] = kk[j] * (NEGKG ? -E : E);
           if constexpr (LOADQ) qg[j] = (REV ? a.scale : 1.0f) * qq[j] * E;
           if constexpr (PAIR) {
             kt[r][j] = kk[j] * ex2(gc[j] - G);  // e^{G_15 - G} <= 1; e^{-G} alone may overflow
@@ -513,16 +520,18 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
       // A = StrictTril(Diag(beta) raw) in the accumulator layout (An) and its
       // transpose (At); A_qk keeps the diagonal.
       f32x4 An, At;
+      f32x4 bcol;  // beta of rows 4g4..4g4+3
       {
         const float* bet = reinterpret_cast<const float*>(sl + sBeta);
         const float bm = bet[m];
         const f32x4 bi = *reinterpret_cast<const f32x4*>(bet + 4 * g4);
+        bcol = bi;
         f32x4 aq;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g4 + e;
-          At[e] = i < m ? bm * dk[e] : 0.f;
-          An[e] = m < i ? bi[e] * dn[e] : 0.f;
+          At[e] = i < m ? (kAsign * bm) * dk[e] : 0.f;
+          An[e] = m < i ? (kAsign * bi[e]) * dn[e] : 0.f;
           aq[e] = i <= m ? dq[e] : 0.f;
         }
         if constexpr (NEEDQ) store4(reinterpret_cast<__bf16*>(sl + sAqk) + m * TS + 4 * g4, aq);
@@ -532,7 +541,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
               make_rsrc(a.ck_at + ((size_t)t0 * H + h) * PT, (uint32_t)((L - 1) * H + 1) * PT * 4);
           f32x4 ar;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ar[e] = 4 * g4 + e < m ? dk[e] : 0.f;
+          for (int e = 0; e < 4; ++e) ar[e] = 4 * g4 + e < m ? kAsign * dk[e] : 0.f;
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, ar), rsa, m * H * PT * 4 + g4 * 16, 0, 0);
         }
         if constexpr (REV) {
@@ -566,7 +575,8 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) reinterpret_cast<__bf16*>(sl + sT)[(4 * g4 + e) * TS + m] = (__bf16)R[e];
         } else {
-          store4(reinterpret_cast<__bf16*>(sl + sT) + m * TS + 4 * g4, R);
+          // T Diag(beta): lane (m, g4) holds T[m][4g4+e], scaled by beta_{4g4+e}
+          store4(reinterpret_cast<__bf16*>(sl + sT) + m * TS + 4 * g4, R * bcol);
         }
       }
       if constexpr (REV) {
@@ -784,15 +794,28 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
           S[ct][b] = S[ct][b] * egv[ct];
         }
 
-      // Y = V - (e^G K) S ;  V~ = T (beta * Y)
+      // Y = V - (e^G K) S (accumulated onto V; the slot holds -(e^G K)
+      // outside reverse mode); reverse mode: Kt dS'
       f32x4 acc[CNTV];
 #pragma unroll
-      for (int b = 0; b < CNTV; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < CNTV; ++b) acc[b] = REV ? f32x4{0.f, 0.f, 0.f, 0.f} : vv[b];
 #pragma unroll
       for (int ks = 0; ks < PDK / 32; ++ks)
 #pragma unroll
         for (int b = 0; b < CNTV; ++b)
           acc[b] = M::k32(kgf[ks][0], kgf[ks][1], Sf[2 * ks][b], Sf[2 * ks + 1][b], acc[b]);
+      // The inter-tile part of the output, (e^G Q) S, does not depend on V~:
+      // issued here, it overlaps the V~ chain.
+      f32x4 oc[CNTV];
+      if constexpr (NEEDQ) {
+#pragma unroll
+        for (int b = 0; b < CNTV; ++b) oc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < PDK / 32; ++ks)
+#pragma unroll
+          for (int b = 0; b < CNTV; ++b)
+            oc[b] = M::k32(qgf[ks][0], qgf[ks][1], Sf[2 * ks][b], Sf[2 * ks + 1][b], oc[b]);
+      }
       if constexpr (REV) {
         // acc = Kt dS'; dV~ = acc + A_qk^T dO; dY = T^T dV~;
         // dS <- (decayed dS') + (e^G Q)^T dO - (e^G K)^T (beta dY)
@@ -812,11 +835,11 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
         signal_add(&done[slot], lane);
         continue;
       }
+      // V~ = (T Diag(beta)) Y
       frag Xf[CNTV];
 #pragma unroll
       for (int b = 0; b < CNTV; ++b) {
-        const f32x4 y = (vv[b] - acc[b]) * bb;
-        const f32x4 x = M::k16(tf, M::make(y), f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 x = M::k16n(tf, M::make(acc[b]), f32x4{0.f, 0.f, 0.f, 0.f});
         Xf[b] = M::make(x);
         if constexpr (CKPT) {
           const uint32_t rows = (uint32_t)((L - 1) * H + 1) * PDV * 2;
@@ -824,20 +847,14 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
               make_rsrc(static_cast<__bf16*>(a.ck_u) + ((size_t)t0 * H + h) * PDV, rows);
           const __amdgpu_buffer_rsrc_t rsv =
               make_rsrc(static_cast<__bf16*>(a.ck_vt) + ((size_t)t0 * H + h) * PDV, rows);
-          store_pairs(vv[b] - acc[b], rsu, ovoff2, rowo, 32 * b);
+          store_pairs(acc[b], rsu, ovoff2, rowo, 32 * b);
           store_pairs(x, rsv, ovoff2, rowo, 32 * b);
         }
       }
-      // O = A_qk V~ + (e^G Q) S
+      // O = (e^G Q) S + A_qk V~
       if (want_o) {
-        f32x4 oc[CNTV];
 #pragma unroll
-        for (int b = 0; b < CNTV; ++b) oc[b] = M::k16(aq, Xf[b], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int ks = 0; ks < PDK / 32; ++ks)
-#pragma unroll
-          for (int b = 0; b < CNTV; ++b)
-            oc[b] = M::k32(qgf[ks][0], qgf[ks][1], Sf[2 * ks][b], Sf[2 * ks + 1][b], oc[b]);
+        for (int b = 0; b < CNTV; ++b) oc[b] = M::k16(aq, Xf[b], oc[b]);
         const __amdgpu_buffer_rsrc_t rso =
             make_rsrc(o + ((size_t)t0 * H + h) * PDV, (uint32_t)((L - 1) * H + 1) * PDV * 2);
         // Each lane packs its rows (0,1) and (2,3) into bf16 pairs, adjacent
@@ -896,11 +913,12 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
                                                 2 * rowo + 32 * b, 0);
         }
       }
-      // S <- Diag(e^{G_15}) S + (K e^{G_15 - G})^T V~  (the decay is applied above)
+      // S <- Diag(e^{G_15}) S + (K e^{G_15 - G})^T V~  (the decay is applied
+      // above, so the accumulator was last written by VALU)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int b = 0; b < CNTV; ++b) S[ct][b] = M::k16(ktf[ct], Xf[b], S[ct][b]);
+        for (int b = 0; b < CNTV; ++b) S[ct][b] = M::k16n(ktf[ct], Xf[b], S[ct][b]);
       __builtin_amdgcn_s_waitcnt(0xc07f);
       signal_add(&done[slot], lane);
     }

@@ -66,14 +66,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
-// One matrix-core shape per precision. On gfx950, accumulator chains that mix
+// Matrix-core shapes. On gfx950, accumulator chains that mix
 // v_mfma_f32_16x16x32_bf16 and v_mfma_f32_16x16x16_bf16 were observed to
-// produce stale accumulator values (for example a 16x16x32 result fed as the
-// accumulator of a 16x16x16 less than five wait states later; the hardware
-// does not interlock that pair and the compiler does not pad it). The bf16
-// path therefore issues only 16x16x32: a k16 product is a 16x16x32 whose
-// second half of the contraction is zero. The fp32 path issues only
-// 16x16x4 f32.
+// produce stale accumulator values (a 16x16x32 result fed as the accumulator
+// of a 16x16x16 less than five wait states later; the hardware does not
+// interlock that pair and the compiler does not pad it). So k16 is a
+// 16x16x32 whose second half of the contraction is zero, safe in any chain;
+// k16n, the native 16x16x16, is used only where its accumulator is zero or
+// comes from VALU (the direction 16x16x16 -> 16x16x32 is interlocked). The
+// fp32 path issues only 16x16x4 f32.
 // ---------------------------------------------------------------- traits --
 // Operand storage type and the k16 / k32 products for each input precision.
 
@@ -84,12 +85,8 @@ template <>
 struct Mma<__bf16> {
   using frag = bf16x4;  // k16 fragment: 4 x bf16 = 8 bytes
   static __device__ __forceinline__ frag make(const f32x4& x) {
-    frag f;
-    f[0] = (__bf16)x[0];
-    f[1] = (__bf16)x[1];
-    f[2] = (__bf16)x[2];
-    f[3] = (__bf16)x[3];
-    return f;
+    const uint2 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+    return __builtin_bit_cast(frag, w);
   }
   static __device__ __forceinline__ frag make_neg(const f32x4& x) {
     frag f;
@@ -107,6 +104,15 @@ struct Mma<__bf16> {
     const bf16x8 a8 = {a[0], a[1], a[2], a[3], z, z, z, z};
     const bf16x8 b8 = {b[0], b[1], b[2], b[3], z, z, z, z};
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, c, 0, 0, 0);
+  }
+  // The same K = 16 product on the native 16x16x16 instruction (lane group
+  // g = lane / 16 holds k = 4g..4g+3, the grouping k32 uses for each of its
+  // halves), which needs no zero-padded operand copies. Only for an
+  // accumulator that is zero or was last written by VALU or by another k16n:
+  // a 16x16x32 result read as its accumulator is the unpadded hazard above.
+  static __device__ __forceinline__ f32x4 k16n(const frag& a, const frag& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ f32x4 k32(const frag& a0, const frag& a1, const frag& b0,
                                               const frag& b1, f32x4 c) {
