@@ -56,10 +56,12 @@ constexpr int CNTV = CCOLS / 16;    // 16-column tiles per consumer
 constexpr int kSpinLimit = 1 << 15;
 
 // LDS row strides (elements). Matrix-core fragments are read as 8 bytes per
-// lane from 16 rows; the padding spreads the 16 rows of a half-wavefront over
-// all 64 banks (an unpadded 256-byte row stride puts them in the same two).
-constexpr int RS = PDK + 8;  // token-major [16][128] bf16 arrays
-constexpr int TS = PT + 8;   // token-contiguous [*][16] bf16 arrays
+// lane from 16 rows, 16 lanes per LDS cycle over 32 four-byte banks. A row
+// stride of 2 x odd dwords puts those 16 rows on 16 distinct bank pairs (an
+// unpadded 256-byte row stride puts them all on the same pair). Rows are
+// then 8-byte but not 16-byte aligned, so rows are written 8 bytes at a time.
+constexpr int RS = PDK + 4;  // token-major [16][128] bf16 arrays: 66 dwords
+constexpr int TS = PT + 12;  // token-contiguous [*][16] bf16 arrays: 14 dwords
 // Slot layout (bytes). bf16 unless noted.
 // (reverse mode: sKg holds k e^{G15-G} row-major, sQg (k e^{G})^T, sKtT
 // (q e^{G})^T, sVT dO^T, sT T^T and sAqk A_qk^T)
@@ -79,6 +81,7 @@ constexpr int pKd = 0;                      // k e^{-G}     [16][RS] bf16
 constexpr int kPrivBytes = pKd + PT * RS * 2;
 constexpr int kLdsBytes = NSLOT * kSlotBytes + NPROD * kPrivBytes + (3 * NSLOT + 1) * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+static_assert(sT - sKtT >= PT * PDK * 4 + PT * PDK * 2, "position-pair scratch fits in KtT and VT");
 
 __device__ __forceinline__ float ex2(float x) { return fast_exp2(x); }
 
@@ -111,6 +114,12 @@ __device__ __forceinline__ void signal_set(int* p, int value) {
 __device__ __forceinline__ void signal_add(int* p, int lane) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   if (lane == 0) __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// 16 bytes to an 8-byte-aligned LDS address, as two 8-byte writes
+__device__ __forceinline__ void st8x2(char* p, const uint32_t (&w)[4]) {
+  reinterpret_cast<uint2*>(p)[0] = uint2{w[0], w[1]};
+  reinterpret_cast<uint2*>(p)[1] = uint2{w[2], w[3]};
 }
 
 __device__ __forceinline__ uint32_t perm_lo16(uint32_t a, uint32_t b) {
@@ -383,9 +392,9 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
             u[r / 2] = (j & 1) ? perm_hi16(a0, a1) : perm_lo16(a0, a1);
           }
         }
-        *reinterpret_cast<uint4*>(sl + sKtT + (c * TS + r0) * 2) = uint4{w[0], w[1], w[2], w[3]};
+        st8x2(sl + sKtT + (c * TS + r0) * 2, w);
         if constexpr (!TRANS)
-          *reinterpret_cast<uint4*>(sl + sVT + (c * TS + r0) * 2) = uint4{u[0], u[1], u[2], u[3]};
+          st8x2(sl + sVT + (c * TS + r0) * 2, u);
       }
       };
       if (lane < PT) reinterpret_cast<float*>(sl + sBeta)[lane] = rb;
@@ -613,9 +622,9 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
             wq[r / 2] = (j & 1) ? perm_hi16(q0, q1) : perm_lo16(q0, q1);
             u[r / 2] = (j & 1) ? perm_hi16(a0, a1) : perm_lo16(a0, a1);
           }
-          *reinterpret_cast<uint4*>(sl + sQg + (c * TS + r0) * 2) = uint4{wk[0], wk[1], wk[2], wk[3]};
-          *reinterpret_cast<uint4*>(sl + sKtT + (c * TS + r0) * 2) = uint4{wq[0], wq[1], wq[2], wq[3]};
-          *reinterpret_cast<uint4*>(sl + sVT + (c * TS + r0) * 2) = uint4{u[0], u[1], u[2], u[3]};
+          st8x2(sl + sQg + (c * TS + r0) * 2, wk);
+          st8x2(sl + sKtT + (c * TS + r0) * 2, wq);
+          st8x2(sl + sVT + (c * TS + r0) * 2, u);
         }
         if (step + NPROD < nsteps) load_tile(step + NPROD);
       }
