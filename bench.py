@@ -469,6 +469,13 @@ def main(argv=None):
     kernel_ms = sum(launch_ms) / args.steps
     log(f"bench: {args.steps} steps, wall {ms_per_step:.3f} ms/step, event {kernel_ms:.3f} ms/launch")
 
+    # pieces of the context split kda_chunk_fwd took by itself for long dense
+    # sequences (its workspace then opens with the piece table 0, Lp, 2 Lp ...)
+    segments = args.split
+    if args.split == 1 and args.epilogue == "none" and d["cu_seqlens"] is None and ws >= 256:
+        lp = int(workspace[4:8].view(torch.int32).item())
+        if lp > 0:
+            segments = -(-w.T // lp)
     tok_heads = n_tokens * w.H
     value = tok_heads / (ms_per_step / 1e3)
     bytes_alg = algorithmic_bytes(w, n_tokens, N * w.H, d["h0"] is not None)
@@ -504,7 +511,7 @@ def main(argv=None):
         "config": {"workload": w.name, "batch": int(d["q"].shape[0]), "seq_len": w.T, "heads": w.H,
                    "d_k": w.Dk, "d_v": w.Dv, "chunk": w.chunk, "gate": args.gate,
                    "g_min": w.g_min, "initial_state": d["h0"] is not None,
-                   "sequences": N, "segments": args.split, "epilogue": args.epilogue},
+                   "sequences": N, "segments": segments, "epilogue": args.epilogue},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "mfma_peak_frac": flops / (kernel_ms / 1e3) / (BF16_DENSE_PEAK_TFLOPS * 1e12)

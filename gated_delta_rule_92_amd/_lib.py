@@ -26,7 +26,8 @@ KDA_GATE_SOFTPLUS = 3
 
 # Every symbol include/kda.h declares.
 EXPORTED = ("kda_status_string", "kda_version", "kda_gate", "kda_chunk_fwd_workspace_size",
-            "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_gated_rmsnorm", "kda_chunk_transition",
+            "kda_chunk_fwd", "kda_chunk_fwd_split_workspace_size", "kda_chunk_fwd_split",
+            "kda_chunk_fwd_gated", "kda_gated_rmsnorm", "kda_chunk_transition",
             "kda_compose_states", "kda_recurrent_step", "kda_chunk_bwd_workspace_size",
             "kda_chunk_bwd", "kda_gate_bwd")
 
@@ -66,6 +67,13 @@ def load(path: str = LIB_PATH):
     lib.kda_chunk_fwd_gated.restype = i32
     lib.kda_gated_rmsnorm.argtypes = [vp, vp, i32, fp, f32, ctypes.c_long, i32, vp, vp]
     lib.kda_gated_rmsnorm.restype = i32
+    lib.kda_chunk_fwd_split_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
+                                                       ctypes.POINTER(sz)]
+    lib.kda_chunk_fwd_split_workspace_size.restype = i32
+    lib.kda_chunk_fwd_split.argtypes = [vp, vp, vp, i32, fp, i32, fp, f32, fp, fp,
+                                        i32, i32, i32, i32, i32, i32, i32,  # B T H Dk Dv chunk segs
+                                        f32, vp, fp, vp, sz, vp]
+    lib.kda_chunk_fwd_split.restype = i32
     lib.kda_chunk_transition.argtypes = [vp, i32, fp, i32, fp, f32, fp, ip,
                                          i32, i32, i32, i32, i32, i32,  # N B T H Dk chunk
                                          fp, vp, sz, vp]

@@ -43,7 +43,63 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
                             const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
                             int Dv, int chunk, float scale, void* o, float* final_state,
                             void* workspace, size_t workspace_bytes, kda_stream_t stream,
-                            const void* og, const float* onw, float oeps);
+                            const void* og, const float* onw, float oeps, int segments);
+
+// Workspace of the longest-first order of packed sequences (cu_seqlens only).
+size_t order_bytes(int B, int N) {
+  return (B == 1 && N > 1 && N <= kda::kMaxOrderN) ? round_up(sizeof(int32_t) * (size_t)N, kWorkspaceAlign)
+                                                  : 0;
+}
+
+// Context split of dense sequences on one GPU: each of the B sequences is cut
+// into P consecutive pieces of Lp tokens (a multiple of the chunk; the last
+// piece takes the rest). The pieces run in parallel, first for their state
+// maps and zero-start final states, then, after the entry states are chained,
+// for the output. The state recurrence is linear in the state, so this equals
+// the unsplit forward up to rounding.
+struct SplitPlan {
+  int P = 1;
+  int Lp = 0;
+  size_t M = 0, b = 0, starts = 0, bytes = 0;  // workspace offsets; the piece table is at 0
+};
+
+SplitPlan split_layout(int B, int T, int H, int Dk, int Dv, int P, int chunk) {
+  SplitPlan p;
+  if (P < 2 || T <= 0 || (long)B * T > 0x7fffffffL) return p;
+  p.P = P;
+  p.Lp = (int)round_up((size_t)((T + P - 1) / P), (size_t)chunk);
+  const size_t pieces = (size_t)B * P;
+  p.M = round_up(sizeof(int32_t) * (pieces + 1), kWorkspaceAlign);
+  p.b = p.M + round_up(pieces * H * Dk * Dk * sizeof(float), kWorkspaceAlign);
+  p.starts = p.b + round_up(pieces * H * Dk * Dv * sizeof(float), kWorkspaceAlign);
+  p.bytes = p.starts + round_up(pieces * H * Dk * Dv * sizeof(float), kWorkspaceAlign);
+  return p;
+}
+
+// The split kda_chunk_fwd takes by itself: dense sequences of at least
+// 2 * kSplitMinPiece tokens whose (sequence, head) units fill at most half of
+// the device's compute units (each unit is one serial chain on one CU).
+constexpr int kSplitMinPiece = 4096;
+constexpr int kSplitMaxPieces = 64;
+
+int device_compute_units() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
+SplitPlan auto_split(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype_t dtype) {
+  if (!kda::chunk_pipe_supported(dtype == KDA_BFLOAT16, Dk, Dv, chunk)) return SplitPlan{};
+  const long units = (long)B * H;
+  if (T < 2 * kSplitMinPiece) return SplitPlan{};
+  const int cus = device_compute_units();
+  if (cus <= 0 || 2 * units > cus) return SplitPlan{};
+  long P = cus / units;
+  if (P > T / kSplitMinPiece) P = T / kSplitMinPiece;
+  if (P > kSplitMaxPieces) P = kSplitMaxPieces;
+  return split_layout(B, T, H, Dk, Dv, (int)P, chunk);
+}
 
 }  // namespace
 
@@ -82,10 +138,20 @@ kda_status_t kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, i
   if (!bytes || B <= 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || N < 0 || chunk <= 0)
     return KDA_ERROR_INVALID_VALUE;
   if (dtype != KDA_FLOAT32 && dtype != KDA_BFLOAT16) return KDA_ERROR_INVALID_VALUE;
-  // Longest-first order of packed sequences (used only with cu_seqlens).
-  size_t need = 0;
-  if (B == 1 && N > 1 && N <= kda::kMaxOrderN) need += round_up(sizeof(int32_t) * (size_t)N, kWorkspaceAlign);
-  *bytes = need;
+  // Longest-first order of packed sequences (used only with cu_seqlens), or
+  // the context split of long dense sequences with few units.
+  const size_t order = order_bytes(B, N);
+  const size_t split = N == B ? auto_split(B, T, H, Dk, Dv, chunk, dtype).bytes : 0;
+  *bytes = order > split ? order : split;
+  return KDA_SUCCESS;
+}
+
+kda_status_t kda_chunk_fwd_split_workspace_size(int B, int T, int H, int Dk, int Dv, int segments,
+                                                int chunk, kda_dtype_t dtype, size_t* bytes) {
+  if (!bytes || B <= 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || segments <= 0 || chunk <= 0)
+    return KDA_ERROR_INVALID_VALUE;
+  if (dtype != KDA_FLOAT32 && dtype != KDA_BFLOAT16) return KDA_ERROR_INVALID_VALUE;
+  *bytes = split_layout(B, T, H, Dk, Dv, segments, chunk).bytes;
   return KDA_SUCCESS;
 }
 
@@ -97,7 +163,26 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtyp
                            void* workspace, size_t workspace_bytes, kda_stream_t stream) {
   return chunk_fwd_impl(q, k, v, dtype, g, gate_input, A_log, g_min, beta, initial_state,
                         cu_seqlens, N, B, T, H, Dk, Dv, chunk, scale, o, final_state, workspace,
-                        workspace_bytes, stream, nullptr, nullptr, 0.f);
+                        workspace_bytes, stream, nullptr, nullptr, 0.f, 0);
+}
+
+kda_status_t kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                                 const float* g, kda_gate_input_t gate_input, const float* A_log,
+                                 float g_min, const float* beta, const float* initial_state,
+                                 int B, int T, int H, int Dk, int Dv, int chunk, int segments,
+                                 float scale, void* o, float* final_state, void* workspace,
+                                 size_t workspace_bytes, kda_stream_t stream) {
+  if (segments <= 0) return KDA_ERROR_INVALID_VALUE;
+  if (!o) return KDA_ERROR_INVALID_VALUE;
+  if (segments > 1 && !kda::chunk_pipe_supported(dtype == KDA_BFLOAT16, Dk, Dv, chunk))
+    return KDA_ERROR_NOT_SUPPORTED;
+  if (segments > 1 && (gate_input == KDA_GATE_SOFTPLUS ||
+                       (gate_input == KDA_GATE_LOGITS && g_min < kda::kMinFusedGmin)))
+    return KDA_ERROR_NOT_SUPPORTED;
+  if ((long)B * T > 0x7fffffffL) return KDA_ERROR_NOT_SUPPORTED;
+  return chunk_fwd_impl(q, k, v, dtype, g, gate_input, A_log, g_min, beta, initial_state, nullptr,
+                        B, B, T, H, Dk, Dv, chunk, scale, o, final_state, workspace,
+                        workspace_bytes, stream, nullptr, nullptr, 0.f, segments);
 }
 
 kda_status_t kda_chunk_fwd_gated(const void* q, const void* k, const void* v, kda_dtype_t dtype,
@@ -112,7 +197,7 @@ kda_status_t kda_chunk_fwd_gated(const void* q, const void* k, const void* v, kd
   if (Dv > 512) return KDA_ERROR_NOT_SUPPORTED;
   return chunk_fwd_impl(q, k, v, dtype, g, gate_input, A_log, g_min, beta, initial_state,
                         cu_seqlens, N, B, T, H, Dk, Dv, chunk, scale, y, final_state, workspace,
-                        workspace_bytes, stream, out_gate, norm_weight, eps);
+                        workspace_bytes, stream, out_gate, norm_weight, eps, 0);
 }
 
 kda_status_t kda_gated_rmsnorm(const void* o, const void* gate, kda_dtype_t dtype,
@@ -136,7 +221,7 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
                             const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
                             int Dv, int chunk, float scale, void* o, float* final_state,
                             void* workspace, size_t workspace_bytes, kda_stream_t stream,
-                            const void* og, const float* onw, float oeps) {
+                            const void* og, const float* onw, float oeps, int segments) {
   kda::Seqs s;
   kda_status_t st = check_seqs(cu_seqlens, N, B, T, &s);
   if (st != KDA_SUCCESS) return st;
@@ -168,13 +253,66 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
     if (Dk > 256) return KDA_ERROR_NOT_SUPPORTED;
     if (gate_input == KDA_GATE_CUMSUM) return KDA_ERROR_NOT_SUPPORTED;
   }
-  size_t need = 0;
-  st = kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, s.N, chunk, dtype, &need);
-  if (st != KDA_SUCCESS) return st;
+  // Explicit split (segments > 0): its workspace is required. Otherwise the
+  // split is taken when it applies and the workspace holds it; only the
+  // order array of packed sequences is required.
+  SplitPlan split;
+  if (segments > 0) {
+    split = split_layout(B, T, H, Dk, Dv, segments, chunk);
+    if (split.P > 1 && (!workspace || workspace_bytes < split.bytes))
+      return KDA_ERROR_INSUFFICIENT_WORKSPACE;
+  } else if (!cu_seqlens && o && fused && !softplus && workspace) {
+    split = auto_split(B, T, H, Dk, Dv, chunk, dtype);
+    if (workspace_bytes < split.bytes) split = SplitPlan{};
+  }
+  const size_t need = order_bytes(B, s.N);
   if (workspace && workspace_bytes < need) return KDA_ERROR_INSUFFICIENT_WORKSPACE;
   if (s.N == 0) return KDA_SUCCESS;
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (split.P > 1) {
+    // 1. piece table; 2. per piece its state map M and its zero-start final
+    // state b; 3. entry states chained per sequence; 4. every piece from its
+    // entry state, with output; 5. each sequence's final state = its last
+    // piece's.
+    char* ws = static_cast<char*>(workspace);
+    int32_t* cu = reinterpret_cast<int32_t*>(ws);
+    float* M = reinterpret_cast<float*>(ws + split.M);
+    float* bst = reinterpret_cast<float*>(ws + split.b);
+    float* starts = reinterpret_cast<float*>(ws + split.starts);
+    const int P = split.P;
+    hipError_t e = kda::launch_split_pieces(cu, B, T, P, split.Lp, hs);
+    kda::ChunkArgs a;
+    a.k = k; a.g = g; a.gate_mode = (int)gate_input;
+    a.A_log = A_log; a.g_min = g_min; a.beta = beta;
+    a.seqs.cu = cu; a.seqs.N = B * P; a.seqs.T = T; a.seqs.Ttot = (long)B * T;
+    a.order = nullptr;
+    a.H = H; a.Dk = Dk; a.Dv = Dv; a.scale = scale; a.bf16 = bf16;
+    if (e == hipSuccess) {
+      kda::ChunkArgs t = a;  // state maps: v = 0 from S = I
+      t.q = nullptr; t.v = nullptr; t.o = nullptr; t.h0 = nullptr; t.hT = M; t.Dv = Dk;
+      t.scale = 1.0f;
+      e = kda::launch_chunk_transition(t, hs);
+    }
+    if (e == hipSuccess) {
+      kda::ChunkArgs z = a;  // zero-start final states, no output
+      z.q = nullptr; z.v = v; z.o = nullptr; z.h0 = nullptr; z.hT = bst;
+      e = kda::launch_chunk_pipe(z, hs);
+    }
+    if (e == hipSuccess) e = kda::launch_compose(M, bst, initial_state, B, P, H, Dk, Dv, starts, hs);
+    if (e == hipSuccess) {
+      kda::ChunkArgs f = a;  // the output, each piece from its entry state
+      f.q = q; f.v = v; f.o = o; f.h0 = starts; f.hT = final_state ? bst : nullptr;
+      f.og = og; f.onw = onw; f.oeps = oeps;
+      e = kda::launch_chunk_pipe(f, hs);
+    }
+    if (e == hipSuccess && final_state) {
+      const size_t st_bytes = (size_t)H * Dk * Dv * sizeof(float);
+      e = hipMemcpy2DAsync(final_state, st_bytes, bst + (size_t)(P - 1) * H * Dk * Dv,
+                           (size_t)P * st_bytes, st_bytes, (size_t)B, hipMemcpyDeviceToDevice, hs);
+    }
+    return launch_status(e);
+  }
   if (fused) {
     kda::ChunkArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.gate_mode = (int)gate_input;
@@ -236,9 +374,7 @@ kda_status_t kda_chunk_transition(const void* k, kda_dtype_t dtype, const float*
   if (!kda::chunk_pipe_supported(bf16, Dk, Dk, chunk)) return KDA_ERROR_NOT_SUPPORTED;
   if (gate_input == KDA_GATE_SOFTPLUS) return KDA_ERROR_NOT_SUPPORTED;
   if (gate_input == KDA_GATE_LOGITS && g_min < kda::kMinFusedGmin) return KDA_ERROR_NOT_SUPPORTED;
-  size_t need = 0;
-  st = kda_chunk_fwd_workspace_size(B, T, H, Dk, Dk, s.N, chunk, dtype, &need);
-  if (st != KDA_SUCCESS) return st;
+  const size_t need = order_bytes(B, s.N);
   if (workspace && workspace_bytes < need) return KDA_ERROR_INSUFFICIENT_WORKSPACE;
   if (s.N == 0) return KDA_SUCCESS;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);

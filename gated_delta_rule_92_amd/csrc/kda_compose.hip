@@ -70,7 +70,29 @@ __global__ void __launch_bounds__(kComposeThreads) compose_kernel(const float* _
   }
 }
 
+// Boundaries of the pieces of a context split: B dense sequences of T tokens,
+// each cut into P consecutive pieces of Lp tokens (the last may be shorter).
+// cu[s*P + p] = s*T + min(p*Lp, T), cu[B*P] = B*T.
+__global__ void split_pieces_kernel(int32_t* __restrict__ cu, int B, int T, int P, int Lp) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int n = B * P;
+  if (i > n) return;
+  if (i == n) {
+    cu[i] = B * T;
+    return;
+  }
+  const int s = i / P, p = i - s * P;
+  cu[i] = s * T + min(p * Lp, T);
+}
+
 }  // namespace
+
+hipError_t launch_split_pieces(int32_t* cu, int B, int T, int P, int Lp, hipStream_t stream) {
+  const int n = B * P + 1;
+  hipLaunchKernelGGL(split_pieces_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     cu, B, T, P, Lp);
+  return hipGetLastError();
+}
 
 hipError_t launch_compose(const float* M, const float* b, const float* S0, int nseq, int P, int H,
                           int Dk, int Dv, float* starts, hipStream_t stream) {

@@ -124,7 +124,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
         final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
     if final_state is not None:
         _need(final_state, "final_state", torch.float32, dev)
-    ws_bytes = workspace_size(B, T, H, Dk, Dv, N, chunk, dt)
+    with torch.cuda.device(dev):
+        ws_bytes = workspace_size(B, T, H, Dk, Dv, N, chunk, dt)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -311,29 +312,66 @@ def chunk_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
          state b from a zero start (kda_chunk_fwd without output);
       2. the pieces' entry states, chained per sequence (kda_compose_states);
       3. every piece again from its entry state, producing o.
-    Same results as chunk_fwd up to rounding. Returns (o, final_state), the
-    final state as a view of the last pieces' states."""
+    Same results as chunk_fwd up to rounding. Dense inputs make one
+    kda_chunk_fwd_split call, which runs these steps on the stream. Packed
+    inputs (cu_seqlens) read the sequence lengths to the host to cut the
+    pieces and make the three calls from here. Returns (o, final_state)."""
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
-    if cu_seqlens is not None:
-        lengths = [int(x) for x in torch.diff(cu_seqlens.cpu().to(torch.int64)).tolist()]
-        qq, kk, vv, gg, bb = q, k, v, g, beta
-    else:
-        lengths = [T] * B
-        qq, kk, vv = (x.reshape(1, B * T, H, x.shape[-1]) for x in (q, k, v))
-        gg, bb = g.reshape(1, B * T, H, Dk), beta.reshape(1, B * T, H)
+    if cu_seqlens is None:
+        return _chunk_fwd_split_dense(q, k, v, g, beta, initial_state, segments, gate, A_log,
+                                      g_min, chunk, scale)
+    lengths = [int(x) for x in torch.diff(cu_seqlens.cpu().to(torch.int64)).tolist()]
     nseq = len(lengths)
     pieces = split_lengths(lengths, segments, chunk)
     cu = torch.zeros(len(pieces) + 1, dtype=torch.int64)
     cu[1:] = torch.cumsum(torch.tensor(pieces, dtype=torch.int64), 0)
     cu = cu.to(torch.int32).to(q.device)
     common = dict(cu_seqlens=cu, gate=gate, A_log=A_log, g_min=g_min, chunk=chunk)
-    M = transition(kk, gg, bb, **common)
-    _, b = chunk_fwd(qq, kk, vv, gg, bb, None, output=False, scale=scale, **common)
+    M = transition(k, g, beta, **common)
+    _, b = chunk_fwd(q, k, v, g, beta, None, output=False, scale=scale, **common)
     starts = compose_states(M, b, initial_state, nseq, segments)
-    o, finals = chunk_fwd(qq, kk, vv, gg, bb, starts, scale=scale, **common)
-    o = o.reshape(q.shape[:3] + (Dv,))
+    o, finals = chunk_fwd(q, k, v, g, beta, starts, scale=scale, **common)
     return o, finals.view(nseq, segments, H, Dk, Dv)[:, segments - 1]
+
+
+def _chunk_fwd_split_dense(q, k, v, g, beta, initial_state, segments, gate, A_log, g_min, chunk,
+                           scale):
+    import ctypes
+    lib = _lib.load()
+    dev = q.device
+    dt = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, dt, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or g.shape != q.shape or \
+            beta.shape != q.shape[:3]:
+        raise ValueError("shape mismatch among q, k, v, g, beta")
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, dev)
+        if tuple(initial_state.shape) != (B, H, Dk, Dv):
+            raise ValueError("initial_state must be [B, H, Dk, Dv]")
+    if A_log is not None:
+        _need(A_log, "A_log", torch.float32, dev)
+    o = torch.empty((B, T, H, Dv), dtype=dt, device=dev)
+    final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    out = ctypes.c_size_t(0)
+    _lib.check(lib.kda_chunk_fwd_split_workspace_size(B, T, H, Dk, Dv, int(segments), int(chunk),
+                                                      _dtype_code(q), ctypes.byref(out)),
+               "kda_chunk_fwd_split_workspace_size")
+    ws_len = int(out.value)
+    workspace = torch.empty(ws_len, dtype=torch.uint8, device=dev) if ws_len > 0 else None
+    with torch.cuda.device(dev):
+        rc = lib.kda_chunk_fwd_split(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g),
+                                     _GATES[gate], _ptr(A_log), float(g_min), _ptr(beta),
+                                     _ptr(initial_state), B, T, H, Dk, Dv, int(chunk),
+                                     int(segments), float(scale), _ptr(o), _ptr(final_state),
+                                     _ptr(workspace), ws_len, _stream(dev))
+    _lib.check(rc, "kda_chunk_fwd_split")
+    return o, final_state
 
 
 def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

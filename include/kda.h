@@ -112,7 +112,13 @@ kda_status_t kda_gate(const float* z, const float* A_log, float g_min,
 
 /*
  * kda_chunk_fwd_workspace_size — bytes of device workspace kda_chunk_fwd
- * needs for these sizes (may be 0). The workspace must be 256-byte aligned.
+ * uses for these sizes (may be 0). The workspace must be 256-byte aligned.
+ * With packed sequences (B = 1, N > 1) it holds their longest-first order.
+ * For dense bf16 Dk = Dv = 128 sequences of T >= 8192 tokens whose B*H
+ * (sequence, head) units fill at most half of the current device's compute
+ * units, it holds the context split kda_chunk_fwd then takes (see there):
+ * the piece table, and per piece and head a state map and two states
+ * (B * P * H * (Dk*Dk + 2*Dk*Dv) * 4 bytes; P = min(CUs / (B*H), T / 4096, 64)).
  */
 kda_status_t kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, int N,
                                           int chunk, kda_dtype_t dtype, size_t* bytes);
@@ -141,8 +147,14 @@ kda_status_t kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, i
  *            final state is computed (final_state must then be non-NULL)
  * final_state device fp32 [N, H, Dk, Dv] or NULL (written); may alias
  *            initial_state
- * workspace  device, >= kda_chunk_fwd_workspace_size(...) bytes, or NULL
- *            when that size is 0
+ * workspace  device, >= kda_chunk_fwd_workspace_size(...) bytes, or NULL.
+ *            Required only for the order of packed sequences (N <= 8192);
+ *            without it they run in index order.
+ * Long dense sequences with few units: when the workspace holds the split
+ * kda_chunk_fwd_workspace_size sizes for (cu_seqlens NULL, o non-NULL, bf16
+ * Dk = Dv = 128, a gate other than KDA_GATE_SOFTPLUS), every sequence is cut
+ * into P chunk-aligned pieces that run in parallel, exactly as
+ * kda_chunk_fwd_split with segments = P; otherwise one serial chain per unit.
  * Supported: bf16 with Dk, Dv in {64, 128}; fp32 with Dk = Dv = 64 on the
  * matrix-core chunk path; any other Dk, Dv <= 256 (and fp32 at 128) runs a
  * token-serial kernel with the same results, as does KDA_GATE_LOGITS with
@@ -196,6 +208,39 @@ kda_status_t kda_gated_rmsnorm(const void* o, const void* gate, kda_dtype_t dtyp
                                kda_stream_t stream);
 
 /*
+ * kda_chunk_fwd_split_workspace_size — bytes of device workspace
+ * kda_chunk_fwd_split needs (0 for segments = 1).
+ */
+kda_status_t kda_chunk_fwd_split_workspace_size(int B, int T, int H, int Dk, int Dv, int segments,
+                                                int chunk, kda_dtype_t dtype, size_t* bytes);
+
+/*
+ * kda_chunk_fwd_split — kda_chunk_fwd for dense sequences with each sequence
+ * cut into `segments` consecutive pieces of Lp = 64 * ceil(ceil(T / segments)
+ * / 64) tokens (the last takes the rest; pieces may be empty) that run in
+ * parallel: the one-GPU form of a context split. The KDA equation is linear
+ * in the state [KDA-blog §Kimi Delta Attention, KDA equation], so a piece's
+ * final state is M S_entry + b with M its state map and b its zero-start final
+ * state. On the stream, in order: the piece table; M and b of every piece
+ * (kda_chunk_transition and the state-only forward); the entry states
+ * chained per sequence (kda_compose_states); every piece from its entry state
+ * with output; each sequence's final state copied from its last piece. The
+ * results equal kda_chunk_fwd's up to rounding.
+ * Arguments as for kda_chunk_fwd without cu_seqlens (N = B); o must be
+ * non-NULL. workspace: device, >= kda_chunk_fwd_split_workspace_size(...)
+ * bytes (KDA_ERROR_INSUFFICIENT_WORKSPACE otherwise).
+ * Supported for segments > 1: bf16, Dk = Dv = 128, chunk = 64, B*T < 2^31,
+ * gates other than KDA_GATE_SOFTPLUS with log-decay >= -5.5
+ * (KDA_ERROR_NOT_SUPPORTED otherwise). segments = 1 is kda_chunk_fwd.
+ */
+kda_status_t kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                                 const float* g, kda_gate_input_t gate_input, const float* A_log,
+                                 float g_min, const float* beta, const float* initial_state,
+                                 int B, int T, int H, int Dk, int Dv, int chunk, int segments,
+                                 float scale, void* o, float* final_state, void* workspace,
+                                 size_t workspace_bytes, kda_stream_t stream);
+
+/*
  * kda_chunk_transition — the state map of each (sequence, head).
  * The KDA equation is linear in the state [KDA-blog §Kimi Delta Attention,
  * KDA equation], so the state a sequence leaves behind is affine in the state
@@ -210,7 +255,7 @@ kda_status_t kda_gated_rmsnorm(const void* o, const void* gate, kda_dtype_t dtyp
  * g, gate_input, A_log, g_min, beta, cu_seqlens, N, B, T, H, chunk
  *            as for kda_chunk_fwd
  * M          device fp32 [N, H, Dk, Dk] (written), row-major per (n, h)
- * workspace  as for kda_chunk_fwd with Dv = Dk
+ * workspace  the order of packed sequences, as for kda_chunk_fwd, or NULL
  * Supported: bf16, Dk = 128, chunk = 64, per-token log-decay >= -5.5
  * (KDA_ERROR_NOT_SUPPORTED otherwise).
  */

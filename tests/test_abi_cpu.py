@@ -138,6 +138,37 @@ def test_transition_and_compose_validation():
     assert comp(nseq=0) == _lib.KDA_SUCCESS
 
 
+def test_split_forward_validation_and_workspace():
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    # piece table (B*P + 1 int32, 256-aligned), then per piece and head a
+    # Dk x Dk state map and two Dk x Dv states
+    assert lib.kda_chunk_fwd_split_workspace_size(1, 262144, 32, 128, 128, 8, 64, 1,
+                                                  ctypes.byref(n)) == 0
+    assert n.value == 256 + 3 * 8 * 32 * 128 * 128 * 4
+    assert lib.kda_chunk_fwd_split_workspace_size(2, 1000, 2, 128, 128, 1, 64, 1,
+                                                  ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.kda_chunk_fwd_split_workspace_size(2, 1000, 2, 128, 128, 0, 64, 1,
+                                                  ctypes.byref(n)) == _lib.KDA_ERROR_INVALID_VALUE
+
+    def split(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, g=FAKE, gate=2, A=None, g_min=-5.0, beta=FAKE,
+                 h0=None, B=1, T=8192, H=2, Dk=128, Dv=128, chunk=64, segments=4, scale=1.0,
+                 o=FAKE, hT=None, ws=FAKE, ws_bytes=1 << 30, stream=None)
+        a.update(kw)
+        return lib.kda_chunk_fwd_split(*a.values())
+    assert split(segments=0) == _lib.KDA_ERROR_INVALID_VALUE
+    assert split(o=None) == _lib.KDA_ERROR_INVALID_VALUE
+    assert split(q=FAKE + 4) == _lib.KDA_ERROR_INVALID_VALUE
+    assert split(dtype=0) == _lib.KDA_ERROR_NOT_SUPPORTED
+    assert split(Dk=64) == _lib.KDA_ERROR_NOT_SUPPORTED
+    assert split(gate=3) == _lib.KDA_ERROR_NOT_SUPPORTED
+    assert split(g_min=-8.0) == _lib.KDA_ERROR_NOT_SUPPORTED
+    assert split(ws=None, ws_bytes=0) == _lib.KDA_ERROR_INSUFFICIENT_WORKSPACE
+    assert split(ws_bytes=1024) == _lib.KDA_ERROR_INSUFFICIENT_WORKSPACE
+
+
 def test_epilogue_entry_points_validation():
     lib = _lib.load()
 

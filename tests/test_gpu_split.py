@@ -118,3 +118,41 @@ def test_split_long256k_full_size_sampled():
     eo, es = compare_units(got, ref)
     print(f"  units={units} err_o={eo:.3e} err_state={es:.3e} tol={TOL_BF16:g}", flush=True)
     assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_chunk_fwd_splits_long_dense_sequences_by_itself():
+    """kda_chunk_fwd on a long dense sequence with few (sequence, head) units
+    takes the context split when its workspace holds it (the size query asks
+    for it); with a workspace too small for it the same call runs one serial
+    chain per unit. Both against the unsplit oracle, and the split's final
+    state written over the initial state it started from."""
+    _print_case("automatic split: dense B=1 H=2 T=16384")
+    from gated_delta_rule_92_amd import workspace_size
+    B, T, H = 1, 16384, 2
+    ws = workspace_size(B, T, H, 128, 128, B, 64, torch.bfloat16)
+    # 2 units on >= 4 CUs: P = min(CUs / 2, T / 4096) = 4 pieces of 4096 tokens
+    assert ws == 256 + 3 * 4 * H * 128 * 128 * 4, ws
+    d = make_inputs(B, T, H, 128, 128, torch.bfloat16, h0_std=0.02, seed=34)
+    dd = to_dev(d)
+    wsp = torch.zeros(ws, dtype=torch.uint8, device="cuda")
+    o_split, hT_split = chunk_fwd(dd["q"], dd["k"], dd["v"], dd["z"], dd["beta"], dd["h0"],
+                                  gate="logits", workspace=wsp)
+    small = torch.empty(256, dtype=torch.uint8, device="cuda")
+    o_one, hT_one = chunk_fwd(dd["q"], dd["k"], dd["v"], dd["z"], dd["beta"], dd["h0"],
+                              gate="logits", workspace=small)
+    state = dd["h0"].clone()
+    o_alias, _ = chunk_fwd(dd["q"], dd["k"], dd["v"], dd["z"], dd["beta"], state, gate="logits",
+                           final_state=state)
+    torch.cuda.synchronize()
+    ref = oracle_forward(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"], None, None, -5.0)
+    for name, o, hT in (("split", o_split, hT_split), ("one chain", o_one, hT_one),
+                        ("split, final state over initial", o_alias, state)):
+        eo, es = rel_err(o, ref[0]), rel_err(hT, ref[1])
+        print(f"  {name}: err_o={eo:.3e} err_state={es:.3e} tol={TOL_BF16:g}", flush=True)
+        assert eo <= TOL_BF16 and es <= TOL_BF16
+    # the split ran: its piece table opens the workspace
+    assert wsp[:20].view(torch.int32).cpu().tolist() == [0, 4096, 8192, 12288, 16384]
+    # With this gate a piece's state map underflows to zero within a few
+    # tiles, so every piece starts from exactly the state the unsplit chain
+    # has there and both paths give the same bits.
+    assert torch.equal(o_split, o_one)
