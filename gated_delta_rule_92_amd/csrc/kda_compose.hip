@@ -82,7 +82,8 @@ __global__ void split_pieces_kernel(int32_t* __restrict__ cu, int B, int T, int 
     return;
   }
   const int s = i / P, p = i - s * P;
-  cu[i] = s * T + min(p * Lp, T);
+  const long start = (long)p * Lp < (long)T ? (long)p * Lp : (long)T;
+  cu[i] = (int32_t)((long)s * T + start);
 }
 
 }  // namespace
