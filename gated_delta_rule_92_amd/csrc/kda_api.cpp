@@ -76,10 +76,14 @@ SplitPlan split_layout(int B, int T, int H, int Dk, int Dv, int P, int chunk) {
   return p;
 }
 
-// The split kda_chunk_fwd takes by itself: dense sequences of at least
-// 2 * kSplitMinPiece tokens whose (sequence, head) units fill at most half of
-// the device's compute units (each unit is one serial chain on one CU).
-constexpr int kSplitMinPiece = 4096;
+// The split kda_chunk_fwd takes by itself, for dense sequences whose B*H
+// (sequence, head) units leave compute units idle (each unit is one serial
+// chain of 16-token tiles on one CU, about a microsecond per tile):
+// P = min(CUs / units, T / kSplitMinPiece, kSplitMaxPieces) pieces, taken when
+// P >= 4 and its three passes over T / P tokens plus about 20 us of fixed
+// cost (piece table, composition, launches) beat one pass over T by 10%:
+// T (0.9 - 3 / P) > 300 tile-microseconds' worth of tokens.
+constexpr int kSplitMinPiece = 256;
 constexpr int kSplitMaxPieces = 64;
 
 int device_compute_units() {
@@ -92,12 +96,12 @@ int device_compute_units() {
 SplitPlan auto_split(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype_t dtype) {
   if (!kda::chunk_pipe_supported(dtype == KDA_BFLOAT16, Dk, Dv, chunk)) return SplitPlan{};
   const long units = (long)B * H;
-  if (T < 2 * kSplitMinPiece) return SplitPlan{};
   const int cus = device_compute_units();
-  if (cus <= 0 || 2 * units > cus) return SplitPlan{};
+  if (cus <= 0 || units <= 0) return SplitPlan{};
   long P = cus / units;
   if (P > T / kSplitMinPiece) P = T / kSplitMinPiece;
   if (P > kSplitMaxPieces) P = kSplitMaxPieces;
+  if (P < 4 || (long)T * (9 * P - 30) <= 3000 * P) return SplitPlan{};
   return split_layout(B, T, H, Dk, Dv, (int)P, chunk);
 }
 
@@ -400,6 +404,7 @@ kda_status_t kda_compose_states(const float* M, const float* b, const float* ini
   if (nseq > 0 && P > 0 && (!starts || (P > 1 && (!M || !b)))) return KDA_ERROR_INVALID_VALUE;
   if (Dk > 256) return KDA_ERROR_NOT_SUPPORTED;
   if ((size_t)nseq * P * H > (size_t)0x7fffffff) return KDA_ERROR_INVALID_VALUE;
+  if (!aligned16(M)) return KDA_ERROR_INVALID_VALUE;
   return launch_status(kda::launch_compose(M, b, initial_state, nseq, P, H, Dk, Dv, starts,
                                            reinterpret_cast<hipStream_t>(stream)));
 }

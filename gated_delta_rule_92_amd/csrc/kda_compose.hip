@@ -70,6 +70,77 @@ __global__ void __launch_bounds__(kComposeThreads) compose_kernel(const float* _
   }
 }
 
+// Dk = 128 on fp32 matrix cores: a workgroup of 8 wavefronts per (sequence,
+// head, 16 value columns); wavefront w forms rows [16w, 16w + 16) of each next
+// entry state, start_{p+1} = M_p start_p + b_p, as 32 16x16x4 products with
+// b_p as the initial accumulator. The contraction index k is split as
+// k = 32 g + kk (g = lane / 16, kk = the product's step), so that each lane
+// reads 32 consecutive entries of its row of M_p (eight 16-byte loads, issued
+// one step ahead) and 32 consecutive rows of its column of the running slice,
+// which is kept transposed in LDS.
+constexpr int kC128 = 128;
+constexpr int kCT = kC128 + 4;  // padded row of the transposed slice
+
+__global__ void __launch_bounds__(512) compose128_kernel(const float* __restrict__ M,
+                                                         const float* __restrict__ b,
+                                                         const float* __restrict__ S0, int P, int H,
+                                                         int Dv, float* __restrict__ starts) {
+  __shared__ __attribute__((aligned(16))) float curT[kComposeCols][kCT];
+  const int sh = blockIdx.x;  // sequence * H + head
+  const int seq = sh / H, h = sh % H;
+  const int c0 = blockIdx.y * kComposeCols;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int row0 = 16 * w;
+  const bool cvalid = c0 + n < Dv;
+
+  for (int i = tid; i < kComposeCols * kC128; i += 512) {
+    const int col = i % kComposeCols, row = i / kComposeCols;
+    curT[col][row] = (S0 && c0 + col < Dv) ? S0[(((size_t)seq * H + h) * kC128 + row) * Dv + c0 + col]
+                                           : 0.f;
+  }
+  // row row0 + n of M_p, entries 32g .. 32g + 31
+  auto load_m = [&](int p, f32x4 (&a)[8]) {
+    const float* Mp = M + (((size_t)seq * P + p) * H + h) * (size_t)kC128 * kC128 +
+                      (size_t)(row0 + n) * kC128 + 32 * g;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const f32x4*>(Mp + 4 * i);
+  };
+  f32x4 am[8];
+  if (P > 1) load_m(0, am);
+  __syncthreads();
+
+  for (int p = 0; p < P; ++p) {
+    const size_t sp = (size_t)seq * P + p;
+    float* out = starts + (sp * H + h) * (size_t)kC128 * Dv;
+    if (cvalid) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[(size_t)(row0 + 4 * g + e) * Dv + c0 + n] = curT[n][row0 + 4 * g + e];
+    }
+    if (p == P - 1) break;
+    const float* bp = b + (sp * H + h) * (size_t)kC128 * Dv;
+    f32x4 acc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = cvalid ? bp[(size_t)(row0 + 4 * g + e) * Dv + c0 + n] : 0.f;
+    f32x4 bc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bc[i] = *reinterpret_cast<const f32x4*>(&curT[n][32 * g + 4 * i]);
+    f32x4 an[8];
+    if (p + 1 < P - 1) load_m(p + 1, an);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(am[i][e], bc[i][e], acc, 0, 0, 0);
+    __syncthreads();  // every wavefront has read the slice
+#pragma unroll
+    for (int e = 0; e < 4; ++e) curT[n][row0 + 4 * g + e] = acc[e];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am[i] = an[i];
+    __syncthreads();
+  }
+}
+
 // Boundaries of the pieces of a context split: B dense sequences of T tokens,
 // each cut into P consecutive pieces of Lp tokens (the last may be shorter).
 // cu[s*P + p] = s*T + min(p*Lp, T), cu[B*P] = B*T.
@@ -100,6 +171,10 @@ hipError_t launch_compose(const float* M, const float* b, const float* S0, int n
   if (nseq == 0 || P == 0 || H == 0) return hipSuccess;
   if (Dk > kComposeMaxDk) return hipErrorInvalidValue;
   dim3 grid((unsigned)(nseq * H), (unsigned)((Dv + kComposeCols - 1) / kComposeCols));
+  if (Dk == kC128) {
+    hipLaunchKernelGGL(compose128_kernel, grid, dim3(512), 0, stream, M, b, S0, P, H, Dv, starts);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(compose_kernel, grid, dim3(kComposeThreads), 0, stream, M, b, S0, P, H, Dk, Dv,
                      starts);
   return hipGetLastError();

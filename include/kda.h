@@ -114,11 +114,13 @@ kda_status_t kda_gate(const float* z, const float* A_log, float g_min,
  * kda_chunk_fwd_workspace_size — bytes of device workspace kda_chunk_fwd
  * uses for these sizes (may be 0). The workspace must be 256-byte aligned.
  * With packed sequences (B = 1, N > 1) it holds their longest-first order.
- * For dense bf16 Dk = Dv = 128 sequences of T >= 8192 tokens whose B*H
- * (sequence, head) units fill at most half of the current device's compute
- * units, it holds the context split kda_chunk_fwd then takes (see there):
- * the piece table, and per piece and head a state map and two states
- * (B * P * H * (Dk*Dk + 2*Dk*Dv) * 4 bytes; P = min(CUs / (B*H), T / 4096, 64)).
+ * For dense bf16 Dk = Dv = 128 sequences whose B*H (sequence, head) units
+ * leave the current device's compute units idle, it holds the context split
+ * kda_chunk_fwd then takes (see there): the piece table, and per piece and
+ * head a state map and two states (B * P * H * (Dk*Dk + 2*Dk*Dv) * 4 bytes),
+ * with P = min(CUs / (B*H), T / 256, 64), taken when P >= 4 and
+ * T (0.9 - 3/P) > 300 (three passes over T/P tokens plus a fixed cost must
+ * beat one pass over T).
  */
 kda_status_t kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, int N,
                                           int chunk, kda_dtype_t dtype, size_t* bytes);
@@ -276,7 +278,8 @@ kda_status_t kda_chunk_transition(const void* k, kda_dtype_t dtype, const float*
  * b              device fp32 [nseq*P, H, Dk, Dv] (entries p = P-1 unused)
  * initial_state  device fp32 [nseq, H, Dk, Dv] or NULL (zeros)
  * starts         device fp32 [nseq*P, H, Dk, Dv] (written)
- * fp32 arithmetic, one workgroup per (sequence, head, 16 value columns),
+ * M must be 16-byte aligned. fp32 arithmetic (on fp32 matrix cores for
+ * Dk = 128), one workgroup per (sequence, head, 16 value columns),
  * sequential over p. Supported: Dk <= 256.
  */
 kda_status_t kda_compose_states(const float* M, const float* b, const float* initial_state,
