@@ -293,15 +293,11 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
     a.order = nullptr;
     a.H = H; a.Dk = Dk; a.Dv = Dv; a.scale = scale; a.bf16 = bf16;
     if (e == hipSuccess) {
-      kda::ChunkArgs t = a;  // state maps: v = 0 from S = I
-      t.q = nullptr; t.v = nullptr; t.o = nullptr; t.h0 = nullptr; t.hT = M; t.Dv = Dk;
-      t.scale = 1.0f;
-      e = kda::launch_chunk_transition(t, hs);
-    }
-    if (e == hipSuccess) {
-      kda::ChunkArgs z = a;  // zero-start final states, no output
-      z.q = nullptr; z.v = v; z.o = nullptr; z.h0 = nullptr; z.hT = bst;
-      e = kda::launch_chunk_pipe(z, hs);
+      // state maps (v = 0 from S = I) and zero-start final states, in one
+      // launch that reads k, v, g and beta once
+      kda::ChunkArgs z = a;
+      z.q = nullptr; z.v = v; z.o = nullptr; z.h0 = nullptr; z.hT = M; z.hT2 = bst;
+      e = kda::launch_chunk_split_pass(z, hs);
     }
     if (e == hipSuccess) e = kda::launch_compose(M, bst, initial_state, B, P, H, Dk, Dv, starts, hs);
     if (e == hipSuccess) {

@@ -143,6 +143,10 @@ __device__ __forceinline__ uint32_t perm_hi16(uint32_t a, uint32_t b) {
 //     fourth tile (every 64 tokens) is written in bf16, and per token
 //     U = V - (e^G K) S and the pseudo-values V~ (what the backward pass
 //     reads).
+//   kModeSplitPass: the first pass of a context split in one launch: the
+//     transition (written to a.hT) and the zero-start final state (written
+//     to a.hT2) of each (sequence, head), with eight consumer wavefronts
+//     (four per result) fed by the same producers (q, o, h0 unused).
 //   kModeReverse: the backward's state-gradient recurrence, tiles taken last
 //     to first (a.v holds dO, a.h0 the final-state gradient, a.hT receives
 //     the initial-state gradient):
@@ -156,12 +160,16 @@ enum {
   kModeTransition = 2,
   kModeForwardGated = 3,
   kModeCheckpoint = 4,
-  kModeReverse = 5
+  kModeReverse = 5,
+  kModeSplitPass = 6
 };
 
 template <int GATE, int MODE>
-__global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
+__global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : PNTHR, 1)
+    chunk_pipe_kernel(ChunkArgs a) {
   constexpr bool TRANS = MODE == kModeTransition;
+  constexpr bool DUAL = MODE == kModeSplitPass;
+  constexpr int ncons = DUAL ? 2 * NCONS : NCONS;  // consumer wavefronts
   // Unbounded gate (the pages' earlier -e^A softplus(z)): in-tile reciprocal
   // decay factors can overflow, so the diagonal tiles A_kk, A_qk are formed
   // position pair by position pair with e^{G_r - G_i} <= 1 (VALU) instead of
@@ -272,7 +280,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
       const long t0 = bos + (long)tile * PT;
       const int L = (int)min((long)PT, len - (long)tile * PT);
       // the slot's previous tile must have been consumed by every consumer
-      if (use > 0) wait_at_least(&done[slot], NCONS * use, abort_flag);
+      if (use > 0) wait_at_least(&done[slot], ncons * use, abort_flag);
 
       // cumulative log2-decay of this lane's rows (local to the half for the
       // incremental gate forms, absolute for the cumulative-sum form)
@@ -641,8 +649,11 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
     // The consumers carry the recurrence's serial chain; when a producer and
     // a consumer on one SIMD are both ready to issue, the consumer goes first.
     __builtin_amdgcn_s_setprio(3);
-    const int c = wave - NPROD;
+    const int c = (wave - NPROD) % NCONS;
     const int vc0 = c * CCOLS;
+    // this consumer runs the transition (v = 0 from S = I): in transition
+    // mode, and for the first four consumers of the split pass
+    const bool tmap = TRANS || (DUAL && wave - NPROD < NCONS);
     constexpr int NCT = PDK / 16;
     f32x4 S[NCT][CNTV];
     const size_t sbase = ((size_t)n * H + h) * PDK * PDV;
@@ -651,7 +662,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int b = 0; b < CNTV; ++b) S[ct][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (TRANS) {
+    if (tmap) {
       // the identity: row 16ct+4g4+e, column vc0+16b+m
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
@@ -755,7 +766,7 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
       } else {
 #pragma unroll
         for (int b = 0; b < CNTV; ++b)
-          vv[b] = TRANS ? f32x4{0.f, 0.f, 0.f, 0.f} : load4_f32(VT + (vc0 + 16 * b + m) * TS + 4 * g4);
+          vv[b] = tmap ? f32x4{0.f, 0.f, 0.f, 0.f} : load4_f32(VT + (vc0 + 16 * b + m) * TS + 4 * g4);
       }
       frag aq = {};
       if (REV) aq = load_frag(Aqk + m * TS + 4 * g4);
@@ -931,8 +942,9 @@ __global__ void __launch_bounds__(PNTHR, 1) chunk_pipe_kernel(ChunkArgs a) {
       __builtin_amdgcn_s_waitcnt(0xc07f);
       signal_add(&done[slot], lane);
     }
-    if (a.hT) {
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.hT + sbase, PDK * PDV * 4);
+    float* hT = (DUAL && !tmap) ? a.hT2 : a.hT;
+    if (hT) {
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(hT + sbase, PDK * PDV * 4);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -953,7 +965,7 @@ bool chunk_pipe_supported(bool bf16, int Dk, int Dv, int chunk) {
 
 template <int MODE>
 static void launch_pipe_t(const ChunkArgs& a, hipStream_t stream) {
-  dim3 grid((unsigned)(a.seqs.N * a.H)), block(PNTHR);
+  dim3 grid((unsigned)(a.seqs.N * a.H)), block(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : PNTHR);
   switch (a.gate_mode) {
     case kGateLogDecay:
       hipLaunchKernelGGL((chunk_pipe_kernel<kGateLogDecay, MODE>), grid, block, 0, stream, a);
@@ -992,6 +1004,12 @@ hipError_t launch_chunk_checkpoint(const ChunkArgs& a, hipStream_t stream) {
 hipError_t launch_chunk_reverse(const ChunkArgs& a, hipStream_t stream) {
   if (a.seqs.N == 0 || a.H == 0) return hipSuccess;
   launch_pipe_t<kModeReverse>(a, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_split_pass(const ChunkArgs& a, hipStream_t stream) {
+  if (a.seqs.N == 0 || a.H == 0) return hipSuccess;
+  launch_pipe_t<kModeSplitPass>(a, stream);
   return hipGetLastError();
 }
 

@@ -75,6 +75,7 @@ struct ChunkArgs {
   void* ck_u = nullptr;
   void* ck_vt = nullptr;
   float* ck_at = nullptr;  // checkpoint mode: A_kk / beta per tile row, fp32 [Ttot, H, 16]
+  float* hT2 = nullptr;    // split pass: zero-start final states [N, H, Dk, Dv]
 };
 bool chunk_fused_supported(bool bf16, int Dk, int Dv, int chunk);
 // Pipelined producer/consumer chunk kernel (bf16, Dk = Dv = 128).
@@ -83,6 +84,10 @@ hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t stream);
 // Same kernel in transition mode: writes M (a.hT, [N, H, Dk, Dk]) with
 // S_final = M S_initial + S_final(0); reads k, g and beta only.
 hipError_t launch_chunk_transition(const ChunkArgs& a, hipStream_t stream);
+// Both at once, the first pass of a context split: M to a.hT (as
+// launch_chunk_transition) and the zero-start final states to a.hT2 (as the
+// state-only forward), reading k, v, g and beta once.
+hipError_t launch_chunk_split_pass(const ChunkArgs& a, hipStream_t stream);
 // Same kernel in checkpoint mode (ck_state, ck_u, ck_vt must be set).
 hipError_t launch_chunk_checkpoint(const ChunkArgs& a, hipStream_t stream);
 // Same kernel in reverse mode, the backward's state-gradient recurrence:
