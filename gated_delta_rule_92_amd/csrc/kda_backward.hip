@@ -54,8 +54,12 @@ constexpr int BT = 16;   // tokens per tile
 constexpr int NWB = 4;   // wavefronts per workgroup
 constexpr int NTH = 64 * NWB;
 
+// Row padding of the LDS operand arrays. bf16 fragments are read as 8 bytes
+// per lane from 16 rows, 16 lanes per cycle over 32 four-byte banks: rows of
+// 2 x odd dwords (DK + 4 = 66, 16 + 4 = 10) put the 16 rows on distinct bank
+// pairs. Every LDS access to the bf16 arrays is at most 8 bytes wide.
 template <typename T>
-constexpr int pad_of() { return sizeof(T) == 2 ? 8 : 4; }
+constexpr int pad_of() { return 4; }
 
 template <typename T, int DK, int DV>
 struct BCfg {
