@@ -277,8 +277,8 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
   if (split.P > 1) {
     // 1. piece table; 2. per piece its state map M and its zero-start final
     // state b; 3. entry states chained per sequence; 4. every piece from its
-    // entry state, with output; 5. each sequence's final state = its last
-    // piece's.
+    // entry state, with output, each sequence's last piece writing the
+    // sequence's final state.
     char* ws = static_cast<char*>(workspace);
     int32_t* cu = reinterpret_cast<int32_t*>(ws);
     float* M = reinterpret_cast<float*>(ws + split.M);
@@ -301,15 +301,12 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
     }
     if (e == hipSuccess) e = kda::launch_compose(M, bst, initial_state, B, P, H, Dk, Dv, starts, hs);
     if (e == hipSuccess) {
-      kda::ChunkArgs f = a;  // the output, each piece from its entry state
-      f.q = q; f.v = v; f.o = o; f.h0 = starts; f.hT = final_state ? bst : nullptr;
+      // the output, each piece from its entry state; each sequence's last
+      // piece writes the sequence's final state
+      kda::ChunkArgs f = a;
+      f.q = q; f.v = v; f.o = o; f.h0 = starts; f.hT = final_state; f.hT_group = P;
       f.og = og; f.onw = onw; f.oeps = oeps;
       e = kda::launch_chunk_pipe(f, hs);
-    }
-    if (e == hipSuccess && final_state) {
-      const size_t st_bytes = (size_t)H * Dk * Dv * sizeof(float);
-      e = hipMemcpy2DAsync(final_state, st_bytes, bst + (size_t)(P - 1) * H * Dk * Dv,
-                           (size_t)P * st_bytes, st_bytes, (size_t)B, hipMemcpyDeviceToDevice, hs);
     }
     return launch_status(e);
   }

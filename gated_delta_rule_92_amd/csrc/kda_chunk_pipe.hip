@@ -943,8 +943,15 @@ __global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : 
       signal_add(&done[slot], lane);
     }
     float* hT = (DUAL && !tmap) ? a.hT2 : a.hT;
+    size_t hbase = sbase;
+    if (a.hT_group > 0) {
+      // pieces of a context split: only the last piece of each sequence
+      // writes, to its sequence's slot
+      if (n % a.hT_group != a.hT_group - 1) hT = nullptr;
+      hbase = ((size_t)(n / a.hT_group) * H + h) * PDK * PDV;
+    }
     if (hT) {
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(hT + sbase, PDK * PDV * 4);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(hT + hbase, PDK * PDV * 4);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll

@@ -77,7 +77,8 @@ __global__ void __launch_bounds__(kComposeThreads) compose_kernel(const float* _
 // k = 32 g + kk (g = lane / 16, kk = the product's step), so that each lane
 // reads 32 consecutive entries of its row of M_p (eight 16-byte loads, issued
 // one step ahead) and 32 consecutive rows of its column of the running slice,
-// which is kept transposed in LDS.
+// which is kept transposed in LDS. The lane's four entries of b_p are loaded
+// one step ahead as well.
 constexpr int kC128 = 128;
 constexpr int kCT = kC128 + 4;  // padded row of the transposed slice
 
@@ -107,8 +108,17 @@ __global__ void __launch_bounds__(512) compose128_kernel(const float* __restrict
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const f32x4*>(Mp + 4 * i);
   };
-  f32x4 am[8];
-  if (P > 1) load_m(0, am);
+  // entries (row0 + 4g + e, c0 + n) of b_p
+  auto load_b = [&](int p, f32x4& v) {
+    const float* bp = b + (((size_t)seq * P + p) * H + h) * (size_t)kC128 * Dv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = cvalid ? bp[(size_t)(row0 + 4 * g + e) * Dv + c0 + n] : 0.f;
+  };
+  f32x4 am[8], bv = {0.f, 0.f, 0.f, 0.f};
+  if (P > 1) {
+    load_m(0, am);
+    load_b(0, bv);
+  }
   __syncthreads();
 
   for (int p = 0; p < P; ++p) {
@@ -119,15 +129,15 @@ __global__ void __launch_bounds__(512) compose128_kernel(const float* __restrict
       for (int e = 0; e < 4; ++e) out[(size_t)(row0 + 4 * g + e) * Dv + c0 + n] = curT[n][row0 + 4 * g + e];
     }
     if (p == P - 1) break;
-    const float* bp = b + (sp * H + h) * (size_t)kC128 * Dv;
-    f32x4 acc;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = cvalid ? bp[(size_t)(row0 + 4 * g + e) * Dv + c0 + n] : 0.f;
+    f32x4 acc = bv;
     f32x4 bc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) bc[i] = *reinterpret_cast<const f32x4*>(&curT[n][32 * g + 4 * i]);
     f32x4 an[8];
-    if (p + 1 < P - 1) load_m(p + 1, an);
+    if (p + 1 < P - 1) {
+      load_m(p + 1, an);
+      load_b(p + 1, bv);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll

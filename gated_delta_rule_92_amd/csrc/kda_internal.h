@@ -76,6 +76,10 @@ struct ChunkArgs {
   void* ck_vt = nullptr;
   float* ck_at = nullptr;  // checkpoint mode: A_kk / beta per tile row, fp32 [Ttot, H, 16]
   float* hT2 = nullptr;    // split pass: zero-start final states [N, H, Dk, Dv]
+  // pipelined kernel, > 0: the N units are N / hT_group sequences of hT_group
+  // consecutive pieces, and only each sequence's last piece writes its final
+  // state, to hT[n / hT_group]
+  int hT_group = 0;
 };
 bool chunk_fused_supported(bool bf16, int Dk, int Dv, int chunk);
 // Pipelined producer/consumer chunk kernel (bf16, Dk = Dv = 128).

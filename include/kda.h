@@ -224,9 +224,11 @@ kda_status_t kda_chunk_fwd_split_workspace_size(int B, int T, int H, int Dk, int
  * in the state [KDA-blog §Kimi Delta Attention, KDA equation], so a piece's
  * final state is M S_entry + b with M its state map and b its zero-start final
  * state. On the stream, in order: the piece table; M and b of every piece
- * (kda_chunk_transition and the state-only forward); the entry states
+ * (what kda_chunk_transition and the state-only forward compute, in one
+ * launch that reads k, v, g and beta once); the entry states
  * chained per sequence (kda_compose_states); every piece from its entry state
- * with output; each sequence's final state copied from its last piece. The
+ * with output, each sequence's last piece writing the sequence's final
+ * state. The
  * results equal kda_chunk_fwd's up to rounding.
  * Arguments as for kda_chunk_fwd without cu_seqlens (N = B); o must be
  * non-NULL. workspace: device, >= kda_chunk_fwd_split_workspace_size(...)
