@@ -182,7 +182,8 @@ def chunk_fwd_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
     _need(y, "y", dt, dev)
     if output_final_state and final_state is None:
         final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
-    ws_bytes = workspace_size(B, T, H, Dk, Dv, N, chunk, dt)
+    with torch.cuda.device(dev):
+        ws_bytes = workspace_size(B, T, H, Dk, Dv, N, chunk, dt)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -246,7 +247,8 @@ def transition(k: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
     if M is None:
         M = torch.empty((N, H, Dk, Dk), dtype=torch.float32, device=dev)
     _need(M, "M", torch.float32, dev)
-    ws_bytes = workspace_size(B, T, H, Dk, Dk, N, chunk, k.dtype)
+    # the transition's workspace holds only the order of packed sequences
+    ws_bytes = workspace_size(B, T, H, Dk, Dk, N, chunk, k.dtype) if cu_seqlens is not None else 0
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
