@@ -16,8 +16,8 @@ Public API (thin wrappers over the C ABI in include/kda.h):
 """
 from .ops import (bwd_workspace_size, chunk_bwd, chunk_fwd, chunk_fwd_gated,  # noqa: F401
                   chunk_fwd_split, compose_states, gate, gate_bwd, gated_rmsnorm, recurrent_step,
-                  split_lengths, transition, workspace_size)
+                  transition, workspace_size)
 
 __all__ = ["bwd_workspace_size", "chunk_bwd", "chunk_fwd", "chunk_fwd_gated", "chunk_fwd_split",
            "compose_states", "gate", "gate_bwd", "gated_rmsnorm", "recurrent_step",
-           "split_lengths", "transition", "workspace_size"]
+           "transition", "workspace_size"]

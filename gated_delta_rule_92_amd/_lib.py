@@ -67,11 +67,11 @@ def load(path: str = LIB_PATH):
     lib.kda_chunk_fwd_gated.restype = i32
     lib.kda_gated_rmsnorm.argtypes = [vp, vp, i32, fp, f32, ctypes.c_long, i32, vp, vp]
     lib.kda_gated_rmsnorm.restype = i32
-    lib.kda_chunk_fwd_split_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
+    lib.kda_chunk_fwd_split_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                                        ctypes.POINTER(sz)]
     lib.kda_chunk_fwd_split_workspace_size.restype = i32
-    lib.kda_chunk_fwd_split.argtypes = [vp, vp, vp, i32, fp, i32, fp, f32, fp, fp,
-                                        i32, i32, i32, i32, i32, i32, i32,  # B T H Dk Dv chunk segs
+    lib.kda_chunk_fwd_split.argtypes = [vp, vp, vp, i32, fp, i32, fp, f32, fp, fp, ip,
+                                        i32, i32, i32, i32, i32, i32, i32, i32,  # N B T H Dk Dv chunk segs
                                         f32, vp, fp, vp, sz, vp]
     lib.kda_chunk_fwd_split.restype = i32
     lib.kda_chunk_transition.argtypes = [vp, i32, fp, i32, fp, f32, fp, ip,

@@ -59,16 +59,17 @@ size_t order_bytes(int B, int N) {
 // the unsplit forward up to rounding.
 struct SplitPlan {
   int P = 1;
-  int Lp = 0;
   size_t M = 0, b = 0, starts = 0, bytes = 0;  // workspace offsets; the piece table is at 0
 };
 
-SplitPlan split_layout(int B, int T, int H, int Dk, int Dv, int P, int chunk) {
+// Workspace of a split of nseq sequences into P pieces each: the piece table
+// (nseq * P + 1 int32), then per piece and head the state map M, the
+// zero-start final state b and the entry state.
+SplitPlan split_layout(int nseq, int H, int Dk, int Dv, int P) {
   SplitPlan p;
-  if (P < 2 || T <= 0 || (long)B * T > 0x7fffffffL) return p;
+  if (P < 2 || nseq <= 0) return p;
   p.P = P;
-  p.Lp = (int)round_up((size_t)((T + P - 1) / P), (size_t)chunk);
-  const size_t pieces = (size_t)B * P;
+  const size_t pieces = (size_t)nseq * P;
   p.M = round_up(sizeof(int32_t) * (pieces + 1), kWorkspaceAlign);
   p.b = p.M + round_up(pieces * H * Dk * Dk * sizeof(float), kWorkspaceAlign);
   p.starts = p.b + round_up(pieces * H * Dk * Dv * sizeof(float), kWorkspaceAlign);
@@ -102,7 +103,8 @@ SplitPlan auto_split(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype_t
   if (P > T / kSplitMinPiece) P = T / kSplitMinPiece;
   if (P > kSplitMaxPieces) P = kSplitMaxPieces;
   if (P < 4 || (long)T * (9 * P - 30) <= 3000 * P) return SplitPlan{};
-  return split_layout(B, T, H, Dk, Dv, (int)P, chunk);
+  if ((long)B * T > 0x7fffffffL) return SplitPlan{};  // the piece table is int32
+  return split_layout(B, H, Dk, Dv, (int)P);
 }
 
 }  // namespace
@@ -150,12 +152,14 @@ kda_status_t kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, i
   return KDA_SUCCESS;
 }
 
-kda_status_t kda_chunk_fwd_split_workspace_size(int B, int T, int H, int Dk, int Dv, int segments,
-                                                int chunk, kda_dtype_t dtype, size_t* bytes) {
-  if (!bytes || B <= 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || segments <= 0 || chunk <= 0)
+kda_status_t kda_chunk_fwd_split_workspace_size(int B, int T, int H, int Dk, int Dv, int N,
+                                                int segments, int chunk, kda_dtype_t dtype,
+                                                size_t* bytes) {
+  if (!bytes || B <= 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || N < 0 || segments <= 0 ||
+      chunk <= 0)
     return KDA_ERROR_INVALID_VALUE;
   if (dtype != KDA_FLOAT32 && dtype != KDA_BFLOAT16) return KDA_ERROR_INVALID_VALUE;
-  *bytes = split_layout(B, T, H, Dk, Dv, segments, chunk).bytes;
+  *bytes = split_layout(N, H, Dk, Dv, segments).bytes;
   return KDA_SUCCESS;
 }
 
@@ -173,9 +177,10 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtyp
 kda_status_t kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_dtype_t dtype,
                                  const float* g, kda_gate_input_t gate_input, const float* A_log,
                                  float g_min, const float* beta, const float* initial_state,
-                                 int B, int T, int H, int Dk, int Dv, int chunk, int segments,
-                                 float scale, void* o, float* final_state, void* workspace,
-                                 size_t workspace_bytes, kda_stream_t stream) {
+                                 const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
+                                 int Dv, int chunk, int segments, float scale, void* o,
+                                 float* final_state, void* workspace, size_t workspace_bytes,
+                                 kda_stream_t stream) {
   if (segments <= 0) return KDA_ERROR_INVALID_VALUE;
   if (!o) return KDA_ERROR_INVALID_VALUE;
   if (segments > 1 && !kda::chunk_pipe_supported(dtype == KDA_BFLOAT16, Dk, Dv, chunk))
@@ -184,8 +189,8 @@ kda_status_t kda_chunk_fwd_split(const void* q, const void* k, const void* v, kd
                        (gate_input == KDA_GATE_LOGITS && g_min < kda::kMinFusedGmin)))
     return KDA_ERROR_NOT_SUPPORTED;
   if ((long)B * T > 0x7fffffffL) return KDA_ERROR_NOT_SUPPORTED;
-  return chunk_fwd_impl(q, k, v, dtype, g, gate_input, A_log, g_min, beta, initial_state, nullptr,
-                        B, B, T, H, Dk, Dv, chunk, scale, o, final_state, workspace,
+  return chunk_fwd_impl(q, k, v, dtype, g, gate_input, A_log, g_min, beta, initial_state,
+                        cu_seqlens, N, B, T, H, Dk, Dv, chunk, scale, o, final_state, workspace,
                         workspace_bytes, stream, nullptr, nullptr, 0.f, segments);
 }
 
@@ -262,7 +267,7 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
   // order array of packed sequences is required.
   SplitPlan split;
   if (segments > 0) {
-    split = split_layout(B, T, H, Dk, Dv, segments, chunk);
+    split = split_layout(s.N, H, Dk, Dv, segments);
     if (split.P > 1 && (!workspace || workspace_bytes < split.bytes))
       return KDA_ERROR_INSUFFICIENT_WORKSPACE;
   } else if (!cu_seqlens && o && fused && !softplus && workspace) {
@@ -285,11 +290,12 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
     float* bst = reinterpret_cast<float*>(ws + split.b);
     float* starts = reinterpret_cast<float*>(ws + split.starts);
     const int P = split.P;
-    hipError_t e = kda::launch_split_pieces(cu, B, T, P, split.Lp, hs);
+    const int nseq = s.N;
+    hipError_t e = kda::launch_split_pieces(cu, cu_seqlens, nseq, T, P, chunk, hs);
     kda::ChunkArgs a;
     a.k = k; a.g = g; a.gate_mode = (int)gate_input;
     a.A_log = A_log; a.g_min = g_min; a.beta = beta;
-    a.seqs.cu = cu; a.seqs.N = B * P; a.seqs.T = T; a.seqs.Ttot = (long)B * T;
+    a.seqs.cu = cu; a.seqs.N = nseq * P; a.seqs.T = T; a.seqs.Ttot = s.Ttot;
     a.order = nullptr;
     a.H = H; a.Dk = Dk; a.Dv = Dv; a.scale = scale; a.bf16 = bf16;
     if (e == hipSuccess) {
@@ -299,7 +305,7 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
       z.q = nullptr; z.v = v; z.o = nullptr; z.h0 = nullptr; z.hT = M; z.hT2 = bst;
       e = kda::launch_chunk_split_pass(z, hs);
     }
-    if (e == hipSuccess) e = kda::launch_compose(M, bst, initial_state, B, P, H, Dk, Dv, starts, hs);
+    if (e == hipSuccess) e = kda::launch_compose(M, bst, initial_state, nseq, P, H, Dk, Dv, starts, hs);
     if (e == hipSuccess) {
       // the output, each piece from its entry state; each sequence's last
       // piece writes the sequence's final state

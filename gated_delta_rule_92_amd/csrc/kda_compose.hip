@@ -151,28 +151,36 @@ __global__ void __launch_bounds__(512) compose128_kernel(const float* __restrict
   }
 }
 
-// Boundaries of the pieces of a context split: B dense sequences of T tokens,
-// each cut into P consecutive pieces of Lp tokens (the last may be shorter).
-// cu[s*P + p] = s*T + min(p*Lp, T), cu[B*P] = B*T.
-__global__ void split_pieces_kernel(int32_t* __restrict__ cu, int B, int T, int P, int Lp) {
+// Boundaries of the pieces of a context split: each of nseq sequences (B
+// dense sequences of T tokens when cu is null, else the packed sequences of
+// cu) is cut into P consecutive pieces of Lp = chunk * ceil(ceil(L / P) /
+// chunk) tokens, the last taking the rest (pieces may be empty):
+// out[s*P + p] = start(s) + min(p*Lp, L(s)), out[nseq*P] = the total.
+__global__ void split_pieces_kernel(int32_t* __restrict__ out, const int32_t* __restrict__ cu,
+                                    int nseq, int T, int P, int chunk) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  const int n = B * P;
+  const int n = nseq * P;
   if (i > n) return;
   if (i == n) {
-    cu[i] = B * T;
+    out[i] = cu ? cu[nseq] : (int32_t)((long)nseq * T);
     return;
   }
   const int s = i / P, p = i - s * P;
-  const long start = (long)p * Lp < (long)T ? (long)p * Lp : (long)T;
-  cu[i] = (int32_t)((long)s * T + start);
+  const long start = cu ? (long)cu[s] : (long)s * T;
+  const long L = cu ? (long)cu[s + 1] - start : (long)T;
+  const long per = (L + P - 1) / P;
+  const long Lp = (per + chunk - 1) / chunk * chunk;
+  const long off = (long)p * Lp < L ? (long)p * Lp : L;
+  out[i] = (int32_t)(start + off);
 }
 
 }  // namespace
 
-hipError_t launch_split_pieces(int32_t* cu, int B, int T, int P, int Lp, hipStream_t stream) {
-  const int n = B * P + 1;
+hipError_t launch_split_pieces(int32_t* out, const int32_t* cu, int nseq, int T, int P, int chunk,
+                               hipStream_t stream) {
+  const int n = nseq * P + 1;
   hipLaunchKernelGGL(split_pieces_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                     cu, B, T, P, Lp);
+                     out, cu, nseq, T, P, chunk);
   return hipGetLastError();
 }
 

@@ -106,9 +106,11 @@ hipError_t launch_gated_rmsnorm(const void* o, const void* z, bool bf16, const f
 // Chains segment maps: starts[0] = S0, starts[p+1] = M_p starts[p] + b_p.
 hipError_t launch_compose(const float* M, const float* b, const float* S0, int nseq, int P,
                           int H, int Dk, int Dv, float* starts, hipStream_t stream);
-// Piece table of a context split of B dense sequences into P pieces of Lp
-// tokens: cu[B*P + 1] (device int32; the caller keeps B*T below 2^31).
-hipError_t launch_split_pieces(int32_t* cu, int B, int T, int P, int Lp, hipStream_t stream);
+// Piece table of a context split: each of nseq sequences (dense of T tokens
+// when cu is null, else packed by cu) into P chunk-aligned pieces:
+// out[nseq*P + 1] (device int32; dense callers keep nseq*T below 2^31).
+hipError_t launch_split_pieces(int32_t* out, const int32_t* cu, int nseq, int T, int P, int chunk,
+                               hipStream_t stream);
 // Lowest per-token log-decay the chunk path handles (16 * 5.5 = 88 < 88.7 = ln FLT_MAX).
 constexpr float kMinFusedGmin = -5.5f;
 hipError_t launch_chunk_fused(const ChunkArgs& a, hipStream_t stream);

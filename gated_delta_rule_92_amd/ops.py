@@ -286,22 +286,6 @@ def compose_states(M: torch.Tensor, b: torch.Tensor, initial_state: Optional[tor
     return out
 
 
-def split_lengths(lengths, segments: int, align: int = 64):
-    """Cut each sequence into `segments` consecutive pieces whose lengths are
-    multiples of `align` (the last piece takes the rest; pieces may be empty).
-    Returns the flat list of piece lengths, sequence by sequence."""
-    out = []
-    for L in lengths:
-        per = -(-int(L) // segments)
-        per = -(-per // align) * align
-        rest = int(L)
-        for p in range(segments):
-            n = rest if p == segments - 1 else min(per, rest)
-            out.append(n)
-            rest -= n
-    return out
-
-
 def chunk_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                     beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
                     cu_seqlens: Optional[torch.Tensor] = None, segments: int = 8,
@@ -309,36 +293,11 @@ def chunk_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
                     g_min: float = -5.0, chunk: int = 64, scale: float = 1.0
                     ) -> Tuple[torch.Tensor, torch.Tensor]:
     """The chunk forward with every sequence cut into `segments` consecutive
-    pieces that run in parallel (the one-GPU form of a context split):
-      1. per piece, its state map M (kda_chunk_transition) and its final
-         state b from a zero start (kda_chunk_fwd without output);
-      2. the pieces' entry states, chained per sequence (kda_compose_states);
-      3. every piece again from its entry state, producing o.
-    Same results as chunk_fwd up to rounding. Dense inputs make one
-    kda_chunk_fwd_split call, which runs these steps on the stream. Packed
-    inputs (cu_seqlens) read the sequence lengths to the host to cut the
-    pieces and make the three calls from here. Returns (o, final_state)."""
-    B, T, H, Dk = q.shape
-    Dv = v.shape[-1]
-    if cu_seqlens is None:
-        return _chunk_fwd_split_dense(q, k, v, g, beta, initial_state, segments, gate, A_log,
-                                      g_min, chunk, scale)
-    lengths = [int(x) for x in torch.diff(cu_seqlens.cpu().to(torch.int64)).tolist()]
-    nseq = len(lengths)
-    pieces = split_lengths(lengths, segments, chunk)
-    cu = torch.zeros(len(pieces) + 1, dtype=torch.int64)
-    cu[1:] = torch.cumsum(torch.tensor(pieces, dtype=torch.int64), 0)
-    cu = cu.to(torch.int32).to(q.device)
-    common = dict(cu_seqlens=cu, gate=gate, A_log=A_log, g_min=g_min, chunk=chunk)
-    M = transition(k, g, beta, **common)
-    _, b = chunk_fwd(q, k, v, g, beta, None, output=False, scale=scale, **common)
-    starts = compose_states(M, b, initial_state, nseq, segments)
-    o, finals = chunk_fwd(q, k, v, g, beta, starts, scale=scale, **common)
-    return o, finals.view(nseq, segments, H, Dk, Dv)[:, segments - 1]
-
-
-def _chunk_fwd_split_dense(q, k, v, g, beta, initial_state, segments, gate, A_log, g_min, chunk,
-                           scale):
+    pieces that run in parallel (the one-GPU form of a context split), one
+    kda_chunk_fwd_split call: per piece its state map and zero-start final
+    state, the entry states chained per sequence, then every piece from its
+    entry state. Same results as chunk_fwd up to rounding. Returns
+    (o, final_state)."""
     import ctypes
     lib = _lib.load()
     dev = q.device
@@ -352,16 +311,21 @@ def _chunk_fwd_split_dense(q, k, v, g, beta, initial_state, segments, gate, A_lo
     if k.shape != q.shape or v.shape[:3] != q.shape[:3] or g.shape != q.shape or \
             beta.shape != q.shape[:3]:
         raise ValueError("shape mismatch among q, k, v, g, beta")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
     if initial_state is not None:
         _need(initial_state, "initial_state", torch.float32, dev)
-        if tuple(initial_state.shape) != (B, H, Dk, Dv):
-            raise ValueError("initial_state must be [B, H, Dk, Dv]")
+        if tuple(initial_state.shape) != (N, H, Dk, Dv):
+            raise ValueError("initial_state must be [N, H, Dk, Dv]")
     if A_log is not None:
         _need(A_log, "A_log", torch.float32, dev)
     o = torch.empty((B, T, H, Dv), dtype=dt, device=dev)
-    final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
     out = ctypes.c_size_t(0)
-    _lib.check(lib.kda_chunk_fwd_split_workspace_size(B, T, H, Dk, Dv, int(segments), int(chunk),
+    _lib.check(lib.kda_chunk_fwd_split_workspace_size(B, T, H, Dk, Dv, N, int(segments), int(chunk),
                                                       _dtype_code(q), ctypes.byref(out)),
                "kda_chunk_fwd_split_workspace_size")
     ws_len = int(out.value)
@@ -369,9 +333,9 @@ def _chunk_fwd_split_dense(q, k, v, g, beta, initial_state, segments, gate, A_lo
     with torch.cuda.device(dev):
         rc = lib.kda_chunk_fwd_split(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g),
                                      _GATES[gate], _ptr(A_log), float(g_min), _ptr(beta),
-                                     _ptr(initial_state), B, T, H, Dk, Dv, int(chunk),
-                                     int(segments), float(scale), _ptr(o), _ptr(final_state),
-                                     _ptr(workspace), ws_len, _stream(dev))
+                                     _ptr(initial_state), _ptr(cu_seqlens), N, B, T, H, Dk, Dv,
+                                     int(chunk), int(segments), float(scale), _ptr(o),
+                                     _ptr(final_state), _ptr(workspace), ws_len, _stream(dev))
     _lib.check(rc, "kda_chunk_fwd_split")
     return o, final_state
 

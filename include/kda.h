@@ -213,26 +213,27 @@ kda_status_t kda_gated_rmsnorm(const void* o, const void* gate, kda_dtype_t dtyp
  * kda_chunk_fwd_split_workspace_size — bytes of device workspace
  * kda_chunk_fwd_split needs (0 for segments = 1).
  */
-kda_status_t kda_chunk_fwd_split_workspace_size(int B, int T, int H, int Dk, int Dv, int segments,
-                                                int chunk, kda_dtype_t dtype, size_t* bytes);
+kda_status_t kda_chunk_fwd_split_workspace_size(int B, int T, int H, int Dk, int Dv, int N,
+                                                int segments, int chunk, kda_dtype_t dtype,
+                                                size_t* bytes);
 
 /*
- * kda_chunk_fwd_split — kda_chunk_fwd for dense sequences with each sequence
- * cut into `segments` consecutive pieces of Lp = 64 * ceil(ceil(T / segments)
- * / 64) tokens (the last takes the rest; pieces may be empty) that run in
- * parallel: the one-GPU form of a context split. The KDA equation is linear
- * in the state [KDA-blog §Kimi Delta Attention, KDA equation], so a piece's
- * final state is M S_entry + b with M its state map and b its zero-start final
- * state. On the stream, in order: the piece table; M and b of every piece
- * (what kda_chunk_transition and the state-only forward compute, in one
- * launch that reads k, v, g and beta once); the entry states
- * chained per sequence (kda_compose_states); every piece from its entry state
- * with output, each sequence's last piece writing the sequence's final
- * state. The
- * results equal kda_chunk_fwd's up to rounding.
- * Arguments as for kda_chunk_fwd without cu_seqlens (N = B); o must be
- * non-NULL. workspace: device, >= kda_chunk_fwd_split_workspace_size(...)
- * bytes (KDA_ERROR_INSUFFICIENT_WORKSPACE otherwise).
+ * kda_chunk_fwd_split — kda_chunk_fwd with each sequence (dense, or packed by
+ * cu_seqlens) cut into `segments` consecutive pieces of Lp = 64 *
+ * ceil(ceil(L / segments) / 64) tokens, L its length (the last piece takes
+ * the rest; pieces may be empty), that run in parallel: the one-GPU form of
+ * a context split. The KDA equation is linear in the state [KDA-blog §Kimi
+ * Delta Attention, KDA equation], so a piece's final state is M S_entry + b
+ * with M its state map and b its zero-start final state. On the stream, in
+ * order: the piece table (computed on the device from cu_seqlens); M and b
+ * of every piece (what kda_chunk_transition and the state-only forward
+ * compute, in one launch that reads k, v, g and beta once); the entry states
+ * chained per sequence (kda_compose_states); every piece from its entry
+ * state with output, each sequence's last piece writing the sequence's
+ * final state. The results equal kda_chunk_fwd's up to rounding.
+ * Arguments as for kda_chunk_fwd; o must be non-NULL. workspace: device,
+ * >= kda_chunk_fwd_split_workspace_size(...) bytes
+ * (KDA_ERROR_INSUFFICIENT_WORKSPACE otherwise).
  * Supported for segments > 1: bf16, Dk = Dv = 128, chunk = 64, B*T < 2^31,
  * gates other than KDA_GATE_SOFTPLUS with log-decay >= -5.5
  * (KDA_ERROR_NOT_SUPPORTED otherwise). segments = 1 is kda_chunk_fwd.
@@ -240,9 +241,10 @@ kda_status_t kda_chunk_fwd_split_workspace_size(int B, int T, int H, int Dk, int
 kda_status_t kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_dtype_t dtype,
                                  const float* g, kda_gate_input_t gate_input, const float* A_log,
                                  float g_min, const float* beta, const float* initial_state,
-                                 int B, int T, int H, int Dk, int Dv, int chunk, int segments,
-                                 float scale, void* o, float* final_state, void* workspace,
-                                 size_t workspace_bytes, kda_stream_t stream);
+                                 const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
+                                 int Dv, int chunk, int segments, float scale, void* o,
+                                 float* final_state, void* workspace, size_t workspace_bytes,
+                                 kda_stream_t stream);
 
 /*
  * kda_chunk_transition — the state map of each (sequence, head).

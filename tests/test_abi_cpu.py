@@ -143,19 +143,23 @@ def test_split_forward_validation_and_workspace():
     n = ctypes.c_size_t(0)
     # piece table (B*P + 1 int32, 256-aligned), then per piece and head a
     # Dk x Dk state map and two Dk x Dv states
-    assert lib.kda_chunk_fwd_split_workspace_size(1, 262144, 32, 128, 128, 8, 64, 1,
+    assert lib.kda_chunk_fwd_split_workspace_size(1, 262144, 32, 128, 128, 1, 8, 64, 1,
                                                   ctypes.byref(n)) == 0
     assert n.value == 256 + 3 * 8 * 32 * 128 * 128 * 4
-    assert lib.kda_chunk_fwd_split_workspace_size(2, 1000, 2, 128, 128, 1, 64, 1,
+    # 64 packed sequences into 4 pieces: a table of 257 int32, 256 pieces' states
+    assert lib.kda_chunk_fwd_split_workspace_size(1, 1 << 20, 32, 128, 128, 64, 4, 64, 1,
+                                                  ctypes.byref(n)) == 0
+    assert n.value == 1280 + 3 * 256 * 32 * 128 * 128 * 4
+    assert lib.kda_chunk_fwd_split_workspace_size(2, 1000, 2, 128, 128, 2, 1, 64, 1,
                                                   ctypes.byref(n)) == 0
     assert n.value == 0
-    assert lib.kda_chunk_fwd_split_workspace_size(2, 1000, 2, 128, 128, 0, 64, 1,
+    assert lib.kda_chunk_fwd_split_workspace_size(2, 1000, 2, 128, 128, 2, 0, 64, 1,
                                                   ctypes.byref(n)) == _lib.KDA_ERROR_INVALID_VALUE
 
     def split(**kw):
         a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, g=FAKE, gate=2, A=None, g_min=-5.0, beta=FAKE,
-                 h0=None, B=1, T=8192, H=2, Dk=128, Dv=128, chunk=64, segments=4, scale=1.0,
-                 o=FAKE, hT=None, ws=FAKE, ws_bytes=1 << 30, stream=None)
+                 h0=None, cu=None, N=1, B=1, T=8192, H=2, Dk=128, Dv=128, chunk=64, segments=4,
+                 scale=1.0, o=FAKE, hT=None, ws=FAKE, ws_bytes=1 << 30, stream=None)
         a.update(kw)
         return lib.kda_chunk_fwd_split(*a.values())
     assert split(segments=0) == _lib.KDA_ERROR_INVALID_VALUE
@@ -167,6 +171,8 @@ def test_split_forward_validation_and_workspace():
     assert split(g_min=-8.0) == _lib.KDA_ERROR_NOT_SUPPORTED
     assert split(ws=None, ws_bytes=0) == _lib.KDA_ERROR_INSUFFICIENT_WORKSPACE
     assert split(ws_bytes=1024) == _lib.KDA_ERROR_INSUFFICIENT_WORKSPACE
+    assert split(N=2) == _lib.KDA_ERROR_INVALID_VALUE            # dense needs N == B
+    assert split(cu=FAKE, N=3, B=2) == _lib.KDA_ERROR_INVALID_VALUE  # packed needs B == 1
 
 
 def test_epilogue_entry_points_validation():
@@ -191,19 +197,6 @@ def test_epilogue_entry_points_validation():
         assert rms(**kw) == _lib.KDA_ERROR_INVALID_VALUE, kw
     assert rms(Dv=513) == _lib.KDA_ERROR_NOT_SUPPORTED
     assert rms(rows=0) == _lib.KDA_SUCCESS
-
-
-def test_split_lengths_cover_each_sequence_in_aligned_pieces():
-    from gated_delta_rule_92_amd.ops import split_lengths
-    for lengths, P in (([262144], 8), ([1, 63, 64, 65, 1000, 0], 3), ([130, 7], 5)):
-        pieces = split_lengths(lengths, P)
-        assert len(pieces) == len(lengths) * P
-        for i, L in enumerate(lengths):
-            mine = pieces[i * P:(i + 1) * P]
-            assert sum(mine) == L and min(mine) >= 0
-            # every non-empty piece starts on a 64-token chunk boundary
-            starts = [sum(mine[:j]) for j in range(P) if mine[j] > 0]
-            assert all(st % 64 == 0 for st in starts)
 
 
 def test_python_binding_fails_loudly_without_gpu_tensors():

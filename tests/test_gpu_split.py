@@ -103,6 +103,41 @@ def test_split_forward_matches_unsplit_oracle(name, kw, P, mode):
     del hT_ref_gpu
 
 
+def test_packed_piece_table():
+    """The piece table kda_chunk_fwd_split builds on the device from
+    cu_seqlens: every sequence in `segments` consecutive pieces of
+    64 * ceil(ceil(L / P) / 64) tokens, the last taking the rest."""
+    import ctypes
+    from gated_delta_rule_92_amd import _lib
+    from gated_delta_rule_92_amd.ops import _ptr, _stream
+    _print_case("packed piece table")
+    lens, P, H = [0, 1, 63, 64, 65, 700, 130], 3, 2
+    d = make_inputs(1, 0, H, 128, 128, torch.bfloat16, lengths=lens, seed=36)
+    dd = to_dev(d)
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    assert lib.kda_chunk_fwd_split_workspace_size(1, sum(lens), H, 128, 128, len(lens), P, 64,
+                                                  _lib.KDA_BFLOAT16, ctypes.byref(n)) == 0
+    ws = torch.zeros(n.value, dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(dd["v"])
+    rc = lib.kda_chunk_fwd_split(_ptr(dd["q"]), _ptr(dd["k"]), _ptr(dd["v"]), _lib.KDA_BFLOAT16,
+                                 _ptr(dd["z"]), _lib.KDA_GATE_LOGITS, None, -5.0, _ptr(dd["beta"]),
+                                 None, _ptr(dd["cu_seqlens"]), len(lens), 1, sum(lens), H, 128, 128,
+                                 64, P, 1.0, _ptr(o), None, _ptr(ws), n.value,
+                                 _stream(torch.device("cuda")))
+    assert rc == 0
+    table = ws[:4 * (len(lens) * P + 1)].view(torch.int32).cpu().tolist()
+    want, start = [], 0
+    for L in lens:
+        per = -(-(-(-L // P)) // 64) * 64
+        want += [start + min(p * per, L) for p in range(P)]
+        start += L
+    want.append(start)
+    assert table == want
+    ref = oracle_forward(d["q"], d["k"], d["v"], d["z"], d["beta"], None, d["cu_seqlens"], None, -5.0)
+    assert rel_err(o, ref[0]) <= TOL_BF16
+
+
 def test_split_long256k_full_size_sampled():
     """The 256K-token single sequence at full size (32 heads), split into 8
     segments so that all 256 units run at once; one head checked against the
