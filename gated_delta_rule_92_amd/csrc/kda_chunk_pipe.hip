@@ -726,6 +726,41 @@ __global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : 
       for (int b = 0; b < CNTV; ++b) nw[b] = a.onw ? a.onw[vc0 + 16 * b + m] : 1.0f;
       if (nsteps > 0) load_gate(0);
     }
+    // Gated epilogue, one tile behind: a tile's outputs wait in registers
+    // while the next tile is computed, so that the four consumers' sums of
+    // squares are usually all posted when a consumer needs them.
+    f32x4 pv_oc[CNTV];
+    short pv_zg[CNTV][4];
+    int pv_slot = 0, pv_use = 0, pv_L = 1;
+    long pv_t0 = 0;
+    auto finish_prev = [&]() {
+      const __amdgpu_buffer_rsrc_t pv_rso =
+          make_rsrc(o + ((size_t)pv_t0 * H + h) * PDV, (uint32_t)((pv_L - 1) * H + 1) * PDV * 2);
+      wait_at_least(&nrm_ready[pv_slot], NCONS * (pv_use + 1), abort_flag);
+      const float* nrm = reinterpret_cast<const float*>(smem + pv_slot * kSlotBytes + sNrm);
+      f32x4 tot = *reinterpret_cast<const f32x4*>(nrm + 4 * g4);
+#pragma unroll
+      for (int cc = 1; cc < NCONS; ++cc) tot = tot + *reinterpret_cast<const f32x4*>(nrm + cc * PT + 4 * g4);
+      f32x4 rinv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rinv[e] = __builtin_amdgcn_rsqf(tot[e] * (1.0f / PDV) + a.oeps);
+#pragma unroll
+      for (int b = 0; b < CNTV; ++b) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float z = bits_float((int)(uint32_t)(uint16_t)pv_zg[b][e] << 16);
+          const float sg = __builtin_amdgcn_rcpf(1.0f + ex2(-kLog2e * z));
+          v[e] = pv_oc[b][e] * rinv[e] * nw[b] * sg;
+        }
+        const uint32_t p01 = pack_bf16x2(v[0], v[1]), p23 = pack_bf16x2(v[2], v[3]);
+        const uint32_t q01 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p01, 0xB1, 0xF, 0xF, false);
+        const uint32_t q23 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p23, 0xB1, 0xF, 0xF, false);
+        __builtin_amdgcn_raw_buffer_store_b32((int)__builtin_amdgcn_perm(q01, p01, psel), pv_rso, ovoff2, 32 * b, 0);
+        __builtin_amdgcn_raw_buffer_store_b32((int)__builtin_amdgcn_perm(q23, p23, psel), pv_rso, ovoff2,
+                                              2 * rowo + 32 * b, 0);
+      }
+    };
 
     for (int step = 0; step < nsteps; ++step) {
       const int slot = step % NSLOT;
@@ -887,8 +922,9 @@ __global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : 
         }
         if constexpr (GATED) {
           // mean square over the d_v outputs of each row: this consumer's 32
-          // columns summed over the 16 lanes of the row group (DPP), then the
-          // four consumers' sums exchanged through LDS
+          // columns summed over the 16 lanes of the row group (DPP), posted
+          // for the other consumers; the previous tile is finished now, this
+          // one at the next tile (or after the last)
           f32x4 ss = oc[0] * oc[0];
 #pragma unroll
           for (int b = 1; b < CNTV; ++b) ss = ss + oc[b] * oc[b];
@@ -905,32 +941,29 @@ __global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : 
           if (m == 0) *reinterpret_cast<f32x4*>(nrm + c * PT + 4 * g4) = ss;
           __builtin_amdgcn_s_waitcnt(0xc07f);
           signal_add(&nrm_ready[slot], lane);
-          wait_at_least(&nrm_ready[slot], NCONS * (step / NSLOT + 1), abort_flag);
-          f32x4 tot = *reinterpret_cast<const f32x4*>(nrm + 4 * g4);
+          if (step > 0) finish_prev();
 #pragma unroll
-          for (int cc = 1; cc < NCONS; ++cc) tot = tot + *reinterpret_cast<const f32x4*>(nrm + cc * PT + 4 * g4);
-          f32x4 rinv;
+          for (int b = 0; b < CNTV; ++b) {
+            pv_oc[b] = oc[b];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) rinv[e] = __builtin_amdgcn_rsqf(tot[e] * (1.0f / PDV) + a.oeps);
-#pragma unroll
-          for (int b = 0; b < CNTV; ++b)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float z = bits_float((int)(uint32_t)(uint16_t)zg[b][e] << 16);
-              const float sg = __builtin_amdgcn_rcpf(1.0f + ex2(-kLog2e * z));
-              oc[b][e] = oc[b][e] * rinv[e] * nw[b] * sg;
-            }
+            for (int e = 0; e < 4; ++e) pv_zg[b][e] = zg[b][e];
+          }
+          pv_slot = slot;
+          pv_use = step / NSLOT;
+          pv_t0 = t0;
+          pv_L = L;
           if (step + 1 < nsteps) load_gate(step + 1);
-        }
+        } else {
 #pragma unroll
-        for (int b = 0; b < CNTV; ++b) {
-          const f32x4 v = oc[b];
-          const uint32_t p01 = pack_bf16x2(v[0], v[1]), p23 = pack_bf16x2(v[2], v[3]);
-          const uint32_t q01 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p01, 0xB1, 0xF, 0xF, false);
-          const uint32_t q23 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p23, 0xB1, 0xF, 0xF, false);
-          __builtin_amdgcn_raw_buffer_store_b32((int)__builtin_amdgcn_perm(q01, p01, psel), rso, ovoff2, 32 * b, 0);
-          __builtin_amdgcn_raw_buffer_store_b32((int)__builtin_amdgcn_perm(q23, p23, psel), rso, ovoff2,
-                                                2 * rowo + 32 * b, 0);
+          for (int b = 0; b < CNTV; ++b) {
+            const f32x4 v = oc[b];
+            const uint32_t p01 = pack_bf16x2(v[0], v[1]), p23 = pack_bf16x2(v[2], v[3]);
+            const uint32_t q01 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p01, 0xB1, 0xF, 0xF, false);
+            const uint32_t q23 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p23, 0xB1, 0xF, 0xF, false);
+            __builtin_amdgcn_raw_buffer_store_b32((int)__builtin_amdgcn_perm(q01, p01, psel), rso, ovoff2, 32 * b, 0);
+            __builtin_amdgcn_raw_buffer_store_b32((int)__builtin_amdgcn_perm(q23, p23, psel), rso, ovoff2,
+                                                  2 * rowo + 32 * b, 0);
+          }
         }
       }
       // S <- Diag(e^{G_15}) S + (K e^{G_15 - G})^T V~  (the decay is applied
@@ -941,6 +974,9 @@ __global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : 
         for (int b = 0; b < CNTV; ++b) S[ct][b] = M::k16n(ktf[ct], Xf[b], S[ct][b]);
       __builtin_amdgcn_s_waitcnt(0xc07f);
       signal_add(&done[slot], lane);
+    }
+    if constexpr (GATED) {
+      if (nsteps > 0) finish_prev();
     }
     float* hT = (DUAL && !tmap) ? a.hT2 : a.hT;
     size_t hbase = sbase;
