@@ -373,6 +373,74 @@ def bench_decode(args, d, w, dev):
     return 0
 
 
+def bench_gate(args, d, w, dev):
+    """One step = one kda_gate launch over the whole workload: the gate
+    g = g_min * sigmoid(z) and its chunk-local inclusive cumsum, fp32 in and
+    out (4 + 4 bytes per element)."""
+    from gated_delta_rule_92_amd import gate
+    z = d["z"]
+    out = torch_empty_like(z)
+
+    def step():
+        gate(z, None, w.g_min, w.chunk, d["cu_seqlens"], out=out)
+
+    ms_per_step, launch_ms = _timed(step, args.steps, args.warmup, dev)
+    kernel_ms = sum(launch_ms) / args.steps
+    elems = z.numel()
+    bytes_alg = 8 * elems
+    achieved = bytes_alg / (kernel_ms / 1e3) / 1e9
+    log(f"bench: gate {args.steps} steps, event {kernel_ms:.3f} ms/launch, {achieved:.0f} GB/s")
+    cpu = None
+    if not args.skip_cpu_baseline:
+        # the oracle's gate and chunk cumsum on a bounded sample: the first
+        # 4096 tokens of the first sequence, repeated for about 3 s
+        from oracle import oracle_cumsum, oracle_gate
+        rows = min(int(z.shape[1]), 4096)
+        zs = z[:1, :rows].cpu()
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 3.0:
+            oracle_cumsum(oracle_gate(zs, None, w.g_min), w.chunk)
+            reps += 1
+        wall = time.perf_counter() - t0
+        cpu = {"value": reps * rows * w.H / wall, "unit": "tokens·heads/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{reps} passes over {rows} tokens x {w.H} heads x {w.Dk} channels of "
+                         f"the {w.name} workload, fp64 gate then chunk cumsum, one thread, "
+                         f"{wall:.1f} s wall"}
+    n_tokens = int(z.shape[0] * z.shape[1])
+    line = {
+        "metric": "KDA gate + chunk cumsum tokens·heads/s (H=32,d=128)",
+        "value": n_tokens * w.H / (ms_per_step / 1e3),
+        "unit": "tokens·heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "gate", "heads": w.H, "d_k": w.Dk,
+                   "chunk": w.chunk, "g_min": w.g_min},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "scope": "one kda_gate launch; bytes = z read and g written once (fp32)"},
+        "kernel_ms": kernel_ms,
+        "kernel_ms_median": launch_ms[len(launch_ms) // 2],
+        "kernel_ms_min": launch_ms[0],
+        "kernel_ms_max": launch_ms[-1],
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def torch_empty_like(x):
+    import torch
+    return torch.empty_like(x)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -390,11 +458,12 @@ def main(argv=None):
     ap.add_argument("--split", type=int, default=1,
                     help="cut every sequence into this many segments that run in parallel "
                          "(state maps + composition + re-run); 1 = the plain forward")
-    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "decode"],
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "decode", "gate"],
                     default="forward",
                     help="forward: kda_chunk_fwd (the default line); backward: kda_chunk_bwd with "
                          "seeded normal output and final-state gradients; decode: one "
-                         "kda_recurrent_step for every (sequence, head)")
+                         "kda_recurrent_step for every (sequence, head); gate: one kda_gate "
+                         "(gate and chunk-local cumsum) over the workload's logits")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -427,6 +496,8 @@ def main(argv=None):
         return bench_backward(args, d, w, dev)
     if args.which == "decode":
         return bench_decode(args, d, w, dev)
+    if args.which == "gate":
+        return bench_gate(args, d, w, dev)
 
     if args.epilogue != "none":
         gen = torch.Generator(device=dev).manual_seed(1)
