@@ -1,0 +1,114 @@
+// HBM stream rates on one GPU, the reference points for the roofline of the
+// memory-heavy kernels: a read-only sum (4 or 8 16-byte loads in flight per
+// lane), a copy, and five read streams into one write stream (about the
+// forward's ratio of bytes read to bytes written), each over 512 MiB buffers
+// at grids of 256 to 16384 workgroups of 256 threads (one to 64 per compute
+// unit); best of 8 launches, timed with HIP events. Standalone:
+//   hipcc --offload-arch=gfx950 -O3 -Xclang -target-feature -Xclang -packed-fp32-ops \
+//     bench_hbm.hip -o bench_hbm && ./bench_hbm
+#include <hip/hip_runtime.h>
+#include <cstdio>
+#include <cstdlib>
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+#define CK(x) do { hipError_t e_ = (x); if (e_ != hipSuccess) { printf("HIP error %s at %d\n", hipGetErrorString(e_), __LINE__); exit(1); } } while (0)
+
+template <int U>
+__global__ void read_sum(const f4* __restrict__ a, size_t n4, float* __restrict__ out) {
+  const size_t gid = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  f4 acc = {0, 0, 0, 0};
+  for (size_t base = gid; base < n4; base += stride * U) {
+    f4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = base + u * stride;
+      v[u] = i < n4 ? __builtin_nontemporal_load(a + i) : f4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc += v[u];
+  }
+  out[gid] = acc.x + acc.y + acc.z + acc.w;
+}
+
+template <int U>
+__global__ void copy4(const f4* __restrict__ a, f4* __restrict__ b, size_t n4) {
+  const size_t gid = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t base = gid; base < n4; base += stride * U) {
+    f4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = base + u * stride;
+      if (i < n4) v[u] = a[i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = base + u * stride;
+      if (i < n4) b[i] = v[u];
+    }
+  }
+}
+
+// five read streams, one write stream (the forward reads about five bytes per byte written)
+__global__ void mix51(const f4* __restrict__ a0, const f4* __restrict__ a1, const f4* __restrict__ a2,
+                      const f4* __restrict__ a3, const f4* __restrict__ a4, f4* __restrict__ b, size_t n4) {
+  const size_t gid = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = gid; i < n4; i += stride) b[i] = a0[i] + a1[i] + a2[i] + a3[i] + a4[i];
+}
+
+int main() {
+  const size_t bytes = (size_t)512 << 20;
+  const size_t n4 = bytes / 16;
+  f4* buf[7];
+  for (int i = 0; i < 7; ++i) {
+    CK(hipMalloc(&buf[i], bytes));
+    CK(hipMemset(buf[i], 0, bytes));
+  }
+  const int maxthreads = 256 * 64 * 1024;
+  float* out;
+  CK(hipMalloc(&out, (size_t)maxthreads * sizeof(float)));
+  hipEvent_t e0, e1;
+  CK(hipEventCreate(&e0));
+  CK(hipEventCreate(&e1));
+  const int grids[] = {256, 512, 1024, 2048, 4096, 8192, 16384};
+  for (int gi = 0; gi < 7; ++gi) {
+    const int grid = grids[gi], block = 256;
+    if ((size_t)grid * block > (size_t)maxthreads) continue;
+    float best[4] = {1e9f, 1e9f, 1e9f, 1e9f};
+    for (int rep = 0; rep < 8; ++rep) {
+      float ms;
+      CK(hipEventRecord(e0));
+      hipLaunchKernelGGL(read_sum<4>, dim3(grid), dim3(block), 0, 0, buf[0], n4, out);
+      CK(hipEventRecord(e1));
+      CK(hipEventSynchronize(e1));
+      CK(hipEventElapsedTime(&ms, e0, e1));
+      best[0] = ms < best[0] ? ms : best[0];
+      CK(hipEventRecord(e0));
+      hipLaunchKernelGGL(read_sum<8>, dim3(grid), dim3(block), 0, 0, buf[0], n4, out);
+      CK(hipEventRecord(e1));
+      CK(hipEventSynchronize(e1));
+      CK(hipEventElapsedTime(&ms, e0, e1));
+      best[1] = ms < best[1] ? ms : best[1];
+      CK(hipEventRecord(e0));
+      hipLaunchKernelGGL(copy4<4>, dim3(grid), dim3(block), 0, 0, buf[0], buf[1], n4);
+      CK(hipEventRecord(e1));
+      CK(hipEventSynchronize(e1));
+      CK(hipEventElapsedTime(&ms, e0, e1));
+      best[2] = ms < best[2] ? ms : best[2];
+      CK(hipEventRecord(e0));
+      hipLaunchKernelGGL(mix51, dim3(grid), dim3(block), 0, 0, buf[0], buf[1], buf[2], buf[3], buf[4], buf[5], n4);
+      CK(hipEventRecord(e1));
+      CK(hipEventSynchronize(e1));
+      CK(hipEventElapsedTime(&ms, e0, e1));
+      best[3] = ms < best[3] ? ms : best[3];
+    }
+    printf("grid %6d  read4 %6.0f GB/s  read8 %6.0f GB/s  copy %6.0f GB/s  mix51 %6.0f GB/s\n", grid,
+           bytes / best[0] / 1e6, bytes / best[1] / 1e6, 2.0 * bytes / best[2] / 1e6, 6.0 * bytes / best[3] / 1e6);
+    fflush(stdout);
+  }
+  CK(hipDeviceSynchronize());
+  return 0;
+}
