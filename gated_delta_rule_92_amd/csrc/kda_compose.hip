@@ -73,12 +73,13 @@ __global__ void __launch_bounds__(kComposeThreads) compose_kernel(const float* _
 // Dk = 128 on fp32 matrix cores: a workgroup of 8 wavefronts per (sequence,
 // head, 16 value columns); wavefront w forms rows [16w, 16w + 16) of each next
 // entry state, start_{p+1} = M_p start_p + b_p, as 32 16x16x4 products with
-// b_p as the initial accumulator. The contraction index k is split as
-// k = 32 g + kk (g = lane / 16, kk = the product's step), so that each lane
-// reads 32 consecutive entries of its row of M_p (eight 16-byte loads, issued
-// one step ahead) and 32 consecutive rows of its column of the running slice,
-// which is kept transposed in LDS. The lane's four entries of b_p are loaded
-// one step ahead as well.
+// b_p as the initial accumulator. The contraction index is taken as
+// k = 16 i + 4 g + e (g = lane / 16; i, e the product's step), so that the
+// four lanes of a row read 64 consecutive bytes of M_p per 16-byte load
+// (eight loads per lane, issued one step ahead; a sixteenth of the cache lines
+// a lane-per-row split would touch per load) and the matching entries of
+// their column of the running slice, which is kept transposed in LDS. The
+// lane's four entries of b_p are loaded one step ahead as well.
 constexpr int kC128 = 128;
 constexpr int kCT = kC128 + 4;  // padded row of the transposed slice
 
@@ -101,12 +102,12 @@ __global__ void __launch_bounds__(512) compose128_kernel(const float* __restrict
     curT[col][row] = (S0 && c0 + col < Dv) ? S0[(((size_t)seq * H + h) * kC128 + row) * Dv + c0 + col]
                                            : 0.f;
   }
-  // row row0 + n of M_p, entries 32g .. 32g + 31
+  // row row0 + n of M_p, entries 16i + 4g .. 16i + 4g + 3 for i = 0..7
   auto load_m = [&](int p, f32x4 (&a)[8]) {
     const float* Mp = M + (((size_t)seq * P + p) * H + h) * (size_t)kC128 * kC128 +
-                      (size_t)(row0 + n) * kC128 + 32 * g;
+                      (size_t)(row0 + n) * kC128 + 4 * g;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const f32x4*>(Mp + 4 * i);
+    for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const f32x4*>(Mp + 16 * i);
   };
   // entries (row0 + 4g + e, c0 + n) of b_p
   auto load_b = [&](int p, f32x4& v) {
@@ -132,7 +133,7 @@ __global__ void __launch_bounds__(512) compose128_kernel(const float* __restrict
     f32x4 acc = bv;
     f32x4 bc[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) bc[i] = *reinterpret_cast<const f32x4*>(&curT[n][32 * g + 4 * i]);
+    for (int i = 0; i < 8; ++i) bc[i] = *reinterpret_cast<const f32x4*>(&curT[n][16 * i + 4 * g]);
     f32x4 an[8];
     if (p + 1 < P - 1) {
       load_m(p + 1, an);
