@@ -45,10 +45,11 @@ def test_transition_matches_oracle():
     assert torch.equal(M[4].cpu(), eye[4])   # empty sequence: the identity
 
 
-def test_compose_matches_fp64_chain():
-    _print_case("compose, fp32")
-    gen = torch.Generator().manual_seed(32)
-    nseq, P, H, Dk, Dv = 2, 5, 3, 128, 40
+@pytest.mark.parametrize("P,Dv,Dk", [(5, 40, 128), (1, 16, 128), (2, 128, 128), (3, 7, 128), (4, 24, 64)])
+def test_compose_matches_fp64_chain(P, Dv, Dk):
+    _print_case(f"compose, fp32, P={P} Dk={Dk} Dv={Dv}")
+    gen = torch.Generator().manual_seed(32 + P)
+    nseq, H = 2, 3
     M = (torch.eye(Dk) + 0.05 * torch.randn(nseq * P, H, Dk, Dk, generator=gen)).contiguous()
     b = torch.randn(nseq * P, H, Dk, Dv, generator=gen)
     S0 = torch.randn(nseq, H, Dk, Dv, generator=gen)
