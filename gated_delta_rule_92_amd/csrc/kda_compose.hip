@@ -87,7 +87,8 @@ __global__ void __launch_bounds__(512) compose128_kernel(const float* __restrict
                                                          const float* __restrict__ b,
                                                          const float* __restrict__ S0, int P, int H,
                                                          int Dv, float* __restrict__ starts) {
-  __shared__ __attribute__((aligned(16))) float curT[kComposeCols][kCT];
+  // ping-pong: step p reads slice p & 1 and writes slice (p + 1) & 1
+  __shared__ __attribute__((aligned(16))) float curT2[2][kComposeCols][kCT];
   const int sh = blockIdx.x;  // sequence * H + head
   const int seq = sh / H, h = sh % H;
   const int c0 = blockIdx.y * kComposeCols;
@@ -99,8 +100,8 @@ __global__ void __launch_bounds__(512) compose128_kernel(const float* __restrict
 
   for (int i = tid; i < kComposeCols * kC128; i += 512) {
     const int col = i % kComposeCols, row = i / kComposeCols;
-    curT[col][row] = (S0 && c0 + col < Dv) ? S0[(((size_t)seq * H + h) * kC128 + row) * Dv + c0 + col]
-                                           : 0.f;
+    curT2[0][col][row] = (S0 && c0 + col < Dv) ? S0[(((size_t)seq * H + h) * kC128 + row) * Dv + c0 + col]
+                                               : 0.f;
   }
   // row row0 + n of M_p, entries 16i + 4g .. 16i + 4g + 3 for i = 0..7
   auto load_m = [&](int p, f32x4 (&a)[8]) {
@@ -123,6 +124,8 @@ __global__ void __launch_bounds__(512) compose128_kernel(const float* __restrict
   __syncthreads();
 
   for (int p = 0; p < P; ++p) {
+    float (*curT)[kCT] = curT2[p & 1];
+    float (*nxtT)[kCT] = curT2[(p + 1) & 1];
     const size_t sp = (size_t)seq * P + p;
     float* out = starts + (sp * H + h) * (size_t)kC128 * Dv;
     if (cvalid) {
@@ -130,7 +133,8 @@ __global__ void __launch_bounds__(512) compose128_kernel(const float* __restrict
       for (int e = 0; e < 4; ++e) out[(size_t)(row0 + 4 * g + e) * Dv + c0 + n] = curT[n][row0 + 4 * g + e];
     }
     if (p == P - 1) break;
-    f32x4 acc = bv;
+    // four independent accumulation chains, one per e
+    f32x4 acc[4] = {bv, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     f32x4 bc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) bc[i] = *reinterpret_cast<const f32x4*>(&curT[n][16 * i + 4 * g]);
@@ -142,10 +146,11 @@ __global__ void __launch_bounds__(512) compose128_kernel(const float* __restrict
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(am[i][e], bc[i][e], acc, 0, 0, 0);
-    __syncthreads();  // every wavefront has read the slice
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[i][e], bc[i][e], acc[e], 0, 0, 0);
+    const f32x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    // the other slice was last read in step p - 1, before that step's barrier
 #pragma unroll
-    for (int e = 0; e < 4; ++e) curT[n][row0 + 4 * g + e] = acc[e];
+    for (int e = 0; e < 4; ++e) nxtT[n][row0 + 4 * g + e] = sum[e];
 #pragma unroll
     for (int i = 0; i < 8; ++i) am[i] = an[i];
     __syncthreads();
