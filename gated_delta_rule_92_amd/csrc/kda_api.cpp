@@ -291,11 +291,24 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
     float* starts = reinterpret_cast<float*>(ws + split.starts);
     const int P = split.P;
     const int nseq = s.N;
-    hipError_t e = kda::launch_split_pieces(cu, cu_seqlens, nseq, T, P, chunk, hs);
+    // packed sequences: the piece table from cu_seqlens, on the device;
+    // dense ones: the kernels derive the pieces from (T, P, Lp) and the split
+    // pass writes the same table
+    hipError_t e = hipSuccess;
     kda::ChunkArgs a;
     a.k = k; a.g = g; a.gate_mode = (int)gate_input;
     a.A_log = A_log; a.g_min = g_min; a.beta = beta;
-    a.seqs.cu = cu; a.seqs.N = nseq * P; a.seqs.T = T; a.seqs.Ttot = s.Ttot;
+    a.seqs.N = nseq * P; a.seqs.T = T; a.seqs.Ttot = s.Ttot;
+    if (cu_seqlens) {
+      e = kda::launch_split_pieces(cu, cu_seqlens, nseq, T, P, chunk, hs);
+      a.seqs.cu = cu;
+    } else {
+      const long per = ((long)T + P - 1) / P;
+      a.seqs.cu = nullptr;
+      a.seqs.split_P = P;
+      a.seqs.split_Lp = (int)((per + chunk - 1) / chunk * chunk);
+      a.piece_table = cu;
+    }
     a.order = nullptr;
     a.H = H; a.Dk = Dk; a.Dv = Dv; a.scale = scale; a.bf16 = bf16;
     if (e == hipSuccess) {

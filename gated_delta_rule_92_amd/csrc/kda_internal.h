@@ -17,6 +17,12 @@ struct Seqs {
   int N;
   int T;        // dense sequence length (ignored when cu != nullptr)
   long Ttot;    // total tokens in the packed token axis
+  // dense context split (cu == nullptr, pipelined kernel only): the N units
+  // are N / split_P sequences of T tokens, each in split_P pieces of
+  // split_Lp tokens, unit n = piece n % split_P of sequence n / split_P
+  // covering its tokens [min(p Lp, T), min((p + 1) Lp, T))
+  int split_P = 0;
+  int split_Lp = 0;
 };
 
 hipError_t launch_gate(const float* z, const float* A_log, float g_min, Seqs s, int H, int Dk,
@@ -76,6 +82,9 @@ struct ChunkArgs {
   void* ck_vt = nullptr;
   float* ck_at = nullptr;  // checkpoint mode: A_kk / beta per tile row, fp32 [Ttot, H, 16]
   float* hT2 = nullptr;    // split pass: zero-start final states [N, H, Dk, Dv]
+  // split pass over a dense split (seqs.split_P > 0): receives the piece
+  // table, out[i] = start of unit i, out[N] = the total (int32, N + 1)
+  int32_t* piece_table = nullptr;
   // pipelined kernel, > 0: the N units are N / hT_group sequences of hT_group
   // consecutive pieces, and only each sequence's last piece writes its final
   // state, to hT[n / hT_group]

@@ -225,7 +225,8 @@ kda_status_t kda_chunk_fwd_split_workspace_size(int B, int T, int H, int Dk, int
  * a context split. The KDA equation is linear in the state [KDA-blog §Kimi
  * Delta Attention, KDA equation], so a piece's final state is M S_entry + b
  * with M its state map and b its zero-start final state. On the stream, in
- * order: the piece table (computed on the device from cu_seqlens); M and b
+ * order: the piece table (computed on the device from cu_seqlens; dense
+ * pieces follow from T and are written by the next launch); M and b
  * of every piece (what kda_chunk_transition and the state-only forward
  * compute, in one launch that reads k, v, g and beta once); the entry states
  * chained per sequence (kda_compose_states); every piece from its entry
