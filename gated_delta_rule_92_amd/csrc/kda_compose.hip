@@ -72,14 +72,16 @@ __global__ void __launch_bounds__(kComposeThreads) compose_kernel(const float* _
 
 // Dk = 128 on fp32 matrix cores: a workgroup of 8 wavefronts per (sequence,
 // head, 16 value columns); wavefront w forms rows [16w, 16w + 16) of each next
-// entry state, start_{p+1} = M_p start_p + b_p, as 32 16x16x4 products with
-// b_p as the initial accumulator. The contraction index is taken as
-// k = 16 i + 4 g + e (g = lane / 16; i, e the product's step), so that the
-// four lanes of a row read 64 consecutive bytes of M_p per 16-byte load
-// (eight loads per lane, issued one step ahead; a sixteenth of the cache lines
-// a lane-per-row split would touch per load) and the matching entries of
-// their column of the running slice, which is kept transposed in LDS. The
-// lane's four entries of b_p are loaded one step ahead as well.
+// entry state, start_{p+1} = M_p start_p + b_p, as 32 16x16x4 products in
+// four independent accumulation chains (one per e below), b_p starting the
+// first. The contraction index is taken as k = 16 i + 4 g + e (g = lane / 16;
+// i, e the product's step), so that the four lanes of a row read 64
+// consecutive bytes of M_p per 16-byte load (eight loads per lane, issued one
+// step ahead; 16 cache lines per load instead of the 64 that a lane reading
+// its own 128-byte segment touches) and the matching entries of their column
+// of the running slice. The slice is kept transposed and double-buffered in
+// LDS, so one barrier per step suffices. The lane's four entries of b_p are
+// loaded one step ahead as well.
 constexpr int kC128 = 128;
 constexpr int kCT = kC128 + 4;  // padded row of the transposed slice
 
