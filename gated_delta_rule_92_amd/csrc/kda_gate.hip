@@ -54,7 +54,8 @@ __device__ __forceinline__ long seq_begin(const Seqs& s, int n) {
 }
 
 // Gate + chunk-local cumsum. Thread = (window of `chunk` tokens aligned to
-// the global token axis, head, 4 channels). A chunk of a sequence spans at
+// the global token axis, head, 4 channels); a workgroup takes every
+// (gridDim.x / col_blocks)-th window. A chunk of a sequence spans at
 // most two windows; when the window starts inside a chunk, the thread first
 // sums the part of that chunk lying before the window (re-reading z, mostly
 // from L2).
@@ -63,40 +64,51 @@ __global__ void __launch_bounds__(256) gate_cumsum_kernel(
     int Dk4, int chunk, int col_blocks, float* __restrict__ g) {
   int ncol = H * Dk4;
   int col = (blockIdx.x % col_blocks) * blockDim.x + threadIdx.x;
-  long w = blockIdx.x / col_blocks;
   if (col >= ncol) return;
   int h = col / Dk4;
   float es = A_log ? __expf(A_log[h]) : 1.0f;
-  long t0 = w * chunk;
-  long t1 = t0 + chunk < s.Ttot ? t0 + chunk : s.Ttot;
-  if (t0 >= t1) return;
-  int n = s.cu ? find_seq(s.cu, s.N, t0) : (int)(t0 / s.T);
-  long bos = seq_begin(s, n);
-  long eos = s.cu ? (long)s.cu[n + 1] : bos + s.T;
-  long cs = bos + ((t0 - bos) / chunk) * chunk;  // start of the chunk holding t0
   const f32x4* z4 = reinterpret_cast<const f32x4*>(z);
   f32x4* g4 = reinterpret_cast<f32x4*>(g);
-  f32x4 run = {0.f, 0.f, 0.f, 0.f};
-  for (long t = cs; t < t0; ++t) {
-    f32x4 x = z4[t * ncol + col];
-    run[0] += gate_value(x[0], es, g_min);
-    run[1] += gate_value(x[1], es, g_min);
-    run[2] += gate_value(x[2], es, g_min);
-    run[3] += gate_value(x[3], es, g_min);
-  }
-  for (long t = t0; t < t1; ++t) {
-    while (t >= eos) {  // crossed into the next non-empty sequence
-      ++n;
-      bos = seq_begin(s, n);
-      eos = s.cu ? (long)s.cu[n + 1] : bos + s.T;
+  const long nwin = (s.Ttot + chunk - 1) / chunk;
+  const long wstride = gridDim.x / col_blocks;
+  // a bounded grid strides over the windows
+  for (long w = blockIdx.x / col_blocks; w < nwin; w += wstride) {
+    long t0 = w * chunk;
+    long t1 = t0 + chunk < s.Ttot ? t0 + chunk : s.Ttot;
+    int n = s.cu ? find_seq(s.cu, s.N, t0) : (int)(t0 / s.T);
+    long bos = seq_begin(s, n);
+    long eos = s.cu ? (long)s.cu[n + 1] : bos + s.T;
+    long cs = bos + ((t0 - bos) / chunk) * chunk;  // start of the chunk holding t0
+    f32x4 run = {0.f, 0.f, 0.f, 0.f};
+    for (long t = cs; t < t0; ++t) {
+      f32x4 x = z4[t * ncol + col];
+      run[0] += gate_value(x[0], es, g_min);
+      run[1] += gate_value(x[1], es, g_min);
+      run[2] += gate_value(x[2], es, g_min);
+      run[3] += gate_value(x[3], es, g_min);
     }
-    if ((t - bos) % chunk == 0) run = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 x = z4[t * ncol + col];
-    run[0] += gate_value(x[0], es, g_min);
-    run[1] += gate_value(x[1], es, g_min);
-    run[2] += gate_value(x[2], es, g_min);
-    run[3] += gate_value(x[3], es, g_min);
-    g4[t * ncol + col] = run;
+    // eight tokens' loads in flight per lane, then their serial sums
+    for (long tb = t0; tb < t1; tb += 8) {
+      f32x4 xs[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xs[j] = tb + j < t1 ? z4[(tb + j) * ncol + col] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const long t = tb + j;
+        if (t >= t1) break;
+        while (t >= eos) {  // crossed into the next non-empty sequence
+          ++n;
+          bos = seq_begin(s, n);
+          eos = s.cu ? (long)s.cu[n + 1] : bos + s.T;
+        }
+        if ((t - bos) % chunk == 0) run = f32x4{0.f, 0.f, 0.f, 0.f};
+        run[0] += gate_value(xs[j][0], es, g_min);
+        run[1] += gate_value(xs[j][1], es, g_min);
+        run[2] += gate_value(xs[j][2], es, g_min);
+        run[3] += gate_value(xs[j][3], es, g_min);
+        g4[t * ncol + col] = run;
+      }
+    }
   }
 }
 
@@ -114,7 +126,9 @@ hipError_t launch_gate(const float* z, const float* A_log, float g_min, Seqs s, 
     int ncol = H * Dk4;
     int col_blocks = (ncol + 255) / 256;
     long windows = (s.Ttot + chunk - 1) / chunk;
-    long blocks = windows * col_blocks;
+    // about 512 workgroups: HBM streams best from a few deep streams per CU
+    const long wcap = col_blocks >= 512 ? 1 : 512 / col_blocks;
+    long blocks = (windows < wcap ? windows : wcap) * col_blocks;
     if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(gate_cumsum_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, z, A_log,
                        g_min, s, H, Dk4, chunk, col_blocks, g);
