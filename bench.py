@@ -6,6 +6,11 @@ inter-chunk state scan and the output, all inside the library's kernels. The
 workload is the training-shaped batch B=8, H=32, T=8192, d_k=d_v=128, bf16,
 chunk 64, zero initial state (synthetic, seeded; inputs resident in HBM).
 
+Before the W warm-up steps, the step is run untimed for at least 200 ms
+(`prewarm_ms` in the line): a fresh GPU ramps its clocks over the first
+tens of launches, and a short warm-up would time that ramp. The timed loop is
+unchanged by it.
+
 Prints one JSON line. `roofline` reports the fused chunk kernel against HBM
 bandwidth: algorithmic bytes per launch (q, k, v, o in bf16; gate logits and
 beta in fp32; the fp32 state written once per (sequence, head)) divided by the
@@ -44,6 +49,10 @@ BWD_KERNEL_SOURCES = KERNEL_SOURCES + [os.path.join(ROOT, "gated_delta_rule_92_a
                                                     "kda_backward.hip")]
 
 
+PREWARM_MS = 200.0
+PROBE_LIB = os.path.join(ROOT, "libhbm_probe.so")
+
+
 def log(msg: str):
     print(msg, file=sys.stderr, flush=True)
 
@@ -74,6 +83,16 @@ def algorithmic_flops(w, n_tokens: int) -> float:
     P, dk, dv = 16, w.Dk, w.Dv
     per_tile = 2 * (2 * P * P * dk) + 3 * (2 * P * dk * dv) + 2 * (2 * P * P * dv)
     return per_tile / P * n_tokens * w.H
+
+
+def chunk_form_flops(w, n_tokens: int) -> float:
+    """Matrix-core flops of the pages' chunk form with C = 64 per token·head
+    (causal 16-row tiles of the intra-chunk products, the three state
+    products, the 64x64 triangular inverse): 2C(3 d_k + 2 d_v) 5/8 +
+    6 d_k d_v + about 2,219 for the inverse."""
+    C = w.chunk
+    per = 2 * C * (3 * w.Dk + 2 * w.Dv) * 5 / 8 + 6 * w.Dk * w.Dv + 2219
+    return per * n_tokens * w.H
 
 
 def backward_algorithmic_bytes(w, n_tokens: int, n_units: int) -> int:
@@ -107,8 +126,8 @@ def backward_design_bytes(w, n_tokens: int, n_units: int) -> int:
 def cpu_baseline_backward(d, do, dhT, w, budget_s: float = 15.0):
     """The fp64 oracle's backward on a bounded sample of (sequence, head)
     units (each keeps T+1 states of d_k*d_v doubles, so at most 8 threads)."""
-    from oracle import oracle_backward, oracle_gate
-    cores = min(os.cpu_count() or 1, 8)
+    from oracle import host_threads, oracle_backward, oracle_gate
+    cores = min(host_threads(), 8)
     B, T, H = d["q"].shape[0], d["q"].shape[1], d["q"].shape[2]
 
     def run(units, threads):
@@ -138,12 +157,14 @@ def cpu_baseline_backward(d, do, dhT, w, budget_s: float = 15.0):
 
 def cpu_baseline(d, w, budget_s: float = 25.0):
     """The fp64 oracle on a bounded sample of (sequence, head) units of the
-    same workload, on the host cores; returns a dict for the JSON line.
-    The sample holds about `budget_s` seconds of single-thread oracle work
-    (at most the whole workload), spread over up to 16 threads."""
+    same workload, on the host cores this process may use (at most the host
+    share of one GPU, 16 threads); returns a dict for the JSON line. The
+    sample holds about `budget_s` seconds of single-thread oracle work (at most
+    the whole workload). One unit is also timed on one thread: the per-core
+    rate."""
     import numpy as np
-    from oracle import oracle_forward
-    cores = min(os.cpu_count() or 1, 16)
+    from oracle import host_threads, oracle_forward
+    cores = host_threads()
     T = d["q"].shape[1]
     H = d["q"].shape[2]
 
@@ -160,7 +181,7 @@ def cpu_baseline(d, w, budget_s: float = 25.0):
         cat = lambda xs: torch.cat(xs, 0)[None, :, None]  # noqa: E731
         return cat(qs), cat(ks), cat(vs), cat(zs), torch.cat(bs, 0)[None, :, None], cu
 
-    # one unit on one thread to size the sample
+    # one unit on one thread: the per-core rate, and the size of the sample
     q, k, v, z, b, cu = unit_inputs([(0, 0)])
     t0 = time.perf_counter()
     oracle_forward(q, k, v, z, b, None, cu, None, w.g_min, 1.0, nthreads=1)
@@ -173,10 +194,18 @@ def cpu_baseline(d, w, budget_s: float = 25.0):
     t0 = time.perf_counter()
     oracle_forward(q, k, v, z, b, None, cu, None, w.g_min, 1.0, nthreads=cores)
     wall = time.perf_counter() - t0
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
     return {"value": n_units * T / wall, "unit": "tokens·heads/s", "cores": cores,
             "kind": "oracle",
+            "per_core_value": T / per_unit,
+            "nproc": os.cpu_count(), "usable_cores": affinity,
             "sample": f"{n_units} (sequence, head) units x {T} tokens of the {w.name} workload, "
-                      f"fp64 token-by-token recurrence, {cores} threads, {wall:.1f} s wall"}
+                      f"fp64 token-by-token recurrence, {cores} threads (host share of one GPU; "
+                      f"{affinity} usable of {os.cpu_count()} cores), {wall:.1f} s wall; "
+                      f"per_core_value: one unit on one thread, {per_unit:.2f} s"}
 
 
 def copy_calibration(n_bytes: int = 1 << 30):
@@ -212,8 +241,66 @@ def copy_bandwidth(dev, n_bytes: int = 1 << 30, reps: int = 10) -> float:
     return gbs
 
 
+def prewarm(step, min_ms: float = PREWARM_MS):
+    """Runs `step` untimed until at least `min_ms` of wall time has passed
+    (synchronising after each batch of launches). Returns (launches, ms)."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(4):
+            step()
+        n += 4
+        torch.cuda.synchronize()
+    return n, (time.perf_counter() - t0) * 1e3
+
+
+def probe_copy_bandwidth(dev, n_bytes: int = 1 << 30, reps: int = 10):
+    """Rate of the hand-written HBM copy in libhbm_probe.so (bench_hbm.hip:
+    four 16-byte loads in flight per lane, then the stores), best over grids
+    of 256, 512 and 1024 workgroups: bytes read + bytes written per second
+    (GB/s), timed with HIP events on the stream it is launched on. Returns
+    (GB/s, grid) or (None, None) if the probe is not built."""
+    import ctypes
+
+    import torch
+    if not os.path.exists(PROBE_LIB):
+        return None, None
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.hbm_copy_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                    ctypes.c_int, ctypes.c_void_p]
+    lib.hbm_copy_launch.restype = ctypes.c_int
+    x = torch.empty(n_bytes // 4, dtype=torch.float32, device=dev).normal_()
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+    best, best_grid = 0.0, None
+    for grid in (256, 512, 1024):
+        def launch():
+            rc = lib.hbm_copy_launch(x.data_ptr(), y.data_ptr(), n_bytes // 16, grid,
+                                     stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"hbm_copy_launch failed: {rc}")
+        for _ in range(3):
+            launch()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gbs = 2 * n_bytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+        if gbs > best:
+            best, best_grid = gbs, grid
+    if not torch.equal(x, y):
+        raise RuntimeError("hbm probe copy is wrong")
+    del x, y
+    torch.cuda.empty_cache()
+    return best, best_grid
+
+
 def _timed(step, steps, warmup, dev):
     import torch
+    prewarm(step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -330,8 +417,8 @@ def bench_decode(args, d, w, dev):
     if not args.skip_cpu_baseline:
         # the oracle's token recurrence on one token per unit from the same
         # state, repeated for about 5 s
-        from oracle import oracle_forward
-        cores = min(os.cpu_count() or 1, 16)
+        from oracle import host_threads, oracle_forward
+        cores = host_threads()
         hq, hk, hv, hz, hb = (x.cpu()[:, None] for x in (q, k, v, z, beta))
         h0 = state.cpu()
         reps, t0 = 0, time.perf_counter()
@@ -521,6 +608,7 @@ def main(argv=None):
         if args.epilogue == "separate":
             gated_rmsnorm(o, out_gate, norm_w, 1e-6, y=y)
 
+    prewarm_n, prewarm_ms = prewarm(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -558,14 +646,18 @@ def main(argv=None):
         if rec.get("source_sha256") == kernel_source_hash() and rec.get("workload") == w.name:
             traffic = rec.get("bytes_per_launch")
 
-    copy_gbs = copy_bandwidth(dev)
-    log(f"bench: device copy {copy_gbs:.0f} GB/s; kernel at {achieved / copy_gbs:.1%} of it")
+    torch_copy_gbs = copy_bandwidth(dev)
+    probe_gbs, probe_grid = probe_copy_bandwidth(dev)
+    copy_gbs = probe_gbs if probe_gbs else torch_copy_gbs
+    log(f"bench: hand-written copy {probe_gbs or 0:.0f} GB/s (grid {probe_grid}), torch copy "
+        f"{torch_copy_gbs:.0f} GB/s; kernel at {achieved / copy_gbs:.1%} of the first")
 
     cpu = None
     if not args.skip_cpu_baseline and d["cu_seqlens"] is None:
         log("bench: timing the fp64 oracle on a bounded sample (cpu_baseline)")
         cpu = cpu_baseline(d, w)
 
+    peak_tf = BF16_DENSE_PEAK_TFLOPS if w.dtype_name == "bf16" else FP32_MATRIX_PEAK_TFLOPS
     line = {
         "metric": "KDA chunk fwd tokens·heads/s (H=32,d=128,bf16,T=8K); % MFMA peak",
         "value": value,
@@ -585,10 +677,14 @@ def main(argv=None):
                    "sequences": N, "segments": segments, "epilogue": args.epilogue},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
-        "mfma_peak_frac": flops / (kernel_ms / 1e3) / (BF16_DENSE_PEAK_TFLOPS * 1e12)
-        if w.dtype_name == "bf16" else flops / (kernel_ms / 1e3) / (FP32_MATRIX_PEAK_TFLOPS * 1e12),
+        "mfma_peak_frac": chunk_form_flops(w, n_tokens) / (kernel_ms / 1e3) / (peak_tf * 1e12),
+        "mfma_peak_frac_tile_form": flops / (kernel_ms / 1e3) / (peak_tf * 1e12),
         "copy_gbs": copy_gbs,
+        "copy_kind": "hand-written copy (bench_hbm.hip), best grid" if probe_gbs else "torch copy",
+        "torch_copy_gbs": torch_copy_gbs,
         "frac_of_copy": achieved / copy_gbs,
+        "prewarm_ms": prewarm_ms,
+        "prewarm_launches": prewarm_n,
         "kernel_ms": kernel_ms,
         "kernel_ms_median": launch_ms[len(launch_ms) // 2],
         "kernel_ms_min": launch_ms[0],

@@ -1,18 +1,22 @@
 // HBM stream rates on one GPU, the reference points for the roofline of the
 // memory-heavy kernels: a read-only sum (4 or 8 16-byte loads in flight per
 // lane), a copy, and five read streams into one write stream (about the
-// forward's ratio of bytes read to bytes written), each over 512 MiB buffers
-// at grids of 256 to 16384 workgroups of 256 threads (one to 64 per compute
-// unit); best of 8 launches, timed with HIP events. Standalone:
-//   hipcc --offload-arch=gfx950 -O3 -Xclang -target-feature -Xclang -packed-fp32-ops \
-//     bench_hbm.hip -o bench_hbm && ./bench_hbm
+// forward's ratio of bytes read to bytes written).
+//
+// Two ways to use it:
+//   * as a library (libhbm_probe.so, built by gated_delta_rule_92_amd/build.py):
+//     bench.py launches `hbm_copy_launch` on buffers it owns and times it with
+//     HIP events on its stream; the best rate is the measured copy ceiling
+//     reported beside the spec peak. Nothing here allocates.
+//   * standalone, with a main() that sweeps grids of 256 to 16384 workgroups
+//     over 512 MiB buffers (best of 8 launches, HIP events):
+//       hipcc --offload-arch=gfx950 -O3 -Xclang -target-feature -Xclang -packed-fp32-ops \
+//         -DHBM_PROBE_MAIN bench_hbm.hip -o bench_hbm && ./bench_hbm
 #include <hip/hip_runtime.h>
 #include <cstdio>
 #include <cstdlib>
 
 typedef float f4 __attribute__((ext_vector_type(4)));
-
-#define CK(x) do { hipError_t e_ = (x); if (e_ != hipSuccess) { printf("HIP error %s at %d\n", hipGetErrorString(e_), __LINE__); exit(1); } } while (0)
 
 template <int U>
 __global__ void read_sum(const f4* __restrict__ a, size_t n4, float* __restrict__ out) {
@@ -32,6 +36,8 @@ __global__ void read_sum(const f4* __restrict__ a, size_t n4, float* __restrict_
   out[gid] = acc.x + acc.y + acc.z + acc.w;
 }
 
+// Each lane moves U 16-byte elements per step, all loads issued before the
+// stores; the grid strides over the buffer.
 template <int U>
 __global__ void copy4(const f4* __restrict__ a, f4* __restrict__ b, size_t n4) {
   const size_t gid = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
@@ -58,6 +64,19 @@ __global__ void mix51(const f4* __restrict__ a0, const f4* __restrict__ a1, cons
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = gid; i < n4; i += stride) b[i] = a0[i] + a1[i] + a2[i] + a3[i] + a4[i];
 }
+
+// Enqueues one copy of n16 16-byte elements from src to dst (device pointers,
+// 16-byte aligned, not overlapping) on `stream` with `grid` workgroups of 256
+// threads. Returns 0, or the HIP error code of the launch.
+extern "C" int hbm_copy_launch(const void* src, void* dst, size_t n16, int grid, void* stream) {
+  if (grid <= 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy4<4>, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const f4*>(src), static_cast<f4*>(dst), n16);
+  return (int)hipGetLastError();
+}
+
+#ifdef HBM_PROBE_MAIN
+#define CK(x) do { hipError_t e_ = (x); if (e_ != hipSuccess) { printf("HIP error %s at %d\n", hipGetErrorString(e_), __LINE__); exit(1); } } while (0)
 
 int main() {
   const size_t bytes = (size_t)512 << 20;
@@ -112,3 +131,4 @@ int main() {
   CK(hipDeviceSynchronize());
   return 0;
 }
+#endif

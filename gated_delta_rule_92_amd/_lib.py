@@ -8,7 +8,12 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+# KDA_HOST_CHECK_LIB names a host-check build of the C ABI (argument
+# validation and dispatch compiled with sanitizers, kernel launches replaced by
+# stubs that do nothing): used only by the CPU sanitizer test, it computes
+# nothing.
+LIB_PATH = os.environ.get("KDA_HOST_CHECK_LIB") or \
+    os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
 KDA_SUCCESS = 0
 KDA_ERROR_INVALID_VALUE = 1

@@ -17,6 +17,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libkda.so")
+# the HBM copy probe bench.py times beside the spec peak (measurement only,
+# not part of the library)
+PROBE_SRC = os.path.join(ROOT, "bench_hbm.hip")
+PROBE_PATH = os.path.join(ROOT, "libhbm_probe.so")
 ARCH = "gfx950"
 
 SOURCES = ["kda_api.cpp", "kda_gate.hip", "kda_recurrent.hip", "kda_chunk.hip", "kda_chunk_pipe.hip", "kda_backward.hip",
@@ -50,10 +54,23 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def build_probe(verbose: bool = False) -> str:
+    """libhbm_probe.so: the hand-written HBM copy bench.py measures."""
+    tmp = PROBE_PATH + ".tmp"
+    cmd = [hipcc(), "-x", "hip", "-shared", PROBE_SRC, "-o", tmp] + COMMON_FLAGS
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, PROBE_PATH)
+    return PROBE_PATH
+
+
 def build(jobs: int = 4, verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        probe = ex.submit(build_probe, verbose)
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        probe.result()
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     if verbose:

@@ -1038,17 +1038,9 @@ hipError_t launch_bwd_d(const BwdArgs& a, int Dk, int Dv, long slots, hipStream_
 
 }  // namespace
 
-bool chunk_bwd_supported(int Dk, int Dv) {
-  return (Dk == 64 || Dk == 128) && (Dv == 64 || Dv == 128);
-}
-
-int chunk_bwd_checkpoint_tokens(bool bf16) { return BT * (bf16 ? ckt_of<__bf16>() : ckt_of<float>()); }
-
-long chunk_bwd_slots(const Seqs& s, bool bf16) {
-  const int CT = chunk_bwd_checkpoint_tokens(bf16);
-  if (s.cu) return s.Ttot / CT + s.N;
-  return (long)s.N * ((s.T + CT - 1) / CT);
-}
+static_assert(BT * ckt_of<__bf16>() == kBwdCheckpointTokensBf16 &&
+                  BT * ckt_of<float>() == kBwdCheckpointTokensFp32,
+              "checkpoint spacing the host sizes the workspace with");
 
 hipError_t launch_chunk_bwd(const BwdArgs& a, bool bf16, int Dk, int Dv, long slots,
                             hipStream_t stream) {

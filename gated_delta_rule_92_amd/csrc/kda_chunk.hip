@@ -641,11 +641,7 @@ __global__ void __launch_bounds__(1024) order_kernel(const int32_t* __restrict__
 
 }  // namespace
 
-bool chunk_fused_supported(bool bf16, int Dk, int Dv, int chunk) {
-  if (chunk != C) return false;
-  if (bf16) return (Dk == 64 || Dk == 128) && (Dv == 64 || Dv == 128);
-  return Dk == 64 && Dv == 64;
-}
+static_assert(C == kChunkTokens, "chunk length the host dispatches on");
 
 hipError_t launch_chunk_fused(const ChunkArgs& a, hipStream_t stream) {
   if (a.seqs.N == 0 || a.H == 0) return hipSuccess;

@@ -1014,9 +1014,7 @@ __global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : 
 
 }  // namespace
 
-bool chunk_pipe_supported(bool bf16, int Dk, int Dv, int chunk) {
-  return bf16 && Dk == PDK && Dv == PDV && chunk == 64;
-}
+static_assert(PDK == 128 && PDV == 128, "shape chunk_pipe_supported dispatches");
 
 template <int MODE>
 static void launch_pipe_t(const ChunkArgs& a, hipStream_t stream) {

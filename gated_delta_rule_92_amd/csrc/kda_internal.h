@@ -90,9 +90,18 @@ struct ChunkArgs {
   // state, to hT[n / hT_group]
   int hT_group = 0;
 };
-bool chunk_fused_supported(bool bf16, int Dk, int Dv, int chunk);
+// Shapes the tile kernel instantiates: chunk 64; bf16 with Dk, Dv in
+// {64, 128}; fp32 with Dk = Dv = 64.
+constexpr int kChunkTokens = 64;
+inline bool chunk_fused_supported(bool bf16, int Dk, int Dv, int chunk) {
+  if (chunk != kChunkTokens) return false;
+  if (bf16) return (Dk == 64 || Dk == 128) && (Dv == 64 || Dv == 128);
+  return Dk == 64 && Dv == 64;
+}
 // Pipelined producer/consumer chunk kernel (bf16, Dk = Dv = 128).
-bool chunk_pipe_supported(bool bf16, int Dk, int Dv, int chunk);
+inline bool chunk_pipe_supported(bool bf16, int Dk, int Dv, int chunk) {
+  return bf16 && Dk == 128 && Dv == 128 && chunk == kChunkTokens;
+}
 hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t stream);
 // Same kernel in transition mode: writes M (a.hT, [N, H, Dk, Dk]) with
 // S_final = M S_initial + S_final(0); reads k, g and beta only.
@@ -161,9 +170,19 @@ struct BwdArgs {
   float* At;           // [Ttot, H, 16] row r of each tile's A~ = A_kk / beta
                        // (strictly lower part; zeros elsewhere)
 };
-bool chunk_bwd_supported(int Dk, int Dv);
-int chunk_bwd_checkpoint_tokens(bool bf16);
-long chunk_bwd_slots(const Seqs& s, bool bf16);
+inline bool chunk_bwd_supported(int Dk, int Dv) {
+  return (Dk == 64 || Dk == 128) && (Dv == 64 || Dv == 128);
+}
+// Tokens between checkpoints: four 16-token tiles for bf16, one for fp32.
+constexpr int kBwdCheckpointTokensBf16 = 64, kBwdCheckpointTokensFp32 = 16;
+inline int chunk_bwd_checkpoint_tokens(bool bf16) {
+  return bf16 ? kBwdCheckpointTokensBf16 : kBwdCheckpointTokensFp32;
+}
+inline long chunk_bwd_slots(const Seqs& s, bool bf16) {
+  const int CT = chunk_bwd_checkpoint_tokens(bf16);
+  if (s.cu) return s.Ttot / CT + s.N;
+  return (long)s.N * ((s.T + CT - 1) / CT);
+}
 hipError_t launch_chunk_bwd(const BwdArgs& a, bool bf16, int Dk, int Dv, long slots,
                             hipStream_t stream);
 // Gradient of the gate w.r.t. z (dz, may alias dg) and, if dA != nullptr,

@@ -20,5 +20,6 @@ from .oracle import (  # noqa: F401
     oracle_forward_softplus,
     oracle_gate_softplus,
     library_path,
+    host_threads,
 )
 from .epilogue import oracle_gated_rmsnorm  # noqa: F401

@@ -23,6 +23,20 @@ _LIB_NAME = "libkda_oracle.so"
 _lib = None
 
 
+def host_threads() -> int:
+    """Threads the oracle runs on by default: the cores this process may use,
+    capped by OMP_NUM_THREADS (16 when unset), the host share of one GPU."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - non-Linux
+        avail = os.cpu_count() or 1
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "16"))
+    except ValueError:
+        cap = 16
+    return max(1, min(avail, cap if cap > 0 else 16))
+
+
 def library_path() -> str:
     return os.path.join(_HERE, _LIB_NAME)
 
@@ -42,6 +56,9 @@ def _load(path: Optional[str] = None):
     global _lib
     if path is not None:
         return _bind(ctypes.CDLL(path))
+    if _lib is None and os.environ.get("KDA_ORACLE_LIB"):
+        # a build of the same source with sanitizers (the CPU sanitizer test)
+        _lib = _bind(ctypes.CDLL(os.environ["KDA_ORACLE_LIB"]))
     if _lib is None:
         if not os.path.exists(library_path()) or (
                 os.path.getmtime(library_path()) < os.path.getmtime(_SRC)):
@@ -147,7 +164,7 @@ def oracle_recurrence(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
     h064 = None if initial_state is None else _f64(initial_state)
     o = np.zeros((B, T, H, Dv), dtype=np.float64)
     hT = np.zeros((N, H, Dk, Dv), dtype=np.float64)
-    nthreads = nthreads or os.cpu_count() or 1
+    nthreads = nthreads or host_threads()
     rc = lib.kda_oracle_recurrence(_dp(q64), _dp(k64), _dp(v64), _dp(g64), _dp(b64),
                                    _dp(h064), cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                                    N, H, Dk, Dv, float(scale), _dp(o), _dp(hT), int(nthreads))
@@ -179,7 +196,7 @@ def oracle_backward(q, k, v, g, beta, do, initial_state=None, d_final_state=None
     out = {"dq": np.zeros_like(q64), "dk": np.zeros_like(k64), "dv": np.zeros_like(v64),
            "dg": np.zeros_like(g64), "dbeta": np.zeros_like(b64),
            "dh0": np.zeros((N, H, Dk, Dv), dtype=np.float64)}
-    nthreads = nthreads or os.cpu_count() or 1
+    nthreads = nthreads or host_threads()
     rc = lib.kda_oracle_backward(_dp(q64), _dp(k64), _dp(v64), _dp(g64), _dp(b64), _dp(h064),
                                  cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), N, H, Dk, Dv,
                                  float(scale), _dp(do64), _dp(dhT64), _dp(out["dq"]),

@@ -13,8 +13,7 @@ import torch
 from gated_delta_rule_92_amd import chunk_fwd, chunk_fwd_split, compose_states, gate, transition
 from gated_delta_rule_92_amd.inputs import make_inputs, make_workload
 from oracle import oracle_forward, oracle_recurrence
-from tests.gpu_helpers import (TOL_BF16, TOL_FP32, compare_units, gpu_units, oracle_units, rel_err,
-                               to_dev)
+from tests.gpu_helpers import TOL_BF16, TOL_FP32, rel_err, to_dev
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -76,6 +75,9 @@ CASES = [
     ("varlen P=5 cumsum gate", dict(B=1, T=0, lengths=[700, 129, 64], h0_std=0.0), 5, "cumsum"),
     ("dense B=1 T=1000 P=8 logdecay", dict(B=1, T=1000, lengths=None, h0_std=0.02), 8,
      "logdecay"),
+    # Lp = 64: pieces 5-7 of each sequence are empty
+    ("dense B=2 T=300 P=8 empty trailing pieces", dict(B=2, T=300, lengths=None, h0_std=0.02), 8,
+     "logits"),
 ]
 
 
@@ -139,20 +141,49 @@ def test_packed_piece_table():
     assert rel_err(o, ref[0]) <= TOL_BF16
 
 
-def test_split_long256k_full_size_sampled():
+def test_split_long256k_explicit_equals_automatic():
     """The 256K-token single sequence at full size (32 heads), split into 8
-    segments so that all 256 units run at once; one head checked against the
-    oracle on a subset of value columns (exact by column separability)."""
-    _print_case("split forward: long256k, 8 segments")
+    segments explicitly, gives the same bits as kda_chunk_fwd's automatic
+    split (8 pieces of 32,768 tokens on a 256-CU device), whose every element
+    test_gpu_parity checks against the oracle."""
+    _print_case("split forward: long256k, explicit 8 segments vs automatic")
+    from gated_delta_rule_92_amd import workspace_size
     d = make_workload("long256k", device="cuda")
-    o, hT = chunk_fwd_split(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"], d["cu_seqlens"],
-                            segments=8, gate="logits")
+    ws = workspace_size(1, d["q"].shape[1], 32, 128, 128, 1, 64, torch.bfloat16)
+    wsp = torch.empty(ws, dtype=torch.uint8, device="cuda")
+    o_a, h_a = chunk_fwd(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"], d["cu_seqlens"],
+                         gate="logits", workspace=wsp)
     torch.cuda.synchronize()
-    units, cols = [(0, 5)], list(range(0, 128, 16))
-    ref = oracle_units(d, units, cols)
-    got = gpu_units(o, hT, d, units, cols)
-    eo, es = compare_units(got, ref)
-    print(f"  units={units} err_o={eo:.3e} err_state={es:.3e} tol={TOL_BF16:g}", flush=True)
+    Lp = int(wsp[4:8].view(torch.int32).item())
+    P = -(-d["q"].shape[1] // Lp)
+    print(f"  automatic split: P={P} Lp={Lp}", flush=True)
+    o_e, h_e = chunk_fwd_split(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"],
+                               d["cu_seqlens"], segments=P, gate="logits")
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_e) and torch.equal(h_a, h_e)
+
+
+def test_automatic_split_with_empty_trailing_pieces():
+    """B=1, H=16, T=4160: the automatic split takes P = 16 pieces of
+    Lp = 320 tokens, so pieces 13-15 are empty; every element against the
+    unsplit oracle."""
+    _print_case("automatic split, empty trailing pieces: B=1 H=16 T=4160")
+    from gated_delta_rule_92_amd import workspace_size
+    B, T, H = 1, 4160, 16
+    d = make_inputs(B, T, H, 128, 128, torch.bfloat16, h0_std=0.02, seed=37)
+    dd = to_dev(d)
+    ws = workspace_size(B, T, H, 128, 128, B, 64, torch.bfloat16)
+    wsp = torch.zeros(ws, dtype=torch.uint8, device="cuda")
+    o, hT = chunk_fwd(dd["q"], dd["k"], dd["v"], dd["z"], dd["beta"], dd["h0"], gate="logits",
+                      workspace=wsp)
+    torch.cuda.synchronize()
+    table = wsp[:4 * 17].view(torch.int32).cpu().tolist()
+    print(f"  piece table {table}", flush=True)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert table == [min(p * 320, T) for p in range(17)]
+    ref = oracle_forward(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"], None, None, -5.0)
+    eo, es = rel_err(o, ref[0]), rel_err(hT, ref[1])
+    print(f"  err_o={eo:.3e} err_state={es:.3e} tol={TOL_BF16:g}", flush=True)
     assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
