@@ -246,7 +246,7 @@ def prewarm(step, min_ms: float = PREWARM_MS):
     (synchronising after each batch of launches). Returns (launches, ms)."""
     import torch
     n, t0 = 0, time.perf_counter()
-    while (time.perf_counter() - t0) * 1e3 < min_ms:
+    while min_ms > 0 and (time.perf_counter() - t0) * 1e3 < min_ms:
         for _ in range(4):
             step()
         n += 4
@@ -298,9 +298,9 @@ def probe_copy_bandwidth(dev, n_bytes: int = 1 << 30, reps: int = 10):
     return best, best_grid
 
 
-def _timed(step, steps, warmup, dev):
+def _timed(step, steps, warmup, dev, prewarm_ms: float = PREWARM_MS):
     import torch
-    prewarm(step)
+    prewarm(step, prewarm_ms)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -335,7 +335,7 @@ def bench_backward(args, d, w, dev):
         chunk_bwd(d["q"], d["k"], d["v"], d["z"], d["beta"], do, d["h0"], dhT, d["cu_seqlens"],
                   gate="logits", g_min=w.g_min, chunk=w.chunk, workspace=workspace)
 
-    ms_per_step, launch_ms = _timed(step, args.steps, args.warmup, dev)
+    ms_per_step, launch_ms = _timed(step, args.steps, args.warmup, dev, args.prewarm_ms)
     kernel_ms = sum(launch_ms) / args.steps
     log(f"bench: backward {args.steps} steps, wall {ms_per_step:.3f} ms/step, "
         f"event {kernel_ms:.3f} ms/call")
@@ -405,7 +405,7 @@ def bench_decode(args, d, w, dev):
     def step():
         recurrent_step(q, k, v, z, beta, state, gate="logits", g_min=w.g_min, o=o)
 
-    ms_per_step, launch_ms = _timed(step, args.steps, args.warmup, dev)
+    ms_per_step, launch_ms = _timed(step, args.steps, args.warmup, dev, args.prewarm_ms)
     kernel_ms = sum(launch_ms) / args.steps
     el = 2 if w.dtype_name == "bf16" else 4
     units = N * w.H
@@ -471,7 +471,7 @@ def bench_gate(args, d, w, dev):
     def step():
         gate(z, None, w.g_min, w.chunk, d["cu_seqlens"], out=out)
 
-    ms_per_step, launch_ms = _timed(step, args.steps, args.warmup, dev)
+    ms_per_step, launch_ms = _timed(step, args.steps, args.warmup, dev, args.prewarm_ms)
     kernel_ms = sum(launch_ms) / args.steps
     elems = z.numel()
     bytes_alg = 8 * elems
@@ -535,6 +535,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--workload", default="train8k")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--prewarm-ms", type=float, default=PREWARM_MS,
+                    help="untimed launches before the warm-up steps, in ms of wall time (0: none; "
+                         "counter runs under a profiler use 0)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--gate", choices=["logits", "softplus"], default="logits",
                     help="logits: g = g_min sigmoid(z), diagonal tiles on matrix cores; softplus: "
@@ -608,7 +611,7 @@ def main(argv=None):
         if args.epilogue == "separate":
             gated_rmsnorm(o, out_gate, norm_w, 1e-6, y=y)
 
-    prewarm_n, prewarm_ms = prewarm(step)
+    prewarm_n, prewarm_ms = prewarm(step, args.prewarm_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -13,11 +13,13 @@ Public API (thin wrappers over the C ABI in include/kda.h):
     gated_rmsnorm(o, out_gate, norm_weight=None, eps=1e-6)
     chunk_bwd(q, k, v, g, beta, do, initial_state=None, d_final_state=None, ...)
     gate_bwd(z, dg, A_log=None, g_min=-5.0)
+    device_status(clear=False)        (device-side failure flags)
 """
 from .ops import (bwd_workspace_size, chunk_bwd, chunk_fwd, chunk_fwd_gated,  # noqa: F401
-                  chunk_fwd_split, compose_states, gate, gate_bwd, gated_rmsnorm, recurrent_step,
+                  chunk_fwd_split, debug_set_spin_limit, device_status, compose_states, gate, gate_bwd, gated_rmsnorm, recurrent_step,
                   transition, workspace_size)
 
-__all__ = ["bwd_workspace_size", "chunk_bwd", "chunk_fwd", "chunk_fwd_gated", "chunk_fwd_split",
+__all__ = ["bwd_workspace_size", "chunk_bwd", "chunk_fwd", "chunk_fwd_gated",
+           "chunk_fwd_split", "debug_set_spin_limit", "device_status",
            "compose_states", "gate", "gate_bwd", "gated_rmsnorm", "recurrent_step",
            "transition", "workspace_size"]

@@ -34,7 +34,11 @@ EXPORTED = ("kda_status_string", "kda_version", "kda_gate", "kda_chunk_fwd_works
             "kda_chunk_fwd", "kda_chunk_fwd_split_workspace_size", "kda_chunk_fwd_split",
             "kda_chunk_fwd_gated", "kda_gated_rmsnorm", "kda_chunk_transition",
             "kda_compose_states", "kda_recurrent_step", "kda_chunk_bwd_workspace_size",
-            "kda_chunk_bwd", "kda_gate_bwd")
+            "kda_chunk_bwd", "kda_gate_bwd", "kda_device_status",
+            "kda_debug_set_spin_limit")
+
+KDA_DEVICE_WAIT_TIMEOUT = 0x1
+KDA_DEVICE_DECAY_OUT_OF_RANGE = 0x2
 
 _lib = None
 
@@ -97,6 +101,10 @@ def load(path: str = LIB_PATH):
     lib.kda_chunk_bwd.restype = i32
     lib.kda_gate_bwd.argtypes = [fp, fp, f32, fp, ctypes.c_long, i32, i32, fp, fp, vp]
     lib.kda_gate_bwd.restype = i32
+    lib.kda_device_status.argtypes = [ctypes.POINTER(ctypes.c_uint32), i32, vp]
+    lib.kda_device_status.restype = i32
+    lib.kda_debug_set_spin_limit.argtypes = [i32]
+    lib.kda_debug_set_spin_limit.restype = i32
     if path == LIB_PATH:
         _lib = lib
     return lib

@@ -3,10 +3,21 @@
 // every entry point are in include/kda.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
 #include <stdint.h>
 
 #include "kda.h"
 #include "kda_internal.h"
+
+// Device-side failure flags (KDA_DEVICE_* of kda.h), one sticky word per
+// device: the chunk kernels set bits in it with a global atomic OR, and
+// kda_device_status reads (and optionally clears) it. Host code uses the
+// device address looked up per device, never the name.
+static __device__ __align__(256) unsigned int device_flags[64];
+static_assert(KDA_DEVICE_WAIT_TIMEOUT == kda::kDeviceWaitTimeout &&
+                  KDA_DEVICE_DECAY_OUT_OF_RANGE == kda::kDeviceDecayOutOfRange,
+              "device flag bits");
 
 namespace {
 
@@ -105,6 +116,37 @@ SplitPlan auto_split(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype_t
   if (P < 4 || (long)T * (9 * P - 30) <= 3000 * P) return SplitPlan{};
   if ((long)B * T > 0x7fffffffL) return SplitPlan{};  // the piece table is int32
   return split_layout(B, H, Dk, Dv, (int)P);
+}
+
+// Device address of `device_flags` on the current device, looked up once per
+// device with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_symbols_mu;
+void* g_flags_ptr[kMaxDevices] = {};
+
+kda_status_t device_flags_word(unsigned int** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return KDA_ERROR_LAUNCH_FAILURE;
+  if (dev < 0 || dev >= kMaxDevices) return KDA_ERROR_NOT_SUPPORTED;
+  std::lock_guard<std::mutex> lock(g_symbols_mu);
+  if (!g_flags_ptr[dev]) {
+    void* f = nullptr;
+    if (hipGetSymbolAddress(&f, HIP_SYMBOL(device_flags)) != hipSuccess || !f)
+      return KDA_ERROR_LAUNCH_FAILURE;
+    g_flags_ptr[dev] = f;
+  }
+  *out = static_cast<unsigned int*>(g_flags_ptr[dev]);
+  return KDA_SUCCESS;
+}
+
+// Polls after which a bounded wait of the pipelined kernel gives up (0: the
+// kernel's default); lowered only to exercise the failure report.
+std::atomic<int> g_spin_limit{0};
+
+// The device flags word and the wait bound every chunk-kernel launch carries.
+kda_status_t failure_reporting(unsigned int** flags, int* spin_limit) {
+  *spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  return device_flags_word(flags);
 }
 
 }  // namespace
@@ -277,6 +319,12 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
   const size_t need = order_bytes(B, s.N);
   if (workspace && workspace_bytes < need) return KDA_ERROR_INSUFFICIENT_WORKSPACE;
   if (s.N == 0) return KDA_SUCCESS;
+  unsigned int* flags = nullptr;
+  int spin_limit = 0;
+  if (fused) {
+    st = failure_reporting(&flags, &spin_limit);
+    if (st != KDA_SUCCESS) return st;
+  }
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (split.P > 1) {
@@ -311,6 +359,7 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
     }
     a.order = nullptr;
     a.H = H; a.Dk = Dk; a.Dv = Dv; a.scale = scale; a.bf16 = bf16;
+    a.status = flags; a.spin_limit = spin_limit;
     if (e == hipSuccess) {
       // state maps (v = 0 from S = I) and zero-start final states, in one
       // launch that reads k, v, g and beta once
@@ -336,6 +385,7 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
     a.h0 = initial_state; a.hT = final_state; a.o = o;
     a.seqs = s; a.order = nullptr;
     a.H = H; a.Dk = Dk; a.Dv = Dv; a.scale = scale; a.bf16 = bf16;
+    a.status = flags; a.spin_limit = spin_limit;
     if (cu_seqlens && workspace && need > 0 && s.N > 1) {
       int32_t* order = static_cast<int32_t*>(workspace);
       hipError_t e = kda::launch_order(cu_seqlens, s.N, order, hs);
@@ -395,6 +445,8 @@ kda_status_t kda_chunk_transition(const void* k, kda_dtype_t dtype, const float*
   if (s.N == 0) return KDA_SUCCESS;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   kda::ChunkArgs a;
+  st = failure_reporting(&a.status, &a.spin_limit);
+  if (st != KDA_SUCCESS) return st;
   a.q = nullptr; a.k = k; a.v = nullptr; a.g = g; a.gate_mode = (int)gate_input;
   a.A_log = A_log; a.g_min = g_min; a.beta = beta;
   a.h0 = nullptr; a.hT = M; a.o = nullptr;
@@ -533,6 +585,8 @@ kda_status_t kda_chunk_bwd(const void* q, const void* k, const void* v, kda_dtyp
   a.dY = ws + 2 * ck + 2 * tok;
   a.At = reinterpret_cast<float*>(ws + 2 * ck + 3 * tok);
   a.order = nullptr;
+  st = failure_reporting(&a.status, &a.spin_limit);
+  if (st != KDA_SUCCESS) return st;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (cu_seqlens && B == 1 && s.N > 1 && s.N <= kda::kMaxOrderN) {
     const size_t at = round_up((size_t)B * T * H * 16 * sizeof(float), kWorkspaceAlign);
@@ -552,6 +606,30 @@ kda_status_t kda_gate_bwd(const float* z, const float* A_log, float g_min, const
   if (Dk % 4 != 0 || Dk > 1024 || H > 65535) return KDA_ERROR_NOT_SUPPORTED;
   return launch_status(kda::launch_gate_bwd(z, A_log, g_min, dg, rows, H, Dk, dz, dA_log,
                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_device_status(uint32_t* flags, int clear, kda_stream_t stream) {
+  if (!flags) return KDA_ERROR_INVALID_VALUE;
+  unsigned int* word = nullptr;
+  kda_status_t st = device_flags_word(&word);
+  if (st != KDA_SUCCESS) return st;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  unsigned int value = 0;
+  if (hipMemcpyAsync(&value, word, sizeof(value), hipMemcpyDeviceToHost, hs) != hipSuccess)
+    return KDA_ERROR_LAUNCH_FAILURE;
+  if (hipStreamSynchronize(hs) != hipSuccess) return KDA_ERROR_LAUNCH_FAILURE;
+  if (clear) {
+    if (hipMemsetAsync(word, 0, sizeof(unsigned int), hs) != hipSuccess) return KDA_ERROR_LAUNCH_FAILURE;
+    if (hipStreamSynchronize(hs) != hipSuccess) return KDA_ERROR_LAUNCH_FAILURE;
+  }
+  *flags = value;
+  return KDA_SUCCESS;
+}
+
+kda_status_t kda_debug_set_spin_limit(int polls) {
+  if (polls < 0) return KDA_ERROR_INVALID_VALUE;
+  g_spin_limit.store(polls, std::memory_order_relaxed);
+  return KDA_SUCCESS;
 }
 
 }  // extern "C"

@@ -1001,6 +1001,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, long slots, hipStream_t stream) {
     c.order = a.order;
     c.H = a.H; c.Dk = DK; c.Dv = DV; c.scale = a.scale; c.bf16 = true;
     c.ck_state = a.ckS; c.ck_u = a.U; c.ck_vt = a.Vt; c.ck_at = a.At;
+    c.status = a.status; c.spin_limit = a.spin_limit;
     hipError_t e = launch_chunk_checkpoint(c, stream);
     if (e != hipSuccess) return e;
   } else {
@@ -1016,6 +1017,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, long slots, hipStream_t stream) {
     c.order = a.order;
     c.H = a.H; c.Dk = DK; c.Dv = DV; c.scale = a.scale; c.bf16 = true;
     c.ck_state = a.ckdS; c.ck_vt = a.dY;
+    c.status = a.status; c.spin_limit = a.spin_limit;
     hipError_t e = launch_chunk_reverse(c, stream);
     if (e != hipSuccess) return e;
   } else {

@@ -353,6 +353,18 @@ __global__ void __launch_bounds__(64 * waves_for<DV>(), 1) chunk_fused_kernel(Ch
       for (int i = 0; i < RPG; ++i)
         if (rg * RPG + i >= Lr) gl[i] = glast;
     }
+    if constexpr (GATE == kGateLogDecay || GATE == kGateCumsum) {
+      // a per-token log-decay passed in directly is not bounded by the gate:
+      // report a 16-token tile whose reciprocal factors overflow
+      bool bad = false;
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bad |= !(rho[I + 1][e] - rho[I][e] >= kMinTileLog2Decay);
+      if (__builtin_amdgcn_ballot_w64(bad) != 0 && a.status && (threadIdx.x & 63) == 0)
+        __hip_atomic_fetch_or(a.status, kDeviceDecayOutOfRange, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     {
       const f32x4 rI = rho[tileI], rI1 = rho[tileI + 1], rC = rho[4];

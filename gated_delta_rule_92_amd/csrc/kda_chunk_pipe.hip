@@ -52,8 +52,16 @@ constexpr int CCOLS = PDV / NCONS;  // value columns per consumer
 constexpr int CNTV = CCOLS / 16;    // 16-column tiles per consumer
 // Legitimate waits last a few thousand cycles; a wait that reaches this many
 // polls (about a millisecond) marks the workgroup aborted, and every later
-// wait returns at once, so the kernel always finishes.
+// wait returns at once, so the kernel always finishes; the give-up is
+// reported to the host through the device flags word. The host may lower the
+// limit (ChunkArgs::spin_limit) to exercise that path.
 constexpr int kSpinLimit = 1 << 15;
+
+// Sets `flag` in the device flags word (one global atomic OR per wavefront).
+__device__ __forceinline__ void report(unsigned int* status, unsigned int flag) {
+  if (status && (threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_or(status, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // LDS row strides (elements). Matrix-core fragments are read as 8 bytes per
 // lane from 16 rows, 16 lanes per LDS cycle over 32 four-byte banks. A row
@@ -89,14 +97,17 @@ __device__ __forceinline__ int lds_load_relaxed(int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Wait until *p >= target, bounded by kSpinLimit polls and by the
-// workgroup's abort flag.
-__device__ __forceinline__ void wait_at_least(int* p, int target, int* abort_flag) {
+// Wait until *p >= target, bounded by spin_limit polls and by the
+// workgroup's abort flag; a wait that gives up aborts the workgroup and
+// reports KDA_DEVICE_WAIT_TIMEOUT.
+__device__ __forceinline__ void wait_at_least(int* p, int target, int* abort_flag, int spin_limit,
+                                              unsigned int* status) {
   int spins = 0;
   while (lds_load_relaxed(p) < target) {
     if (lds_load_relaxed(abort_flag) != 0) break;
-    if (++spins >= kSpinLimit) {
+    if (++spins >= spin_limit) {
       __hip_atomic_store(abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      report(status, kDeviceWaitTimeout);
       break;
     }
     __builtin_amdgcn_s_sleep(1);
@@ -204,6 +215,7 @@ __global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : 
   // wavefront index, known to the compiler as uniform (kept in scalar registers)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 15, g4 = lane >> 4;
+  const int spin_limit = a.spin_limit > 0 ? a.spin_limit : kSpinLimit;
 
   const int n = a.order ? a.order[blockIdx.x / H] : (int)(blockIdx.x / H);
   const int h = blockIdx.x % H;
@@ -292,7 +304,7 @@ __global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : 
       const long t0 = bos + (long)tile * PT;
       const int L = (int)min((long)PT, len - (long)tile * PT);
       // the slot's previous tile must have been consumed by every consumer
-      if (use > 0) wait_at_least(&done[slot], ncons * use, abort_flag);
+      if (use > 0) wait_at_least(&done[slot], ncons * use, abort_flag, spin_limit, a.status);
 
       // cumulative log2-decay of this lane's rows (local to the half for the
       // incremental gate forms, absolute for the cumulative-sum form)
@@ -350,6 +362,14 @@ __global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : 
           off[j] = hr ? other : 0.f;
           gc[j] = Gl[7][j] + other;
         }
+      }
+      if constexpr (GATE == kGateLogDecay || GATE == kGateCumsum) {
+        // a per-token log-decay passed in directly is not bounded by the
+        // gate: report a tile whose reciprocal factors 2^{-G} overflow
+        bool bad = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bad |= !(gc[j] >= kMinTileLog2Decay);
+        if (__builtin_amdgcn_ballot_w64(bad) != 0) report(a.status, kDeviceDecayOutOfRange);
       }
       float eg[4];
 #pragma unroll
@@ -748,7 +768,7 @@ __global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : 
     auto finish_prev = [&]() {
       const __amdgpu_buffer_rsrc_t pv_rso =
           make_rsrc(o + ((size_t)pv_t0 * H + h) * PDV, (uint32_t)((pv_L - 1) * H + 1) * PDV * 2);
-      wait_at_least(&nrm_ready[pv_slot], NCONS * (pv_use + 1), abort_flag);
+      wait_at_least(&nrm_ready[pv_slot], NCONS * (pv_use + 1), abort_flag, spin_limit, a.status);
       const float* nrm = reinterpret_cast<const float*>(smem + pv_slot * kSlotBytes + sNrm);
       f32x4 tot = *reinterpret_cast<const f32x4*>(nrm + 4 * g4);
 #pragma unroll
@@ -780,7 +800,7 @@ __global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : 
       const int tile = tile_of(step);
       const long t0 = bos + (long)tile * PT;
       const int L = (int)min((long)PT, len - (long)tile * PT);
-      wait_at_least(&ready[slot], step + 1, abort_flag);
+      wait_at_least(&ready[slot], step + 1, abort_flag, spin_limit, a.status);
       const __bf16* Kg = reinterpret_cast<const __bf16*>(sl + sKg);
       const __bf16* Qg = reinterpret_cast<const __bf16*>(sl + sQg);
       const __bf16* KtT = reinterpret_cast<const __bf16*>(sl + sKtT);

@@ -9,6 +9,11 @@ namespace kda {
 
 enum GateMode { kGateLogDecay = 0, kGateCumsum = 1, kGateLogits = 2, kGateSoftplus = 3 };
 
+// Bits of the device flags word (KDA_DEVICE_WAIT_TIMEOUT and
+// KDA_DEVICE_DECAY_OUT_OF_RANGE of kda.h; kda_api.cpp checks they agree).
+constexpr unsigned int kDeviceWaitTimeout = 1u;
+constexpr unsigned int kDeviceDecayOutOfRange = 2u;
+
 // Sequence geometry shared by the launchers. Either cu (device, N+1 entries)
 // describes packed sequences, or cu == nullptr and sequence n covers tokens
 // [n*T, (n+1)*T) of a dense batch.
@@ -89,6 +94,11 @@ struct ChunkArgs {
   // consecutive pieces, and only each sequence's last piece writes its final
   // state, to hT[n / hT_group]
   int hT_group = 0;
+  // device-side failure reporting: the device's flags word (KDA_DEVICE_* of
+  // kda.h, set with a global atomic OR; nullptr: not reported), and the polls
+  // after which a bounded wait of the pipelined kernel gives up (0: default)
+  unsigned int* status = nullptr;
+  int spin_limit = 0;
 };
 // Shapes the tile kernel instantiates: chunk 64; bf16 with Dk, Dv in
 // {64, 128}; fp32 with Dk = Dv = 64.
@@ -131,6 +141,12 @@ hipError_t launch_split_pieces(int32_t* out, const int32_t* cu, int nseq, int T,
                                hipStream_t stream);
 // Lowest per-token log-decay the chunk path handles (16 * 5.5 = 88 < 88.7 = ln FLT_MAX).
 constexpr float kMinFusedGmin = -5.5f;
+// Lowest total log2-decay of one 16-token tile the chunk kernels accept
+// without reporting KDA_DEVICE_DECAY_OUT_OF_RANGE: 16 tokens at the lowest
+// supported per-token log-decay give 16 * (-5.5) / ln 2 = -126.96 (allowed,
+// with rounding to spare), and the tile's reciprocal factors 2^{-G} overflow
+// fp32 and bf16 at 2^128.
+constexpr float kMinTileLog2Decay = -127.0f;
 hipError_t launch_chunk_fused(const ChunkArgs& a, hipStream_t stream);
 
 // Backward of the chunk forward (three kernels: forward scan writing the
@@ -167,6 +183,8 @@ struct BwdArgs {
   void* U;             // [Ttot, H, Dv] V - Kg S
   void* Vt;            // [Ttot, H, Dv] pseudo-values
   void* dY;            // [Ttot, H, Dv] T^T dV~
+  unsigned int* status = nullptr;  // device flags word, as in ChunkArgs
+  int spin_limit = 0;
   float* At;           // [Ttot, H, 16] row r of each tile's A~ = A_kk / beta
                        // (strictly lower part; zeros elsewhere)
 };

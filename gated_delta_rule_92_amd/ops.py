@@ -461,3 +461,23 @@ def gate_bwd(z: torch.Tensor, dg: torch.Tensor, A_log: Optional[torch.Tensor] = 
                               _ptr(dA), _stream(z.device))
     _lib.check(rc, "kda_gate_bwd")
     return dz, dA
+
+
+def device_status(clear: bool = False, device: Optional[torch.device] = None) -> int:
+    """kda_device_status: the sticky device-side failure flags of the current
+    (or given) device, KDA_DEVICE_WAIT_TIMEOUT | KDA_DEVICE_DECAY_OUT_OF_RANGE
+    bits; waits for the device's current stream. clear=True resets them."""
+    import ctypes
+    lib = _lib.load()
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    out = ctypes.c_uint32(0)
+    with torch.cuda.device(dev):
+        _lib.check(lib.kda_device_status(ctypes.byref(out), int(bool(clear)), _stream(dev)),
+                   "kda_device_status")
+    return int(out.value)
+
+
+def debug_set_spin_limit(polls: int) -> None:
+    """kda_debug_set_spin_limit (testing aid): polls before a bounded wait of
+    the pipelined kernel gives up; 0 restores the default."""
+    _lib.check(_lib.load().kda_debug_set_spin_limit(int(polls)), "kda_debug_set_spin_limit")

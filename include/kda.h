@@ -35,8 +35,10 @@
  *   inconsistent sizes, misaligned pointers; KDA_ERROR_NOT_SUPPORTED for
  *   shapes outside the supported set; KDA_ERROR_INSUFFICIENT_WORKSPACE.
  *   A failed launch returns KDA_ERROR_LAUNCH_FAILURE. On any error nothing
- *   has been enqueued. Not checked (documented preconditions): contiguity,
- *   g within [g_min, 0] when g is passed directly, cu_seqlens well formed.
+ *   has been enqueued. Not checked on the host (documented preconditions):
+ *   contiguity, g within [g_min, 0] when g is passed directly, cu_seqlens
+ *   well formed. Failures only the device can see are reported through the
+ *   device flags read by kda_device_status (see there).
  * Precision.  q, k, v, o share `dtype` (fp32 or bf16). g, z, A_log, beta and
  *   the states are always fp32. Accumulation is fp32. For bf16 inputs the
  *   matrix products round their operands to bf16.
@@ -375,6 +377,45 @@ kda_status_t kda_chunk_bwd(const void* q, const void* k, const void* v, kda_dtyp
 kda_status_t kda_gate_bwd(const float* z, const float* A_log, float g_min, const float* dg,
                           long rows, int H, int Dk, float* dz, float* dA_log,
                           kda_stream_t stream);
+
+/*
+ * Device-side failure reporting. The chunk kernels set bits in a sticky
+ * flags word of the device they run on (one word per device, shared by all
+ * calls and streams on it) when they meet a failure the host cannot check
+ * before the launch; the call itself has already returned KDA_SUCCESS, and
+ * the results of the call that set a flag are not valid.
+ *   KDA_DEVICE_WAIT_TIMEOUT: a bounded wait between the producer and
+ *     consumer wavefronts of the pipelined bf16 d = 128 kernel gave up (the
+ *     workgroup then finishes without waiting, so the kernel always ends).
+ *   KDA_DEVICE_DECAY_OUT_OF_RANGE: a 16-token tile's total log-decay fell
+ *     below -127 ln 2 = -88.03 (16 tokens at -5.5 give -88), which a
+ *     per-token log-decay passed directly (KDA_GATE_LOGDECAY,
+ *     KDA_GATE_CUMSUM) below -5.5 can cause: inside the tile the reciprocal
+ *     decay factors then approach or pass fp32's largest value 2^128
+ *     [Baidu-1 §1.2: the lower bound of the gate is what keeps 16-token
+ *     tiles finite]. The logits gate with g_min >= -5.5 cannot cause it.
+ */
+#define KDA_DEVICE_WAIT_TIMEOUT 0x1u
+#define KDA_DEVICE_DECAY_OUT_OF_RANGE 0x2u
+
+/*
+ * kda_device_status — reads the current device's flags word: enqueues a copy
+ * of it on `stream`, waits for the stream, and stores it in *flags (host
+ * pointer). With clear != 0 the word is then reset to 0 (flags that other
+ * streams set between the read and the reset are lost). Synchronous; not for
+ * use under graph capture. KDA_ERROR_INVALID_VALUE if flags is NULL.
+ */
+kda_status_t kda_device_status(uint32_t* flags, int clear, kda_stream_t stream);
+
+/*
+ * kda_debug_set_spin_limit — testing aid: the number of polls after which a
+ * bounded wait of the pipelined kernel gives up, for launches enqueued after
+ * this call in this process (0 restores the default of 32768, about a
+ * millisecond). A small limit makes the waits give up, so that the report
+ * above can be checked; the kernels still finish normally.
+ * KDA_ERROR_INVALID_VALUE if polls < 0.
+ */
+kda_status_t kda_debug_set_spin_limit(int polls);
 
 #ifdef __cplusplus
 }

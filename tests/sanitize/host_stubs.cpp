@@ -8,7 +8,8 @@
 // success for empty problems, which the ABI tests rely on): a host-check
 // build computes nothing and is loaded only by the sanitizer test. hipGetDevice and
 // hipDeviceGetAttribute report one device with 256 compute units, so the
-// automatic context split is planned as on an MI355X.
+// automatic context split is planned as on an MI355X. hipGetSymbolAddress
+// returns the host shadow of a device variable (a plain host array here).
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -25,6 +26,27 @@ hipError_t hipGetDevice(int* device) {
   *device = 0;
   return hipSuccess;
 }
+
+// The host build has no device code: a symbol's address is its host address.
+hipError_t hipGetSymbolAddress(void** devPtr, const void* symbol) {
+  if (!devPtr || !symbol) return hipErrorInvalidValue;
+  *devPtr = const_cast<void*>(symbol);
+  return hipSuccess;
+}
+
+// Copies, fills and waits act on host memory at once (the host build's
+// device variables are host arrays).
+hipError_t hipMemcpyAsync(void* dst, const void* src, size_t bytes, hipMemcpyKind, hipStream_t) {
+  if (bytes && (!dst || !src)) return hipErrorInvalidValue;
+  std::memcpy(dst, src, bytes);
+  return hipSuccess;
+}
+hipError_t hipMemsetAsync(void* dst, int value, size_t bytes, hipStream_t) {
+  if (bytes && !dst) return hipErrorInvalidValue;
+  std::memset(dst, value, bytes);
+  return hipSuccess;
+}
+hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
 
 hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t attr, int device) {
   if (!value || device != 0) return hipErrorInvalidValue;

@@ -271,3 +271,10 @@ def test_gate_bwd_validation():
     assert call(g_min=0.0) == _lib.KDA_ERROR_INVALID_VALUE
     assert call(dg=FAKE + 4) == _lib.KDA_ERROR_INVALID_VALUE
     assert call(Dk=6) == _lib.KDA_ERROR_NOT_SUPPORTED
+
+
+def test_device_status_and_spin_limit_validation():
+    lib = _lib.load()
+    assert lib.kda_device_status(None, 0, None) == _lib.KDA_ERROR_INVALID_VALUE
+    assert lib.kda_debug_set_spin_limit(-1) == _lib.KDA_ERROR_INVALID_VALUE
+    assert lib.kda_debug_set_spin_limit(0) == _lib.KDA_SUCCESS

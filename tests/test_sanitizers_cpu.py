@@ -33,7 +33,10 @@ def test_host_abi_and_oracle_under_asan_ubsan(tmp_path):
         pytest.skip("sanitizer runtimes not installed")
     host_lib = str(tmp_path / "libkda_hostcheck.so")
     oracle_lib = str(tmp_path / "libkda_oracle_san.so")
+    # __align__ and HIP_SYMBOL come from the HIP compiler's device headers, which g++
+    # does not see
     subprocess.run(["g++", "-std=c++17", "-shared", "-fPIC", "-D__HIP_PLATFORM_AMD__",
+                    "-D__align__(x)=__attribute__((aligned(x)))", "-DHIP_SYMBOL(x)=x",
                     "-I/opt/rocm/include", f"-I{ROOT}/include", f"-I{CSRC}"] + SAN +
                    [os.path.join(CSRC, "kda_api.cpp"),
                     os.path.join(ROOT, "tests", "sanitize", "host_stubs.cpp"), "-o", host_lib],
