@@ -9,6 +9,7 @@ Public API (thin wrappers over the C ABI in include/kda.h):
     transition(k, g, beta, cu_seqlens=None, gate="logdecay", ...)
     compose_states(M, b, initial_state, nseq, P)
     chunk_fwd_split(q, k, v, g, beta, initial_state=None, cu_seqlens=None, segments=8, ...)
+    chunk_fwd_noalloc(q, k, v, g, beta, o, final_state, ...)   (no allocation)
     chunk_fwd_gated(q, k, v, g, beta, out_gate, norm_weight=None, eps=1e-6, ...)
     gated_rmsnorm(o, out_gate, norm_weight=None, eps=1e-6)
     chunk_bwd(q, k, v, g, beta, do, initial_state=None, d_final_state=None, ...)
@@ -16,10 +17,10 @@ Public API (thin wrappers over the C ABI in include/kda.h):
     device_status(clear=False)        (device-side failure flags)
 """
 from .ops import (bwd_workspace_size, chunk_bwd, chunk_fwd, chunk_fwd_gated,  # noqa: F401
-                  chunk_fwd_split, debug_set_spin_limit, device_status, compose_states, gate, gate_bwd, gated_rmsnorm, recurrent_step,
+                  chunk_fwd_noalloc, chunk_fwd_split, debug_set_spin_limit, device_status, compose_states, gate, gate_bwd, gated_rmsnorm, recurrent_step,
                   transition, workspace_size)
 
-__all__ = ["bwd_workspace_size", "chunk_bwd", "chunk_fwd", "chunk_fwd_gated",
+__all__ = ["bwd_workspace_size", "chunk_bwd", "chunk_fwd", "chunk_fwd_gated", "chunk_fwd_noalloc",
            "chunk_fwd_split", "debug_set_spin_limit", "device_status",
            "compose_states", "gate", "gate_bwd", "gated_rmsnorm", "recurrent_step",
            "transition", "workspace_size"]

@@ -34,7 +34,7 @@ EXPORTED = ("kda_status_string", "kda_version", "kda_gate", "kda_chunk_fwd_works
             "kda_chunk_fwd", "kda_chunk_fwd_split_workspace_size", "kda_chunk_fwd_split",
             "kda_chunk_fwd_gated", "kda_gated_rmsnorm", "kda_chunk_transition",
             "kda_compose_states", "kda_recurrent_step", "kda_chunk_bwd_workspace_size",
-            "kda_chunk_bwd", "kda_gate_bwd", "kda_device_status",
+            "kda_chunk_bwd", "kda_gate_bwd", "kda_device_status", "kda_chunk_fwd_noalloc",
             "kda_debug_set_spin_limit")
 
 KDA_DEVICE_WAIT_TIMEOUT = 0x1
@@ -70,6 +70,10 @@ def load(path: str = LIB_PATH):
                                   i32, i32, i32, i32, i32, i32, i32,  # N B T H Dk Dv chunk
                                   f32, vp, fp, vp, sz, vp]
     lib.kda_chunk_fwd.restype = i32
+    lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, i32, fp, i32, fp, f32, fp, fp, ip,
+                                          i32, i32, i32, i32, i32, i32, i32,  # N B T H Dk Dv chunk
+                                          f32, vp, fp, vp]
+    lib.kda_chunk_fwd_noalloc.restype = i32
     lib.kda_chunk_fwd_gated.argtypes = [vp, vp, vp, i32, fp, i32, fp, f32, fp, fp, ip,
                                         i32, i32, i32, i32, i32, i32, i32,  # N B T H Dk Dv chunk
                                         f32, vp, fp, f32, vp, fp, vp, sz, vp]

@@ -10,6 +10,15 @@
 #include "kda.h"
 #include "kda_internal.h"
 
+// Device scratch of kda_chunk_fwd_noalloc, for callers that cannot allocate:
+// the forward's workspace (the longest-first order of packed sequences, or
+// the context split's piece table, state maps and states) in a static array
+// each device holds from the library's load until the process ends. Host code
+// never passes `scratch` itself to a kernel (on the host it only names the
+// symbol); it uses the device address hipGetSymbolAddress returns for the
+// current device, kept per device in noalloc_scratch().
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
 // Device-side failure flags (KDA_DEVICE_* of kda.h), one sticky word per
 // device: the chunk kernels set bits in it with a global atomic OR, and
 // kda_device_status reads (and optionally clears) it. Host code uses the
@@ -139,6 +148,27 @@ kda_status_t device_flags_word(unsigned int** out) {
   return KDA_SUCCESS;
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current (at the first kda_chunk_fwd_noalloc call
+// on it).
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+kda_status_t noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return KDA_ERROR_LAUNCH_FAILURE;
+  if (dev < 0 || dev >= kMaxDevices) return KDA_ERROR_NOT_SUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+      return KDA_ERROR_LAUNCH_FAILURE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KDA_SUCCESS;
+}
+
 // Polls after which a bounded wait of the pipelined kernel gives up (0: the
 // kernel's default); lowered only to exercise the failure report.
 std::atomic<int> g_spin_limit{0};
@@ -214,6 +244,31 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtyp
   return chunk_fwd_impl(q, k, v, dtype, g, gate_input, A_log, g_min, beta, initial_state,
                         cu_seqlens, N, B, T, H, Dk, Dv, chunk, scale, o, final_state, workspace,
                         workspace_bytes, stream, nullptr, nullptr, 0.f, 0);
+}
+
+kda_status_t kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                                   const float* g, kda_gate_input_t gate_input, const float* A_log,
+                                   float g_min, const float* beta, const float* initial_state,
+                                   const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
+                                   int Dv, int chunk, float scale, void* o, float* final_state,
+                                   kda_stream_t stream) {
+  // The workspace kda_chunk_fwd would be given, carved from the static
+  // scratch: sizes beyond it are rejected before anything is enqueued.
+  size_t need = 0;
+  if (B > 0 && T >= 0 && H > 0 && Dk > 0 && Dv > 0 && N >= 0 && chunk > 0 &&
+      (dtype == KDA_FLOAT32 || dtype == KDA_BFLOAT16)) {
+    kda_status_t st = kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, N, chunk, dtype, &need);
+    if (st != KDA_SUCCESS) return st;
+    if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERROR_INSUFFICIENT_WORKSPACE;
+  }
+  void* ws = nullptr;
+  if (need > 0) {
+    kda_status_t st = noalloc_scratch(&ws);
+    if (st != KDA_SUCCESS) return st;
+  }
+  return chunk_fwd_impl(q, k, v, dtype, g, gate_input, A_log, g_min, beta, initial_state,
+                        cu_seqlens, N, B, T, H, Dk, Dv, chunk, scale, o, final_state, ws, need,
+                        stream, nullptr, nullptr, 0.f, 0);
 }
 
 kda_status_t kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_dtype_t dtype,

@@ -138,6 +138,47 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     return o, final_state
 
 
+def chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                      beta: torch.Tensor, o: torch.Tensor, final_state: Optional[torch.Tensor],
+                      initial_state: Optional[torch.Tensor] = None,
+                      cu_seqlens: Optional[torch.Tensor] = None, gate: str = "logdecay",
+                      A_log: Optional[torch.Tensor] = None, g_min: float = -5.0, chunk: int = 64,
+                      scale: float = 1.0) -> None:
+    """kda_chunk_fwd_noalloc: chunk_fwd into caller-provided o [B, T, H, Dv] and
+    final_state [N, H, Dk, Dv] (or None), with the library's static device
+    scratch as the workspace; neither this binding nor the library allocates."""
+    lib = _lib.load()
+    dev = q.device
+    dt = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _need(t, name, dt, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or g.shape != q.shape or \
+            beta.shape != q.shape[:3] or o.shape != v.shape:
+        raise ValueError("shape mismatch among q, k, v, g, beta, o")
+    N = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        N = cu_seqlens.numel() - 1
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None:
+            _need(t, name, torch.float32, dev)
+            if tuple(t.shape) != (N, H, Dk, Dv):
+                raise ValueError(f"{name} must be [N, H, Dk, Dv]")
+    if A_log is not None:
+        _need(A_log, "A_log", torch.float32, dev)
+    with torch.cuda.device(dev):
+        rc = lib.kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g),
+                                       _GATES[gate], _ptr(A_log), float(g_min), _ptr(beta),
+                                       _ptr(initial_state), _ptr(cu_seqlens), N, B, T, H, Dk, Dv,
+                                       int(chunk), float(scale), _ptr(o), _ptr(final_state),
+                                       _stream(dev))
+    _lib.check(rc, "kda_chunk_fwd_noalloc")
+
+
 def chunk_fwd_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                     beta: torch.Tensor, out_gate: torch.Tensor,
                     norm_weight: Optional[torch.Tensor] = None, eps: float = 1e-6,

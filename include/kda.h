@@ -176,6 +176,34 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtyp
                            void* workspace, size_t workspace_bytes, kda_stream_t stream);
 
 /*
+ * kda_chunk_fwd_noalloc — kda_chunk_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same computation, with the workspace
+ * kda_chunk_fwd_workspace_size asks for taken from a static device array of
+ * KDA_NOALLOC_SCRATCH_BYTES that each device holds from the library's first
+ * use until the process ends. No hipMalloc, hipFree or other allocation is
+ * made. Results equal kda_chunk_fwd's with a workspace of that size (the same
+ * kernels and the same context-split decision).
+ * Arguments as for kda_chunk_fwd, without workspace. The caller still owns
+ * q, k, v, g, beta, initial_state, o and final_state.
+ * Errors: as kda_chunk_fwd; KDA_ERROR_INSUFFICIENT_WORKSPACE when
+ * kda_chunk_fwd_workspace_size for these sizes exceeds the scratch (it holds
+ * every automatic context split on a device of up to 256 compute units, and
+ * the order of up to 8192 packed sequences).
+ * Concurrency: every call on one device shares that device's scratch, which
+ * keeps the last call's contents (no call relies on it starting zeroed).
+ * Calls that overlap on one device (different streams, or host threads
+ * without ordering) race on it and must be serialised by the caller.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+kda_status_t kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                                   const float* g, kda_gate_input_t gate_input, const float* A_log,
+                                   float g_min, const float* beta, const float* initial_state,
+                                   const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
+                                   int Dv, int chunk, float scale, void* o, float* final_state,
+                                   kda_stream_t stream);
+
+/*
  * kda_chunk_fwd_gated — kda_chunk_fwd followed by the attention block's
  * output epilogue [KDA-blog §Gated MLA, output equation; the weight product
  * W_o after it is not part of this library]:

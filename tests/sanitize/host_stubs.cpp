@@ -8,7 +8,8 @@
 // success for empty problems, which the ABI tests rely on): a host-check
 // build computes nothing and is loaded only by the sanitizer test. hipGetDevice and
 // hipDeviceGetAttribute report one device with 256 compute units, so the
-// automatic context split is planned as on an MI355X. hipGetSymbolAddress
+// automatic context split is planned as on an MI355X (a test may change the
+// count with kda_host_check_set_compute_units). hipGetSymbolAddress
 // returns the host shadow of a device variable (a plain host array here).
 #include <hip/hip_runtime.h>
 
@@ -20,6 +21,9 @@ extern "C" {
 char kda_host_check_last_launch[64] = "";
 int kda_host_check_launches = 0;
 int kda_host_check_build(void) { return 1; }
+// compute units hipDeviceGetAttribute reports (256, as on an MI355X)
+static int g_cus = 256;
+void kda_host_check_set_compute_units(int n) { g_cus = n; }
 
 hipError_t hipGetDevice(int* device) {
   if (!device) return hipErrorInvalidValue;
@@ -50,7 +54,7 @@ hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
 
 hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t attr, int device) {
   if (!value || device != 0) return hipErrorInvalidValue;
-  *value = attr == hipDeviceAttributeMultiprocessorCount ? 256 : 0;
+  *value = attr == hipDeviceAttributeMultiprocessorCount ? g_cus : 0;
   return hipSuccess;
 }
 }

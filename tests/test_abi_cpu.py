@@ -278,3 +278,42 @@ def test_device_status_and_spin_limit_validation():
     assert lib.kda_device_status(None, 0, None) == _lib.KDA_ERROR_INVALID_VALUE
     assert lib.kda_debug_set_spin_limit(-1) == _lib.KDA_ERROR_INVALID_VALUE
     assert lib.kda_debug_set_spin_limit(0) == _lib.KDA_SUCCESS
+
+
+def test_noalloc_validation_before_any_gpu_work():
+    lib = _lib.load()
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, g=FAKE, gate=0, A=None, g_min=-5.0, beta=FAKE,
+                 h0=None, cu=None, N=1, B=1, T=64, H=2, Dk=128, Dv=128, chunk=64, scale=1.0,
+                 o=FAKE, hT=None, stream=None)
+        a.update(kw)
+        return lib.kda_chunk_fwd_noalloc(*a.values())
+    assert call(q=None) == _lib.KDA_ERROR_INVALID_VALUE
+    assert call(B=0) == _lib.KDA_ERROR_INVALID_VALUE
+    assert call(q=FAKE + 4) == _lib.KDA_ERROR_INVALID_VALUE
+    assert call(Dk=512) == _lib.KDA_ERROR_NOT_SUPPORTED
+    assert call(cu=FAKE, N=0, T=0) == _lib.KDA_SUCCESS       # nothing to do, nothing enqueued
+
+
+def test_noalloc_rejects_a_workspace_beyond_the_scratch():
+    """Only in the host-check build (the CPU sanitizer run), whose stand-in
+    device can report more compute units: on 1024 of them a dense 16-head
+    sequence of 64K tokens would be split into 64 pieces, whose maps and
+    states (192 MiB) exceed the 64 MiB scratch, so the call is refused before
+    anything is enqueued; on 256 the split fits and the call goes through."""
+    lib = _lib.load()
+    if not hasattr(lib, "kda_host_check_build"):
+        pytest.skip("needs the host-check build (tests/test_sanitizers_cpu.py)")
+    lib.kda_host_check_set_compute_units.argtypes = [ctypes.c_int]
+
+    def call():
+        return lib.kda_chunk_fwd_noalloc(FAKE, FAKE, FAKE, 1, FAKE, 2, None, -5.0, FAKE, None, None,
+                                         1, 1, 65536, 16, 128, 128, 64, 1.0, FAKE, None, None)
+    try:
+        lib.kda_host_check_set_compute_units(1024)
+        assert call() == _lib.KDA_ERROR_INSUFFICIENT_WORKSPACE
+        lib.kda_host_check_set_compute_units(256)
+        assert call() == _lib.KDA_SUCCESS
+    finally:
+        lib.kda_host_check_set_compute_units(256)
