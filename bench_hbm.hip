@@ -65,6 +65,47 @@ __global__ void mix51(const f4* __restrict__ a0, const f4* __restrict__ a1, cons
   for (size_t i = gid; i < n4; i += stride) b[i] = a0[i] + a1[i] + a2[i] + a3[i] + a4[i];
 }
 
+// The chunk forward's load pattern with no compute: one workgroup per
+// (sequence, head) unit of a [B, T, H, 128] layout, four wavefronts taking the
+// unit's 16-token tiles p, p+4, ... in turn; per tile a lane reads 8 rows of
+// 4 bf16 channels of k, q and v (8 bytes each) and of 4 fp32 gate logits
+// (16 bytes), as the forward's producers do. `ahead` tiles are in flight per
+// wavefront. The loaded values are summed so that no load is dropped.
+template <int AHEAD>
+__global__ void kda_load_pattern(const uint2* __restrict__ k, const uint2* __restrict__ q,
+                                 const uint2* __restrict__ v, const f4* __restrict__ z, int T, int H,
+                                 float* __restrict__ out) {
+  const int unit = blockIdx.x, n = unit / H, h = unit % H;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int hr = lane >> 5, cq = lane & 31;
+  const long rowk = (long)H * 32, rowz = (long)H * 32;  // row strides in uint2 / f4 units
+  const long basek = ((long)n * T * H + h) * 32 + cq, basez = ((long)n * T * H + h) * 32 + cq;
+  const int ntiles = T / 16;
+  float acc = 0.f;
+  for (int t0 = wave; t0 < ntiles; t0 += 4 * AHEAD) {
+    uint2 rk[AHEAD][8], rq[AHEAD][8], rv[AHEAD][8];
+    f4 rz[AHEAD][8];
+#pragma unroll
+    for (int a = 0; a < AHEAD; ++a) {
+      const int tile = t0 + 4 * a;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const long row = (tile < ntiles) ? (long)tile * 16 + 8 * hr + r : 0;
+        rk[a][r] = k[basek + row * rowk];
+        rq[a][r] = q[basek + row * rowk];
+        rv[a][r] = v[basek + row * rowk];
+        rz[a][r] = z[basez + row * rowz];
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < AHEAD; ++a)
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        acc += __uint_as_float(rk[a][r].x ^ rq[a][r].y ^ rv[a][r].x) + rz[a][r].x + rz[a][r].w;
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
 // Enqueues one copy of n16 16-byte elements from src to dst (device pointers,
 // 16-byte aligned, not overlapping) on `stream` with `grid` workgroups of 256
 // threads. Returns 0, or the HIP error code of the launch.
@@ -127,6 +168,56 @@ int main() {
     printf("grid %6d  read4 %6.0f GB/s  read8 %6.0f GB/s  copy %6.0f GB/s  mix51 %6.0f GB/s\n", grid,
            bytes / best[0] / 1e6, bytes / best[1] / 1e6, 2.0 * bytes / best[2] / 1e6, 6.0 * bytes / best[3] / 1e6);
     fflush(stdout);
+  }
+  // small copies: the decode step moves a 16 MiB state in and out
+  for (size_t mb : {16, 64, 256}) {
+    const size_t nb = mb << 20, n16 = nb / 16;
+    float best = 1e9f;
+    int best_grid = 0;
+    for (int grid : {256, 512, 1024, 2048, 4096}) {
+      for (int rep = 0; rep < 20; ++rep) {
+        float ms;
+        CK(hipEventRecord(e0));
+        hipLaunchKernelGGL(copy4<4>, dim3(grid), dim3(256), 0, 0, buf[0], buf[1], n16);
+        CK(hipEventRecord(e1));
+        CK(hipEventSynchronize(e1));
+        CK(hipEventElapsedTime(&ms, e0, e1));
+        if (ms < best) { best = ms; best_grid = grid; }
+      }
+    }
+    printf("copy of %zu MiB: best %.2f us (grid %d), %6.0f GB/s read + write\n", mb, best * 1e3,
+           best_grid, 2.0 * nb / best / 1e6);
+    fflush(stdout);
+  }
+  // the forward's load pattern at the training shape (B = 8, T = 8192, H = 32)
+  {
+    const int B = 8, T = 8192, H = 32;
+    const size_t kb = (size_t)B * T * H * 128 * 2, zb = (size_t)B * T * H * 128 * 4;
+    void *k, *q, *v, *z;
+    CK(hipMalloc(&k, kb)); CK(hipMalloc(&q, kb)); CK(hipMalloc(&v, kb)); CK(hipMalloc(&z, zb));
+    CK(hipMemset(k, 0, kb)); CK(hipMemset(q, 0, kb)); CK(hipMemset(v, 0, kb)); CK(hipMemset(z, 0, zb));
+    float* o2;
+    CK(hipMalloc(&o2, (size_t)B * H * 256 * sizeof(float)));
+    for (int ahead = 1; ahead <= 2; ++ahead) {
+      float best = 1e9f;
+      for (int rep = 0; rep < 8; ++rep) {
+        float ms;
+        CK(hipEventRecord(e0));
+        if (ahead == 1)
+          hipLaunchKernelGGL(kda_load_pattern<1>, dim3(B * H), dim3(256), 0, 0, (const uint2*)k,
+                             (const uint2*)q, (const uint2*)v, (const f4*)z, T, H, o2);
+        else
+          hipLaunchKernelGGL(kda_load_pattern<2>, dim3(B * H), dim3(256), 0, 0, (const uint2*)k,
+                             (const uint2*)q, (const uint2*)v, (const f4*)z, T, H, o2);
+        CK(hipEventRecord(e1));
+        CK(hipEventSynchronize(e1));
+        CK(hipEventElapsedTime(&ms, e0, e1));
+        best = ms < best ? ms : best;
+      }
+      printf("forward load pattern (train8k, %d tile(s) in flight per wavefront): %.3f ms, %6.0f GB/s\n",
+             ahead, best, (3.0 * kb + zb) / best / 1e6);
+      fflush(stdout);
+    }
   }
   CK(hipDeviceSynchronize());
   return 0;

@@ -125,8 +125,102 @@ __global__ void __launch_bounds__(kRecCols * kRecParts) recurrent_kernel(Recurre
   }
 }
 
+// Decode step for d_k = 128 (one token per (sequence, head), dense): every
+// wavefront owns 16 value columns of one state, lane (cg = lane / 16,
+// r = lane % 16) holding columns 4cg..4cg+3 of rows r, r+16, ..., r+112, read
+// and written as 16-byte pieces. The two 128-long dot products of the token
+// (u = S^T k after the decay, o = S^T q after the write) are summed over a lane's
+// 8 rows and then over the 16 lanes of its row group with DPP moves, so the
+// step needs no LDS and no barrier: it is the state's read, a few hundred
+// instructions, and its write.
+constexpr int kDecRowsPerLane = 8;
+constexpr int kDecDk = 16 * kDecRowsPerLane;  // 128
+constexpr int kDecColsPerWave = 16;
+constexpr int kDecWaves = 4;
+
+__device__ __forceinline__ float dec_sum16(float t) {
+  // sum over the 16 lanes of a row: quad swaps, then the half-row and row mirrors
+  t += bits_float(__builtin_amdgcn_mov_dpp(float_bits(t), 0xB1, 0xF, 0xF, false));   // lane ^ 1
+  t += bits_float(__builtin_amdgcn_mov_dpp(float_bits(t), 0x4E, 0xF, 0xF, false));   // lane ^ 2
+  t += bits_float(__builtin_amdgcn_mov_dpp(float_bits(t), 0x141, 0xF, 0xF, false));  // half-row mirror
+  t += bits_float(__builtin_amdgcn_mov_dpp(float_bits(t), 0x140, 0xF, 0xF, false));  // row mirror
+  return t;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(64 * kDecWaves) decode128_kernel(RecurrentArgs a) {
+  const T* __restrict__ q = reinterpret_cast<const T*>(a.q);
+  const T* __restrict__ k = reinterpret_cast<const T*>(a.k);
+  const T* __restrict__ v = reinterpret_cast<const T*>(a.v);
+  T* __restrict__ o = reinterpret_cast<T*>(a.o);
+  const int H = a.H, Dv = a.Dv;
+  const int unit = blockIdx.x, h = unit % H;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cg = lane >> 4, r = lane & 15;
+  const int col = (blockIdx.y * kDecWaves + wave) * kDecColsPerWave + 4 * cg;
+  if (col >= Dv) return;  // a whole row group: the DPP sums stay within live lanes
+  const size_t srow = (size_t)unit * kDecDk;       // first state row of this unit
+  const size_t tok = (size_t)unit * kDecDk;        // q, k, g rows of the unit's token
+  f32x4 S[kDecRowsPerLane];
+#pragma unroll
+  for (int i = 0; i < kDecRowsPerLane; ++i)
+    S[i] = *reinterpret_cast<const f32x4*>(a.h0 + (srow + r + 16 * i) * Dv + col);
+  float kr[kDecRowsPerLane], qr[kDecRowsPerLane], al[kDecRowsPerLane];
+  const float es = ((a.gate_mode == kGateLogits || a.gate_mode == kGateSoftplus) && a.A_log)
+                       ? __expf(a.A_log[h]) : 1.0f;
+#pragma unroll
+  for (int i = 0; i < kDecRowsPerLane; ++i) {
+    const size_t c = tok + r + 16 * i;
+    kr[i] = to_f32(k[c]);
+    qr[i] = to_f32(q[c]);
+    float gv = a.g[c];
+    if (a.gate_mode == kGateLogits) gv = a.g_min / (1.0f + __expf(-es * gv));
+    if (a.gate_mode == kGateSoftplus) gv = -es * (fmaxf(gv, 0.f) + log1pf(__expf(-fabsf(gv))));
+    al[i] = __expf(gv);
+  }
+  f32x4 vv;
+  {
+    const T* vp = v + (size_t)unit * Dv + col;
+    vv = f32x4{to_f32(vp[0]), to_f32(vp[1]), to_f32(vp[2]), to_f32(vp[3])};
+  }
+  const float beta = a.beta[unit];
+  // decay, then u = S^T k
+  f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kDecRowsPerLane; ++i) {
+    S[i] = S[i] * al[i];
+    u = u + S[i] * kr[i];
+  }
+  f32x4 d;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) d[e] = beta * (vv[e] - dec_sum16(u[e]));
+  // write, then o = S^T q
+  f32x4 oo = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kDecRowsPerLane; ++i) {
+    S[i] = S[i] + d * kr[i];
+    oo = oo + S[i] * qr[i];
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) oo[e] = a.scale * dec_sum16(oo[e]);
+  if (r == 0) store4(o + (size_t)unit * Dv + col, oo);
+#pragma unroll
+  for (int i = 0; i < kDecRowsPerLane; ++i)
+    *reinterpret_cast<f32x4*>(a.hT + (srow + r + 16 * i) * Dv + col) = S[i];
+}
+
+bool decode128_applies(const RecurrentArgs& a) {
+  return a.Dk == kDecDk && a.Dv % 4 == 0 && !a.seqs.cu && a.seqs.T == 1 && a.h0 && a.hT && a.o;
+}
+
 template <typename T>
 static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream) {
+  if (decode128_applies(a)) {
+    const int cols_per_block = kDecWaves * kDecColsPerWave;
+    dim3 grid((unsigned)(a.seqs.N * a.H), (unsigned)((a.Dv + cols_per_block - 1) / cols_per_block));
+    hipLaunchKernelGGL((decode128_kernel<T>), grid, dim3(64 * kDecWaves), 0, stream, a);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)(a.seqs.N * a.H), (unsigned)((a.Dv + kRecCols - 1) / kRecCols));
   int rpp = (a.Dk + kRecParts - 1) / kRecParts;
   static_assert(kRecMaxDk / kRecParts <= 32, "rows per part");

@@ -206,8 +206,14 @@ def test_beta_zero_pure_decay_of_the_state(dtype, D, T):
 
 @pytest.mark.parametrize("dtype,Dk,Dv", [(torch.bfloat16, 128, 128), (torch.float32, 64, 64),
                                          (torch.float32, 96, 40), (torch.float32, 256, 130),
-                                         (torch.bfloat16, 8, 200)])
+                                         (torch.bfloat16, 8, 200), (torch.float32, 128, 64),
+                                         (torch.bfloat16, 128, 20), (torch.float32, 128, 132),
+                                         (torch.float32, 128, 130)])
 def test_decode_steps_match_oracle(dtype, Dk, Dv):
+    """T decode steps (one kda_recurrent_step per token) against the oracle's
+    recurrence; d_k = 128 with d_v a multiple of 4 runs the decode kernel
+    (including a partly filled wavefront at d_v = 20 and 132), other shapes
+    the general token-serial kernel."""
     _print_case(f"decode steps {dtype} Dk={Dk} Dv={Dv}")
     N, H, T = 3, 4, 6
     d = make_inputs(N, T, H, Dk, Dv, dtype, h0_std=0.02, seed=16)
@@ -222,6 +228,27 @@ def test_decode_steps_match_oracle(dtype, Dk, Dv):
     torch.cuda.synchronize()
     o = torch.stack(outs, dim=1)
     _check(o, state, _oracle(d), dtype, "decode")
+
+
+@pytest.mark.parametrize("gate_mode", ["logits", "softplus"])
+def test_decode128_gates_with_A_log(gate_mode):
+    """The d_k = 128 decode kernel with the gate applied in place (bounded
+    logits gate and the earlier softplus gate, per-head A_log)."""
+    from oracle import oracle_forward_softplus
+    _print_case(f"decode d_k=128 with {gate_mode} gate and A_log")
+    d = make_inputs(2, 1, 3, 128, 128, torch.bfloat16, h0_std=0.02, seed=24)
+    dd = to_dev(d)
+    A = torch.tensor([0.3, -0.2, 0.0])
+    state = dd["h0"].clone()
+    o = recurrent_step(dd["q"][:, 0].contiguous(), dd["k"][:, 0].contiguous(),
+                       dd["v"][:, 0].contiguous(), dd["z"][:, 0].contiguous(),
+                       dd["beta"][:, 0].contiguous(), state, gate=gate_mode, A_log=A.cuda())
+    torch.cuda.synchronize()
+    if gate_mode == "logits":
+        ref = _oracle(d, A=A)
+    else:
+        ref = oracle_forward_softplus(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"], None, A)
+    _check(o[:, None], state, ref, torch.bfloat16, f"decode128-{gate_mode}")
 
 
 def test_decode_logits_gate_in_place():
