@@ -134,11 +134,12 @@ __device__ __forceinline__ void st8x2(char* p, const uint32_t (&w)[4]) {
 }
 
 __device__ __forceinline__ uint32_t perm_lo16(uint32_t a, uint32_t b) {
-  // (a.lo16, b.lo16) -> one dword with a.lo in the low half
-  return (a & 0xffffu) | (b << 16);
+  // (a.lo16, b.lo16) -> one dword with a.lo in the low half (one v_perm_b32:
+  // selector bytes 0-3 pick from a, 4-7 from b)
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
 }
 __device__ __forceinline__ uint32_t perm_hi16(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
 // What one launch computes.

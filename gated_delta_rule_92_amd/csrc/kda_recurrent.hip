@@ -131,8 +131,13 @@ __global__ void __launch_bounds__(kRecCols * kRecParts) recurrent_kernel(Recurre
 // and written as 16-byte pieces. The two 128-long dot products of the token
 // (u = S^T k after the decay, o = S^T q after the write) are summed over a lane's
 // 8 rows and then over the 16 lanes of its row group with DPP moves, so the
-// step needs no LDS and no barrier: it is the state's read, a few hundred
-// instructions, and its write.
+// step needs no LDS and no barrier. The token's small rows are loaded before
+// the state, so that the gate is computed while the state is in flight; each
+// row's decay is computed by one lane of the wavefront and fetched by the
+// other three row groups (ds_bpermute), and the state is written before the
+// output's sums: a state-only copy with the same loads and stores measured
+// 8.8 us per step for 256 states of 128 x 128, this kernel 9.0 (11.2 with
+// every lane computing the decays of its 8 rows after the state's loads).
 constexpr int kDecRowsPerLane = 8;
 constexpr int kDecDk = 16 * kDecRowsPerLane;  // 128
 constexpr int kDecColsPerWave = 16;
@@ -158,32 +163,47 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode128_kernel(RecurrentArgs
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cg = lane >> 4, r = lane & 15;
   const int col = (blockIdx.y * kDecWaves + wave) * kDecColsPerWave + 4 * cg;
-  if (col >= Dv) return;  // a whole row group: the DPP sums stay within live lanes
+  // a row group past d_v reads column 0 and stores nothing; it stays active
+  // because the other row groups fetch decays from it
+  const bool live = col < Dv;
+  const int lc = live ? col : 0;
   const size_t srow = (size_t)unit * kDecDk;       // first state row of this unit
   const size_t tok = (size_t)unit * kDecDk;        // q, k, g rows of the unit's token
-  f32x4 S[kDecRowsPerLane];
+  // gate inputs of rows r + 16(2cg) and r + 16(2cg + 1): this lane's share
+  float gl[2];
 #pragma unroll
-  for (int i = 0; i < kDecRowsPerLane; ++i)
-    S[i] = *reinterpret_cast<const f32x4*>(a.h0 + (srow + r + 16 * i) * Dv + col);
+  for (int j = 0; j < 2; ++j) gl[j] = a.g[tok + r + 16 * (2 * cg + j)];
   float kr[kDecRowsPerLane], qr[kDecRowsPerLane], al[kDecRowsPerLane];
-  const float es = ((a.gate_mode == kGateLogits || a.gate_mode == kGateSoftplus) && a.A_log)
-                       ? __expf(a.A_log[h]) : 1.0f;
 #pragma unroll
   for (int i = 0; i < kDecRowsPerLane; ++i) {
     const size_t c = tok + r + 16 * i;
     kr[i] = to_f32(k[c]);
     qr[i] = to_f32(q[c]);
-    float gv = a.g[c];
-    if (a.gate_mode == kGateLogits) gv = a.g_min / (1.0f + __expf(-es * gv));
-    if (a.gate_mode == kGateSoftplus) gv = -es * (fmaxf(gv, 0.f) + log1pf(__expf(-fabsf(gv))));
-    al[i] = __expf(gv);
   }
   f32x4 vv;
   {
-    const T* vp = v + (size_t)unit * Dv + col;
+    const T* vp = v + (size_t)unit * Dv + lc;
     vv = f32x4{to_f32(vp[0]), to_f32(vp[1]), to_f32(vp[2]), to_f32(vp[3])};
   }
   const float beta = a.beta[unit];
+  f32x4 S[kDecRowsPerLane];
+#pragma unroll
+  for (int i = 0; i < kDecRowsPerLane; ++i)
+    S[i] = *reinterpret_cast<const f32x4*>(a.h0 + (srow + r + 16 * i) * Dv + lc);
+  const float es = ((a.gate_mode == kGateLogits || a.gate_mode == kGateSoftplus) && a.A_log)
+                       ? __expf(a.A_log[h]) : 1.0f;
+  float am[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    float gv = gl[j];
+    if (a.gate_mode == kGateLogits) gv = a.g_min / (1.0f + __expf(-es * gv));
+    if (a.gate_mode == kGateSoftplus) gv = -es * (fmaxf(gv, 0.f) + log1pf(__expf(-fabsf(gv))));
+    am[j] = __expf(gv);
+  }
+  // decay of row r + 16i: slot i % 2 of lane 16 (i / 2) + r
+#pragma unroll
+  for (int i = 0; i < kDecRowsPerLane; ++i)
+    al[i] = bits_float(__builtin_amdgcn_ds_bpermute((16 * (i >> 1) + r) * 4, float_bits(am[i & 1])));
   // decay, then u = S^T k
   f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -201,12 +221,14 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode128_kernel(RecurrentArgs
     S[i] = S[i] + d * kr[i];
     oo = oo + S[i] * qr[i];
   }
+  if (live) {
+#pragma unroll
+    for (int i = 0; i < kDecRowsPerLane; ++i)
+      *reinterpret_cast<f32x4*>(a.hT + (srow + r + 16 * i) * Dv + col) = S[i];
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) oo[e] = a.scale * dec_sum16(oo[e]);
-  if (r == 0) store4(o + (size_t)unit * Dv + col, oo);
-#pragma unroll
-  for (int i = 0; i < kDecRowsPerLane; ++i)
-    *reinterpret_cast<f32x4*>(a.hT + (srow + r + 16 * i) * Dv + col) = S[i];
+  if (live && r == 0) store4(o + (size_t)unit * Dv + col, oo);
 }
 
 bool decode128_applies(const RecurrentArgs& a) {
