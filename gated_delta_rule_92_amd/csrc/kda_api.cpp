@@ -3,6 +3,7 @@
 // every entry point are in include/kda.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <stdint.h>
@@ -63,7 +64,8 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
                             const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
                             int Dv, int chunk, float scale, void* o, float* final_state,
                             void* workspace, size_t workspace_bytes, kda_stream_t stream,
-                            const void* og, const float* onw, float oeps, int segments);
+                            const void* og, const float* onw, float oeps, int segments,
+                            bool first_out_ok);
 
 // Workspace of the longest-first order of packed sequences (cu_seqlens only).
 size_t order_bytes(int B, int N) {
@@ -71,26 +73,44 @@ size_t order_bytes(int B, int N) {
                                                   : 0;
 }
 
-// Context split of dense sequences on one GPU: each of the B sequences is cut
-// into P consecutive pieces of Lp tokens (a multiple of the chunk; the last
-// piece takes the rest). The pieces run in parallel, first for their state
-// maps and zero-start final states, then, after the entry states are chained,
-// for the output. The state recurrence is linear in the state, so this equals
-// the unsplit forward up to rounding.
+// Context split on one GPU: each sequence is cut into P consecutive pieces
+// that run in parallel. The state recurrence is linear in the state, so a
+// piece's final state is M S_entry + b with M its state map and b its
+// zero-start final state; chaining those gives every piece's entry state, and
+// every piece then runs from its entry state with output. The result equals
+// the unsplit forward up to rounding. Two schedules:
+//   mapped:     pieces of Lp tokens (a multiple of the chunk; the last takes
+//               the rest); M and b of every piece but each sequence's last
+//               (split pass), entry states chained from the initial state,
+//               then every piece with output.
+//   first-out:  piece 0 (L0 tokens), whose entry state is the initial state,
+//               runs with output on a second stream while the split pass
+//               maps pieces 1..P-2 (Lp tokens each; the last takes the
+//               rest); the entry states of pieces 2..P-1 are chained from
+//               piece 0's final state, then pieces 1..P-1 run with output.
+//               L0 is chosen so that piece 0's forward and the split pass
+//               end together.
 struct SplitPlan {
   int P = 1;
-  size_t M = 0, b = 0, starts = 0, bytes = 0;  // workspace offsets; the piece table is at 0
+  bool first_out = false;
+  int L0 = 0, Lp = 0;  // first-out: token counts (dense); mapped: Lp from each length
+  // workspace offsets: the piece table is at 0
+  size_t first = 0, middle = 0, later = 0, mapped = 0, M = 0, b = 0, starts = 0, bytes = 0;
 };
 
 // Workspace of a split of nseq sequences into P pieces each: the piece table
-// (nseq * P + 1 int32), then per piece and head the state map M, the
-// zero-start final state b and the entry state.
+// (nseq * P + 1 int32), the unit orders, then per piece and head the state
+// map M, the zero-start final state b and the entry state.
 SplitPlan split_layout(int nseq, int H, int Dk, int Dv, int P) {
   SplitPlan p;
   if (P < 2 || nseq <= 0) return p;
   p.P = P;
-  const size_t pieces = (size_t)nseq * P;
-  p.M = round_up(sizeof(int32_t) * (pieces + 1), kWorkspaceAlign);
+  const size_t pieces = (size_t)nseq * P, i4 = sizeof(int32_t);
+  p.first = round_up(i4 * (pieces + 1), kWorkspaceAlign);
+  p.middle = p.first + round_up(i4 * nseq, kWorkspaceAlign);
+  p.later = p.middle + round_up(i4 * nseq * (P - 2), kWorkspaceAlign);
+  p.mapped = p.later + round_up(i4 * nseq * (P - 1), kWorkspaceAlign);
+  p.M = p.mapped + round_up(i4 * nseq * (P - 1), kWorkspaceAlign);
   p.b = p.M + round_up(pieces * H * Dk * Dk * sizeof(float), kWorkspaceAlign);
   p.starts = p.b + round_up(pieces * H * Dk * Dv * sizeof(float), kWorkspaceAlign);
   p.bytes = p.starts + round_up(pieces * H * Dk * Dv * sizeof(float), kWorkspaceAlign);
@@ -99,13 +119,25 @@ SplitPlan split_layout(int nseq, int H, int Dk, int Dv, int P) {
 
 // The split kda_chunk_fwd takes by itself, for dense sequences whose B*H
 // (sequence, head) units leave compute units idle (each unit is one serial
-// chain of 16-token tiles on one CU, about a microsecond per tile):
-// P = min(CUs / units, T / kSplitMinPiece, kSplitMaxPieces) pieces, taken when
-// P >= 4 and its three passes over T / P tokens plus about 20 us of fixed
-// cost (piece table, composition, launches) beat one pass over T by 10%:
-// T (0.9 - 3 / P) > 300 tile-microseconds' worth of tokens.
+// chain of 16-token tiles on one CU, about a microsecond per tile). The split
+// is taken when the mapped schedule with P = min(CUs / units, T /
+// kSplitMinPiece, kSplitMaxPieces) has P >= 4 and its three passes over T / P
+// tokens plus about 20 us of fixed cost (piece table, composition, launches)
+// beat one pass over T by 10%: T (0.9 - 3 / P) > 300 tile-microseconds' worth
+// of tokens. With a second stream, the first-out schedule with the lowest
+// modelled time replaces it when that is lower. Model, in tokens of one
+// chain on a loaded GPU: the split pass costs kSplitPassRatio per token
+// (90.8 vs 80.8 ns measured for long256k's pieces, the two sharing the
+// GPU), a forward 1, a
+// composition step kComposeStepTokens (about 2.6 us against 16 tokens per
+// 1.4 us), and the first-out schedule's fork to the second stream and join
+// back kForkJoinTokens (about 6 + 12 us measured between the two queues'
+// kernels).
 constexpr int kSplitMinPiece = 256;
 constexpr int kSplitMaxPieces = 64;
+constexpr double kSplitPassRatio = 1.12;
+constexpr double kComposeStepTokens = 30.0;
+constexpr double kForkJoinTokens = 200.0;
 
 int device_compute_units() {
   int dev = 0, n = 0;
@@ -114,7 +146,8 @@ int device_compute_units() {
   return n;
 }
 
-SplitPlan auto_split(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype_t dtype) {
+SplitPlan auto_split(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype_t dtype,
+                     bool first_out) {
   if (!kda::chunk_pipe_supported(dtype == KDA_BFLOAT16, Dk, Dv, chunk)) return SplitPlan{};
   const long units = (long)B * H;
   const int cus = device_compute_units();
@@ -124,8 +157,45 @@ SplitPlan auto_split(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype_t
   if (P > kSplitMaxPieces) P = kSplitMaxPieces;
   if (P < 4 || (long)T * (9 * P - 30) <= 3000 * P) return SplitPlan{};
   if ((long)B * T > 0x7fffffffL) return SplitPlan{};  // the piece table is int32
-  return split_layout(B, H, Dk, Dv, (int)P);
+  SplitPlan best = split_layout(B, H, Dk, Dv, (int)P);
+  if (!first_out) return best;
+  const long Lm = ((long)T + P - 1) / P, Lpm = (Lm + chunk - 1) / chunk * chunk;
+  double best_cost = (1.0 + kSplitPassRatio) * (double)Lpm + kComposeStepTokens * (double)(P - 1);
+  const long jobs = cus / units;  // pieces per pass that find a CU of their own
+  for (long Pf = 3; Pf <= jobs + 1 && Pf - 1 <= kSplitMaxPieces; ++Pf) {
+    // middle pieces of a tokens and a first piece of about kSplitPassRatio * a,
+    // both whole chunks; the last piece takes the rest, at most a
+    const double per = (double)T / ((double)(Pf - 1) + kSplitPassRatio);
+    const long a = ((long)per + chunk - 1) / chunk * chunk;
+    long L0 = (long)(kSplitPassRatio * (double)a) / chunk * chunk;
+    long last = (long)T - L0 - (Pf - 2) * a;
+    if (last > a) {
+      L0 += (last - a + chunk - 1) / chunk * chunk;
+      last = (long)T - L0 - (Pf - 2) * a;
+    }
+    if (a < kSplitMinPiece || L0 < a || last <= 0) continue;
+    const double cost = std::max((double)L0, kSplitPassRatio * (double)a) + (double)a +
+                        kComposeStepTokens * (double)(Pf - 2) + kForkJoinTokens;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = split_layout(B, H, Dk, Dv, (int)Pf);
+      best.first_out = true;
+      best.L0 = (int)L0;
+      best.Lp = (int)a;
+    }
+  }
+  return best;
 }
+
+// Second stream of the first-out schedule and its fork / join events, one
+// set per device, created at the first such split on the device and kept
+// until the process ends. g_aux_mu is held from the fork to the join, so
+// calls from several host threads do not interleave their event records.
+struct AuxStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool failed = false;
+};
 
 // Device address of `device_flags` on the current device, looked up once per
 // device with that device current.
@@ -167,6 +237,27 @@ kda_status_t noalloc_scratch(void** out) {
   }
   *out = g_scratch_ptr[dev];
   return KDA_SUCCESS;
+}
+
+std::mutex g_aux_mu;
+AuxStream g_aux[kMaxDevices];
+
+// The current device's second stream (created on first use), or nullptr when
+// it cannot be had. Call with g_aux_mu held.
+AuxStream* aux_stream_locked() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  AuxStream& x = g_aux[dev];
+  if (x.failed) return nullptr;
+  if (!x.s) {
+    if (hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&x.join, hipEventDisableTiming) != hipSuccess) {
+      x.failed = true;
+      return nullptr;
+    }
+  }
+  return &x;
 }
 
 // Polls after which a bounded wait of the pipelined kernel gives up (0: the
@@ -218,8 +309,12 @@ kda_status_t kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, i
   if (dtype != KDA_FLOAT32 && dtype != KDA_BFLOAT16) return KDA_ERROR_INVALID_VALUE;
   // Longest-first order of packed sequences (used only with cu_seqlens), or
   // the context split of long dense sequences with few units.
+  // Either schedule may be taken (kda_chunk_fwd_noalloc takes the mapped one).
   const size_t order = order_bytes(B, N);
-  const size_t split = N == B ? auto_split(B, T, H, Dk, Dv, chunk, dtype).bytes : 0;
+  const size_t split =
+      N == B ? std::max(auto_split(B, T, H, Dk, Dv, chunk, dtype, true).bytes,
+                        auto_split(B, T, H, Dk, Dv, chunk, dtype, false).bytes)
+             : 0;
   *bytes = order > split ? order : split;
   return KDA_SUCCESS;
 }
@@ -243,7 +338,7 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtyp
                            void* workspace, size_t workspace_bytes, kda_stream_t stream) {
   return chunk_fwd_impl(q, k, v, dtype, g, gate_input, A_log, g_min, beta, initial_state,
                         cu_seqlens, N, B, T, H, Dk, Dv, chunk, scale, o, final_state, workspace,
-                        workspace_bytes, stream, nullptr, nullptr, 0.f, 0);
+                        workspace_bytes, stream, nullptr, nullptr, 0.f, 0, true);
 }
 
 kda_status_t kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, kda_dtype_t dtype,
@@ -268,7 +363,7 @@ kda_status_t kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, 
   }
   return chunk_fwd_impl(q, k, v, dtype, g, gate_input, A_log, g_min, beta, initial_state,
                         cu_seqlens, N, B, T, H, Dk, Dv, chunk, scale, o, final_state, ws, need,
-                        stream, nullptr, nullptr, 0.f, 0);
+                        stream, nullptr, nullptr, 0.f, 0, false);
 }
 
 kda_status_t kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_dtype_t dtype,
@@ -288,7 +383,7 @@ kda_status_t kda_chunk_fwd_split(const void* q, const void* k, const void* v, kd
   if ((long)B * T > 0x7fffffffL) return KDA_ERROR_NOT_SUPPORTED;
   return chunk_fwd_impl(q, k, v, dtype, g, gate_input, A_log, g_min, beta, initial_state,
                         cu_seqlens, N, B, T, H, Dk, Dv, chunk, scale, o, final_state, workspace,
-                        workspace_bytes, stream, nullptr, nullptr, 0.f, segments);
+                        workspace_bytes, stream, nullptr, nullptr, 0.f, segments, false);
 }
 
 kda_status_t kda_chunk_fwd_gated(const void* q, const void* k, const void* v, kda_dtype_t dtype,
@@ -303,7 +398,7 @@ kda_status_t kda_chunk_fwd_gated(const void* q, const void* k, const void* v, kd
   if (Dv > 512) return KDA_ERROR_NOT_SUPPORTED;
   return chunk_fwd_impl(q, k, v, dtype, g, gate_input, A_log, g_min, beta, initial_state,
                         cu_seqlens, N, B, T, H, Dk, Dv, chunk, scale, y, final_state, workspace,
-                        workspace_bytes, stream, out_gate, norm_weight, eps, 0);
+                        workspace_bytes, stream, out_gate, norm_weight, eps, 0, true);
 }
 
 kda_status_t kda_gated_rmsnorm(const void* o, const void* gate, kda_dtype_t dtype,
@@ -327,7 +422,8 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
                             const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
                             int Dv, int chunk, float scale, void* o, float* final_state,
                             void* workspace, size_t workspace_bytes, kda_stream_t stream,
-                            const void* og, const float* onw, float oeps, int segments) {
+                            const void* og, const float* onw, float oeps, int segments,
+                            bool first_out_ok) {
   kda::Seqs s;
   kda_status_t st = check_seqs(cu_seqlens, N, B, T, &s);
   if (st != KDA_SUCCESS) return st;
@@ -368,7 +464,7 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
     if (split.P > 1 && (!workspace || workspace_bytes < split.bytes))
       return KDA_ERROR_INSUFFICIENT_WORKSPACE;
   } else if (!cu_seqlens && o && fused && !softplus && workspace) {
-    split = auto_split(B, T, H, Dk, Dv, chunk, dtype);
+    split = auto_split(B, T, H, Dk, Dv, chunk, dtype, first_out_ok);
     if (workspace_bytes < split.bytes) split = SplitPlan{};
   }
   const size_t need = order_bytes(B, s.N);
@@ -383,58 +479,91 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (split.P > 1) {
-    // 1. piece table; 2. per piece its state map M and its zero-start final
-    // state b; 3. entry states chained per sequence; 4. every piece from its
-    // entry state, with output, each sequence's last piece writing the
-    // sequence's final state.
     char* ws = static_cast<char*>(workspace);
-    int32_t* cu = reinterpret_cast<int32_t*>(ws);
+    kda::SplitTables tab;
+    tab.table = reinterpret_cast<int32_t*>(ws);
+    tab.first = reinterpret_cast<int32_t*>(ws + split.first);
+    tab.middle = reinterpret_cast<int32_t*>(ws + split.middle);
+    tab.later = reinterpret_cast<int32_t*>(ws + split.later);
+    tab.mapped = reinterpret_cast<int32_t*>(ws + split.mapped);
     float* M = reinterpret_cast<float*>(ws + split.M);
     float* bst = reinterpret_cast<float*>(ws + split.b);
     float* starts = reinterpret_cast<float*>(ws + split.starts);
     const int P = split.P;
     const int nseq = s.N;
-    // packed sequences: the piece table from cu_seqlens, on the device;
-    // dense ones: the kernels derive the pieces from (T, P, Lp) and the split
-    // pass writes the same table
-    hipError_t e = hipSuccess;
-    kda::ChunkArgs a;
-    a.k = k; a.g = g; a.gate_mode = (int)gate_input;
+    const size_t piece = (size_t)H * Dk * Dv;  // floats of one piece's states
+    const size_t piece_m = (size_t)H * Dk * Dk;
+    hipError_t e = kda::launch_split_tables(tab, cu_seqlens, nseq, T, P, split.first_out ? split.L0 : 0,
+                                            split.Lp, chunk, hs);
+    if (e != hipSuccess) return KDA_ERROR_LAUNCH_FAILURE;
+    kda::ChunkArgs a{};
+    a.q = nullptr; a.k = k; a.v = v; a.g = g; a.gate_mode = (int)gate_input;
     a.A_log = A_log; a.g_min = g_min; a.beta = beta;
-    a.seqs.N = nseq * P; a.seqs.T = T; a.seqs.Ttot = s.Ttot;
-    if (cu_seqlens) {
-      e = kda::launch_split_pieces(cu, cu_seqlens, nseq, T, P, chunk, hs);
-      a.seqs.cu = cu;
-    } else {
-      const long per = ((long)T + P - 1) / P;
-      a.seqs.cu = nullptr;
-      a.seqs.split_P = P;
-      a.seqs.split_Lp = (int)((per + chunk - 1) / chunk * chunk);
-      a.piece_table = cu;
-    }
-    a.order = nullptr;
+    a.h0 = nullptr; a.hT = nullptr; a.o = nullptr; a.order = nullptr;
+    a.seqs.cu = tab.table; a.seqs.N = 0; a.seqs.T = T; a.seqs.Ttot = s.Ttot;
     a.H = H; a.Dk = Dk; a.Dv = Dv; a.scale = scale; a.bf16 = bf16;
     a.status = flags; a.spin_limit = spin_limit;
-    if (e == hipSuccess) {
-      // state maps (v = 0 from S = I) and zero-start final states, in one
-      // launch that reads k, v, g and beta once
+    // with output: q, o and the epilogue
+    auto with_output = [&](kda::ChunkArgs f) {
+      f.q = q; f.o = o; f.og = og; f.onw = onw; f.oeps = oeps;
+      return f;
+    };
+    // the split pass over the pieces in `order`: M and the zero-start final
+    // state b, in one launch that reads k, v, g and beta once
+    auto map_pieces = [&](const int32_t* order, int count) {
       kda::ChunkArgs z = a;
-      z.q = nullptr; z.v = v; z.o = nullptr; z.h0 = nullptr; z.hT = M; z.hT2 = bst;
-      e = kda::launch_chunk_split_pass(z, hs);
+      z.order = order; z.seqs.N = count; z.hT = M; z.hT2 = bst;
+      return kda::launch_chunk_split_pass(z, hs);
+    };
+    if (split.first_out) {
+      std::lock_guard<std::mutex> lock(g_aux_mu);
+      AuxStream* aux = aux_stream_locked();
+      if (!aux) return KDA_ERROR_LAUNCH_FAILURE;
+      // piece 0 of every sequence from the initial state, with output, on
+      // the second stream; its final state is piece 1's entry state
+      kda::ChunkArgs f0 = with_output(a);
+      f0.order = tab.first; f0.seqs.N = nseq;
+      f0.h0 = initial_state; f0.h0_group = P; f0.hT = starts + piece;
+      if (hipEventRecord(aux->fork, hs) != hipSuccess ||
+          hipStreamWaitEvent(aux->s, aux->fork, 0) != hipSuccess)
+        return KDA_ERROR_LAUNCH_FAILURE;
+      e = kda::launch_chunk_pipe(f0, aux->s);
+      const hipError_t ej = hipEventRecord(aux->join, aux->s);
+      if (e == hipSuccess) e = ej;
+      // meanwhile the maps of pieces 1..P-2
+      if (e == hipSuccess && P > 2) e = map_pieces(tab.middle, nseq * (P - 2));
+      // the join is enqueued even after an error, so the stream never runs
+      // ahead of piece 0's launch
+      const hipError_t ew = hipStreamWaitEvent(hs, aux->join, 0);
+      if (e == hipSuccess) e = ew;
+      // entry states of pieces 2..P-1 from piece 1's
+      if (e == hipSuccess)
+        e = kda::launch_compose(M + piece_m, bst + piece, starts + piece, P, nseq, P - 1, P, H, Dk,
+                                Dv, starts + piece, hs);
+      if (e == hipSuccess) {
+        kda::ChunkArgs f = with_output(a);
+        f.order = tab.later; f.seqs.N = nseq * (P - 1);
+        f.h0 = starts; f.hT = final_state; f.hT_group = P;
+        e = kda::launch_chunk_pipe(f, hs);
+      }
+      return launch_status(e);
     }
-    if (e == hipSuccess) e = kda::launch_compose(M, bst, initial_state, nseq, P, H, Dk, Dv, starts, hs);
+    // mapped: the maps of every piece but each sequence's last, entry states
+    // from the initial state, then every piece with output; each sequence's
+    // last piece writes the sequence's final state
+    e = map_pieces(tab.mapped, nseq * (P - 1));
+    if (e == hipSuccess)
+      e = kda::launch_compose(M, bst, initial_state, 1, nseq, P, P, H, Dk, Dv, starts, hs);
     if (e == hipSuccess) {
-      // the output, each piece from its entry state; each sequence's last
-      // piece writes the sequence's final state
-      kda::ChunkArgs f = a;
-      f.q = q; f.v = v; f.o = o; f.h0 = starts; f.hT = final_state; f.hT_group = P;
-      f.og = og; f.onw = onw; f.oeps = oeps;
+      kda::ChunkArgs f = with_output(a);
+      f.order = nullptr; f.seqs.N = nseq * P;
+      f.h0 = starts; f.hT = final_state; f.hT_group = P;
       e = kda::launch_chunk_pipe(f, hs);
     }
     return launch_status(e);
   }
   if (fused) {
-    kda::ChunkArgs a;
+    kda::ChunkArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.gate_mode = (int)gate_input;
     a.A_log = A_log; a.g_min = g_min; a.beta = beta;
     a.h0 = initial_state; a.hT = final_state; a.o = o;
@@ -456,7 +585,7 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
       e = kda::launch_gated_rmsnorm(o, og, bf16, onw, oeps, s.Ttot * H, Dv, o, hs);
     return launch_status(e);
   }
-  kda::RecurrentArgs r;
+  kda::RecurrentArgs r{};
   r.q = q; r.k = k; r.v = v; r.g = g; r.gate_mode = (int)gate_input;
   r.A_log = A_log; r.g_min = g_min; r.beta = beta;
   r.h0 = initial_state; r.hT = final_state; r.o = o;
@@ -499,7 +628,7 @@ kda_status_t kda_chunk_transition(const void* k, kda_dtype_t dtype, const float*
   if (workspace && workspace_bytes < need) return KDA_ERROR_INSUFFICIENT_WORKSPACE;
   if (s.N == 0) return KDA_SUCCESS;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  kda::ChunkArgs a;
+  kda::ChunkArgs a{};
   st = failure_reporting(&a.status, &a.spin_limit);
   if (st != KDA_SUCCESS) return st;
   a.q = nullptr; a.k = k; a.v = nullptr; a.g = g; a.gate_mode = (int)gate_input;
@@ -524,7 +653,7 @@ kda_status_t kda_compose_states(const float* M, const float* b, const float* ini
   if (Dk > 256) return KDA_ERROR_NOT_SUPPORTED;
   if ((size_t)nseq * P * H > (size_t)0x7fffffff) return KDA_ERROR_INVALID_VALUE;
   if (!aligned16(M)) return KDA_ERROR_INVALID_VALUE;
-  return launch_status(kda::launch_compose(M, b, initial_state, nseq, P, H, Dk, Dv, starts,
+  return launch_status(kda::launch_compose(M, b, initial_state, 1, nseq, P, P, H, Dk, Dv, starts,
                                            reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -545,7 +674,7 @@ kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v, kda
     return KDA_ERROR_INVALID_VALUE;
   if (Dk > 256) return KDA_ERROR_NOT_SUPPORTED;
   if (N == 0) return KDA_SUCCESS;
-  kda::RecurrentArgs r;
+  kda::RecurrentArgs r{};
   r.q = q; r.k = k; r.v = v; r.g = g; r.gate_mode = (int)gate_input;
   r.A_log = A_log; r.g_min = g_min; r.beta = beta;
   r.h0 = state; r.hT = state; r.o = o;
@@ -630,7 +759,7 @@ kda_status_t kda_chunk_bwd(const void* q, const void* k, const void* v, kda_dtyp
   const size_t ck = round_up((size_t)bwd_slots_bound(B, T, s.N, dtype) * H * Dk * Dv * e, kWorkspaceAlign);
   const size_t tok = round_up((size_t)B * T * H * Dv * e, kWorkspaceAlign);
   char* ws = static_cast<char*>(workspace);
-  kda::BwdArgs a;
+  kda::BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.g = g; a.gate = (int)gate_input;
   a.A_log = A_log; a.g_min = g_min; a.beta = beta; a.h0 = initial_state;
   a.cu = cu_seqlens; a.N = s.N; a.T = T; a.H = H; a.scale = scale;

@@ -224,18 +224,6 @@ __global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : 
   if (a.seqs.cu) {
     bos = a.seqs.cu[n];
     len = (long)a.seqs.cu[n + 1] - bos;
-  } else if (a.seqs.split_P > 0) {
-    const int P = a.seqs.split_P, sq = n / P, pc = n - sq * P;
-    const long T = a.seqs.T, lo = min((long)pc * a.seqs.split_Lp, T);
-    bos = (long)sq * T + lo;
-    len = min((long)(pc + 1) * a.seqs.split_Lp, T) - lo;
-    if constexpr (DUAL) {
-      if (a.piece_table && blockIdx.x == 0)
-        for (int i = tid; i <= a.seqs.N; i += blockDim.x) {
-          const int si = i / P, pi = i - si * P;
-          a.piece_table[i] = (int32_t)(i == a.seqs.N ? (long)si * T : (long)si * T + min((long)pi * a.seqs.split_Lp, T));
-        }
-    }
   } else {
     bos = (long)n * a.seqs.T;
     len = a.seqs.T;
@@ -704,7 +692,8 @@ __global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : 
 #pragma unroll
           for (int e = 0; e < 4; ++e) S[ct][b][e] = (16 * ct + 4 * g4 + e == vc0 + 16 * b + m) ? 1.f : 0.f;
     } else if (a.h0) {
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.h0 + sbase, PDK * PDV * 4);
+      const size_t h0base = a.h0_group > 0 ? ((size_t)(n / a.h0_group) * H + h) * PDK * PDV : sbase;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.h0 + h0base, PDK * PDV * 4);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll

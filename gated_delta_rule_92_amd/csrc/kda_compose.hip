@@ -20,11 +20,15 @@ constexpr int kComposeThreads = 256;
 constexpr int kComposeCols = 16;
 constexpr int kComposeMaxDk = 256;
 
+// Segment p of sequence s is entry s * stride + p of M, b and starts; the
+// sequence's entry state is entry s * s0_stride of S0, which may be the
+// sequence's starts[0] itself (read into LDS before the first write, so S0
+// and starts carry no __restrict__).
 __global__ void __launch_bounds__(kComposeThreads) compose_kernel(const float* __restrict__ M,
                                                                   const float* __restrict__ b,
-                                                                  const float* __restrict__ S0, int P,
-                                                                  int H, int Dk, int Dv,
-                                                                  float* __restrict__ starts) {
+                                                                  const float* S0, int s0_stride,
+                                                                  int P, int stride, int H, int Dk,
+                                                                  int Dv, float* starts) {
   __shared__ float cur[kComposeMaxDk][kComposeCols];
   const int sh = blockIdx.x;  // sequence * H + head
   const int seq = sh / H, h = sh % H;
@@ -37,11 +41,11 @@ __global__ void __launch_bounds__(kComposeThreads) compose_kernel(const float* _
 
   // entry state of segment 0
   for (int r = rg; r < Dk; r += kRowGroups)
-    cur[r][c] = (S0 && cvalid) ? S0[(((size_t)seq * H + h) * Dk + r) * Dv + c0 + c] : 0.f;
+    cur[r][c] = (S0 && cvalid) ? S0[(((size_t)seq * s0_stride * H + h) * Dk + r) * Dv + c0 + c] : 0.f;
   __syncthreads();
 
   for (int p = 0; p < P; ++p) {
-    const size_t sp = (size_t)seq * P + p;
+    const size_t sp = (size_t)seq * stride + p;
     float* out = starts + (sp * H + h) * (size_t)Dk * Dv;
     if (cvalid)
       for (int r = rg; r < Dk; r += kRowGroups) out[(size_t)r * Dv + c0 + c] = cur[r][c];
@@ -87,8 +91,8 @@ constexpr int kCT = kC128 + 4;  // padded row of the transposed slice
 
 __global__ void __launch_bounds__(512) compose128_kernel(const float* __restrict__ M,
                                                          const float* __restrict__ b,
-                                                         const float* __restrict__ S0, int P, int H,
-                                                         int Dv, float* __restrict__ starts) {
+                                                         const float* S0, int s0_stride, int P,
+                                                         int stride, int H, int Dv, float* starts) {
   // ping-pong: step p reads slice p & 1 and writes slice (p + 1) & 1
   __shared__ __attribute__((aligned(16))) float curT2[2][kComposeCols][kCT];
   const int sh = blockIdx.x;  // sequence * H + head
@@ -102,19 +106,20 @@ __global__ void __launch_bounds__(512) compose128_kernel(const float* __restrict
 
   for (int i = tid; i < kComposeCols * kC128; i += 512) {
     const int col = i % kComposeCols, row = i / kComposeCols;
-    curT2[0][col][row] = (S0 && c0 + col < Dv) ? S0[(((size_t)seq * H + h) * kC128 + row) * Dv + c0 + col]
-                                               : 0.f;
+    curT2[0][col][row] = (S0 && c0 + col < Dv)
+                             ? S0[(((size_t)seq * s0_stride * H + h) * kC128 + row) * Dv + c0 + col]
+                             : 0.f;
   }
   // row row0 + n of M_p, entries 16i + 4g .. 16i + 4g + 3 for i = 0..7
   auto load_m = [&](int p, f32x4 (&a)[8]) {
-    const float* Mp = M + (((size_t)seq * P + p) * H + h) * (size_t)kC128 * kC128 +
+    const float* Mp = M + (((size_t)seq * stride + p) * H + h) * (size_t)kC128 * kC128 +
                       (size_t)(row0 + n) * kC128 + 4 * g;
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const f32x4*>(Mp + 16 * i);
   };
   // entries (row0 + 4g + e, c0 + n) of b_p
   auto load_b = [&](int p, f32x4& v) {
-    const float* bp = b + (((size_t)seq * P + p) * H + h) * (size_t)kC128 * Dv;
+    const float* bp = b + (((size_t)seq * stride + p) * H + h) * (size_t)kC128 * Dv;
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = cvalid ? bp[(size_t)(row0 + 4 * g + e) * Dv + c0 + n] : 0.f;
   };
@@ -128,7 +133,7 @@ __global__ void __launch_bounds__(512) compose128_kernel(const float* __restrict
   for (int p = 0; p < P; ++p) {
     float (*curT)[kCT] = curT2[p & 1];
     float (*nxtT)[kCT] = curT2[(p + 1) & 1];
-    const size_t sp = (size_t)seq * P + p;
+    const size_t sp = (size_t)seq * stride + p;
     float* out = starts + (sp * H + h) * (size_t)kC128 * Dv;
     if (cvalid) {
 #pragma unroll
@@ -159,50 +164,60 @@ __global__ void __launch_bounds__(512) compose128_kernel(const float* __restrict
   }
 }
 
-// Boundaries of the pieces of a context split: each of nseq sequences (B
-// dense sequences of T tokens when cu is null, else the packed sequences of
-// cu) is cut into P consecutive pieces of Lp = chunk * ceil(ceil(L / P) /
-// chunk) tokens, the last taking the rest (pieces may be empty):
-// out[s*P + p] = start(s) + min(p*Lp, L(s)), out[nseq*P] = the total.
-__global__ void split_pieces_kernel(int32_t* __restrict__ out, const int32_t* __restrict__ cu,
-                                    int nseq, int T, int P, int chunk) {
+// Piece table and unit orders of a context split (see launch_split_tables):
+// one thread per table entry and one per order entry of each sequence.
+__global__ void split_tables_kernel(SplitTables t, const int32_t* __restrict__ cu, int nseq, int T,
+                                    int P, int L0, int Lp, int chunk) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   const int n = nseq * P;
+  if (i < nseq) t.first[i] = i * P;
+  if (i < nseq * (P - 2)) t.middle[i] = (i / (P - 2)) * P + 1 + i % (P - 2);
+  if (i < nseq * (P - 1)) {
+    t.later[i] = (i / (P - 1)) * P + 1 + i % (P - 1);
+    t.mapped[i] = (i / (P - 1)) * P + i % (P - 1);
+  }
   if (i > n) return;
   if (i == n) {
-    out[i] = cu ? cu[nseq] : (int32_t)((long)nseq * T);
+    t.table[i] = cu ? cu[nseq] : (int32_t)((long)nseq * T);
     return;
   }
   const int s = i / P, p = i - s * P;
   const long start = cu ? (long)cu[s] : (long)s * T;
   const long L = cu ? (long)cu[s + 1] - start : (long)T;
-  const long per = (L + P - 1) / P;
-  const long Lp = (per + chunk - 1) / chunk * chunk;
-  const long off = (long)p * Lp < L ? (long)p * Lp : L;
-  out[i] = (int32_t)(start + off);
+  long off;
+  if (L0 > 0) {
+    off = p == 0 ? 0 : (long)L0 + (long)(p - 1) * Lp;
+  } else {
+    const long per = (L + P - 1) / P;
+    off = (long)p * ((per + chunk - 1) / chunk * chunk);
+  }
+  t.table[i] = (int32_t)(start + (off < L ? off : L));
 }
 
 }  // namespace
 
-hipError_t launch_split_pieces(int32_t* out, const int32_t* cu, int nseq, int T, int P, int chunk,
-                               hipStream_t stream) {
+hipError_t launch_split_tables(const SplitTables& t, const int32_t* cu, int nseq, int T, int P,
+                               int L0, int Lp, int chunk, hipStream_t stream) {
+  if (nseq <= 0 || P < 2) return hipErrorInvalidValue;
   const int n = nseq * P + 1;
-  hipLaunchKernelGGL(split_pieces_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                     out, cu, nseq, T, P, chunk);
+  hipLaunchKernelGGL(split_tables_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     t, cu, nseq, T, P, L0, Lp, chunk);
   return hipGetLastError();
 }
 
-hipError_t launch_compose(const float* M, const float* b, const float* S0, int nseq, int P, int H,
-                          int Dk, int Dv, float* starts, hipStream_t stream) {
+hipError_t launch_compose(const float* M, const float* b, const float* S0, int s0_stride, int nseq,
+                          int P, int stride, int H, int Dk, int Dv, float* starts,
+                          hipStream_t stream) {
   if (nseq == 0 || P == 0 || H == 0) return hipSuccess;
   if (Dk > kComposeMaxDk) return hipErrorInvalidValue;
   dim3 grid((unsigned)(nseq * H), (unsigned)((Dv + kComposeCols - 1) / kComposeCols));
   if (Dk == kC128) {
-    hipLaunchKernelGGL(compose128_kernel, grid, dim3(512), 0, stream, M, b, S0, P, H, Dv, starts);
+    hipLaunchKernelGGL(compose128_kernel, grid, dim3(512), 0, stream, M, b, S0, s0_stride, P,
+                       stride, H, Dv, starts);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(compose_kernel, grid, dim3(kComposeThreads), 0, stream, M, b, S0, P, H, Dk, Dv,
-                     starts);
+  hipLaunchKernelGGL(compose_kernel, grid, dim3(kComposeThreads), 0, stream, M, b, S0, s0_stride, P,
+                     stride, H, Dk, Dv, starts);
   return hipGetLastError();
 }
 

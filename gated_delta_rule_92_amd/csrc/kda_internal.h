@@ -18,16 +18,10 @@ constexpr unsigned int kDeviceDecayOutOfRange = 2u;
 // describes packed sequences, or cu == nullptr and sequence n covers tokens
 // [n*T, (n+1)*T) of a dense batch.
 struct Seqs {
-  const int32_t* cu;
-  int N;
-  int T;        // dense sequence length (ignored when cu != nullptr)
-  long Ttot;    // total tokens in the packed token axis
-  // dense context split (cu == nullptr, pipelined kernel only): the N units
-  // are N / split_P sequences of T tokens, each in split_P pieces of
-  // split_Lp tokens, unit n = piece n % split_P of sequence n / split_P
-  // covering its tokens [min(p Lp, T), min((p + 1) Lp, T))
-  int split_P = 0;
-  int split_Lp = 0;
+  const int32_t* cu = nullptr;
+  int N = 0;
+  int T = 0;    // dense sequence length (ignored when cu != nullptr)
+  long Ttot = 0;  // total tokens in the packed token axis
 };
 
 hipError_t launch_gate(const float* z, const float* A_log, float g_min, Seqs s, int H, int Dk,
@@ -37,42 +31,42 @@ hipError_t launch_gate(const float* z, const float* A_log, float g_min, Seqs s, 
 // (sequence, head), the state held on chip. Used for decode (one token per
 // sequence) and for shapes the chunk path does not cover.
 struct RecurrentArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const float* g;
-  int gate_mode;  // kGateLogDecay, kGateLogits or kGateSoftplus
-  const float* A_log;
-  float g_min;
-  const float* beta;
-  const float* h0;   // [N, H, Dk, Dv] or nullptr
-  float* hT;         // [N, H, Dk, Dv] or nullptr (may alias h0)
-  void* o;
-  Seqs seqs;
-  int H, Dk, Dv;
-  float scale;
-  bool bf16;
+  const void* q = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const float* g = nullptr;
+  int gate_mode = 0;  // kGateLogDecay, kGateLogits or kGateSoftplus
+  const float* A_log = nullptr;
+  float g_min = 0.f;
+  const float* beta = nullptr;
+  const float* h0 = nullptr;   // [N, H, Dk, Dv] or nullptr
+  float* hT = nullptr;  // [N, H, Dk, Dv] or nullptr (may alias h0)
+  void* o = nullptr;
+  Seqs seqs{};
+  int H = 0, Dk = 0, Dv = 0;
+  float scale = 0.f;
+  bool bf16 = false;
 };
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream);
 
 // Fused chunk kernel (matrix cores), one workgroup per (sequence, head).
 struct ChunkArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const float* g;
-  int gate_mode;
-  const float* A_log;
-  float g_min;
-  const float* beta;
-  const float* h0;
-  float* hT;
-  void* o;
-  Seqs seqs;
-  const int32_t* order;  // [N] longest-first sequence order, or nullptr
-  int H, Dk, Dv;
-  float scale;
-  bool bf16;
+  const void* q = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const float* g = nullptr;
+  int gate_mode = 0;
+  const float* A_log = nullptr;
+  float g_min = 0.f;
+  const float* beta = nullptr;
+  const float* h0 = nullptr;
+  float* hT = nullptr;
+  void* o = nullptr;
+  Seqs seqs{};
+  const int32_t* order = nullptr;  // [N] longest-first sequence order, or nullptr
+  int H = 0, Dk = 0, Dv = 0;
+  float scale = 0.f;
+  bool bf16 = false;
   // output epilogue (pipelined kernel only; og == nullptr: plain output):
   // o = sigmoid(og) * RMSNorm(o) * onw, eps oeps
   const void* og = nullptr;
@@ -87,13 +81,13 @@ struct ChunkArgs {
   void* ck_vt = nullptr;
   float* ck_at = nullptr;  // checkpoint mode: A_kk / beta per tile row, fp32 [Ttot, H, 16]
   float* hT2 = nullptr;    // split pass: zero-start final states [N, H, Dk, Dv]
-  // split pass over a dense split (seqs.split_P > 0): receives the piece
-  // table, out[i] = start of unit i, out[N] = the total (int32, N + 1)
-  int32_t* piece_table = nullptr;
   // pipelined kernel, > 0: the N units are N / hT_group sequences of hT_group
   // consecutive pieces, and only each sequence's last piece writes its final
   // state, to hT[n / hT_group]
   int hT_group = 0;
+  // pipelined kernel, > 0: unit n starts from h0[n / h0_group] (the initial
+  // state of a split sequence's first piece)
+  int h0_group = 0;
   // device-side failure reporting: the device's flags word (KDA_DEVICE_* of
   // kda.h, set with a global atomic OR; nullptr: not reported), and the polls
   // after which a bounded wait of the pipelined kernel gives up (0: default)
@@ -131,14 +125,35 @@ hipError_t launch_chunk_reverse(const ChunkArgs& a, hipStream_t stream);
 // Dv (<= 512) elements; y may alias o.
 hipError_t launch_gated_rmsnorm(const void* o, const void* z, bool bf16, const float* w, float eps,
                                 long rows, int Dv, void* y, hipStream_t stream);
-// Chains segment maps: starts[0] = S0, starts[p+1] = M_p starts[p] + b_p.
-hipError_t launch_compose(const float* M, const float* b, const float* S0, int nseq, int P,
-                          int H, int Dk, int Dv, float* starts, hipStream_t stream);
-// Piece table of a context split: each of nseq sequences (dense of T tokens
-// when cu is null, else packed by cu) into P chunk-aligned pieces:
-// out[nseq*P + 1] (device int32; dense callers keep nseq*T below 2^31).
-hipError_t launch_split_pieces(int32_t* out, const int32_t* cu, int nseq, int T, int P, int chunk,
-                               hipStream_t stream);
+// Chains segment maps: for each of nseq sequences, starts[0] = S0,
+// starts[p+1] = M_p starts[p] + b_p for p < P - 1, where segment p of
+// sequence s is entry s * stride + p of M, b and starts ([*, H, Dk, Dk] and
+// [*, H, Dk, Dv]) and S0 is entry s * s0_stride of S0 (nullptr: zeros). S0
+// may be starts[0] itself: it is read before anything is written.
+hipError_t launch_compose(const float* M, const float* b, const float* S0, int s0_stride, int nseq,
+                          int P, int stride, int H, int Dk, int Dv, float* starts,
+                          hipStream_t stream);
+// Piece table and unit orders of a context split of nseq sequences (dense of
+// T tokens when cu is null, else packed by cu) into P >= 2 pieces each.
+// Pieces: with L0 > 0 (dense only), piece 0 takes the first L0 tokens and
+// pieces 1.. take Lp each, the last one the rest; with L0 == 0, every piece
+// takes Lp(s) = chunk * ceil(ceil(L(s) / P) / chunk) tokens of its sequence,
+// the last one the rest (pieces may be empty). table[nseq*P + 1]: start of
+// piece s*P + p, then the total. Orders, s = 0..nseq-1 in turn:
+//   first[nseq]          s*P                 (each sequence's first piece)
+//   middle[nseq*(P-2)]   s*P + 1 .. s*P + P-2
+//   later[nseq*(P-1)]    s*P + 1 .. s*P + P-1
+//   mapped[nseq*(P-1)]   s*P .. s*P + P-2    (every piece but the last)
+// Device int32; dense callers keep nseq*T below 2^31.
+struct SplitTables {
+  int32_t* table;
+  int32_t* first;
+  int32_t* middle;
+  int32_t* later;
+  int32_t* mapped;
+};
+hipError_t launch_split_tables(const SplitTables& t, const int32_t* cu, int nseq, int T, int P,
+                               int L0, int Lp, int chunk, hipStream_t stream);
 // Lowest per-token log-decay the chunk path handles (16 * 5.5 = 88 < 88.7 = ln FLT_MAX).
 constexpr float kMinFusedGmin = -5.5f;
 // Lowest total log2-decay of one 16-token tile the chunk kernels accept
@@ -157,36 +172,36 @@ hipError_t launch_chunk_fused(const ChunkArgs& a, hipStream_t stream);
 // base(n) + c, base(n) = floor(cu[n] / CT) + n (packed) or n * ceil(T / CT)
 // (dense).
 struct BwdArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const float* g;
-  int gate;  // kGateLogDecay or kGateLogits
-  const float* A_log;
-  float g_min;
-  const float* beta;
-  const float* h0;     // [N, H, Dk, Dv] or nullptr
-  const int32_t* cu;   // packed sequences or nullptr (dense)
-  const int32_t* order;  // [N] longest-first sequence order for the scans, or nullptr
-  int N, T, H;         // T: dense sequence length
-  float scale;
-  const void* dO;      // [Ttot, H, Dv]
-  const float* dhT;    // [N, H, Dk, Dv] or nullptr
-  void* dq;
-  void* dk;
-  void* dv;
-  float* dg;
-  float* dbeta;
-  float* dh0;          // or nullptr
-  void* ckS;           // [slots, H, Dk, Dv] states entering each checkpoint chunk
-  void* ckdS;          // [slots, H, Dk, Dv] state gradients leaving each chunk
-  void* U;             // [Ttot, H, Dv] V - Kg S
-  void* Vt;            // [Ttot, H, Dv] pseudo-values
-  void* dY;            // [Ttot, H, Dv] T^T dV~
+  const void* q = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const float* g = nullptr;
+  int gate = 0;  // kGateLogDecay or kGateLogits
+  const float* A_log = nullptr;
+  float g_min = 0.f;
+  const float* beta = nullptr;
+  const float* h0 = nullptr;     // [N, H, Dk, Dv] or nullptr
+  const int32_t* cu = nullptr;  // packed sequences or nullptr (dense)
+  const int32_t* order = nullptr;  // [N] longest-first sequence order for the scans, or nullptr
+  int N = 0, T = 0, H = 0;         // T: dense sequence length
+  float scale = 0.f;
+  const void* dO = nullptr;      // [Ttot, H, Dv]
+  const float* dhT = nullptr;    // [N, H, Dk, Dv] or nullptr
+  void* dq = nullptr;
+  void* dk = nullptr;
+  void* dv = nullptr;
+  float* dg = nullptr;
+  float* dbeta = nullptr;
+  float* dh0 = nullptr;          // or nullptr
+  void* ckS = nullptr;           // [slots, H, Dk, Dv] states entering each checkpoint chunk
+  void* ckdS = nullptr;          // [slots, H, Dk, Dv] state gradients leaving each chunk
+  void* U = nullptr;             // [Ttot, H, Dv] V - Kg S
+  void* Vt = nullptr;            // [Ttot, H, Dv] pseudo-values
+  void* dY = nullptr;            // [Ttot, H, Dv] T^T dV~
   unsigned int* status = nullptr;  // device flags word, as in ChunkArgs
   int spin_limit = 0;
-  float* At;           // [Ttot, H, 16] row r of each tile's A~ = A_kk / beta
-                       // (strictly lower part; zeros elsewhere)
+  float* At = nullptr;  // [Ttot, H, 16] row r of each tile's A~ = A_kk / beta
+                        // (strictly lower part; zeros elsewhere)
 };
 inline bool chunk_bwd_supported(int Dk, int Dv) {
   return (Dk == 64 || Dk == 128) && (Dv == 64 || Dv == 128);

@@ -118,9 +118,10 @@ kda_status_t kda_gate(const float* z, const float* A_log, float g_min,
  * With packed sequences (B = 1, N > 1) it holds their longest-first order.
  * For dense bf16 Dk = Dv = 128 sequences whose B*H (sequence, head) units
  * leave the current device's compute units idle, it holds the context split
- * kda_chunk_fwd then takes (see there): the piece table, and per piece and
- * head a state map and two states (B * P * H * (Dk*Dk + 2*Dk*Dv) * 4 bytes),
- * with P = min(CUs / (B*H), T / 256, 64), taken when P >= 4 and
+ * kda_chunk_fwd then takes (see there): the piece table and unit orders, and
+ * per piece and head a state map and two states (B * P * H * (Dk*Dk +
+ * 2*Dk*Dv) * 4 bytes), for the larger of the two schedules' P. The split is
+ * taken when P = min(CUs / (B*H), T / 256, 64) has P >= 4 and
  * T (0.9 - 3/P) > 300 (three passes over T/P tokens plus a fixed cost must
  * beat one pass over T).
  */
@@ -157,8 +158,16 @@ kda_status_t kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, i
  * Long dense sequences with few units: when the workspace holds the split
  * kda_chunk_fwd_workspace_size sizes for (cu_seqlens NULL, o non-NULL, bf16
  * Dk = Dv = 128, a gate other than KDA_GATE_SOFTPLUS), every sequence is cut
- * into P chunk-aligned pieces that run in parallel, exactly as
- * kda_chunk_fwd_split with segments = P; otherwise one serial chain per unit.
+ * into chunk-aligned pieces that run in parallel; otherwise one serial chain
+ * per unit. Either as kda_chunk_fwd_split with segments = P (equal pieces),
+ * or, when a cost model of the two finds it faster, first-out: each
+ * sequence's first piece, whose entry state is the initial state, runs with
+ * output on a second stream of the library's (one per device, created at
+ * the first such call, kept until the process ends; forked from and joined
+ * back into `stream` with events, so the call stays ordered on `stream`)
+ * while the state maps of the middle pieces are formed (its length chosen
+ * so that both end together); the other pieces then run from entry states
+ * chained from its final state.
  * Supported: bf16 with Dk, Dv in {64, 128}; fp32 with Dk = Dv = 64 on the
  * matrix-core chunk path; any other Dk, Dv <= 256 (and fp32 at 128) runs a
  * token-serial kernel with the same results, as does KDA_GATE_LOGITS with
@@ -183,7 +192,10 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtyp
  * KDA_NOALLOC_SCRATCH_BYTES that each device holds from the library's first
  * use until the process ends. No hipMalloc, hipFree or other allocation is
  * made. Results equal kda_chunk_fwd's with a workspace of that size (the same
- * kernels and the same context-split decision).
+ * kernels and the same context-split decision), except where kda_chunk_fwd
+ * runs a longer first piece on its second stream: this entry point creates
+ * no stream and takes the equal-piece split instead, whose results agree
+ * with it up to rounding.
  * Arguments as for kda_chunk_fwd, without workspace. The caller still owns
  * q, k, v, g, beta, initial_state, o and final_state.
  * Errors: as kda_chunk_fwd; KDA_ERROR_INSUFFICIENT_WORKSPACE when
@@ -255,13 +267,12 @@ kda_status_t kda_chunk_fwd_split_workspace_size(int B, int T, int H, int Dk, int
  * a context split. The KDA equation is linear in the state [KDA-blog §Kimi
  * Delta Attention, KDA equation], so a piece's final state is M S_entry + b
  * with M its state map and b its zero-start final state. On the stream, in
- * order: the piece table (computed on the device from cu_seqlens; dense
- * pieces follow from T and are written by the next launch); M and b
- * of every piece (what kda_chunk_transition and the state-only forward
- * compute, in one launch that reads k, v, g and beta once); the entry states
- * chained per sequence (kda_compose_states); every piece from its entry
- * state with output, each sequence's last piece writing the sequence's
- * final state. The results equal kda_chunk_fwd's up to rounding.
+ * order: the piece table (computed on the device); M and b of every piece
+ * but each sequence's last (what kda_chunk_transition and the state-only
+ * forward compute, in one launch that reads k, v, g and beta once); the
+ * entry states chained per sequence (kda_compose_states); every piece from
+ * its entry state with output, each sequence's last piece writing the
+ * sequence's final state. The results equal kda_chunk_fwd's up to rounding.
  * Arguments as for kda_chunk_fwd; o must be non-NULL. workspace: device,
  * >= kda_chunk_fwd_split_workspace_size(...) bytes
  * (KDA_ERROR_INSUFFICIENT_WORKSPACE otherwise).

@@ -14,12 +14,26 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <initializer_list>
 
 #include "kda_internal.h"
 
 extern "C" {
 char kda_host_check_last_launch[64] = "";
 int kda_host_check_launches = 0;
+// What the latest launches were given, in order (the first 64 since the log
+// was cleared): a chunk-kernel launch records (q, h0, hT, hT2, o, order, cu, v)
+// and (seqs.N, h0_group, hT_group, 0); the composition (M, b, S0, starts)
+// and (nseq, P, stride, s0_stride); the split tables (table, first, middle,
+// later, mapped, cu) and (nseq, P, L0, Lp).
+struct KdaHostCheckLaunch {
+  char name[24];
+  const void* ptr[8];
+  int val[4];
+};
+KdaHostCheckLaunch kda_host_check_log[64];
+int kda_host_check_log_len = 0;
+void kda_host_check_log_clear(void) { kda_host_check_log_len = 0; }
 int kda_host_check_build(void) { return 1; }
 // compute units hipDeviceGetAttribute reports (256, as on an MI355X)
 static int g_cus = 256;
@@ -52,6 +66,27 @@ hipError_t hipMemsetAsync(void* dst, int value, size_t bytes, hipStream_t) {
 }
 hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
 
+// The second stream and events of the first-out context split: handles that
+// are never dereferenced, so any distinct non-null values do.
+static char g_handles[3];
+static int g_next_handle = 0;
+hipError_t hipStreamCreateWithFlags(hipStream_t* stream, unsigned int) {
+  if (!stream) return hipErrorInvalidValue;
+  *stream = reinterpret_cast<hipStream_t>(&g_handles[g_next_handle++ % 3]);
+  return hipSuccess;
+}
+hipError_t hipEventCreateWithFlags(hipEvent_t* event, unsigned int) {
+  if (!event) return hipErrorInvalidValue;
+  *event = reinterpret_cast<hipEvent_t>(&g_handles[g_next_handle++ % 3]);
+  return hipSuccess;
+}
+hipError_t hipEventRecord(hipEvent_t event, hipStream_t) {
+  return event ? hipSuccess : hipErrorInvalidValue;
+}
+hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t event, unsigned int) {
+  return event ? hipSuccess : hipErrorInvalidValue;
+}
+
 hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t attr, int device) {
   if (!value || device != 0) return hipErrorInvalidValue;
   *value = attr == hipDeviceAttributeMultiprocessorCount ? g_cus : 0;
@@ -60,10 +95,24 @@ hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t attr, int devi
 }
 
 namespace {
-hipError_t record(const char* name) {
+hipError_t record(const char* name, std::initializer_list<const void*> ptrs = {},
+                  std::initializer_list<int> vals = {}) {
   std::strncpy(kda_host_check_last_launch, name, sizeof(kda_host_check_last_launch) - 1);
   ++kda_host_check_launches;
+  if (kda_host_check_log_len < 64) {
+    KdaHostCheckLaunch& e = kda_host_check_log[kda_host_check_log_len++];
+    std::memset(&e, 0, sizeof(e));
+    std::strncpy(e.name, name, sizeof(e.name) - 1);
+    int i = 0;
+    for (const void* p : ptrs) e.ptr[i++] = p;
+    i = 0;
+    for (int v : vals) e.val[i++] = v;
+  }
   return hipSuccess;
+}
+hipError_t record_chunk(const char* name, const kda::ChunkArgs& a) {
+  return record(name, {a.q, a.h0, a.hT, a.hT2, a.o, a.order, a.seqs.cu, a.v},
+                {a.seqs.N, a.h0_group, a.hT_group, 0});
 }
 }  // namespace
 
@@ -72,21 +121,27 @@ hipError_t launch_gate(const float*, const float*, float, Seqs, int, int, int, f
   return record("gate");
 }
 hipError_t launch_recurrent(const RecurrentArgs&, hipStream_t) { return record("recurrent"); }
-hipError_t launch_chunk_pipe(const ChunkArgs&, hipStream_t) { return record("chunk_pipe"); }
-hipError_t launch_chunk_transition(const ChunkArgs&, hipStream_t) { return record("chunk_transition"); }
-hipError_t launch_chunk_split_pass(const ChunkArgs&, hipStream_t) { return record("chunk_split_pass"); }
+hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t) { return record_chunk("chunk_pipe", a); }
+hipError_t launch_chunk_transition(const ChunkArgs& a, hipStream_t) {
+  return record_chunk("chunk_transition", a);
+}
+hipError_t launch_chunk_split_pass(const ChunkArgs& a, hipStream_t) {
+  return record_chunk("chunk_split_pass", a);
+}
 hipError_t launch_chunk_checkpoint(const ChunkArgs&, hipStream_t) { return record("chunk_checkpoint"); }
 hipError_t launch_chunk_reverse(const ChunkArgs&, hipStream_t) { return record("chunk_reverse"); }
 hipError_t launch_gated_rmsnorm(const void*, const void*, bool, const float*, float, long, int, void*,
                                 hipStream_t) {
   return record("gated_rmsnorm");
 }
-hipError_t launch_compose(const float*, const float*, const float*, int, int, int, int, int, float*,
-                          hipStream_t) {
-  return record("compose");
+hipError_t launch_compose(const float* M, const float* b, const float* S0, int s0_stride, int nseq,
+                          int P, int stride, int, int, int, float* starts, hipStream_t) {
+  return record("compose", {M, b, S0, starts}, {nseq, P, stride, s0_stride});
 }
-hipError_t launch_split_pieces(int32_t*, const int32_t*, int, int, int, int, hipStream_t) {
-  return record("split_pieces");
+hipError_t launch_split_tables(const SplitTables& t, const int32_t* cu, int nseq, int, int P, int L0,
+                               int Lp, int, hipStream_t) {
+  return record("split_tables", {t.table, t.first, t.middle, t.later, t.mapped, cu},
+                {nseq, P, L0, Lp});
 }
 hipError_t launch_chunk_fused(const ChunkArgs&, hipStream_t) { return record("chunk_fused"); }
 hipError_t launch_chunk_bwd(const BwdArgs&, bool, int, int, long, hipStream_t) {

@@ -141,15 +141,20 @@ def test_transition_and_compose_validation():
 def test_split_forward_validation_and_workspace():
     lib = _lib.load()
     n = ctypes.c_size_t(0)
-    # piece table (B*P + 1 int32, 256-aligned), then per piece and head a
-    # Dk x Dk state map and two Dk x Dv states
+    # piece table (nseq*P + 1 int32) and the four unit orders (nseq, nseq*(P-2),
+    # nseq*(P-1), nseq*(P-1) int32), each 256-aligned, then per piece and
+    # head a Dk x Dk state map and two Dk x Dv states
+    def layout(nseq, P):
+        up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+        ints = up(4 * (nseq * P + 1)) + up(4 * nseq) + up(4 * nseq * (P - 2)) + 2 * up(4 * nseq * (P - 1))
+        return ints + 3 * nseq * P * 32 * 128 * 128 * 4
     assert lib.kda_chunk_fwd_split_workspace_size(1, 262144, 32, 128, 128, 1, 8, 64, 1,
                                                   ctypes.byref(n)) == 0
-    assert n.value == 256 + 3 * 8 * 32 * 128 * 128 * 4
-    # 64 packed sequences into 4 pieces: a table of 257 int32, 256 pieces' states
+    assert n.value == layout(1, 8) == 5 * 256 + 3 * 8 * 32 * 128 * 128 * 4
+    # 64 packed sequences into 4 pieces: 256 pieces' states
     assert lib.kda_chunk_fwd_split_workspace_size(1, 1 << 20, 32, 128, 128, 64, 4, 64, 1,
                                                   ctypes.byref(n)) == 0
-    assert n.value == 1280 + 3 * 256 * 32 * 128 * 128 * 4
+    assert n.value == layout(64, 4)
     assert lib.kda_chunk_fwd_split_workspace_size(2, 1000, 2, 128, 128, 2, 1, 64, 1,
                                                   ctypes.byref(n)) == 0
     assert n.value == 0
@@ -317,3 +322,91 @@ def test_noalloc_rejects_a_workspace_beyond_the_scratch():
         assert call() == _lib.KDA_SUCCESS
     finally:
         lib.kda_host_check_set_compute_units(256)
+
+
+class _Launch(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 24), ("ptr", ctypes.c_void_p * 8),
+                ("val", ctypes.c_int * 4)]
+
+
+def _split_offsets(nseq, P, H=32, Dk=128, Dv=128):
+    """Workspace offsets of a context split (piece table at 0)."""
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    o = {"first": up(4 * (nseq * P + 1))}
+    o["middle"] = o["first"] + up(4 * nseq)
+    o["later"] = o["middle"] + up(4 * nseq * (P - 2))
+    o["mapped"] = o["later"] + up(4 * nseq * (P - 1))
+    o["M"] = o["mapped"] + up(4 * nseq * (P - 1))
+    o["b"] = o["M"] + up(4 * nseq * P * H * Dk * Dk)
+    o["starts"] = o["b"] + up(4 * nseq * P * H * Dk * Dv)
+    return o
+
+
+def test_split_schedules_launch_what_they_should():
+    """Only in the host-check build, whose stub launchers record what each
+    launch is given: the two context-split schedules of long256k (B=1,
+    T=262144, H=32) on a 256-CU device, launch by launch. The split pass
+    must get no initial state, no q and no o (it computes state maps and
+    zero-start states); the first-out schedule runs piece 0 from the
+    initial state (h0_group = P) into piece 1's entry slot, maps pieces
+    1..P-2, chains from piece 1 and runs pieces 1..P-1; the equal-piece
+    schedule maps every piece but the last, chains from the initial state
+    and runs every piece."""
+    lib = _lib.load()
+    if not hasattr(lib, "kda_host_check_build"):
+        pytest.skip("needs the host-check build (tests/test_sanitizers_cpu.py)")
+    lib.kda_host_check_set_compute_units.argtypes = [ctypes.c_int]
+    lib.kda_host_check_set_compute_units(256)
+    log = (_Launch * 64).in_dll(lib, "kda_host_check_log")
+    n = ctypes.c_int.in_dll(lib, "kda_host_check_log_len")
+    T, H = 262144, 32
+    Q, K, V, G, BETA, H0, O, HT, WS = (FAKE * (i + 1) for i in range(9))
+    piece = 4 * H * 128 * 128  # bytes of one piece's states (and maps)
+
+    def launches():
+        return [(log[i].name.decode(), [p or 0 for p in log[i].ptr], list(log[i].val))
+                for i in range(n.value)]
+
+    # first-out: 9 pieces, the first of 32256 tokens, 7 of 28800, the last 28288
+    ws = ctypes.c_size_t(0)
+    assert lib.kda_chunk_fwd_workspace_size(1, T, H, 128, 128, 1, 64, 1, ctypes.byref(ws)) == 0
+    lib.kda_host_check_log_clear()
+    assert lib.kda_chunk_fwd(Q, K, V, 1, G, 2, None, -5.0, BETA, H0, None, 1, 1, T, H, 128, 128,
+                             64, 1.0, O, HT, WS, ws.value, None) == 0
+    got = launches()
+    off = _split_offsets(1, 9)
+    assert [g[0] for g in got] == ["split_tables", "chunk_pipe", "chunk_split_pass", "compose",
+                                   "chunk_pipe"]
+    assert got[0][1][:6] == [WS, WS + off["first"], WS + off["middle"], WS + off["later"],
+                             WS + off["mapped"], 0]
+    assert got[0][2] == [1, 9, 32256, 28800]
+    # piece 0: q, h0 = the initial state of its sequence, hT = piece 1's entry, o
+    assert got[1][1] == [Q, H0, WS + off["starts"] + piece, 0, O, WS + off["first"], WS, V]
+    assert got[1][2] == [1, 9, 0, 0]
+    # split pass over pieces 1..7: no q, no h0, no o
+    assert got[2][1] == [0, 0, WS + off["M"], WS + off["b"], 0, WS + off["middle"], WS, V]
+    assert got[2][2] == [7, 0, 0, 0]
+    # entries of pieces 2..8 from piece 1's, stride 9
+    assert got[3][1][:4] == [WS + off["M"] + piece, WS + off["b"] + piece,
+                             WS + off["starts"] + piece, WS + off["starts"] + piece]
+    assert got[3][2] == [1, 8, 9, 9]
+    # pieces 1..8 from their entries; the last writes the final state
+    assert got[4][1] == [Q, WS + off["starts"], HT, 0, O, WS + off["later"], WS, V]
+    assert got[4][2] == [8, 0, 9, 0]
+
+    # equal pieces (the explicit split, 8 segments)
+    assert lib.kda_chunk_fwd_split_workspace_size(1, T, H, 128, 128, 1, 8, 64, 1,
+                                                  ctypes.byref(ws)) == 0
+    lib.kda_host_check_log_clear()
+    assert lib.kda_chunk_fwd_split(Q, K, V, 1, G, 2, None, -5.0, BETA, H0, None, 1, 1, T, H, 128,
+                                   128, 64, 8, 1.0, O, HT, WS, ws.value, None) == 0
+    got = launches()
+    off = _split_offsets(1, 8)
+    assert [g[0] for g in got] == ["split_tables", "chunk_split_pass", "compose", "chunk_pipe"]
+    assert got[0][2] == [1, 8, 0, 0]
+    assert got[1][1] == [0, 0, WS + off["M"], WS + off["b"], 0, WS + off["mapped"], WS, V]
+    assert got[1][2] == [7, 0, 0, 0]
+    assert got[2][1][:4] == [WS + off["M"], WS + off["b"], H0, WS + off["starts"]]
+    assert got[2][2] == [1, 8, 8, 1]
+    assert got[3][1] == [Q, WS + off["starts"], HT, 0, O, 0, WS, V]
+    assert got[3][2] == [8, 0, 8, 0]

@@ -141,35 +141,78 @@ def test_packed_piece_table():
     assert rel_err(o, ref[0]) <= TOL_BF16
 
 
-def test_split_long256k_explicit_equals_automatic():
-    """The 256K-token single sequence at full size (32 heads), split into 8
-    segments explicitly, gives the same bits as kda_chunk_fwd's automatic
-    split (8 pieces of 32,768 tokens on a 256-CU device), whose every element
-    test_gpu_parity checks against the oracle."""
-    _print_case("split forward: long256k, explicit 8 segments vs automatic")
+def _first_out_plan(T, cus_per_unit, chunk=64):
+    """The piece table of the first-out split the library plans for one dense
+    sequence (its cost model: a split-pass token costs 1.12 forward tokens,
+    a composition step 30 tokens, the fork to the second stream and the
+    join back 200; middle pieces of a tokens, a first piece of about
+    1.12 a, both whole chunks, the last piece the rest), or None when it
+    plans equal pieces."""
+    P = min(cus_per_unit, T // 256, 64)
+    Lp = -(-(-(-T // P)) // chunk) * chunk
+    best, best_cost = None, 2.12 * Lp + 30 * (P - 1)
+    for Pf in range(3, cus_per_unit + 2):
+        if Pf - 1 > 64:
+            break
+        a = -(-int(T / ((Pf - 1) + 1.12)) // chunk) * chunk
+        L0 = int(1.12 * a) // chunk * chunk
+        last = T - L0 - (Pf - 2) * a
+        if last > a:
+            L0 += -(-(last - a) // chunk) * chunk
+            last = T - L0 - (Pf - 2) * a
+        if a < 256 or L0 < a or last <= 0:
+            continue
+        cost = max(L0, 1.12 * a) + a + 30 * (Pf - 2) + 200
+        if cost < best_cost:
+            best, best_cost = [0] + [L0 + p * a for p in range(Pf - 1)] + [T], cost
+    return best
+
+
+def test_split_long256k_schedules_agree():
+    """The 256K-token single sequence at full size (32 heads): kda_chunk_fwd's
+    automatic split (on a 256-CU device the first-out schedule, 9 pieces:
+    the first of 32,256 tokens run with output on the library's second
+    stream, 7 of 28,800, the last of 28,288) and the explicit 8-segment
+    split (equal pieces,
+    one stream) give the same bits. With this workload's gate every piece's
+    state map underflows to zero within a few tiles, so both equal the
+    unsplit chain; test_gpu_parity checks the automatic split's every
+    element against the oracle."""
+    _print_case("split forward: long256k, automatic (first-out) vs explicit 8 segments")
     from gated_delta_rule_92_amd import workspace_size
     d = make_workload("long256k", device="cuda")
-    ws = workspace_size(1, d["q"].shape[1], 32, 128, 128, 1, 64, torch.bfloat16)
+    T = d["q"].shape[1]
+    ws = workspace_size(1, T, 32, 128, 128, 1, 64, torch.bfloat16)
     wsp = torch.empty(ws, dtype=torch.uint8, device="cuda")
     o_a, h_a = chunk_fwd(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"], d["cu_seqlens"],
                          gate="logits", workspace=wsp)
     torch.cuda.synchronize()
-    Lp = int(wsp[4:8].view(torch.int32).item())
-    P = -(-d["q"].shape[1] // Lp)
-    print(f"  automatic split: P={P} Lp={Lp}", flush=True)
+    table = wsp[:4 * 10].view(torch.int32).cpu().tolist()
+    print(f"  automatic split: piece table {table}", flush=True)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        want = _first_out_plan(T, 8)
+        assert want == [0] + [32256 + p * 28800 for p in range(8)] + [T]
+        assert table == want
     o_e, h_e = chunk_fwd_split(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"],
-                               d["cu_seqlens"], segments=P, gate="logits")
+                               d["cu_seqlens"], segments=8, gate="logits")
     torch.cuda.synchronize()
     assert torch.equal(o_a, o_e) and torch.equal(h_a, h_e)
 
 
-def test_automatic_split_with_empty_trailing_pieces():
-    """B=1, H=16, T=4160: the automatic split takes P = 16 pieces of
-    Lp = 320 tokens, so pieces 13-15 are empty; every element against the
+@pytest.mark.parametrize("T,H,first_out,want", [
+    # equal pieces of 320 tokens: pieces 13-15 are empty
+    (4160, 16, False, [min(p * 320, 4160) for p in range(17)]),
+    # first-out: a first piece of 576 tokens with output on the second
+    # stream, 37 of 512 and a last one of 480
+    (20000, 2, True, [0] + [576 + p * 512 for p in range(38)] + [20000]),
+])
+def test_automatic_splits_with_ragged_and_empty_pieces(T, H, first_out, want):
+    """Dense B=1 with an initial state: kda_chunk_fwd's automatic split, its
+    piece table as planned on a 256-CU device, every element against the
     unsplit oracle."""
-    _print_case("automatic split, empty trailing pieces: B=1 H=16 T=4160")
+    _print_case(f"automatic split: B=1 H={H} T={T}")
     from gated_delta_rule_92_amd import workspace_size
-    B, T, H = 1, 4160, 16
+    B = 1
     d = make_inputs(B, T, H, 128, 128, torch.bfloat16, h0_std=0.02, seed=37)
     dd = to_dev(d)
     ws = workspace_size(B, T, H, 128, 128, B, 64, torch.bfloat16)
@@ -177,10 +220,11 @@ def test_automatic_split_with_empty_trailing_pieces():
     o, hT = chunk_fwd(dd["q"], dd["k"], dd["v"], dd["z"], dd["beta"], dd["h0"], gate="logits",
                       workspace=wsp)
     torch.cuda.synchronize()
-    table = wsp[:4 * 17].view(torch.int32).cpu().tolist()
+    table = wsp[:4 * len(want)].view(torch.int32).cpu().tolist()
     print(f"  piece table {table}", flush=True)
     if torch.cuda.get_device_properties(0).multi_processor_count == 256:
-        assert table == [min(p * 320, T) for p in range(17)]
+        assert _first_out_plan(T, 256 // H) == (want if first_out else None)
+        assert table == want
     ref = oracle_forward(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"], None, None, -5.0)
     eo, es = rel_err(o, ref[0]), rel_err(hT, ref[1])
     print(f"  err_o={eo:.3e} err_state={es:.3e} tol={TOL_BF16:g}", flush=True)
@@ -216,27 +260,34 @@ def test_chunk_fwd_splits_long_dense_sequences_by_itself():
         eo, es = rel_err(o, ref[0]), rel_err(hT, ref[1])
         print(f"  {name}: err_o={eo:.3e} err_state={es:.3e} tol={TOL_BF16:g}", flush=True)
         assert eo <= TOL_BF16 and es <= TOL_BF16
-    # the split ran: its piece table 0, Lp, 2 Lp, ..., T opens the workspace,
-    # and the workspace holds P pieces' maps and states
-    table = wsp[:4 * 65].view(torch.int32).cpu().tolist()
-    Lp = table[1]
-    P = -(-T // Lp)
-    print(f"  pieces: P={P} Lp={Lp}", flush=True)
-    assert 4 <= P <= 64 and Lp % 64 == 0
-    assert table[:P + 1] == [min(p * Lp, T) for p in range(P + 1)]
-    assert ws == -(-4 * (P + 1) // 256) * 256 + 3 * P * H * 128 * 128 * 4
+    # the split ran: its piece table opens the workspace (on a 256-CU device
+    # the first-out schedule: 32 pieces of 512 tokens)
+    table = wsp[:4 * 66].view(torch.int32).cpu().tolist()
+    P = table.index(T)
+    print(f"  pieces: P={P} table {table[:P + 1]}", flush=True)
+    assert table[0] == 0 and 4 <= P <= 65
+    assert all(0 < b - a and a % 64 == 0 for a, b in zip(table[:P], table[1:P + 1]))
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        want = _first_out_plan(T, 128)
+        assert want == [p * 512 for p in range(33)]
+        assert table[:P + 1] == want
     # With this gate a piece's state map underflows to zero within a few
     # tiles, so every piece starts from exactly the state the unsplit chain
     # has there and both paths give the same bits.
     assert torch.equal(o_split, o_one)
 
 
-def test_split_with_slowly_decaying_state():
+@pytest.mark.parametrize("T", [4096, 16384])
+def test_split_with_slowly_decaying_state(T):
     """A gate near zero keeps the state alive across every piece, so the
     entry states come from the composed maps, not from underflow: the split
-    (explicit and automatic) against the unsplit oracle."""
-    _print_case("split, slow decay: dense B=1 H=2 T=4096, P = 8 and automatic")
-    B, T, H = 1, 4096, 2
+    (explicit and automatic) against the unsplit oracle. On a 256-CU device
+    the automatic split of T = 4096 has 16 equal pieces, that of T = 16384
+    is first-out (32 pieces of 512, the first with output on the second
+    stream and the entry states of the others chained from its final
+    state)."""
+    _print_case(f"split, slow decay: dense B=1 H=2 T={T}, P = 8 and automatic")
+    B, H = 1, 2
     d = make_inputs(B, T, H, 128, 128, torch.bfloat16, h0_std=0.02, seed=35)
     g = (-0.002 * torch.sigmoid(d["z"])).contiguous()  # per-token log-decay in [-0.002, 0]
     dd = to_dev(d)

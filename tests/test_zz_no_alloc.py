@@ -2,9 +2,11 @@
 workspace is the library's static device scratch) against kda_chunk_fwd with
 a workspace of the size the query asks for, called through the C ABI, on
 consecutive calls with shrinking inputs, so the second call sees the first
-call's leftovers in the shared scratch. The two must give the same bits
-(same kernels, same context-split decision), and both must meet the oracle's
-bar."""
+call's leftovers in the shared scratch. Both must meet the oracle's bar and
+agree with each other to it: where kda_chunk_fwd splits with its first piece
+on a second stream, kda_chunk_fwd_noalloc (which creates no stream) takes the
+equal-piece split, whose rounding may differ; elsewhere they run the same
+kernels and give the same bits."""
 import ctypes
 
 import pytest
@@ -52,11 +54,16 @@ def test_noalloc_matches_chunk_fwd_on_consecutive_calls():
         o_ref, hT_ref = chunk_fwd(dd["q"], dd["k"], dd["v"], dd["z"], dd["beta"], dd["h0"],
                                   dd["cu_seqlens"], gate="logits")
         torch.cuda.synchronize()
-        assert torch.equal(o, o_ref) and torch.equal(hT, hT_ref)
+        same = torch.equal(o, o_ref) and torch.equal(hT, hT_ref)
+        do, ds = rel_err(o, o_ref.double().cpu()), rel_err(hT, hT_ref.double().cpu())
         ref = oracle_forward(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"], d["cu_seqlens"],
                              None, -5.0)
         eo, es = rel_err(o, ref[0]), rel_err(hT, ref[1])
-        print(f"  equal to kda_chunk_fwd; err_o={eo:.3e} err_state={es:.3e}", flush=True)
+        print(f"  vs kda_chunk_fwd: same bits {same}, o {do:.3e}, state {ds:.3e}; "
+              f"vs oracle: err_o={eo:.3e} err_state={es:.3e}", flush=True)
+        assert do <= TOL_BF16 and ds <= TOL_BF16
+        if lengths is not None:  # packed sequences: no split, the same kernels
+            assert same
         assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
