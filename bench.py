@@ -632,12 +632,17 @@ def main(argv=None):
     log(f"bench: {args.steps} steps, wall {ms_per_step:.3f} ms/step, event {kernel_ms:.3f} ms/launch")
 
     # pieces of the context split kda_chunk_fwd took by itself for long dense
-    # sequences (its workspace then opens with the piece table 0, Lp, 2 Lp ...)
-    segments = args.split
-    if args.split == 1 and args.epilogue == "none" and d["cu_seqlens"] is None and ws >= 256:
-        lp = int(workspace[4:8].view(torch.int32).item())
-        if lp > 0:
-            segments = -(-w.T // lp)
+    # sequences (its workspace then opens with the piece table: the starts of
+    # the first sequence's pieces, the first piece ending at T closing it)
+    segments, piece_tokens = args.split, None
+    if args.split == 1 and args.epilogue == "none" and d["cu_seqlens"] is None and ws >= 4 * 66:
+        table = workspace[:4 * 66].view(torch.int32).cpu().tolist()
+        if table[0] == 0 and 0 < table[1] <= w.T and w.T in table[1:]:
+            segments = table[1:].index(w.T) + 1
+            if segments > 1:
+                # first, second and last piece (the first-out schedule's first
+                # piece is longer, the last takes the rest)
+                piece_tokens = [table[1], table[2] - table[1], w.T - table[segments - 1]]
     tok_heads = n_tokens * w.H
     value = tok_heads / (ms_per_step / 1e3)
     bytes_alg = algorithmic_bytes(w, n_tokens, N * w.H, d["h0"] is not None)
@@ -677,7 +682,8 @@ def main(argv=None):
         "config": {"workload": w.name, "batch": int(d["q"].shape[0]), "seq_len": w.T, "heads": w.H,
                    "d_k": w.Dk, "d_v": w.Dv, "chunk": w.chunk, "gate": args.gate,
                    "g_min": w.g_min, "initial_state": d["h0"] is not None,
-                   "sequences": N, "segments": segments, "epilogue": args.epilogue},
+                   "sequences": N, "segments": segments, "epilogue": args.epilogue,
+                   **({"piece_tokens": piece_tokens} if piece_tokens else {})},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "mfma_peak_frac": chunk_form_flops(w, n_tokens) / (kernel_ms / 1e3) / (peak_tf * 1e12),
