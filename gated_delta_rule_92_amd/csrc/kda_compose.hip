@@ -74,25 +74,45 @@ __global__ void __launch_bounds__(kComposeThreads) compose_kernel(const float* _
   }
 }
 
-// Dk = 128 on fp32 matrix cores: a workgroup of 8 wavefronts per (sequence,
-// head, 16 value columns); wavefront w forms rows [16w, 16w + 16) of each next
-// entry state, start_{p+1} = M_p start_p + b_p, as 32 16x16x4 products in
-// four independent accumulation chains (one per e below), b_p starting the
-// first. The contraction index is taken as k = 16 i + 4 g + e (g = lane / 16;
-// i, e the product's step), so that the four lanes of a row read 64
-// consecutive bytes of M_p per 16-byte load (eight loads per lane, issued one
-// step ahead; 16 cache lines per load instead of the 64 that a lane reading
-// its own 128-byte segment touches) and the matching entries of their column
-// of the running slice. The slice is kept transposed and double-buffered in
-// LDS, so one barrier per step suffices. The lane's four entries of b_p are
-// loaded one step ahead as well.
+// Dk = 128 on fp32 matrix cores: a workgroup of 8 compute wavefronts per
+// (sequence, head, 16 value columns); wavefront w forms rows [16w, 16w + 16)
+// of each next entry state, start_{p+1} = M_p start_p + b_p, as 32 16x16x4
+// products in four independent accumulation chains (one per e below), b_p
+// starting the first. The contraction index is taken as k = 16 i + 4 g + e
+// (g = lane / 16; i, e the product's step), so that the four lanes of a row
+// read 64 consecutive bytes of M_p per 16-byte load (eight loads per lane; 16
+// cache lines per load instead of the 64 that a lane reading its own
+// 128-byte segment touches) and the matching entries of their column of the
+// running slice. The slice is kept transposed and double-buffered in LDS, so
+// one barrier per step suffices, and that barrier orders LDS only.
+//
+// The steps are a dependent chain of short matrix products, so what a step
+// waits on sets the pace. M_p and b_p are loaded two steps ahead into one of
+// three register sets used in turn, with no branch around the loads and no
+// copy between sets (either made the compiler wait for every outstanding
+// load, the prefetch included, at each step). A ninth wavefront writes the
+// entry states from LDS to memory, one step behind the compute wavefronts,
+// which therefore never store (a compute wavefront's stores made its next
+// prefetch wait for them).
 constexpr int kC128 = 128;
 constexpr int kCT = kC128 + 4;  // padded row of the transposed slice
+constexpr int kComposeComputeWaves = kC128 / 16;
+constexpr int kCompose128Threads = 64 * (kComposeComputeWaves + 1);
 
-__global__ void __launch_bounds__(512) compose128_kernel(const float* __restrict__ M,
-                                                         const float* __restrict__ b,
-                                                         const float* S0, int s0_stride, int P,
-                                                         int stride, int H, int Dv, float* starts) {
+struct ComposeSet {
+  f32x4 m[8];  // row row0 + n of M_p, entries 16i + 4g .. 16i + 4g + 3
+  f32x4 b;     // entries (row0 + 4g + e, c0 + n) of b_p
+};
+
+__device__ __forceinline__ void compose_lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__global__ void __launch_bounds__(kCompose128Threads) compose128_kernel(
+    const float* __restrict__ M, const float* __restrict__ b, const float* S0, int s0_stride, int P,
+    int stride, int H, int Dv, float* starts) {
   // ping-pong: step p reads slice p & 1 and writes slice (p + 1) & 1
   __shared__ __attribute__((aligned(16))) float curT2[2][kComposeCols][kCT];
   const int sh = blockIdx.x;  // sequence * H + head
@@ -100,67 +120,90 @@ __global__ void __launch_bounds__(512) compose128_kernel(const float* __restrict
   const int c0 = blockIdx.y * kComposeCols;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15, g = lane >> 4;
-  const int row0 = 16 * w;
-  const bool cvalid = c0 + n < Dv;
 
-  for (int i = tid; i < kComposeCols * kC128; i += 512) {
+  for (int i = tid; i < kComposeCols * kC128; i += kCompose128Threads) {
     const int col = i % kComposeCols, row = i / kComposeCols;
     curT2[0][col][row] = (S0 && c0 + col < Dv)
                              ? S0[(((size_t)seq * s0_stride * H + h) * kC128 + row) * Dv + c0 + col]
                              : 0.f;
   }
-  // row row0 + n of M_p, entries 16i + 4g .. 16i + 4g + 3 for i = 0..7
-  auto load_m = [&](int p, f32x4 (&a)[8]) {
-    const float* Mp = M + (((size_t)seq * stride + p) * H + h) * (size_t)kC128 * kC128 +
-                      (size_t)(row0 + n) * kC128 + 4 * g;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const f32x4*>(Mp + 16 * i);
-  };
-  // entries (row0 + 4g + e, c0 + n) of b_p
-  auto load_b = [&](int p, f32x4& v) {
-    const float* bp = b + (((size_t)seq * stride + p) * H + h) * (size_t)kC128 * Dv;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = cvalid ? bp[(size_t)(row0 + 4 * g + e) * Dv + c0 + n] : 0.f;
-  };
-  f32x4 am[8], bv = {0.f, 0.f, 0.f, 0.f};
-  if (P > 1) {
-    load_m(0, am);
-    load_b(0, bv);
-  }
-  __syncthreads();
+  compose_lds_barrier();  // the entry state is in slice 0
 
-  for (int p = 0; p < P; ++p) {
-    float (*curT)[kCT] = curT2[p & 1];
-    float (*nxtT)[kCT] = curT2[(p + 1) & 1];
-    const size_t sp = (size_t)seq * stride + p;
-    float* out = starts + (sp * H + h) * (size_t)kC128 * Dv;
-    if (cvalid) {
+  if (w == kComposeComputeWaves) {
+    // the store wavefront: entry p after the barrier that ends step p - 1 (it
+    // takes part in every barrier of the compute wavefronts); lane l writes
+    // 16-byte pieces of rows, row r = (l / 4) + 16 j, columns 4 (l % 4) ..
+    const int cq = lane & 3, rq = lane >> 2;
+    const bool cv = c0 + 4 * cq + 3 < Dv;
+    for (int p = 0; p < P; ++p) {
+      if (p > 0) compose_lds_barrier();
+      const float (*curT)[kCT] = curT2[p & 1];
+      float* out = starts + (((size_t)seq * stride + p) * H + h) * (size_t)kC128 * Dv;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) out[(size_t)(row0 + 4 * g + e) * Dv + c0 + n] = curT[n][row0 + 4 * g + e];
+      for (int j = 0; j < kC128 / 16; ++j) {
+        const int row = rq + 16 * j;
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = curT[4 * cq + e][row];
+        if (cv) {
+          *reinterpret_cast<f32x4*>(out + (size_t)row * Dv + c0 + 4 * cq) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c0 + 4 * cq + e < Dv) out[(size_t)row * Dv + c0 + 4 * cq + e] = v[e];
+        }
+      }
     }
-    if (p == P - 1) break;
-    // four independent accumulation chains, one per e
-    f32x4 acc[4] = {bv, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    return;
+  }
+
+  const int n = lane & 15, g = lane >> 4;
+  const int row0 = 16 * w;
+  // M_p and b_p of step p into a register set. The loads are unconditional:
+  // p past the last step re-reads step P - 2, and a column past Dv reads
+  // column c0. A column of the products depends only on that column of the
+  // slice and of b, so such a column computes values that are never stored.
+  const int bcol = c0 + n < Dv ? c0 + n : c0;
+  auto load = [&](int p, ComposeSet& x) {
+    const size_t sp = (size_t)seq * stride + min(p, P - 2);
+    const float* Mp = M + (sp * H + h) * (size_t)kC128 * kC128 + (size_t)(row0 + n) * kC128 + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x.m[i] = *reinterpret_cast<const f32x4*>(Mp + 16 * i);
+    const float* bp = b + (sp * H + h) * (size_t)kC128 * Dv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x.b[e] = bp[(size_t)(row0 + 4 * g + e) * Dv + bcol];
+  };
+  ComposeSet set0, set1, set2;
+  if (P > 1) {
+    load(0, set0);
+    load(1, set1);
+  }
+  // step p: prefetch M, b of step p + 2 into `pre`, then
+  // start_{p+1} = M_p start_p + b_p from `cur`
+  auto step = [&](int p, const ComposeSet& cur, ComposeSet& pre) {
+    load(p + 2, pre);
+    const float (*curT)[kCT] = curT2[p & 1];
+    float (*nxtT)[kCT] = curT2[(p + 1) & 1];
     f32x4 bc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) bc[i] = *reinterpret_cast<const f32x4*>(&curT[n][16 * i + 4 * g]);
-    f32x4 an[8];
-    if (p + 1 < P - 1) {
-      load_m(p + 1, an);
-      load_b(p + 1, bv);
-    }
+    f32x4 acc[4] = {cur.b, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[i][e], bc[i][e], acc[e], 0, 0, 0);
+      for (int e = 0; e < 4; ++e)
+        acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.m[i][e], bc[i][e], acc[e], 0, 0, 0);
     const f32x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    // the other slice was last read in step p - 1, before that step's barrier
+    // the other slice was last read in step p - 1 (and by the store
+    // wavefront before that step's barrier)
 #pragma unroll
     for (int e = 0; e < 4; ++e) nxtT[n][row0 + 4 * g + e] = sum[e];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) am[i] = an[i];
-    __syncthreads();
+    compose_lds_barrier();
+  };
+  for (int p = 0; p + 1 < P; p += 3) {
+    step(p, set0, set2);
+    if (p + 2 < P) step(p + 1, set1, set0);
+    if (p + 3 < P) step(p + 2, set2, set1);
   }
 }
 
@@ -212,8 +255,8 @@ hipError_t launch_compose(const float* M, const float* b, const float* S0, int s
   if (Dk > kComposeMaxDk) return hipErrorInvalidValue;
   dim3 grid((unsigned)(nseq * H), (unsigned)((Dv + kComposeCols - 1) / kComposeCols));
   if (Dk == kC128) {
-    hipLaunchKernelGGL(compose128_kernel, grid, dim3(512), 0, stream, M, b, S0, s0_stride, P,
-                       stride, H, Dv, starts);
+    hipLaunchKernelGGL(compose128_kernel, grid, dim3(kCompose128Threads), 0, stream, M, b, S0,
+                       s0_stride, P, stride, H, Dv, starts);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(compose_kernel, grid, dim3(kComposeThreads), 0, stream, M, b, S0, s0_stride, P,
