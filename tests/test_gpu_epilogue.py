@@ -42,6 +42,10 @@ CASES = [
     ("bf16 d=128 dense, weight", torch.bfloat16, 128, 128, dict(B=2, T=300, lengths=None), True),
     ("bf16 d=128 dense 4096 tokens, weight (context split taken by itself)", torch.bfloat16, 128,
      128, dict(B=1, T=4096, lengths=None), True),
+    # the first-out split: the first piece's epilogue runs on the library's
+    # second stream
+    ("bf16 d=128 dense 20000 tokens, weight (first-out context split)", torch.bfloat16, 128,
+     128, dict(B=1, T=20000, lengths=None), True),
     ("bf16 d=128 varlen, no weight", torch.bfloat16, 128, 128,
      dict(B=1, T=0, lengths=[0, 1, 63, 64, 65, 130, 16]), False),
     ("bf16 d=64 (tile kernel + epilogue)", torch.bfloat16, 64, 64, dict(B=2, T=200, lengths=None), True),

@@ -231,6 +231,35 @@ def test_automatic_splits_with_ragged_and_empty_pieces(T, H, first_out, want):
     assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
+@pytest.mark.parametrize("mode", ["cumsum", "logdecay"])
+def test_first_out_split_with_precomputed_gates(mode):
+    """The first-out automatic split (B=1, H=2, T=20000 with an initial
+    state; on a 256-CU device a first piece of 576 tokens, then 37 of 512
+    and 480) fed the gate as per-token log-decay or as its cumulative sum
+    within 64-token chunks (kda_gate's output): every piece starts on a chunk
+    boundary, so each piece's tiles rebase the chunk-local sums correctly.
+    Every element against the unsplit oracle."""
+    _print_case(f"first-out split, gate input {mode}: B=1 H=2 T=20000")
+    from gated_delta_rule_92_amd import workspace_size
+    B, T, H = 1, 20000, 2
+    d = make_inputs(B, T, H, 128, 128, torch.bfloat16, h0_std=0.02, seed=38)
+    dd = to_dev(d)
+    g = gate(dd["z"], None, -5.0, 64 if mode == "cumsum" else 0, None)
+    ws = workspace_size(B, T, H, 128, 128, B, 64, torch.bfloat16)
+    wsp = torch.zeros(ws, dtype=torch.uint8, device="cuda")
+    o, hT = chunk_fwd(dd["q"], dd["k"], dd["v"], g, dd["beta"], dd["h0"], gate=mode,
+                      workspace=wsp)
+    torch.cuda.synchronize()
+    table = wsp[:4 * 40].view(torch.int32).cpu().tolist()
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert table == [0] + [576 + p * 512 for p in range(38)] + [T]
+    assert all(t % 64 == 0 for t in table[:-1])
+    ref = oracle_forward(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"], None, None, -5.0)
+    eo, es = rel_err(o, ref[0]), rel_err(hT, ref[1])
+    print(f"  err_o={eo:.3e} err_state={es:.3e} tol={TOL_BF16:g}", flush=True)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
 def test_chunk_fwd_splits_long_dense_sequences_by_itself():
     """kda_chunk_fwd on a long dense sequence with few (sequence, head) units
     takes the context split when its workspace holds it (the size query asks
