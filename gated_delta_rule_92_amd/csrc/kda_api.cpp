@@ -464,6 +464,12 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
     if (split.P > 1 && (!workspace || workspace_bytes < split.bytes))
       return KDA_ERROR_INSUFFICIENT_WORKSPACE;
   } else if (!cu_seqlens && o && fused && !softplus && workspace) {
+    // a stream being captured into a graph keeps the one-stream schedule
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (first_out_ok &&
+        (hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cap) != hipSuccess ||
+         cap != hipStreamCaptureStatusNone))
+      first_out_ok = false;
     split = auto_split(B, T, H, Dk, Dv, chunk, dtype, first_out_ok);
     if (workspace_bytes < split.bytes) split = SplitPlan{};
   }

@@ -167,7 +167,8 @@ kda_status_t kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, i
  * back into `stream` with events, so the call stays ordered on `stream`)
  * while the state maps of the middle pieces are formed (its length chosen
  * so that both end together); the other pieces then run from entry states
- * chained from its final state.
+ * chained from its final state. A stream that is being captured into a
+ * graph gets the equal pieces.
  * Supported: bf16 with Dk, Dv in {64, 128}; fp32 with Dk = Dv = 64 on the
  * matrix-core chunk path; any other Dk, Dv <= 256 (and fp32 at 128) runs a
  * token-serial kernel with the same results, as does KDA_GATE_LOGITS with

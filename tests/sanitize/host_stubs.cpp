@@ -86,6 +86,11 @@ hipError_t hipEventRecord(hipEvent_t event, hipStream_t) {
 hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t event, unsigned int) {
   return event ? hipSuccess : hipErrorInvalidValue;
 }
+hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus* status) {
+  if (!status) return hipErrorInvalidValue;
+  *status = hipStreamCaptureStatusNone;
+  return hipSuccess;
+}
 
 hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t attr, int device) {
   if (!value || device != 0) return hipErrorInvalidValue;

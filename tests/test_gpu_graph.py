@@ -1,0 +1,78 @@
+"""The chunk forward captured into a HIP graph (torch.cuda.graph) and replayed.
+
+Two calls are captured: a long dense sequence with few (sequence, head) units,
+whose automatic context split kda_chunk_fwd takes by itself (on a stream that
+is being captured it keeps the one-stream schedule, equal pieces, where eager
+calls of this shape run the first piece on the library's second stream), and
+a packed batch whose longest-first order is computed into the workspace. The
+graph is replayed three times with eager work and synchronisations between the
+replays, and every replay is checked: against the oracle at the forward's
+tolerance, and against the eager call of the same inputs.
+"""
+import pytest
+import torch
+
+from gated_delta_rule_92_amd import chunk_fwd, workspace_size
+from gated_delta_rule_92_amd.inputs import make_inputs
+from oracle import oracle_forward
+from tests.gpu_helpers import TOL_BF16, rel_err, to_dev
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+CASES = [
+    ("dense B=1 H=2 T=20000 (automatic context split)", dict(B=1, T=20000, lengths=None)),
+    ("packed 6 sequences H=2 (longest-first order)",
+     dict(B=1, T=0, lengths=[700, 0, 33, 1290, 64, 517])),
+]
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
+def test_captured_forward_replays(name, kw):
+    print(f"\n[case] graph capture: {name}", flush=True)
+    H = 2
+    d = make_inputs(kw["B"], kw["T"], H, 128, 128, torch.bfloat16, h0_std=0.02,
+                    lengths=kw["lengths"], seed=51)
+    dd = to_dev(d)
+    B, T = d["q"].shape[0], d["q"].shape[1]
+    N = B if d["cu_seqlens"] is None else d["cu_seqlens"].numel() - 1
+    ws = workspace_size(B, T, H, 128, 128, N, 64, torch.bfloat16)
+    wsp = torch.zeros(max(ws, 1), dtype=torch.uint8, device="cuda")
+    o = torch.zeros_like(dd["v"])
+    hT = torch.zeros((N, H, 128, 128), dtype=torch.float32, device="cuda")
+
+    def call():
+        chunk_fwd(dd["q"], dd["k"], dd["v"], dd["z"], dd["beta"], dd["h0"], dd["cu_seqlens"],
+                  gate="logits", o=o, final_state=hT, workspace=wsp)
+
+    # eager reference (for the dense case: the first-out schedule)
+    o_eager, h_eager = chunk_fwd(dd["q"], dd["k"], dd["v"], dd["z"], dd["beta"], dd["h0"],
+                                 dd["cu_seqlens"], gate="logits")
+    # warm up on a side stream, then capture
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    ref = oracle_forward(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"], d["cu_seqlens"], None,
+                         -5.0)
+    for replay in range(3):
+        # eager work between replays: clobber the outputs and the workspace
+        o.fill_(float("nan"))
+        hT.fill_(float("nan"))
+        wsp.fill_(0xFF)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        eo, es = rel_err(o, ref[0]), rel_err(hT, ref[1])
+        do = rel_err(o, o_eager.double().cpu())
+        ds = rel_err(hT, h_eager.double().cpu())
+        print(f"  replay {replay}: vs oracle err_o={eo:.3e} err_state={es:.3e}; vs eager "
+              f"o {do:.3e} state {ds:.3e} (tol {TOL_BF16:g})", flush=True)
+        assert eo <= TOL_BF16 and es <= TOL_BF16
+        assert do <= TOL_BF16 and ds <= TOL_BF16
