@@ -521,10 +521,15 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
       z.order = order; z.seqs.N = count; z.hT = M; z.hT2 = bst;
       return kda::launch_chunk_split_pass(z, hs);
     };
+    // without the second stream (it could not be created) the pieces run as
+    // mapped below, which works for any piece table
+    std::unique_lock<std::mutex> lock(g_aux_mu, std::defer_lock);
+    AuxStream* aux = nullptr;
     if (split.first_out) {
-      std::lock_guard<std::mutex> lock(g_aux_mu);
-      AuxStream* aux = aux_stream_locked();
-      if (!aux) return KDA_ERROR_LAUNCH_FAILURE;
+      lock.lock();
+      aux = aux_stream_locked();
+    }
+    if (aux) {
       // piece 0 of every sequence from the initial state, with output, on
       // the second stream; its final state is piece 1's entry state
       kda::ChunkArgs f0 = with_output(a);
@@ -554,6 +559,7 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dty
       }
       return launch_status(e);
     }
+    if (lock.owns_lock()) lock.unlock();
     // mapped: the maps of every piece but each sequence's last, entry states
     // from the initial state, then every piece with output; each sequence's
     // last piece writes the sequence's final state

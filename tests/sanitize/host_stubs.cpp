@@ -38,10 +38,17 @@ int kda_host_check_build(void) { return 1; }
 // compute units hipDeviceGetAttribute reports (256, as on an MI355X)
 static int g_cus = 256;
 void kda_host_check_set_compute_units(int n) { g_cus = n; }
+// the device hipGetDevice reports (0), and whether hipStreamCreateWithFlags
+// fails (to exercise the split's fallback when its second stream cannot be
+// created; the library keeps one such stream per device)
+static int g_device = 0;
+static int g_fail_streams = 0;
+void kda_host_check_set_device(int d) { g_device = d; }
+void kda_host_check_fail_streams(int fail) { g_fail_streams = fail; }
 
 hipError_t hipGetDevice(int* device) {
   if (!device) return hipErrorInvalidValue;
-  *device = 0;
+  *device = g_device;
   return hipSuccess;
 }
 
@@ -72,6 +79,7 @@ static char g_handles[3];
 static int g_next_handle = 0;
 hipError_t hipStreamCreateWithFlags(hipStream_t* stream, unsigned int) {
   if (!stream) return hipErrorInvalidValue;
+  if (g_fail_streams) return hipErrorOutOfMemory;
   *stream = reinterpret_cast<hipStream_t>(&g_handles[g_next_handle++ % 3]);
   return hipSuccess;
 }
@@ -93,7 +101,7 @@ hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus* status) {
 }
 
 hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t attr, int device) {
-  if (!value || device != 0) return hipErrorInvalidValue;
+  if (!value || device < 0 || device >= 64) return hipErrorInvalidValue;
   *value = attr == hipDeviceAttributeMultiprocessorCount ? g_cus : 0;
   return hipSuccess;
 }

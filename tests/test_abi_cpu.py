@@ -410,3 +410,44 @@ def test_split_schedules_launch_what_they_should():
     assert got[2][2] == [1, 8, 8, 1]
     assert got[3][1] == [Q, WS + off["starts"], HT, 0, O, 0, WS, V]
     assert got[3][2] == [8, 0, 8, 0]
+
+
+def test_split_without_a_second_stream_runs_every_piece_mapped():
+    """Only in the host-check build: when the second stream cannot be created
+    (the stub device 3 refuses streams), a first-out plan runs as the
+    equal-piece schedule does, over the same piece table: the split pass maps
+    every piece but the last, the entries are chained from the initial state
+    and every piece runs with output."""
+    lib = _lib.load()
+    if not hasattr(lib, "kda_host_check_build"):
+        pytest.skip("needs the host-check build (tests/test_sanitizers_cpu.py)")
+    for f in ("kda_host_check_set_compute_units", "kda_host_check_set_device",
+              "kda_host_check_fail_streams"):
+        getattr(lib, f).argtypes = [ctypes.c_int]
+    log = (_Launch * 64).in_dll(lib, "kda_host_check_log")
+    n = ctypes.c_int.in_dll(lib, "kda_host_check_log_len")
+    T, H = 262144, 32
+    Q, K, V, G, BETA, H0, O, HT, WS = (FAKE * (i + 1) for i in range(9))
+    ws = ctypes.c_size_t(0)
+    try:
+        lib.kda_host_check_set_compute_units(256)
+        lib.kda_host_check_set_device(3)
+        lib.kda_host_check_fail_streams(1)
+        assert lib.kda_chunk_fwd_workspace_size(1, T, H, 128, 128, 1, 64, 1, ctypes.byref(ws)) == 0
+        lib.kda_host_check_log_clear()
+        assert lib.kda_chunk_fwd(Q, K, V, 1, G, 2, None, -5.0, BETA, H0, None, 1, 1, T, H, 128, 128,
+                                 64, 1.0, O, HT, WS, ws.value, None) == 0
+        got = [(log[i].name.decode(), [p or 0 for p in log[i].ptr], list(log[i].val))
+               for i in range(n.value)]
+    finally:
+        lib.kda_host_check_fail_streams(0)
+        lib.kda_host_check_set_device(0)
+    off = _split_offsets(1, 9)
+    assert [g[0] for g in got] == ["split_tables", "chunk_split_pass", "compose", "chunk_pipe"]
+    assert got[0][2] == [1, 9, 32256, 28800]   # the first-out piece table
+    assert got[1][1] == [0, 0, WS + off["M"], WS + off["b"], 0, WS + off["mapped"], WS, V]
+    assert got[1][2] == [8, 0, 0, 0]
+    assert got[2][1][:4] == [WS + off["M"], WS + off["b"], H0, WS + off["starts"]]
+    assert got[2][2] == [1, 9, 9, 1]
+    assert got[3][1] == [Q, WS + off["starts"], HT, 0, O, 0, WS, V]
+    assert got[3][2] == [9, 0, 9, 0]
