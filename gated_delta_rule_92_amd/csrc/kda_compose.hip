@@ -182,6 +182,9 @@ __global__ void __launch_bounds__(kCompose128Threads) compose128_kernel(
   // start_{p+1} = M_p start_p + b_p from `cur`
   auto step = [&](int p, const ComposeSet& cur, ComposeSet& pre) {
     load(p + 2, pre);
+    // keep the prefetch at the top of the step: left to itself the scheduler
+    // sinks it below the products, a step later than intended
+    __builtin_amdgcn_sched_barrier(0);
     const float (*curT)[kCT] = curT2[p & 1];
     float (*nxtT)[kCT] = curT2[(p + 1) & 1];
     f32x4 bc[8];
