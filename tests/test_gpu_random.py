@@ -3,9 +3,10 @@
 a fixed seed: dense or packed sequences (0 to 300 tokens, empty ones
 included), 1 to 3 heads, d_k and d_v in {64, 128} independently, bf16 or fp32,
 gate logits or per-token log-decay, with or without an initial state and a
-final-state gradient, output scale in [0.5, 1.5]. The same bar as the other
-parity tests: max|gpu - ref| / max|ref| <= 2e-2 (bf16) and 1e-4 (fp32) per
-output array.
+final-state gradient, output scale in [0.5, 1.5]. A second sweep draws long
+dense problems that kda_chunk_fwd runs as a context split. The same bar as
+the other parity tests: max|gpu - ref| / max|ref| <= 2e-2 (bf16) and 1e-4
+(fp32) per output array.
 """
 import numpy as np
 import pytest
@@ -90,3 +91,54 @@ def test_random_problem_forward_and_backward(seed):
     for n, e in errs.items():
         assert np.all(np.isfinite(got[n].double().cpu().numpy())), n
         assert e <= tol, (n, e)
+
+
+def _split_problem(seed):
+    """A dense bf16 d = 128 problem long enough, with few enough heads, that
+    kda_chunk_fwd splits it by itself (P = CUs / (B H) >= 4 pieces and
+    T (0.9 - 3/P) > 300): on a 256-CU device 1 to 2 sequences of 2,000 to
+    24,000 tokens with 1 to 8 heads; gate logits, per-token log-decay or its
+    cumulative sum within 64-token chunks."""
+    rng = np.random.default_rng(5000 + seed)
+    B = int(rng.integers(1, 3))
+    H = int(rng.choice([1, 2, 4, 8]))
+    T = int(rng.integers(2000, 24001))
+    return dict(B=B, H=H, T=T, gate=str(rng.choice(["logits", "logdecay", "cumsum"])),
+                h0=bool(rng.random() < 0.7), scale=float(np.round(rng.uniform(0.5, 1.5), 3)))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_automatic_split(seed):
+    """kda_chunk_fwd on random long dense problems that take the automatic
+    context split (equal pieces or first-out, as the cost model picks), every
+    element against the unsplit oracle; the piece table is checked to start
+    every piece on a 64-token chunk boundary and to end at T."""
+    from gated_delta_rule_92_amd import gate as gate_fn
+    from gated_delta_rule_92_amd import workspace_size
+    s = _split_problem(seed)
+    print(f"\n[case] random split {seed}: B={s['B']} H={s['H']} T={s['T']} gate={s['gate']} "
+          f"h0={s['h0']} scale={s['scale']}", flush=True)
+    d = make_inputs(s["B"], s["T"], s["H"], 128, 128, torch.bfloat16,
+                    h0_std=0.02 if s["h0"] else 0.0, seed=6000 + seed)
+    dd = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    if s["gate"] == "logits":
+        g = dd["z"]
+    else:
+        g = gate_fn(dd["z"], None, -5.0, 64 if s["gate"] == "cumsum" else 0, None)
+    ws = workspace_size(s["B"], s["T"], s["H"], 128, 128, s["B"], 64, torch.bfloat16)
+    wsp = torch.zeros(max(ws, 1), dtype=torch.uint8, device="cuda")
+    o, hT = chunk_fwd(dd["q"], dd["k"], dd["v"], g, dd["beta"], dd["h0"], gate=s["gate"],
+                      scale=s["scale"], workspace=wsp)
+    torch.cuda.synchronize()
+    if ws >= 4 * 2:
+        table = wsp[:4 * 66].view(torch.int32).cpu().tolist()
+        if table[0] == 0 and s["T"] in table[1:]:
+            P = table[1:].index(s["T"]) + 1
+            print(f"  pieces: {P}, first {table[1]}, second {table[2] - table[1] if P > 1 else 0}",
+                  flush=True)
+            assert all(t % 64 == 0 for t in table[:P])
+    ro, rs = oracle_forward(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"], None, None, -5.0,
+                            s["scale"])
+    eo, es = rel_err(o, ro), rel_err(hT, rs)
+    print(f"  err_o={eo:.2e} err_state={es:.2e}", flush=True)
+    assert eo <= 2e-2 and es <= 2e-2
