@@ -330,3 +330,32 @@ def test_split_with_slowly_decaying_state(T):
         eo, es = rel_err(o, ref[0]), rel_err(hT, ref[1])
         print(f"  {name}: err_o={eo:.3e} err_state={es:.3e} tol={TOL_BF16:g}", flush=True)
         assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+@pytest.mark.parametrize("T", [4096, 20000])
+@pytest.mark.parametrize("stress", ["g_min_everywhere", "g_zero", "beta_one", "large_values"])
+def test_automatic_split_under_numeric_stress(T, stress):
+    """Extreme inputs through kda_chunk_fwd's automatic split (dense B=1, H=2,
+    initial state; on a 256-CU device T = 4096 takes 16 equal pieces and
+    T = 20000 the first-out schedule): the gate at its lower bound on every
+    token (largest in-tile reciprocals), no decay at all (every piece's state
+    map stays a product of (I - beta k k^T), so each entry state depends on
+    the whole history through the composition), every token fully written,
+    and values 100 times larger. Every element against the unsplit oracle."""
+    _print_case(f"automatic split under stress {stress}: B=1 H=2 T={T}")
+    d = make_inputs(1, T, 2, 128, 128, torch.bfloat16, h0_std=0.02, seed=39)
+    if stress == "g_min_everywhere":
+        d["z"] = torch.full_like(d["z"], 40.0)        # sigmoid -> 1, g = g_min
+    elif stress == "g_zero":
+        d["z"] = torch.full_like(d["z"], -200.0)      # sigmoid -> 0, g = 0
+    elif stress == "beta_one":
+        d["beta"] = torch.ones_like(d["beta"])
+    elif stress == "large_values":
+        d["v"] = (d["v"].float() * 100).to(torch.bfloat16)
+    dd = to_dev(d)
+    o, hT = chunk_fwd(dd["q"], dd["k"], dd["v"], dd["z"], dd["beta"], dd["h0"], gate="logits")
+    torch.cuda.synchronize()
+    ref = oracle_forward(d["q"], d["k"], d["v"], d["z"], d["beta"], d["h0"], None, None, -5.0)
+    eo, es = rel_err(o, ref[0]), rel_err(hT, ref[1])
+    print(f"  err_o={eo:.3e} err_state={es:.3e} tol={TOL_BF16:g}", flush=True)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
