@@ -70,8 +70,9 @@ def test_noalloc_matches_chunk_fwd_on_consecutive_calls():
 def test_automatic_splits_fit_the_scratch():
     """The workspace the size query asks for (what the no-allocation entry
     point takes from its scratch) fits the 64 MiB scratch for the automatic
-    splits of the 4096-token (16 pieces of 16 heads) and 256K-token (8 pieces
-    of 32 heads) single sequences on this device. (Sizes beyond the scratch
+    splits of the 4096-token (16 pieces of 16 heads) and 256K-token (8 equal
+    pieces for this entry point, 9 for kda_chunk_fwd's first-out schedule;
+    the query asks for the larger) single sequences on this device. (Sizes beyond the scratch
     are rejected before anything is enqueued; that path needs a device with
     more compute units and is exercised by the host-check build.)"""
     lib = _lib.load()
