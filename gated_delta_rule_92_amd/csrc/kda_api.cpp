@@ -765,7 +765,8 @@ kda_status_t kda_chunk_bwd(const void* q, const void* k, const void* v, kda_dtyp
   if (st != KDA_SUCCESS) return st;
   if (!workspace || workspace_bytes < need) return KDA_ERROR_INSUFFICIENT_WORKSPACE;
   const long slots = kda::chunk_bwd_slots(s, dtype == KDA_BFLOAT16);
-  if (slots > 0x7fffffffL || (long)s.N * H > 0x7fffffffL) return KDA_ERROR_NOT_SUPPORTED;
+  // the gradient kernel's grid has one workgroup per (checkpoint chunk, head)
+  if (slots * H > 0x7fffffffL || (long)s.N * H > 0x7fffffffL) return KDA_ERROR_NOT_SUPPORTED;
   if (s.N == 0) return KDA_SUCCESS;
   const size_t e = bwd_elt(dtype);
   const size_t ck = round_up((size_t)bwd_slots_bound(B, T, s.N, dtype) * H * Dk * Dv * e, kWorkspaceAlign);

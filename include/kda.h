@@ -386,7 +386,9 @@ kda_status_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv, i
  * dbeta          device fp32 [B, T, H] (written)
  * d_initial_state device fp32 [N, H, Dk, Dv] or NULL (not wanted)
  * workspace      device, >= kda_chunk_bwd_workspace_size(...) bytes (required)
- * Supported: Dk, Dv in {64, 128}, fp32 or bf16, H <= 65535; per-token log-decay
+ * Supported: Dk, Dv in {64, 128}, fp32 or bf16, H <= 65535, (checkpoint
+ * chunks of 64 tokens for bf16 or 16 for fp32, about B*T/chunk + N) * H < 2^31
+ * (KDA_ERROR_NOT_SUPPORTED otherwise); per-token log-decay
  * >= -5.5 (KDA_GATE_LOGITS with g_min < -5.5 and KDA_GATE_SOFTPLUS return
  * KDA_ERROR_NOT_SUPPORTED, as does KDA_GATE_CUMSUM). Outputs must not alias
  * inputs. Gradients of bf16 tensors are rounded to bf16; states,
