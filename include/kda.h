@@ -393,7 +393,9 @@ kda_status_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv, i
  * KDA_ERROR_NOT_SUPPORTED, as does KDA_GATE_CUMSUM). Outputs must not alias
  * inputs. Gradients of bf16 tensors are rounded to bf16; states,
  * checkpoints of fp32 inputs and all accumulation are fp32; bf16 inputs keep
- * their checkpoints in bf16.
+ * their checkpoints in bf16. The call allocates nothing, sets no memory with
+ * memset and synchronizes nothing, so it may be captured into a HIP graph; it
+ * is deterministic (a replay equals the eager call bit for bit).
  */
 kda_status_t kda_chunk_bwd(const void* q, const void* k, const void* v, kda_dtype_t dtype,
                            const float* g, kda_gate_input_t gate_input, const float* A_log,
