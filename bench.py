@@ -385,6 +385,85 @@ def bench_backward(args, d, w, dev):
     return 0
 
 
+def bench_train(args, d, w, dev):
+    """One step = a training step's KDA work over the whole batch: the forward
+    and the backward. Timed both ways in one run: the training pair
+    (kda_chunk_fwd_train, which also writes the backward's checkpoints, then
+    kda_chunk_bwd_saved, which skips its first scan) and the regular pair
+    (kda_chunk_fwd, then kda_chunk_bwd)."""
+    import torch
+    from gated_delta_rule_92_amd import (bwd_workspace_size, chunk_bwd, chunk_fwd, chunk_fwd_train,
+                                         workspace_size)
+    B, T = d["q"].shape[0], d["q"].shape[1]
+    N = d["N"]
+    gen = torch.Generator(device=dev).manual_seed(2)
+    do = torch.randn(d["v"].shape, generator=gen, device=dev).to(w.dtype)
+    dhT = torch.randn((N, w.H, w.Dk, w.Dv), generator=gen, device=dev)
+    bws = torch.empty(max(bwd_workspace_size(B, T, w.H, w.Dk, w.Dv, N, w.chunk, w.dtype), 1),
+                      dtype=torch.uint8, device=dev)
+    fws = torch.empty(max(workspace_size(B, T, w.H, w.Dk, w.Dv, N, w.chunk, w.dtype), 1),
+                      dtype=torch.uint8, device=dev)
+    o = torch.empty(d["v"].shape, dtype=w.dtype, device=dev)
+    hT = torch.empty((N, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+    args_in = (d["q"], d["k"], d["v"], d["z"], d["beta"])
+
+    def step_pair():
+        chunk_fwd_train(*args_in, d["h0"], d["cu_seqlens"], gate="logits", g_min=w.g_min,
+                        chunk=w.chunk, bwd_workspace=bws)
+        chunk_bwd(*args_in, do, d["h0"], dhT, d["cu_seqlens"], gate="logits", g_min=w.g_min,
+                  chunk=w.chunk, workspace=bws, saved=True)
+
+    def step_regular():
+        chunk_fwd(*args_in, d["h0"], d["cu_seqlens"], gate="logits", g_min=w.g_min, chunk=w.chunk,
+                  o=o, final_state=hT, workspace=fws)
+        chunk_bwd(*args_in, do, d["h0"], dhT, d["cu_seqlens"], gate="logits", g_min=w.g_min,
+                  chunk=w.chunk, workspace=bws)
+
+    reg_ms, reg_launch = _timed(step_regular, args.steps, args.warmup, dev, args.prewarm_ms)
+    ms_per_step, launch_ms = _timed(step_pair, args.steps, args.warmup, dev, args.prewarm_ms)
+    kernel_ms = sum(launch_ms) / args.steps
+    reg_kernel_ms = sum(reg_launch) / args.steps
+    log(f"bench: training step {args.steps} steps: kda_chunk_fwd_train + kda_chunk_bwd_saved "
+        f"{kernel_ms:.3f} ms (wall {ms_per_step:.3f}); kda_chunk_fwd + kda_chunk_bwd "
+        f"{reg_kernel_ms:.3f} ms (wall {reg_ms:.3f})")
+    n_tokens = int(B * T)
+    bytes_alg = algorithmic_bytes(w, n_tokens, N * w.H, d["h0"] is not None) + \
+        backward_algorithmic_bytes(w, n_tokens, N * w.H)
+    achieved = bytes_alg / (kernel_ms / 1e3) / 1e9
+    line = {
+        "metric": "KDA chunk fwd+bwd (training step) tokens·heads/s (H=32,d=128,bf16,T=8K)",
+        "value": n_tokens * w.H / (ms_per_step / 1e3),
+        "unit": "tokens·heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype_name,
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "train", "batch": int(B), "seq_len": w.T,
+                   "heads": w.H, "d_k": w.Dk, "d_v": w.Dv, "chunk": w.chunk, "gate": "logits",
+                   "g_min": w.g_min, "initial_state": d["h0"] is not None, "sequences": N},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "scope": "the forward and the backward of one step (HIP events around the "
+                              "two calls); bytes = the forward's algorithmic bytes plus the "
+                              "minimum any backward must move",
+                     "algorithmic_bytes": bytes_alg},
+        "kernel_ms": kernel_ms,
+        "kernel_ms_median": launch_ms[len(launch_ms) // 2],
+        "kernel_ms_min": launch_ms[0],
+        "kernel_ms_max": launch_ms[-1],
+        "regular_pair": {"kernel_ms": reg_kernel_ms, "ms_per_step": reg_ms,
+                         "calls": "kda_chunk_fwd + kda_chunk_bwd"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def bench_decode(args, d, w, dev):
     """One step = one kda_recurrent_step: a single token for every (sequence,
     head) of the workload, the fp32 state updated in place. The step reads and
@@ -548,10 +627,12 @@ def main(argv=None):
     ap.add_argument("--split", type=int, default=1,
                     help="cut every sequence into this many segments that run in parallel "
                          "(state maps + composition + re-run); 1 = the plain forward")
-    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "decode", "gate"],
-                    default="forward",
+    ap.add_argument("--pass", dest="which",
+                    choices=["forward", "backward", "train", "decode", "gate"], default="forward",
                     help="forward: kda_chunk_fwd (the default line); backward: kda_chunk_bwd with "
-                         "seeded normal output and final-state gradients; decode: one "
+                         "seeded normal output and final-state gradients; train: forward and "
+                         "backward of a training step, kda_chunk_fwd_train + kda_chunk_bwd_saved "
+                         "next to kda_chunk_fwd + kda_chunk_bwd; decode: one "
                          "kda_recurrent_step for every (sequence, head); gate: one kda_gate "
                          "(gate and chunk-local cumsum) over the workload's logits")
     args = ap.parse_args(argv)
@@ -584,6 +665,8 @@ def main(argv=None):
 
     if args.which == "backward":
         return bench_backward(args, d, w, dev)
+    if args.which == "train":
+        return bench_train(args, d, w, dev)
     if args.which == "decode":
         return bench_decode(args, d, w, dev)
     if args.which == "gate":

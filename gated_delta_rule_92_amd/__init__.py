@@ -17,10 +17,10 @@ Public API (thin wrappers over the C ABI in include/kda.h):
     device_status(clear=False)        (device-side failure flags)
 """
 from .ops import (bwd_workspace_size, chunk_bwd, chunk_fwd, chunk_fwd_gated,  # noqa: F401
-                  chunk_fwd_noalloc, chunk_fwd_split, debug_set_spin_limit, device_status, compose_states, gate, gate_bwd, gated_rmsnorm, recurrent_step,
+                  chunk_fwd_noalloc, chunk_fwd_split, chunk_fwd_train, debug_set_spin_limit, device_status, compose_states, gate, gate_bwd, gated_rmsnorm, recurrent_step,
                   transition, workspace_size)
 
 __all__ = ["bwd_workspace_size", "chunk_bwd", "chunk_fwd", "chunk_fwd_gated", "chunk_fwd_noalloc",
-           "chunk_fwd_split", "debug_set_spin_limit", "device_status",
+           "chunk_fwd_split", "chunk_fwd_train", "debug_set_spin_limit", "device_status",
            "compose_states", "gate", "gate_bwd", "gated_rmsnorm", "recurrent_step",
            "transition", "workspace_size"]

@@ -35,7 +35,7 @@ EXPORTED = ("kda_status_string", "kda_version", "kda_gate", "kda_chunk_fwd_works
             "kda_chunk_fwd_gated", "kda_gated_rmsnorm", "kda_chunk_transition",
             "kda_compose_states", "kda_recurrent_step", "kda_chunk_bwd_workspace_size",
             "kda_chunk_bwd", "kda_gate_bwd", "kda_device_status", "kda_chunk_fwd_noalloc",
-            "kda_debug_set_spin_limit")
+            "kda_debug_set_spin_limit", "kda_chunk_fwd_train", "kda_chunk_bwd_saved")
 
 KDA_DEVICE_WAIT_TIMEOUT = 0x1
 KDA_DEVICE_DECAY_OUT_OF_RANGE = 0x2
@@ -103,6 +103,12 @@ def load(path: str = LIB_PATH):
                                   i32, i32, i32, i32, i32, i32, i32,  # N B T H Dk Dv chunk
                                   f32, vp, fp, vp, vp, vp, fp, fp, fp, vp, sz, vp]
     lib.kda_chunk_bwd.restype = i32
+    lib.kda_chunk_bwd_saved.argtypes = lib.kda_chunk_bwd.argtypes
+    lib.kda_chunk_bwd_saved.restype = i32
+    lib.kda_chunk_fwd_train.argtypes = [vp, vp, vp, i32, fp, i32, fp, f32, fp, fp, ip,
+                                        i32, i32, i32, i32, i32, i32, i32,  # N B T H Dk Dv chunk
+                                        f32, vp, fp, vp, sz, vp]
+    lib.kda_chunk_fwd_train.restype = i32
     lib.kda_gate_bwd.argtypes = [fp, fp, f32, fp, ctypes.c_long, i32, i32, fp, fp, vp]
     lib.kda_gate_bwd.restype = i32
     lib.kda_device_status.argtypes = [ctypes.POINTER(ctypes.c_uint32), i32, vp]

@@ -695,6 +695,7 @@ kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v, kda
   return launch_status(kda::launch_recurrent(r, reinterpret_cast<hipStream_t>(stream)));
 }
 
+extern "C++" {
 namespace {
 
 size_t bwd_elt(kda_dtype_t dtype) { return dtype == KDA_BFLOAT16 ? 2 : 4; }
@@ -708,21 +709,125 @@ long bwd_slots_bound(int B, int T, int N, kda_dtype_t dtype) {
   return dense > packed ? dense : packed;
 }
 
+// The backward's workspace: the state and state-gradient checkpoints (ck
+// bytes each), U, V~ and dY (tok bytes each), A~ (at bytes) and, for packed
+// sequences, the longest-first order of the scans (ord bytes), in that order.
+struct BwdLayout {
+  size_t ck = 0, tok = 0, at = 0, ord = 0;
+  size_t ckS() const { return 0; }
+  size_t ckdS() const { return ck; }
+  size_t U() const { return 2 * ck; }
+  size_t Vt() const { return 2 * ck + tok; }
+  size_t dY() const { return 2 * ck + 2 * tok; }
+  size_t At() const { return 2 * ck + 3 * tok; }
+  size_t order() const { return 2 * ck + 3 * tok + at; }
+  size_t bytes() const { return 2 * ck + 3 * tok + at + ord; }
+};
+
+BwdLayout bwd_layout(int B, int T, int H, int Dk, int Dv, int N, kda_dtype_t dtype) {
+  BwdLayout l;
+  const size_t e = bwd_elt(dtype);
+  l.ck = round_up((size_t)bwd_slots_bound(B, T, N, dtype) * H * Dk * Dv * e, kWorkspaceAlign);
+  l.tok = round_up((size_t)B * T * H * Dv * e, kWorkspaceAlign);
+  l.at = round_up((size_t)B * T * H * 16 * sizeof(float), kWorkspaceAlign);
+  l.ord = (B == 1 && N > 1 && N <= kda::kMaxOrderN) ? round_up(sizeof(int32_t) * (size_t)N, kWorkspaceAlign)
+                                                     : 0;
+  return l;
+}
+
+// The checks kda_chunk_bwd, kda_chunk_bwd_saved and kda_chunk_fwd_train
+// share: sequences, shapes, gate, alignment, support and workspace size.
+kda_status_t check_bwd_args(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                            const float* g, kda_gate_input_t gate_input, float g_min,
+                            const float* beta, const float* initial_state,
+                            const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk, int Dv,
+                            int chunk, void* workspace, size_t workspace_bytes, kda::Seqs* s,
+                            long* slots) {
+  kda_status_t st = check_seqs(cu_seqlens, N, B, T, s);
+  if (st != KDA_SUCCESS) return st;
+  if (!cu_seqlens && N != B) return KDA_ERROR_INVALID_VALUE;
+  if (H <= 0 || Dk <= 0 || Dv <= 0 || chunk <= 0) return KDA_ERROR_INVALID_VALUE;
+  if (dtype != KDA_FLOAT32 && dtype != KDA_BFLOAT16) return KDA_ERROR_INVALID_VALUE;
+  if (gate_input != KDA_GATE_LOGDECAY && gate_input != KDA_GATE_CUMSUM &&
+      gate_input != KDA_GATE_LOGITS && gate_input != KDA_GATE_SOFTPLUS)
+    return KDA_ERROR_INVALID_VALUE;
+  if (gate_input == KDA_GATE_LOGITS && !(g_min < 0.0f)) return KDA_ERROR_INVALID_VALUE;
+  if (s->Ttot > 0 && (!q || !k || !v || !g || !beta)) return KDA_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(initial_state))
+    return KDA_ERROR_INVALID_VALUE;
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) % kWorkspaceAlign) != 0)
+    return KDA_ERROR_INVALID_VALUE;
+  if (chunk != 64) return KDA_ERROR_NOT_SUPPORTED;
+  if (gate_input == KDA_GATE_CUMSUM || gate_input == KDA_GATE_SOFTPLUS)
+    return KDA_ERROR_NOT_SUPPORTED;
+  if (gate_input == KDA_GATE_LOGITS && g_min < kda::kMinFusedGmin) return KDA_ERROR_NOT_SUPPORTED;
+  if (!kda::chunk_bwd_supported(Dk, Dv)) return KDA_ERROR_NOT_SUPPORTED;
+  // keeps the gradient kernel's 32-bit per-lane byte offsets within a chunk
+  // below 2^32
+  if (H > 65535) return KDA_ERROR_NOT_SUPPORTED;
+  if (!workspace || workspace_bytes < bwd_layout(B, T, H, Dk, Dv, s->N, dtype).bytes())
+    return KDA_ERROR_INSUFFICIENT_WORKSPACE;
+  *slots = kda::chunk_bwd_slots(*s, dtype == KDA_BFLOAT16);
+  // the gradient kernel's grid has one workgroup per (checkpoint chunk, head)
+  if (*slots * H > 0x7fffffffL || (long)s->N * H > 0x7fffffffL) return KDA_ERROR_NOT_SUPPORTED;
+  return KDA_SUCCESS;
+}
+
+kda_status_t chunk_bwd_impl(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                            const float* g, kda_gate_input_t gate_input, const float* A_log,
+                            float g_min, const float* beta, const float* initial_state,
+                            const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk, int Dv,
+                            int chunk, float scale, const void* d_o, const float* d_final_state,
+                            void* dq, void* dk, void* dv, float* dg, float* dbeta,
+                            float* d_initial_state, void* workspace, size_t workspace_bytes,
+                            kda_stream_t stream, bool saved) {
+  kda::Seqs s;
+  long slots = 0;
+  kda_status_t st = check_bwd_args(q, k, v, dtype, g, gate_input, g_min, beta, initial_state,
+                                   cu_seqlens, N, B, T, H, Dk, Dv, chunk, workspace,
+                                   workspace_bytes, &s, &slots);
+  if (st != KDA_SUCCESS) return st;
+  if (s.Ttot > 0 && (!d_o || !dq || !dk || !dv || !dg || !dbeta)) return KDA_ERROR_INVALID_VALUE;
+  if (!aligned16(d_o) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dg) ||
+      !aligned16(d_final_state) || !aligned16(d_initial_state))
+    return KDA_ERROR_INVALID_VALUE;
+  // checkpoints written by kda_chunk_fwd_train exist only for its shape
+  if (saved && !kda::chunk_pipe_supported(dtype == KDA_BFLOAT16, Dk, Dv, chunk))
+    return KDA_ERROR_NOT_SUPPORTED;
+  if (s.N == 0) return KDA_SUCCESS;
+  const BwdLayout l = bwd_layout(B, T, H, Dk, Dv, s.N, dtype);
+  char* ws = static_cast<char*>(workspace);
+  kda::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.gate = (int)gate_input;
+  a.A_log = A_log; a.g_min = g_min; a.beta = beta; a.h0 = initial_state;
+  a.cu = cu_seqlens; a.N = s.N; a.T = T; a.H = H; a.scale = scale;
+  a.dO = d_o; a.dhT = d_final_state;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = d_initial_state;
+  a.ckS = ws + l.ckS(); a.ckdS = ws + l.ckdS(); a.U = ws + l.U(); a.Vt = ws + l.Vt();
+  a.dY = ws + l.dY();
+  a.At = reinterpret_cast<float*>(ws + l.At());
+  a.order = nullptr;
+  a.skip_fwd_scan = saved;
+  st = failure_reporting(&a.status, &a.spin_limit);
+  if (st != KDA_SUCCESS) return st;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (l.ord > 0 && cu_seqlens) {
+    int32_t* order = reinterpret_cast<int32_t*>(ws + l.order());
+    if (kda::launch_order(cu_seqlens, s.N, order, hs) != hipSuccess) return KDA_ERROR_LAUNCH_FAILURE;
+    a.order = order;
+  }
+  return launch_status(kda::launch_chunk_bwd(a, dtype == KDA_BFLOAT16, Dk, Dv, slots, hs));
+}
+
 }  // namespace
+}  // extern "C++"
 
 kda_status_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv, int N, int chunk,
                                           kda_dtype_t dtype, size_t* bytes) {
   if (!bytes || B <= 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || N < 0 || chunk <= 0)
     return KDA_ERROR_INVALID_VALUE;
   if (dtype != KDA_FLOAT32 && dtype != KDA_BFLOAT16) return KDA_ERROR_INVALID_VALUE;
-  const size_t e = bwd_elt(dtype);
-  const size_t ck = round_up((size_t)bwd_slots_bound(B, T, N, dtype) * H * Dk * Dv * e, kWorkspaceAlign);
-  const size_t tok = round_up((size_t)B * T * H * Dv * e, kWorkspaceAlign);
-  const size_t at = round_up((size_t)B * T * H * 16 * sizeof(float), kWorkspaceAlign);
-  // longest-first order of packed sequences for the two scans
-  const size_t ord = (B == 1 && N > 1 && N <= kda::kMaxOrderN)
-                         ? round_up(sizeof(int32_t) * (size_t)N, kWorkspaceAlign) : 0;
-  *bytes = 2 * ck + 3 * tok + at + ord;
+  *bytes = bwd_layout(B, T, H, Dk, Dv, N, dtype).bytes();
   return KDA_SUCCESS;
 }
 
@@ -734,64 +839,62 @@ kda_status_t kda_chunk_bwd(const void* q, const void* k, const void* v, kda_dtyp
                            void* dq, void* dk, void* dv, float* dg, float* dbeta,
                            float* d_initial_state, void* workspace, size_t workspace_bytes,
                            kda_stream_t stream) {
+  return chunk_bwd_impl(q, k, v, dtype, g, gate_input, A_log, g_min, beta, initial_state,
+                        cu_seqlens, N, B, T, H, Dk, Dv, chunk, scale, d_o, d_final_state, dq, dk,
+                        dv, dg, dbeta, d_initial_state, workspace, workspace_bytes, stream, false);
+}
+
+kda_status_t kda_chunk_bwd_saved(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                                 const float* g, kda_gate_input_t gate_input, const float* A_log,
+                                 float g_min, const float* beta, const float* initial_state,
+                                 const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
+                                 int Dv, int chunk, float scale, const void* d_o,
+                                 const float* d_final_state, void* dq, void* dk, void* dv,
+                                 float* dg, float* dbeta, float* d_initial_state,
+                                 void* workspace, size_t workspace_bytes, kda_stream_t stream) {
+  return chunk_bwd_impl(q, k, v, dtype, g, gate_input, A_log, g_min, beta, initial_state,
+                        cu_seqlens, N, B, T, H, Dk, Dv, chunk, scale, d_o, d_final_state, dq, dk,
+                        dv, dg, dbeta, d_initial_state, workspace, workspace_bytes, stream, true);
+}
+
+kda_status_t kda_chunk_fwd_train(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                                 const float* g, kda_gate_input_t gate_input, const float* A_log,
+                                 float g_min, const float* beta, const float* initial_state,
+                                 const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
+                                 int Dv, int chunk, float scale, void* o, float* final_state,
+                                 void* bwd_workspace, size_t bwd_workspace_bytes,
+                                 kda_stream_t stream) {
   kda::Seqs s;
-  kda_status_t st = check_seqs(cu_seqlens, N, B, T, &s);
+  long slots = 0;
+  kda_status_t st = check_bwd_args(q, k, v, dtype, g, gate_input, g_min, beta, initial_state,
+                                   cu_seqlens, N, B, T, H, Dk, Dv, chunk, bwd_workspace,
+                                   bwd_workspace_bytes, &s, &slots);
   if (st != KDA_SUCCESS) return st;
-  if (!cu_seqlens && N != B) return KDA_ERROR_INVALID_VALUE;
-  if (H <= 0 || Dk <= 0 || Dv <= 0 || chunk <= 0) return KDA_ERROR_INVALID_VALUE;
-  if (dtype != KDA_FLOAT32 && dtype != KDA_BFLOAT16) return KDA_ERROR_INVALID_VALUE;
-  if (gate_input != KDA_GATE_LOGDECAY && gate_input != KDA_GATE_CUMSUM &&
-      gate_input != KDA_GATE_LOGITS && gate_input != KDA_GATE_SOFTPLUS)
-    return KDA_ERROR_INVALID_VALUE;
-  if (gate_input == KDA_GATE_LOGITS && !(g_min < 0.0f)) return KDA_ERROR_INVALID_VALUE;
-  if (s.Ttot > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
-    return KDA_ERROR_INVALID_VALUE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(d_o) ||
-      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dg) ||
-      !aligned16(initial_state) || !aligned16(d_final_state) || !aligned16(d_initial_state))
-    return KDA_ERROR_INVALID_VALUE;
-  if (workspace && (reinterpret_cast<uintptr_t>(workspace) % kWorkspaceAlign) != 0)
-    return KDA_ERROR_INVALID_VALUE;
-  if (chunk != 64) return KDA_ERROR_NOT_SUPPORTED;
-  if (gate_input == KDA_GATE_CUMSUM || gate_input == KDA_GATE_SOFTPLUS)
-    return KDA_ERROR_NOT_SUPPORTED;
-  if (gate_input == KDA_GATE_LOGITS && g_min < kda::kMinFusedGmin) return KDA_ERROR_NOT_SUPPORTED;
-  if (!kda::chunk_bwd_supported(Dk, Dv)) return KDA_ERROR_NOT_SUPPORTED;
-  // the gradient kernel's grid has one row per head (at most 65535), which
-  // also keeps its 32-bit per-lane byte offsets within a chunk below 2^32
-  if (H > 65535) return KDA_ERROR_NOT_SUPPORTED;
-  size_t need = 0;
-  st = kda_chunk_bwd_workspace_size(B, T, H, Dk, Dv, s.N, chunk, dtype, &need);
-  if (st != KDA_SUCCESS) return st;
-  if (!workspace || workspace_bytes < need) return KDA_ERROR_INSUFFICIENT_WORKSPACE;
-  const long slots = kda::chunk_bwd_slots(s, dtype == KDA_BFLOAT16);
-  // the gradient kernel's grid has one workgroup per (checkpoint chunk, head)
-  if (slots * H > 0x7fffffffL || (long)s.N * H > 0x7fffffffL) return KDA_ERROR_NOT_SUPPORTED;
+  if (s.Ttot > 0 && !o) return KDA_ERROR_INVALID_VALUE;
+  if (!aligned16(o) || !aligned16(final_state)) return KDA_ERROR_INVALID_VALUE;
+  if (!kda::chunk_pipe_supported(dtype == KDA_BFLOAT16, Dk, Dv, chunk)) return KDA_ERROR_NOT_SUPPORTED;
   if (s.N == 0) return KDA_SUCCESS;
-  const size_t e = bwd_elt(dtype);
-  const size_t ck = round_up((size_t)bwd_slots_bound(B, T, s.N, dtype) * H * Dk * Dv * e, kWorkspaceAlign);
-  const size_t tok = round_up((size_t)B * T * H * Dv * e, kWorkspaceAlign);
-  char* ws = static_cast<char*>(workspace);
-  kda::BwdArgs a{};
-  a.q = q; a.k = k; a.v = v; a.g = g; a.gate = (int)gate_input;
-  a.A_log = A_log; a.g_min = g_min; a.beta = beta; a.h0 = initial_state;
-  a.cu = cu_seqlens; a.N = s.N; a.T = T; a.H = H; a.scale = scale;
-  a.dO = d_o; a.dhT = d_final_state;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = d_initial_state;
-  a.ckS = ws; a.ckdS = ws + ck; a.U = ws + 2 * ck; a.Vt = ws + 2 * ck + tok;
-  a.dY = ws + 2 * ck + 2 * tok;
-  a.At = reinterpret_cast<float*>(ws + 2 * ck + 3 * tok);
-  a.order = nullptr;
+  const BwdLayout l = bwd_layout(B, T, H, Dk, Dv, s.N, dtype);
+  char* ws = static_cast<char*>(bwd_workspace);
+  kda::ChunkArgs a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.gate_mode = (int)gate_input;
+  a.A_log = A_log; a.g_min = g_min; a.beta = beta;
+  a.h0 = initial_state; a.hT = final_state; a.o = o;
+  a.seqs = s; a.order = nullptr;
+  a.H = H; a.Dk = Dk; a.Dv = Dv; a.scale = scale; a.bf16 = true;
+  a.ck_state = ws + l.ckS(); a.ck_u = ws + l.U(); a.ck_vt = ws + l.Vt();
+  a.ck_at = reinterpret_cast<float*>(ws + l.At());
   st = failure_reporting(&a.status, &a.spin_limit);
   if (st != KDA_SUCCESS) return st;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  if (cu_seqlens && B == 1 && s.N > 1 && s.N <= kda::kMaxOrderN) {
-    const size_t at = round_up((size_t)B * T * H * 16 * sizeof(float), kWorkspaceAlign);
-    int32_t* order = reinterpret_cast<int32_t*>(ws + 2 * ck + 3 * tok + at);
+  if (l.ord > 0 && cu_seqlens) {
+    // the same longest-first order the backward's scans take (it only sets
+    // the order in which units start; kda_chunk_bwd_saved computes it again)
+    int32_t* order = reinterpret_cast<int32_t*>(ws + l.order());
     if (kda::launch_order(cu_seqlens, s.N, order, hs) != hipSuccess) return KDA_ERROR_LAUNCH_FAILURE;
     a.order = order;
   }
-  return launch_status(kda::launch_chunk_bwd(a, dtype == KDA_BFLOAT16, Dk, Dv, slots, hs));
+  return launch_status(kda::launch_chunk_fwd_checkpoint(a, hs));
 }
 
 kda_status_t kda_gate_bwd(const float* z, const float* A_log, float g_min, const float* dg,

@@ -994,7 +994,11 @@ __global__ void __launch_bounds__(64 * (DK / 16)) bwd_tile_grad(BwdArgs a) {
 template <typename T, int DK, int DV>
 hipError_t launch_bwd_t(const BwdArgs& a, long slots, hipStream_t stream) {
   const unsigned units = (unsigned)(a.N * a.H);
-  if (std::is_same<T, __bf16>::value && chunk_pipe_supported(true, DK, DV, 64)) {
+  constexpr bool pipe = std::is_same<T, __bf16>::value && DK == 128 && DV == 128;
+  if (a.skip_fwd_scan) {
+    // only the pipelined forward writes checkpoints outside this call
+    if (!pipe) return hipErrorInvalidValue;
+  } else if (pipe) {
     // the pipelined forward kernel in checkpoint mode writes the same
     // checkpoints, U and V~ as bwd_fwd_scan
     ChunkArgs c;

@@ -166,6 +166,9 @@ __device__ __forceinline__ uint32_t perm_hi16(uint32_t a, uint32_t b) {
 //       dS = Diag(e^{G_15}) dS' + (e^G Q)^T dO - (e^G K)^T (beta dY);
 //     writes dY per token (a.ck_vt) and, in bf16, the state gradient leaving
 //     the last tile of every 64-token chunk (a.ck_state).
+//   kModeForwardCheckpoint: kModeForward and kModeCheckpoint in one pass: o
+//     and the final state, and the checkpoints, U, V~ and A~ that the
+//     backward would otherwise recompute with a kModeCheckpoint launch.
 enum {
   kModeForward = 0,
   kModeStateOnly = 1,
@@ -173,7 +176,8 @@ enum {
   kModeForwardGated = 3,
   kModeCheckpoint = 4,
   kModeReverse = 5,
-  kModeSplitPass = 6
+  kModeSplitPass = 6,
+  kModeForwardCheckpoint = 7
 };
 
 template <int GATE, int MODE>
@@ -188,8 +192,8 @@ __global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : 
   // as one matrix-core product.
   constexpr bool PAIR = GATE == kGateSoftplus;
   constexpr bool GATED = MODE == kModeForwardGated;
-  constexpr bool NEEDQ = MODE == kModeForward || GATED;
-  constexpr bool CKPT = MODE == kModeCheckpoint;
+  constexpr bool NEEDQ = MODE == kModeForward || GATED || MODE == kModeForwardCheckpoint;
+  constexpr bool CKPT = MODE == kModeCheckpoint || MODE == kModeForwardCheckpoint;
   constexpr bool REV = MODE == kModeReverse;
   constexpr bool LOADQ = NEEDQ || REV;
   // Outside reverse mode the slot holds -(k e^G), so that the consumers form
@@ -1061,6 +1065,12 @@ hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t stream) {
 hipError_t launch_chunk_checkpoint(const ChunkArgs& a, hipStream_t stream) {
   if (a.seqs.N == 0 || a.H == 0) return hipSuccess;
   launch_pipe_t<kModeCheckpoint>(a, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_fwd_checkpoint(const ChunkArgs& a, hipStream_t stream) {
+  if (a.seqs.N == 0 || a.H == 0) return hipSuccess;
+  launch_pipe_t<kModeForwardCheckpoint>(a, stream);
   return hipGetLastError();
 }
 

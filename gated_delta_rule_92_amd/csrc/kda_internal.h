@@ -116,6 +116,8 @@ hipError_t launch_chunk_transition(const ChunkArgs& a, hipStream_t stream);
 hipError_t launch_chunk_split_pass(const ChunkArgs& a, hipStream_t stream);
 // Same kernel in checkpoint mode (ck_state, ck_u, ck_vt must be set).
 hipError_t launch_chunk_checkpoint(const ChunkArgs& a, hipStream_t stream);
+// The forward (o, hT as launch_chunk_pipe) and checkpoint mode in one launch.
+hipError_t launch_chunk_fwd_checkpoint(const ChunkArgs& a, hipStream_t stream);
 // Same kernel in reverse mode, the backward's state-gradient recurrence:
 // v = dO, h0 = final-state gradient (or nullptr), hT = initial-state gradient
 // (or nullptr); writes dY (ck_vt) and the bf16 state gradient leaving every
@@ -202,6 +204,9 @@ struct BwdArgs {
   int spin_limit = 0;
   float* At = nullptr;  // [Ttot, H, 16] row r of each tile's A~ = A_kk / beta
                         // (strictly lower part; zeros elsewhere)
+  // ckS, U, Vt and At already hold what the forward scan writes (a training
+  // forward wrote them): the forward scan is not launched
+  bool skip_fwd_scan = false;
 };
 inline bool chunk_bwd_supported(int Dk, int Dv) {
   return (Dk == 64 || Dk == 128) && (Dv == 64 || Dv == 128);

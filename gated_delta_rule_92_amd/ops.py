@@ -430,12 +430,14 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               cu_seqlens: Optional[torch.Tensor] = None, gate: str = "logdecay",
               A_log: Optional[torch.Tensor] = None, g_min: float = -5.0, chunk: int = 64,
               scale: float = 1.0, want_dh0: bool = True,
-              workspace: Optional[torch.Tensor] = None) -> dict:
+              workspace: Optional[torch.Tensor] = None, saved: bool = False) -> dict:
     """Gradients of chunk_fwd: given do [B, T, H, Dv] and d_final_state
     [N, H, Dk, Dv] (None = zero), returns a dict with dq, dk, dv (input
     dtype), dg (fp32, w.r.t. the per-token log-decay), dbeta (fp32) and dh0
     (fp32 [N, H, Dk, Dv], or None when want_dh0 is False). gate is
-    "logdecay" (g = log-decay) or "logits" (g = z)."""
+    "logdecay" (g = log-decay) or "logits" (g = z). saved=True calls
+    kda_chunk_bwd_saved: workspace must be the one chunk_fwd_train filled from
+    the same inputs."""
     lib = _lib.load()
     dev = q.device
     dt = q.dtype
@@ -466,17 +468,71 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
            else None}
     ws_bytes = bwd_workspace_size(B, T, H, Dk, Dv, N, chunk, dt)
     if workspace is None:
+        if saved:
+            raise ValueError("saved=True needs the workspace chunk_fwd_train filled")
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     ws_len = workspace.numel() * workspace.element_size()
+    fn = lib.kda_chunk_bwd_saved if saved else lib.kda_chunk_bwd
     with torch.cuda.device(dev):
-        rc = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _GATES[gate],
+        rc = fn(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _GATES[gate],
                                _ptr(A_log), float(g_min), _ptr(beta), _ptr(initial_state),
                                _ptr(cu_seqlens), N, B, T, H, Dk, Dv, int(chunk), float(scale),
                                _ptr(do), _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]),
                                _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
                                _ptr(out["dh0"]), _ptr(workspace), ws_len, _stream(dev))
-    _lib.check(rc, "kda_chunk_bwd")
+    _lib.check(rc, "kda_chunk_bwd_saved" if saved else "kda_chunk_bwd")
     return out
+
+
+def chunk_fwd_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                    cu_seqlens: Optional[torch.Tensor] = None, gate: str = "logdecay",
+                    A_log: Optional[torch.Tensor] = None, g_min: float = -5.0, chunk: int = 64,
+                    scale: float = 1.0, output_final_state: bool = True,
+                    bwd_workspace: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor], torch.Tensor]:
+    """kda_chunk_fwd_train: chunk_fwd's (o, final_state) and, in the same
+    pass, the backward's checkpoints in a backward workspace (allocated when
+    bwd_workspace is None). Returns (o, final_state, bwd_workspace); pass the
+    workspace to chunk_bwd(..., saved=True) with the same inputs."""
+    lib = _lib.load()
+    dev = q.device
+    dt = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, dt, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or g.shape != q.shape or \
+            beta.shape != q.shape[:3]:
+        raise ValueError("shape mismatch among q, k, v, g, beta")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, dev)
+        if tuple(initial_state.shape) != (N, H, Dk, Dv):
+            raise ValueError("initial_state must be [N, H, Dk, Dv]")
+    if A_log is not None:
+        _need(A_log, "A_log", torch.float32, dev)
+    o = torch.empty((B, T, H, Dv), dtype=dt, device=dev)
+    final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev) \
+        if output_final_state else None
+    ws_bytes = bwd_workspace_size(B, T, H, Dk, Dv, N, chunk, dt)
+    if bwd_workspace is None:
+        bwd_workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws_len = bwd_workspace.numel() * bwd_workspace.element_size()
+    with torch.cuda.device(dev):
+        rc = lib.kda_chunk_fwd_train(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g),
+                                     _GATES[gate], _ptr(A_log), float(g_min), _ptr(beta),
+                                     _ptr(initial_state), _ptr(cu_seqlens), N, B, T, H, Dk, Dv,
+                                     int(chunk), float(scale), _ptr(o), _ptr(final_state),
+                                     _ptr(bwd_workspace), ws_len, _stream(dev))
+    _lib.check(rc, "kda_chunk_fwd_train")
+    return o, final_state, bwd_workspace
 
 
 def gate_bwd(z: torch.Tensor, dg: torch.Tensor, A_log: Optional[torch.Tensor] = None,

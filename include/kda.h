@@ -407,6 +407,53 @@ kda_status_t kda_chunk_bwd(const void* q, const void* k, const void* v, kda_dtyp
                            kda_stream_t stream);
 
 /*
+ * kda_chunk_fwd_train — kda_chunk_fwd for training: the same o and
+ * final_state, and in the same pass what kda_chunk_bwd's first scan would
+ * recompute (the state entering every 64-token chunk, U, the pseudo-values V~
+ * and A~ = A_kk / beta per tile row), written into bwd_workspace, a
+ * kda_chunk_bwd workspace for the same shapes. A later kda_chunk_bwd_saved
+ * with the same inputs and that workspace then skips that scan. Training
+ * forward and backward are thereby one pass over the inputs shorter; the
+ * forward writes 1088 more bytes per token·head (bf16, d = 128).
+ *
+ * Arguments as for kda_chunk_fwd (no workspace of its own, no automatic
+ * context split: one chain per (sequence, head)), plus bwd_workspace and its
+ * size (>= kda_chunk_bwd_workspace_size(B, T, H, Dk, Dv, N, 64, dtype); 256-byte
+ * aligned). o is required; final_state may be NULL.
+ * Supported: bf16, Dk = Dv = 128, chunk = 64, gate_input KDA_GATE_LOGDECAY or
+ * KDA_GATE_LOGITS with g_min >= -5.5, H <= 65535 (KDA_ERROR_NOT_SUPPORTED
+ * otherwise); KDA_ERROR_INSUFFICIENT_WORKSPACE for a missing or short
+ * bwd_workspace. o and final_state equal kda_chunk_fwd's unsplit results.
+ */
+kda_status_t kda_chunk_fwd_train(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                                 const float* g, kda_gate_input_t gate_input, const float* A_log,
+                                 float g_min, const float* beta, const float* initial_state,
+                                 const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
+                                 int Dv, int chunk, float scale, void* o, float* final_state,
+                                 void* bwd_workspace, size_t bwd_workspace_bytes,
+                                 kda_stream_t stream);
+
+/*
+ * kda_chunk_bwd_saved — kda_chunk_bwd for a workspace that
+ * kda_chunk_fwd_train has filled from the same q, k, v, g, gate_input, A_log,
+ * g_min, beta, initial_state, cu_seqlens and shapes: its first scan is not
+ * run, the checkpoints, U, V~ and A~ are read from the workspace, and the
+ * gradients equal kda_chunk_bwd's bit for bit. The workspace must not have
+ * been used by another call in between (the results are otherwise undefined;
+ * nothing checks it). Arguments, outputs and errors as for kda_chunk_bwd;
+ * KDA_ERROR_NOT_SUPPORTED outside kda_chunk_fwd_train's shapes (bf16,
+ * Dk = Dv = 128, chunk = 64).
+ */
+kda_status_t kda_chunk_bwd_saved(const void* q, const void* k, const void* v, kda_dtype_t dtype,
+                                 const float* g, kda_gate_input_t gate_input, const float* A_log,
+                                 float g_min, const float* beta, const float* initial_state,
+                                 const int32_t* cu_seqlens, int N, int B, int T, int H, int Dk,
+                                 int Dv, int chunk, float scale, const void* d_o,
+                                 const float* d_final_state, void* dq, void* dk, void* dv,
+                                 float* dg, float* dbeta, float* d_initial_state,
+                                 void* workspace, size_t workspace_bytes, kda_stream_t stream);
+
+/*
  * kda_gate_bwd — gradient of the gate g = g_min * sigmoid(exp(A_h) z)
  * [KDA-blog §Chunkwise parallel form, new-gate equation], elementwise over
  * rows x H x Dk (layout [rows, H, Dk]):

@@ -142,6 +142,10 @@ hipError_t launch_chunk_split_pass(const ChunkArgs& a, hipStream_t) {
   return record_chunk("chunk_split_pass", a);
 }
 hipError_t launch_chunk_checkpoint(const ChunkArgs&, hipStream_t) { return record("chunk_checkpoint"); }
+hipError_t launch_chunk_fwd_checkpoint(const ChunkArgs& a, hipStream_t) {
+  return record("chunk_fwd_checkpoint", {a.q, a.o, a.hT, a.order, a.ck_state, a.ck_u, a.ck_vt, a.ck_at},
+                {a.seqs.N, a.H, 0, 0});
+}
 hipError_t launch_chunk_reverse(const ChunkArgs&, hipStream_t) { return record("chunk_reverse"); }
 hipError_t launch_gated_rmsnorm(const void*, const void*, bool, const float*, float, long, int, void*,
                                 hipStream_t) {
@@ -157,8 +161,9 @@ hipError_t launch_split_tables(const SplitTables& t, const int32_t* cu, int nseq
                 {nseq, P, L0, Lp});
 }
 hipError_t launch_chunk_fused(const ChunkArgs&, hipStream_t) { return record("chunk_fused"); }
-hipError_t launch_chunk_bwd(const BwdArgs&, bool, int, int, long, hipStream_t) {
-  return record("chunk_bwd");
+hipError_t launch_chunk_bwd(const BwdArgs& a, bool, int, int, long slots, hipStream_t) {
+  return record("chunk_bwd", {a.ckS, a.ckdS, a.U, a.Vt, a.dY, a.At, a.order, a.h0},
+                {a.skip_fwd_scan ? 1 : 0, (int)slots, a.N, 0});
 }
 hipError_t launch_gate_bwd(const float*, const float*, float, const float*, long, int, int, float*,
                            float*, hipStream_t) {

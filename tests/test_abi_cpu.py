@@ -451,3 +451,80 @@ def test_split_without_a_second_stream_runs_every_piece_mapped():
     assert got[2][2] == [1, 9, 9, 1]
     assert got[3][1] == [Q, WS + off["starts"], HT, 0, O, 0, WS, V]
     assert got[3][2] == [9, 0, 9, 0]
+
+
+def _train_call(lib, fn, **kw):
+    """kda_chunk_fwd_train (fn = "fwd") or kda_chunk_bwd_saved (fn = "bwd")
+    on fake device addresses: every call here is refused before any launch,
+    except in the host-check build, whose launchers only record."""
+    a = dict(dtype=1, gate=2, g_min=-5.0, h0=None, cu=None, N=2, B=2, T=1000, H=4, Dk=128,
+             Dv=128, chunk=64, o=FAKE * 7, hT=None, ws=FAKE * 9, ws_bytes=None)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        n = ctypes.c_size_t(0)
+        assert lib.kda_chunk_bwd_workspace_size(a["B"], a["T"], a["H"], a["Dk"], a["Dv"], a["N"],
+                                                64, a["dtype"], ctypes.byref(n)) == 0
+        a["ws_bytes"] = n.value
+    head = (FAKE, FAKE * 2, FAKE * 3, a["dtype"], FAKE * 4, a["gate"], None, a["g_min"], FAKE * 5,
+            a["h0"], a["cu"], a["N"], a["B"], a["T"], a["H"], a["Dk"], a["Dv"], a["chunk"], 1.0)
+    if fn == "fwd":
+        return lib.kda_chunk_fwd_train(*head, a["o"], a["hT"], a["ws"], a["ws_bytes"], None)
+    return lib.kda_chunk_bwd_saved(*head, FAKE * 10, None, FAKE * 11, FAKE * 12, FAKE * 13,
+                                   FAKE * 14, FAKE * 15, None, a["ws"], a["ws_bytes"], None)
+
+
+def test_training_forward_and_saved_backward_reject_what_they_do_not_support():
+    lib = _lib.load()
+    for fn in ("fwd", "bwd"):
+        call = lambda **kw: _train_call(lib, fn, **kw)  # noqa: E731
+        assert call(dtype=0) == _lib.KDA_ERROR_NOT_SUPPORTED          # fp32
+        assert call(Dk=64, Dv=64) == _lib.KDA_ERROR_NOT_SUPPORTED     # d = 64
+        assert call(chunk=32) == _lib.KDA_ERROR_NOT_SUPPORTED
+        assert call(gate=3) == _lib.KDA_ERROR_NOT_SUPPORTED           # softplus
+        assert call(gate=2, g_min=-8.0) == _lib.KDA_ERROR_NOT_SUPPORTED
+        assert call(ws=None) == _lib.KDA_ERROR_INSUFFICIENT_WORKSPACE
+        assert call(ws_bytes=1024) == _lib.KDA_ERROR_INSUFFICIENT_WORKSPACE
+        assert call(ws=FAKE + 8) == _lib.KDA_ERROR_INVALID_VALUE     # misaligned workspace
+        assert call(gate=7) == _lib.KDA_ERROR_INVALID_VALUE
+    assert _train_call(lib, "fwd", o=None) == _lib.KDA_ERROR_INVALID_VALUE
+
+
+def test_training_forward_writes_what_the_saved_backward_reads():
+    """Only in the host-check build: kda_chunk_fwd_train launches the forward
+    with checkpoints into the backward workspace, at exactly the state
+    checkpoint, U, V~ and A~ addresses that kda_chunk_bwd's gradient launch
+    reads; kda_chunk_bwd_saved reads the same addresses with the forward scan
+    skipped, kda_chunk_bwd without."""
+    lib = _lib.load()
+    if not hasattr(lib, "kda_host_check_build"):
+        pytest.skip("needs the host-check build (tests/test_sanitizers_cpu.py)")
+    log = (_Launch * 64).in_dll(lib, "kda_host_check_log")
+    n = ctypes.c_int.in_dll(lib, "kda_host_check_log_len")
+
+    def launches():
+        return [(log[i].name.decode(), [p or 0 for p in log[i].ptr], list(log[i].val))
+                for i in range(n.value)]
+
+    WS, O, HT, H0 = FAKE * 9, FAKE * 7, FAKE * 8, FAKE * 6
+    lib.kda_host_check_log_clear()
+    assert _train_call(lib, "fwd", hT=HT, h0=H0) == 0
+    assert _train_call(lib, "bwd", h0=H0) == 0
+    ws = ctypes.c_size_t(0)
+    assert lib.kda_chunk_bwd_workspace_size(2, 1000, 4, 128, 128, 2, 64, 1, ctypes.byref(ws)) == 0
+    assert lib.kda_chunk_bwd(FAKE, FAKE * 2, FAKE * 3, 1, FAKE * 4, 2, None, -5.0, FAKE * 5, H0,
+                             None, 2, 2, 1000, 4, 128, 128, 64, 1.0, FAKE * 10, None, FAKE * 11,
+                             FAKE * 12, FAKE * 13, FAKE * 14, FAKE * 15, None, WS, ws.value,
+                             None) == 0
+    got = launches()
+    assert [g[0] for g in got] == ["chunk_fwd_checkpoint", "chunk_bwd", "chunk_bwd"]
+    fwd, saved, full = got
+    # q, o, the final state, no order (dense), then the four checkpoint arrays
+    assert fwd[1][:4] == [FAKE, O, HT, 0]
+    assert fwd[2][:2] == [2, 4]
+    ckS, U, Vt, At = fwd[1][4:8]
+    for b in (saved, full):
+        assert [b[1][0], b[1][2], b[1][3], b[1][5]] == [ckS, U, Vt, At]
+        assert b[1][7] == H0
+    assert ckS == WS and len({ckS, U, Vt, At}) == 4
+    assert saved[2][0] == 1 and full[2][0] == 0       # the forward scan skipped / run
+    assert saved[2][1:3] == full[2][1:3]              # same slots, same sequences
