@@ -424,6 +424,9 @@ kda_status_t kda_chunk_bwd(const void* q, const void* k, const void* v, kda_dtyp
  * KDA_GATE_LOGITS with g_min >= -5.5, H <= 65535 (KDA_ERROR_NOT_SUPPORTED
  * otherwise); KDA_ERROR_INSUFFICIENT_WORKSPACE for a missing or short
  * bwd_workspace. o and final_state equal kda_chunk_fwd's unsplit results.
+ * Like kda_chunk_bwd, this call and kda_chunk_bwd_saved allocate nothing,
+ * memset nothing and synchronize nothing: the pair may be captured into a
+ * HIP graph.
  */
 kda_status_t kda_chunk_fwd_train(const void* q, const void* k, const void* v, kda_dtype_t dtype,
                                  const float* g, kda_gate_input_t gate_input, const float* A_log,

@@ -139,3 +139,52 @@ def test_captured_backward_replays(name, kw):
               f" (tol {TOL_BF16:g}); equal to eager: {same}", flush=True)
         assert same
         assert all(e <= TOL_BF16 for e in errs.values()), errs
+
+
+def test_captured_training_pair_replays():
+    """kda_chunk_fwd_train and kda_chunk_bwd_saved captured together (packed
+    sequences: both compute the longest-first order into the backward
+    workspace): every replay equals the eager pair bit for bit."""
+    print("\n[case] graph capture, training pair: packed 6 sequences H=2", flush=True)
+    from gated_delta_rule_92_amd import chunk_fwd_train
+    H, D = 2, 128
+    d = make_inputs(1, 0, H, D, D, torch.bfloat16, h0_std=0.02,
+                    lengths=[700, 0, 33, 1290, 64, 517], seed=55)
+    B, T = d["q"].shape[0], d["q"].shape[1]
+    N = d["cu_seqlens"].numel() - 1
+    gen = torch.Generator().manual_seed(56)
+    do = torch.randn(B, T, H, D, generator=gen).to(torch.bfloat16).cuda()
+    dhT = torch.randn(N, H, D, D, generator=gen).cuda()
+    dd = to_dev(d)
+    wsp = torch.zeros(bwd_workspace_size(B, T, H, D, D, N, 64, torch.bfloat16), dtype=torch.uint8,
+                      device="cuda")
+    ins = (dd["q"], dd["k"], dd["v"], dd["z"], dd["beta"])
+
+    def call():
+        o, hT, _ = chunk_fwd_train(*ins, dd["h0"], dd["cu_seqlens"], gate="logits",
+                                   bwd_workspace=wsp)
+        g = chunk_bwd(*ins, do, dd["h0"], dhT, dd["cu_seqlens"], gate="logits", workspace=wsp,
+                      saved=True)
+        return dict(o=o, hT=hT, **g)
+
+    eager = {n: t.clone() for n, t in call().items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = call()
+    torch.cuda.synchronize()
+    for replay in range(3):
+        for t in out.values():
+            t.fill_(float("nan"))
+        wsp.fill_(0xFF)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        same = {n: torch.equal(out[n], eager[n]) for n in eager}
+        print(f"  replay {replay}: equal to eager: {all(same.values())}", flush=True)
+        assert all(same.values()), same
