@@ -6,7 +6,9 @@ gate logits or per-token log-decay, with or without an initial state and a
 final-state gradient, output scale in [0.5, 1.5]. A second sweep draws long
 dense problems that kda_chunk_fwd runs as a context split. The same bar as
 the other parity tests: max|gpu - ref| / max|ref| <= 2e-2 (bf16) and 1e-4
-(fp32) per output array.
+(fp32) per output array. For bf16 d_k = d_v = 128 problems the training pair
+(kda_chunk_fwd_train, kda_chunk_bwd_saved) must also equal the plain calls bit
+for bit.
 """
 import numpy as np
 import pytest
@@ -91,6 +93,23 @@ def test_random_problem_forward_and_backward(seed):
     for n, e in errs.items():
         assert np.all(np.isfinite(got[n].double().cpu().numpy())), n
         assert e <= tol, (n, e)
+
+    if s["dtype"] == torch.bfloat16 and s["Dk"] == 128 and s["Dv"] == 128:
+        # the training pair (one pass for the forward and the backward's
+        # checkpoints, then the backward without its first scan) equals the
+        # plain calls bit for bit
+        from gated_delta_rule_92_amd import chunk_fwd_train
+        o2, h2, ws = chunk_fwd_train(dev(d["q"]), dev(d["k"]), dev(d["v"]), dev(g_in),
+                                     dev(d["beta"]), dev(d["h0"]), dev(d["cu_seqlens"]),
+                                     gate=s["gate"], scale=s["scale"])
+        got2 = chunk_bwd(dev(d["q"]), dev(d["k"]), dev(d["v"]), dev(g_in), dev(d["beta"]), dev(do),
+                         dev(d["h0"]), dev(dhT), dev(d["cu_seqlens"]), gate=s["gate"],
+                         scale=s["scale"], workspace=ws, saved=True)
+        torch.cuda.synchronize()
+        same = torch.equal(o2, o) and torch.equal(h2, hT) and \
+            all(torch.equal(got2[n], got[n]) for n in errs)
+        print(f"  training pair equal to the plain calls: {same}", flush=True)
+        assert same
 
 
 def _split_problem(seed):
