@@ -735,6 +735,41 @@ BwdLayout bwd_layout(int B, int T, int H, int Dk, int Dv, int N, kda_dtype_t dty
   return l;
 }
 
+// Context split of the backward's two scans, for dense sequences whose B*H
+// (sequence, head) chains leave compute units idle: the pieces kda_chunk_fwd
+// would take (equal pieces on 64-token chunks), after the base layout. Its
+// region holds the piece table and orders, the state maps M, the zero-start
+// final states b and the entry states (split_layout), then the maps
+// transposed, the pieces' zero-start initial-state gradients c and their
+// exit gradients.
+//   checkpoint scan: M, b of every piece (split pass), entry states chained
+//     from the initial state, then checkpoint mode over every piece from its
+//     entry state, writing the sequences' checkpoint slots;
+//   reverse scan: c of pieces 1..P-1 (reverse mode from zero, nothing
+//     stored), exit gradients chained from the final-state gradient down
+//     through M^T (per tile the reverse recurrence's linear part is the
+//     transpose of the forward one), then reverse mode over every piece from
+//     its exit gradient; piece 0 writes the initial-state gradient.
+struct BwdSplit {
+  int P = 1;
+  SplitPlan base;  // tables, M, b, entry states
+  size_t MT = 0, C = 0, X = 0, bytes = 0;
+};
+
+BwdSplit bwd_split(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype_t dtype) {
+  BwdSplit s;
+  const SplitPlan p = auto_split(B, T, H, Dk, Dv, chunk, dtype, false);
+  if (p.P <= 1) return s;
+  s.P = p.P;
+  s.base = split_layout(B, H, Dk, Dv, p.P);
+  const size_t pieces = (size_t)B * p.P;
+  s.MT = s.base.bytes;
+  s.C = s.MT + round_up(pieces * H * Dk * Dk * sizeof(float), kWorkspaceAlign);
+  s.X = s.C + round_up(pieces * H * Dk * Dv * sizeof(float), kWorkspaceAlign);
+  s.bytes = s.X + round_up(pieces * H * Dk * Dv * sizeof(float), kWorkspaceAlign);
+  return s;
+}
+
 // The checks kda_chunk_bwd, kda_chunk_bwd_saved and kda_chunk_fwd_train
 // share: sequences, shapes, gate, alignment, support and workspace size.
 kda_status_t check_bwd_args(const void* q, const void* k, const void* v, kda_dtype_t dtype,
@@ -811,6 +846,66 @@ kda_status_t chunk_bwd_impl(const void* q, const void* k, const void* v, kda_dty
   st = failure_reporting(&a.status, &a.spin_limit);
   if (st != KDA_SUCCESS) return st;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const BwdSplit sp = cu_seqlens ? BwdSplit{} : bwd_split(B, T, H, Dk, Dv, chunk, dtype);
+  if (sp.P > 1 && workspace_bytes >= l.bytes() + sp.bytes) {
+    char* sw = ws + l.bytes();
+    const int P = sp.P, nseq = s.N;
+    kda::SplitTables tab;
+    tab.table = reinterpret_cast<int32_t*>(sw);
+    tab.first = reinterpret_cast<int32_t*>(sw + sp.base.first);
+    tab.middle = reinterpret_cast<int32_t*>(sw + sp.base.middle);
+    tab.later = reinterpret_cast<int32_t*>(sw + sp.base.later);
+    tab.mapped = reinterpret_cast<int32_t*>(sw + sp.base.mapped);
+    float* Mm = reinterpret_cast<float*>(sw + sp.base.M);
+    float* bz = reinterpret_cast<float*>(sw + sp.base.b);
+    float* E = reinterpret_cast<float*>(sw + sp.base.starts);
+    float* MT = reinterpret_cast<float*>(sw + sp.MT);
+    float* C = reinterpret_cast<float*>(sw + sp.C);
+    float* X = reinterpret_cast<float*>(sw + sp.X);
+    hipError_t e = kda::launch_split_tables(tab, nullptr, nseq, T, P, 0, 0, chunk, hs);
+    // every piece as a unit (the piece table as packed sequences)
+    kda::ChunkArgs c{};
+    c.k = k; c.v = v; c.g = g; c.gate_mode = (int)gate_input;
+    c.A_log = A_log; c.g_min = g_min; c.beta = beta;
+    c.seqs.cu = tab.table; c.seqs.N = nseq * P; c.seqs.T = T; c.seqs.Ttot = s.Ttot;
+    c.H = H; c.Dk = Dk; c.Dv = Dv; c.scale = scale; c.bf16 = true;
+    c.status = a.status; c.spin_limit = a.spin_limit;
+    if (!saved) {
+      // the maps (and their transposes) of every piece, the entry states,
+      // then the checkpoints
+      kda::ChunkArgs z = c;
+      z.hT = Mm; z.hT2 = bz; z.hT3 = MT;
+      if (e == hipSuccess) e = kda::launch_chunk_split_pass(z, hs);
+      if (e == hipSuccess)
+        e = kda::launch_compose(Mm, bz, initial_state, 1, nseq, P, P, H, Dk, Dv, E, hs);
+      kda::ChunkArgs f = c;
+      f.h0 = E; f.ck_pieces = P;
+      f.ck_state = a.ckS; f.ck_u = a.U; f.ck_vt = a.Vt; f.ck_at = a.At;
+      if (e == hipSuccess) e = kda::launch_chunk_checkpoint(f, hs);
+    } else {
+      // the checkpoints are there: only the transposed maps
+      kda::ChunkArgs z = c;
+      z.hT3 = MT;
+      if (e == hipSuccess) e = kda::launch_chunk_transition(z, hs);
+    }
+    // reverse: pieces 1..P-1 from a zero exit gradient, then the exit
+    // gradients chained down from the final-state gradient, then every piece
+    kda::ChunkArgs r = c;
+    r.q = q; r.v = d_o;
+    kda::ChunkArgs rz = r;
+    rz.order = tab.later; rz.seqs.N = nseq * (P - 1); rz.hT = C;
+    if (e == hipSuccess) e = kda::launch_chunk_reverse(rz, hs);
+    if (e == hipSuccess)
+      e = kda::launch_compose(MT, C, d_final_state, 1, nseq, P, P, H, Dk, Dv, X, hs, true);
+    kda::ChunkArgs rf = r;
+    rf.h0 = X; rf.hT = d_initial_state; rf.hT_group = P; rf.ck_pieces = P;
+    rf.ck_state = a.ckdS; rf.ck_vt = a.dY;
+    if (e == hipSuccess) e = kda::launch_chunk_reverse(rf, hs);
+    a.skip_fwd_scan = true;
+    a.skip_rev_scan = true;
+    if (e == hipSuccess) e = kda::launch_chunk_bwd(a, true, Dk, Dv, slots, hs);
+    return launch_status(e);
+  }
   if (l.ord > 0 && cu_seqlens) {
     int32_t* order = reinterpret_cast<int32_t*>(ws + l.order());
     if (kda::launch_order(cu_seqlens, s.N, order, hs) != hipSuccess) return KDA_ERROR_LAUNCH_FAILURE;
@@ -827,7 +922,10 @@ kda_status_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv, i
   if (!bytes || B <= 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || N < 0 || chunk <= 0)
     return KDA_ERROR_INVALID_VALUE;
   if (dtype != KDA_FLOAT32 && dtype != KDA_BFLOAT16) return KDA_ERROR_INVALID_VALUE;
-  *bytes = bwd_layout(B, T, H, Dk, Dv, N, dtype).bytes();
+  // plus the split of the scans, when dense sequences of this shape take it
+  // (kda_chunk_bwd runs unsplit in a workspace without it)
+  const size_t split = N == B ? bwd_split(B, T, H, Dk, Dv, chunk, dtype).bytes : 0;
+  *bytes = bwd_layout(B, T, H, Dk, Dv, N, dtype).bytes() + split;
   return KDA_SUCCESS;
 }
 

@@ -1015,7 +1015,9 @@ hipError_t launch_bwd_t(const BwdArgs& a, long slots, hipStream_t stream) {
   } else {
     hipLaunchKernelGGL((bwd_fwd_scan<T, DK, DV>), dim3(units), dim3(NTH), 0, stream, a);
   }
-  if (std::is_same<T, __bf16>::value && chunk_pipe_supported(true, DK, DV, 64)) {
+  if (a.skip_rev_scan) {
+    if (!pipe) return hipErrorInvalidValue;
+  } else if (pipe) {
     // the pipelined kernel in reverse mode: same checkpoints, dY and dS_0
     ChunkArgs c;
     c.q = a.q; c.k = a.k; c.v = a.dO; c.g = a.g; c.gate_mode = a.gate;

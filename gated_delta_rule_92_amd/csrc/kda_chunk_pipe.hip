@@ -92,6 +92,8 @@ static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 static_assert(sT - sKtT >= PT * PDK * 4 + PT * PDK * 2, "position-pair scratch fits in KtT and VT");
 
 __device__ __forceinline__ float ex2(float x) { return fast_exp2(x); }
+// Bit pattern of a float vector passed by value (see float_bits).
+__device__ __forceinline__ i32x4 vec_bits(f32x4 x) { return __builtin_bit_cast(i32x4, x); }
 
 __device__ __forceinline__ int lds_load_relaxed(int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -728,7 +730,11 @@ __global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : 
     // checkpoint and reverse modes: first 64-token slot of this sequence
     long ckbase = 0;
     if constexpr (CKPT || REV)
-      ckbase = a.seqs.cu ? (long)(a.seqs.cu[n] / 64) + n : (long)n * ((a.seqs.T + 63) / 64);
+      ckbase = a.ck_pieces > 0
+                   // a piece of a dense sequence: that sequence's slots
+                   ? (long)(n / a.ck_pieces) * ((a.seqs.T + 63) / 64) +
+                         (bos - (long)a.seqs.cu[(n / a.ck_pieces) * a.ck_pieces]) / 64
+                   : a.seqs.cu ? (long)(a.seqs.cu[n] / 64) + n : (long)n * ((a.seqs.T + 63) / 64);
     const int ckvoff = (4 * g4 + (odd ? 1 : 0)) * (PDV * 2) + (vc0 + (m & ~1)) * 2;
     // gated epilogue: this lane's norm weights (columns vc0 + 16b + m) and the
     // gate logits of its rows 4g4+e, loaded one tile ahead
@@ -846,7 +852,8 @@ __global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : 
       // in place (independent of the products, so it overlaps them)
       frag Sf[NCT][CNTV];
       if constexpr (REV) {
-        if (tile % 4 == 3 || tile == nsteps - 1) {
+        // (no checkpoint array: a pass that wants only the initial-state gradient)
+        if (a.ck_state && (tile % 4 == 3 || tile == nsteps - 1)) {
           const __amdgpu_buffer_rsrc_t rsc = make_rsrc(
               static_cast<__bf16*>(a.ck_state) + ((size_t)(ckbase + tile / 4) * H + h) * PDK * PDV,
               PDK * PDV * 2);
@@ -907,7 +914,7 @@ __global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : 
         for (int b = 0; b < CNTV; ++b) {
           const f32x4 dv = M::k16(aq, dof[b], acc[b]);
           const f32x4 dy = M::k16(tf, M::make(dv), f32x4{0.f, 0.f, 0.f, 0.f});
-          store_pairs(dy, rsy, ovoff2, rowo, 32 * b);
+          if (a.ck_vt) store_pairs(dy, rsy, ovoff2, rowo, 32 * b);
           const frag nb = M::make_neg(dy * bb);
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) S[ct][b] = M::k32(ktf[ct], kgtf[ct], dof[b], nb, S[ct][b]);
@@ -1008,8 +1015,8 @@ __global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : 
     size_t hbase = sbase;
     if (a.hT_group > 0) {
       // pieces of a context split: only the last piece of each sequence
-      // writes, to its sequence's slot
-      if (n % a.hT_group != a.hT_group - 1) hT = nullptr;
+      // (reverse mode: the first) writes, to its sequence's slot
+      if (n % a.hT_group != (REV ? 0 : a.hT_group - 1)) hT = nullptr;
       hbase = ((size_t)(n / a.hT_group) * H + h) * PDK * PDV;
     }
     if (hT) {
@@ -1022,6 +1029,20 @@ __global__ void __launch_bounds__(MODE == kModeSplitPass ? PNTHR + 64 * NCONS : 
           for (int e = 0; e < 4; ++e)
             __builtin_amdgcn_raw_buffer_store_b32(float_bits(S[ct][b][e]), rs, svoff,
                                                   ((16 * ct + e) * PDV + 16 * b) * 4, 0);
+    }
+    if constexpr (DUAL || TRANS) {
+      if (tmap && a.hT3) {
+        // the map transposed, M^T[col][row]: a lane's four rows 4g4..4g4+3 of
+        // column vc0 + 16b + m are consecutive there
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.hT3 + hbase, PDK * PDV * 4);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int b = 0; b < CNTV; ++b)
+            __builtin_amdgcn_raw_buffer_store_b128(vec_bits(S[ct][b]), rs,
+                                                   ((vc0 + m) * PDK + 4 * g4) * 4,
+                                                   (16 * b * PDK + 16 * ct) * 4, 0);
+      }
     }
   }
 }

@@ -112,13 +112,16 @@ __device__ __forceinline__ void compose_lds_barrier() {
 
 __global__ void __launch_bounds__(kCompose128Threads) compose128_kernel(
     const float* __restrict__ M, const float* __restrict__ b, const float* S0, int s0_stride, int P,
-    int stride, int H, int Dv, float* starts) {
+    int stride, int H, int Dv, float* starts, int rev) {
   // ping-pong: step p reads slice p & 1 and writes slice (p + 1) & 1
   __shared__ __attribute__((aligned(16))) float curT2[2][kComposeCols][kCT];
   const int sh = blockIdx.x;  // sequence * H + head
   const int seq = sh / H, h = sh % H;
   const int c0 = blockIdx.y * kComposeCols;
   const int tid = threadIdx.x, lane = tid & 63;
+  // rev: step p takes M, b of index P - 1 - p and entry p goes to index
+  // P - 1 - p (a chain run from the last index down)
+  auto at = [&](int p) { return rev ? P - 1 - p : p; };
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   for (int i = tid; i < kComposeCols * kC128; i += kCompose128Threads) {
@@ -138,7 +141,7 @@ __global__ void __launch_bounds__(kCompose128Threads) compose128_kernel(
     for (int p = 0; p < P; ++p) {
       if (p > 0) compose_lds_barrier();
       const float (*curT)[kCT] = curT2[p & 1];
-      float* out = starts + (((size_t)seq * stride + p) * H + h) * (size_t)kC128 * Dv;
+      float* out = starts + (((size_t)seq * stride + at(p)) * H + h) * (size_t)kC128 * Dv;
 #pragma unroll
       for (int j = 0; j < kC128 / 16; ++j) {
         const int row = rq + 16 * j;
@@ -165,7 +168,7 @@ __global__ void __launch_bounds__(kCompose128Threads) compose128_kernel(
   // slice and of b, so such a column computes values that are never stored.
   const int bcol = c0 + n < Dv ? c0 + n : c0;
   auto load = [&](int p, ComposeSet& x) {
-    const size_t sp = (size_t)seq * stride + min(p, P - 2);
+    const size_t sp = (size_t)seq * stride + at(min(p, P - 2));
     const float* Mp = M + (sp * H + h) * (size_t)kC128 * kC128 + (size_t)(row0 + n) * kC128 + 4 * g;
 #pragma unroll
     for (int i = 0; i < 8; ++i) x.m[i] = *reinterpret_cast<const f32x4*>(Mp + 16 * i);
@@ -253,13 +256,13 @@ hipError_t launch_split_tables(const SplitTables& t, const int32_t* cu, int nseq
 
 hipError_t launch_compose(const float* M, const float* b, const float* S0, int s0_stride, int nseq,
                           int P, int stride, int H, int Dk, int Dv, float* starts,
-                          hipStream_t stream) {
+                          hipStream_t stream, bool rev) {
   if (nseq == 0 || P == 0 || H == 0) return hipSuccess;
-  if (Dk > kComposeMaxDk) return hipErrorInvalidValue;
+  if (Dk > kComposeMaxDk || (rev && Dk != kC128)) return hipErrorInvalidValue;
   dim3 grid((unsigned)(nseq * H), (unsigned)((Dv + kComposeCols - 1) / kComposeCols));
   if (Dk == kC128) {
     hipLaunchKernelGGL(compose128_kernel, grid, dim3(kCompose128Threads), 0, stream, M, b, S0,
-                       s0_stride, P, stride, H, Dv, starts);
+                       s0_stride, P, stride, H, Dv, starts, rev ? 1 : 0);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(compose_kernel, grid, dim3(kComposeThreads), 0, stream, M, b, S0, s0_stride, P,

@@ -81,10 +81,16 @@ struct ChunkArgs {
   void* ck_vt = nullptr;
   float* ck_at = nullptr;  // checkpoint mode: A_kk / beta per tile row, fp32 [Ttot, H, 16]
   float* hT2 = nullptr;    // split pass: zero-start final states [N, H, Dk, Dv]
+  float* hT3 = nullptr;    // split pass, transition: the maps transposed [N, H, Dk, Dk], or nullptr
   // pipelined kernel, > 0: the N units are N / hT_group sequences of hT_group
-  // consecutive pieces, and only each sequence's last piece writes its final
-  // state, to hT[n / hT_group]
+  // consecutive pieces, and only each sequence's last piece (reverse mode: its
+  // first) writes its final state, to hT[n / hT_group]
   int hT_group = 0;
+  // checkpoint and reverse modes, > 0: the N units are pieces of dense
+  // sequences of seqs.T tokens, ck_pieces per sequence, seqs.cu the piece
+  // table (each piece starting on a 64-token chunk of its sequence); the
+  // checkpoints go to the sequences' slots (n ceil(T/64) + chunk)
+  int ck_pieces = 0;
   // pipelined kernel, > 0: unit n starts from h0[n / h0_group] (the initial
   // state of a split sequence's first piece)
   int h0_group = 0;
@@ -132,9 +138,12 @@ hipError_t launch_gated_rmsnorm(const void* o, const void* z, bool bf16, const f
 // sequence s is entry s * stride + p of M, b and starts ([*, H, Dk, Dk] and
 // [*, H, Dk, Dv]) and S0 is entry s * s0_stride of S0 (nullptr: zeros). S0
 // may be starts[0] itself: it is read before anything is written.
+// rev (Dk = 128 only): the chain runs from the last index down, entry p of
+// the chain at index P - 1 - p: starts[P-1] = S0 and
+// starts[q-1] = M_q starts[q] + b_q for q = P-1 .. 1.
 hipError_t launch_compose(const float* M, const float* b, const float* S0, int s0_stride, int nseq,
                           int P, int stride, int H, int Dk, int Dv, float* starts,
-                          hipStream_t stream);
+                          hipStream_t stream, bool rev = false);
 // Piece table and unit orders of a context split of nseq sequences (dense of
 // T tokens when cu is null, else packed by cu) into P >= 2 pieces each.
 // Pieces: with L0 > 0 (dense only), piece 0 takes the first L0 tokens and
@@ -205,8 +214,12 @@ struct BwdArgs {
   float* At = nullptr;  // [Ttot, H, 16] row r of each tile's A~ = A_kk / beta
                         // (strictly lower part; zeros elsewhere)
   // ckS, U, Vt and At already hold what the forward scan writes (a training
-  // forward wrote them): the forward scan is not launched
+  // forward, or the caller's own split scans, wrote them): the forward scan is
+  // not launched
   bool skip_fwd_scan = false;
+  // ckdS, dY and dh0 already hold what the reverse scan writes (the caller's
+  // split scans): the reverse scan is not launched
+  bool skip_rev_scan = false;
 };
 inline bool chunk_bwd_supported(int Dk, int Dv) {
   return (Dk == 64 || Dk == 128) && (Dv == 64 || Dv == 128);

@@ -127,6 +127,11 @@ hipError_t record_chunk(const char* name, const kda::ChunkArgs& a) {
   return record(name, {a.q, a.h0, a.hT, a.hT2, a.o, a.order, a.seqs.cu, a.v},
                 {a.seqs.N, a.h0_group, a.hT_group, 0});
 }
+// checkpoint, reverse and transition launches (the backward's scans)
+hipError_t record_scan(const char* name, const kda::ChunkArgs& a) {
+  return record(name, {a.q, a.h0, a.hT, a.hT3, a.order, a.seqs.cu, a.ck_state, a.ck_vt},
+                {a.seqs.N, a.hT_group, a.ck_pieces, a.seqs.T});
+}
 }  // namespace
 
 namespace kda {
@@ -136,24 +141,26 @@ hipError_t launch_gate(const float*, const float*, float, Seqs, int, int, int, f
 hipError_t launch_recurrent(const RecurrentArgs&, hipStream_t) { return record("recurrent"); }
 hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t) { return record_chunk("chunk_pipe", a); }
 hipError_t launch_chunk_transition(const ChunkArgs& a, hipStream_t) {
-  return record_chunk("chunk_transition", a);
+  return record_scan("chunk_transition", a);
 }
 hipError_t launch_chunk_split_pass(const ChunkArgs& a, hipStream_t) {
   return record_chunk("chunk_split_pass", a);
 }
-hipError_t launch_chunk_checkpoint(const ChunkArgs&, hipStream_t) { return record("chunk_checkpoint"); }
+hipError_t launch_chunk_checkpoint(const ChunkArgs& a, hipStream_t) {
+  return record_scan("chunk_checkpoint", a);
+}
 hipError_t launch_chunk_fwd_checkpoint(const ChunkArgs& a, hipStream_t) {
   return record("chunk_fwd_checkpoint", {a.q, a.o, a.hT, a.order, a.ck_state, a.ck_u, a.ck_vt, a.ck_at},
                 {a.seqs.N, a.H, 0, 0});
 }
-hipError_t launch_chunk_reverse(const ChunkArgs&, hipStream_t) { return record("chunk_reverse"); }
+hipError_t launch_chunk_reverse(const ChunkArgs& a, hipStream_t) { return record_scan("chunk_reverse", a); }
 hipError_t launch_gated_rmsnorm(const void*, const void*, bool, const float*, float, long, int, void*,
                                 hipStream_t) {
   return record("gated_rmsnorm");
 }
 hipError_t launch_compose(const float* M, const float* b, const float* S0, int s0_stride, int nseq,
-                          int P, int stride, int, int, int, float* starts, hipStream_t) {
-  return record("compose", {M, b, S0, starts}, {nseq, P, stride, s0_stride});
+                          int P, int stride, int, int, int, float* starts, hipStream_t, bool rev) {
+  return record(rev ? "compose_rev" : "compose", {M, b, S0, starts}, {nseq, P, stride, s0_stride});
 }
 hipError_t launch_split_tables(const SplitTables& t, const int32_t* cu, int nseq, int, int P, int L0,
                                int Lp, int, hipStream_t) {
@@ -163,7 +170,7 @@ hipError_t launch_split_tables(const SplitTables& t, const int32_t* cu, int nseq
 hipError_t launch_chunk_fused(const ChunkArgs&, hipStream_t) { return record("chunk_fused"); }
 hipError_t launch_chunk_bwd(const BwdArgs& a, bool, int, int, long slots, hipStream_t) {
   return record("chunk_bwd", {a.ckS, a.ckdS, a.U, a.Vt, a.dY, a.At, a.order, a.h0},
-                {a.skip_fwd_scan ? 1 : 0, (int)slots, a.N, 0});
+                {a.skip_fwd_scan ? 1 : 0, (int)slots, a.N, a.skip_rev_scan ? 1 : 0});
 }
 hipError_t launch_gate_bwd(const float*, const float*, float, const float*, long, int, int, float*,
                            float*, hipStream_t) {

@@ -528,3 +528,74 @@ def test_training_forward_writes_what_the_saved_backward_reads():
     assert ckS == WS and len({ckS, U, Vt, At}) == 4
     assert saved[2][0] == 1 and full[2][0] == 0       # the forward scan skipped / run
     assert saved[2][1:3] == full[2][1:3]              # same slots, same sequences
+
+
+def test_split_backward_launches_what_it_should():
+    """Only in the host-check build, on a 256-CU stand-in device: kda_chunk_bwd
+    on long256k (B=1, T=262144, H=32: 32 chains) splits both scans into the
+    8 equal pieces kda_chunk_fwd would take. Launch by launch: the piece table;
+    the split pass over every piece (maps, zero-start states, maps transposed);
+    the entry states from the initial state; checkpoint mode over every piece
+    from its entry state into the sequence's slots; reverse mode over pieces
+    1..7 from zero, storing nothing but each piece's initial-state gradient;
+    the exit gradients chained down from the final-state gradient through the
+    transposed maps; reverse mode over every piece from its exit gradient,
+    piece 0 writing the initial-state gradient; then the gradient kernel with
+    both scans skipped. A workspace without the split region runs unsplit."""
+    lib = _lib.load()
+    if not hasattr(lib, "kda_host_check_build"):
+        pytest.skip("needs the host-check build (tests/test_sanitizers_cpu.py)")
+    lib.kda_host_check_set_compute_units.argtypes = [ctypes.c_int]
+    lib.kda_host_check_set_compute_units(256)
+    log = (_Launch * 64).in_dll(lib, "kda_host_check_log")
+    n = ctypes.c_int.in_dll(lib, "kda_host_check_log_len")
+    T, H, D, P = 262144, 32, 128, 8
+    Q, K, V, G, BETA, H0, DO, DHT, DH0, WS = (FAKE * (i + 1) for i in range(10))
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    ck = up(4097 * H * D * D * 2)        # slots: max(4096 dense, 4096 + 1 packed)
+    tok = up(T * H * D * 2)
+    at = up(T * H * 16 * 4)
+    base = 2 * ck + 3 * tok + at
+    off = _split_offsets(1, P)
+    state = up(P * H * D * D * 4)
+    split_base = off["starts"] + state
+    MT, C, X = split_base, split_base + state, split_base + 2 * state
+    ws = ctypes.c_size_t(0)
+    assert lib.kda_chunk_bwd_workspace_size(1, T, H, D, D, 1, 64, 1, ctypes.byref(ws)) == 0
+    assert ws.value == base + X + state
+
+    def call(ws_bytes):
+        lib.kda_host_check_log_clear()
+        assert lib.kda_chunk_bwd(Q, K, V, 1, G, 2, None, -5.0, BETA, H0, None, 1, 1, T, H, D, D, 64,
+                                 1.0, DO, DHT, FAKE * 11, FAKE * 12, FAKE * 13, FAKE * 14,
+                                 FAKE * 15, DH0, WS, ws_bytes, None) == 0
+        return [(log[i].name.decode(), [p or 0 for p in log[i].ptr], list(log[i].val))
+                for i in range(n.value)]
+
+    got = call(ws.value)
+    assert [g[0] for g in got] == ["split_tables", "chunk_split_pass", "compose", "chunk_checkpoint",
+                                   "chunk_reverse", "compose_rev", "chunk_reverse", "chunk_bwd"]
+    S = WS + base  # the split region
+    assert got[0][1][0] == S and got[0][2] == [1, P, 0, 0]
+    # split pass: no q, h0 or o; maps and zero-start states of all 8 pieces
+    assert got[1][1] == [0, 0, S + off["M"], S + off["b"], 0, 0, S, V] and got[1][2][0] == P
+    assert got[2][1][:4] == [S + off["M"], S + off["b"], H0, S + off["starts"]]
+    assert got[2][2] == [1, P, P, 1]
+    # checkpoints: from the entry states, every piece, into the sequence's slots
+    assert got[3][1] == [0, S + off["starts"], 0, 0, 0, S, WS, WS + 2 * ck + tok]
+    assert got[3][2] == [P, 0, P, T]
+    # pieces 1..7 from zero: only their initial-state gradients, nothing stored
+    assert got[4][1] == [Q, 0, S + C, 0, S + off["later"], S, 0, 0]
+    assert got[4][2] == [P - 1, 0, 0, T]
+    # exit gradients from the final-state gradient, down through M^T
+    assert got[5][1][:4] == [S + MT, S + C, DHT, S + X] and got[5][2] == [1, P, P, 1]
+    # every piece from its exit gradient; piece 0 writes dh0; dS' and dY stored
+    assert got[6][1] == [Q, S + X, DH0, 0, 0, S, WS + ck, WS + 2 * ck + 2 * tok]
+    assert got[6][2] == [P, P, P, T]
+    # the gradient kernel alone
+    assert got[7][2][0] == 1 and got[7][2][3] == 1
+
+    # a workspace of the base layout only: the scans run unsplit
+    got = call(base)
+    assert [g[0] for g in got] == ["chunk_bwd"]
+    assert got[0][2][0] == 0 and got[0][2][3] == 0
