@@ -770,6 +770,56 @@ BwdSplit bwd_split(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype_t d
   return s;
 }
 
+// Addresses in a backward split region that starts at `sw`.
+struct BwdSplitPtrs {
+  kda::SplitTables tab;
+  float *M, *b, *E, *MT, *C, *X;
+};
+
+BwdSplitPtrs bwd_split_ptrs(const BwdSplit& sp, char* sw) {
+  BwdSplitPtrs p;
+  p.tab.table = reinterpret_cast<int32_t*>(sw);
+  p.tab.first = reinterpret_cast<int32_t*>(sw + sp.base.first);
+  p.tab.middle = reinterpret_cast<int32_t*>(sw + sp.base.middle);
+  p.tab.later = reinterpret_cast<int32_t*>(sw + sp.base.later);
+  p.tab.mapped = reinterpret_cast<int32_t*>(sw + sp.base.mapped);
+  p.M = reinterpret_cast<float*>(sw + sp.base.M);
+  p.b = reinterpret_cast<float*>(sw + sp.base.b);
+  p.E = reinterpret_cast<float*>(sw + sp.base.starts);
+  p.MT = reinterpret_cast<float*>(sw + sp.MT);
+  p.C = reinterpret_cast<float*>(sw + sp.C);
+  p.X = reinterpret_cast<float*>(sw + sp.X);
+  return p;
+}
+
+// Launch arguments of every piece of a split as a unit (the piece table as
+// packed sequences), with the inputs every scan reads.
+kda::ChunkArgs piece_args(const BwdSplitPtrs& p, int nseq, int P, int T, long Ttot, int H, int Dk,
+                          int Dv, const void* k, const void* v, const float* g, int gate_mode,
+                          const float* A_log, float g_min, const float* beta, float scale,
+                          unsigned int* status, int spin_limit) {
+  kda::ChunkArgs c{};
+  c.k = k; c.v = v; c.g = g; c.gate_mode = gate_mode;
+  c.A_log = A_log; c.g_min = g_min; c.beta = beta;
+  c.seqs.cu = p.tab.table; c.seqs.N = nseq * P; c.seqs.T = T; c.seqs.Ttot = Ttot;
+  c.H = H; c.Dk = Dk; c.Dv = Dv; c.scale = scale; c.bf16 = true;
+  c.status = status; c.spin_limit = spin_limit;
+  return c;
+}
+
+// The forward direction of a split: the maps (and their transposes) and
+// zero-start final states of every piece, then the entry states chained
+// from the initial state.
+hipError_t split_forward_maps(const kda::ChunkArgs& c, const BwdSplitPtrs& p, int nseq, int P,
+                              const float* initial_state, hipStream_t hs) {
+  kda::ChunkArgs z = c;
+  z.hT = p.M; z.hT2 = p.b; z.hT3 = p.MT;
+  hipError_t e = kda::launch_chunk_split_pass(z, hs);
+  if (e == hipSuccess)
+    e = kda::launch_compose(p.M, p.b, initial_state, 1, nseq, P, P, c.H, c.Dk, c.Dv, p.E, hs);
+  return e;
+}
+
 // The checks kda_chunk_bwd, kda_chunk_bwd_saved and kda_chunk_fwd_train
 // share: sequences, shapes, gate, alignment, support and workspace size.
 kda_status_t check_bwd_args(const void* q, const void* k, const void* v, kda_dtype_t dtype,
@@ -848,57 +898,31 @@ kda_status_t chunk_bwd_impl(const void* q, const void* k, const void* v, kda_dty
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const BwdSplit sp = cu_seqlens ? BwdSplit{} : bwd_split(B, T, H, Dk, Dv, chunk, dtype);
   if (sp.P > 1 && workspace_bytes >= l.bytes() + sp.bytes) {
-    char* sw = ws + l.bytes();
     const int P = sp.P, nseq = s.N;
-    kda::SplitTables tab;
-    tab.table = reinterpret_cast<int32_t*>(sw);
-    tab.first = reinterpret_cast<int32_t*>(sw + sp.base.first);
-    tab.middle = reinterpret_cast<int32_t*>(sw + sp.base.middle);
-    tab.later = reinterpret_cast<int32_t*>(sw + sp.base.later);
-    tab.mapped = reinterpret_cast<int32_t*>(sw + sp.base.mapped);
-    float* Mm = reinterpret_cast<float*>(sw + sp.base.M);
-    float* bz = reinterpret_cast<float*>(sw + sp.base.b);
-    float* E = reinterpret_cast<float*>(sw + sp.base.starts);
-    float* MT = reinterpret_cast<float*>(sw + sp.MT);
-    float* C = reinterpret_cast<float*>(sw + sp.C);
-    float* X = reinterpret_cast<float*>(sw + sp.X);
-    hipError_t e = kda::launch_split_tables(tab, nullptr, nseq, T, P, 0, 0, chunk, hs);
-    // every piece as a unit (the piece table as packed sequences)
-    kda::ChunkArgs c{};
-    c.k = k; c.v = v; c.g = g; c.gate_mode = (int)gate_input;
-    c.A_log = A_log; c.g_min = g_min; c.beta = beta;
-    c.seqs.cu = tab.table; c.seqs.N = nseq * P; c.seqs.T = T; c.seqs.Ttot = s.Ttot;
-    c.H = H; c.Dk = Dk; c.Dv = Dv; c.scale = scale; c.bf16 = true;
-    c.status = a.status; c.spin_limit = a.spin_limit;
+    const BwdSplitPtrs p = bwd_split_ptrs(sp, ws + l.bytes());
+    hipError_t e = kda::launch_split_tables(p.tab, nullptr, nseq, T, P, 0, 0, chunk, hs);
+    const kda::ChunkArgs c = piece_args(p, nseq, P, T, s.Ttot, H, Dk, Dv, k, v, g, (int)gate_input,
+                                        A_log, g_min, beta, scale, a.status, a.spin_limit);
     if (!saved) {
-      // the maps (and their transposes) of every piece, the entry states,
-      // then the checkpoints
-      kda::ChunkArgs z = c;
-      z.hT = Mm; z.hT2 = bz; z.hT3 = MT;
-      if (e == hipSuccess) e = kda::launch_chunk_split_pass(z, hs);
-      if (e == hipSuccess)
-        e = kda::launch_compose(Mm, bz, initial_state, 1, nseq, P, P, H, Dk, Dv, E, hs);
+      // the maps, the entry states, then the checkpoints (kda_chunk_fwd_train
+      // took the same split and left all of these)
+      if (e == hipSuccess) e = split_forward_maps(c, p, nseq, P, initial_state, hs);
       kda::ChunkArgs f = c;
-      f.h0 = E; f.ck_pieces = P;
+      f.h0 = p.E; f.ck_pieces = P;
       f.ck_state = a.ckS; f.ck_u = a.U; f.ck_vt = a.Vt; f.ck_at = a.At;
       if (e == hipSuccess) e = kda::launch_chunk_checkpoint(f, hs);
-    } else {
-      // the checkpoints are there: only the transposed maps
-      kda::ChunkArgs z = c;
-      z.hT3 = MT;
-      if (e == hipSuccess) e = kda::launch_chunk_transition(z, hs);
     }
     // reverse: pieces 1..P-1 from a zero exit gradient, then the exit
     // gradients chained down from the final-state gradient, then every piece
     kda::ChunkArgs r = c;
     r.q = q; r.v = d_o;
     kda::ChunkArgs rz = r;
-    rz.order = tab.later; rz.seqs.N = nseq * (P - 1); rz.hT = C;
+    rz.order = p.tab.later; rz.seqs.N = nseq * (P - 1); rz.hT = p.C;
     if (e == hipSuccess) e = kda::launch_chunk_reverse(rz, hs);
     if (e == hipSuccess)
-      e = kda::launch_compose(MT, C, d_final_state, 1, nseq, P, P, H, Dk, Dv, X, hs, true);
+      e = kda::launch_compose(p.MT, p.C, d_final_state, 1, nseq, P, P, H, Dk, Dv, p.X, hs, true);
     kda::ChunkArgs rf = r;
-    rf.h0 = X; rf.hT = d_initial_state; rf.hT_group = P; rf.ck_pieces = P;
+    rf.h0 = p.X; rf.hT = d_initial_state; rf.hT_group = P; rf.ck_pieces = P;
     rf.ck_state = a.ckdS; rf.ck_vt = a.dY;
     if (e == hipSuccess) e = kda::launch_chunk_reverse(rf, hs);
     a.skip_fwd_scan = true;
@@ -985,6 +1009,24 @@ kda_status_t kda_chunk_fwd_train(const void* q, const void* k, const void* v, kd
   st = failure_reporting(&a.status, &a.spin_limit);
   if (st != KDA_SUCCESS) return st;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  // dense sequences with few (sequence, head) chains: the split kda_chunk_bwd
+  // takes in this workspace, whose maps, transposed maps and entry states
+  // kda_chunk_bwd_saved then reuses; every piece runs from its entry state
+  // with output and checkpoints, the last one writing the final state
+  const BwdSplit sp = cu_seqlens ? BwdSplit{} : bwd_split(B, T, H, Dk, Dv, chunk, dtype);
+  if (sp.P > 1 && bwd_workspace_bytes >= l.bytes() + sp.bytes) {
+    const int P = sp.P, nseq = s.N;
+    const BwdSplitPtrs p = bwd_split_ptrs(sp, ws + l.bytes());
+    hipError_t e = kda::launch_split_tables(p.tab, nullptr, nseq, T, P, 0, 0, chunk, hs);
+    const kda::ChunkArgs c = piece_args(p, nseq, P, T, s.Ttot, H, Dk, Dv, k, v, g, (int)gate_input,
+                                        A_log, g_min, beta, scale, a.status, a.spin_limit);
+    if (e == hipSuccess) e = split_forward_maps(c, p, nseq, P, initial_state, hs);
+    kda::ChunkArgs f = a;
+    f.seqs = c.seqs;
+    f.h0 = p.E; f.hT_group = P; f.ck_pieces = P;
+    if (e == hipSuccess) e = kda::launch_chunk_fwd_checkpoint(f, hs);
+    return launch_status(e);
+  }
   if (l.ord > 0 && cu_seqlens) {
     // the same longest-first order the backward's scans take (it only sets
     // the order in which units start; kda_chunk_bwd_saved computes it again)

@@ -357,7 +357,14 @@ kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v, kda
  * per-token [B*T, H, Dv] arrays, all in the input dtype, one fp32
  * [B*T, H, 16] array, and, for packed sequences (B == 1, 1 < N <= 8192), N
  * int32 (the longest-first order in which the scans take the sequences);
- * slots = max(B * ceil(T/C), B*T/C + N).
+ * slots = max(B * ceil(T/C), B*T/C + N). For dense bf16 sequences
+ * (N == B) with Dk = Dv = 128 whose B*H (sequence, head) chains leave most
+ * compute units idle, it adds the context split of the two scans (the P
+ * pieces per sequence that kda_chunk_fwd would take): a piece table and six
+ * fp32 [B*P, H, 128, 128] arrays (state maps, their transposes, zero-start
+ * final states, entry states, zero-start initial-state gradients, exit
+ * gradients). kda_chunk_bwd, kda_chunk_bwd_saved and kda_chunk_fwd_train
+ * split exactly when the workspace they are given holds that region.
  */
 kda_status_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv, int N,
                                           int chunk, kda_dtype_t dtype, size_t* bytes);
@@ -371,7 +378,11 @@ kda_status_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv, i
  * that recurrence, evaluated on 16-token tiles: a forward scan stores the
  * state entering every 64-token chunk (16 for fp32), a reverse scan the
  * state gradient leaving it, and every chunk then forms its gradients on its
- * own, rebuilding the states inside it.
+ * own, rebuilding the states inside it. Both scans are linear in the state
+ * (in its gradient): with the split region in the workspace, each runs over
+ * pieces of every sequence in parallel, from entry states (exit gradients)
+ * chained through the pieces' maps (their transposes); the gradients equal
+ * the unsplit ones up to rounding.
  *
  * Inputs as for kda_chunk_fwd (same layouts, dtype, gate, scale, sequences);
  * gate_input is KDA_GATE_LOGDECAY (g = log-decay) or KDA_GATE_LOGITS (g = z,
@@ -416,14 +427,18 @@ kda_status_t kda_chunk_bwd(const void* q, const void* k, const void* v, kda_dtyp
  * forward and backward are thereby one pass over the inputs shorter; the
  * forward writes 1088 more bytes per token·head (bf16, d = 128).
  *
- * Arguments as for kda_chunk_fwd (no workspace of its own, no automatic
- * context split: one chain per (sequence, head)), plus bwd_workspace and its
- * size (>= kda_chunk_bwd_workspace_size(B, T, H, Dk, Dv, N, 64, dtype); 256-byte
- * aligned). o is required; final_state may be NULL.
+ * Arguments as for kda_chunk_fwd (no workspace of its own), plus
+ * bwd_workspace and its size (>= kda_chunk_bwd_workspace_size(B, T, H, Dk,
+ * Dv, N, 64, dtype); 256-byte aligned). o is required; final_state may be
+ * NULL. When the workspace holds the backward's split region, the forward
+ * runs over the same pieces (maps, entry states, then every piece with
+ * output and checkpoints) and leaves the maps' transposes there for
+ * kda_chunk_bwd_saved.
  * Supported: bf16, Dk = Dv = 128, chunk = 64, gate_input KDA_GATE_LOGDECAY or
  * KDA_GATE_LOGITS with g_min >= -5.5, H <= 65535 (KDA_ERROR_NOT_SUPPORTED
  * otherwise); KDA_ERROR_INSUFFICIENT_WORKSPACE for a missing or short
- * bwd_workspace. o and final_state equal kda_chunk_fwd's unsplit results.
+ * bwd_workspace. o and final_state equal kda_chunk_fwd's unsplit results
+ * (split: up to rounding).
  * Like kda_chunk_bwd, this call and kda_chunk_bwd_saved allocate nothing,
  * memset nothing and synchronize nothing: the pair may be captured into a
  * HIP graph.
@@ -441,7 +456,9 @@ kda_status_t kda_chunk_fwd_train(const void* q, const void* k, const void* v, kd
  * kda_chunk_fwd_train has filled from the same q, k, v, g, gate_input, A_log,
  * g_min, beta, initial_state, cu_seqlens and shapes: its first scan is not
  * run, the checkpoints, U, V~ and A~ are read from the workspace, and the
- * gradients equal kda_chunk_bwd's bit for bit. The workspace must not have
+ * gradients equal kda_chunk_bwd's bit for bit. workspace_bytes must be the
+ * size kda_chunk_fwd_train was given (both take the split from it). The
+ * workspace must not have
  * been used by another call in between (the results are otherwise undefined;
  * nothing checks it). Arguments, outputs and errors as for kda_chunk_bwd;
  * KDA_ERROR_NOT_SUPPORTED outside kda_chunk_fwd_train's shapes (bf16,

@@ -30,6 +30,7 @@ struct KdaHostCheckLaunch {
   char name[24];
   const void* ptr[8];
   int val[4];
+  const void* ext[4];  // more pointers, for the launches that need them
 };
 KdaHostCheckLaunch kda_host_check_log[64];
 int kda_host_check_log_len = 0;
@@ -109,7 +110,8 @@ hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t attr, int devi
 
 namespace {
 hipError_t record(const char* name, std::initializer_list<const void*> ptrs = {},
-                  std::initializer_list<int> vals = {}) {
+                  std::initializer_list<int> vals = {},
+                  std::initializer_list<const void*> ext = {}) {
   std::strncpy(kda_host_check_last_launch, name, sizeof(kda_host_check_last_launch) - 1);
   ++kda_host_check_launches;
   if (kda_host_check_log_len < 64) {
@@ -120,6 +122,8 @@ hipError_t record(const char* name, std::initializer_list<const void*> ptrs = {}
     for (const void* p : ptrs) e.ptr[i++] = p;
     i = 0;
     for (int v : vals) e.val[i++] = v;
+    i = 0;
+    for (const void* p : ext) e.ext[i++] = p;
   }
   return hipSuccess;
 }
@@ -144,14 +148,16 @@ hipError_t launch_chunk_transition(const ChunkArgs& a, hipStream_t) {
   return record_scan("chunk_transition", a);
 }
 hipError_t launch_chunk_split_pass(const ChunkArgs& a, hipStream_t) {
-  return record_chunk("chunk_split_pass", a);
+  // the split pass has no q: its slot holds the transposed maps
+  return record("chunk_split_pass", {a.hT3, a.h0, a.hT, a.hT2, a.o, a.order, a.seqs.cu, a.v},
+                {a.seqs.N, a.h0_group, a.hT_group, 0});
 }
 hipError_t launch_chunk_checkpoint(const ChunkArgs& a, hipStream_t) {
   return record_scan("chunk_checkpoint", a);
 }
 hipError_t launch_chunk_fwd_checkpoint(const ChunkArgs& a, hipStream_t) {
   return record("chunk_fwd_checkpoint", {a.q, a.o, a.hT, a.order, a.ck_state, a.ck_u, a.ck_vt, a.ck_at},
-                {a.seqs.N, a.H, 0, 0});
+                {a.seqs.N, a.H, a.hT_group, a.ck_pieces}, {a.h0, a.seqs.cu});
 }
 hipError_t launch_chunk_reverse(const ChunkArgs& a, hipStream_t) { return record_scan("chunk_reverse", a); }
 hipError_t launch_gated_rmsnorm(const void*, const void*, bool, const float*, float, long, int, void*,

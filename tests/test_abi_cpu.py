@@ -326,7 +326,7 @@ def test_noalloc_rejects_a_workspace_beyond_the_scratch():
 
 class _Launch(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 24), ("ptr", ctypes.c_void_p * 8),
-                ("val", ctypes.c_int * 4)]
+                ("val", ctypes.c_int * 4), ("ext", ctypes.c_void_p * 4)]
 
 
 def _split_offsets(nseq, P, H=32, Dk=128, Dv=128):
@@ -530,6 +530,26 @@ def test_training_forward_writes_what_the_saved_backward_reads():
     assert saved[2][1:3] == full[2][1:3]              # same slots, same sequences
 
 
+def _long256k_bwd_split_layout(lib, T=262144, H=32, D=128, P=8):
+    """Offsets of kda_chunk_bwd's workspace for long256k (B = 1) on a 256-CU
+    device: the base layout (checkpoints, per-token arrays), then the split
+    region (piece table and orders, M, b, entry states, M^T, c, exit
+    gradients). Returns (ck, tok, base, off, MT, C, X, total bytes)."""
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    ck = up(4097 * H * D * D * 2)        # slots: max(4096 dense, 4096 + 1 packed)
+    tok = up(T * H * D * 2)
+    at = up(T * H * 16 * 4)
+    base = 2 * ck + 3 * tok + at
+    off = _split_offsets(1, P)
+    state = up(P * H * D * D * 4)
+    split_base = off["starts"] + state
+    MT, C, X = split_base, split_base + state, split_base + 2 * state
+    ws = ctypes.c_size_t(0)
+    assert lib.kda_chunk_bwd_workspace_size(1, T, H, D, D, 1, 64, 1, ctypes.byref(ws)) == 0
+    assert ws.value == base + X + state
+    return ck, tok, base, off, MT, C, X, ws
+
+
 def test_split_backward_launches_what_it_should():
     """Only in the host-check build, on a 256-CU stand-in device: kda_chunk_bwd
     on long256k (B=1, T=262144, H=32: 32 chains) splits both scans into the
@@ -551,18 +571,7 @@ def test_split_backward_launches_what_it_should():
     n = ctypes.c_int.in_dll(lib, "kda_host_check_log_len")
     T, H, D, P = 262144, 32, 128, 8
     Q, K, V, G, BETA, H0, DO, DHT, DH0, WS = (FAKE * (i + 1) for i in range(10))
-    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    ck = up(4097 * H * D * D * 2)        # slots: max(4096 dense, 4096 + 1 packed)
-    tok = up(T * H * D * 2)
-    at = up(T * H * 16 * 4)
-    base = 2 * ck + 3 * tok + at
-    off = _split_offsets(1, P)
-    state = up(P * H * D * D * 4)
-    split_base = off["starts"] + state
-    MT, C, X = split_base, split_base + state, split_base + 2 * state
-    ws = ctypes.c_size_t(0)
-    assert lib.kda_chunk_bwd_workspace_size(1, T, H, D, D, 1, 64, 1, ctypes.byref(ws)) == 0
-    assert ws.value == base + X + state
+    ck, tok, base, off, MT, C, X, ws = _long256k_bwd_split_layout(lib)
 
     def call(ws_bytes):
         lib.kda_host_check_log_clear()
@@ -577,8 +586,10 @@ def test_split_backward_launches_what_it_should():
                                    "chunk_reverse", "compose_rev", "chunk_reverse", "chunk_bwd"]
     S = WS + base  # the split region
     assert got[0][1][0] == S and got[0][2] == [1, P, 0, 0]
-    # split pass: no q, h0 or o; maps and zero-start states of all 8 pieces
-    assert got[1][1] == [0, 0, S + off["M"], S + off["b"], 0, 0, S, V] and got[1][2][0] == P
+    # split pass: no h0 or o; maps, their transposes and zero-start states of
+    # all 8 pieces
+    assert got[1][1] == [S + MT, 0, S + off["M"], S + off["b"], 0, 0, S, V]
+    assert got[1][2][0] == P
     assert got[2][1][:4] == [S + off["M"], S + off["b"], H0, S + off["starts"]]
     assert got[2][2] == [1, P, P, 1]
     # checkpoints: from the entry states, every piece, into the sequence's slots
@@ -599,3 +610,60 @@ def test_split_backward_launches_what_it_should():
     got = call(base)
     assert [g[0] for g in got] == ["chunk_bwd"]
     assert got[0][2][0] == 0 and got[0][2][3] == 0
+
+
+def test_split_training_pair_launches_what_it_should():
+    """Only in the host-check build, on a 256-CU stand-in device, long256k:
+    kda_chunk_fwd_train with the split region runs the piece table, the split
+    pass (maps, their transposes, zero-start final states), the entry states
+    from the initial state, then the forward with checkpoints over every piece
+    from its entry state, writing o, the sequence's checkpoint slots and, from
+    the last piece, the final state. kda_chunk_bwd_saved then runs the reverse
+    split only, through the transposes the forward left, and the gradient
+    kernel with both scans skipped. Without the split region both run
+    unsplit."""
+    lib = _lib.load()
+    if not hasattr(lib, "kda_host_check_build"):
+        pytest.skip("needs the host-check build (tests/test_sanitizers_cpu.py)")
+    lib.kda_host_check_set_compute_units.argtypes = [ctypes.c_int]
+    lib.kda_host_check_set_compute_units(256)
+    log = (_Launch * 64).in_dll(lib, "kda_host_check_log")
+    n = ctypes.c_int.in_dll(lib, "kda_host_check_log_len")
+    T, H, D, P = 262144, 32, 128, 8
+    WS, O, HT, H0 = FAKE * 9, FAKE * 7, FAKE * 8, FAKE * 6
+    ck, tok, base, off, MT, C, X, ws = _long256k_bwd_split_layout(lib)
+    S = WS + base
+
+    def pair(ws_bytes):
+        lib.kda_host_check_log_clear()
+        kw = dict(B=1, N=1, T=T, H=H, h0=H0, ws=WS, ws_bytes=ws_bytes)
+        assert _train_call(lib, "fwd", hT=HT, **kw) == 0
+        assert _train_call(lib, "bwd", **kw) == 0
+        return [(log[i].name.decode(), [p or 0 for p in log[i].ptr], list(log[i].val),
+                 [p or 0 for p in log[i].ext]) for i in range(n.value)]
+
+    got = pair(ws.value)
+    assert [g[0] for g in got] == ["split_tables", "chunk_split_pass", "compose",
+                                   "chunk_fwd_checkpoint", "split_tables", "chunk_reverse",
+                                   "compose_rev", "chunk_reverse", "chunk_bwd"]
+    assert got[0][2] == [1, P, 0, 0] and got[4][2] == [1, P, 0, 0]
+    assert got[1][1] == [S + MT, 0, S + off["M"], S + off["b"], 0, 0, S, FAKE * 3]
+    assert got[2][1][:4] == [S + off["M"], S + off["b"], H0, S + off["starts"]]
+    # every piece from its entry state: q, o, the final state from the last
+    # piece, the checkpoint arrays at the base layout's addresses
+    fwd = got[3]
+    assert fwd[1][:4] == [FAKE, O, HT, 0]
+    assert fwd[1][4:8] == [WS, WS + 2 * ck, WS + 2 * ck + tok, WS + 2 * ck + 3 * tok]
+    assert fwd[2] == [P, H, P, P]
+    assert fwd[3][:2] == [S + off["starts"], S]
+    # the saved backward: reverse split through the forward's transposes
+    assert got[6][1][:4] == [S + MT, S + C, 0, S + X]
+    assert got[7][1][:3] == [FAKE, S + X, 0] and got[7][2] == [P, P, P, T]
+    assert got[8][2][0] == 1 and got[8][2][3] == 1
+    assert got[8][1][0] == WS
+
+    # a workspace of the base layout only: both unsplit
+    got = pair(base)
+    assert [g[0] for g in got] == ["chunk_fwd_checkpoint", "chunk_bwd"]
+    assert got[0][2] == [1, H, 0, 0] and got[0][3][:2] == [H0, 0]
+    assert got[1][2][0] == 1 and got[1][2][3] == 0
