@@ -166,6 +166,11 @@ def _stress(kind):
             d["beta"] = torch.zeros_like(d["beta"])
         elif kind == "beta_one":
             d["beta"] = torch.ones_like(d["beta"])
+        elif kind == "beta_some_zero":
+            # the first 64-token chunk mixes beta = 0 and 1e-35 rows (dbeta
+            # formed from v) with ordinary ones; later chunks divide by beta
+            d["beta"][:, 0:64:3] = 0.0
+            d["beta"][:, 1:64:7] = 1e-35
         elif kind == "identical_keys":
             d["k"] = d["k"][:, :1].expand_as(d["k"]).contiguous()
         elif kind == "large_values":
@@ -174,13 +179,14 @@ def _stress(kind):
 
 
 @pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)])
-@pytest.mark.parametrize("stress", ["g_min_everywhere", "g_zero", "beta_zero", "beta_one",
-                                    "identical_keys", "large_values"])
+@pytest.mark.parametrize("stress", ["g_min_everywhere", "g_zero", "beta_zero", "beta_some_zero",
+                                    "beta_one", "identical_keys", "large_values"])
 def test_bwd_numeric_stress(dtype, D, stress):
     """The forward's extreme cases, differentiated: the gate's lower bound on
     every token (largest in-tile decay ratios), no decay, no writes (beta = 0:
-    the gradient w.r.t. beta is still nonzero), full writes, identical keys
-    (rank-one key-key matrix) and large values."""
+    the gradient w.r.t. beta is still nonzero; also zero and 1e-35 betas
+    among ordinary ones), full writes, identical keys (rank-one key-key
+    matrix) and large values."""
     _run(f"stress {stress} {dtype} D={D}", 1, 150, 2, D, D, dtype, mutate=_stress(stress), seed=46)
 
 

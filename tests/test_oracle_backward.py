@@ -203,12 +203,14 @@ def test_planted_mistakes_fail_the_pin(tmp_path, old, new):
     assert _fd_mismatch(got, fd) > 1e-3
 
 
+@pytest.mark.parametrize("betas", ["sigmoid", "zeros"])
 @pytest.mark.parametrize("T", [1, 15, 16, 17, 50])
-def test_tile_arrangement_matches_oracle(T):
+def test_tile_arrangement_matches_oracle(T, betas):
     """The 16-token tile arrangement the GPU backward uses (forward scan for
     U and V~, reverse scan for dY and the state gradients, then per-tile
     gradients through the decay factors), written in fp64 numpy, gives the
-    oracle's gradients to rounding."""
+    oracle's gradients to rounding; with "zeros" some beta are 0 or 1e-35
+    (tokens that write nothing, whose beta gradient is still nonzero)."""
     from tests.chunk_mirror import tile_backward
     rng = np.random.default_rng(12 + T)
     Dk, Dv = 8, 6
@@ -218,6 +220,9 @@ def test_tile_arrangement_matches_oracle(T):
     v = rng.standard_normal((T, Dv))
     g = -5.0 * expit(rng.standard_normal((T, Dk)))
     beta = expit(rng.standard_normal(T))
+    if betas == "zeros":
+        beta[::3] = 0.0
+        beta[1::5] = 1e-35
     S0, dST = rng.standard_normal((Dk, Dv)), rng.standard_normal((Dk, Dv))
     do = rng.standard_normal((T, Dv))
     got = tile_backward(q, k, v, g, beta, S0, do, dST, scale=0.8)
