@@ -235,8 +235,103 @@ bool decode128_applies(const RecurrentArgs& a) {
   return a.Dk == kDecDk && a.Dv % 4 == 0 && !a.seqs.cu && a.seqs.T == 1 && a.h0 && a.hT && a.o;
 }
 
+// Decode step for d_k = d_v = 128, read and written the way a copy streams
+// memory: one workgroup of 256 threads per state, thread t holding columns
+// 4 (t % 32) .. 4 (t % 32) + 3 of rows t / 32 + 8 i (i = 0..15), so that each
+// 16-byte load or store instruction of a wavefront covers two whole 512-byte
+// rows. The token's rows (k, q, the decays) go through LDS. Both dot products
+// are taken before the update: with S the decayed state, u = S^T k and
+// w = S^T q, d = beta (v - u), S' = S + k d^T and o = S'^T q = w + d (k . q),
+// so one barrier sums both over the eight row groups.
+constexpr int kDecStThreads = 256;
+constexpr int kDecStQuads = 32;                          // 16-byte column pieces per row
+constexpr int kDecStGroups = kDecStThreads / kDecStQuads;  // row groups: 8
+constexpr int kDecStRows = kDecDk / kDecStGroups;        // rows per thread: 16
+constexpr int kDecStWaves = kDecStThreads / 64;
+
+template <typename T>
+__global__ void __launch_bounds__(kDecStThreads) decode_state_kernel(RecurrentArgs a) {
+  const T* __restrict__ q = reinterpret_cast<const T*>(a.q);
+  const T* __restrict__ k = reinterpret_cast<const T*>(a.k);
+  const T* __restrict__ v = reinterpret_cast<const T*>(a.v);
+  T* __restrict__ o = reinterpret_cast<T*>(a.o);
+  __shared__ float s_k[kDecDk], s_q[kDecDk], s_a[kDecDk];
+  __shared__ f32x4 s_uw[kDecStWaves][2][kDecStQuads];  // per wavefront: u, w partial sums
+  __shared__ float s_kq[kDecStWaves];
+  const int unit = blockIdx.x, h = unit % a.H;
+  const int t = threadIdx.x, cq = t % kDecStQuads, rg = t / kDecStQuads;
+  const int lane = t & 63, wave = t >> 6;
+  const size_t sbase = (size_t)unit * kDecDk * kDecDk + 4 * cq;
+  f32x4 S[kDecStRows];
+#pragma unroll
+  for (int i = 0; i < kDecStRows; ++i)
+    S[i] = *reinterpret_cast<const f32x4*>(a.h0 + sbase + (size_t)(rg + kDecStGroups * i) * kDecDk);
+  const size_t tok = (size_t)unit * kDecDk;
+  if (t < kDecDk) {
+    s_k[t] = to_f32(k[tok + t]);
+    s_q[t] = to_f32(q[tok + t]);
+    const float es = ((a.gate_mode == kGateLogits || a.gate_mode == kGateSoftplus) && a.A_log)
+                         ? __expf(a.A_log[h]) : 1.0f;
+    float gv = a.g[tok + t];
+    if (a.gate_mode == kGateLogits) gv = a.g_min / (1.0f + __expf(-es * gv));
+    if (a.gate_mode == kGateSoftplus) gv = -es * (fmaxf(gv, 0.f) + log1pf(__expf(-fabsf(gv))));
+    s_a[t] = __expf(gv);
+  }
+  const f32x4 vv = load4_f32(v + (size_t)unit * kDecDk + 4 * cq);
+  const float beta = a.beta[unit];
+  __syncthreads();
+  // decay, then this thread's rows of u = S^T k and w = S^T q
+  f32x4 u = {0.f, 0.f, 0.f, 0.f}, w = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kDecStRows; ++i) {
+    const int r = rg + kDecStGroups * i;
+    S[i] = S[i] * s_a[r];
+    u = u + S[i] * s_k[r];
+    w = w + S[i] * s_q[r];
+  }
+  // lanes l and l + 32 of a wavefront hold the same columns
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    u[e] += __shfl_xor(u[e], 32, 64);
+    w[e] += __shfl_xor(w[e], 32, 64);
+  }
+  if (lane < kDecStQuads) {
+    s_uw[wave][0][cq] = u;
+    s_uw[wave][1][cq] = w;
+  }
+  // k . q: each wavefront takes kDecDk / kDecStWaves of the 128 rows
+  constexpr int kqr = kDecDk / kDecStWaves;
+  static_assert(kqr <= 64 && (kqr & (kqr - 1)) == 0, "rows of k . q per wavefront");
+  float kq = lane < kqr ? s_k[kqr * wave + lane] * s_q[kqr * wave + lane] : 0.f;
+#pragma unroll
+  for (int m = kqr / 2; m >= 1; m >>= 1) kq += __shfl_xor(kq, m, 64);
+  if (lane == 0) s_kq[wave] = kq;
+  __syncthreads();
+  u = s_uw[0][0][cq];
+  w = s_uw[0][1][cq];
+  kq = s_kq[0];
+#pragma unroll
+  for (int ww = 1; ww < kDecStWaves; ++ww) {
+    u = u + s_uw[ww][0][cq];
+    w = w + s_uw[ww][1][cq];
+    kq += s_kq[ww];
+  }
+  const f32x4 d = (vv - u) * beta;
+#pragma unroll
+  for (int i = 0; i < kDecStRows; ++i) {
+    const int r = rg + kDecStGroups * i;
+    *reinterpret_cast<f32x4*>(a.hT + sbase + (size_t)r * kDecDk) = S[i] + d * s_k[r];
+  }
+  if (rg == 0) store4(o + (size_t)unit * kDecDk + 4 * cq, (w + d * kq) * a.scale);
+}
+
 template <typename T>
 static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream) {
+  if (decode128_applies(a) && a.Dv == kDecDk) {
+    hipLaunchKernelGGL((decode_state_kernel<T>), dim3((unsigned)(a.seqs.N * a.H)),
+                       dim3(kDecStThreads), 0, stream, a);
+    return hipGetLastError();
+  }
   if (decode128_applies(a)) {
     const int cols_per_block = kDecWaves * kDecColsPerWave;
     dim3 grid((unsigned)(a.seqs.N * a.H), (unsigned)((a.Dv + cols_per_block - 1) / cols_per_block));

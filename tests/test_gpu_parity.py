@@ -204,16 +204,18 @@ def test_beta_zero_pure_decay_of_the_state(dtype, D, T):
 
 # ------------------------------------------------------------ decode step ---
 
-@pytest.mark.parametrize("dtype,Dk,Dv", [(torch.bfloat16, 128, 128), (torch.float32, 64, 64),
+@pytest.mark.parametrize("dtype,Dk,Dv", [(torch.bfloat16, 128, 128), (torch.float32, 128, 128),
+                                         (torch.float32, 64, 64),
                                          (torch.float32, 96, 40), (torch.float32, 256, 130),
                                          (torch.bfloat16, 8, 200), (torch.float32, 128, 64),
                                          (torch.bfloat16, 128, 20), (torch.float32, 128, 132),
                                          (torch.float32, 128, 130)])
 def test_decode_steps_match_oracle(dtype, Dk, Dv):
     """T decode steps (one kda_recurrent_step per token) against the oracle's
-    recurrence; d_k = 128 with d_v a multiple of 4 runs the decode kernel
-    (including a partly filled wavefront at d_v = 20 and 132), other shapes
-    the general token-serial kernel."""
+    recurrence; d_k = d_v = 128 runs the one-workgroup-per-state decode
+    kernel, other d_v (multiples of 4) at d_k = 128 the column-slice decode
+    kernel (including a partly filled wavefront at d_v = 20 and 132), other
+    shapes the general token-serial kernel."""
     _print_case(f"decode steps {dtype} Dk={Dk} Dv={Dv}")
     N, H, T = 3, 4, 6
     d = make_inputs(N, T, H, Dk, Dv, dtype, h0_std=0.02, seed=16)
