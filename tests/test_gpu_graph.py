@@ -12,8 +12,11 @@ tolerance, and against the eager call of the same inputs.
 
 The backward (kda_chunk_bwd: checkpoint scan, reverse scan, per-chunk
 gradients, and for packed sequences the longest-first order it computes into
-the workspace) is captured the same way. It is deterministic, so every replay
-must equal the eager call bit for bit, besides matching the oracle.
+the workspace; for the long dense sequence both scans' context split: piece
+table, split pass, compositions, scans over the pieces) is captured the same
+way, and so is the training pair (kda_chunk_fwd_train, kda_chunk_bwd_saved).
+Both are deterministic, so every replay must equal the eager call bit for
+bit, besides matching the oracle.
 """
 import pytest
 import torch
@@ -88,6 +91,7 @@ def test_captured_forward_replays(name, kw):
 BWD_CASES = [
     ("dense B=1 H=2 T=1000 logits", dict(B=1, T=1000, lengths=None)),
     ("packed 6 sequences H=2 with h0 and dhT", dict(B=1, T=0, lengths=[700, 0, 33, 1290, 64, 517])),
+    ("dense B=1 H=2 T=20000 (context split of both scans)", dict(B=1, T=20000, lengths=None)),
 ]
 GRADS = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
 
@@ -141,17 +145,26 @@ def test_captured_backward_replays(name, kw):
         assert all(e <= TOL_BF16 for e in errs.values()), errs
 
 
-def test_captured_training_pair_replays():
+TRAIN_CASES = [
+    ("packed 6 sequences H=2", dict(T=0, lengths=[700, 0, 33, 1290, 64, 517])),
+    ("dense B=1 H=2 T=20000 (context split)", dict(T=20000, lengths=None)),
+]
+
+
+@pytest.mark.parametrize("name,kw", TRAIN_CASES, ids=[c[0] for c in TRAIN_CASES])
+def test_captured_training_pair_replays(name, kw):
     """kda_chunk_fwd_train and kda_chunk_bwd_saved captured together (packed
     sequences: both compute the longest-first order into the backward
-    workspace): every replay equals the eager pair bit for bit."""
-    print("\n[case] graph capture, training pair: packed 6 sequences H=2", flush=True)
+    workspace; the long dense sequence: both take the context split, the
+    forward leaving the maps' transposes for the backward): every replay
+    equals the eager pair bit for bit."""
+    print(f"\n[case] graph capture, training pair: {name}", flush=True)
     from gated_delta_rule_92_amd import chunk_fwd_train
     H, D = 2, 128
-    d = make_inputs(1, 0, H, D, D, torch.bfloat16, h0_std=0.02,
-                    lengths=[700, 0, 33, 1290, 64, 517], seed=55)
+    d = make_inputs(1, kw["T"], H, D, D, torch.bfloat16, h0_std=0.02, lengths=kw["lengths"],
+                    seed=55)
     B, T = d["q"].shape[0], d["q"].shape[1]
-    N = d["cu_seqlens"].numel() - 1
+    N = B if d["cu_seqlens"] is None else d["cu_seqlens"].numel() - 1
     gen = torch.Generator().manual_seed(56)
     do = torch.randn(B, T, H, D, generator=gen).to(torch.bfloat16).cuda()
     dhT = torch.randn(N, H, D, D, generator=gen).cuda()
