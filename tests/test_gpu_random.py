@@ -4,7 +4,8 @@ a fixed seed: dense or packed sequences (0 to 300 tokens, empty ones
 included), 1 to 3 heads, d_k and d_v in {64, 128} independently, bf16 or fp32,
 gate logits or per-token log-decay, with or without an initial state and a
 final-state gradient, output scale in [0.5, 1.5]. A second sweep draws long
-dense problems that kda_chunk_fwd runs as a context split. The same bar as
+dense problems that kda_chunk_fwd runs as a context split, and a third such
+problems for kda_chunk_bwd, whose two scans split the same way. The same bar as
 the other parity tests: max|gpu - ref| / max|ref| <= 2e-2 (bf16) and 1e-4
 (fp32) per output array. For bf16 d_k = d_v = 128 problems the training pair
 (kda_chunk_fwd_train, kda_chunk_bwd_saved) must also equal the plain calls bit
@@ -161,3 +162,69 @@ def test_random_automatic_split(seed):
     eo, es = rel_err(o, ro), rel_err(hT, rs)
     print(f"  err_o={eo:.2e} err_state={es:.2e}", flush=True)
     assert eo <= 2e-2 and es <= 2e-2
+
+
+def _split_bwd_problem(seed):
+    """A long dense bf16 d = 128 problem whose backward scans split (as
+    _split_problem), with gate logits, per-token log-decay, or a log-decay in
+    [-0.002, 0] that keeps states and gradients alive across every piece, so
+    that the composed maps decide the result."""
+    rng = np.random.default_rng(7000 + seed)
+    B = int(rng.integers(1, 3))
+    H = int(rng.choice([1, 2, 4, 8]))
+    T = int(rng.integers(2000, 24001))
+    return dict(B=B, H=H, T=T, gate=str(rng.choice(["logits", "logdecay", "slow"])),
+                h0=bool(rng.random() < 0.7), dh=bool(rng.random() < 0.7),
+                scale=float(np.round(rng.uniform(0.5, 1.5), 3)))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_split_backward(seed):
+    """kda_chunk_bwd on random long dense problems that take the context
+    split of both scans: every element of every sequence of up to two heads
+    against the oracle's derivative (the heads are independent, so the oracle
+    runs on those heads alone), and every element of all heads against the
+    same call in a workspace without the split region (unsplit)."""
+    from gated_delta_rule_92_amd.ops import bwd_workspace_size
+    s = _split_bwd_problem(seed)
+    print(f"\n[case] random split backward {seed}: B={s['B']} H={s['H']} T={s['T']} "
+          f"gate={s['gate']} h0={s['h0']} dhT={s['dh']} scale={s['scale']}", flush=True)
+    B, H, T, D = s["B"], s["H"], s["T"], 128
+    d = make_inputs(B, T, H, D, D, torch.bfloat16, h0_std=0.02 if s["h0"] else 0.0,
+                    seed=8000 + seed)
+    gen = torch.Generator().manual_seed(9000 + seed)
+    do = torch.randn(B, T, H, D, generator=gen).to(torch.bfloat16)
+    dhT = torch.randn(B, H, D, D, generator=gen) if s["dh"] else None
+    if s["gate"] == "logits":
+        g_in, mode, g_ref = d["z"], "logits", oracle_gate(d["z"], None, -5.0)
+    elif s["gate"] == "slow":
+        g_in = (-0.002 * torch.sigmoid(d["z"])).contiguous()
+        mode, g_ref = "logdecay", g_in
+    else:
+        g_in = torch.from_numpy(oracle_gate(d["z"], None, -5.0)).float()
+        mode, g_ref = "logdecay", g_in
+    dev = lambda x: None if x is None else x.cuda()  # noqa: E731
+    ins = (dev(d["q"]), dev(d["k"]), dev(d["v"]), dev(g_in), dev(d["beta"]), dev(do), dev(d["h0"]),
+           dev(dhT), None)
+    split = chunk_bwd(*ins, gate=mode, scale=s["scale"])
+    base = torch.empty(bwd_workspace_size(B, T, H, D, D, B + 1, 64, torch.bfloat16),
+                       dtype=torch.uint8, device="cuda")
+    plain = chunk_bwd(*ins, gate=mode, scale=s["scale"], workspace=base)
+    torch.cuda.synchronize()
+    names = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+    vs = {n: rel_err(split[n], plain[n].double().cpu()) for n in names}
+    heads = [0] if H == 1 else [0, H - 1]
+    sl = lambda x: None if x is None else x[:, :, heads].contiguous()  # noqa: E731
+    slh = lambda x: None if x is None else x[:, heads].contiguous()  # noqa: E731
+    g_sl = g_ref[:, :, heads] if isinstance(g_ref, np.ndarray) else sl(g_ref)
+    ref = oracle_backward(sl(d["q"]), sl(d["k"]), sl(d["v"]), g_sl, sl(d["beta"]), sl(do),
+                          slh(d["h0"]), slh(dhT), None, s["scale"])
+    errs = {}
+    for n in names:
+        x = split[n][:, heads] if n == "dh0" else split[n][:, :, heads]
+        errs[n] = rel_err(x, ref[n])
+    print("  split vs oracle (heads %s) " % heads +
+          " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+    print("  split vs unsplit " + " ".join(f"{n}={e:.2e}" for n, e in vs.items()), flush=True)
+    assert all(e <= 2e-2 for e in errs.values()), errs
+    assert all(e <= 2e-2 for e in vs.values()), vs
