@@ -414,6 +414,9 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
 
 def bwd_workspace_size(B: int, T: int, H: int, Dk: int, Dv: int, N: int, chunk: int = 64,
                        dtype=torch.bfloat16) -> int:
+    """kda_chunk_bwd_workspace_size: bytes of the backward workspace, with the
+    region of the scans' context split where dense sequences (N == B) of this
+    shape take it on the current device."""
     lib = _lib.load()
     import ctypes
     out = ctypes.c_size_t(0)
@@ -494,7 +497,10 @@ def chunk_fwd_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
     """kda_chunk_fwd_train: chunk_fwd's (o, final_state) and, in the same
     pass, the backward's checkpoints in a backward workspace (allocated when
     bwd_workspace is None). Returns (o, final_state, bwd_workspace); pass the
-    workspace to chunk_bwd(..., saved=True) with the same inputs."""
+    workspace to chunk_bwd(..., saved=True) with the same inputs. Its size
+    decides whether both calls take the context split of long dense
+    sequences (bwd_workspace_size includes it where it applies), so the two
+    calls must get the same tensor."""
     lib = _lib.load()
     dev = q.device
     dt = q.dtype
