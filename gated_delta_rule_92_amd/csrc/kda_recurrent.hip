@@ -236,21 +236,22 @@ bool decode128_applies(const RecurrentArgs& a) {
 }
 
 // Decode step for d_k = d_v = 128, read and written the way a copy streams
-// memory: one workgroup of 256 threads per state, thread t holding columns
-// 4 (t % 32) .. 4 (t % 32) + 3 of rows t / 32 + 8 i (i = 0..15), so that each
+// memory: one workgroup of NT threads per state, thread t holding columns
+// 4 (t % 32) .. 4 (t % 32) + 3 of rows t / 32 + (NT / 32) i, so that each
 // 16-byte load or store instruction of a wavefront covers two whole 512-byte
 // rows. The token's rows (k, q, the decays) go through LDS. Both dot products
 // are taken before the update: with S the decayed state, u = S^T k and
 // w = S^T q, d = beta (v - u), S' = S + k d^T and o = S'^T q = w + d (k . q),
-// so one barrier sums both over the eight row groups.
-constexpr int kDecStThreads = 256;
-constexpr int kDecStQuads = 32;                          // 16-byte column pieces per row
-constexpr int kDecStGroups = kDecStThreads / kDecStQuads;  // row groups: 8
-constexpr int kDecStRows = kDecDk / kDecStGroups;        // rows per thread: 16
-constexpr int kDecStWaves = kDecStThreads / 64;
+// so one barrier sums both over the row groups. NT = 512 when every state
+// has a compute unit of its own (more wavefronts per state, half the rows
+// each), 256 when several workgroups share a compute unit and overlap.
+constexpr int kDecStQuads = 32;  // 16-byte column pieces per row
 
-template <typename T>
-__global__ void __launch_bounds__(kDecStThreads) decode_state_kernel(RecurrentArgs a) {
+template <typename T, int NT>
+__global__ void __launch_bounds__(NT) decode_state_kernel(RecurrentArgs a) {
+  constexpr int kDecStGroups = NT / kDecStQuads;       // row groups
+  constexpr int kDecStRows = kDecDk / kDecStGroups;    // rows per thread
+  constexpr int kDecStWaves = NT / 64;
   const T* __restrict__ q = reinterpret_cast<const T*>(a.q);
   const T* __restrict__ k = reinterpret_cast<const T*>(a.k);
   const T* __restrict__ v = reinterpret_cast<const T*>(a.v);
@@ -328,8 +329,15 @@ __global__ void __launch_bounds__(kDecStThreads) decode_state_kernel(RecurrentAr
 template <typename T>
 static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream) {
   if (decode128_applies(a) && a.Dv == kDecDk) {
-    hipLaunchKernelGGL((decode_state_kernel<T>), dim3((unsigned)(a.seqs.N * a.H)),
-                       dim3(kDecStThreads), 0, stream, a);
+    const dim3 grid((unsigned)(a.seqs.N * a.H));
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidDevice;
+    if ((long)a.seqs.N * a.H <= cus)
+      hipLaunchKernelGGL((decode_state_kernel<T, 512>), grid, dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_state_kernel<T, 256>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   if (decode128_applies(a)) {

@@ -232,6 +232,27 @@ def test_decode_steps_match_oracle(dtype, Dk, Dv):
     _check(o, state, _oracle(d), dtype, "decode")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_decode_more_states_than_compute_units(dtype):
+    """Decode of 128 x 128 states with more (sequence, head) units than a
+    256-CU device has compute units (70 x 4 = 280): the decode kernel then
+    runs 256 threads per state, several workgroups sharing a compute unit
+    (the other decode cases, with fewer states, run 512)."""
+    _print_case(f"decode steps {dtype} 280 states of 128 x 128")
+    N, H, T = 70, 4, 2
+    d = make_inputs(N, T, H, 128, 128, dtype, h0_std=0.02, seed=19)
+    dd = to_dev(d)
+    state = dd["h0"].clone()
+    outs = []
+    for t in range(T):
+        g = gate(dd["z"][:, t:t + 1].contiguous(), None, -5.0)[:, 0].contiguous()
+        outs.append(recurrent_step(dd["q"][:, t].contiguous(), dd["k"][:, t].contiguous(),
+                                   dd["v"][:, t].contiguous(), g, dd["beta"][:, t].contiguous(),
+                                   state))
+    torch.cuda.synchronize()
+    _check(torch.stack(outs, dim=1), state, _oracle(d), dtype, "decode-280")
+
+
 @pytest.mark.parametrize("gate_mode", ["logits", "softplus"])
 def test_decode128_gates_with_A_log(gate_mode):
     """The d_k = 128 decode kernel with the gate applied in place (bounded
