@@ -136,6 +136,46 @@ def test_backward_one_token_closed_forms():
     np.testing.assert_allclose(got["dh0"][0, 0], ref_dS0, rtol=1e-12, atol=1e-12)
 
 
+def test_backward_pure_decay_closed_forms():
+    """beta = 0 on every token [KDA-blog §Kimi Delta Attention, KDA
+    equation]: nothing is written, S_t = Diag(e^{G_t}) S0 with G_t the
+    inclusive cumulative log-decay, o_t = s S_t^T q_t. Then, with
+    Gtot_t = sum_{t' >= t} Diag(e^{G_t' - G_t}) s q_t' do_t'^T
+    + Diag(e^{G_T - G_t}) dhT the total gradient on S_t:
+    dq_t = s S_t do_t, dk = dv = 0,
+    dS0 = sum_t Diag(e^{G_t}) s q_t do_t^T + Diag(e^{G_T}) dhT,
+    dg_tau = sum_{t >= tau} dL/dG_t with
+    dL/dG_t[c] = e^{G_t[c]} S0[c,:] . (s q_t[c] do_t + [t = T] dhT[c,:]),
+    and dbeta_t = (Gtot_t^T k_t) . (v_t - S_t^T k_t), the derivative of the
+    write term beta_t k_t (v_t - S^T k_t)^T at beta = 0, over 37 tokens."""
+    rng = np.random.default_rng(11)
+    T, Dk, Dv, s = 37, 6, 5, 0.7
+    cu = np.array([0, T], dtype=np.int32)
+    x, do, dhT = _problem(rng, T, 1, Dk, Dv, 1)
+    x["beta"][:] = 0.0
+    q, k, v, g = (x[n][0, :, 0] for n in ("q", "k", "v", "g"))
+    dO, S0, dST = do[0, :, 0], x["h0"][0, 0], dhT[0, 0]
+    G = np.cumsum(g, axis=0)                        # [T, Dk], inclusive
+    E = np.exp(G)
+    S = E[:, :, None] * S0[None]                    # S_t, [T, Dk, Dv]
+    got = oracle_backward(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["h0"], dhT, cu, s)
+    np.testing.assert_allclose(got["dq"][0, :, 0], s * np.einsum("tcv,tv->tc", S, dO),
+                               rtol=1e-12, atol=1e-12)
+    assert not np.any(got["dk"]) and not np.any(got["dv"])
+    dS0 = s * np.einsum("tc,tc,tv->cv", E, q, dO) + E[-1][:, None] * dST
+    np.testing.assert_allclose(got["dh0"][0, 0], dS0, rtol=1e-12, atol=1e-12)
+    dG = s * q * E * np.einsum("cv,tv->tc", S0, dO)
+    dG[-1] += E[-1] * np.sum(S0 * dST, axis=1)
+    dg = np.cumsum(dG[::-1], axis=0)[::-1]
+    np.testing.assert_allclose(got["dg"][0, :, 0], dg, rtol=1e-11, atol=1e-12)
+    dbeta = np.empty(T)
+    for t in range(T):
+        R = np.exp(G[t:] - G[t])                    # e^{G_t' - G_t}, [T - t, Dk]
+        Gtot = s * np.einsum("uc,uc,uv->cv", R, q[t:], dO[t:]) + R[-1][:, None] * dST
+        dbeta[t] = (Gtot.T @ k[t]) @ (v[t] - S[t].T @ k[t])
+    np.testing.assert_allclose(got["dbeta"][0, :, 0], dbeta, rtol=1e-11, atol=1e-12)
+
+
 def test_backward_zero_cotangent_and_empty_sequence():
     rng = np.random.default_rng(10)
     x, do, dhT = _problem(rng, int(CU[-1]), 2, 4, 3, 3)
